@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic
+input:
+  prefill of one linear-attention layer of the 0.8B hybrid shape
+  (T = 4096 tokens, 16 key / 16 value heads, head dims 128, bf16 pre-conv x):
+      gdn_conv_qk_prep  -> gdn_chunk_prefill_local -> gdn_chunk_prefill_state
+  followed by one decode step of 256 sequences (gdn_decode_step, fp32 state in place).
+
+`value` is prefill tokens/s (4096 tokens over the summed per-step event time of
+the three prefill kernels); the decode part is reported under "decode" as
+tokens/s and state GB/s.  Each kernel is timed with HIP events recorded on the
+stream it is launched on; inputs rotate over several copies at different
+addresses so that the 256 MB Infinity Cache cannot hold them between steps.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+
+METRIC = "GDN prefill tokens/s + decode state GB/s (fraction of MI355X roofline)"
+
+
+def algorithmic_counts(T, Hk, Hv, d, C, N, B):
+    """Algorithmic work per launch of each kernel (bytes moved once / flops of the
+    chunk form, lower triangles only; split-operand MFMA repeats are not counted)."""
+    conv_dim = 2 * Hk * d + Hv * d
+    prep_bytes = T * conv_dim * 2 + T * (2 * Hk * d + Hv * d) * 4 + conv_dim * 4 * 2 + N * 3 * conv_dim * 2
+    # chunk-local per token and value head: K K^T, Q K^T, W, U, P W, P U (each C*d) + diagonal solves
+    local_flops = T * Hv * (6 * C * d + C * C // 3)
+    # state pass per token and value head: W S, Qt S, K^T Delta (each 2 d d)
+    state_flops = T * Hv * 6 * d * d
+    dec_state = 2 * B * Hv * d * d * 4
+    dec_bytes = dec_state + B * conv_dim * 2 + 2 * B * 3 * conv_dim * 2 + B * Hv * d * 4 + 2 * B * Hv * 4 \
+        + conv_dim * 4 * 2
+    return prep_bytes, local_flops, state_flops, dec_bytes
+
+
+def cpu_baseline(wl):
+    """The fp64 oracle on the same prefill batch, on this host's cores."""
+    import numpy as np
+    import oracle
+    x = wl.x.float().numpy()
+    w = wl.conv_w.float().numpy()
+    cu = wl.cu_seqlens.numpy()
+    g = wl.g.numpy()
+    b = wl.beta.numpy()
+    oracle.lib()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        q, k, v, _ = oracle.prep(x, w, cu, wl.Hk, wl.Hv, wl.dk, wl.dv)
+        oracle.recurrence(q, k, v, g, b, cu)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": oracle.threads(1 << 30), "kind": "oracle",
+            "sample": f"full layer_4k prefill (conv+SiLU+L2 over T={wl.T}, then the fp64 token recurrence for all "
+                      f"{wl.Hv} heads), median of 3 runs, {t:.2f} s each; OpenMP over tokens (prep) and heads "
+                      f"(recurrence)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path is data-parallel per sequence and per head and this "
+              "build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hybrid_linear_attention_gated_amd as gdn
+    from hybrid_linear_attention_gated_amd import inputs
+
+    gdn.lib()   # fails loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = inputs.layer_4k()
+    dw = inputs.decode256()
+    T, Hk, Hv, d, N = wl.T, wl.Hk, wl.Hv, wl.dk, wl.N
+    B = dw.N
+    R = max(2, args.sets)
+
+    # prefill buffers (inputs rotated over R copies)
+    xs = [wl.x.to(dev) for _ in range(R)]
+    gs = [wl.g.to(dev) for _ in range(R)]
+    bs = [wl.beta.to(dev) for _ in range(R)]
+    cw = wl.conv_w.to(dev)
+    cu = wl.cu_seqlens.to(dev)
+    q = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((T, Hv, d), dtype=torch.float32, device=dev)
+    o = torch.empty((T, Hv, d), dtype=torch.float32, device=dev)
+    cso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty((N, Hv, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.workspace_size(T, N, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=dev)
+
+    # decode buffers: >= 2 state sets (>= 512 MiB) so no step finds its state in the Infinity Cache
+    Rd = 2
+    dstate = [dw.state.to(dev) for _ in range(Rd)]
+    dcs = [dw.conv_state.to(dev) for _ in range(Rd)]
+    dx = dw.x.to(dev)
+    dcw = dw.conv_w.to(dev)
+    dg = dw.g.to(dev)
+    db = dw.beta.to(dev)
+    do = torch.empty((B, Hv, d), dtype=torch.float32, device=dev)
+
+    names = ["prep", "chunk_local", "state_pass", "decode"]
+
+    def step(i, ev):
+        r = i % R
+        ev[0].record()
+        gdn.conv_qk_prep(xs[r], cw, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, q=q, k=k, v=v)
+        ev[1].record()
+        gdn.chunk_prefill_local(q, k, v, gs[r], bs[r], ws, cu_seqlens=cu)
+        ev[2].record()
+        gdn.chunk_prefill_state(ws, o, T, Hk, Hv, d, d, cu_seqlens=cu, final_state=fin)
+        ev[3].record()
+        gdn.decode_step(dx, dcw, dcs[i % Rd], dg, db, dstate[i % Rd], Hk, Hv, d, d, o=do)
+        ev[4].record()
+
+    def events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    for i in range(args.warmup):
+        step(i, events())
+    torch.cuda.synchronize()
+    evs = [events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: 0.0 for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n] += ev[j].elapsed_time(ev[j + 1])
+    per = {n: per[n] / args.steps for n in names}   # ms per launch
+
+    prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
+    prefill_ms = per["prep"] + per["chunk_local"] + per["state_pass"]
+    kern = {
+        "prep": {"bound": "hbm", "achieved": prep_b / per["prep"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+        "chunk_local": {"bound": "mfma", "achieved": local_f / per["chunk_local"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
+                        "unit": "TFLOP/s"},
+        "state_pass": {"bound": "mfma", "achieved": state_f / per["state_pass"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
+                       "unit": "TFLOP/s"},
+        "decode": {"bound": "hbm", "achieved": dec_b / per["decode"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+    }
+    for n in names:
+        kern[n]["ms"] = per[n]
+        kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
+    dominant = max(["prep", "chunk_local", "state_pass"], key=lambda n: per[n])
+    roof = dict(kern[dominant])
+    roof["kernel"] = dominant
+    roof["traffic"] = None
+    roof.pop("ms")
+
+    out = {
+        "metric": METRIC,
+        "value": T / (prefill_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x; fp16/bf16 MFMA with fp32 accumulation; fp32 state",
+        "data": "synthetic",
+        "config": {"workload": "layer_4k prefill (T=4096, Hk=Hv=16, dk=dv=128, chunk 64, bf16 x, fp32 q/k/v/o) "
+                               "+ decode256 step (B=256, fp32 state 256 MiB, 2 rotating state sets)",
+                   "T": T, "heads_k": Hk, "heads_v": Hv, "head_dim": d, "chunk": 64, "decode_batch": B},
+        "prefill": {"ms": prefill_ms, "tokens_per_s": T / (prefill_ms / 1e3),
+                    "algorithmic_tflops": (local_f + state_f) / prefill_ms / 1e9},
+        "decode": {"ms": per["decode"], "tokens_per_s": B / (per["decode"] / 1e3),
+                   "state_gb_per_s": dec_b / per["decode"] / 1e6, "frac_hbm": kern["decode"]["frac"],
+                   "bytes_per_step": dec_b},
+        "roofline": roof,
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,238 @@
+"""Gated DeltaNet token mixer for AMD MI355X (gfx950): Python binding of libgdn.so.
+
+The library (``libgdn.so``, built from ``csrc/`` by ``build.py``) exports the C ABI
+declared in ``include/gdn.h``.  This module only marshals arguments: it takes
+torch tensors that already live on the GPU, checks their dtype / shape /
+contiguity, allocates outputs and workspace with torch, and passes raw device
+pointers and the current HIP stream to the library.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+
+    q, k, v = conv_qk_prep(x, conv_w, Hk, Hv, dk, dv, cu_seqlens, conv_state_in, conv_state_out)
+    o, final_state = chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state)
+    o = decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["conv_qk_prep", "chunk_prefill", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
+           "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "LIB_PATH", "abi_version", "mfma_supported"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+GDN_F32, GDN_BF16 = 0, 1
+GDN_MATH_F32, GDN_MATH_MFMA = 0, 1
+_lib = None
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().gdn_status_string(status).decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgdn.so; raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hybrid_linear_attention_gated_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.gdn_conv_qk_prep.argtypes = [P, P, P, I, P, P, P, P, P, I, I, I, I, I, I, F, P]
+        L.gdn_conv_qk_prep.restype = I
+        L.gdn_chunk_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
+        L.gdn_chunk_prefill_workspace_size.restype = Z
+        L.gdn_chunk_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_chunk_prefill.restype = I
+        L.gdn_chunk_prefill_local.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, P, Z, P]
+        L.gdn_chunk_prefill_local.restype = I
+        L.gdn_chunk_prefill_state.argtypes = [P, I, P, P, P, I, I, I, I, I, P, Z, P]
+        L.gdn_chunk_prefill_state.restype = I
+        L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P]
+        L.gdn_decode_step.restype = I
+        L.gdn_status_string.argtypes = [I]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_abi_version.argtypes = []
+        L.gdn_abi_version.restype = I
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().gdn_abi_version()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported element dtype {t.dtype}")
+
+
+def _check(t, name, dtype=None, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _seqs(cu_seqlens, T):
+    if cu_seqlens is None:
+        return None, 1
+    _check(cu_seqlens, "cu_seqlens", torch.int32)
+    return cu_seqlens, cu_seqlens.numel() - 1
+
+
+def conv_qk_prep(x, conv_w, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None, conv_state_out=None,
+                 l2_eps=1e-6, q=None, k=None, v=None):
+    """Depthwise causal conv (kernel 4) + SiLU + split + L2(q, k).
+
+    x [T, conv_dim], conv_w [conv_dim, 4]; conv states [N, 3, conv_dim].
+    Returns fp32 q, k [T, Hk, dk] and v [T, Hv, dv].
+    """
+    dt = x.dtype
+    C = 2 * Hk * dk + Hv * dv
+    _check(x, "x", dt)
+    if x.dim() != 2 or x.shape[1] != C:
+        raise ValueError(f"x must be [T, {C}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    cu, N = _seqs(cu_seqlens, T)
+    _check(conv_w, "conv_w", dt, (C, 4))
+    _check(conv_state_in, "conv_state_in", dt, (N, 3, C), optional=True)
+    _check(conv_state_out, "conv_state_out", dt, (N, 3, C), optional=True)
+    f32 = torch.float32
+    q = torch.empty((T, Hk, dk), dtype=f32, device=x.device) if q is None else _check(q, "q", f32, (T, Hk, dk))
+    k = torch.empty((T, Hk, dk), dtype=f32, device=x.device) if k is None else _check(k, "k", f32, (T, Hk, dk))
+    v = torch.empty((T, Hv, dv), dtype=f32, device=x.device) if v is None else _check(v, "v", f32, (T, Hv, dv))
+    st = lib().gdn_conv_qk_prep(_p(x), _p(conv_w), _p(cu), N, _p(conv_state_in), _p(conv_state_out),
+                                _p(q), _p(k), _p(v), T, Hk, Hv, dk, dv, _dt(x), float(l2_eps), _stream())
+    if st != 0:
+        raise GdnError("gdn_conv_qk_prep", st)
+    return q, k, v
+
+
+def mfma_supported(dk, dv) -> bool:
+    return dk == dv and dk in (64, 128)
+
+
+def _math(math, dk, dv) -> int:
+    if math == "auto":
+        return GDN_MATH_MFMA if mfma_supported(dk, dv) else GDN_MATH_F32
+    return {"f32": GDN_MATH_F32, "mfma": GDN_MATH_MFMA}[math]
+
+
+def workspace_size(T, N, Hk, Hv, dk, dv, math="auto") -> int:
+    return int(lib().gdn_chunk_prefill_workspace_size(T, N, Hk, Hv, dk, dv, _math(math, dk, dv)))
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, final_state=None, scale=1.0,
+                  output_final_state=True, o=None, workspace=None, math="auto"):
+    """Gated delta rule over packed sequences.
+
+    q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv]; states [N, Hv, dk, dv]; all fp32.
+    math: "mfma" (chunked MFMA path), "f32" (fp32 token recurrence) or "auto"
+    (mfma where the head dims allow it).
+    Returns (o [T, Hv, dv] fp32, final_state or None).  final_state may be initial_state
+    (updated in place).
+    """
+    dt = torch.float32
+    _check(q, "q", dt)
+    T, Hk, dk = q.shape
+    _check(k, "k", dt, (T, Hk, dk))
+    _check(v, "v", dt)
+    if v.dim() != 3 or v.shape[0] != T:
+        raise ValueError("v must be [T, Hv, dv]")
+    Hv, dv = v.shape[1], v.shape[2]
+    _check(g, "g", torch.float32, (T, Hv))
+    _check(beta, "beta", torch.float32, (T, Hv))
+    cu, N = _seqs(cu_seqlens, T)
+    _check(initial_state, "initial_state", torch.float32, (N, Hv, dk, dv), optional=True)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device)
+    _check(final_state, "final_state", torch.float32, (N, Hv, dk, dv), optional=True)
+    o = torch.empty((T, Hv, dv), dtype=torch.float32, device=q.device) if o is None else \
+        _check(o, "o", torch.float32, (T, Hv, dv))
+    m = _math(math, dk, dv)
+    need = workspace_size(T, N, Hk, Hv, dk, dv, math)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().gdn_chunk_prefill(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, _p(initial_state),
+                                 _p(final_state), _p(o), float(scale), T, Hk, Hv, dk, dv, m,
+                                 _p(workspace), ws_bytes, _stream())
+    if st != 0:
+        raise GdnError("gdn_chunk_prefill", st)
+    return o, final_state
+
+
+def chunk_prefill_local(q, k, v, g, beta, workspace, cu_seqlens=None, scale=1.0):
+    """First phase of the MFMA chunked prefill: per-chunk quantities into `workspace`."""
+    T, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    cu, N = _seqs(cu_seqlens, T)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta")):
+        _check(t, n, torch.float32)
+    _check(workspace, "workspace")
+    st = lib().gdn_chunk_prefill_local(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, float(scale), T, Hk, Hv,
+                                       dk, dv, _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_chunk_prefill_local", st)
+
+
+def chunk_prefill_state(workspace, o, T, Hk, Hv, dk, dv, cu_seqlens=None, initial_state=None, final_state=None):
+    """Second phase of the MFMA chunked prefill: the state pass over chunks."""
+    cu, N = _seqs(cu_seqlens, T)
+    _check(o, "o", torch.float32, (T, Hv, dv))
+    _check(workspace, "workspace")
+    _check(initial_state, "initial_state", torch.float32, (N, Hv, dk, dv), optional=True)
+    _check(final_state, "final_state", torch.float32, (N, Hv, dk, dv), optional=True)
+    st = lib().gdn_chunk_prefill_state(_p(cu), N, _p(initial_state), _p(final_state), _p(o), T, Hk, Hv, dk, dv,
+                                       _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_chunk_prefill_state", st)
+
+
+def decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6, o=None):
+    """One decode token per row; conv_state [B, 3, conv_dim] and state [B, Hv, dk, dv]
+    are updated in place.  Returns o [B, Hv, dv] fp32."""
+    dt = x.dtype
+    C = 2 * Hk * dk + Hv * dv
+    _check(x, "x", dt)
+    if x.dim() != 2 or x.shape[1] != C:
+        raise ValueError(f"x must be [B, {C}]")
+    B = x.shape[0]
+    _check(conv_w, "conv_w", dt, (C, 4))
+    _check(conv_state, "conv_state", dt, (B, 3, C))
+    _check(g, "g", torch.float32, (B, Hv))
+    _check(beta, "beta", torch.float32, (B, Hv))
+    _check(state, "state", torch.float32, (B, Hv, dk, dv))
+    o = torch.empty((B, Hv, dv), dtype=torch.float32, device=x.device) if o is None else \
+        _check(o, "o", torch.float32, (B, Hv, dv))
+    st = lib().gdn_decode_step(_p(x), _p(conv_w), _p(conv_state), _p(g), _p(beta), _p(state), _p(o),
+                               float(scale), float(l2_eps), B, Hk, Hv, dk, dv, _dt(x), _stream())
+    if st != 0:
+        raise GdnError("gdn_decode_step", st)
+    return o

@@ -1,0 +1,575 @@
+// gdn_chunk.hip -- chunked (chunk 64, WY / UT form) prefill of the gated delta
+// rule on MFMA for gfx950, for packed varlen sequences with initial and final
+// states.
+//
+// Method.  The recurrence is the recurrent-mode GatedDeltaNet step of "Hugging
+// Face Transformers: Qwen3.5-MoE series explained", section 4.3; its prefill
+// is the chunk-mode call of section 8.2, which returns the outputs and the last
+// state.  The chunk form below follows from unrolling that recurrence over a
+// chunk of c <= 64 tokens (key-major state S[dk][dv], local cumulative
+// log-decay G_t = g_1 + ... + g_t, q already multiplied by `scale`):
+//
+//   A[t][i] = b_t e^{G_t - G_i} (k_t . k_i)  for i < t,   T = (I + A)^-1
+//   W = T diag(b e^G) K,     U = T diag(b) V,      Delta = U - W S
+//   P[t][i] = e^{G_t - G_i} (q_t . k_i)  for i <= t
+//   O = diag(e^G) Q S + P Delta = Qt S + Ol,   Qt = diag(e^G) Q - P W,  Ol = P U
+//   S' = e^{G_c} S + K^T diag(e^{G_c - G}) Delta
+//
+// It equals the token recurrence in exact arithmetic (the CPU tests check the
+// fp64 version of it against the token-by-token oracle).
+//
+// Precision.  Inputs q, k, v are fp32.  The outputs of this layer are heavy
+// tailed (the largest |o| is tens of times its RMS), so one bf16 rounding of
+// an operand costs up to ~2^-9 of the largest value, which is more than the
+// 2e-2 RMS-relative accuracy the layer is held to.  Products therefore use
+//  - in the chunk-local kernel: two-term bf16 splits (hi + lo) of both operands,
+//    three MFMAs per product (K K^T, Q K^T, the block solve, P W, P U);
+//  - in the state pass: fp16 MFMA (11-bit significand) with W, Qt and the state
+//    as single fp16 operands, and K and the decayed Delta as fp16 hi + lo pairs
+//    (three MFMAs for K^T Delta).
+//    fp16 operands assume |state|, |Delta| < 6.5e4; the fp32 master state is
+//    never rounded.
+//
+// Kernels.
+//  chunk_local_kernel: one 4-wave workgroup per (chunk, value head), fully
+//    parallel.  K K^T and Q K^T, the 16x16 diagonal blocks of T by forward
+//    substitution in fp32, W and U by block forward substitution on MFMA (no
+//    explicit T), then Qt and Ol.  Writes W, Qt, K^T as fp16 MFMA A-operand
+//    fragments and U, Ol as fp32 accumulator-layout tiles, so the state pass
+//    reads every operand with one coalesced 16-byte load per lane.
+//  state_pass_kernel: one wave per (sequence, value head, 16-column strip of
+//    the state); the strip's fp32 state lives in MFMA accumulators for the
+//    whole sequence and the chunk loop runs Delta = U - W S, O = Qt S + Ol,
+//    S = g S + K^T (decay * Delta) with every operand in registers.
+//    Accumulator tiles are reused as B operands directly: the k index of an
+//    MFMA may be permuted as long as A and B share the permutation, and the
+//    stored A fragments carry the permutation that matches two stacked
+//    accumulator tiles (kperm).
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// Byte offsets inside one (chunk, value head) workspace record.
+template <int D>
+struct Rec {
+    static constexpr int NKS = D / 32;                  // 32-wide k steps over the head dim
+    static constexpr int NTD = D / 16;                  // 16-wide tiles over the head dim
+    static constexpr int W_OFF = 0;                     // W   f16 A frags [4 row tiles][NKS][64 lanes][8]
+    static constexpr int Q_OFF = W_OFF + 64 * D * 2;    // Qt  f16 A frags [4][NKS][64][8]
+    static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // K^T f16 A frags, hi and lo: [2][NTD row tiles][2][64][8]
+    static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U   f32 tiles [NTD col tiles][4 row tiles][64][4]
+    static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
+    static constexpr int DC_OFF = O_OFF + 64 * D * 4;   // e^{G_c - G_t}, f32 [64]
+    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32
+    static constexpr int SIZE = (GM_OFF + 16 + 255) / 256 * 256;
+};
+
+// Wave-parallel: first chunk index of sequence s in the packed chunk list.
+__device__ __forceinline__ int chunk_base_wave(const int32_t *cu, int s) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int acc = 0;
+    if (cu) {
+        for (int i0 = 0; i0 < s; i0 += kWave) {
+            const int i = i0 + lane;
+            if (i < s) acc += n_chunks(cu[i + 1] - cu[i]);
+        }
+    }
+    for (int m = 1; m < kWave; m <<= 1) acc += __shfl_xor(acc, m, kWave);
+    return acc;
+}
+
+// Wave-parallel: which sequence holds packed chunk gc, and which chunk of it.
+// Returns false when gc is past the last chunk.
+__device__ __forceinline__ bool locate_chunk_wave(const int32_t *cu, int N, int Ttot, int gc, int &s_out,
+                                                  int &c_out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    if (!cu) {
+        s_out = 0; c_out = gc;
+        return gc < n_chunks(Ttot);
+    }
+    int base = 0;
+    for (int i0 = 0; i0 < N; i0 += kWave) {
+        const int i = i0 + lane;
+        const int n = i < N ? n_chunks(cu[i + 1] - cu[i]) : 0;
+        int incl = n;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += y;
+        }
+        const int excl = base + incl - n;
+        const unsigned long long hit = __ballot(i < N && n > 0 && gc >= excl && gc < excl + n);
+        if (hit) {
+            const int src = __ffsll((long long)hit) - 1;
+            s_out = i0 + src;
+            c_out = gc - __shfl(excl, src, kWave);
+            return true;
+        }
+        base += __shfl(incl, kWave - 1, kWave);
+    }
+    return false;
+}
+
+// ============================================================== chunk-local
+
+template <int D>
+__global__ __launch_bounds__(256) void chunk_local_kernel(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
+    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws) {
+    using R = Rec<D>;
+    constexpr int NKS = R::NKS, NTD = R::NTD;
+    constexpr int LD = D + 8;    // row stride (elements) of the 64 x D 16-bit LDS tiles
+    constexpr int LA = 64 + 4;   // fp32 row stride of A
+    constexpr int LP = 64 + 8;   // bf16 row stride of P
+    constexpr int TPW = NTD / 2; // accumulator column tiles per wave in the solve
+
+    __shared__ __attribute__((aligned(16))) bf16 Kh[64 * LD];
+    __shared__ __attribute__((aligned(16))) bf16 Kl[64 * LD];
+    __shared__ __attribute__((aligned(16))) bf16 Qh[64 * LD];   // later: W staging (f16)
+    __shared__ __attribute__((aligned(16))) bf16 Ql[64 * LD];   // later: Qt staging (f16)
+    __shared__ __attribute__((aligned(16))) float As[64 * LA];
+    __shared__ __attribute__((aligned(16))) bf16 Ph[64 * LP];
+    __shared__ __attribute__((aligned(16))) bf16 Pl[64 * LP];
+    __shared__ float Gs[64], Bs[64], Eg[64], Dc[64];
+    __shared__ float Td[4][16][17];
+    __shared__ int loc[3];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int gc = blockIdx.x, h = blockIdx.y;
+    const int kh = h / (Hv / Hk);
+
+    if (wave == 0) {
+        int s, c;
+        const bool ok = locate_chunk_wave(cu, N, Ttot, gc, s, c);
+        if (lane == 0) {
+            loc[0] = ok ? 1 : 0;
+            if (ok) {
+                loc[1] = seq_begin(cu, s) + c * kChunk;
+                loc[2] = min(kChunk, seq_end(cu, s, Ttot) - loc[1]);
+            }
+        }
+    }
+    __syncthreads();
+    if (!loc[0]) return;
+    const int t0 = loc[1], L = loc[2];
+    char *rec = ws + ((size_t)gc * Hv + h) * R::SIZE;
+
+    // ---- K and Q (key head kh) as bf16 hi/lo planes; rows >= L are zero
+    for (int e = tid; e < 64 * (D / 4); e += 256) {
+        const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (r < L) {
+            kv = *reinterpret_cast<const float4 *>(k + ((size_t)(t0 + r) * Hk + kh) * D + c4);
+            qv = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + r) * Hk + kh) * D + c4);
+        }
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+        bf16x4 khi, klo, qhi, qlo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            khi[i] = (bf16)kk[i]; klo[i] = (bf16)(kk[i] - (float)khi[i]);
+            qhi[i] = (bf16)qq[i]; qlo[i] = (bf16)(qq[i] - (float)qhi[i]);
+        }
+        *reinterpret_cast<bf16x4 *>(Kh + r * LD + c4) = khi;
+        *reinterpret_cast<bf16x4 *>(Kl + r * LD + c4) = klo;
+        *reinterpret_cast<bf16x4 *>(Qh + r * LD + c4) = qhi;
+        *reinterpret_cast<bf16x4 *>(Ql + r * LD + c4) = qlo;
+    }
+    if (wave == 0) {
+        float gg = 0.f, bb = 0.f;
+        if (lane < L) { gg = g[(size_t)(t0 + lane) * Hv + h]; bb = beta[(size_t)(t0 + lane) * Hv + h]; }
+        float G = gg;   // inclusive prefix sum over the chunk
+        for (int o = 1; o < 64; o <<= 1) {
+            const float y = __shfl_up(G, o, kWave);
+            if (lane >= o) G += y;
+        }
+        const float Gc = __shfl(G, 63, kWave);
+        Gs[lane] = G;
+        Bs[lane] = bb;
+        Eg[lane] = __expf(G);
+        Dc[lane] = __expf(Gc - G);
+        reinterpret_cast<float *>(rec + R::DC_OFF)[lane] = __expf(Gc - G);
+        if (lane == 0) *reinterpret_cast<float *>(rec + R::GM_OFF) = __expf(Gc);
+    }
+    __syncthreads();
+
+    // ---- K K^T and Q K^T, lower triangle by 16x16 tiles; wave w owns row tile w
+    {
+        const int r = wave;
+        const int row = 16 * r + l16;
+        for (int c = 0; c < 4; ++c) {
+            const int i = 16 * c + l16;
+            if (c <= r) {
+                f32x4 akk = zero4(), aqk = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off_a = row * LD + 32 * ks + 8 * kg, off_b = i * LD + 32 * ks + 8 * kg;
+                    const Split8 ka{*reinterpret_cast<const bf16x8 *>(Kh + off_a), *reinterpret_cast<const bf16x8 *>(Kl + off_a)};
+                    const Split8 qa{*reinterpret_cast<const bf16x8 *>(Qh + off_a), *reinterpret_cast<const bf16x8 *>(Ql + off_a)};
+                    const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off_b), *reinterpret_cast<const bf16x8 *>(Kl + off_b)};
+                    akk = mfma16x3(ka, kb, akk);
+                    aqk = mfma16x3(qa, kb, aqk);
+                }
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int t = 16 * r + 4 * kg + qq;
+                    const float dec = __expf(Gs[t] - Gs[min(i, t)]);
+                    As[t * LA + i] = (i < t) ? Bs[t] * dec * akk[qq] : 0.f;
+                    const float p = (i <= t) ? scale * dec * aqk[qq] : 0.f;
+                    const bf16 ph = (bf16)p;
+                    Ph[t * LP + i] = ph;
+                    Pl[t * LP + i] = (bf16)(p - (float)ph);
+                }
+            } else {
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int t = 16 * r + 4 * kg + qq;
+                    As[t * LA + i] = 0.f;
+                    Ph[t * LP + i] = (bf16)0.f;
+                    Pl[t * LP + i] = (bf16)0.f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution (fp32)
+    if (lane < 16) {
+        const int r = wave, j = lane;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float acc = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < t; ++i) acc = fmaf(-As[(16 * r + t) * LA + 16 * r + i], x[i], acc);
+            x[t] = acc;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Td[r][t][j] = x[t];
+    }
+    __syncthreads();
+
+    // ---- X = (I + A)^-1 [diag(b e^G) K | diag(b) V] by block forward substitution.
+    // Waves 0,1 own W column tiles, waves 2,3 own U column tiles (TPW each).
+    const bool isW = wave < 2;
+    const int tile0 = (wave & 1) * TPW;
+    f32x4 X[4][TPW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {
+            const int col = 16 * (tile0 + jj) + l16;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int t = 16 * r + 4 * kg + qq;
+                float val;
+                if (isW) val = Bs[t] * Eg[t] * ((float)Kh[t * LD + col] + (float)Kl[t * LD + col]);
+                else val = t < L ? Bs[t] * v[((size_t)(t0 + t) * Hv + h) * D + col] : 0.f;
+                acc[jj][qq] = val;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; 2 * ks < r; ++ks) {
+            float a[8];
+#pragma unroll
+            for (int vv = 0; vv < 8; ++vv) {
+                const int i = 32 * ks + kperm(kg, vv);
+                a[vv] = (i < 16 * r) ? -As[(16 * r + l16) * LA + i] : 0.f;
+            }
+            const Split8 as = split8(a);
+#pragma unroll
+            for (int jj = 0; jj < TPW; ++jj) {
+                const f32x4 hi = (2 * ks + 1 < r) ? X[2 * ks + 1][jj] : zero4();
+                acc[jj] = mfma16x3(as, split_tiles(X[2 * ks][jj], hi), acc[jj]);
+            }
+        }
+        float ta[8];
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) ta[vv] = vv < 4 ? Td[r][l16][4 * kg + vv] : 0.f;
+        const Split8 ts = split8(ta);
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) X[r][jj] = mfma16x3(ts, split_tiles(acc[jj], zero4()), zero4());
+    }
+
+    // ---- Qt = diag(e^G) scale Q - P W  (W waves),  Ol = P U  (U waves)
+    f32x4 Y[4][TPW];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int jj = 0; jj < TPW; ++jj) {
+            const int col = 16 * (tile0 + jj) + l16;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int t = 16 * r + 4 * kg + qq;
+                Y[r][jj][qq] = isW ? Eg[t] * scale * ((float)Qh[t * LD + col] + (float)Ql[t * LD + col]) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks <= r / 2; ++ks) {
+            Split8 pa;
+#pragma unroll
+            for (int vv = 0; vv < 8; ++vv) {
+                const int idx = (16 * r + l16) * LP + 32 * ks + kperm(kg, vv);
+                const bf16 ph = Ph[idx], pl = Pl[idx];
+                pa.hi[vv] = isW ? -ph : ph;
+                pa.lo[vv] = isW ? -pl : pl;
+            }
+#pragma unroll
+            for (int jj = 0; jj < TPW; ++jj)
+                Y[r][jj] = mfma16x3(pa, split_tiles(X[2 * ks][jj], X[2 * ks + 1][jj]), Y[r][jj]);
+        }
+    }
+
+    if (!isW) {
+        // U and Ol as fp32 accumulator-layout tiles: [col tile][row tile][lane][4]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int jj = 0; jj < TPW; ++jj) {
+                const int nt = tile0 + jj;
+                *reinterpret_cast<f32x4 *>(rec + R::U_OFF + (((nt * 4 + r) * 64 + lane) * 4) * 4) = X[r][jj];
+                *reinterpret_cast<f32x4 *>(rec + R::O_OFF + (((nt * 4 + r) * 64 + lane) * 4) * 4) = Y[r][jj];
+            }
+        }
+    }
+    __syncthreads();   // every wave is done reading Qh / Ql
+    f16 *Wl = reinterpret_cast<f16 *>(Qh);
+    f16 *Ql16 = reinterpret_cast<f16 *>(Ql);
+    if (isW) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int jj = 0; jj < TPW; ++jj) {
+                const int col = 16 * (tile0 + jj) + l16;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int t = 16 * r + 4 * kg + qq;
+                    Wl[t * LD + col] = (f16)X[r][jj][qq];
+                    Ql16[t * LD + col] = (f16)Y[r][jj][qq];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- fp16 A-operand fragments: W and Qt (k = head dim), K^T hi and lo (k = token)
+    constexpr int NF_W = 4 * NKS;
+    constexpr int NF_K = NTD * 2;
+    for (int f = wave; f < 2 * NF_W + NF_K; f += 4) {
+        f16x8 frag, frag_lo;
+        int off;
+        if (f < 2 * NF_W) {
+            const f16 *Sm = f < NF_W ? Wl : Ql16;
+            const int ff = f < NF_W ? f : f - NF_W;
+            const int mt = ff / NKS, ks = ff % NKS;
+            const f16 *p = Sm + (16 * mt + l16) * LD + 32 * ks + 4 * kg;
+            const f16x4 lo = *reinterpret_cast<const f16x4 *>(p);
+            const f16x4 hi = *reinterpret_cast<const f16x4 *>(p + 16);
+            frag[0] = lo[0]; frag[1] = lo[1]; frag[2] = lo[2]; frag[3] = lo[3];
+            frag[4] = hi[0]; frag[5] = hi[1]; frag[6] = hi[2]; frag[7] = hi[3];
+            off = (f < NF_W ? R::W_OFF : R::Q_OFF) + (ff * 64 + lane) * 16;
+        } else {
+            const int ff = f - 2 * NF_W;
+            const int mt = ff / 2, ks = ff % 2;
+            const int d = 16 * mt + l16;
+#pragma unroll
+            for (int vv = 0; vv < 8; ++vv) {
+                const int t = 32 * ks + kperm(kg, vv);
+                const float kv = (float)Kh[t * LD + d] + (float)Kl[t * LD + d];
+                frag[vv] = (f16)kv;
+                frag_lo[vv] = (f16)(kv - (float)frag[vv]);
+            }
+            off = R::K_OFF + (ff * 64 + lane) * 16;
+            *reinterpret_cast<f16x8 *>(rec + off + NF_K * 64 * 16) = frag_lo;
+        }
+        *reinterpret_cast<f16x8 *>(rec + off) = frag;
+    }
+}
+
+// ============================================================== state pass
+
+template <int D>
+__global__ __launch_bounds__(64) void state_pass_kernel(
+    const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
+    const float *s0, float *sf, float *__restrict__ o) {
+    using R = Rec<D>;
+    constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16;
+    // block -> (unit, strip) so that the NS strips of one unit land on the same XCD
+    const int b = blockIdx.x;
+    const int u = 8 * (b / (8 * NS)) + (b % 8);
+    const int j = (b / 8) % NS;
+    if (u >= units) return;
+    const int s = u / Hv, h = u % Hv;
+    const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
+    const int col = 16 * j + l16;
+    const int t0 = seq_begin(cu, s);
+    const int L = seq_end(cu, s, Ttot) - t0;
+    const int nc = n_chunks(L);
+    const int gbase = chunk_base_wave(cu, s);
+
+    f32x4 S[NTD];
+    const size_t st_off = ((size_t)s * Hv + h) * D * D;
+#pragma unroll
+    for (int m = 0; m < NTD; ++m)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            S[m][qq] = s0 ? s0[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] : 0.f;
+
+    if (nc > 0) {
+        f16x8 Wf[4][NKS], Qf[4][NKS], Kf[NTD][2], Kfl[NTD][2];
+        f32x4 Uf[4], Of[4], Dcf[4];
+        float gm;
+        auto rec_of = [&](int c) { return ws + ((size_t)(gbase + c) * Hv + h) * R::SIZE; };
+        auto load_W = [&](const char *rec) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    Wf[mt][ks] = *reinterpret_cast<const f16x8 *>(rec + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                Uf[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+            }
+        };
+        auto load_Q = [&](const char *rec) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    Qf[mt][ks] = *reinterpret_cast<const f16x8 *>(rec + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                Of[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+            }
+        };
+        auto load_K = [&](const char *rec) {
+#pragma unroll
+            for (int m = 0; m < NTD; ++m)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    Kf[m][ks] = *reinterpret_cast<const f16x8 *>(rec + R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16);
+                    Kfl[m][ks] = *reinterpret_cast<const f16x8 *>(rec + R::K_OFF + (((NTD + m) * 2 + ks) * 64 + lane) * 16);
+                }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                Dcf[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
+            gm = *reinterpret_cast<const float *>(rec + R::GM_OFF);
+        };
+        load_W(rec_of(0));
+        load_Q(rec_of(0));
+        load_K(rec_of(0));
+
+        for (int c = 0; c < nc; ++c) {
+            const char *recn = rec_of(min(c + 1, nc - 1));   // next chunk (re-loads the last one at the end)
+            f16x8 Sh[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
+
+            // Delta = U - W S
+            f32x4 Dl[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) acc = mfma16(Wf[mt][ks], Sh[ks], acc);
+                Dl[mt] = Uf[mt] - acc;
+            }
+            load_W(recn);
+
+            // O = Qt S + Ol
+            f32x4 Ot[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc = Of[mt];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) acc = mfma16(Qf[mt][ks], Sh[ks], acc);
+                Ot[mt] = acc;
+            }
+            load_Q(recn);
+
+            // S = gamma S + K^T (decay * Delta), decayed Delta as an fp16 hi + lo pair
+            f16x8 Dh[2], Dlo[2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 d0 = Dl[2 * ks] * Dcf[2 * ks], d1 = Dl[2 * ks + 1] * Dcf[2 * ks + 1];
+                Dh[ks] = pack_h(d0, d1);
+                f32x4 r0, r1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    r0[e] = d0[e] - (float)Dh[ks][e];
+                    r1[e] = d1[e] - (float)Dh[ks][4 + e];
+                }
+                Dlo[ks] = pack_h(r0, r1);
+            }
+#pragma unroll
+            for (int m = 0; m < NTD; ++m) {
+                f32x4 acc = S[m] * gm;
+                acc = mfma16(Kfl[m][0], Dh[0], acc);
+                acc = mfma16(Kfl[m][1], Dh[1], acc);
+                acc = mfma16(Kf[m][0], Dlo[0], acc);
+                acc = mfma16(Kf[m][1], Dlo[1], acc);
+                acc = mfma16(Kf[m][0], Dh[0], acc);
+                S[m] = mfma16(Kf[m][1], Dh[1], acc);
+            }
+            load_K(recn);
+
+            // store this chunk's outputs
+            const int tb = t0 + c * kChunk;
+            const int rows = min(kChunk, L - c * kChunk);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int r = 16 * mt + 4 * kg + qq;
+                    if (r < rows) o[((size_t)(tb + r) * Hv + h) * D + col] = Ot[mt][qq];
+                }
+        }
+    }
+    if (sf) {
+#pragma unroll
+        for (int m = 0; m < NTD; ++m)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) sf[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = S[m][qq];
+    }
+}
+
+// ============================================================== host side
+
+bool chunked_supported(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
+
+static size_t max_chunks(int T, int N) { return (size_t)(T / kChunk) + (size_t)N; }
+
+size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
+    (void)dv;
+    const size_t rec = dk == 64 ? (size_t)Rec<64>::SIZE : (size_t)Rec<128>::SIZE;
+    return max_chunks(T, N) * (size_t)Hv * rec;
+}
+
+template <int D>
+static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int phases) {
+    const size_t nc = max_chunks(a.T, a.N);
+    char *ws = (char *)a.ws;
+    if ((phases & 1) && nc > 0 && a.T > 0) {
+        hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)nc, a.Hv), dim3(256), 0, st, a.q, a.k, a.v,
+                           a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (phases & 2) {
+        const int units = a.N * a.Hv;
+        constexpr int NS = D / 16;
+        const int blocks = 8 * NS * ((units + 7) / 8);
+        hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(64), 0, st, (const char *)ws, a.cu, a.T,
+                           a.Hv, units, a.s0, a.sf, a.o);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases) {
+    switch (a.dk) {
+        case 64: return launch_chunked_t<64>(a, st, phases);
+        case 128: return launch_chunked_t<128>(a, st, phases);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,203 @@
+// gdn_decode.hip -- one decode step of the Gated DeltaNet mixer for B sequences:
+// conv-cache advance + conv + SiLU + L2(q, k) + one step of the gated delta rule
+// on the fp32 state, in place.
+//
+// Method: the decode branch of "Hugging Face Transformers: Qwen3.5-MoE series
+// explained", section 8.2 (conv-cache update, then the recurrent rule, then
+// both caches written back) with the recurrent-mode step of section 4.3:
+// S <- a S; m = S^T k; delta = b (v - m); S <- S + k delta^T; o = S^T q.
+//
+// Design (HBM-bound, ~0.84 flop per byte): one 256-thread workgroup per
+// (sequence, key head) owns the conv channels of that key head and of all value
+// heads that read it, so the in-place conv-cache shift has a single writer per
+// channel.  For each value head the dk x dv fp32 state is streamed once: thread
+// (row group, column quad) keeps its rows as float4 registers, so a wave reads
+// and writes whole 512-byte rows.  Since S' = a S + k delta^T, both reductions
+// needed (S^T k and S^T q, over dk) are taken from the OLD state in the same
+// pass:  m = a (S^T k),  o = a (S^T q) + delta (k . q).  Row-group partial sums
+// are combined with xor shuffles inside a wave and through LDS across waves.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+constexpr int kDecThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ float conv_step(const T *__restrict__ x, const T *__restrict__ w, T *cs,
+                                           int b, int c, int conv_dim) {
+    // window = [slot0, slot1, slot2, x]; afterwards the cache is [slot1, slot2, x]
+    T *cb = cs + (size_t)b * kConvHist * conv_dim + c;
+    const float s0 = to_f32(cb[0]);
+    const float s1 = to_f32(cb[(size_t)conv_dim]);
+    const T s2raw = cb[2 * (size_t)conv_dim];
+    const T xraw = x[(size_t)b * conv_dim + c];
+    const float s2 = to_f32(s2raw), xn = to_f32(xraw);
+    const T *wc = w + (size_t)c * kConvK;
+    float acc = to_f32(wc[0]) * s0;
+    acc = fmaf(to_f32(wc[1]), s1, acc);
+    acc = fmaf(to_f32(wc[2]), s2, acc);
+    acc = fmaf(to_f32(wc[3]), xn, acc);
+    cb[0] = cb[(size_t)conv_dim];
+    cb[(size_t)conv_dim] = s2raw;
+    cb[2 * (size_t)conv_dim] = xraw;
+    return silu(acc);
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+    const T *__restrict__ x, const T *__restrict__ w, T *cs, const float *__restrict__ g,
+    const float *__restrict__ beta, float *state, float *__restrict__ o, float scale, float eps,
+    int Hk, int Hv) {
+    constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
+    constexpr int RG = kDecThreads / TPR;        // row groups
+    constexpr int RPT = DK >= RG ? DK / RG : 1;  // rows per thread
+    constexpr int NW = kDecThreads / kWave;
+    static_assert(TPR <= kWave, "row must fit in a wave");
+
+    __shared__ float qk_s[2 * DK];   // raw SiLU(conv) of q then k
+    __shared__ float v_s[DV];
+    __shared__ float red[NW][2][DV];
+    __shared__ float scal[3];
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int b = blockIdx.x / Hk, kh = blockIdx.x % Hk;
+    const int group = Hv / Hk;
+    const int conv_dim = 2 * Hk * DK + Hv * DV;
+    const int cg = tid % TPR, rg = tid / TPR;
+    const bool row_active = rg < DK;
+
+    // first value head's state: issue the loads before the conv work
+    float4 S[RPT];
+    auto load_state = [&](int h) {
+        const float *sp = state + ((size_t)b * Hv + h) * DK * DV + 4 * cg;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + RG * r;
+            S[r] = row_active ? *reinterpret_cast<const float4 *>(sp + (size_t)i * DV) : make_float4(0, 0, 0, 0);
+        }
+    };
+    load_state(kh * group);
+
+    // q and k channels of this key head
+    for (int ch = tid; ch < 2 * DK; ch += kDecThreads) {
+        const int c = ch < DK ? kh * DK + ch : Hk * DK + kh * DK + (ch - DK);
+        qk_s[ch] = conv_step(x, w, cs, b, c, conv_dim);
+    }
+    __syncthreads();
+    if (wave < 3) {
+        float acc = 0.f;
+        for (int i = lane; i < DK; i += kWave) {
+            const float qi = qk_s[i], ki = qk_s[DK + i];
+            acc += wave == 0 ? qi * qi : (wave == 1 ? ki * ki : qi * ki);
+        }
+        acc = group_sum<kWave>(acc);
+        if (lane == 0) scal[wave] = acc;
+    }
+    __syncthreads();
+    const float rq = rsqrtf(scal[0] + eps) * scale;  // q_hat * scale
+    const float rk = rsqrtf(scal[1] + eps);
+    const float kq = scal[2] * rq * rk;                // k_hat . (scale q_hat)
+
+    float kr[RPT], qr[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int i = rg + RG * r;
+        kr[r] = row_active ? qk_s[DK + i] * rk : 0.f;
+        qr[r] = row_active ? qk_s[i] * rq : 0.f;
+    }
+
+    for (int gi = 0; gi < group; ++gi) {
+        const int h = kh * group + gi;
+        if (gi > 0) load_state(h);
+        for (int ch = tid; ch < DV; ch += kDecThreads)
+            v_s[ch] = conv_step(x, w, cs, b, 2 * Hk * DK + h * DV + ch, conv_dim);
+
+        float pm[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            pm[0] = fmaf(S[r].x, kr[r], pm[0]); pm[1] = fmaf(S[r].y, kr[r], pm[1]);
+            pm[2] = fmaf(S[r].z, kr[r], pm[2]); pm[3] = fmaf(S[r].w, kr[r], pm[3]);
+            pq[0] = fmaf(S[r].x, qr[r], pq[0]); pq[1] = fmaf(S[r].y, qr[r], pq[1]);
+            pq[2] = fmaf(S[r].z, qr[r], pq[2]); pq[3] = fmaf(S[r].w, qr[r], pq[3]);
+        }
+#pragma unroll
+        for (int m = TPR; m < kWave; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pm[e] += __shfl_xor(pm[e], m, kWave);
+                pq[e] += __shfl_xor(pq[e], m, kWave);
+            }
+        }
+        if (lane < TPR) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { red[wave][0][4 * cg + e] = pm[e]; red[wave][1][4 * cg + e] = pq[e]; }
+        }
+        __syncthreads();   // red and v_s complete
+        const float a = __expf(g[(size_t)b * Hv + h]);
+        const float bt = beta[(size_t)b * Hv + h];
+        float delta[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) { sk += red[ww][0][4 * cg + e]; sq += red[ww][1][4 * cg + e]; }
+            delta[e] = bt * (v_s[4 * cg + e] - a * sk);
+            pq[e] = a * sq + delta[e] * kq;   // output column 4cg+e
+        }
+        if (rg == 0) {
+            *reinterpret_cast<float4 *>(o + ((size_t)b * Hv + h) * DV + 4 * cg) = make_float4(pq[0], pq[1], pq[2], pq[3]);
+        }
+        if (row_active) {
+            float *sp = state + ((size_t)b * Hv + h) * DK * DV + 4 * cg;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) {
+                const int i = rg + RG * r;
+                float4 n;
+                n.x = fmaf(a, S[r].x, kr[r] * delta[0]);
+                n.y = fmaf(a, S[r].y, kr[r] * delta[1]);
+                n.z = fmaf(a, S[r].z, kr[r] * delta[2]);
+                n.w = fmaf(a, S[r].w, kr[r] * delta[3]);
+                *reinterpret_cast<float4 *>(sp + (size_t)i * DV) = n;
+            }
+        }
+        __syncthreads();   // red / v_s reused by the next value head
+    }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
+    if (a.B == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
+                       (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, a.o,
+                       a.scale, a.eps, a.Hk, a.Hv);
+    return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t launch_decode_dv(const DecodeArgs &a, hipStream_t st) {
+    switch (a.dv) {
+        case 16: return launch_decode_t<T, DK, 16>(a, st);
+        case 32: return launch_decode_t<T, DK, 32>(a, st);
+        case 64: return launch_decode_t<T, DK, 64>(a, st);
+        case 128: return launch_decode_t<T, DK, 128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+static hipError_t launch_decode_dk(const DecodeArgs &a, hipStream_t st) {
+    switch (a.dk) {
+        case 16: return launch_decode_dv<T, 16>(a, st);
+        case 32: return launch_decode_dv<T, 32>(a, st);
+        case 64: return launch_decode_dv<T, 64>(a, st);
+        case 128: return launch_decode_dv<T, 128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
+    return a.bf16 ? launch_decode_dk<bf16>(a, st) : launch_decode_dk<float>(a, st);
+}
+
+}  // namespace gdn

@@ -1,0 +1,160 @@
+// gdn_device.hpp -- device-side helpers shared by the gfx950 kernels:
+// element conversion, wavefront reductions, MFMA fragment types and the
+// sequence/chunk bookkeeping for packed varlen batches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kConvK = 4;          // conv kernel width
+constexpr int kConvHist = kConvK - 1;
+constexpr int kChunk = 64;         // chunk length of the chunked prefill
+
+// ---------------------------------------------------------------- element I/O
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// gfx950 converts with round-to-nearest-even (v_cvt_pk_bf16_f32)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Load / store 8 consecutive elements as fp32.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void load(const bf16 *p, float *out) {
+        bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+    }
+    static __device__ __forceinline__ void store(bf16 *p, const float *in) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (bf16)in[i];
+        *reinterpret_cast<bf16x8 *>(p) = v;
+    }
+};
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float *p, float *out) {
+        float4 a = *reinterpret_cast<const float4 *>(p);
+        float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float *in) {
+        *reinterpret_cast<float4 *>(p) = make_float4(in[0], in[1], in[2], in[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(in[4], in[5], in[6], in[7]);
+    }
+};
+
+__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+
+// ---------------------------------------------------------------- reductions
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------- varlen bookkeeping
+
+__device__ __forceinline__ int seq_begin(const int32_t *cu, int s) { return cu ? cu[s] : 0; }
+__device__ __forceinline__ int seq_end(const int32_t *cu, int s, int T) { return cu ? cu[s + 1] : T; }
+
+// Sequence index containing token t (largest s with cu[s] <= t); cu[N] = T.
+__device__ __forceinline__ int find_seq(const int32_t *cu, int N, int t) {
+    if (!cu) return 0;
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int n_chunks(int len) { return (len + kChunk - 1) / kChunk; }
+
+// Index of the first chunk of sequence s in the packed chunk list (chunks
+// restart at every sequence start).  O(s) scan; N is small on this path.
+__device__ __forceinline__ int chunk_base(const int32_t *cu, int s) {
+    if (!cu) return 0;
+    int base = 0;
+    for (int i = 0; i < s; ++i) base += n_chunks(cu[i + 1] - cu[i]);
+    return base;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D += A * B with A 16x32, B 32x16 (bf16), D 16x16 (fp32).  Lane l holds
+// A[l%16][k(l/16, v)], B[k(l/16, v)][l%16] for v < 8 and D[4*(l/16)+r][l%16].
+// Any bijection k(kg, v) onto 0..31 that A and B share gives the same product.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two-term bf16 representation of an fp32 value: hi = bf16(x), lo = bf16(x - hi)
+// (about 16 significant bits together).  A product of two split operands is
+// taken as hi*hi + hi*lo + lo*hi on bf16 MFMA.
+struct Split8 {
+    bf16x8 hi, lo;
+};
+__device__ __forceinline__ Split8 split8(const float *x) {
+    Split8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const bf16 h = (bf16)x[i];
+        r.hi[i] = h;
+        r.lo[i] = (bf16)(x[i] - (float)h);
+    }
+    return r;
+}
+__device__ __forceinline__ f32x4 mfma16x3(const Split8 &a, const Split8 &b, f32x4 c) {
+    c = mfma16(a.lo, b.hi, c);
+    c = mfma16(a.hi, b.lo, c);
+    return mfma16(a.hi, b.hi, c);
+}
+
+// The k order used when a B operand is built from two fp32 D tiles held in
+// registers (rows 0-15 in tile 0, rows 16-31 in tile 1): lane group kg holds
+// k = 4kg..4kg+3 (tile 0) and 16+4kg..16+4kg+3 (tile 1).  Every A operand that
+// meets such a B uses the same order.
+__device__ __forceinline__ int kperm(int kg, int v) { return (v < 4) ? (4 * kg + v) : (16 + 4 * kg + (v - 4)); }
+
+// Gather the 8 B-operand values of two stacked accumulator tiles (see kperm).
+__device__ __forceinline__ void gather8(f32x4 t0, f32x4 t1, float *x) {
+    x[0] = t0[0]; x[1] = t0[1]; x[2] = t0[2]; x[3] = t0[3];
+    x[4] = t1[0]; x[5] = t1[1]; x[6] = t1[2]; x[7] = t1[3];
+}
+__device__ __forceinline__ f16x8 pack_h(f32x4 t0, f32x4 t1) {
+    f16x8 r;
+    r[0] = (f16)t0[0]; r[1] = (f16)t0[1]; r[2] = (f16)t0[2]; r[3] = (f16)t0[3];
+    r[4] = (f16)t1[0]; r[5] = (f16)t1[1]; r[6] = (f16)t1[2]; r[7] = (f16)t1[3];
+    return r;
+}
+__device__ __forceinline__ Split8 split_tiles(f32x4 t0, f32x4 t1) {
+    float x[8];
+    gather8(t0, t1, x);
+    return split8(x);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+}  // namespace gdn

@@ -1,0 +1,61 @@
+// gdn_launch.hpp -- host-side launch entry points of the kernels (one per
+// translation unit).  Arguments are validated by gdn_api.cpp before any of
+// these is called; each returns the first HIP error it meets.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct PrepArgs {
+    const void *x, *w;
+    const int32_t *cu;
+    int N;
+    const void *cs_in;
+    void *cs_out;
+    float *q, *k, *v;
+    int T, Hk, Hv, dk, dv;
+    bool bf16;   // element type of x / conv_w / conv states
+    float eps;
+};
+
+struct PrefillArgs {
+    const float *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu;
+    int N;
+    const float *s0;
+    float *sf;
+    float *o;
+    float scale;
+    int T, Hk, Hv, dk, dv;
+    void *ws;
+    size_t ws_bytes;
+};
+
+struct DecodeArgs {
+    const void *x, *w;
+    void *cs;
+    const float *g, *beta;
+    float *state;
+    float *o;
+    float scale, eps;
+    int B, Hk, Hv, dk, dv;
+    bool bf16;
+};
+
+hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+
+// token-recurrent fp32 path (GDN_F32 and the small head dims)
+hipError_t launch_prefill_recurrent(const PrefillArgs &a, hipStream_t st);
+
+// chunked MFMA path (dk = dv in {64, 128})
+bool chunked_supported(int dk, int dv);
+size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv);
+// phases: bit 0 = chunk-local kernel, bit 1 = state-pass kernel
+hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases);
+
+}  // namespace gdn

@@ -88,7 +88,7 @@ class Workload:
     Hv: int
     dk: int
     dv: int
-    dtype: str                      # "bf16" or "f32": element type of x / q / k / v / o
+    dtype: str                      # "bf16" or "f32": element type of x / conv weights / conv caches
     cu_seqlens: torch.Tensor        # int32 [N+1]
     g: torch.Tensor                 # fp32 [T, Hv] (decode: [B, Hv])
     beta: torch.Tensor              # fp32 [T, Hv]
@@ -186,9 +186,8 @@ def long_64k() -> Workload:
 
 
 def core_workload(name: str, index: int, lengths, Hk: int, Hv: int, dk: int, dv: int,
-                  dtype: str = "bf16", random_states: bool = False, decay: str = "softplus",
-                  scale: float = 1.0) -> Workload:
-    """Core-only inputs (already-normalised q, k; v ~ N(0,1)) for the chunked prefill."""
+                  random_states: bool = False, decay: str = "softplus", scale: float = 1.0) -> Workload:
+    """Core-only fp32 inputs (unit-norm q, k; v ~ N(0,1)) for the chunked prefill."""
     rng = _rng(index)
     lengths = [int(x) for x in lengths]
     T = int(sum(lengths))
@@ -203,9 +202,8 @@ def core_workload(name: str, index: int, lengths, Hk: int, Hv: int, dk: int, dv:
         g = _log_uniform_decay(rng, (T, Hv), 0.99, 1.0)
     else:
         g = _log_uniform_decay(rng, (T, Hv))
-    conv = _bf16 if dtype == "bf16" else _f32
-    wl = Workload(name, T, N, Hk, Hv, dk, dv, dtype, _cu(lengths), _f32(g), _f32(beta),
-                  q=conv(q), k=conv(k), v=conv(v), scale=scale)
+    wl = Workload(name, T, N, Hk, Hv, dk, dv, "f32", _cu(lengths), _f32(g), _f32(beta),
+                  q=_f32(q), k=_f32(k), v=_f32(v), scale=scale)
     if random_states:
         wl.state = _f32(_normal_f32(rng, (N, Hv, dk, dv), std=0.1))
     return wl

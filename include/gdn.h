@@ -1,0 +1,187 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet token-mixer library for AMD MI355X (gfx950).
+ *
+ * The library computes the linear-attention core of a hybrid model's
+ * "linear_attention" layers: a depthwise causal conv1d (kernel 4) + SiLU over
+ * the mixed q|k|v projection, L2 normalisation of q and k, and the gated delta
+ * rule over a fixed-size per-head state,
+ *
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = S_t q_t,
+ *
+ * computed step by step (decay, retrieve, correct, write, read) as in the
+ * recurrent-mode GatedDeltaNet formula of "Hugging Face Transformers:
+ * Qwen3.5-MoE series explained", section 4.3, and in "7.6 Qwen3.5: the
+ * linear-attention hybrid" (LLM full-stack book), section 7.6.2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named as tensors are DEVICE pointers on the current HIP device,
+ *    row-major and contiguous.  The caller owns every buffer; the library keeps
+ *    no pointer after a call returns and allocates no device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ *    work is enqueued asynchronously on it; buffers must stay valid until the
+ *    stream work completes.
+ *  - Element type `dtype` (gdn_conv_qk_prep, gdn_decode_step) is the type of the
+ *    pre-conv input x, the conv weights and the conv caches: GDN_BF16 or GDN_F32.
+ *    Everything computed is fp32: q, k, v, o, g, beta and the recurrent states.
+ *    (The outputs of this layer are heavy tailed -- the largest |o| is tens of
+ *    times its RMS -- so a 16-bit q / k / v / o tensor alone would cost more than
+ *    the 2e-2 RMS-relative accuracy the layer is held to.)
+ *  - g is the log of the decay gate (a = exp(g), g <= 0); beta is the update gate.
+ *  - Heads: Hk key heads, Hv value heads, Hv % Hk == 0; value head h reads key
+ *    head h / (Hv / Hk).  conv_dim = 2*Hk*dk + Hv*dv with channel order q | k | v.
+ *  - The recurrent state is key-major: state[n][h][i][j], i < dk, j < dv, i.e.
+ *    the transpose of S_t above; outputs are identical.
+ *  - cu_seqlens (int32, N+1 entries, cu[0] = 0, non-decreasing, cu[N] = T) packs
+ *    N variable-length sequences along T.  NULL means one sequence of length T
+ *    (N must then be 1).  Zero-length sequences are allowed.  These device values
+ *    are a precondition and are not validated.
+ *  - Tensor pointers may be NULL when the tensor is empty (T = 0, or B = 0).
+ *  - Return value: GDN_OK or a gdn_status code.  Argument errors are detected on
+ *    the host before anything is enqueued; nothing is written then.  Launch
+ *    failures map to GDN_ERR_HIP.  No function aborts or throws.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                         */
+    GDN_ERR_BAD_SHAPE = 2,      /* negative size, Hv % Hk != 0, N inconsistent, ...     */
+    GDN_ERR_UNSUPPORTED = 3,    /* head dim / dtype combination not implemented         */
+    GDN_ERR_WORKSPACE = 4,      /* workspace NULL or smaller than the queried size      */
+    GDN_ERR_HIP = 5,            /* a HIP launch or runtime call failed                  */
+    GDN_ERR_ALIAS = 6           /* an output overlaps an input it must not overlap      */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* Arithmetic of gdn_chunk_prefill.
+ *  GDN_MATH_F32 : token-by-token recurrence in fp32 (any dk, dv in {16, 32, 64, 128}).
+ *  GDN_MATH_MFMA: chunked WY / UT form (chunk 64) on 16-bit MFMA with split
+ *                 operands where the accuracy needs them (dk = dv in {64, 128});
+ *                 about 1e-3 RMS-relative on the 0.8B layer shape. */
+typedef enum { GDN_MATH_F32 = 0, GDN_MATH_MFMA = 1 } gdn_math;
+
+/*
+ * gdn_conv_qk_prep -- depthwise causal conv1d (kernel 4, no bias) + SiLU + split
+ * + per-head L2 normalisation of q and k.
+ * Source: "7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2 (conv over
+ * conv_dim = 2*key_dim + value_dim channels, one filter per channel, left
+ * context only; q and k L2-normalised before the recurrence); conv cache per
+ * "Hugging Face Transformers: Qwen3.5-MoE series explained", section 8.2.
+ *
+ *   x              [T][conv_dim]        pre-conv mixed q|k|v
+ *   conv_w         [conv_dim][4]        tap 3 multiplies the current token
+ *   cu_seqlens     [N+1] or NULL
+ *   conv_state_in  [N][3][conv_dim] or NULL (zero history); slot 0 is the oldest
+ *   conv_state_out [N][3][conv_dim] or NULL; receives the last three inputs of
+ *                  each sequence (reaching into conv_state_in for sequences
+ *                  shorter than three).  May alias conv_state_in exactly.
+ *   q, k           [T][Hk][dk] fp32     q / sqrt(|q|^2 + l2_eps), same for k
+ *   v              [T][Hv][dv] fp32     SiLU(conv) of the value channels
+ * y[t][c] = sum_j conv_w[c][j] * x[t-3+j][c] with history from conv_state_in,
+ * never crossing a sequence boundary.  dk, dv must be multiples of 8 and <= 256.
+ */
+int gdn_conv_qk_prep(const void *x, const void *conv_w,
+                     const int32_t *cu_seqlens, int N,
+                     const void *conv_state_in, void *conv_state_out,
+                     float *q, float *k, float *v,
+                     int T, int Hk, int Hv, int dk, int dv, int dtype,
+                     float l2_eps, void *stream);
+
+/*
+ * Workspace bytes gdn_chunk_prefill needs for these sizes and `math` (0 when
+ * none is needed).  Upper bound valid for any cu_seqlens with the given T and N.
+ */
+size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv, int math);
+
+/*
+ * gdn_chunk_prefill -- gated delta rule over packed sequences, returning the
+ * per-token outputs and the final state of each sequence (the chunk-mode call
+ * of the prefill path in "Hugging Face Transformers: Qwen3.5-MoE series
+ * explained", section 8.2, which returns the output and the last recurrent state).
+ *
+ *   q, k           [T][Hk][dk] fp32 (L2-normalised by the caller or by gdn_conv_qk_prep)
+ *   v              [T][Hv][dv] fp32
+ *   g, beta        [T][Hv] fp32
+ *   cu_seqlens     [N+1] or NULL
+ *   initial_state  [N][Hv][dk][dv] fp32 or NULL (zero state)
+ *   final_state    [N][Hv][dk][dv] fp32 or NULL; may alias initial_state exactly
+ *   o              [T][Hv][dv]   fp32; o_t = S_t (scale * q_t); must not overlap any input
+ *   workspace      device scratch of at least gdn_chunk_prefill_workspace_size()
+ *                  bytes (may be NULL when that size is 0); contents are scratch.
+ *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
+ */
+int gdn_chunk_prefill(const float *q, const float *k, const float *v,
+                      const float *g, const float *beta,
+                      const int32_t *cu_seqlens, int N,
+                      const float *initial_state, float *final_state,
+                      float *o, float scale,
+                      int T, int Hk, int Hv, int dk, int dv, int math,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The two phases of gdn_chunk_prefill with GDN_MATH_MFMA, for callers that
+ * schedule them separately (for example to overlap the parallel chunk-local
+ * phase of one layer with other work).  gdn_chunk_prefill_local computes the
+ * per-chunk quantities of the chunk form (W, U, the decay-weighted query, the
+ * intra-chunk outputs) into `workspace`; gdn_chunk_prefill_state then runs the
+ * sequential pass over chunks that carries the state, writes o and the final
+ * state.  Arguments mean what they mean for gdn_chunk_prefill; the workspace
+ * must not be modified between the two calls, and cu_seqlens, N, T and the head
+ * sizes must be the same in both.  Running local then state equals one
+ * gdn_chunk_prefill call with GDN_MATH_MFMA.
+ */
+int gdn_chunk_prefill_local(const float *q, const float *k, const float *v,
+                            const float *g, const float *beta,
+                            const int32_t *cu_seqlens, int N, float scale,
+                            int T, int Hk, int Hv, int dk, int dv,
+                            void *workspace, size_t workspace_bytes, void *stream);
+int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N,
+                            const float *initial_state, float *final_state, float *o,
+                            int T, int Hk, int Hv, int dk, int dv,
+                            const void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_decode_step -- one token for each of B sequences: advance the conv cache by
+ * one input, conv + SiLU + L2 on the window, one step of the recurrence on the
+ * state, in place (the decode branch of "Hugging Face Transformers: Qwen3.5-MoE
+ * series explained", section 8.2: conv-cache update followed by the recurrent
+ * rule, both caches written back).
+ *
+ *   x           [B][conv_dim]       the new token's pre-conv mixed q|k|v
+ *   conv_w      [conv_dim][4]
+ *   conv_state  [B][3][conv_dim]    in/out: window = [slot0, slot1, slot2, x];
+ *                                   afterwards [slot1, slot2, x]
+ *   g, beta     [B][Hv] fp32
+ *   state       [B][Hv][dk][dv]     fp32, in/out
+ *   o           [B][Hv][dv]         fp32; must not overlap any other argument
+ * dk, dv in {16, 32, 64, 128}.
+ */
+int gdn_decode_step(const void *x, const void *conv_w, void *conv_state,
+                    const float *g, const float *beta,
+                    float *state, float *o,
+                    float scale, float l2_eps,
+                    int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *gdn_status_string(int status);
+
+/* GDN_ABI_VERSION of the built library. */
+int gdn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

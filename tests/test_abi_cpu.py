@@ -1,0 +1,130 @@
+"""The C-ABI library loads and exports every symbol include/gdn.h declares, and
+host-side validation returns the documented status codes (CPU only: every call
+here fails validation before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import hybrid_linear_attention_gated_amd as gdn
+    if not os.path.exists(gdn.LIB_PATH):
+        from hybrid_linear_attention_gated_amd import build
+        build.build()
+    return gdn.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size",
+            "gdn_decode_step", "gdn_status_string", "gdn_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.gdn_abi_version() == 1
+    for code in range(7):
+        assert L.gdn_status_string(code).decode().startswith("GDN_")
+    assert b"unknown" in L.gdn_status_string(99)
+
+
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+
+
+def _ptr(off):
+    return ctypes.c_void_p(0x10000000 + off)
+
+
+def test_prep_validation(L):
+    P = _ptr
+    args = dict(x=P(0), w=P(1 << 24), cu=None, N=1, csi=None, cso=None, q=P(2 << 24), k=P(3 << 24), v=P(4 << 24),
+                T=8, Hk=2, Hv=2, dk=16, dv=16, dt=1, eps=1e-6)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.gdn_conv_qk_prep(a["x"], a["w"], a["cu"], a["N"], a["csi"], a["cso"], a["q"], a["k"], a["v"],
+                                  a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"], a["eps"], None)
+    assert call(x=None) == 1
+    assert call(Hv=3) == 2             # Hv % Hk != 0
+    assert call(N=2) == 2              # no cu_seqlens with N > 1
+    assert call(T=-1) == 2
+    assert call(dt=7) == 3
+    assert call(dk=24) == 3
+    assert call(dv=12) == 3
+    assert call(eps=float("nan")) == 2
+    assert call(q=P(8)) == 6           # q overlaps x
+    assert call(cso=P(5 << 24), csi=P((5 << 24) + 64)) == 6   # partial overlap of the conv caches
+
+
+def test_prefill_validation(L):
+    P = _ptr
+    T, H, d = 128, 2, 128
+    need = L.gdn_chunk_prefill_workspace_size(T, 1, H, H, d, d, 1)
+    assert need > 0
+    assert L.gdn_chunk_prefill_workspace_size(T, 1, H, H, d, d, 0) == 0      # fp32 path needs none
+    assert L.gdn_chunk_prefill_workspace_size(T, 1, H, H, 32, 32, 1) == 0    # recurrent path needs none
+
+    base = dict(q=P(0), k=P(1 << 24), v=P(2 << 24), g=P(3 << 24), b=P(4 << 24), cu=None, N=1, s0=None, sf=None,
+                o=P(5 << 24), scale=1.0, T=T, Hk=H, Hv=H, dk=d, dv=d, dt=1, ws=P(1 << 30), wsb=need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["N"], a["s0"], a["sf"], a["o"],
+                                   ctypes.c_float(a["scale"]), a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"],
+                                   a["ws"], ctypes.c_size_t(a["wsb"]), None)
+    assert call(o=None) == 1
+    assert call(Hk=3, Hv=4) == 2
+    assert call(dk=256) == 3
+    assert call(dt=5) == 3
+    assert call(ws=None) == 4
+    assert call(wsb=need - 1) == 4
+    assert call(o=P(16)) == 6                                   # o overlaps q
+    assert call(s0=P(6 << 24), sf=P((6 << 24) + 4)) == 6          # partial state alias
+    assert call(scale=float("inf")) == 2
+
+
+def test_decode_validation(L):
+    P = _ptr
+    base = dict(x=P(0), w=P(1 << 24), cs=P(2 << 24), g=P(3 << 24), b=P(4 << 24), st=P(5 << 24), o=P(6 << 24),
+                B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_decode_step(a["x"], a["w"], a["cs"], a["g"], a["b"], a["st"], a["o"], ctypes.c_float(1.0),
+                                 ctypes.c_float(1e-6), a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"], None)
+    assert call(st=None) == 1
+    assert call(B=-1) == 2
+    assert call(Hv=3) == 2
+    assert call(dk=256) == 3
+    assert call(o=P(8)) == 6
+    assert call(cs=P((5 << 24) + 8)) == 6                     # conv cache overlaps the state
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import hybrid_linear_attention_gated_amd as gdn
+    monkeypatch.setattr(gdn, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(gdn, "_lib", None)
+    with pytest.raises(ImportError):
+        gdn.lib()
+
+
+def test_product_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "hybrid_linear_attention_gated_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "gdn_oracle" not in text, f

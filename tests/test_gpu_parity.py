@@ -1,0 +1,250 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Every case feeds the same seeded inputs to both sides and checks
+max|gpu - oracle| <= tol * RMS(oracle) per output tensor (tol 1e-4 for the
+fp32 element type, 2e-2 for bf16 inputs with an fp32 state); copies of input
+values (conv caches) must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL_BF16, TOL_F32, announce, assert_parity, f32np
+from hybrid_linear_attention_gated_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import hybrid_linear_attention_gated_amd as m
+    m.lib()
+    return m
+
+
+def _cuda(t):
+    return None if t is None else t.to(DEV).contiguous()
+
+
+def _rand(rng, shape, std=1.0):
+    return rng.standard_normal(shape).astype(np.float32) * np.float32(std)
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("B,Hk,Hv,d,dtype", [(3, 2, 2, 16, "f32"), (5, 2, 4, 32, "bf16"), (4, 1, 2, 64, "f32"),
+                                            (7, 2, 2, 128, "bf16"), (2, 2, 4, 128, "f32")])
+def test_decode_small(gdn, B, Hk, Hv, d, dtype):
+    announce(f"decode B={B} Hk={Hk} Hv={Hv} d={d} {dtype}")
+    rng = np.random.default_rng(1000 + B + d)
+    C = 2 * Hk * d + Hv * d
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(_rand(rng, (B, C))).to(tdt)
+    w = torch.from_numpy(_rand(rng, (C, 4), 0.5)).to(tdt)
+    cs = torch.from_numpy(_rand(rng, (B, 3, C))).to(tdt)
+    g = torch.from_numpy(np.log(rng.uniform(0.9, 1.0, (B, Hv))).astype(np.float32))
+    b = torch.from_numpy((1 / (1 + np.exp(-rng.standard_normal((B, Hv))))).astype(np.float32))
+    st = torch.from_numpy(_rand(rng, (B, Hv, d, d), 0.1))
+    o_ref, st_ref, cs_ref = oracle.decode(f32np(x), f32np(w), f32np(cs), f32np(g), f32np(b), f32np(st),
+                                          Hk, Hv, d, d, scale=0.5)
+    csd, std = _cuda(cs), _cuda(st)
+    o = gdn.decode_step(_cuda(x), _cuda(w), csd, _cuda(g), _cuda(b), std, Hk, Hv, d, d, scale=0.5)
+    torch.cuda.synchronize()
+    # decode computes in fp32 from the stored inputs whatever their element type
+    assert_parity("o", f32np(o), o_ref, TOL_F32)
+    assert_parity("state", f32np(std), st_ref, TOL_F32)
+    np.testing.assert_array_equal(f32np(csd), cs_ref)
+
+
+def test_decode256_full(gdn):
+    announce("decode256 full config")
+    wl = inputs.decode256()
+    o_ref, st_ref, cs_ref = oracle.decode(f32np(wl.x), f32np(wl.conv_w), f32np(wl.conv_state), f32np(wl.g),
+                                          f32np(wl.beta), f32np(wl.state), wl.Hk, wl.Hv, wl.dk, wl.dv)
+    csd, std = _cuda(wl.conv_state), _cuda(wl.state)
+    o = gdn.decode_step(_cuda(wl.x), _cuda(wl.conv_w), csd, _cuda(wl.g), _cuda(wl.beta), std,
+                        wl.Hk, wl.Hv, wl.dk, wl.dv)
+    torch.cuda.synchronize()
+    assert_parity("o", f32np(o), o_ref, TOL_F32)
+    assert_parity("state", f32np(std), st_ref, TOL_F32)
+    np.testing.assert_array_equal(f32np(csd), cs_ref)
+
+
+# ------------------------------------------------------------------ prep
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 16), ("bf16", 64)])
+def test_prep_varlen(gdn, dtype, d):
+    announce(f"prep varlen {dtype} d={d}")
+    rng = np.random.default_rng(77 + d)
+    lengths = [1, 2, 0, 37, 16, 100, 3]
+    Hk, Hv = 2, 4
+    C = 2 * Hk * d + Hv * d
+    T = sum(lengths)
+    N = len(lengths)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = torch.from_numpy(_rand(rng, (T, C))).to(tdt)
+    w = torch.from_numpy(_rand(rng, (C, 4), 0.5)).to(tdt)
+    cs = torch.from_numpy(_rand(rng, (N, 3, C))).to(tdt)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int32)
+    q_ref, k_ref, v_ref, cs_ref = oracle.prep(f32np(x), f32np(w), cu.numpy(), Hk, Hv, d, d, cs_in=f32np(cs))
+    cso = torch.empty((N, 3, C), dtype=tdt, device=DEV)
+    q, k, v = gdn.conv_qk_prep(_cuda(x), _cuda(w), Hk, Hv, d, d, cu_seqlens=_cuda(cu), conv_state_in=_cuda(cs),
+                               conv_state_out=cso)
+    torch.cuda.synchronize()
+    def check(name, gpu, ref):   # fp32 outputs computed in fp32 from the stored inputs
+        assert_parity(name, f32np(gpu), ref, TOL_F32)
+    check("q", q, q_ref)
+    check("k", k, k_ref)
+    check("v", v, v_ref)
+    np.testing.assert_array_equal(f32np(cso), cs_ref)
+    # conv_state_out may alias conv_state_in
+    csd = _cuda(cs)
+    gdn.conv_qk_prep(_cuda(x), _cuda(w), Hk, Hv, d, d, cu_seqlens=_cuda(cu), conv_state_in=csd, conv_state_out=csd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f32np(csd), cs_ref)
+    # zero history when no conv_state_in is given
+    q0, _, v0 = gdn.conv_qk_prep(_cuda(x), _cuda(w), Hk, Hv, d, d, cu_seqlens=_cuda(cu))
+    q0_ref, _, v0_ref, _ = oracle.prep(f32np(x), f32np(w), cu.numpy(), Hk, Hv, d, d)
+    torch.cuda.synchronize()
+    check("q (zero history)", q0, q0_ref)
+    check("v (zero history)", v0, v0_ref)
+
+
+# ------------------------------------------------------------------ core (chunk prefill)
+
+def _core_case(gdn, wl, math, heads=None, inplace=False):
+    tol = TOL_F32 if math == "f32" else TOL_BF16
+    cu = wl.cu_seqlens
+    o_ref, f_ref = oracle.recurrence(f32np(wl.q), f32np(wl.k), f32np(wl.v), f32np(wl.g), f32np(wl.beta),
+                                     cu.numpy(), s0=None if wl.state is None else f32np(wl.state),
+                                     scale=wl.scale, heads=heads)
+    s0 = _cuda(wl.state)
+    fin = s0 if (inplace and s0 is not None) else None
+    o, f = gdn.chunk_prefill(_cuda(wl.q), _cuda(wl.k), _cuda(wl.v), _cuda(wl.g), _cuda(wl.beta),
+                             cu_seqlens=_cuda(cu), initial_state=s0, final_state=fin, scale=wl.scale,
+                             math=math)
+    torch.cuda.synchronize()
+    o, f = f32np(o), f32np(f)
+    if heads is not None:
+        o, o_ref = o[:, heads], o_ref[:, heads]
+        f, f_ref = f[:, heads], f_ref[:, heads]
+    assert_parity("o", o, o_ref, tol)
+    assert_parity("final_state", f, f_ref, tol)
+
+
+def test_tiny_f32_config(gdn):
+    announce("tiny_f32 config (fp32 recurrent path)")
+    _core_case(gdn, inputs.tiny_f32(), "f32")
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 32), (128, 128)])
+def test_core_f32_path(gdn, dk, dv):
+    announce(f"core fp32 recurrent path dk={dk} dv={dv}")
+    wl = inputs.core_workload("rec", 500 + dk + dv, [70, 0, 5, 130], 2, 4, dk, dv, random_states=True, scale=0.5)
+    _core_case(gdn, wl, "f32")
+
+
+@pytest.mark.parametrize("lengths", [[1], [63], [64], [65], [127, 128, 129], [1, 0, 200, 64, 3, 0, 191]])
+def test_core_chunked_lengths(gdn, lengths):
+    announce(f"core chunked d=128 lengths={lengths}")
+    wl = inputs.core_workload("chunk", 600 + len(lengths) + sum(lengths), lengths, 2, 2, 128, 128,
+                              random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_core_chunked_gqa_scale_slow_decay(gdn, d):
+    announce(f"core chunked GQA d={d} slow decay")
+    wl = inputs.core_workload("gqa", 700 + d, [300, 129], 2, 4, d, d, random_states=True,
+                              decay="slow", scale=d ** -0.5)
+    _core_case(gdn, wl, "mfma")
+
+
+def test_core_chunked_inplace_state(gdn):
+    announce("core chunked in-place state (final_state aliases initial_state)")
+    wl = inputs.core_workload("inplace", 801, [150, 64], 2, 2, 128, 128, random_states=True)
+    _core_case(gdn, wl, "mfma", inplace=True)
+
+
+def test_core_f32_inplace_state(gdn):
+    announce("core fp32 in-place state")
+    wl = inputs.core_workload("inplace32", 802, [40, 9], 2, 2, 32, 32, random_states=True)
+    _core_case(gdn, wl, "f32", inplace=True)
+
+
+def test_core_empty_sequences(gdn):
+    announce("core: all sequences empty (T = 0)")
+    H, d = 2, 128
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    s0 = torch.randn((3, H, d, d), device=DEV)
+    e = torch.empty((0, H, d), dtype=torch.float32, device=DEV)
+    z = torch.empty((0, H), dtype=torch.float32, device=DEV)
+    o, f = gdn.chunk_prefill(e, e, e, z, z, cu_seqlens=cu, initial_state=s0, math="mfma")
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, d)
+    assert torch.equal(f, s0)
+
+
+# ------------------------------------------------------------------ end to end: prep + chunk prefill
+
+def _e2e(gdn, wl, heads=None):
+    cu = wl.cu_seqlens
+    N = wl.N
+    x32 = f32np(wl.x)
+    q_r, k_r, v_r, cs_r = oracle.prep(x32, f32np(wl.conv_w), cu.numpy(), wl.Hk, wl.Hv, wl.dk, wl.dv,
+                                      cs_in=None if wl.conv_state is None else f32np(wl.conv_state))
+    del x32
+    o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu.numpy(),
+                                     s0=None if wl.state is None else f32np(wl.state), heads=heads)
+    del q_r, k_r, v_r
+    cso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=DEV)
+    q, k, v = gdn.conv_qk_prep(_cuda(wl.x), _cuda(wl.conv_w), wl.Hk, wl.Hv, wl.dk, wl.dv, cu_seqlens=_cuda(cu),
+                               conv_state_in=_cuda(wl.conv_state), conv_state_out=cso)
+    o, f = gdn.chunk_prefill(q, k, v, _cuda(wl.g), _cuda(wl.beta), cu_seqlens=_cuda(cu),
+                             initial_state=_cuda(wl.state), math="mfma")
+    torch.cuda.synchronize()
+    o, f = f32np(o), f32np(f)
+    if heads is not None:
+        o, o_ref, f, f_ref = o[:, heads], o_ref[:, heads], f[:, heads], f_ref[:, heads]
+    assert_parity("o", o, o_ref, TOL_BF16)
+    assert_parity("final_state", f, f_ref, TOL_BF16)
+    np.testing.assert_array_equal(f32np(cso), cs_r)
+
+
+def test_layer_4k_config(gdn):
+    announce("layer_4k config end to end")
+    _e2e(gdn, inputs.layer_4k())
+
+
+def test_varlen8_config(gdn):
+    announce("varlen8 config end to end")
+    _e2e(gdn, inputs.varlen8())
+
+
+def test_long_64k_config_sampled_heads(gdn):
+    announce("long_64k config end to end (oracle on sampled value heads 0, 1, 17, 31)")
+    _e2e(gdn, inputs.long_64k(), heads=[0, 1, 17, 31])
+
+
+# ------------------------------------------------------------------ decode steps == prefill
+
+def test_decode_steps_equal_prefill(gdn):
+    announce("16 decode steps vs one prefill of 16 tokens (both against the oracle)")
+    wl = inputs.prefill_workload("dec_vs_pre", 900, [16], 2, 4, 64)
+    C = wl.conv_dim
+    q_r, k_r, v_r, _ = oracle.prep(f32np(wl.x), f32np(wl.conv_w), wl.cu_seqlens.numpy(), 2, 4, 64, 64)
+    o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), wl.cu_seqlens.numpy())
+    cs = torch.zeros((1, 3, C), dtype=torch.bfloat16, device=DEV)
+    st = torch.zeros((1, 4, 64, 64), dtype=torch.float32, device=DEV)
+    xs, gs, bs, ws = _cuda(wl.x), _cuda(wl.g), _cuda(wl.beta), _cuda(wl.conv_w)
+    outs = []
+    for t in range(16):
+        outs.append(gdn.decode_step(xs[t:t + 1].contiguous(), ws, cs, gs[t:t + 1].contiguous(),
+                                    bs[t:t + 1].contiguous(), st, 2, 4, 64, 64))
+    torch.cuda.synchronize()
+    assert_parity("o (decode)", f32np(torch.cat(outs)), o_ref, TOL_BF16)
+    assert_parity("state (decode)", f32np(st), f_ref, TOL_BF16)
+    np.testing.assert_array_equal(f32np(cs)[0], f32np(wl.x)[-3:])
