@@ -40,7 +40,8 @@
 //  state_pass_kernel: one wave per (sequence, value head, 16-column strip of
 //    the state); the strip's fp32 state lives in MFMA accumulators for the
 //    whole sequence and the chunk loop runs Delta = U - W S, O = Qt S + Ol,
-//    S = g S + K^T (decay * Delta) with every operand in registers.
+//    S = g S + K^T (decay * Delta), with the chunk's A operands double-buffered
+//    in LDS.
 //    Accumulator tiles are reused as B operands directly: the k index of an
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
@@ -61,7 +62,7 @@ struct Rec {
     static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U   f32 tiles [NTD col tiles][4 row tiles][64][4]
     static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
     static constexpr int DC_OFF = O_OFF + 64 * D * 4;   // e^{G_c - G_t}, f32 [64]
-    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32
+    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32, stored 4 times (vector loads)
     static constexpr int SIZE = (GM_OFF + 16 + 255) / 256 * 256;
 };
 
@@ -157,14 +158,15 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     char *rec = ws + ((size_t)gc * Hv + h) * R::SIZE;
 
     // ---- K and Q (key head kh) as bf16 hi/lo planes; rows >= L are zero
+#pragma unroll
     for (int e = tid; e < 64 * (D / 4); e += 256) {
         const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-        if (r < L) {
-            kv = *reinterpret_cast<const float4 *>(k + ((size_t)(t0 + r) * Hk + kh) * D + c4);
-            qv = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + r) * Hk + kh) * D + c4);
-        }
-        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+        const int rr = min(r, L - 1);   // clamped row: loads stay unconditional, padded rows are zeroed
+        const float4 kv0 = *reinterpret_cast<const float4 *>(k + ((size_t)(t0 + rr) * Hk + kh) * D + c4);
+        const float4 qv0 = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + rr) * Hk + kh) * D + c4);
+        const bool live = r < L;
+        const float kk[4] = {live ? kv0.x : 0.f, live ? kv0.y : 0.f, live ? kv0.z : 0.f, live ? kv0.w : 0.f};
+        const float qq[4] = {live ? qv0.x : 0.f, live ? qv0.y : 0.f, live ? qv0.z : 0.f, live ? qv0.w : 0.f};
         bf16x4 khi, klo, qhi, qlo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -178,7 +180,12 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     }
     if (wave == 0) {
         float gg = 0.f, bb = 0.f;
-        if (lane < L) { gg = g[(size_t)(t0 + lane) * Hv + h]; bb = beta[(size_t)(t0 + lane) * Hv + h]; }
+        {
+            const int rr = min(lane, L - 1);
+            const float g0 = g[(size_t)(t0 + rr) * Hv + h], b0 = beta[(size_t)(t0 + rr) * Hv + h];
+            gg = lane < L ? g0 : 0.f;
+            bb = lane < L ? b0 : 0.f;
+        }
         float G = gg;   // inclusive prefix sum over the chunk
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(G, o, kWave);
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         Eg[lane] = __expf(G);
         Dc[lane] = __expf(Gc - G);
         reinterpret_cast<float *>(rec + R::DC_OFF)[lane] = __expf(Gc - G);
-        if (lane == 0) *reinterpret_cast<float *>(rec + R::GM_OFF) = __expf(Gc);
+        if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
     }
     __syncthreads();
 
@@ -254,6 +261,19 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     // Waves 0,1 own W column tiles, waves 2,3 own U column tiles (TPW each).
     const bool isW = wave < 2;
     const int tile0 = (wave & 1) * TPW;
+    // U waves: their V columns for all 64 rows, loaded up front (clamped rows, no branches)
+    float Vr[4][TPW][4];
+    if (!isW) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int jj = 0; jj < TPW; ++jj)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int t = 16 * r + 4 * kg + qq;
+                    Vr[r][jj][qq] = v[((size_t)(t0 + min(t, L - 1)) * Hv + h) * D + 16 * (tile0 + jj) + l16];
+                }
+    }
     f32x4 X[4][TPW];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -264,10 +284,9 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const int t = 16 * r + 4 * kg + qq;
-                float val;
-                if (isW) val = Bs[t] * Eg[t] * ((float)Kh[t * LD + col] + (float)Kl[t * LD + col]);
-                else val = t < L ? Bs[t] * v[((size_t)(t0 + t) * Hv + h) * D + col] : 0.f;
-                acc[jj][qq] = val;
+                // Bs[t] = 0 on padded rows
+                acc[jj][qq] = isW ? Bs[t] * Eg[t] * ((float)Kh[t * LD + col] + (float)Kl[t * LD + col])
+                                  : Bs[t] * Vr[r][jj][qq];
             }
         }
 #pragma unroll
@@ -390,12 +409,33 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 
 // ============================================================== state pass
 
+// Copy `bytes` (a multiple of 1 KiB) from global to LDS with 16-byte direct
+// loads: each wave instruction moves 1 KiB (lane l writes base + 16 l).  The
+// waves of the block split the copy; completion is tracked by vmcnt.
+__device__ __forceinline__ void copy_to_lds(const char *src, char *dst, int bytes, int wave, int nwaves, int lane) {
+    for (int off = wave * 1024; off < bytes; off += nwaves * 1024)
+        __builtin_amdgcn_global_load_lds((const void *)(src + off + lane * 16),
+                                         (__attribute__((address_space(3))) void *)(dst + off), 16, 0, 0);
+}
+
+// One single-wave workgroup per (sequence, value head, 16-column strip of the
+// state).  The strip's fp32 state lives in MFMA accumulators for the whole
+// sequence.  The chunk's A operands (W, Qt, K^T hi / lo fragments: the first
+// Rec::U_OFF bytes of its record, shared by all strips of the head and kept in
+// L2 by placing those strips on one XCD) are staged in LDS, double-buffered:
+// the direct copy of chunk c + 1 runs while chunk c is computed.  Fragments are
+// read from LDS in groups, and the reads of group g + 1 are issued right after
+// the first MFMA of group g, so LDS latency hides behind the rest of group g.
 template <int D>
 __global__ __launch_bounds__(64) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
     const float *s0, float *sf, float *__restrict__ o) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16;
+    constexpr int ABYTES = R::U_OFF;       // A-operand fragments of one chunk
+    static_assert(ABYTES % 1024 == 0, "copy granularity");
+    __shared__ __attribute__((aligned(16))) char abuf[2][ABYTES];
+
     // block -> (unit, strip) so that the NS strips of one unit land on the same XCD
     const int b = blockIdx.x;
     const int u = 8 * (b / (8 * NS)) + (b % 8);
@@ -411,81 +451,84 @@ __global__ __launch_bounds__(64) void state_pass_kernel(
 
     f32x4 S[NTD];
     const size_t st_off = ((size_t)s * Hv + h) * D * D;
+    if (s0) {
 #pragma unroll
-    for (int m = 0; m < NTD; ++m)
+        for (int m = 0; m < NTD; ++m)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-            S[m][qq] = s0 ? s0[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] : 0.f;
+            for (int qq = 0; qq < 4; ++qq) S[m][qq] = s0[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col];
+    } else {
+#pragma unroll
+        for (int m = 0; m < NTD; ++m) S[m] = zero4();
+    }
 
     if (nc > 0) {
-        f16x8 Wf[4][NKS], Qf[4][NKS], Kf[NTD][2], Kfl[NTD][2];
+        auto rec_of = [&](int c) { return ws + ((size_t)(gbase + c) * Hv + h) * R::SIZE; };
         f32x4 Uf[4], Of[4], Dcf[4];
         float gm;
-        auto rec_of = [&](int c) { return ws + ((size_t)(gbase + c) * Hv + h) * R::SIZE; };
-        auto load_W = [&](const char *rec) {
+        auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, f32x4 *D_, float &g_) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    Wf[mt][ks] = *reinterpret_cast<const f16x8 *>(rec + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                Uf[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+                U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+                O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+                D_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
             }
+            // lane-varying address: a vector load (no scalar load in the loop)
+            g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
         };
-        auto load_Q = [&](const char *rec) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    Qf[mt][ks] = *reinterpret_cast<const f16x8 *>(rec + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                Of[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
-            }
-        };
-        auto load_K = [&](const char *rec) {
-#pragma unroll
-            for (int m = 0; m < NTD; ++m)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    Kf[m][ks] = *reinterpret_cast<const f16x8 *>(rec + R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16);
-                    Kfl[m][ks] = *reinterpret_cast<const f16x8 *>(rec + R::K_OFF + (((NTD + m) * 2 + ks) * 64 + lane) * 16);
-                }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                Dcf[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
-            gm = *reinterpret_cast<const float *>(rec + R::GM_OFF);
-        };
-        load_W(rec_of(0));
-        load_Q(rec_of(0));
-        load_K(rec_of(0));
+        copy_to_lds(rec_of(0), abuf[0], ABYTES, 0, 1, lane);
+        load_strip(rec_of(0), Uf, Of, Dcf, gm);
+        __builtin_amdgcn_s_waitcnt(0);
 
         for (int c = 0; c < nc; ++c) {
-            const char *recn = rec_of(min(c + 1, nc - 1));   // next chunk (re-loads the last one at the end)
+            const char *A = abuf[c & 1];
+            f32x4 Un[4], On[4], Dn[4];
+            float gn = 0.f;
+            if (c + 1 < nc) {
+                copy_to_lds(rec_of(c + 1), abuf[(c + 1) & 1], ABYTES, 0, 1, lane);
+                load_strip(rec_of(c + 1), Un, On, Dn, gn);
+            }
             f16x8 Sh[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
 
-            // Delta = U - W S
-            f32x4 Dl[4];
+            // ---- Delta = U - W S ;  O = Qt S + Ol.  Group mt = 2 NKS fragments (W and Qt rows of tile mt).
+            f16x8 fa[2][2 * NKS];
+            auto read_wq = [&](int mt, f16x8 *F) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    F[ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                    F[NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                }
+            };
+            // K group m = 4 fragments (hi and lo, both k steps of row tile m)
+            f16x8 fk[2][4];
+            auto read_k = [&](int m, f16x8 *F) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    F[ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16);
+                    F[2 + ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((NTD + m) * 2 + ks) * 64 + lane) * 16);
+                }
+            };
+            read_wq(0, fa[0]);
+            f32x4 Dl[4], Ot[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 acc = zero4();
+                const f16x8 *F = fa[mt & 1];
+                f32x4 acc = mfma16(F[0], Sh[0], zero4());
+                __builtin_amdgcn_sched_barrier(0);
+                if (mt + 1 < 4) read_wq(mt + 1, fa[(mt + 1) & 1]);
+                else read_k(0, fk[0]);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 oacc = Of[mt];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) acc = mfma16(Wf[mt][ks], Sh[ks], acc);
+                for (int ks = 1; ks < NKS; ++ks) acc = mfma16(F[ks], Sh[ks], acc);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) oacc = mfma16(F[NKS + ks], Sh[ks], oacc);
                 Dl[mt] = Uf[mt] - acc;
+                Ot[mt] = oacc;
             }
-            load_W(recn);
 
-            // O = Qt S + Ol
-            f32x4 Ot[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 acc = Of[mt];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) acc = mfma16(Qf[mt][ks], Sh[ks], acc);
-                Ot[mt] = acc;
-            }
-            load_Q(recn);
-
-            // S = gamma S + K^T (decay * Delta), decayed Delta as an fp16 hi + lo pair
+            // ---- S = gamma S + K^T (decay * Delta), K and the decayed Delta as fp16 hi + lo pairs
             f16x8 Dh[2], Dlo[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
@@ -501,26 +544,41 @@ __global__ __launch_bounds__(64) void state_pass_kernel(
             }
 #pragma unroll
             for (int m = 0; m < NTD; ++m) {
-                f32x4 acc = S[m] * gm;
-                acc = mfma16(Kfl[m][0], Dh[0], acc);
-                acc = mfma16(Kfl[m][1], Dh[1], acc);
-                acc = mfma16(Kf[m][0], Dlo[0], acc);
-                acc = mfma16(Kf[m][1], Dlo[1], acc);
-                acc = mfma16(Kf[m][0], Dh[0], acc);
-                S[m] = mfma16(Kf[m][1], Dh[1], acc);
+                const f16x8 *F = fk[m & 1];
+                f32x4 acc = mfma16(F[0], Dh[0], S[m] * gm);
+                __builtin_amdgcn_sched_barrier(0);
+                if (m + 1 < NTD) read_k(m + 1, fk[(m + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                acc = mfma16(F[1], Dh[1], acc);
+                acc = mfma16(F[0], Dlo[0], acc);
+                acc = mfma16(F[1], Dlo[1], acc);
+                acc = mfma16(F[2], Dh[0], acc);
+                S[m] = mfma16(F[3], Dh[1], acc);
             }
-            load_K(recn);
 
-            // store this chunk's outputs
+            // ---- this chunk's outputs
             const int tb = t0 + c * kChunk;
             const int rows = min(kChunk, L - c * kChunk);
+            float *ob = o + ((size_t)tb * Hv + h) * D + col;
+            if (rows == kChunk) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int r = 16 * mt + 4 * kg + qq;
-                    if (r < rows) o[((size_t)(tb + r) * Hv + h) * D + col] = Ot[mt][qq];
-                }
+                    for (int qq = 0; qq < 4; ++qq) ob[(size_t)(16 * mt + 4 * kg + qq) * Hv * D] = Ot[mt][qq];
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        const int r = 16 * mt + 4 * kg + qq;
+                        if (r < rows) ob[(size_t)r * Hv * D] = Ot[mt][qq];
+                    }
+            }
+
+            __builtin_amdgcn_s_waitcnt(0);   // next chunk's copy and strip data have landed
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; Dcf[mt] = Dn[mt]; }
+            gm = gn;
         }
     }
     if (sf) {
