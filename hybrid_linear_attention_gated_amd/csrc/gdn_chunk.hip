@@ -37,11 +37,11 @@
 //    explicit T), then Qt and Ol.  Writes W, Qt, K^T as fp16 MFMA A-operand
 //    fragments and U, Ol as fp32 accumulator-layout tiles, so the state pass
 //    reads every operand with one coalesced 16-byte load per lane.
-//  state_pass_kernel: one wave per (sequence, value head, 16-column strip of
-//    the state); the strip's fp32 state lives in MFMA accumulators for the
-//    whole sequence and the chunk loop runs Delta = U - W S, O = Qt S + Ol,
+//  state_pass_kernel: one workgroup per (sequence, value head, two 16-column
+//    strips of the state); a strip's fp32 state lives in MFMA accumulators for
+//    the whole sequence and the chunk loop runs Delta = U - W S, O = Qt S + Ol,
 //    S = g S + K^T (decay * Delta), with the chunk's A operands double-buffered
-//    in LDS.
+//    in LDS by two copy waves.
 //    Accumulator tiles are reused as B operands directly: the k index of an
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
@@ -62,8 +62,8 @@ struct Rec {
     static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U   f32 tiles [NTD col tiles][4 row tiles][64][4]
     static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
     static constexpr int DC_OFF = O_OFF + 64 * D * 4;   // e^{G_c - G_t}, f32 [64]
-    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32, stored 4 times (vector loads)
-    static constexpr int SIZE = (GM_OFF + 16 + 255) / 256 * 256;
+    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32, stored 4 times
+    static constexpr int SIZE = DC_OFF + 1024;          // the decay slot is padded to 1 KiB
 };
 
 // Wave-parallel: first chunk index of sequence s in the packed chunk list.
@@ -117,7 +117,7 @@ template <int D>
 __global__ __launch_bounds__(256) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
-    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws) {
+    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD;
     constexpr int LD = D + 8;    // row stride (elements) of the 64 x D 16-bit LDS tiles
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     __syncthreads();
     if (!loc[0]) return;
     const int t0 = loc[1], L = loc[2];
-    char *rec = ws + ((size_t)gc * Hv + h) * R::SIZE;
+    char *rec = ws + ((size_t)h * ncmax + gc) * R::SIZE;   // head-major: a head's chunks are contiguous
 
     // ---- K and Q (key head kh) as bf16 hi/lo planes; rows >= L are zero
 #pragma unroll
@@ -409,45 +409,88 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 
 // ============================================================== state pass
 
-// Copy `bytes` (a multiple of 1 KiB) from global to LDS with 16-byte direct
-// loads: each wave instruction moves 1 KiB (lane l writes base + 16 l).  The
-// waves of the block split the copy; completion is tracked by vmcnt.
-__device__ __forceinline__ void copy_to_lds(const char *src, char *dst, int bytes, int wave, int nwaves, int lane) {
-    for (int off = wave * 1024; off < bytes; off += nwaves * 1024)
-        __builtin_amdgcn_global_load_lds((const void *)(src + off + lane * 16),
-                                         (__attribute__((address_space(3))) void *)(dst + off), 16, 0, 0);
+// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit elements;
+// out-of-range loads return 0 and out-of-range stores are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-// One single-wave workgroup per (sequence, value head, 16-column strip of the
-// state).  The strip's fp32 state lives in MFMA accumulators for the whole
-// sequence.  The chunk's A operands (W, Qt, K^T hi / lo fragments: the first
-// Rec::U_OFF bytes of its record, shared by all strips of the head and kept in
-// L2 by placing those strips on one XCD) are staged in LDS, double-buffered:
-// the direct copy of chunk c + 1 runs while chunk c is computed.  Fragments are
-// read from LDS in groups, and the reads of group g + 1 are issued right after
-// the first MFMA of group g, so LDS latency hides behind the rest of group g.
+// Copy `bytes` (a multiple of 1 KiB) at byte `src_off` of the buffer to LDS:
+// each wave instruction moves 1 KiB (lane l -> base + 16 l); completion is
+// tracked by vmcnt.  Addresses are all scalar except the constant lane offset.
+// The block order is rotated by `rot` so that workgroups copying the same
+// record at the same time touch different L2 lines.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_off, char *dst, int bytes, int lane,
+                                            int rot = 0) {
+    const int nblk = bytes / 1024;
+#pragma unroll 8
+    for (int i = 0; i < nblk; ++i) {
+        int blk = i + rot;
+        blk = blk >= nblk ? blk - nblk : blk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + blk * 1024), 16,
+                                                 lane * 16, src_off + blk * 1024, 0, 0);
+    }
+}
+
+// One 4-wave workgroup per (sequence, value head, pair of 16-column strips of
+// the state).  Waves 0 and 1 compute one strip each; waves 2 and 3 only copy.
+// A strip's fp32 state lives in MFMA accumulators for the whole sequence.  Each
+// chunk's A operands (W, Qt, K^T hi / lo fragments: the first Rec::U_OFF bytes
+// of its record, shared by all strips of the head and kept in L2 by placing
+// those workgroups on one XCD) are staged in LDS by the copy waves,
+// double-buffered, while the compute waves work on the previous chunk: a single
+// wave keeps too few requests in flight to stream a record at memory latency,
+// and a wave with direct-to-LDS loads in flight cannot wait on its own LDS reads
+// precisely.  The compute waves prefetch their strip's U, Ol and decay factors
+// one chunk ahead into registers and read fragments from LDS in groups; the
+// reads of group g + 1 are issued right after the first MFMA of group g.
 template <int D>
-__global__ __launch_bounds__(64) void state_pass_kernel(
+__global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o) {
+    const float *s0, float *sf, float *__restrict__ o, int ncmax) {
     using R = Rec<D>;
-    constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16;
-    constexpr int ABYTES = R::U_OFF;       // A-operand fragments of one chunk
-    static_assert(ABYTES % 1024 == 0, "copy granularity");
+    constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
+    constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
+    static_assert(ABYTES % 2048 == 0, "copy granularity");
     __shared__ __attribute__((aligned(16))) char abuf[2][ABYTES];
 
-    // block -> (unit, strip) so that the NS strips of one unit land on the same XCD
+    // block -> (unit, strip pair) so that the NP blocks of one unit land on the same XCD
     const int b = blockIdx.x;
-    const int u = 8 * (b / (8 * NS)) + (b % 8);
-    const int j = (b / 8) % NS;
+    const int u = 8 * (b / (8 * NP)) + (b % 8);
+    const int pair = (b / 8) % NP;
     if (u >= units) return;
     const int s = u / Hv, h = u % Hv;
-    const int lane = threadIdx.x, l16 = lane & 15, kg = lane >> 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool copier = wave >= 2;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int j = 2 * pair + (wave & 1);
     const int col = 16 * j + l16;
-    const int t0 = seq_begin(cu, s);
-    const int L = seq_end(cu, s, Ttot) - t0;
+    // wave-uniform values, kept in scalar registers (buffer resources must be uniform)
+    const int t0 = __builtin_amdgcn_readfirstlane(seq_begin(cu, s));
+    const int L = __builtin_amdgcn_readfirstlane(seq_end(cu, s, Ttot) - t0);
     const int nc = n_chunks(L);
-    const int gbase = chunk_base_wave(cu, s);
+    const int gbase = __builtin_amdgcn_readfirstlane(chunk_base_wave(cu, s));
+    auto rec_of = [&](int c) { return ws + ((size_t)h * ncmax + gbase + c) * R::SIZE; };
+
+    if (copier) {
+        // Each copy wave moves half of the A operands with direct-to-LDS buffer loads
+        // (lane l of each 16-byte load lands at base + 16 l), then waits for them before
+        // the barrier that hands the buffer to the compute waves.
+        const int half = (wave - 2) * (ABYTES / 2);
+        auto stage = [&](int c, char *dst) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(c), R::SIZE);
+            copy_to_lds(r, half, dst + half, ABYTES / 2, lane);
+        };
+        if (nc > 0) stage(0, abuf[0]);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        for (int c = 0; c < nc; ++c) {
+            if (c + 1 < nc) stage(c + 1, abuf[(c + 1) & 1]);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
 
     f32x4 S[NTD];
     const size_t st_off = ((size_t)s * Hv + h) * D * D;
@@ -460,126 +503,139 @@ __global__ __launch_bounds__(64) void state_pass_kernel(
 #pragma unroll
         for (int m = 0; m < NTD; ++m) S[m] = zero4();
     }
-
-    if (nc > 0) {
-        auto rec_of = [&](int c) { return ws + ((size_t)(gbase + c) * Hv + h) * R::SIZE; };
-        f32x4 Uf[4], Of[4], Dcf[4];
-        float gm;
-        auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, f32x4 *D_, float &g_) {
+    f32x4 Uf[4], Of[4], Dcf[4];
+    float gm = 0.f;
+    auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, f32x4 *D_, float &g_) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
-                O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
-                D_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
+        for (int mt = 0; mt < 4; ++mt) {
+            U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+            O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
+            D_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
+        }
+        // lane-varying address: a vector load (no scalar load shares lgkmcnt with LDS reads)
+        g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
+    };
+    if (nc > 0) load_strip(rec_of(0), Uf, Of, Dcf, gm);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int c = 0; c < nc; ++c) {
+        const char *A = abuf[c & 1];
+        // strip data of the next chunk
+        f32x4 Un[4], On[4], Dn[4];
+        float gn = 0.f;
+        if (c + 1 < nc) load_strip(rec_of(c + 1), Un, On, Dn, gn);
+        f16x8 Sh[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
+
+        // ---- Delta = U - W S ;  O = Qt S + Ol.  Group mt: W and Qt fragments of row tile mt.
+        f16x8 fa[2][2 * NKS];
+        auto read_wq = [&](int mt, f16x8 *F) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                F[ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                F[NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
             }
-            // lane-varying address: a vector load (no scalar load in the loop)
-            g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
         };
-        copy_to_lds(rec_of(0), abuf[0], ABYTES, 0, 1, lane);
-        load_strip(rec_of(0), Uf, Of, Dcf, gm);
-        __builtin_amdgcn_s_waitcnt(0);
-
-        for (int c = 0; c < nc; ++c) {
-            const char *A = abuf[c & 1];
-            f32x4 Un[4], On[4], Dn[4];
-            float gn = 0.f;
-            if (c + 1 < nc) {
-                copy_to_lds(rec_of(c + 1), abuf[(c + 1) & 1], ABYTES, 0, 1, lane);
-                load_strip(rec_of(c + 1), Un, On, Dn, gn);
-            }
-            f16x8 Sh[NKS];
+        // K group: two row tiles m, m + 1 (hi and lo fragments, both k steps) = 8 fragments
+        f16x8 fk[2][8];
+        auto read_k = [&](int m, f16x8 *F) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
-
-            // ---- Delta = U - W S ;  O = Qt S + Ol.  Group mt = 2 NKS fragments (W and Qt rows of tile mt).
-            f16x8 fa[2][2 * NKS];
-            auto read_wq = [&](int mt, f16x8 *F) {
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    F[ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                    F[NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                }
-            };
-            // K group m = 4 fragments (hi and lo, both k steps of row tile m)
-            f16x8 fk[2][4];
-            auto read_k = [&](int m, f16x8 *F) {
+            for (int dm = 0; dm < 2; ++dm)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    F[ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16);
-                    F[2 + ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((NTD + m) * 2 + ks) * 64 + lane) * 16);
+                    F[4 * dm + ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((m + dm) * 2 + ks) * 64 + lane) * 16);
+                    F[4 * dm + 2 + ks] =
+                        *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((NTD + m + dm) * 2 + ks) * 64 + lane) * 16);
                 }
-            };
-            read_wq(0, fa[0]);
-            f32x4 Dl[4], Ot[4];
+        };
+        read_wq(0, fa[0]);
+        f32x4 Dl[4], Ot[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const f16x8 *F = fa[mt & 1];
-                f32x4 acc = mfma16(F[0], Sh[0], zero4());
-                __builtin_amdgcn_sched_barrier(0);
-                if (mt + 1 < 4) read_wq(mt + 1, fa[(mt + 1) & 1]);
-                else read_k(0, fk[0]);
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4 oacc = Of[mt];
+        for (int mt = 0; mt < 4; ++mt) {
+            const f16x8 *F = fa[mt & 1];
+            f32x4 acc = mfma16(F[0], Sh[0], zero4());
+            __builtin_amdgcn_sched_barrier(0);
+            if (mt + 1 < 4) read_wq(mt + 1, fa[(mt + 1) & 1]);
+            else read_k(0, fk[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            // four independent accumulation chains (a dependent MFMA waits ~44 cycles,
+            // one issues every 16): even / odd k steps of W S and of Qt S
+            f32x4 oacc = mfma16(F[NKS], Sh[0], Of[mt]);
+            f32x4 acc1 = mfma16(F[1], Sh[1], zero4());
+            f32x4 oacc1 = mfma16(F[NKS + 1], Sh[1], zero4());
 #pragma unroll
-                for (int ks = 1; ks < NKS; ++ks) acc = mfma16(F[ks], Sh[ks], acc);
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) oacc = mfma16(F[NKS + ks], Sh[ks], oacc);
-                Dl[mt] = Uf[mt] - acc;
-                Ot[mt] = oacc;
+            for (int ks = 2; ks < NKS; ks += 2) {
+                acc = mfma16(F[ks], Sh[ks], acc);
+                oacc = mfma16(F[NKS + ks], Sh[ks], oacc);
+                acc1 = mfma16(F[ks + 1], Sh[ks + 1], acc1);
+                oacc1 = mfma16(F[NKS + ks + 1], Sh[ks + 1], oacc1);
             }
-
-            // ---- S = gamma S + K^T (decay * Delta), K and the decayed Delta as fp16 hi + lo pairs
-            f16x8 Dh[2], Dlo[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 d0 = Dl[2 * ks] * Dcf[2 * ks], d1 = Dl[2 * ks + 1] * Dcf[2 * ks + 1];
-                Dh[ks] = pack_h(d0, d1);
-                f32x4 r0, r1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    r0[e] = d0[e] - (float)Dh[ks][e];
-                    r1[e] = d1[e] - (float)Dh[ks][4 + e];
-                }
-                Dlo[ks] = pack_h(r0, r1);
-            }
-#pragma unroll
-            for (int m = 0; m < NTD; ++m) {
-                const f16x8 *F = fk[m & 1];
-                f32x4 acc = mfma16(F[0], Dh[0], S[m] * gm);
-                __builtin_amdgcn_sched_barrier(0);
-                if (m + 1 < NTD) read_k(m + 1, fk[(m + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                acc = mfma16(F[1], Dh[1], acc);
-                acc = mfma16(F[0], Dlo[0], acc);
-                acc = mfma16(F[1], Dlo[1], acc);
-                acc = mfma16(F[2], Dh[0], acc);
-                S[m] = mfma16(F[3], Dh[1], acc);
-            }
-
-            // ---- this chunk's outputs
-            const int tb = t0 + c * kChunk;
-            const int rows = min(kChunk, L - c * kChunk);
-            float *ob = o + ((size_t)tb * Hv + h) * D + col;
-            if (rows == kChunk) {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) ob[(size_t)(16 * mt + 4 * kg + qq) * Hv * D] = Ot[mt][qq];
-            } else {
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        const int r = 16 * mt + 4 * kg + qq;
-                        if (r < rows) ob[(size_t)r * Hv * D] = Ot[mt][qq];
-                    }
-            }
-
-            __builtin_amdgcn_s_waitcnt(0);   // next chunk's copy and strip data have landed
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; Dcf[mt] = Dn[mt]; }
-            gm = gn;
+            Dl[mt] = Uf[mt] - (acc + acc1);
+            Ot[mt] = oacc + oacc1;
         }
+
+        // ---- S = gamma S + K^T (decay * Delta), K and the decayed Delta as fp16 hi + lo pairs
+        f16x8 Dh[2], Dlo[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f32x4 d0 = Dl[2 * ks] * Dcf[2 * ks], d1 = Dl[2 * ks + 1] * Dcf[2 * ks + 1];
+            Dh[ks] = pack_h(d0, d1);
+            f32x4 r0, r1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r0[e] = d0[e] - (float)Dh[ks][e];
+                r1[e] = d1[e] - (float)Dh[ks][4 + e];
+            }
+            Dlo[ks] = pack_h(r0, r1);
+        }
+#pragma unroll
+        for (int m = 0; m < NTD; m += 2) {
+            const f16x8 *F = fk[(m / 2) & 1];
+            f32x4 a0 = mfma16(F[0], Dh[0], S[m] * gm);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m + 2 < NTD) read_k(m + 2, fk[((m / 2) + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            // row tiles m and m + 1, each as two partial sums: four independent chains
+            f32x4 a1 = mfma16(F[4], Dh[0], S[m + 1] * gm);
+            f32x4 b0 = mfma16(F[0], Dlo[0], zero4());
+            f32x4 b1 = mfma16(F[4], Dlo[0], zero4());
+            a0 = mfma16(F[1], Dh[1], a0);
+            a1 = mfma16(F[5], Dh[1], a1);
+            b0 = mfma16(F[1], Dlo[1], b0);
+            b1 = mfma16(F[5], Dlo[1], b1);
+            a0 = mfma16(F[2], Dh[0], a0);
+            a1 = mfma16(F[6], Dh[0], a1);
+            b0 = mfma16(F[3], Dh[1], b0);
+            b1 = mfma16(F[7], Dh[1], b1);
+            S[m] = a0 + b0;
+            S[m + 1] = a1 + b1;
+        }
+
+        // ---- this chunk's outputs
+        const int tb = t0 + c * kChunk;
+        const int rows = min(kChunk, L - c * kChunk);
+        float *ob = o + ((size_t)tb * Hv + h) * D + col;
+        if (rows == kChunk) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) ob[(size_t)(16 * mt + 4 * kg + qq) * Hv * D] = Ot[mt][qq];
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int r = 16 * mt + 4 * kg + qq;
+                    if (r < rows) ob[(size_t)r * Hv * D] = Ot[mt][qq];
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // next chunk's strip data has landed
+        __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; Dcf[mt] = Dn[mt]; }
+        gm = gn;
     }
     if (sf) {
 #pragma unroll
@@ -607,16 +663,16 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     char *ws = (char *)a.ws;
     if ((phases & 1) && nc > 0 && a.T > 0) {
         hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)nc, a.Hv), dim3(256), 0, st, a.q, a.k, a.v,
-                           a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws);
+                           a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, (int)nc);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phases & 2) {
         const int units = a.N * a.Hv;
-        constexpr int NS = D / 16;
-        const int blocks = 8 * NS * ((units + 7) / 8);
-        hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(64), 0, st, (const char *)ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o);
+        constexpr int NP = D / 32;
+        const int blocks = 8 * NP * ((units + 7) / 8);
+        hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(256), 0, st, (const char *)ws, a.cu, a.T,
+                           a.Hv, units, a.s0, a.sf, a.o, (int)nc);
         return hipGetLastError();
     }
     return hipSuccess;
