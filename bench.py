@@ -31,13 +31,17 @@ METRIC = "GDN prefill tokens/s + decode state GB/s (fraction of MI355X roofline)
 
 
 def algorithmic_counts(T, Hk, Hv, d, C, N, B):
-    """Algorithmic work per launch of each kernel (bytes moved once / flops of the
-    chunk form, lower triangles only; split-operand MFMA repeats are not counted)."""
+    """Algorithmic work per launch of each kernel.
+
+    Prefill flops are the chunk method's own (lower triangles only) per token
+    and value head: (3C-1) dk + 2C dv + C^2/3 for the chunk-local products and
+    the triangular solve (K K^T, Q K^T, T K, T V, P Delta) and 6 dk dv for the
+    state contractions (W S, Q S, K^T Delta); extra products that a kernel
+    issues for its own reasons (split operands, P W) are not counted.  Bytes
+    are those the kernel's interface must move once."""
     conv_dim = 2 * Hk * d + Hv * d
     prep_bytes = T * conv_dim * 2 + T * (2 * Hk * d + Hv * d) * 4 + conv_dim * 4 * 2 + N * 3 * conv_dim * 2
-    # chunk-local per token and value head: K K^T, Q K^T, W, U, P W, P U (each C*d) + diagonal solves
-    local_flops = T * Hv * (6 * C * d + C * C // 3)
-    # state pass per token and value head: W S, Qt S, K^T Delta (each 2 d d)
+    local_flops = T * Hv * ((3 * C - 1) * d + 2 * C * d + C * C // 3)
     state_flops = T * Hv * 6 * d * d
     dec_state = 2 * B * Hv * d * d * 4
     dec_bytes = dec_state + B * conv_dim * 2 + 2 * B * 3 * conv_dim * 2 + B * Hv * d * 4 + 2 * B * Hv * 4 \
@@ -45,8 +49,10 @@ def algorithmic_counts(T, Hk, Hv, d, C, N, B):
     return prep_bytes, local_flops, state_flops, dec_bytes
 
 
-def cpu_baseline(wl):
-    """The fp64 oracle on the same prefill batch, on this host's cores."""
+def cpu_baseline(wl, min_seconds=10.0):
+    """The fp64 oracle on the same prefill batch, on this host's cores: whole
+    passes (prep, then the token recurrence) repeated until at least
+    `min_seconds` have run (three passes at least); the median pass is reported."""
     import numpy as np
     import oracle
     x = wl.x.float().numpy()
@@ -56,16 +62,46 @@ def cpu_baseline(wl):
     b = wl.beta.numpy()
     oracle.lib()
     times = []
-    for _ in range(3):
+    start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - start < min_seconds:
         t0 = time.perf_counter()
         q, k, v, _ = oracle.prep(x, w, cu, wl.Hk, wl.Hv, wl.dk, wl.dv)
         oracle.recurrence(q, k, v, g, b, cu)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": wl.T / t, "unit": "tokens/s", "cores": oracle.threads(1 << 30), "kind": "oracle",
-            "sample": f"full layer_4k prefill (conv+SiLU+L2 over T={wl.T}, then the fp64 token recurrence for all "
-                      f"{wl.Hv} heads), median of 3 runs, {t:.2f} s each; OpenMP over tokens (prep) and heads "
-                      f"(recurrence)"}
+    threads = oracle.threads(1 << 30)
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole layer_4k prefill (conv+SiLU+L2 over T={wl.T}, then the fp64 token recurrence over all "
+                      f"{wl.Hv} heads) repeated {len(times)} times ({sum(times):.1f} s); median pass {t:.2f} s. "
+                      f"OpenMP: {threads} threads over tokens in prep, min({threads}, {wl.Hv}) over heads in the "
+                      f"recurrence"}
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_layer_4k.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, per kernel; a
+    kernel's figure is dropped when the library sources changed since."""
+    from hybrid_linear_attention_gated_amd import profiling
+    rec = profiling.read_traffic(TRAFFIC_FILE)
+    if not rec or rec.get("source_sha256") != profiling.source_sha256():
+        return {}
+    return {k[: -len(".traffic_bytes")]: float(v) for k, v in rec.items() if k.endswith(".traffic_bytes")}
+
+
+def copy_calibration(torch, dev):
+    """A plain streaming copy of known size (torch.neg over 512 MiB) for the
+    FETCH_SIZE / WRITE_SIZE calibration of the counter runs."""
+    from hybrid_linear_attention_gated_amd import profiling
+    n = profiling.COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -75,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, stream 512 MiB through one elementwise kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hot path is data-parallel per sequence and per head and this "
@@ -163,14 +201,14 @@ def main():
                        "unit": "TFLOP/s"},
         "decode": {"bound": "hbm", "achieved": dec_b / per["decode"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
     }
+    traffic = measured_traffic()   # HBM bytes per launch from the counter runs, or None
     for n in names:
         kern[n]["ms"] = per[n]
         kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
+        kern[n]["traffic"] = traffic.get(n)
     dominant = max(["prep", "chunk_local", "state_pass"], key=lambda n: per[n])
-    roof = dict(kern[dominant])
+    roof = {key: kern[dominant][key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
-    roof["traffic"] = None
-    roof.pop("ms")
 
     out = {
         "metric": METRIC,
@@ -196,6 +234,8 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out))

@@ -1,0 +1,149 @@
+"""Summaries of rocprofv3 output for the library's kernels.
+
+  python -m hybrid_linear_attention_gated_amd.profiling stats DIR
+      per-kernel launch count and average / min / max duration from a
+      `rocprofv3 --kernel-trace --stats --output-format csv -d DIR` run.
+  python -m hybrid_linear_attention_gated_amd.profiling traffic FETCH_DIR WRITE_DIR
+      HBM bytes per launch from two `rocprofv3 --pmc FETCH_SIZE` and
+      `--pmc WRITE_SIZE` runs of `bench.py --copy-calibration`: each counter is
+      scaled by what it reads for the plain streaming copy of known size that
+      the calibration launches, and the lines end with the SHA-256 of the kernel
+      sources, so a reader can tell when the figures went stale.
+
+Only text is produced; nothing here touches the GPU.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+# kernel symbol fragment -> short name used by bench.py
+KERNELS = [
+    ("prep_kernel", "prep"),
+    ("conv_state_out_kernel", "conv_state_out"),
+    ("chunk_local_kernel", "chunk_local"),
+    ("state_pass_kernel", "state_pass"),
+    ("prefill_recurrent_kernel", "prefill_recurrent"),
+    ("decode_kernel", "decode"),
+]
+# bench.py --copy-calibration streams a buffer through torch.neg (one elementwise
+# kernel that reads and writes COPY_BYTES); host-to-device uploads use blit
+# kernels of other names and are not counted as the calibration copy.
+COPY_NAMES = ("elementwise_kernel",)
+
+
+def short_name(symbol: str) -> str:
+    for frag, short in KERNELS:
+        if frag in symbol:
+            return short
+    for frag in COPY_NAMES:
+        if frag in symbol:
+            return "copy"
+    return symbol[:48]
+
+
+def source_sha256() -> str:
+    """SHA-256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(_CSRC, "*"))):
+        if path.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(os.path.basename(path).encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def _csv_rows(directory: str, suffix: str):
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    return rows
+
+
+def kernel_stats(directory: str) -> dict:
+    """short name -> {calls, avg_us, min_us, max_us} from the kernel trace."""
+    per = defaultdict(list)
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        per[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return {k: {"calls": len(v), "avg_us": sum(v) / len(v), "min_us": min(v), "max_us": max(v)}
+            for k, v in per.items()}
+
+
+def counter_means(directory: str, counter: str) -> dict:
+    """short name -> (dispatches, mean counter value per dispatch)."""
+    per = defaultdict(list)
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            per[short_name(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in per.items()}
+
+
+# The calibration copy moves this many bytes each way (bench.py --copy-calibration).
+COPY_BYTES = 512 << 20
+
+
+def traffic(fetch_dir: str, write_dir: str) -> dict:
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise RuntimeError("calibration copy not found in the counter runs")
+    # counters are in KiB; the factor maps the counter to the copy's known bytes
+    f_fac = COPY_BYTES / (fetch["copy"][1] * 1024.0)
+    w_fac = COPY_BYTES / (write["copy"][1] * 1024.0)
+    out = {"fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
+    known = {short for _, short in KERNELS}
+    for k in fetch:
+        if k not in known or k not in write:
+            continue
+        fb = fetch[k][1] * 1024.0 * f_fac
+        wb = write[k][1] * 1024.0 * w_fac
+        out["kernels"][k] = {"dispatches": fetch[k][0], "fetch_bytes": fb, "write_bytes": wb,
+                             "traffic_bytes": fb + wb}
+    return out
+
+
+def main(argv):
+    if len(argv) >= 2 and argv[0] == "stats":
+        st = kernel_stats(argv[1])
+        print(f"{'kernel':20s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        for k, v in sorted(st.items(), key=lambda kv: -kv[1]["avg_us"] * kv[1]["calls"]):
+            print(f"{k:20s} {v['calls']:6d} {v['avg_us']:10.2f} {v['min_us']:10.2f} {v['max_us']:10.2f}")
+        return 0
+    if len(argv) >= 3 and argv[0] == "traffic":
+        t = traffic(argv[1], argv[2])
+        print(f"fetch_factor = {t['fetch_factor']:.6f}")
+        print(f"write_factor = {t['write_factor']:.6f}")
+        for k, v in sorted(t["kernels"].items()):
+            print(f"{k}.fetch_bytes = {v['fetch_bytes']:.0f}")
+            print(f"{k}.write_bytes = {v['write_bytes']:.0f}")
+            print(f"{k}.traffic_bytes = {v['traffic_bytes']:.0f}")
+        print(f"source_sha256 = {source_sha256()}")
+        return 0
+    print(__doc__, file=sys.stderr)
+    return 2
+
+
+def read_traffic(path: str) -> dict:
+    """Parse the `key = value` lines written by `traffic`; {} when the file is absent."""
+    if not os.path.exists(path):
+        return {}
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if " = " in line and not line.startswith(("#", " ", "|")):
+                key, val = line.split(" = ", 1)
+                out[key.strip()] = val.strip()
+    return out
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
