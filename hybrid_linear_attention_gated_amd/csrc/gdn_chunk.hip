@@ -25,8 +25,8 @@
 //  - in the chunk-local kernel: two-term bf16 splits (hi + lo) of both operands,
 //    three MFMAs per product (K K^T, Q K^T, the block solve, P W, P U);
 //  - in the state pass: fp16 MFMA (11-bit significand) with W, Qt and the state
-//    as single fp16 operands, and K and the decayed Delta as fp16 hi + lo pairs
-//    (three MFMAs for K^T Delta).
+//    as single fp16 operands, and the decayed keys Kd = diag(e^{G_c - G}) K and
+//    Delta as fp16 hi + lo pairs (three MFMAs for Kd^T Delta).
 //    fp16 operands assume |state|, |Delta| < 6.5e4; the fp32 master state is
 //    never rounded.
 //
@@ -34,18 +34,22 @@
 //  chunk_local_kernel: one 4-wave workgroup per (chunk, value head), fully
 //    parallel.  K K^T and Q K^T, the 16x16 diagonal blocks of T by forward
 //    substitution in fp32, W and U by block forward substitution on MFMA (no
-//    explicit T), then Qt and Ol.  Writes W, Qt, K^T as fp16 MFMA A-operand
+//    explicit T), then Qt and Ol.  Writes -W, Qt, Kd^T as fp16 MFMA A-operand
 //    fragments and U, Ol as fp32 accumulator-layout tiles, so the state pass
-//    reads every operand with one coalesced 16-byte load per lane.
+//    reads every operand with one coalesced 16-byte load per lane and every
+//    product accumulates straight into its MFMA chain (U and Ol seed the
+//    Delta and O chains; the per-token decay is already inside Kd).
 //  state_pass_kernel: one workgroup per (sequence, value head, two 16-column
 //    strips of the state); a strip's fp32 state lives in MFMA accumulators for
-//    the whole sequence and the chunk loop runs Delta = U - W S, O = Qt S + Ol,
-//    S = g S + K^T (decay * Delta), with the chunk's A operands double-buffered
-//    in LDS by two copy waves.
+//    the whole sequence and the chunk loop runs Delta = U + (-W) S,
+//    O = Ol + Qt S, S = e^{G_c} S + Kd^T Delta, with the chunk's A operands
+//    double-buffered in LDS by two copy waves.
 //    Accumulator tiles are reused as B operands directly: the k index of an
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
 //    accumulator tiles (kperm).
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -56,14 +60,14 @@ template <int D>
 struct Rec {
     static constexpr int NKS = D / 32;                  // 32-wide k steps over the head dim
     static constexpr int NTD = D / 16;                  // 16-wide tiles over the head dim
-    static constexpr int W_OFF = 0;                     // W   f16 A frags [4 row tiles][NKS][64 lanes][8]
+    static constexpr int W_OFF = 0;                     // -W  f16 A frags [4 row tiles][NKS][64 lanes][8]
     static constexpr int Q_OFF = W_OFF + 64 * D * 2;    // Qt  f16 A frags [4][NKS][64][8]
-    static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // K^T f16 A frags, hi and lo: [2][NTD row tiles][2][64][8]
+    static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // Kd^T f16 A frags, hi and lo: [2][NTD row tiles][2][64][8],
+                                                        //   Kd = diag(e^{G_c - G_t}) K
     static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U   f32 tiles [NTD col tiles][4 row tiles][64][4]
     static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
-    static constexpr int DC_OFF = O_OFF + 64 * D * 4;   // e^{G_c - G_t}, f32 [64]
-    static constexpr int GM_OFF = DC_OFF + 64 * 4;      // e^{G_c}, f32, stored 4 times
-    static constexpr int SIZE = DC_OFF + 1024;          // the decay slot is padded to 1 KiB
+    static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times
+    static constexpr int SIZE = GM_OFF + 256;           // padded to a multiple of 256 bytes
 };
 
 // Wave-parallel: first chunk index of sequence s in the packed chunk list.
@@ -136,7 +140,8 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     __shared__ float Td[4][16][17];
     __shared__ int loc[3];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // wave index in a scalar register: wave-level branches and LDS bases stay uniform
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
     const int gc = blockIdx.x, h = blockIdx.y;
     const int kh = h / (Hv / Hk);
@@ -196,7 +201,6 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         Bs[lane] = bb;
         Eg[lane] = __expf(G);
         Dc[lane] = __expf(Gc - G);
-        reinterpret_cast<float *>(rec + R::DC_OFF)[lane] = __expf(Gc - G);
         if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
     }
     __syncthreads();
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {
                     const int t = 16 * r + 4 * kg + qq;
-                    Wl[t * LD + col] = (f16)X[r][jj][qq];
+                    Wl[t * LD + col] = (f16)(-X[r][jj][qq]);   // stored negated: Delta = U + (-W) S
                     Ql16[t * LD + col] = (f16)Y[r][jj][qq];
                 }
             }
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 #pragma unroll
             for (int vv = 0; vv < 8; ++vv) {
                 const int t = 32 * ks + kperm(kg, vv);
-                const float kv = (float)Kh[t * LD + d] + (float)Kl[t * LD + d];
+                const float kv = Dc[t] * ((float)Kh[t * LD + d] + (float)Kl[t * LD + d]);
                 frag[vv] = (f16)kv;
                 frag_lo[vv] = (f16)(kv - (float)frag[vv]);
             }
@@ -441,9 +445,11 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 // double-buffered, while the compute waves work on the previous chunk: a single
 // wave keeps too few requests in flight to stream a record at memory latency,
 // and a wave with direct-to-LDS loads in flight cannot wait on its own LDS reads
-// precisely.  The compute waves prefetch their strip's U, Ol and decay factors
-// one chunk ahead into registers and read fragments from LDS in groups; the
-// reads of group g + 1 are issued right after the first MFMA of group g.
+// precisely.  The compute waves prefetch their strip's U and Ol tiles one chunk
+// ahead into registers and read fragments from LDS in groups; the reads of group
+// g + 1 are issued right after the first MFMA of group g, and each group runs
+// four independent MFMA chains (a dependent MFMA waits ~44 cycles, one issues
+// every 16).
 template <int D>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
@@ -460,7 +466,8 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const int pair = (b / 8) % NP;
     if (u >= units) return;
     const int s = u / Hv, h = u % Hv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave index in a scalar register (the direct-to-LDS base and offset must be uniform)
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool copier = wave >= 2;
     const int l16 = lane & 15, kg = lane >> 4;
     const int j = 2 * pair + (wave & 1);
@@ -503,140 +510,163 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 #pragma unroll
         for (int m = 0; m < NTD; ++m) S[m] = zero4();
     }
-    f32x4 Uf[4], Of[4], Dcf[4];
+    // this lane's part of the strip's U and Ol tiles (uniform record base + lane offset)
+    const int strip_off = (j * 4 * 64 + lane) * 16;
+    f32x4 Uf[4], Of[4];
     float gm = 0.f;
-    auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, f32x4 *D_, float &g_) {
+    auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, float &g_) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + ((j * 4 + mt) * 64 + lane) * 16);
-            O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + ((j * 4 + mt) * 64 + lane) * 16);
-            D_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::DC_OFF + (16 * mt + 4 * kg) * 4);
+            U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + strip_off + mt * 1024);
+            O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + strip_off + mt * 1024);
         }
         // lane-varying address: a vector load (no scalar load shares lgkmcnt with LDS reads)
         g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
     };
-    if (nc > 0) load_strip(rec_of(0), Uf, Of, Dcf, gm);
+    if (nc > 0) load_strip(rec_of(0), Uf, Of, gm);
+    // Retire the initial state and strip loads here, once.  Left pending into the loop,
+    // the compiler's wait analysis merges them into the loop header and then waits for
+    // every outstanding access (the previous chunk's o stores and this chunk's prefetch)
+    // before the first MFMA of each chunk.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int c = 0; c < nc; ++c) {
+    // o rows of this lane: row 16 mt + 4 kg + qq of the chunk, column col
+    const int row_stride = Hv * D;
+    const int o_lane = 4 * kg * row_stride + l16;
+
+    // Fragment groups read from LDS.  Phase 1 group p: -W and Qt fragments of row tiles
+    // 2p, 2p + 1 (all k steps).  Phase 2 group p: K^T hi and lo fragments of state row
+    // tiles 4p .. 4p + 3 (both k steps).
+    constexpr int NG1 = 2;                 // phase 1 groups
+    constexpr int NG2 = NTD / 4;           // phase 2 groups
+    constexpr int GF = 16;                 // fragments per group (both phases, D = 128)
+    constexpr int GF1 = 4 * NKS;           // phase 1 fragments per group
+    static_assert(GF1 <= GF, "group size");
+    auto read_p1 = [&](const char *A, int p, f16x8 *F) {
+#pragma unroll
+        for (int dm = 0; dm < 2; ++dm)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int mt = 2 * p + dm;
+                F[dm * 2 * NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+                F[dm * 2 * NKS + NKS + ks] =
+                    *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
+            }
+    };
+    auto read_p2 = [&](const char *A, int p, f16x8 *F) {
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int m = 4 * p + dm;
+                F[dm * 4 + ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16);
+                F[dm * 4 + 2 + ks] =
+                    *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((NTD + m) * 2 + ks) * 64 + lane) * 16);
+            }
+    };
+
+    // One chunk step.  Every chunk but a sequence's last is full, so the main loop runs
+    // LAST = false: its next-chunk prefetch and its 16 o stores are unconditional, and the
+    // compiler can wait for the prefetch alone (vmcnt counts the stores issued after it)
+    // instead of for every outstanding access.
+    auto chunk_step = [&](int c, auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
         const char *A = abuf[c & 1];
-        // strip data of the next chunk
-        f32x4 Un[4], On[4], Dn[4];
+        f32x4 Un[4], On[4];
         float gn = 0.f;
-        if (c + 1 < nc) load_strip(rec_of(c + 1), Un, On, Dn, gn);
+        if constexpr (!LAST) load_strip(rec_of(c + 1), Un, On, gn);
         f16x8 Sh[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
 
-        // ---- Delta = U - W S ;  O = Qt S + Ol.  Group mt: W and Qt fragments of row tile mt.
-        f16x8 fa[2][2 * NKS];
-        auto read_wq = [&](int mt, f16x8 *F) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                F[ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                F[NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-            }
-        };
-        // K group: two row tiles m, m + 1 (hi and lo fragments, both k steps) = 8 fragments
-        f16x8 fk[2][8];
-        auto read_k = [&](int m, f16x8 *F) {
-#pragma unroll
-            for (int dm = 0; dm < 2; ++dm)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    F[4 * dm + ks] = *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((m + dm) * 2 + ks) * 64 + lane) * 16);
-                    F[4 * dm + 2 + ks] =
-                        *reinterpret_cast<const f16x8 *>(A + R::K_OFF + (((NTD + m + dm) * 2 + ks) * 64 + lane) * 16);
-                }
-        };
-        read_wq(0, fa[0]);
+        f16x8 fr[2][GF];
+        read_p1(A, 0, fr[0]);
+
+        // ---- Delta = U + (-W) S and O = Ol + Qt S: four independent accumulation chains
+        // per group (Delta and O of two row tiles), each one MFMA per k step
         f32x4 Dl[4], Ot[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const f16x8 *F = fa[mt & 1];
-            f32x4 acc = mfma16(F[0], Sh[0], zero4());
+        for (int p = 0; p < NG1; ++p) {
+            const f16x8 *F = fr[p & 1];
+            f32x4 d0 = mfma16(F[0], Sh[0], Uf[2 * p]);
             __builtin_amdgcn_sched_barrier(0);
-            if (mt + 1 < 4) read_wq(mt + 1, fa[(mt + 1) & 1]);
-            else read_k(0, fk[0]);
+            if (p + 1 < NG1) read_p1(A, p + 1, fr[(p + 1) & 1]);
+            else read_p2(A, 0, fr[(p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            // four independent accumulation chains (a dependent MFMA waits ~44 cycles,
-            // one issues every 16): even / odd k steps of W S and of Qt S
-            f32x4 oacc = mfma16(F[NKS], Sh[0], Of[mt]);
-            f32x4 acc1 = mfma16(F[1], Sh[1], zero4());
-            f32x4 oacc1 = mfma16(F[NKS + 1], Sh[1], zero4());
+            f32x4 o0 = mfma16(F[NKS], Sh[0], Of[2 * p]);
+            f32x4 d1 = mfma16(F[2 * NKS], Sh[0], Uf[2 * p + 1]);
+            f32x4 o1 = mfma16(F[3 * NKS], Sh[0], Of[2 * p + 1]);
 #pragma unroll
-            for (int ks = 2; ks < NKS; ks += 2) {
-                acc = mfma16(F[ks], Sh[ks], acc);
-                oacc = mfma16(F[NKS + ks], Sh[ks], oacc);
-                acc1 = mfma16(F[ks + 1], Sh[ks + 1], acc1);
-                oacc1 = mfma16(F[NKS + ks + 1], Sh[ks + 1], oacc1);
+            for (int ks = 1; ks < NKS; ++ks) {
+                d0 = mfma16(F[ks], Sh[ks], d0);
+                o0 = mfma16(F[NKS + ks], Sh[ks], o0);
+                d1 = mfma16(F[2 * NKS + ks], Sh[ks], d1);
+                o1 = mfma16(F[3 * NKS + ks], Sh[ks], o1);
             }
-            Dl[mt] = Uf[mt] - (acc + acc1);
-            Ot[mt] = oacc + oacc1;
+            Dl[2 * p] = d0; Dl[2 * p + 1] = d1;
+            Ot[2 * p] = o0; Ot[2 * p + 1] = o1;
         }
 
-        // ---- S = gamma S + K^T (decay * Delta), K and the decayed Delta as fp16 hi + lo pairs
+        // ---- S = gamma S + Kd^T Delta with Kd = diag(e^{G_c - G_t}) K; Kd and Delta as
+        // fp16 hi + lo pairs (the lo x lo term is dropped): one six-MFMA chain per state
+        // row tile, four tiles interleaved per group
         f16x8 Dh[2], Dlo[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const f32x4 d0 = Dl[2 * ks] * Dcf[2 * ks], d1 = Dl[2 * ks + 1] * Dcf[2 * ks + 1];
-            Dh[ks] = pack_h(d0, d1);
+            Dh[ks] = pack_h(Dl[2 * ks], Dl[2 * ks + 1]);
             f32x4 r0, r1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                r0[e] = d0[e] - (float)Dh[ks][e];
-                r1[e] = d1[e] - (float)Dh[ks][4 + e];
+                r0[e] = Dl[2 * ks][e] - (float)Dh[ks][e];
+                r1[e] = Dl[2 * ks + 1][e] - (float)Dh[ks][4 + e];
             }
             Dlo[ks] = pack_h(r0, r1);
         }
 #pragma unroll
-        for (int m = 0; m < NTD; m += 2) {
-            const f16x8 *F = fk[(m / 2) & 1];
-            f32x4 a0 = mfma16(F[0], Dh[0], S[m] * gm);
+        for (int p = 0; p < NG2; ++p) {
+            const f16x8 *F = fr[(NG1 + p) & 1];
+            f32x4 a[4];
+            a[0] = mfma16(F[0], Dh[0], S[4 * p] * gm);
             __builtin_amdgcn_sched_barrier(0);
-            if (m + 2 < NTD) read_k(m + 2, fk[((m / 2) + 1) & 1]);
+            if (p + 1 < NG2) read_p2(A, p + 1, fr[(NG1 + p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            // row tiles m and m + 1, each as two partial sums: four independent chains
-            f32x4 a1 = mfma16(F[4], Dh[0], S[m + 1] * gm);
-            f32x4 b0 = mfma16(F[0], Dlo[0], zero4());
-            f32x4 b1 = mfma16(F[4], Dlo[0], zero4());
-            a0 = mfma16(F[1], Dh[1], a0);
-            a1 = mfma16(F[5], Dh[1], a1);
-            b0 = mfma16(F[1], Dlo[1], b0);
-            b1 = mfma16(F[5], Dlo[1], b1);
-            a0 = mfma16(F[2], Dh[0], a0);
-            a1 = mfma16(F[6], Dh[0], a1);
-            b0 = mfma16(F[3], Dh[1], b0);
-            b1 = mfma16(F[7], Dh[1], b1);
-            S[m] = a0 + b0;
-            S[m + 1] = a1 + b1;
+#pragma unroll
+            for (int dm = 1; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm], Dh[0], S[4 * p + dm] * gm);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 1], Dh[1], a[dm]);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm], Dlo[0], a[dm]);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 1], Dlo[1], a[dm]);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 2], Dh[0], a[dm]);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 3], Dh[1], a[dm]);
+#pragma unroll
+            for (int dm = 0; dm < 4; ++dm) S[4 * p + dm] = a[dm];
         }
 
-        // ---- this chunk's outputs
+        // ---- this chunk's outputs: uniform row base, per-lane 32-bit offsets
         const int tb = t0 + c * kChunk;
+        float *ob = o + ((size_t)tb * Hv + h) * D + 16 * j;
         const int rows = min(kChunk, L - c * kChunk);
-        float *ob = o + ((size_t)tb * Hv + h) * D + col;
-        if (rows == kChunk) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) ob[(size_t)(16 * mt + 4 * kg + qq) * Hv * D] = Ot[mt][qq];
-        } else {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int r = 16 * mt + 4 * kg + qq;
-                    if (r < rows) ob[(size_t)r * Hv * D] = Ot[mt][qq];
-                }
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // next chunk's strip data has landed
+            for (int qq = 0; qq < 4; ++qq) {
+                const int r = 16 * mt + 4 * kg + qq;
+                if (!LAST || r < rows) ob[o_lane + (16 * mt + qq) * row_stride] = Ot[mt][qq];
+            }
         __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
+        if constexpr (!LAST) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; Dcf[mt] = Dn[mt]; }
-        gm = gn;
-    }
+            for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; }
+            gm = gn;
+        }
+    };
+    for (int c = 0; c + 1 < nc; ++c) chunk_step(c, std::false_type{});
+    if (nc > 0) chunk_step(nc - 1, std::true_type{});
     if (sf) {
 #pragma unroll
         for (int m = 0; m < NTD; ++m)
