@@ -117,297 +117,449 @@ __device__ __forceinline__ bool locate_chunk_wave(const int32_t *cu, int N, int 
 
 // ============================================================== chunk-local
 
+// Index of block (c, r), c <= r, in a packed upper triangle of 4 x 4 blocks.
+__host__ __device__ constexpr int tri_idx(int c, int r) { return r * (r + 1) / 2 + c; }
+// Index of block (k, c), k > c, in a packed strict lower triangle of 4 x 4 blocks.
+__host__ __device__ constexpr int stri_idx(int k, int c) { return k * (k - 1) / 2 + c; }
+
+// An A or B operand that holds one 16 x 16 block (k < 16): the four values of
+// this lane in the low half, zeros in the high half (see kperm).
+__device__ __forceinline__ Split8 split_block(f32x4 x) { return split_tiles(x, zero4()); }
+__device__ __forceinline__ Split8 block_operand(bf16x4 hi, bf16x4 lo) {
+    Split8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.hi[i] = hi[i]; r.lo[i] = lo[i];
+        r.hi[4 + i] = (bf16)0.f; r.lo[4 + i] = (bf16)0.f;
+    }
+    return r;
+}
+__device__ __forceinline__ Split8 neg_split(Split8 s) { return Split8{-s.hi, -s.lo}; }
+__device__ __forceinline__ void split_store(f32x4 x, bf16x4 *hi, bf16x4 *lo) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = (bf16)x[i];
+        l[i] = (bf16)(x[i] - (float)h[i]);
+    }
+    *hi = h;
+    *lo = l;
+}
+
+// LDS layout of the chunk-local kernel (bytes).
+template <int D>
+struct LocalSmem {
+    static constexpr int LD = D + 8;                         // bf16 row stride of the K / Q planes
+    static constexpr int PLANE = 64 * LD * 2;
+    static constexpr int KH = 0, KL = PLANE, QH = 2 * PLANE, QL = 3 * PLANE;
+    static constexpr int SCR = 0;                            // after the tile phase: per-wave solve scratch
+    static constexpr int SCR_LANE = 20;                      //   floats per column (padded)
+    static constexpr int SCR_WAVE = 4 * 16 * SCR_LANE * 4;
+    static constexpr int ADIAG = 4 * PLANE;                  // diagonal blocks of A, row-major fp32
+    static constexpr int ADIAG_BLK = 16 * 16 + 4;            //   floats per block (padded)
+    static constexpr int AOFF = ADIAG + 4 * ADIAG_BLK * 4;   // strict-lower blocks of A: [6][hi, lo][64] bf16x4
+    static constexpr int PT = AOFF + 6 * 2 * 64 * 8;         // P^T blocks c <= r: [10][64] f32x4
+    static constexpr int XT = PT + 10 * 64 * 16;             // T^T and M^T blocks c <= r: [2][10][hi, lo][64] bf16x4
+    static constexpr int SCAL = XT + 2 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^G, e^{G_c - G}, scale e^G
+    static constexpr int SIZE = SCAL + 5 * 64 * 4;
+    static_assert(4 * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
+};
+
+// One 4-wave workgroup per (chunk, value head), fully parallel over chunks.
+// The chunk form is evaluated with explicit T = (I + A)^-1 and M = P T:
+//   W = T diag(b e^G) K,  U = T diag(b) V,  Qt = diag(e^G) Q - M diag(b e^G) K,  Ol = M diag(b) V.
+// Every MFMA output lands in the layout its consumer wants, so nothing is
+// transposed through LDS element by element:
+//  1. K K^T row block w and K Q^T row block w (wave w; key block w is the A
+//     operand of all five tiles) -> A (strict lower) and P^T, scaled by the
+//     decays; K K^T is symmetric, so A's accumulator tile (k, c) is also the
+//     A-operand form of A^T block (c, k).
+//  2. Every wave solves the four 16 x 16 diagonal blocks T_cc by forward
+//     substitution (lane (c, j) owns column j of block c), so no barrier.
+//  3. Block back substitution of (I + A^T) X = [I | P^T] gives T^T and M^T in
+//     accumulator layout (wave w: column block 3 - w of T^T, column block w
+//     of M^T), which is the operand form every product below needs.
+//  4. Waves 0, 1 (head-dim halves): W^T = (diag(b e^G) K)^T T^T and
+//     Qt^T = (diag(e^G) Q)^T - (diag(b e^G) K)^T M^T; in accumulator layout
+//     these are exactly the state pass's A-operand fragments of -W and Qt.
+//     Waves 2, 3 (value-dim halves): U = T diag(b) V and Ol = M diag(b) V.
+// Products use two-term bf16 splits of both operands (three MFMAs each).
 template <int D>
 __global__ __launch_bounds__(256) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax) {
     using R = Rec<D>;
-    constexpr int NKS = R::NKS, NTD = R::NTD;
-    constexpr int LD = D + 8;    // row stride (elements) of the 64 x D 16-bit LDS tiles
-    constexpr int LA = 64 + 4;   // fp32 row stride of A
-    constexpr int LP = 64 + 8;   // bf16 row stride of P
-    constexpr int TPW = NTD / 2; // accumulator column tiles per wave in the solve
-
-    __shared__ __attribute__((aligned(16))) bf16 Kh[64 * LD];
-    __shared__ __attribute__((aligned(16))) bf16 Kl[64 * LD];
-    __shared__ __attribute__((aligned(16))) bf16 Qh[64 * LD];   // later: W staging (f16)
-    __shared__ __attribute__((aligned(16))) bf16 Ql[64 * LD];   // later: Qt staging (f16)
-    __shared__ __attribute__((aligned(16))) float As[64 * LA];
-    __shared__ __attribute__((aligned(16))) bf16 Ph[64 * LP];
-    __shared__ __attribute__((aligned(16))) bf16 Pl[64 * LP];
-    __shared__ float Gs[64], Bs[64], Eg[64], Dc[64];
-    __shared__ float Td[4][16][17];
-    __shared__ int loc[3];
+    using SM = LocalSmem<D>;
+    constexpr int NKS = D / 32;   // 32-wide k steps over the head dim
+    constexpr int NM = D / 32;    // 16-wide head-dim tiles per W / U wave
+    constexpr int LD = SM::LD;
+    constexpr int NF_K = (D / 16) * 2;
+    __shared__ __attribute__((aligned(16))) char smem[SM::SIZE];
+    bf16 *Kh = reinterpret_cast<bf16 *>(smem + SM::KH);
+    bf16 *Kl = reinterpret_cast<bf16 *>(smem + SM::KL);
+    bf16 *Qh = reinterpret_cast<bf16 *>(smem + SM::QH);
+    bf16 *Ql = reinterpret_cast<bf16 *>(smem + SM::QL);
+    float *Adiag = reinterpret_cast<float *>(smem + SM::ADIAG);
+    bf16x4 *Aoff = reinterpret_cast<bf16x4 *>(smem + SM::AOFF);     // [6][2][64]
+    f32x4 *Pt = reinterpret_cast<f32x4 *>(smem + SM::PT);           // [10][64]
+    bf16x4 *Xt = reinterpret_cast<bf16x4 *>(smem + SM::XT);         // [2][10][2][64]
+    float *Gs = reinterpret_cast<float *>(smem + SM::SCAL);
+    float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256;
 
     // wave index in a scalar register: wave-level branches and LDS bases stay uniform
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
     const int gc = blockIdx.x, h = blockIdx.y;
     const int kh = h / (Hv / Hk);
+    const bool isW = wave < 2;
 
-    if (wave == 0) {
-        int s, c;
-        const bool ok = locate_chunk_wave(cu, N, Ttot, gc, s, c);
-        if (lane == 0) {
-            loc[0] = ok ? 1 : 0;
-            if (ok) {
-                loc[1] = seq_begin(cu, s) + c * kChunk;
-                loc[2] = min(kChunk, seq_end(cu, s, Ttot) - loc[1]);
-            }
-        }
-    }
-    __syncthreads();
-    if (!loc[0]) return;
-    const int t0 = loc[1], L = loc[2];
+    // ---- where this chunk lives (every wave finds the same answer; no barrier)
+    int s_, c_;
+    if (!locate_chunk_wave(cu, N, Ttot, gc, s_, c_)) return;
+    const int t0 = __builtin_amdgcn_readfirstlane(seq_begin(cu, s_) + c_ * kChunk);
+    const int L = __builtin_amdgcn_readfirstlane(min(kChunk, seq_end(cu, s_, Ttot) - t0));
     char *rec = ws + ((size_t)h * ncmax + gc) * R::SIZE;   // head-major: a head's chunks are contiguous
 
-    // ---- K and Q (key head kh) as bf16 hi/lo planes; rows >= L are zero
+    // ---- global loads, all issued before any is used.  Rows >= L are clamped
+    // (loads stay in bounds and unconditional) and zeroed.
+    constexpr int NV = 64 * (D / 4) / 256;
+    float4 kv[NV], qv[NV];
 #pragma unroll
-    for (int e = tid; e < 64 * (D / 4); e += 256) {
-        const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-        const int rr = min(r, L - 1);   // clamped row: loads stay unconditional, padded rows are zeroed
-        const float4 kv0 = *reinterpret_cast<const float4 *>(k + ((size_t)(t0 + rr) * Hk + kh) * D + c4);
-        const float4 qv0 = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + rr) * Hk + kh) * D + c4);
-        const bool live = r < L;
-        const float kk[4] = {live ? kv0.x : 0.f, live ? kv0.y : 0.f, live ? kv0.z : 0.f, live ? kv0.w : 0.f};
-        const float qq[4] = {live ? qv0.x : 0.f, live ? qv0.y : 0.f, live ? qv0.z : 0.f, live ? qv0.w : 0.f};
-        bf16x4 khi, klo, qhi, qlo;
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + 256 * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        const size_t off = ((size_t)(t0 + min(r, L - 1)) * Hk + kh) * D + c4;
+        kv[i] = *reinterpret_cast<const float4 *>(k + off);
+        qv[i] = *reinterpret_cast<const float4 *>(q + off);
+    }
+    // W waves: Q^T in accumulator layout (rows = head dim, cols = token) seeds Qt^T.
+    // U waves: V in accumulator layout (rows = token) feeds U and Ol.
+    f32x4 Xa[NM][4];
+    const int half = isW ? wave : wave - 2;
+    if (isW) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            khi[i] = (bf16)kk[i]; klo[i] = (bf16)(kk[i] - (float)khi[i]);
-            qhi[i] = (bf16)qq[i]; qlo[i] = (bf16)(qq[i] - (float)qhi[i]);
-        }
-        *reinterpret_cast<bf16x4 *>(Kh + r * LD + c4) = khi;
-        *reinterpret_cast<bf16x4 *>(Kl + r * LD + c4) = klo;
-        *reinterpret_cast<bf16x4 *>(Qh + r * LD + c4) = qhi;
-        *reinterpret_cast<bf16x4 *>(Ql + r * LD + c4) = qlo;
+        for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = 16 * tt + l16, d = 16 * (NM * half + mi) + 4 * kg;
+                const float4 x = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + min(t, L - 1)) * Hk + kh) * D + d);
+                Xa[mi][tt] = t < L ? f32x4{x.x, x.y, x.z, x.w} : zero4();
+            }
+    } else {
+#pragma unroll
+        for (int ni = 0; ni < NM; ++ni)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * rt + 4 * kg + r, col = 16 * (NM * half + ni) + l16;
+                    const float x = v[((size_t)(t0 + min(t, L - 1)) * Hv + h) * D + col];
+                    Xa[ni][rt][r] = t < L ? x : 0.f;
+                }
     }
     if (wave == 0) {
-        float gg = 0.f, bb = 0.f;
-        {
-            const int rr = min(lane, L - 1);
-            const float g0 = g[(size_t)(t0 + rr) * Hv + h], b0 = beta[(size_t)(t0 + rr) * Hv + h];
-            gg = lane < L ? g0 : 0.f;
-            bb = lane < L ? b0 : 0.f;
-        }
+        const int rr = min(lane, L - 1);
+        const float g0 = g[(size_t)(t0 + rr) * Hv + h], b0 = beta[(size_t)(t0 + rr) * Hv + h];
+        const float gg = lane < L ? g0 : 0.f, bb = lane < L ? b0 : 0.f;
         float G = gg;   // inclusive prefix sum over the chunk
         for (int o = 1; o < 64; o <<= 1) {
             const float y = __shfl_up(G, o, kWave);
             if (lane >= o) G += y;
         }
         const float Gc = __shfl(G, 63, kWave);
+        const float eg = __expf(G);
         Gs[lane] = G;
         Bs[lane] = bb;
-        Eg[lane] = __expf(G);
-        Dc[lane] = __expf(Gc - G);
+        BEG[lane] = bb * eg;
+        DCs[lane] = __expf(Gc - G);
+        QS[lane] = scale * eg;
         if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
     }
-    __syncthreads();
-
-    // ---- K K^T and Q K^T, lower triangle by 16x16 tiles; wave w owns row tile w
-    {
-        const int r = wave;
-        const int row = 16 * r + l16;
-        for (int c = 0; c < 4; ++c) {
-            const int i = 16 * c + l16;
-            if (c <= r) {
-                f32x4 akk = zero4(), aqk = zero4();
+    // K and Q as bf16 hi / lo planes, row-major [token][head dim]
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off_a = row * LD + 32 * ks + 8 * kg, off_b = i * LD + 32 * ks + 8 * kg;
-                    const Split8 ka{*reinterpret_cast<const bf16x8 *>(Kh + off_a), *reinterpret_cast<const bf16x8 *>(Kl + off_a)};
-                    const Split8 qa{*reinterpret_cast<const bf16x8 *>(Qh + off_a), *reinterpret_cast<const bf16x8 *>(Ql + off_a)};
-                    const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off_b), *reinterpret_cast<const bf16x8 *>(Kl + off_b)};
-                    akk = mfma16x3(ka, kb, akk);
-                    aqk = mfma16x3(qa, kb, aqk);
-                }
+    for (int i = 0; i < NV; ++i) {
+        const int e = tid + 256 * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        const bool live = r < L;
+        const float kk[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+        const float qq[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
+        bf16x4 khi, klo, qhi, qlo;
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int t = 16 * r + 4 * kg + qq;
-                    const float dec = __expf(Gs[t] - Gs[min(i, t)]);
-                    As[t * LA + i] = (i < t) ? Bs[t] * dec * akk[qq] : 0.f;
-                    const float p = (i <= t) ? scale * dec * aqk[qq] : 0.f;
-                    const bf16 ph = (bf16)p;
-                    Ph[t * LP + i] = ph;
-                    Pl[t * LP + i] = (bf16)(p - (float)ph);
-                }
-            } else {
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int t = 16 * r + 4 * kg + qq;
-                    As[t * LA + i] = 0.f;
-                    Ph[t * LP + i] = (bf16)0.f;
-                    Pl[t * LP + i] = (bf16)0.f;
-                }
-            }
+        for (int j = 0; j < 4; ++j) {
+            const float a = live ? kk[j] : 0.f, b = live ? qq[j] : 0.f;
+            khi[j] = (bf16)a; klo[j] = (bf16)(a - (float)khi[j]);
+            qhi[j] = (bf16)b; qlo[j] = (bf16)(b - (float)qhi[j]);
         }
+        *reinterpret_cast<bf16x4 *>(Kh + r * LD + c4) = khi;
+        *reinterpret_cast<bf16x4 *>(Kl + r * LD + c4) = klo;
+        *reinterpret_cast<bf16x4 *>(Qh + r * LD + c4) = qhi;
+        *reinterpret_cast<bf16x4 *>(Ql + r * LD + c4) = qlo;
     }
     __syncthreads();
 
-    // ---- diagonal 16x16 blocks of T = (I + A)^-1 by forward substitution (fp32)
-    if (lane < 16) {
-        const int r = wave, j = lane;
+    // ---- 1. key block w against every block: K K^T (w, c <= w) and K Q^T (w, r >= w)
+    {
+        Split8 ka[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int off = (16 * wave + l16) * LD + 32 * ks + 8 * kg;
+            ka[ks] = Split8{*reinterpret_cast<const bf16x8 *>(Kh + off), *reinterpret_cast<const bf16x8 *>(Kl + off)};
+        }
+        // decay scalars of this lane's rows (block w) and column
+        const f32x4 Gw = *reinterpret_cast<const f32x4 *>(Gs + 16 * wave + 4 * kg);
+        const f32x4 Bw = *reinterpret_cast<const f32x4 *>(Bs + 16 * wave + 4 * kg);
+        for (int c = 0; c <= wave; ++c) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (16 * c + l16) * LD + 32 * ks + 8 * kg;
+                const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off), *reinterpret_cast<const bf16x8 *>(Kl + off)};
+                acc = mfma16x3(ka[ks], kb, acc);
+            }
+            // A[t][i] = b_t e^{G_t - G_i} k_t . k_i for i < t; t = 16w + 4kg + r, i = 16c + l16
+            const int i = 16 * c + l16;
+            const float Gi = Gs[i];
+            f32x4 a;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * wave + 4 * kg + r;
+                a[r] = i < t ? Bw[r] * __expf(Gw[r] - Gi) * acc[r] : 0.f;
+            }
+            if (c == wave) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Adiag[c * SM::ADIAG_BLK + (4 * kg + r) * 16 + l16] = a[r];
+            } else {
+                const int b = stri_idx(wave, c);
+                split_store(a, &Aoff[(b * 2 + 0) * 64 + lane], &Aoff[(b * 2 + 1) * 64 + lane]);
+            }
+        }
+        for (int r = wave; r < 4; ++r) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (16 * r + l16) * LD + 32 * ks + 8 * kg;
+                const Split8 qb{*reinterpret_cast<const bf16x8 *>(Qh + off), *reinterpret_cast<const bf16x8 *>(Ql + off)};
+                acc = mfma16x3(ka[ks], qb, acc);
+            }
+            // P^T[i][t] = scale e^{G_t - G_i} q_t . k_i for i <= t; i = 16w + 4kg + r, t = 16r' + l16
+            const int t = 16 * r + l16;
+            const float Gt = Gs[t];
+            f32x4 p;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 16 * wave + 4 * kg + rr;
+                p[rr] = i <= t ? scale * __expf(Gt - Gw[rr]) * acc[rr] : 0.f;
+            }
+            Pt[tri_idx(wave, r) * 64 + lane] = p;
+        }
+    }
+
+    // W waves: K^T fragments (A-operand form: lane row = head dim, k = token in kperm
+    // order) from the planes; the decayed copy goes to the record for the state
+    // pass, the (b e^G)-scaled copy stays as this wave's A operand of step 4.
+    Split8 Bop[NM][2];
+    if (isW) {
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+            const int m = NM * half + mi;
+            const int d = 16 * m + l16;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                float bw[8];
+                f16x8 hi, lo;
+#pragma unroll
+                for (int vv = 0; vv < 8; ++vv) {
+                    const int t = 32 * ks + kperm(kg, vv);
+                    const float kvv = (float)Kh[t * LD + d] + (float)Kl[t * LD + d];
+                    const float kd = DCs[t] * kvv;
+                    hi[vv] = (f16)kd;
+                    lo[vv] = (f16)(kd - (float)hi[vv]);
+                    bw[vv] = BEG[t] * kvv;
+                }
+                const int off = R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16;
+                *reinterpret_cast<f16x8 *>(rec + off) = hi;
+                *reinterpret_cast<f16x8 *>(rec + off + NF_K * 64 * 16) = lo;
+                Bop[mi][ks] = split8(bw);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const float qs = QS[16 * tt + l16];
+                Xa[mi][tt] = Xa[mi][tt] * qs;   // Qt^T seed: scale e^{G_t} Q^T
+            }
+        }
+    } else {
+        // U waves: diag(b) V as B operands (k = token in kperm order), two k steps
+#pragma unroll
+        for (int ni = 0; ni < NM; ++ni)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(Bs + 32 * ks + 4 * kg);
+                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(Bs + 32 * ks + 16 + 4 * kg);
+                Bop[ni][ks] = split_tiles(Xa[ni][2 * ks] * b0, Xa[ni][2 * ks + 1] * b1);
+            }
+    }
+    __syncthreads();
+
+    // ---- 2. diagonal blocks T_cc = (I + A_cc)^-1 by forward substitution; lane (c, j)
+    // computes column j of block c, then the columns are regrouped into accumulator
+    // layout through this wave's scratch (lane (kg, l16) gets rows 4kg..4kg+3).
+    Split8 Tcc[4];   // A-operand form of T_cc^T (= accumulator layout of T_cc)
+    {
+        const int c = kg, j = l16;
+        const float *Ab = Adiag + c * SM::ADIAG_BLK;
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            float acc = (t == j) ? 1.f : 0.f;
+            float s0 = (t == j) ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < t; ++i) acc = fmaf(-As[(16 * r + t) * LA + 16 * r + i], x[i], acc);
-            x[t] = acc;
+            for (int i4 = 0; i4 < t; i4 += 4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(Ab + t * 16 + i4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (i4 + e < t) {
+                        if (e & 1) s1 = fmaf(-a[e], x[i4 + e], s1);
+                        else s0 = fmaf(-a[e], x[i4 + e], s0);
+                    }
+            }
+            x[t] = s0 + s1;
+        }
+        float *scr = reinterpret_cast<float *>(smem + SM::SCR + wave * SM::SCR_WAVE);
+#pragma unroll
+        for (int t4 = 0; t4 < 16; t4 += 4)
+            *reinterpret_cast<f32x4 *>(scr + (c * 16 + j) * SM::SCR_LANE + t4) =
+                f32x4{x[t4], x[t4 + 1], x[t4 + 2], x[t4 + 3]};
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's scratch writes are done
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+            Tcc[cc] = split_block(*reinterpret_cast<const f32x4 *>(scr + (cc * 16 + l16) * SM::SCR_LANE + 4 * kg));
+    }
+
+    // ---- 3. back substitution (I + A^T) X = [I | P^T], column block by column block:
+    //   X_cr = T_cc^T (RHS_cr - sum_{k = c+1..r} (A^T)_ck X_kr),  c = r, r-1, .., 0
+    // wave w: column block 3 - w of T^T (RHS = I) and column block w of M^T (RHS = P^T).
+    auto aT = [&](int kk, int c) {   // A-operand form of (A^T)_{c,kk}: accumulator tile (kk, c) of A
+        const int b = stri_idx(kk, c);
+        return block_operand(Aoff[(b * 2 + 0) * 64 + lane], Aoff[(b * 2 + 1) * 64 + lane]);
+    };
+    auto publish = [&](int mat, int c, int r, f32x4 x) {
+        const int b = (mat * 10 + tri_idx(c, r)) * 2;
+        split_store(x, &Xt[(b + 0) * 64 + lane], &Xt[(b + 1) * 64 + lane]);
+    };
+    auto solve_T = [&](auto rtag) {
+        constexpr int r = decltype(rtag)::value;
+        f32x4 X[4];
+        bf16x8 eye;
+#pragma unroll
+        for (int vv = 0; vv < 8; ++vv) eye[vv] = (bf16)((vv < 4 && 4 * kg + vv == l16) ? 1.f : 0.f);
+        X[r] = mfma16(Tcc[r].lo, eye, mfma16(Tcc[r].hi, eye, zero4()));   // T_rr^T
+#pragma unroll
+        for (int c = r - 1; c >= 0; --c) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = c + 1; kk <= r; ++kk) acc = mfma16x3(aT(kk, c), split_block(X[kk]), acc);
+            X[c] = -mfma16x3(Tcc[c], split_block(acc), zero4());
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Td[r][t][j] = x[t];
+        for (int c = 0; c <= r; ++c) publish(0, c, r, X[c]);
+    };
+    auto solve_M = [&](auto rtag) {
+        constexpr int r = decltype(rtag)::value;
+        f32x4 X[4];
+#pragma unroll
+        for (int c = r; c >= 0; --c) {
+            f32x4 acc = Pt[tri_idx(c, r) * 64 + lane];
+#pragma unroll
+            for (int kk = c + 1; kk <= r; ++kk) acc = mfma16x3(neg_split(aT(kk, c)), split_block(X[kk]), acc);
+            X[c] = mfma16x3(Tcc[c], split_block(acc), zero4());
+        }
+#pragma unroll
+        for (int c = 0; c <= r; ++c) publish(1, c, r, X[c]);
+    };
+    switch (wave) {
+    case 0: solve_T(std::integral_constant<int, 3>{}); solve_M(std::integral_constant<int, 0>{}); break;
+    case 1: solve_T(std::integral_constant<int, 2>{}); solve_M(std::integral_constant<int, 1>{}); break;
+    case 2: solve_T(std::integral_constant<int, 1>{}); solve_M(std::integral_constant<int, 2>{}); break;
+    default: solve_T(std::integral_constant<int, 0>{}); solve_M(std::integral_constant<int, 3>{}); break;
     }
     __syncthreads();
 
-    // ---- X = (I + A)^-1 [diag(b e^G) K | diag(b) V] by block forward substitution.
-    // Waves 0,1 own W column tiles, waves 2,3 own U column tiles (TPW each).
-    const bool isW = wave < 2;
-    const int tile0 = (wave & 1) * TPW;
-    // U waves: their V columns for all 64 rows, loaded up front (clamped rows, no branches)
-    float Vr[4][TPW][4];
-    if (!isW) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int t = 16 * r + 4 * kg + qq;
-                    Vr[r][jj][qq] = v[((size_t)(t0 + min(t, L - 1)) * Hv + h) * D + 16 * (tile0 + jj) + l16];
-                }
-    }
-    f32x4 X[4][TPW];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        f32x4 acc[TPW];
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) {
-            const int col = 16 * (tile0 + jj) + l16;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int t = 16 * r + 4 * kg + qq;
-                // Bs[t] = 0 on padded rows
-                acc[jj][qq] = isW ? Bs[t] * Eg[t] * ((float)Kh[t * LD + col] + (float)Kl[t * LD + col])
-                                  : Bs[t] * Vr[r][jj][qq];
-            }
-        }
-#pragma unroll
-        for (int ks = 0; 2 * ks < r; ++ks) {
-            float a[8];
-#pragma unroll
-            for (int vv = 0; vv < 8; ++vv) {
-                const int i = 32 * ks + kperm(kg, vv);
-                a[vv] = (i < 16 * r) ? -As[(16 * r + l16) * LA + i] : 0.f;
-            }
-            const Split8 as = split8(a);
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj) {
-                const f32x4 hi = (2 * ks + 1 < r) ? X[2 * ks + 1][jj] : zero4();
-                acc[jj] = mfma16x3(as, split_tiles(X[2 * ks][jj], hi), acc[jj]);
-            }
-        }
-        float ta[8];
-#pragma unroll
-        for (int vv = 0; vv < 8; ++vv) ta[vv] = vv < 4 ? Td[r][l16][4 * kg + vv] : 0.f;
-        const Split8 ts = split8(ta);
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) X[r][jj] = mfma16x3(ts, split_tiles(acc[jj], zero4()), zero4());
-    }
-
-    // ---- Qt = diag(e^G) scale Q - P W  (W waves),  Ol = P U  (U waves)
-    f32x4 Y[4][TPW];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int jj = 0; jj < TPW; ++jj) {
-            const int col = 16 * (tile0 + jj) + l16;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int t = 16 * r + 4 * kg + qq;
-                Y[r][jj][qq] = isW ? Eg[t] * scale * ((float)Qh[t * LD + col] + (float)Ql[t * LD + col]) : 0.f;
-            }
-        }
-#pragma unroll
-        for (int ks = 0; ks <= r / 2; ++ks) {
-            Split8 pa;
-#pragma unroll
-            for (int vv = 0; vv < 8; ++vv) {
-                const int idx = (16 * r + l16) * LP + 32 * ks + kperm(kg, vv);
-                const bf16 ph = Ph[idx], pl = Pl[idx];
-                pa.hi[vv] = isW ? -ph : ph;
-                pa.lo[vv] = isW ? -pl : pl;
-            }
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj)
-                Y[r][jj] = mfma16x3(pa, split_tiles(X[2 * ks][jj], X[2 * ks + 1][jj]), Y[r][jj]);
-        }
-    }
-
-    if (!isW) {
-        // U and Ol as fp32 accumulator-layout tiles: [col tile][row tile][lane][4]
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj) {
-                const int nt = tile0 + jj;
-                *reinterpret_cast<f32x4 *>(rec + R::U_OFF + (((nt * 4 + r) * 64 + lane) * 4) * 4) = X[r][jj];
-                *reinterpret_cast<f32x4 *>(rec + R::O_OFF + (((nt * 4 + r) * 64 + lane) * 4) * 4) = Y[r][jj];
-            }
-        }
-    }
-    __syncthreads();   // every wave is done reading Qh / Ql
-    f16 *Wl = reinterpret_cast<f16 *>(Qh);
-    f16 *Ql16 = reinterpret_cast<f16 *>(Ql);
-    if (isW) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int jj = 0; jj < TPW; ++jj) {
-                const int col = 16 * (tile0 + jj) + l16;
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int t = 16 * r + 4 * kg + qq;
-                    Wl[t * LD + col] = (f16)(-X[r][jj][qq]);   // stored negated: Delta = U + (-W) S
-                    Ql16[t * LD + col] = (f16)Y[r][jj][qq];
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- fp16 A-operand fragments: W and Qt (k = head dim), K^T hi and lo (k = token)
-    constexpr int NF_W = 4 * NKS;
-    constexpr int NF_K = NTD * 2;
-    for (int f = wave; f < 2 * NF_W + NF_K; f += 4) {
-        f16x8 frag, frag_lo;
-        int off;
-        if (f < 2 * NF_W) {
-            const f16 *Sm = f < NF_W ? Wl : Ql16;
-            const int ff = f < NF_W ? f : f - NF_W;
-            const int mt = ff / NKS, ks = ff % NKS;
-            const f16 *p = Sm + (16 * mt + l16) * LD + 32 * ks + 4 * kg;
-            const f16x4 lo = *reinterpret_cast<const f16x4 *>(p);
-            const f16x4 hi = *reinterpret_cast<const f16x4 *>(p + 16);
-            frag[0] = lo[0]; frag[1] = lo[1]; frag[2] = lo[2]; frag[3] = lo[3];
-            frag[4] = hi[0]; frag[5] = hi[1]; frag[6] = hi[2]; frag[7] = hi[3];
-            off = (f < NF_W ? R::W_OFF : R::Q_OFF) + (ff * 64 + lane) * 16;
+    // ---- 4. the four products.  Row fragment (tt, ks) of T or M: lane row t = 16 tt + l16,
+    // k = t' = 32 ks + kperm(kg, v), i.e. blocks (2ks, tt) and (2ks + 1, tt) of T^T / M^T.
+    auto row_frag = [&](int mat, int tt, int ks) {
+        Split8 f;
+        const int b0 = (mat * 10 + tri_idx(2 * ks, tt)) * 2;
+        const bf16x4 h0 = Xt[b0 * 64 + lane], l0 = Xt[(b0 + 1) * 64 + lane];
+        bf16x4 h1, l1;
+        if (2 * ks + 1 <= tt) {
+            const int b1 = (mat * 10 + tri_idx(2 * ks + 1, tt)) * 2;
+            h1 = Xt[b1 * 64 + lane];
+            l1 = Xt[(b1 + 1) * 64 + lane];
         } else {
-            const int ff = f - 2 * NF_W;
-            const int mt = ff / 2, ks = ff % 2;
-            const int d = 16 * mt + l16;
 #pragma unroll
-            for (int vv = 0; vv < 8; ++vv) {
-                const int t = 32 * ks + kperm(kg, vv);
-                const float kv = Dc[t] * ((float)Kh[t * LD + d] + (float)Kl[t * LD + d]);
-                frag[vv] = (f16)kv;
-                frag_lo[vv] = (f16)(kv - (float)frag[vv]);
-            }
-            off = R::K_OFF + (ff * 64 + lane) * 16;
-            *reinterpret_cast<f16x8 *>(rec + off + NF_K * 64 * 16) = frag_lo;
+            for (int i = 0; i < 4; ++i) { h1[i] = (bf16)0.f; l1[i] = (bf16)0.f; }
         }
-        *reinterpret_cast<f16x8 *>(rec + off) = frag;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f.hi[i] = h0[i]; f.hi[4 + i] = h1[i];
+            f.lo[i] = l0[i]; f.lo[4 + i] = l1[i];
+        }
+        return f;
+    };
+    f32x4 Y[NM][4];
+#pragma unroll
+    for (int a = 0; a < NM; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) Y[a][b] = zero4();
+    if (isW) {
+        // Y = W^T = Bw^T T^T;  Xa = Qt^T = scale e^G Q^T - Bw^T M^T
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ks = 0; 2 * ks <= tt; ++ks) {
+                const Split8 ft = row_frag(0, tt, ks);
+                const Split8 fm = neg_split(row_frag(1, tt, ks));
+#pragma unroll
+                for (int mi = 0; mi < NM; ++mi) {
+                    Y[mi][tt] = mfma16x3(Bop[mi][ks], ft, Y[mi][tt]);
+                    Xa[mi][tt] = mfma16x3(Bop[mi][ks], fm, Xa[mi][tt]);
+                }
+            }
+        // -W and Qt as the state pass's A-operand fragments (k = head dim in kperm order)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int kp = 0; kp < NM / 2; ++kp) {
+                const int ks = (NM * half) / 2 + kp;
+                const int off = ((mt * NKS + ks) * 64 + lane) * 16;
+                *reinterpret_cast<f16x8 *>(rec + R::W_OFF + off) = pack_h(-Y[2 * kp][mt], -Y[2 * kp + 1][mt]);
+                *reinterpret_cast<f16x8 *>(rec + R::Q_OFF + off) = pack_h(Xa[2 * kp][mt], Xa[2 * kp + 1][mt]);
+            }
+    } else {
+        // Y = U = T diag(b) V;  Xa = Ol = M diag(b) V   (Xa's V values are consumed)
+#pragma unroll
+        for (int a = 0; a < NM; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) Xa[a][b] = zero4();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ks = 0; 2 * ks <= rt; ++ks) {
+                const Split8 ft = row_frag(0, rt, ks);
+                const Split8 fm = row_frag(1, rt, ks);
+#pragma unroll
+                for (int ni = 0; ni < NM; ++ni) {
+                    Y[ni][rt] = mfma16x3(ft, Bop[ni][ks], Y[ni][rt]);
+                    Xa[ni][rt] = mfma16x3(fm, Bop[ni][ks], Xa[ni][rt]);
+                }
+            }
+#pragma unroll
+        for (int ni = 0; ni < NM; ++ni)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int nt = NM * half + ni;
+                const int off = ((nt * 4 + rt) * 64 + lane) * 16;
+                *reinterpret_cast<f32x4 *>(rec + R::U_OFF + off) = Y[ni][rt];
+                *reinterpret_cast<f32x4 *>(rec + R::O_OFF + off) = Xa[ni][rt];
+            }
     }
 }
 
