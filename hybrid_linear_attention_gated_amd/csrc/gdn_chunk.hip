@@ -23,27 +23,28 @@
 // an operand costs up to ~2^-9 of the largest value, which is more than the
 // 2e-2 RMS-relative accuracy the layer is held to.  Products therefore use
 //  - in the chunk-local kernel: two-term bf16 splits (hi + lo) of both operands,
-//    three MFMAs per product (K K^T, Q K^T, the block solve, P W, P U);
-//  - in the state pass: fp16 MFMA (11-bit significand) with W, Qt and the state
-//    as single fp16 operands, and the decayed keys Kd = diag(e^{G_c - G}) K and
-//    Delta as fp16 hi + lo pairs (three MFMAs for Kd^T Delta).
-//    fp16 operands assume |state|, |Delta| < 6.5e4; the fp32 master state is
-//    never rounded.
+//    three MFMAs per product (K K^T, K Q^T, the block solves, and the four
+//    products that form W', Qt, U', Ol);
+//  - in the state pass: fp16 MFMA (11-bit significand) with W', Qt and the
+//    state as single fp16 operands, and K and Delta' as bf16 hi + lo pairs
+//    (three MFMAs for K^T Delta').
+//    fp16 operands assume |state| < 6.5e4; the fp32 master state is never
+//    rounded.
 //
 // Kernels.
-//  chunk_local_kernel: one 4-wave workgroup per (chunk, value head), fully
-//    parallel.  K K^T and Q K^T, the 16x16 diagonal blocks of T by forward
-//    substitution in fp32, W and U by block forward substitution on MFMA (no
-//    explicit T), then Qt and Ol.  Writes -W, Qt, Kd^T as fp16 MFMA A-operand
-//    fragments and U, Ol as fp32 accumulator-layout tiles, so the state pass
-//    reads every operand with one coalesced 16-byte load per lane and every
-//    product accumulates straight into its MFMA chain (U and Ol seed the
-//    Delta and O chains; the per-token decay is already inside Kd).
+//  chunk_local_kernel: one workgroup per (chunk, value head), fully parallel.
+//    Explicit T = (I + A)^-1 and M = P T by block back substitution, then four
+//    products.  Writes -W' = -diag(e^{G_c - G}) W and Qt as fp16 MFMA A-operand
+//    fragments, K^T as bf16 hi / lo A-operand fragments, and
+//    U' = diag(e^{G_c - G}) U and Ol as fp32 accumulator-layout tiles, so the
+//    state pass reads every operand with one coalesced 16-byte load per lane and
+//    every product accumulates straight into its MFMA chain:
+//      Delta' = diag(e^{G_c - G}) Delta = U' + (-W') S,   O = Ol + Qt S,
+//      S' = e^{G_c} S + K^T Delta'.
 //  state_pass_kernel: one workgroup per (sequence, value head, two 16-column
 //    strips of the state); a strip's fp32 state lives in MFMA accumulators for
-//    the whole sequence and the chunk loop runs Delta = U + (-W) S,
-//    O = Ol + Qt S, S = e^{G_c} S + Kd^T Delta, with the chunk's A operands
-//    double-buffered in LDS by two copy waves.
+//    the whole sequence and the chunk loop runs the three lines above, with the
+//    chunk's A operands double-buffered in LDS by two copy waves.
 //    Accumulator tiles are reused as B operands directly: the k index of an
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
@@ -60,11 +61,11 @@ template <int D>
 struct Rec {
     static constexpr int NKS = D / 32;                  // 32-wide k steps over the head dim
     static constexpr int NTD = D / 16;                  // 16-wide tiles over the head dim
-    static constexpr int W_OFF = 0;                     // -W  f16 A frags [4 row tiles][NKS][64 lanes][8]
+    static constexpr int W_OFF = 0;                     // -W' f16 A frags [4 row tiles][NKS][64 lanes][8]
     static constexpr int Q_OFF = W_OFF + 64 * D * 2;    // Qt  f16 A frags [4][NKS][64][8]
-    static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // Kd^T f16 A frags, hi and lo: [2][NTD row tiles][2][64][8],
-                                                        //   Kd = diag(e^{G_c - G_t}) K
-    static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U   f32 tiles [NTD col tiles][4 row tiles][64][4]
+    static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // K^T bf16 A frags, hi and lo: [2][NTD row tiles][2][64][8]
+    static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U'  f32 tiles [NTD col tiles][4 row tiles][64][4]
+                                                        //   (W' = diag(e^{G_c - G_t}) W, U' likewise)
     static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
     static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times
     static constexpr int SIZE = GM_OFF + 256;           // padded to a multiple of 256 bytes
@@ -145,10 +146,26 @@ __device__ __forceinline__ void split_store(f32x4 x, bf16x4 *hi, bf16x4 *lo) {
     *hi = h;
     *lo = l;
 }
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {   // exact when a, b hold bf16 values
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = (bf16)a[i]; r[4 + i] = (bf16)b[i]; }
+    return r;
+}
+
+// Workgroup shape of the chunk-local kernel: D / 32 waves per half (head-dim
+// tiles for W and Qt, value tiles for U and Ol), two 16-wide tiles per wave.
+template <int D>
+struct LocalShape {
+    static constexpr int NWH = D / 32;
+    static constexpr int NW = 2 * NWH;
+    static constexpr int THREADS = 64 * NW;
+};
 
 // LDS layout of the chunk-local kernel (bytes).
 template <int D>
 struct LocalSmem {
+    static constexpr int NW = LocalShape<D>::NW;
     static constexpr int LD = D + 8;                         // bf16 row stride of the K / Q planes
     static constexpr int PLANE = 64 * LD * 2;
     static constexpr int KH = 0, KL = PLANE, QH = 2 * PLANE, QL = 3 * PLANE;
@@ -159,40 +176,42 @@ struct LocalSmem {
     static constexpr int ADIAG_BLK = 16 * 16 + 4;            //   floats per block (padded)
     static constexpr int AOFF = ADIAG + 4 * ADIAG_BLK * 4;   // strict-lower blocks of A: [6][hi, lo][64] bf16x4
     static constexpr int PT = AOFF + 6 * 2 * 64 * 8;         // P^T blocks c <= r: [10][64] f32x4
-    static constexpr int XT = PT + 10 * 64 * 16;             // T^T and M^T blocks c <= r: [2][10][hi, lo][64] bf16x4
-    static constexpr int SCAL = XT + 2 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^G, e^{G_c - G}, scale e^G
+    static constexpr int XT = PT + 10 * 64 * 16;             // scaled T^T, M^T blocks c <= r: [4][10][hi, lo][64] bf16x4
+    static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^G, e^{G_c - G}, scale e^G
     static constexpr int SIZE = SCAL + 5 * 64 * 4;
-    static_assert(4 * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
+    static_assert(NW * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
 };
 
-// One 4-wave workgroup per (chunk, value head), fully parallel over chunks.
-// The chunk form is evaluated with explicit T = (I + A)^-1 and M = P T:
-//   W = T diag(b e^G) K,  U = T diag(b) V,  Qt = diag(e^G) Q - M diag(b e^G) K,  Ol = M diag(b) V.
-// Every MFMA output lands in the layout its consumer wants, so nothing is
-// transposed through LDS element by element:
-//  1. K K^T row block w and K Q^T row block w (wave w; key block w is the A
-//     operand of all five tiles) -> A (strict lower) and P^T, scaled by the
-//     decays; K K^T is symmetric, so A's accumulator tile (k, c) is also the
-//     A-operand form of A^T block (c, k).
+// One workgroup per (chunk, value head), fully parallel over chunks.  With
+// T = (I + A)^-1, M = P T, Dc = diag(e^{G_c - G}), Bk = diag(b e^G), Bv = diag(b):
+//   -W' = -Dc T Bk K,  U' = Dc T Bv V,  Qt = diag(scale e^G) Q - M Bk K,  Ol = M Bv V
+// (the state pass uses Delta' = Dc Delta = U' - W' S, so the per-token decay of the
+// state update is already applied and the keys enter it unscaled).  Every MFMA
+// output lands in the layout its consumer wants, so nothing is transposed through
+// LDS element by element:
+//  1. K K^T and K Q^T tiles with key block b as the A operand -> A (strict lower)
+//     and P^T, scaled by the decays.  K K^T is symmetric, so A's accumulator tile
+//     (k, c) is also the A-operand form of A^T block (c, k).
 //  2. Every wave solves the four 16 x 16 diagonal blocks T_cc by forward
 //     substitution (lane (c, j) owns column j of block c), so no barrier.
 //  3. Block back substitution of (I + A^T) X = [I | P^T] gives T^T and M^T in
-//     accumulator layout (wave w: column block 3 - w of T^T, column block w
-//     of M^T), which is the operand form every product below needs.
-//  4. Waves 0, 1 (head-dim halves): W^T = (diag(b e^G) K)^T T^T and
-//     Qt^T = (diag(e^G) Q)^T - (diag(b e^G) K)^T M^T; in accumulator layout
-//     these are exactly the state pass's A-operand fragments of -W and Qt.
-//     Waves 2, 3 (value-dim halves): U = T diag(b) V and Ol = M diag(b) V.
+//     accumulator layout, one column block per chain; the blocks are published
+//     with the scalings above folded in.
+//  4. W waves: W'^T = K^T (Bk T^T Dc) and Qt^T = seed - K^T (Bk M^T); in
+//     accumulator layout these are exactly the state pass's A-operand fragments of
+//     -W' and Qt.  The K^T operand comes from the bf16 planes on MFMA (a 0/1
+//     selector picks 16 head-dim columns), exactly, and is stored as is.
+//     U waves: U' = (Dc T Bv) V and Ol = (M Bv) V.
 // Products use two-term bf16 splits of both operands (three MFMAs each).
 template <int D>
-__global__ __launch_bounds__(256) void chunk_local_kernel(
+__global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
+    constexpr int NWH = LocalShape<D>::NWH, NW = LocalShape<D>::NW, NT = LocalShape<D>::THREADS;
     constexpr int NKS = D / 32;   // 32-wide k steps over the head dim
-    constexpr int NM = D / 32;    // 16-wide head-dim tiles per W / U wave
     constexpr int LD = SM::LD;
     constexpr int NF_K = (D / 16) * 2;
     __shared__ __attribute__((aligned(16))) char smem[SM::SIZE];
@@ -203,16 +222,18 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     float *Adiag = reinterpret_cast<float *>(smem + SM::ADIAG);
     bf16x4 *Aoff = reinterpret_cast<bf16x4 *>(smem + SM::AOFF);     // [6][2][64]
     f32x4 *Pt = reinterpret_cast<f32x4 *>(smem + SM::PT);           // [10][64]
-    bf16x4 *Xt = reinterpret_cast<bf16x4 *>(smem + SM::XT);         // [2][10][2][64]
+    bf16x4 *Xt = reinterpret_cast<bf16x4 *>(smem + SM::XT);         // [4][10][2][64]
     float *Gs = reinterpret_cast<float *>(smem + SM::SCAL);
     float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256;
+    enum { XT_TW = 0, XT_TU = 1, XT_MW = 2, XT_MU = 3 };   // published operand sets
 
     // wave index in a scalar register: wave-level branches and LDS bases stay uniform
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
     const int gc = blockIdx.x, h = blockIdx.y;
     const int kh = h / (Hv / Hk);
-    const bool isW = wave < 2;
+    const bool isW = wave < NWH;
+    const int qw = isW ? wave : wave - NWH;   // this wave's pair of 16-wide tiles: 2qw, 2qw + 1
 
     // ---- where this chunk lives (every wave finds the same answer; no barrier)
     int s_, c_;
@@ -223,36 +244,35 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
 
     // ---- global loads, all issued before any is used.  Rows >= L are clamped
     // (loads stay in bounds and unconditional) and zeroed.
-    constexpr int NV = 64 * (D / 4) / 256;
+    constexpr int NV = 64 * (D / 4) / NT;
     float4 kv[NV], qv[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = tid + 256 * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        const int e = tid + NT * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const size_t off = ((size_t)(t0 + min(r, L - 1)) * Hk + kh) * D + c4;
         kv[i] = *reinterpret_cast<const float4 *>(k + off);
         qv[i] = *reinterpret_cast<const float4 *>(q + off);
     }
     // W waves: Q^T in accumulator layout (rows = head dim, cols = token) seeds Qt^T.
-    // U waves: V in accumulator layout (rows = token) feeds U and Ol.
-    f32x4 Xa[NM][4];
-    const int half = isW ? wave : wave - 2;
+    // U waves: V in accumulator layout (rows = token) feeds U' and Ol.
+    f32x4 Xa[2][4];
     if (isW) {
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
+        for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const int t = 16 * tt + l16, d = 16 * (NM * half + mi) + 4 * kg;
+                const int t = 16 * tt + l16, d = 16 * (2 * qw + mi) + 4 * kg;
                 const float4 x = *reinterpret_cast<const float4 *>(q + ((size_t)(t0 + min(t, L - 1)) * Hk + kh) * D + d);
                 Xa[mi][tt] = t < L ? f32x4{x.x, x.y, x.z, x.w} : zero4();
             }
     } else {
 #pragma unroll
-        for (int ni = 0; ni < NM; ++ni)
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * rt + 4 * kg + r, col = 16 * (NM * half + ni) + l16;
+                    const int t = 16 * rt + 4 * kg + r, col = 16 * (2 * qw + ni) + l16;
                     const float x = v[((size_t)(t0 + min(t, L - 1)) * Hv + h) * D + col];
                     Xa[ni][rt][r] = t < L ? x : 0.f;
                 }
@@ -278,7 +298,7 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     // K and Q as bf16 hi / lo planes, row-major [token][head dim]
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int e = tid + 256 * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        const int e = tid + NT * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const bool live = r < L;
         const float kk[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
         const float qq[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
@@ -296,106 +316,114 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
     }
     __syncthreads();
 
-    // ---- 1. key block w against every block: K K^T (w, c <= w) and K Q^T (w, r >= w)
+    // ---- 1. tiles with key block b as the A operand: K K^T (b, c <= b) and K Q^T (b, r >= b).
+    // Eight waves: wave b takes the K K^T tiles of block b, wave 4 + b the K Q^T tiles;
+    // four waves: wave b takes both.
     {
+        const int b = wave & 3;
+        const bool doKK = NW == 4 || wave < 4, doKQ = NW == 4 || wave >= 4;
         Split8 ka[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            const int off = (16 * wave + l16) * LD + 32 * ks + 8 * kg;
+            const int off = (16 * b + l16) * LD + 32 * ks + 8 * kg;
             ka[ks] = Split8{*reinterpret_cast<const bf16x8 *>(Kh + off), *reinterpret_cast<const bf16x8 *>(Kl + off)};
         }
-        // decay scalars of this lane's rows (block w) and column
-        const f32x4 Gw = *reinterpret_cast<const f32x4 *>(Gs + 16 * wave + 4 * kg);
-        const f32x4 Bw = *reinterpret_cast<const f32x4 *>(Bs + 16 * wave + 4 * kg);
-        for (int c = 0; c <= wave; ++c) {
-            f32x4 acc = zero4();
+        const f32x4 Gb = *reinterpret_cast<const f32x4 *>(Gs + 16 * b + 4 * kg);
+        if (doKK) {
+            const f32x4 Bb = *reinterpret_cast<const f32x4 *>(Bs + 16 * b + 4 * kg);
+            for (int c = 0; c <= b; ++c) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = (16 * c + l16) * LD + 32 * ks + 8 * kg;
-                const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off), *reinterpret_cast<const bf16x8 *>(Kl + off)};
-                acc = mfma16x3(ka[ks], kb, acc);
-            }
-            // A[t][i] = b_t e^{G_t - G_i} k_t . k_i for i < t; t = 16w + 4kg + r, i = 16c + l16
-            const int i = 16 * c + l16;
-            const float Gi = Gs[i];
-            f32x4 a;
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = (16 * c + l16) * LD + 32 * ks + 8 * kg;
+                    const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off),
+                                    *reinterpret_cast<const bf16x8 *>(Kl + off)};
+                    acc = mfma16x3(ka[ks], kb, acc);
+                }
+                // A[t][i] = b_t e^{G_t - G_i} k_t . k_i for i < t; t = 16b + 4kg + r, i = 16c + l16
+                const int i = 16 * c + l16;
+                const float Gi = Gs[i];
+                f32x4 a;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wave + 4 * kg + r;
-                a[r] = i < t ? Bw[r] * __expf(Gw[r] - Gi) * acc[r] : 0.f;
-            }
-            if (c == wave) {
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * b + 4 * kg + r;
+                    a[r] = i < t ? Bb[r] * __expf(Gb[r] - Gi) * acc[r] : 0.f;
+                }
+                if (c == b) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Adiag[c * SM::ADIAG_BLK + (4 * kg + r) * 16 + l16] = a[r];
-            } else {
-                const int b = stri_idx(wave, c);
-                split_store(a, &Aoff[(b * 2 + 0) * 64 + lane], &Aoff[(b * 2 + 1) * 64 + lane]);
+                    for (int r = 0; r < 4; ++r) Adiag[c * SM::ADIAG_BLK + (4 * kg + r) * 16 + l16] = a[r];
+                } else {
+                    const int s = stri_idx(b, c);
+                    split_store(a, &Aoff[(s * 2 + 0) * 64 + lane], &Aoff[(s * 2 + 1) * 64 + lane]);
+                }
             }
         }
-        for (int r = wave; r < 4; ++r) {
-            f32x4 acc = zero4();
+        if (doKQ) {
+            for (int r = b; r < 4; ++r) {
+                f32x4 acc = zero4();
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int off = (16 * r + l16) * LD + 32 * ks + 8 * kg;
-                const Split8 qb{*reinterpret_cast<const bf16x8 *>(Qh + off), *reinterpret_cast<const bf16x8 *>(Ql + off)};
-                acc = mfma16x3(ka[ks], qb, acc);
-            }
-            // P^T[i][t] = scale e^{G_t - G_i} q_t . k_i for i <= t; i = 16w + 4kg + r, t = 16r' + l16
-            const int t = 16 * r + l16;
-            const float Gt = Gs[t];
-            f32x4 p;
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int off = (16 * r + l16) * LD + 32 * ks + 8 * kg;
+                    const Split8 qb{*reinterpret_cast<const bf16x8 *>(Qh + off),
+                                    *reinterpret_cast<const bf16x8 *>(Ql + off)};
+                    acc = mfma16x3(ka[ks], qb, acc);
+                }
+                // P^T[i][t] = scale e^{G_t - G_i} q_t . k_i for i <= t; i = 16b + 4kg + rr, t = 16r + l16
+                const int t = 16 * r + l16;
+                const float Gt = Gs[t];
+                f32x4 p;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int i = 16 * wave + 4 * kg + rr;
-                p[rr] = i <= t ? scale * __expf(Gt - Gw[rr]) * acc[rr] : 0.f;
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int i = 16 * b + 4 * kg + rr;
+                    p[rr] = i <= t ? scale * __expf(Gt - Gb[rr]) * acc[rr] : 0.f;
+                }
+                Pt[tri_idx(b, r) * 64 + lane] = p;
             }
-            Pt[tri_idx(wave, r) * 64 + lane] = p;
         }
     }
 
-    // W waves: K^T fragments (A-operand form: lane row = head dim, k = token in kperm
-    // order) from the planes; the decayed copy goes to the record for the state
-    // pass, the (b e^G)-scaled copy stays as this wave's A operand of step 4.
-    Split8 Bop[NM][2];
+    // W waves: K in accumulator layout (rows = token) for head-dim tiles 2qw, 2qw + 1, on
+    // MFMA from the row fragments: D = K_rows x Sel with Sel[k][j] = (k == 16 hh + j).  The hi
+    // and lo planes go through separately, so the results are exact bf16 values and form the
+    // K^T operand (lane row = head dim, k = token in kperm order) with no rounding.  They go to
+    // the record as they are and stay as this wave's A operand of step 4.
+    // U waves: V as B operands (k = token in kperm order).
+    Split8 Bop[2][2];   // [tile][token k step]
     if (isW) {
+        bf16x8 sel[2];
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-            const int m = NM * half + mi;
-            const int d = 16 * m + l16;
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float bw[8];
-                f16x8 hi, lo;
+            for (int vv = 0; vv < 8; ++vv) sel[hh][vv] = (bf16)((8 * kg + vv == 16 * hh + l16) ? 1.f : 0.f);
+        f32x4 Kth[4][2], Ktl[4][2];   // [token block][tile]
 #pragma unroll
-                for (int vv = 0; vv < 8; ++vv) {
-                    const int t = 32 * ks + kperm(kg, vv);
-                    const float kvv = (float)Kh[t * LD + d] + (float)Kl[t * LD + d];
-                    const float kd = DCs[t] * kvv;
-                    hi[vv] = (f16)kd;
-                    lo[vv] = (f16)(kd - (float)hi[vv]);
-                    bw[vv] = BEG[t] * kvv;
-                }
-                const int off = R::K_OFF + ((m * 2 + ks) * 64 + lane) * 16;
-                *reinterpret_cast<f16x8 *>(rec + off) = hi;
-                *reinterpret_cast<f16x8 *>(rec + off + NF_K * 64 * 16) = lo;
-                Bop[mi][ks] = split8(bw);
+        for (int rt = 0; rt < 4; ++rt) {
+            const int off = (16 * rt + l16) * LD + 32 * qw + 8 * kg;
+            const bf16x8 kh8 = *reinterpret_cast<const bf16x8 *>(Kh + off);
+            const bf16x8 kl8 = *reinterpret_cast<const bf16x8 *>(Kl + off);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                Kth[rt][hh] = mfma16(kh8, sel[hh], zero4());
+                Ktl[rt][hh] = mfma16(kl8, sel[hh], zero4());
             }
+        }
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const float qs = QS[16 * tt + l16];
-                Xa[mi][tt] = Xa[mi][tt] * qs;   // Qt^T seed: scale e^{G_t} Q^T
+        for (int hh = 0; hh < 2; ++hh) {
+            const int m = 2 * qw + hh;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                Bop[hh][kt] = Split8{to_bf16x8(Kth[2 * kt][hh], Kth[2 * kt + 1][hh]),
+                                     to_bf16x8(Ktl[2 * kt][hh], Ktl[2 * kt + 1][hh])};
+                const int off = R::K_OFF + ((m * 2 + kt) * 64 + lane) * 16;
+                *reinterpret_cast<bf16x8 *>(rec + off) = Bop[hh][kt].hi;
+                *reinterpret_cast<bf16x8 *>(rec + off + NF_K * 64 * 16) = Bop[hh][kt].lo;
             }
         }
     } else {
-        // U waves: diag(b) V as B operands (k = token in kperm order), two k steps
 #pragma unroll
-        for (int ni = 0; ni < NM; ++ni)
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 b0 = *reinterpret_cast<const f32x4 *>(Bs + 32 * ks + 4 * kg);
-                const f32x4 b1 = *reinterpret_cast<const f32x4 *>(Bs + 32 * ks + 16 + 4 * kg);
-                Bop[ni][ks] = split_tiles(Xa[ni][2 * ks] * b0, Xa[ni][2 * ks + 1] * b1);
-            }
+            for (int kt = 0; kt < 2; ++kt) Bop[ni][kt] = split_tiles(Xa[ni][2 * kt], Xa[ni][2 * kt + 1]);
     }
     __syncthreads();
 
@@ -433,18 +461,20 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
             Tcc[cc] = split_block(*reinterpret_cast<const f32x4 *>(scr + (cc * 16 + l16) * SM::SCR_LANE + 4 * kg));
     }
 
-    // ---- 3. back substitution (I + A^T) X = [I | P^T], column block by column block:
+    // ---- 3. back substitution (I + A^T) X = [I | P^T], one column block per chain:
     //   X_cr = T_cc^T (RHS_cr - sum_{k = c+1..r} (A^T)_ck X_kr),  c = r, r-1, .., 0
-    // wave w: column block 3 - w of T^T (RHS = I) and column block w of M^T (RHS = P^T).
-    auto aT = [&](int kk, int c) {   // A-operand form of (A^T)_{c,kk}: accumulator tile (kk, c) of A
-        const int b = stri_idx(kk, c);
-        return block_operand(Aoff[(b * 2 + 0) * 64 + lane], Aoff[(b * 2 + 1) * 64 + lane]);
+    // chains 0..3: column blocks of T^T (RHS = I); chains 4..7: column blocks of M^T.
+    auto aT = [&](int kk, int c) __attribute__((always_inline)) {   // A-operand form of (A^T)_{c,kk}: accumulator tile (kk, c) of A
+        const int s = stri_idx(kk, c);
+        return block_operand(Aoff[(s * 2 + 0) * 64 + lane], Aoff[(s * 2 + 1) * 64 + lane]);
     };
-    auto publish = [&](int mat, int c, int r, f32x4 x) {
-        const int b = (mat * 10 + tri_idx(c, r)) * 2;
-        split_store(x, &Xt[(b + 0) * 64 + lane], &Xt[(b + 1) * 64 + lane]);
+    // Publish block (c, r) (rows t' = 16c + 4kg + i, column t = 16r + l16) of a scaled copy.
+    auto publish = [&](int set, int c, int r, f32x4 x, const float *rowscale, float colscale) __attribute__((always_inline)) {
+        const f32x4 rs = *reinterpret_cast<const f32x4 *>(rowscale + 16 * c + 4 * kg);
+        const int s = (set * 10 + tri_idx(c, r)) * 2;
+        split_store(x * rs * colscale, &Xt[(s + 0) * 64 + lane], &Xt[(s + 1) * 64 + lane]);
     };
-    auto solve_T = [&](auto rtag) {
+    auto solve_T = [&](auto rtag) __attribute__((always_inline)) {
         constexpr int r = decltype(rtag)::value;
         f32x4 X[4];
         bf16x8 eye;
@@ -458,10 +488,14 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
             for (int kk = c + 1; kk <= r; ++kk) acc = mfma16x3(aT(kk, c), split_block(X[kk]), acc);
             X[c] = -mfma16x3(Tcc[c], split_block(acc), zero4());
         }
+        const float dc = DCs[16 * r + l16];
 #pragma unroll
-        for (int c = 0; c <= r; ++c) publish(0, c, r, X[c]);
+        for (int c = 0; c <= r; ++c) {
+            publish(XT_TW, c, r, X[c], BEG, dc);
+            publish(XT_TU, c, r, X[c], Bs, dc);
+        }
     };
-    auto solve_M = [&](auto rtag) {
+    auto solve_M = [&](auto rtag) __attribute__((always_inline)) {
         constexpr int r = decltype(rtag)::value;
         f32x4 X[4];
 #pragma unroll
@@ -472,25 +506,40 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
             X[c] = mfma16x3(Tcc[c], split_block(acc), zero4());
         }
 #pragma unroll
-        for (int c = 0; c <= r; ++c) publish(1, c, r, X[c]);
+        for (int c = 0; c <= r; ++c) {
+            publish(XT_MW, c, r, X[c], BEG, 1.f);
+            publish(XT_MU, c, r, X[c], Bs, 1.f);
+        }
     };
-    switch (wave) {
-    case 0: solve_T(std::integral_constant<int, 3>{}); solve_M(std::integral_constant<int, 0>{}); break;
-    case 1: solve_T(std::integral_constant<int, 2>{}); solve_M(std::integral_constant<int, 1>{}); break;
-    case 2: solve_T(std::integral_constant<int, 1>{}); solve_M(std::integral_constant<int, 2>{}); break;
-    default: solve_T(std::integral_constant<int, 0>{}); solve_M(std::integral_constant<int, 3>{}); break;
+    auto run_chain = [&](int ch) __attribute__((always_inline)) {
+        switch (ch) {
+        case 0: solve_T(std::integral_constant<int, 0>{}); break;
+        case 1: solve_T(std::integral_constant<int, 1>{}); break;
+        case 2: solve_T(std::integral_constant<int, 2>{}); break;
+        case 3: solve_T(std::integral_constant<int, 3>{}); break;
+        case 4: solve_M(std::integral_constant<int, 0>{}); break;
+        case 5: solve_M(std::integral_constant<int, 1>{}); break;
+        case 6: solve_M(std::integral_constant<int, 2>{}); break;
+        default: solve_M(std::integral_constant<int, 3>{}); break;
+        }
+    };
+    if (NW == 8) {
+        run_chain(wave);
+    } else {   // four waves: long and short chains paired
+        run_chain(3 - wave);
+        run_chain(4 + wave);
     }
     __syncthreads();
 
-    // ---- 4. the four products.  Row fragment (tt, ks) of T or M: lane row t = 16 tt + l16,
-    // k = t' = 32 ks + kperm(kg, v), i.e. blocks (2ks, tt) and (2ks + 1, tt) of T^T / M^T.
-    auto row_frag = [&](int mat, int tt, int ks) {
+    // ---- 4. the four products.  Row fragment (tt, ks) of a published set: lane row
+    // t = 16 tt + l16, k = t' = 32 ks + kperm(kg, v), i.e. blocks (2ks, tt), (2ks + 1, tt).
+    auto row_frag = [&](int set, int tt, int ks) __attribute__((always_inline)) {
         Split8 f;
-        const int b0 = (mat * 10 + tri_idx(2 * ks, tt)) * 2;
+        const int b0 = (set * 10 + tri_idx(2 * ks, tt)) * 2;
         const bf16x4 h0 = Xt[b0 * 64 + lane], l0 = Xt[(b0 + 1) * 64 + lane];
         bf16x4 h1, l1;
         if (2 * ks + 1 <= tt) {
-            const int b1 = (mat * 10 + tri_idx(2 * ks + 1, tt)) * 2;
+            const int b1 = (set * 10 + tri_idx(2 * ks + 1, tt)) * 2;
             h1 = Xt[b1 * 64 + lane];
             l1 = Xt[(b1 + 1) * 64 + lane];
         } else {
@@ -504,58 +553,59 @@ __global__ __launch_bounds__(256) void chunk_local_kernel(
         }
         return f;
     };
-    f32x4 Y[NM][4];
+    f32x4 Y[2][4];
 #pragma unroll
-    for (int a = 0; a < NM; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) Y[a][b] = zero4();
     if (isW) {
-        // Y = W^T = Bw^T T^T;  Xa = Qt^T = scale e^G Q^T - Bw^T M^T
+        // Y = W'^T = K^T (Bk T^T Dc);  Xa = Qt^T = scale e^G Q^T - K^T (Bk M^T)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt) {
+            const float qs = QS[16 * tt + l16];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) Xa[mi][tt] = Xa[mi][tt] * qs;
 #pragma unroll
             for (int ks = 0; 2 * ks <= tt; ++ks) {
-                const Split8 ft = row_frag(0, tt, ks);
-                const Split8 fm = neg_split(row_frag(1, tt, ks));
+                const Split8 ft = row_frag(XT_TW, tt, ks);
+                const Split8 fm = neg_split(row_frag(XT_MW, tt, ks));
 #pragma unroll
-                for (int mi = 0; mi < NM; ++mi) {
+                for (int mi = 0; mi < 2; ++mi) {
                     Y[mi][tt] = mfma16x3(Bop[mi][ks], ft, Y[mi][tt]);
                     Xa[mi][tt] = mfma16x3(Bop[mi][ks], fm, Xa[mi][tt]);
                 }
             }
-        // -W and Qt as the state pass's A-operand fragments (k = head dim in kperm order)
+        }
+        // -W' and Qt as the state pass's A-operand fragments (k = head dim in kperm order)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int kp = 0; kp < NM / 2; ++kp) {
-                const int ks = (NM * half) / 2 + kp;
-                const int off = ((mt * NKS + ks) * 64 + lane) * 16;
-                *reinterpret_cast<f16x8 *>(rec + R::W_OFF + off) = pack_h(-Y[2 * kp][mt], -Y[2 * kp + 1][mt]);
-                *reinterpret_cast<f16x8 *>(rec + R::Q_OFF + off) = pack_h(Xa[2 * kp][mt], Xa[2 * kp + 1][mt]);
-            }
+        for (int mt = 0; mt < 4; ++mt) {
+            const int off = ((mt * NKS + qw) * 64 + lane) * 16;
+            *reinterpret_cast<f16x8 *>(rec + R::W_OFF + off) = pack_h(-Y[0][mt], -Y[1][mt]);
+            *reinterpret_cast<f16x8 *>(rec + R::Q_OFF + off) = pack_h(Xa[0][mt], Xa[1][mt]);
+        }
     } else {
-        // Y = U = T diag(b) V;  Xa = Ol = M diag(b) V   (Xa's V values are consumed)
+        // Y = U' = (Dc T Bv) V;  Xa = Ol = (M Bv) V   (Xa's V values are consumed)
 #pragma unroll
-        for (int a = 0; a < NM; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b) Xa[a][b] = zero4();
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ks = 0; 2 * ks <= rt; ++ks) {
-                const Split8 ft = row_frag(0, rt, ks);
-                const Split8 fm = row_frag(1, rt, ks);
+                const Split8 ft = row_frag(XT_TU, rt, ks);
+                const Split8 fm = row_frag(XT_MU, rt, ks);
 #pragma unroll
-                for (int ni = 0; ni < NM; ++ni) {
+                for (int ni = 0; ni < 2; ++ni) {
                     Y[ni][rt] = mfma16x3(ft, Bop[ni][ks], Y[ni][rt]);
                     Xa[ni][rt] = mfma16x3(fm, Bop[ni][ks], Xa[ni][rt]);
                 }
             }
 #pragma unroll
-        for (int ni = 0; ni < NM; ++ni)
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                const int nt = NM * half + ni;
+                const int nt = 2 * qw + ni;
                 const int off = ((nt * 4 + rt) * 64 + lane) * 16;
                 *reinterpret_cast<f32x4 *>(rec + R::U_OFF + off) = Y[ni][rt];
                 *reinterpret_cast<f32x4 *>(rec + R::O_OFF + off) = Xa[ni][rt];
@@ -735,7 +785,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         f16x8 fr[2][GF];
         read_p1(A, 0, fr[0]);
 
-        // ---- Delta = U + (-W) S and O = Ol + Qt S: four independent accumulation chains
+        // ---- Delta' = U' + (-W') S and O = Ol + Qt S: four independent accumulation chains
         // per group (Delta and O of two row tiles), each one MFMA per k step
         f32x4 Dl[4], Ot[4];
 #pragma unroll
@@ -760,41 +810,37 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             Ot[2 * p] = o0; Ot[2 * p + 1] = o1;
         }
 
-        // ---- S = gamma S + Kd^T Delta with Kd = diag(e^{G_c - G_t}) K; Kd and Delta as
-        // fp16 hi + lo pairs (the lo x lo term is dropped): one six-MFMA chain per state
-        // row tile, four tiles interleaved per group
-        f16x8 Dh[2], Dlo[2];
+        // ---- S = e^{G_c} S + K^T Delta' with Delta' = diag(e^{G_c - G_t}) Delta; K and
+        // Delta' as bf16 hi + lo pairs (the lo x lo term is dropped): one six-MFMA chain
+        // per state row tile, four tiles interleaved per group
+        bf16x8 Dh[2], Dlo[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            Dh[ks] = pack_h(Dl[2 * ks], Dl[2 * ks + 1]);
-            f32x4 r0, r1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                r0[e] = Dl[2 * ks][e] - (float)Dh[ks][e];
-                r1[e] = Dl[2 * ks + 1][e] - (float)Dh[ks][4 + e];
-            }
-            Dlo[ks] = pack_h(r0, r1);
+            const Split8 sp = split_tiles(Dl[2 * ks], Dl[2 * ks + 1]);
+            Dh[ks] = sp.hi;
+            Dlo[ks] = sp.lo;
         }
+        auto kf = [](f16x8 x) { return __builtin_bit_cast(bf16x8, x); };   // K fragments are bf16
 #pragma unroll
         for (int p = 0; p < NG2; ++p) {
             const f16x8 *F = fr[(NG1 + p) & 1];
             f32x4 a[4];
-            a[0] = mfma16(F[0], Dh[0], S[4 * p] * gm);
+            a[0] = mfma16(kf(F[0]), Dh[0], S[4 * p] * gm);
             __builtin_amdgcn_sched_barrier(0);
             if (p + 1 < NG2) read_p2(A, p + 1, fr[(NG1 + p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int dm = 1; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm], Dh[0], S[4 * p + dm] * gm);
+            for (int dm = 1; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm]), Dh[0], S[4 * p + dm] * gm);
 #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 1], Dh[1], a[dm]);
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm + 1]), Dh[1], a[dm]);
 #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm], Dlo[0], a[dm]);
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm]), Dlo[0], a[dm]);
 #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 1], Dlo[1], a[dm]);
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm + 1]), Dlo[1], a[dm]);
 #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 2], Dh[0], a[dm]);
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm + 2]), Dh[0], a[dm]);
 #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(F[4 * dm + 3], Dh[1], a[dm]);
+            for (int dm = 0; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm + 3]), Dh[1], a[dm]);
 #pragma unroll
             for (int dm = 0; dm < 4; ++dm) S[4 * p + dm] = a[dm];
         }
@@ -844,7 +890,8 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     const size_t nc = max_chunks(a.T, a.N);
     char *ws = (char *)a.ws;
     if ((phases & 1) && nc > 0 && a.T > 0) {
-        hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)nc, a.Hv), dim3(256), 0, st, a.q, a.k, a.v,
+        hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)nc, a.Hv), dim3(LocalShape<D>::THREADS), 0, st,
+                           a.q, a.k, a.v,
                            a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, (int)nc);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
