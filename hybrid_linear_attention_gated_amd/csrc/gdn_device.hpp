@@ -59,15 +59,29 @@ template <> struct Vec8<float> {
     }
 };
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+// SiLU y * sigmoid(y) with the hardware reciprocal (about 1 ulp) instead of an
+// IEEE division sequence; for y < -88 the exponential overflows to +inf and the
+// result is -0, the limit of the function.
+__device__ __forceinline__ float silu(float y) { return y * __builtin_amdgcn_rcpf(1.0f + __expf(-y)); }
 
 // ---------------------------------------------------------------- reductions
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).  Within a
+// 16-lane row the steps are DPP moves (no LDS): quad permutes [1,0,3,2] and
+// [2,3,0,1] sum each quad, the half-row mirror adds the other quad of each 8 and the
+// row mirror the other half of the row; wider groups continue with xor shuffles.
+template <int ctrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
+    if constexpr (width >= 2) v += dpp_mov<0xB1>(v);    // quad_perm(1, 0, 3, 2)
+    if constexpr (width >= 4) v += dpp_mov<0x4E>(v);    // quad_perm(2, 3, 0, 1)
+    if constexpr (width >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+    if constexpr (width >= 16) v += dpp_mov<0x140>(v);  // row_mirror
 #pragma unroll
-    for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
+    for (int m = 16; m < width; m <<= 1) v += __shfl_xor(v, m, kWave);
     return v;
 }
 
