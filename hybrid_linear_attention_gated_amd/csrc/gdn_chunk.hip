@@ -49,6 +49,8 @@
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
 //    accumulator tiles (kperm).
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -207,7 +209,7 @@ template <int D>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
-    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax) {
+    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr int NWH = LocalShape<D>::NWH, NW = LocalShape<D>::NW, NT = LocalShape<D>::THREADS;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // wave index in a scalar register: wave-level branches and LDS bases stay uniform
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, kg = lane >> 4;
-    const int gc = blockIdx.x, h = blockIdx.y;
+    const int gc = g0 + blockIdx.x, h = blockIdx.y;   // packed chunk index, value head
     const int kh = h / (Hv / Hk);
     const bool isW = wave < NWH;
     const int qw = isW ? wave : wave - NWH;   // this wave's pair of 16-wide tiles: 2qw, 2qw + 1
@@ -655,7 +657,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 template <int D>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o, int ncmax) {
+    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -680,6 +682,15 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const int nc = n_chunks(L);
     const int gbase = __builtin_amdgcn_readfirstlane(chunk_base_wave(cu, s));
     auto rec_of = [&](int c) { return ws + ((size_t)h * ncmax + gbase + c) * R::SIZE; };
+    // This launch covers the sequence's chunks whose packed index lies in [g0, g1): local
+    // chunks [c_lo, c_hi).  The state enters from the initial state when the range starts
+    // the sequence and from `mid` otherwise, and leaves to the final state when the range
+    // ends the sequence and to `mid` otherwise.  An empty sequence belongs to the launch
+    // whose range starts at 0 (its final state is its initial state).
+    const int c_lo = min(max(g0 - gbase, 0), nc), c_hi = min(max(g1 - gbase, 0), nc);
+    if (nc > 0 ? c_lo >= c_hi : g0 != 0) return;
+    const float *s_in = c_lo == 0 ? s0 : mid;
+    float *s_out = c_hi == nc ? sf : mid;
 
     if (copier) {
         // Each copy wave moves half of the A operands with direct-to-LDS buffer loads
@@ -690,11 +701,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(c), R::SIZE);
             copy_to_lds(r, half, dst + half, ABYTES / 2, lane);
         };
-        if (nc > 0) stage(0, abuf[0]);
+        if (c_lo < c_hi) stage(c_lo, abuf[c_lo & 1]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        for (int c = 0; c < nc; ++c) {
-            if (c + 1 < nc) stage(c + 1, abuf[(c + 1) & 1]);
+        for (int c = c_lo; c < c_hi; ++c) {
+            if (c + 1 < c_hi) stage(c + 1, abuf[(c + 1) & 1]);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -703,11 +714,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 
     f32x4 S[NTD];
     const size_t st_off = ((size_t)s * Hv + h) * D * D;
-    if (s0) {
+    if (s_in) {
 #pragma unroll
         for (int m = 0; m < NTD; ++m)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) S[m][qq] = s0[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col];
+            for (int qq = 0; qq < 4; ++qq) S[m][qq] = s_in[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col];
     } else {
 #pragma unroll
         for (int m = 0; m < NTD; ++m) S[m] = zero4();
@@ -725,7 +736,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         // lane-varying address: a vector load (no scalar load shares lgkmcnt with LDS reads)
         g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
     };
-    if (nc > 0) load_strip(rec_of(0), Uf, Of, gm);
+    if (c_lo < c_hi) load_strip(rec_of(c_lo), Uf, Of, gm);
     // Retire the initial state and strip loads here, once.  Left pending into the loop,
     // the compiler's wait analysis merges them into the loop header and then waits for
     // every outstanding access (the previous chunk's o stores and this chunk's prefetch)
@@ -863,13 +874,13 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             gm = gn;
         }
     };
-    for (int c = 0; c + 1 < nc; ++c) chunk_step(c, std::false_type{});
-    if (nc > 0) chunk_step(nc - 1, std::true_type{});
-    if (sf) {
+    for (int c = c_lo; c + 1 < c_hi; ++c) chunk_step(c, std::false_type{});
+    if (c_lo < c_hi) chunk_step(c_hi - 1, std::true_type{});
+    if (s_out) {
 #pragma unroll
         for (int m = 0; m < NTD; ++m)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) sf[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = S[m][qq];
+            for (int qq = 0; qq < 4; ++qq) s_out[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = S[m][qq];
     }
 }
 
@@ -879,32 +890,98 @@ bool chunked_supported(int dk, int dv) { return dk == dv && (dk == 64 || dk == 1
 
 static size_t max_chunks(int T, int N) { return (size_t)(T / kChunk) + (size_t)N; }
 
+// Workspace: the per-(chunk, value head) records, then one state per (sequence, value
+// head) that carries a sequence from one pipeline segment to the next.
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     (void)dv;
     const size_t rec = dk == 64 ? (size_t)Rec<64>::SIZE : (size_t)Rec<128>::SIZE;
-    return max_chunks(T, N) * (size_t)Hv * rec;
+    return max_chunks(T, N) * (size_t)Hv * rec + (size_t)N * Hv * dk * dk * sizeof(float);
+}
+
+// ---- segment pipeline of gdn_chunk_prefill: the packed chunk range is cut into
+// segments; the chunk-local kernel of segment k + 1 runs on the caller's stream while
+// the state pass of segment k runs on a second stream of the library, ordered by events
+// only (no spinning).  Each device gets one such stream (default priority) and a small
+// pool of events, created on first use and kept for the life of the process.
+constexpr int kMaxSegments = 4;
+struct PipeRes {
+    hipStream_t side = nullptr;
+    hipEvent_t ev[kMaxSegments + 1] = {};
+    bool ready = false;
+};
+static std::mutex g_pipe_mu;
+static PipeRes g_pipe[64];
+
+static hipError_t pipe_resources(PipeRes **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_pipe_mu);
+    PipeRes &r = g_pipe[dev];
+    if (!r.ready) {
+        e = hipStreamCreateWithFlags(&r.side, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+        for (auto &ev : r.ev) {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        r.ready = true;
+    }
+    *out = &r;
+    return hipSuccess;
+}
+
+template <int D>
+static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
+    if (g1 <= g0 || a.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)(g1 - g0), a.Hv), dim3(LocalShape<D>::THREADS), 0,
+                       st, a.q, a.k, a.v, a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, (char *)a.ws, nc, g0);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
+    const int units = a.N * a.Hv;
+    if (units <= 0) return hipSuccess;
+    constexpr int NP = D / 32;
+    const int blocks = 8 * NP * ((units + 7) / 8);
+    float *mid = reinterpret_cast<float *>((char *)a.ws + (size_t)nc * a.Hv * Rec<D>::SIZE);
+    hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T, a.Hv,
+                       units, a.s0, a.sf, a.o, nc, g0, g1, mid);
+    return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int phases) {
-    const size_t nc = max_chunks(a.T, a.N);
-    char *ws = (char *)a.ws;
-    if ((phases & 1) && nc > 0 && a.T > 0) {
-        hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)nc, a.Hv), dim3(LocalShape<D>::THREADS), 0, st,
-                           a.q, a.k, a.v,
-                           a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, (int)nc);
-        hipError_t e = hipGetLastError();
+    const int nc = (int)max_chunks(a.T, a.N);
+    hipError_t e;
+    if (phases != 3) {   // one phase on its own (split-phase entry points)
+        if (phases & 1) {
+            e = launch_local<D>(a, st, nc, 0, nc);
+            if (e != hipSuccess) return e;
+        }
+        if (phases & 2) return launch_state<D>(a, st, nc, 0, nc);
+        return hipSuccess;
+    }
+    const int G = std::max(1, std::min(kMaxSegments, nc / 8));
+    if (G == 1) {
+        e = launch_local<D>(a, st, nc, 0, nc);
         if (e != hipSuccess) return e;
+        return launch_state<D>(a, st, nc, 0, nc);
     }
-    if (phases & 2) {
-        const int units = a.N * a.Hv;
-        constexpr int NP = D / 32;
-        const int blocks = 8 * NP * ((units + 7) / 8);
-        hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(256), 0, st, (const char *)ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, (int)nc);
-        return hipGetLastError();
+    PipeRes *pr = nullptr;
+    e = pipe_resources(&pr);
+    if (e != hipSuccess) return e;
+    for (int k = 0; k < G; ++k) {
+        const int g0 = (int)((long long)k * nc / G), g1 = (int)((long long)(k + 1) * nc / G);
+        if ((e = launch_local<D>(a, st, nc, g0, g1)) != hipSuccess) return e;
+        if ((e = hipEventRecord(pr->ev[k], st)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(pr->side, pr->ev[k], 0)) != hipSuccess) return e;
+        if ((e = launch_state<D>(a, pr->side, nc, g0, g1)) != hipSuccess) return e;
     }
-    return hipSuccess;
+    if ((e = hipEventRecord(pr->ev[kMaxSegments], pr->side)) != hipSuccess) return e;
+    return hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0);
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases) {

@@ -20,7 +20,13 @@
  *    no pointer after a call returns and allocates no device memory.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *    work is enqueued asynchronously on it; buffers must stay valid until the
- *    stream work completes.
+ *    stream work completes.  gdn_chunk_prefill with GDN_MATH_MFMA may run part of
+ *    its work on a second stream of the library (created once per device, default
+ *    priority, kept with a few events for the life of the process); that work is
+ *    ordered after everything enqueued on `stream` before the call and before
+ *    everything enqueued on it after the call, so to the caller it behaves as if
+ *    it ran on `stream`.  Concurrent calls on one device must use distinct
+ *    workspaces, as always.
  *  - Element type `dtype` (gdn_conv_qk_prep, gdn_decode_step) is the type of the
  *    pre-conv input x, the conv weights and the conv caches: GDN_BF16 or GDN_F32.
  *    Everything computed is fp32: q, k, v, o, g, beta and the recurrent states.
@@ -120,7 +126,15 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *   o              [T][Hv][dv]   fp32; o_t = S_t (scale * q_t); must not overlap any input
  *   workspace      device scratch of at least gdn_chunk_prefill_workspace_size()
  *                  bytes (may be NULL when that size is 0); contents are scratch.
+ *                  With GDN_MATH_MFMA it holds the per-(chunk, value head) results
+ *                  of the chunk-local phase and one state per (sequence, value head).
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
+ *
+ * With GDN_MATH_MFMA and more than a few chunks, the packed chunks are cut into up
+ * to four segments: the chunk-local phase of segment k + 1 runs while the state
+ * pass of segment k runs (on the library's second stream, see the conventions);
+ * a sequence's state passes between segments through the workspace.  The result
+ * is bit-identical to running the two phases below one after the other.
  */
 int gdn_chunk_prefill(const float *q, const float *k, const float *v,
                       const float *g, const float *beta,

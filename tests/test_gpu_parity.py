@@ -175,6 +175,38 @@ def test_core_f32_inplace_state(gdn):
     _core_case(gdn, wl, "f32", inplace=True)
 
 
+# 41 packed chunks: the one-call prefill cuts them into four pipeline segments, so
+# sequences start and end inside segments and span several of them; the batch also holds
+# an empty and a one-token sequence.
+SEGMENTED_LENGTHS = [300, 1, 0, 700, 65, 129, 1000]
+
+
+def test_core_chunked_segmented_varlen(gdn):
+    announce(f"core chunked, segmented pipeline, lengths={SEGMENTED_LENGTHS}")
+    wl = inputs.core_workload("seg", 901, SEGMENTED_LENGTHS, 2, 4, 128, 128, random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
+def test_segmented_equals_split_phases(gdn):
+    """The one-call prefill (segment pipeline over two streams) and the two split-phase
+    calls (one launch each) run the same per-chunk arithmetic: results are bit-identical."""
+    announce("one-call segmented prefill == chunk_prefill_local + chunk_prefill_state (bitwise)")
+    wl = inputs.core_workload("seg2", 902, SEGMENTED_LENGTHS, 2, 4, 128, 128, random_states=True)
+    q, k, v, g, b = (_cuda(t) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    cu, s0 = _cuda(wl.cu_seqlens), _cuda(wl.state)
+    o1, f1 = gdn.chunk_prefill(q, k, v, g, b, cu_seqlens=cu, initial_state=s0, math="mfma")
+    ws = torch.empty(gdn.workspace_size(wl.T, wl.N, wl.Hk, wl.Hv, wl.dk, wl.dv, "mfma"), dtype=torch.uint8,
+                     device=DEV)
+    o2 = torch.empty_like(o1)
+    f2 = torch.empty_like(f1)
+    gdn.chunk_prefill_local(q, k, v, g, b, ws, cu_seqlens=cu)
+    gdn.chunk_prefill_state(ws, o2, wl.T, wl.Hk, wl.Hv, wl.dk, wl.dv, cu_seqlens=cu, initial_state=s0,
+                            final_state=f2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(f1, f2)
+
+
 def test_core_empty_sequences(gdn):
     announce("core: all sequences empty (T = 0)")
     H, d = 2, 128
