@@ -5,16 +5,18 @@ One step = one pass of the whole hot path over one batch of seeded synthetic
 input:
   prefill of one linear-attention layer of the 0.8B hybrid shape
   (T = 4096 tokens, 16 key / 16 value heads, head dims 128, bf16 pre-conv x):
-      gdn_conv_qk_prep -> gdn_chunk_prefill (one call; its chunk-local and
-      state phases overlap segment by segment on two streams)
+      gdn_prefill (one call: conv + SiLU + L2 inside the chunk-local kernel,
+      whose segments overlap the state pass on two streams; q, k, v never
+      reach HBM)
   followed by one decode step of 256 sequences (gdn_decode_step, fp32 state in place).
 
-`value` is prefill tokens/s: 4096 tokens over the event time of the two prefill
-calls, averaged over the timed steps; the decode part is reported under "decode"
-as tokens/s and state GB/s.  A second timed region runs the same prefill through
-the split-phase entry points so that every kernel sits alone between two HIP
-events on the stream it is launched on; those per-kernel durations give
-"kernels" and "roofline".  Inputs rotate over several copies at different
+`value` is prefill tokens/s: 4096 tokens over the event time of the gdn_prefill
+call, averaged over the timed steps; the decode part is reported under "decode"
+as tokens/s and state GB/s.  A second timed region runs the same prefill as
+gdn_conv_qk_prep + gdn_chunk_prefill (reported under "prefill_two_call"), and a
+third through the split-phase entry points so that every kernel sits alone
+between two HIP events on the stream it is launched on; those per-kernel
+durations give "kernels" and "roofline".  Inputs rotate over several copies at different
 addresses and each decode step streams 512 MiB of state, so nothing stays in the
 256 MB Infinity Cache from one step to the next.
 
@@ -163,31 +165,45 @@ def main():
     db = dw.beta.to(dev)
     do = torch.empty((B, Hv, d), dtype=torch.float32, device=dev)
 
-    # Timed region 1 (the metric): one step = gdn_conv_qk_prep + gdn_chunk_prefill (one call:
-    # the chunk-local and state phases overlap segment by segment) + one decode step.
+    # Timed region 1 (the metric): one step = gdn_prefill (prep fused into the chunked
+    # prefill, one call) + one decode step.
     def step(i, ev):
+        r = i % R
+        ev[0].record()
+        gdn.prefill(xs[r], cw, gs[r], bs[r], Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, final_state=fin,
+                    o=o, workspace=ws)
+        ev[1].record()
+        gdn.decode_step(dx, dcw, dcs[i % Rd], dg, db, dstate[i % Rd], Hk, Hv, d, d, o=do)
+        ev[2].record()
+
+    # Timed region 1b: the same prefill as gdn_conv_qk_prep + gdn_chunk_prefill (q, k, v
+    # written to HBM and read back).
+    def step_two(i, ev):
         r = i % R
         ev[0].record()
         gdn.conv_qk_prep(xs[r], cw, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, q=q, k=k, v=v)
         ev[1].record()
         gdn.chunk_prefill(q, k, v, gs[r], bs[r], cu_seqlens=cu, final_state=fin, o=o, workspace=ws, math="mfma")
         ev[2].record()
-        gdn.decode_step(dx, dcw, dcs[i % Rd], dg, db, dstate[i % Rd], Hk, Hv, d, d, o=do)
-        ev[3].record()
 
     # Timed region 2 (per-kernel durations for the roofline): the same prefill through the
-    # split-phase entry points, one kernel between each pair of events.
+    # split-phase entry points, one kernel between each pair of events: the fused chunk-local
+    # kernel (gdn_prefill_local without a conv cache to write, so the interval holds that
+    # kernel alone), the state pass, the decode step; then the two-call path's prep and
+    # chunk-local kernels.
     def step_split(i, ev):
         r = i % R
         ev[0].record()
-        gdn.conv_qk_prep(xs[r], cw, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, q=q, k=k, v=v)
+        gdn.prefill_local(xs[r], cw, gs[r], bs[r], ws, Hk, Hv, d, d, cu_seqlens=cu)
         ev[1].record()
-        gdn.chunk_prefill_local(q, k, v, gs[r], bs[r], ws, cu_seqlens=cu)
-        ev[2].record()
         gdn.chunk_prefill_state(ws, o, T, Hk, Hv, d, d, cu_seqlens=cu, final_state=fin)
-        ev[3].record()
+        ev[2].record()
         gdn.decode_step(dx, dcw, dcs[i % Rd], dg, db, dstate[i % Rd], Hk, Hv, d, d, o=do)
+        ev[3].record()
+        gdn.conv_qk_prep(xs[r], cw, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, q=q, k=k, v=v)
         ev[4].record()
+        gdn.chunk_prefill_local(q, k, v, gs[r], bs[r], ws, cu_seqlens=cu)
+        ev[5].record()
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -195,35 +211,37 @@ def main():
     def mean_ms(ev_list, j):
         return sum(ev[j].elapsed_time(ev[j + 1]) for ev in ev_list) / len(ev_list)
 
-    names = ["prep", "chunk_local", "state_pass", "decode"]
-    if not args.split_only:
+    def timed(fn, n_ev):
         for i in range(args.warmup):
-            step(i, events(4))
+            fn(i, events(n_ev))
         torch.cuda.synchronize()
-        evs = [events(4) for _ in range(args.steps)]
-        torch.cuda.synchronize()
+        evs = [events(n_ev) for _ in range(args.steps)]
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(args.warmup + i, evs[i])
+            fn(args.warmup + i, evs[i])
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        prep_ms, prefill_call_ms, decode_ms = (mean_ms(evs, j) for j in range(3))
-    for i in range(args.warmup):
-        step_split(i, events(5))
-    torch.cuda.synchronize()
-    evs2 = [events(5) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step_split(args.warmup + i, evs2[i])
-    torch.cuda.synchronize()
+        return evs, time.perf_counter() - t0
+
+    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local"]
+    two_call = None
+    if not args.split_only:
+        evs, wall = timed(step, 3)
+        prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)
+        evs_two, _ = timed(step_two, 3)
+        two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
+        two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,
+                    "tokens_per_s": T / ((two_prep + two_call_ms) / 1e3)}
+    evs2, wall2 = timed(step_split, 6)
     per = {n: mean_ms(evs2, j) for j, n in enumerate(names)}   # ms per launch (split phases)
     if args.split_only:   # profiler runs: the metric falls back to the split-phase prefill
-        wall = time.perf_counter() - t0
-        prep_ms, prefill_call_ms, decode_ms = per["prep"], per["chunk_local"] + per["state_pass"], per["decode"]
+        wall = wall2
+        prefill_ms = per["chunk_local_fused"] + per["state_pass"]
+        decode_ms = per["decode"]
 
     prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
-    prefill_ms = prep_ms + prefill_call_ms
     kern = {
+        "chunk_local_fused": {"bound": "mfma", "achieved": local_f / per["chunk_local_fused"] / 1e9,
+                              "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
         "prep": {"bound": "hbm", "achieved": prep_b / per["prep"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
         "chunk_local": {"bound": "mfma", "achieved": local_f / per["chunk_local"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
                         "unit": "TFLOP/s"},
@@ -236,7 +254,7 @@ def main():
         kern[n]["ms"] = per[n]
         kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
         kern[n]["traffic"] = traffic.get(n)
-    dominant = max(["prep", "chunk_local", "state_pass"], key=lambda n: per[n])
+    dominant = max(["chunk_local_fused", "state_pass"], key=lambda n: per[n])   # the metric path's prefill
     roof = {key: kern[dominant][key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
 
@@ -256,10 +274,11 @@ def main():
         "config": {"workload": "layer_4k prefill (T=4096, Hk=Hv=16, dk=dv=128, chunk 64, bf16 x, fp32 q/k/v/o) "
                                "+ decode256 step (B=256, fp32 state 256 MiB, 2 rotating state sets)",
                    "T": T, "heads_k": Hk, "heads_v": Hv, "head_dim": d, "chunk": 64, "decode_batch": B},
-        "prefill": {"ms": prefill_ms, "prep_ms": prep_ms, "chunk_prefill_ms": prefill_call_ms,
+        "prefill": {"ms": prefill_ms, "entry_point": "gdn_prefill" if not args.split_only else "split phases",
                     "tokens_per_s": T / (prefill_ms / 1e3),
                     "algorithmic_tflops": (local_f + state_f) / prefill_ms / 1e9,
                     "frac_mfma": (local_f + state_f) / prefill_ms / 1e9 / PEAK_MFMA_TFLOPS},
+        "prefill_two_call": two_call,
         "decode": {"ms": decode_ms, "tokens_per_s": B / (decode_ms / 1e3),
                    "state_gb_per_s": dec_b / decode_ms / 1e6, "frac_hbm": dec_b / decode_ms / 1e6 / PEAK_HBM_GBS,
                    "bytes_per_step": dec_b},

@@ -9,6 +9,7 @@ computation runs in the library's HIP kernels; there is no fallback.
 
     q, k, v = conv_qk_prep(x, conv_w, Hk, Hv, dk, dv, cu_seqlens, conv_state_in, conv_state_out)
     o, final_state = chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state)
+    o, final_state = prefill(x, conv_w, g, beta, Hk, Hv, dk, dv, cu_seqlens, ...)   # both in one call
     o = decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv)
 """
 from __future__ import annotations
@@ -18,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["conv_qk_prep", "chunk_prefill", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
+__all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
            "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "LIB_PATH", "abi_version", "mfma_supported"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -53,6 +54,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_chunk_prefill_local.restype = I
         L.gdn_chunk_prefill_state.argtypes = [P, I, P, P, P, I, I, I, I, I, P, Z, P]
         L.gdn_chunk_prefill_state.restype = I
+        L.gdn_prefill.argtypes = [P, P, P, I, P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_prefill.restype = I
+        L.gdn_prefill_local.argtypes = [P, P, P, I, P, P, P, P, F, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_prefill_local.restype = I
         L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P]
         L.gdn_decode_step.restype = I
         L.gdn_status_string.argtypes = [I]
@@ -132,6 +137,69 @@ def conv_qk_prep(x, conv_w, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
     if st != 0:
         raise GdnError("gdn_conv_qk_prep", st)
     return q, k, v
+
+
+def prefill(x, conv_w, g, beta, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None, conv_state_out=None,
+            initial_state=None, final_state=None, scale=1.0, l2_eps=1e-6, output_final_state=True, o=None,
+            workspace=None):
+    """conv_qk_prep + chunk_prefill (MFMA path) in one call, q / k / v never written out.
+
+    x [T, conv_dim] (bf16 or fp32), conv_w [conv_dim, 4]; g, beta [T, Hv] fp32; states
+    [N, Hv, dk, dv] fp32; conv states [N, 3, conv_dim].  Returns o [T, Hv, dv] fp32 and
+    the final state (None when output_final_state is False and none is given).
+    """
+    dt = x.dtype
+    C = 2 * Hk * dk + Hv * dv
+    _check(x, "x", dt)
+    if x.dim() != 2 or x.shape[1] != C:
+        raise ValueError(f"x must be [T, {C}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    cu, N = _seqs(cu_seqlens, T)
+    f32 = torch.float32
+    _check(conv_w, "conv_w", dt, (C, 4))
+    _check(conv_state_in, "conv_state_in", dt, (N, 3, C), optional=True)
+    _check(conv_state_out, "conv_state_out", dt, (N, 3, C), optional=True)
+    _check(g, "g", f32, (T, Hv))
+    _check(beta, "beta", f32, (T, Hv))
+    _check(initial_state, "initial_state", f32, (N, Hv, dk, dv), optional=True)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=f32, device=x.device)
+    _check(final_state, "final_state", f32, (N, Hv, dk, dv), optional=True)
+    o = torch.empty((T, Hv, dv), dtype=f32, device=x.device) if o is None else _check(o, "o", f32, (T, Hv, dv))
+    need = workspace_size(T, N, Hk, Hv, dk, dv, "mfma")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace")
+    st = lib().gdn_prefill(_p(x), _p(conv_w), _p(cu), N, _p(conv_state_in), _p(conv_state_out), _p(g), _p(beta),
+                           _p(initial_state), _p(final_state), _p(o), float(scale), float(l2_eps), T, Hk, Hv, dk, dv,
+                           _dt(x), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_prefill", st)
+    return o, final_state
+
+
+def prefill_local(x, conv_w, g, beta, workspace, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
+                  conv_state_out=None, scale=1.0, l2_eps=1e-6):
+    """First phase of `prefill` (conv prep + chunk-local records into `workspace`);
+    `chunk_prefill_state` finishes it."""
+    dt = x.dtype
+    C = 2 * Hk * dk + Hv * dv
+    _check(x, "x", dt)
+    if x.dim() != 2 or x.shape[1] != C:
+        raise ValueError(f"x must be [T, {C}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    cu, N = _seqs(cu_seqlens, T)
+    _check(conv_w, "conv_w", dt, (C, 4))
+    _check(conv_state_in, "conv_state_in", dt, (N, 3, C), optional=True)
+    _check(conv_state_out, "conv_state_out", dt, (N, 3, C), optional=True)
+    _check(g, "g", torch.float32, (T, Hv))
+    _check(beta, "beta", torch.float32, (T, Hv))
+    _check(workspace, "workspace")
+    st = lib().gdn_prefill_local(_p(x), _p(conv_w), _p(cu), N, _p(conv_state_in), _p(conv_state_out), _p(g),
+                                 _p(beta), float(scale), float(l2_eps), T, Hk, Hv, dk, dv, _dt(x), _p(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_prefill_local", st)
 
 
 def mfma_supported(dk, dv) -> bool:

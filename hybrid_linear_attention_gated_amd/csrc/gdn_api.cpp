@@ -166,6 +166,65 @@ int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N, const float *initi
                               workspace_bytes, stream, 2);
 }
 
+namespace {
+
+// Shared validation + dispatch of gdn_prefill (phases 3) and gdn_prefill_local (phase 1).
+int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N, const void *conv_state_in,
+                 void *conv_state_out, const float *g, const float *beta, const float *initial_state,
+                 float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
+                 int dtype, void *workspace, size_t workspace_bytes, void *stream, int phases) {
+    try {
+        if (int e = check_seqs(cu_seqlens, N, T)) return e;
+        if (!conv_w || (T > 0 && (!x || !g || !beta || ((phases & 2) && !o)))) return GDN_ERR_NULL_POINTER;
+        if (int e = check_heads(Hk, Hv)) return e;
+        if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+        if (!gdn::chunked_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
+        if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !std::isfinite(scale)) return GDN_ERR_BAD_SHAPE;
+        const size_t need = gdn::chunked_workspace_bytes(T, N, Hv, dk, dv);
+        if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
+        const size_t eb = elem_bytes(dtype);
+        const size_t conv_dim = 2 * (size_t)Hk * dk + (size_t)Hv * dv;
+        const size_t st_bytes = (size_t)N * Hv * dk * dv * 4;
+        const Range rx{x, (size_t)T * conv_dim * eb}, rw{conv_w, conv_dim * 4 * eb};
+        const Range rci{conv_state_in, (size_t)N * 3 * conv_dim * eb}, rco{conv_state_out, rci.bytes};
+        const Range rg{g, (size_t)T * Hv * 4}, rb{beta, rg.bytes}, rs0{initial_state, st_bytes},
+            rsf{final_state, st_bytes}, ro{o, (size_t)T * Hv * dv * 4}, rws{workspace, need};
+        for (Range in : {rx, rw, rci, rco, rg, rb, rs0, rsf, rws})
+            if (overlap(ro, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rx, rw, rci, rco, rg, rb, rws})
+            if (overlap(rsf, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rx, rw, rg, rb, rs0, rws})
+            if (overlap(rco, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rx, rw, rci, rg, rb, rs0})
+            if (overlap(rws, in)) return GDN_ERR_ALIAS;
+        if (bad_partial_alias(rsf, rs0) || bad_partial_alias(rco, rci)) return GDN_ERR_ALIAS;
+        const gdn::FusedPrep fp{x, conv_w, conv_state_in, conv_state_out, dtype == GDN_BF16, l2_eps};
+        gdn::PrefillArgs a{nullptr, nullptr, nullptr, g, beta, cu_seqlens, N, initial_state, final_state, o, scale,
+                           T, Hk, Hv, dk, dv, workspace, workspace_bytes, &fp};
+        return hip_status(gdn::launch_prefill_chunked(a, (hipStream_t)stream, phases));
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+}  // namespace
+
+int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N, const void *conv_state_in,
+                void *conv_state_out, const float *g, const float *beta, const float *initial_state,
+                float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
+                int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
+                        final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, dtype, workspace, workspace_bytes, stream, 3);
+}
+
+int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
+                      const void *conv_state_in, void *conv_state_out, const float *g, const float *beta,
+                      float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv, int dtype, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    return prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, nullptr, nullptr, nullptr,
+                        scale, l2_eps, T, Hk, Hv, dk, dv, dtype, workspace, workspace_bytes, stream, 1);
+}
+
 int gdn_decode_step(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
                     float *state, float *o, float scale, float l2_eps, int B, int Hk, int Hv, int dk, int dv,
                     int dtype, void *stream) {

@@ -180,6 +180,8 @@ struct LocalSmem {
     static constexpr int PT = AOFF + 6 * 2 * 64 * 8;         // P^T blocks c <= r: [10][64] f32x4
     static constexpr int XT = PT + 10 * 64 * 16;             // scaled T^T, M^T blocks c <= r: [4][10][hi, lo][64] bf16x4
     static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^G, e^{G_c - G}, scale e^G
+    static constexpr int VLD = D + 4;                        // fused conv: fp32 v plane [64][VLD] in the XT region
+    static_assert(64 * VLD * 4 <= SCAL - XT, "v plane fits in the T / M region");
     static constexpr int SIZE = SCAL + 5 * 64 * 4;
     static_assert(NW * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
 };
@@ -205,11 +207,17 @@ struct LocalSmem {
 //     selector picks 16 head-dim columns), exactly, and is stored as is.
 //     U waves: U' = (Dc T Bv) V and Ol = (M Bv) V.
 // Products use two-term bf16 splits of both operands (three MFMAs each).
-template <int D>
+// FUSED: q, k, v are not inputs; the workgroup runs the depthwise conv (kernel 4) + SiLU +
+// per-head L2 of q and k itself from the pre-conv input x (element type TX) of its 64 tokens
+// and the 3 before them ("7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2; history
+// from the sequence's own earlier tokens, else its conv cache, else zeros), with the same
+// arithmetic as gdn_conv_qk_prep.
+template <int D, bool FUSED, typename TX>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
-    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0) {
+    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0,
+    const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr int NWH = LocalShape<D>::NWH, NW = LocalShape<D>::NW, NT = LocalShape<D>::THREADS;
@@ -246,10 +254,10 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 
     // ---- global loads, all issued before any is used.  Rows >= L are clamped
     // (loads stay in bounds and unconditional) and zeroed.
-    constexpr int NV = 64 * (D / 4) / NT;
+    constexpr int NV = FUSED ? 1 : 64 * (D / 4) / NT;
     float4 kv[NV], qv[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+    for (int i = 0; i < NV && !FUSED; ++i) {
         const int e = tid + NT * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const size_t off = ((size_t)(t0 + min(r, L - 1)) * Hk + kh) * D + c4;
         kv[i] = *reinterpret_cast<const float4 *>(k + off);
@@ -258,7 +266,9 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // W waves: Q^T in accumulator layout (rows = head dim, cols = token) seeds Qt^T.
     // U waves: V in accumulator layout (rows = token) feeds U' and Ol.
     f32x4 Xa[2][4];
-    if (isW) {
+    if (FUSED) {
+        // filled from the planes after the conv (below)
+    } else if (isW) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
                     Xa[ni][rt][r] = t < L ? x : 0.f;
                 }
     }
-    if (wave == 0) {
+    if (wave == (FUSED ? NW - 1 : 0)) {
         const int rr = min(lane, L - 1);
         const float g0 = g[(size_t)(t0 + rr) * Hv + h], b0 = beta[(size_t)(t0 + rr) * Hv + h];
         const float gg = lane < L ? g0 : 0.f, bb = lane < L ? b0 : 0.f;
@@ -297,9 +307,81 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         QS[lane] = scale * eg;
         if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
     }
+    if constexpr (FUSED) {
+        // Waves 0 .. 3D/64 - 1 convolve: D/64 waves per group (q, k, v of this workgroup's
+        // heads); lane = (token group tg, 8-channel block cb), 8 tokens x 8 channels each.
+        // Rows past the chunk's last token are zeros (SiLU(0) = 0, and a zero vector stays
+        // zero under the L2 norm), so padded rows of the planes are zero.
+        constexpr int CB = D / 8, TGW = 64 / CB, WPG = D / 64;
+        if (wave < 3 * WPG) {
+            const int grp = wave / WPG, th = wave % WPG;
+            const int cb = lane % CB, tg = lane / CB;
+            const int ch0 = (grp == 0 ? kh * D : grp == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D) + 8 * cb;
+            const int conv_dim = 2 * Hk * D + Hv * D;
+            const int tl0 = th * TGW * 8 + 8 * tg;   // first local token of this lane
+            const bool first = c_ == 0;              // history before the sequence start
+            Raw8<TX> rows[11];
+#pragma unroll
+            for (int r = 0; r < 11; ++r) {
+                const int tl = tl0 - kConvHist + r;
+                if (tl < L && (tl >= 0 || !first)) rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
+                else if (tl < 0 && cs_in) rows[r].load(cs_in + ((size_t)s_ * kConvHist + (kConvHist + tl)) * conv_dim + ch0);
+                else rows[r].zero();
+            }
+            float wt[4][8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wt[j][i] = to_f32(conv_w[(size_t)(ch0 + i) * kConvK + j]);
+            float hw[3][8];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) rows[j].to_f32(hw[j]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float xt[8], y[8];
+                rows[i + kConvHist].to_f32(xt);
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float acc = wt[0][e] * hw[0][e];
+                    acc = fmaf(wt[1][e], hw[1][e], acc);
+                    acc = fmaf(wt[2][e], hw[2][e], acc);
+                    acc = fmaf(wt[3][e], xt[e], acc);
+                    y[e] = silu(acc);
+                    ss = fmaf(y[e], y[e], ss);
+                }
+                const int tl = tl0 + i;
+                if (tl >= L) {   // padded row: zero (its conv window still reaches real rows)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+                    ss = 0.f;
+                }
+                if (grp < 2) {
+                    ss = group_sum<CB>(ss);
+                    const float rn = rsqrtf(ss + l2_eps);
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float yn = y[e] * rn;
+                        hi[e] = (bf16)yn;
+                        lo[e] = (bf16)(yn - (float)hi[e]);
+                    }
+                    bf16 *ph = grp == 0 ? Qh : Kh, *pl = grp == 0 ? Ql : Kl;
+                    *reinterpret_cast<bf16x8 *>(ph + tl * LD + 8 * cb) = hi;
+                    *reinterpret_cast<bf16x8 *>(pl + tl * LD + 8 * cb) = lo;
+                } else {
+                    float *vp = reinterpret_cast<float *>(smem + SM::XT) + tl * SM::VLD + 8 * cb;
+                    *reinterpret_cast<f32x4 *>(vp) = f32x4{y[0], y[1], y[2], y[3]};
+                    *reinterpret_cast<f32x4 *>(vp + 4) = f32x4{y[4], y[5], y[6], y[7]};
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { hw[0][e] = hw[1][e]; hw[1][e] = hw[2][e]; hw[2][e] = xt[e]; }
+            }
+        }
+    }
     // K and Q as bf16 hi / lo planes, row-major [token][head dim]
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
+    for (int i = 0; i < NV && !FUSED; ++i) {
         const int e = tid + NT * i, r = e / (D / 4), c4 = (e % (D / 4)) * 4;
         const bool live = r < L;
         const float kk[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
@@ -390,6 +472,29 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // K^T operand (lane row = head dim, k = token in kperm order) with no rounding.  They go to
     // the record as they are and stay as this wave's A operand of step 4.
     // U waves: V as B operands (k = token in kperm order).
+    if constexpr (FUSED) {
+        if (isW) {   // Q^T seed from the q planes (hi + lo)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int off = (16 * tt + l16) * LD + 16 * (2 * qw + mi) + 4 * kg;
+                    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(Qh + off);
+                    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(Ql + off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Xa[mi][tt][e] = (float)a[e] + (float)b[e];
+                }
+        } else {     // V in accumulator layout from the fp32 v plane
+            const float *vp = reinterpret_cast<const float *>(smem + SM::XT);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        Xa[ni][rt][r] = vp[(16 * rt + 4 * kg + r) * SM::VLD + 16 * (2 * qw + ni) + l16];
+        }
+    }
     Split8 Bop[2][2];   // [tile][token k step]
     if (isW) {
         bf16x8 sel[2];
@@ -935,8 +1040,21 @@ static hipError_t pipe_resources(PipeRes **out) {
 template <int D>
 static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
     if (g1 <= g0 || a.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_local_kernel<D>), dim3((unsigned)(g1 - g0), a.Hv), dim3(LocalShape<D>::THREADS), 0,
-                       st, a.q, a.k, a.v, a.g, a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, (char *)a.ws, nc, g0);
+    const dim3 grid((unsigned)(g1 - g0), a.Hv), block(LocalShape<D>::THREADS);
+    char *ws = (char *)a.ws;
+    if (!a.fp) {
+        hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)nullptr,
+                           (const float *)nullptr, (const float *)nullptr, 0.f);
+    } else if (a.fp->bf16) {
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const bf16 *)a.fp->x,
+                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps);
+    } else {
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)a.fp->x,
+                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps);
+    }
     return hipGetLastError();
 }
 
@@ -952,6 +1070,14 @@ static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int
     return hipGetLastError();
 }
 
+// Fused prefill: conv_state_out after everything that reads conv_state_in (it may alias it).
+static hipError_t launch_fused_cs_out(const PrefillArgs &a, hipStream_t st) {
+    if (!a.fp || !a.fp->cs_out) return hipSuccess;
+    PrepArgs p{a.fp->x, a.fp->w, a.cu, a.N, a.fp->cs_in, a.fp->cs_out, nullptr, nullptr, nullptr,
+               a.T, a.Hk, a.Hv, a.dk, a.dv, a.fp->bf16, a.fp->eps};
+    return launch_conv_state_out(p, st);
+}
+
 template <int D>
 static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int phases) {
     const int nc = (int)max_chunks(a.T, a.N);
@@ -959,6 +1085,8 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     if (phases != 3) {   // one phase on its own (split-phase entry points)
         if (phases & 1) {
             e = launch_local<D>(a, st, nc, 0, nc);
+            if (e != hipSuccess) return e;
+            e = launch_fused_cs_out(a, st);
             if (e != hipSuccess) return e;
         }
         if (phases & 2) return launch_state<D>(a, st, nc, 0, nc);
@@ -968,7 +1096,9 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     if (G == 1) {
         e = launch_local<D>(a, st, nc, 0, nc);
         if (e != hipSuccess) return e;
-        return launch_state<D>(a, st, nc, 0, nc);
+        e = launch_state<D>(a, st, nc, 0, nc);
+        if (e != hipSuccess) return e;
+        return launch_fused_cs_out(a, st);
     }
     PipeRes *pr = nullptr;
     e = pipe_resources(&pr);
@@ -981,7 +1111,8 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
         if ((e = launch_state<D>(a, pr->side, nc, g0, g1)) != hipSuccess) return e;
     }
     if ((e = hipEventRecord(pr->ev[kMaxSegments], pr->side)) != hipSuccess) return e;
-    return hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0);
+    if ((e = hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0)) != hipSuccess) return e;
+    return launch_fused_cs_out(a, st);
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases) {

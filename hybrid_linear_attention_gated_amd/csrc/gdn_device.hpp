@@ -59,6 +59,32 @@ template <> struct Vec8<float> {
     }
 };
 
+template <typename T> struct Raw8;    // 8 elements as loaded, converted later
+template <> struct Raw8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (bf16)0.f;
+    }
+    __device__ __forceinline__ void to_f32(float *o) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = *reinterpret_cast<const float4 *>(p);
+        b = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
+    __device__ __forceinline__ void to_f32(float *o) const {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+
+
 // SiLU y * sigmoid(y) with the hardware reciprocal (about 1 ulp) instead of an
 // IEEE division sequence; for y < -88 the exponential overflows to +inf and the
 // result is -0, the limit of the function.

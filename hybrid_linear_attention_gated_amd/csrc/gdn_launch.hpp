@@ -21,6 +21,16 @@ struct PrepArgs {
     float eps;
 };
 
+// Pre-conv inputs of the fused prefill (gdn_prefill): the chunk-local kernel runs the conv
+// prep itself, and q, k, v of PrefillArgs are unused.
+struct FusedPrep {
+    const void *x, *w;
+    const void *cs_in;
+    void *cs_out;
+    bool bf16;   // element type of x / conv_w / conv states
+    float eps;
+};
+
 struct PrefillArgs {
     const float *q, *k, *v;
     const float *g, *beta;
@@ -33,6 +43,7 @@ struct PrefillArgs {
     int T, Hk, Hv, dk, dv;
     void *ws;
     size_t ws_bytes;
+    const FusedPrep *fp = nullptr;   // set: fused prep (chunked path only)
 };
 
 struct DecodeArgs {
@@ -47,6 +58,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
+// conv_state_out[s] = last three inputs of sequence s (a launch of its own)
+hipError_t launch_conv_state_out(const PrepArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 
 // token-recurrent fp32 path (GDN_F32 and the small head dims)

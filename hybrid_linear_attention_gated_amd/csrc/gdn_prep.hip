@@ -28,26 +28,6 @@ constexpr int kPrepTokPerWave = 16;
 constexpr int kPrepWaves = 4;
 constexpr int kPrepChan = 8 * kWave;  // channels per wave
 
-template <typename T> struct Raw8;    // 8 elements as loaded, converted later
-template <> struct Raw8<bf16> {
-    bf16x8 v;
-    __device__ __forceinline__ void load(const bf16 *p) { v = *reinterpret_cast<const bf16x8 *>(p); }
-    __device__ __forceinline__ void to_f32(float *o) const {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
-    }
-};
-template <> struct Raw8<float> {
-    float4 a, b;
-    __device__ __forceinline__ void load(const float *p) {
-        a = *reinterpret_cast<const float4 *>(p);
-        b = *reinterpret_cast<const float4 *>(p + 4);
-    }
-    __device__ __forceinline__ void to_f32(float *o) const {
-        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-    }
-};
-
 // conv_state_out[s] = the last three inputs of sequence s (from conv_state_in when the
 // sequence is shorter than three), for channels c of this thread.
 template <typename T>
@@ -240,6 +220,20 @@ static hipError_t launch_prep_dk(const PrepArgs &a, hipStream_t st) {
         case 256: return launch_prep_t<T, 256>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <typename T>
+static hipError_t launch_cs_out_t(const PrepArgs &a, hipStream_t st) {
+    const int conv_dim = 2 * a.Hk * a.dk + a.Hv * a.dv;
+    if (!a.cs_out || a.N <= 0) return hipSuccess;
+    dim3 grid((conv_dim + 255) / 256, a.N);
+    hipLaunchKernelGGL((conv_state_out_kernel<T>), grid, dim3(256), 0, st,
+                       (const T *)a.x, a.cu, a.N, (const T *)a.cs_in, (T *)a.cs_out, a.T, conv_dim);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_state_out(const PrepArgs &a, hipStream_t st) {
+    return a.bf16 ? launch_cs_out_t<bf16>(a, st) : launch_cs_out_t<float>(a, st);
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {

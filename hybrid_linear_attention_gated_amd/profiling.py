@@ -27,7 +27,8 @@ _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNELS = [
     ("prep_kernel", "prep"),
     ("conv_state_out_kernel", "conv_state_out"),
-    ("chunk_local_kernel", "chunk_local"),
+    ("chunk_local_kernel", "chunk_local"),   # "chunk_local_fused" for the FUSED = true instances
+    ("chunk_local_fused", "chunk_local_fused"),
     ("state_pass_kernel", "state_pass"),
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
@@ -39,6 +40,8 @@ COPY_NAMES = ("elementwise_kernel",)
 
 
 def short_name(symbol: str) -> str:
+    if "chunk_local_kernel" in symbol and ("ELb1E" in symbol or ", true," in symbol):
+        return "chunk_local_fused"   # mangled or demangled template argument FUSED = true
     for frag, short in KERNELS:
         if frag in symbol:
             return short

@@ -167,6 +167,45 @@ int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N,
                             const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill -- gdn_conv_qk_prep and gdn_chunk_prefill (GDN_MATH_MFMA) in one call,
+ * with the conv prep fused into the chunk-local phase: q, k and v are formed in
+ * on-chip memory for each chunk and never written to HBM.  The conv + SiLU + L2 is
+ * that of gdn_conv_qk_prep ("7.6 Qwen3.5: the linear-attention hybrid", section
+ * 7.6.2) and the recurrence that of gdn_chunk_prefill ("Hugging Face Transformers:
+ * Qwen3.5-MoE series explained", sections 4.3 and 8.2).
+ *
+ *   x, conv_w, conv_state_in, conv_state_out, dtype, l2_eps   as in gdn_conv_qk_prep
+ *                  (conv_state_out may alias conv_state_in exactly, or be NULL)
+ *   g, beta, initial_state, final_state, o, scale   as in gdn_chunk_prefill
+ *   dk = dv in {64, 128} (GDN_ERR_UNSUPPORTED otherwise)
+ *   workspace      at least gdn_chunk_prefill_workspace_size(T, N, Hk, Hv, dk, dv,
+ *                  GDN_MATH_MFMA) bytes; must not overlap any other argument.
+ * o, final_state and conv_state_out must not overlap any input except the exact
+ * aliases named above.  Errors as for the two calls it replaces.
+ */
+int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
+                const void *conv_state_in, void *conv_state_out,
+                const float *g, const float *beta,
+                const float *initial_state, float *final_state, float *o,
+                float scale, float l2_eps,
+                int T, int Hk, int Hv, int dk, int dv, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_local -- the first phase of gdn_prefill: conv prep + chunk-local
+ * quantities into `workspace` (and conv_state_out, written after the phase has
+ * read conv_state_in), for callers that schedule the phases separately.
+ * gdn_chunk_prefill_state then consumes the workspace exactly as after
+ * gdn_chunk_prefill_local; the two together equal one gdn_prefill call.
+ * Arguments mean what they mean for gdn_prefill.
+ */
+int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
+                      const void *conv_state_in, void *conv_state_out,
+                      const float *g, const float *beta, float scale, float l2_eps,
+                      int T, int Hk, int Hv, int dk, int dv, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one token for each of B sequences: advance the conv cache by
  * one input, conv + SiLU + L2 on the window, one step of the recurrence on the
  * state, in place (the decode branch of "Hugging Face Transformers: Qwen3.5-MoE

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
-    assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size",
+    assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_prefill",
             "gdn_decode_step", "gdn_status_string", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
@@ -94,6 +94,44 @@ def test_prefill_validation(L):
     assert call(o=P(16)) == 6                                   # o overlaps q
     assert call(s0=P(6 << 24), sf=P((6 << 24) + 4)) == 6          # partial state alias
     assert call(scale=float("inf")) == 2
+
+
+def test_fused_prefill_validation(L):
+    P = _ptr
+    T, Hk, Hv, d = 128, 2, 2, 128
+    need = L.gdn_chunk_prefill_workspace_size(T, 1, Hk, Hv, d, d, 1)
+    base = dict(x=P(0), w=P(1 << 24), cu=None, N=1, csi=None, cso=None, g=P(3 << 24), b=P(4 << 24), s0=None,
+                sf=None, o=P(5 << 24), scale=1.0, eps=1e-6, T=T, Hk=Hk, Hv=Hv, dk=d, dv=d, dt=1, ws=P(1 << 30),
+                wsb=need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_prefill(a["x"], a["w"], a["cu"], a["N"], a["csi"], a["cso"], a["g"], a["b"], a["s0"], a["sf"],
+                             a["o"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["T"], a["Hk"], a["Hv"],
+                             a["dk"], a["dv"], a["dt"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
+    assert call(w=None) == 1
+    assert call(x=None) == 1
+    assert call(o=None) == 1
+    assert call(Hk=3, Hv=4) == 2
+    assert call(N=2) == 2                                       # no cu_seqlens with N > 1
+    assert call(eps=float("nan")) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(dt=5) == 3
+    assert call(dk=32, dv=32) == 3                              # no chunked path for head dim 32
+    assert call(ws=None) == 4
+    assert call(wsb=need - 1) == 4
+    assert call(o=P(16)) == 6                                   # o overlaps x
+    assert call(cso=P(1 << 24)) == 6                            # conv cache overlaps the weights
+    assert call(csi=P(6 << 24), cso=P((6 << 24) + 2)) == 6      # partial conv cache alias
+    assert call(s0=P(7 << 24), sf=P((7 << 24) + 4)) == 6        # partial state alias
+    assert call(ws=P(8)) == 6                                   # workspace overlaps x
+    # the local phase alone: no o or states
+    assert L.gdn_prefill_local(P(0), None, None, 1, None, None, P(3 << 24), P(4 << 24), ctypes.c_float(1.0),
+                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, P(1 << 30), ctypes.c_size_t(need),
+                               None) == 1                       # no conv weights
+    assert L.gdn_prefill_local(P(0), P(1 << 24), None, 1, None, None, P(3 << 24), P(4 << 24), ctypes.c_float(1.0),
+                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, P(1 << 30), ctypes.c_size_t(need - 1),
+                               None) == 4
 
 
 def test_decode_validation(L):

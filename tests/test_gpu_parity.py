@@ -222,7 +222,7 @@ def test_core_empty_sequences(gdn):
 
 # ------------------------------------------------------------------ end to end: prep + chunk prefill
 
-def _e2e(gdn, wl, heads=None):
+def _e2e(gdn, wl, heads=None, fused=False):
     cu = wl.cu_seqlens
     N = wl.N
     x32 = f32np(wl.x)
@@ -233,10 +233,15 @@ def _e2e(gdn, wl, heads=None):
                                      s0=None if wl.state is None else f32np(wl.state), heads=heads)
     del q_r, k_r, v_r
     cso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=DEV)
-    q, k, v = gdn.conv_qk_prep(_cuda(wl.x), _cuda(wl.conv_w), wl.Hk, wl.Hv, wl.dk, wl.dv, cu_seqlens=_cuda(cu),
-                               conv_state_in=_cuda(wl.conv_state), conv_state_out=cso)
-    o, f = gdn.chunk_prefill(q, k, v, _cuda(wl.g), _cuda(wl.beta), cu_seqlens=_cuda(cu),
-                             initial_state=_cuda(wl.state), math="mfma")
+    if fused:
+        o, f = gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), wl.Hk, wl.Hv, wl.dk, wl.dv,
+                           cu_seqlens=_cuda(cu), conv_state_in=_cuda(wl.conv_state), conv_state_out=cso,
+                           initial_state=_cuda(wl.state))
+    else:
+        q, k, v = gdn.conv_qk_prep(_cuda(wl.x), _cuda(wl.conv_w), wl.Hk, wl.Hv, wl.dk, wl.dv,
+                                   cu_seqlens=_cuda(cu), conv_state_in=_cuda(wl.conv_state), conv_state_out=cso)
+        o, f = gdn.chunk_prefill(q, k, v, _cuda(wl.g), _cuda(wl.beta), cu_seqlens=_cuda(cu),
+                                 initial_state=_cuda(wl.state), math="mfma")
     torch.cuda.synchronize()
     o, f = f32np(o), f32np(f)
     if heads is not None:
@@ -259,6 +264,110 @@ def test_varlen8_config(gdn):
 def test_long_64k_config_sampled_heads(gdn):
     announce("long_64k config end to end (oracle on sampled value heads 0, 1, 17, 31)")
     _e2e(gdn, inputs.long_64k(), heads=[0, 1, 17, 31])
+
+
+# ------------------------------------------------------------------ fused prep + chunk prefill (one call)
+
+def test_fused_layer_4k_config(gdn):
+    announce("layer_4k config, fused prefill")
+    _e2e(gdn, inputs.layer_4k(), fused=True)
+
+
+def test_fused_varlen8_config(gdn):
+    announce("varlen8 config, fused prefill")
+    _e2e(gdn, inputs.varlen8(), fused=True)
+
+
+def test_fused_long_64k_config_sampled_heads(gdn):
+    announce("long_64k config, fused prefill (oracle on sampled value heads 0, 1, 17, 31)")
+    _e2e(gdn, inputs.long_64k(), heads=[0, 1, 17, 31], fused=True)
+
+
+# short and empty sequences, sequences shorter than the conv window, ragged tails
+FUSED_LENGTHS = [1, 2, 0, 37, 64, 65, 3, 200, 129]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_fused_small_varlen(gdn, dtype, d):
+    announce(f"fused prefill {dtype} d={d} lengths={FUSED_LENGTHS}")
+    wl = inputs.prefill_workload("fused_small", 910 + d, FUSED_LENGTHS, 2, 4, d, random_states=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x, w, cs = wl.x.to(tdt), wl.conv_w.to(tdt), wl.conv_state.to(tdt)
+    cu = wl.cu_seqlens
+    q_r, k_r, v_r, cs_r = oracle.prep(f32np(x), f32np(w), cu.numpy(), 2, 4, d, d, cs_in=f32np(cs))
+    o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu.numpy(), s0=f32np(wl.state),
+                                     scale=0.3)
+    cso = torch.empty(cs.shape, dtype=tdt, device=DEV)
+    o, f = gdn.prefill(_cuda(x), _cuda(w), _cuda(wl.g), _cuda(wl.beta), 2, 4, d, d, cu_seqlens=_cuda(cu),
+                       conv_state_in=_cuda(cs), conv_state_out=cso, initial_state=_cuda(wl.state), scale=0.3)
+    torch.cuda.synchronize()
+    assert_parity("o", f32np(o), o_ref, TOL_BF16)
+    assert_parity("final_state", f32np(f), f_ref, TOL_BF16)
+    np.testing.assert_array_equal(f32np(cso), cs_r)
+    # conv_state_out aliasing conv_state_in, final_state aliasing initial_state
+    csd, sd = _cuda(cs), _cuda(wl.state)
+    o2, f2 = gdn.prefill(_cuda(x), _cuda(w), _cuda(wl.g), _cuda(wl.beta), 2, 4, d, d, cu_seqlens=_cuda(cu),
+                         conv_state_in=csd, conv_state_out=csd, initial_state=sd, final_state=sd, scale=0.3)
+    torch.cuda.synchronize()
+    assert f2 is sd
+    assert torch.equal(o2, o)
+    assert torch.equal(sd, f)
+    np.testing.assert_array_equal(f32np(csd), cs_r)
+    # zero conv history and zero initial state
+    q0, k0, v0, _ = oracle.prep(f32np(x), f32np(w), cu.numpy(), 2, 4, d, d)
+    o0_ref, f0_ref = oracle.recurrence(q0, k0, v0, f32np(wl.g), f32np(wl.beta), cu.numpy())
+    o0, f0 = gdn.prefill(_cuda(x), _cuda(w), _cuda(wl.g), _cuda(wl.beta), 2, 4, d, d, cu_seqlens=_cuda(cu))
+    torch.cuda.synchronize()
+    assert_parity("o (zero history)", f32np(o0), o0_ref, TOL_BF16)
+    assert_parity("final_state (zero history)", f32np(f0), f0_ref, TOL_BF16)
+
+
+def test_fused_segmented_varlen(gdn):
+    """Enough chunks that the one call runs the segment pipeline (local and state
+    passes on two streams)."""
+    lengths = [3000, 1, 0, 2000, 65, 129, 2500]
+    announce(f"fused prefill, segmented pipeline, lengths={lengths}")
+    _e2e(gdn, inputs.prefill_workload("fused_seg", 913, lengths, 2, 4, 128, random_states=True), fused=True)
+
+
+def test_fused_equals_split_phases(gdn):
+    """gdn_prefill_local + gdn_chunk_prefill_state run the same kernels as one gdn_prefill
+    call (which overlaps them segment by segment): results are bit-identical."""
+    lengths = [3000, 1, 0, 2000, 65, 129, 2500]
+    announce("one-call fused prefill == prefill_local + chunk_prefill_state (bitwise)")
+    wl = inputs.prefill_workload("fused_split", 914, lengths, 2, 4, 128, random_states=True)
+    x, w, g, b, cu, s0, cs = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.cu_seqlens, wl.state,
+                                                 wl.conv_state))
+    cso1, cso2 = torch.empty_like(cs), torch.empty_like(cs)
+    o1, f1 = gdn.prefill(x, w, g, b, 2, 4, 128, 128, cu_seqlens=cu, conv_state_in=cs, conv_state_out=cso1,
+                         initial_state=s0)
+    ws = torch.empty(gdn.workspace_size(wl.T, wl.N, 2, 4, 128, 128, "mfma"), dtype=torch.uint8, device=DEV)
+    o2, f2 = torch.empty_like(o1), torch.empty_like(f1)
+    gdn.prefill_local(x, w, g, b, ws, 2, 4, 128, 128, cu_seqlens=cu, conv_state_in=cs, conv_state_out=cso2)
+    gdn.chunk_prefill_state(ws, o2, wl.T, 2, 4, 128, 128, cu_seqlens=cu, initial_state=s0, final_state=f2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(f1, f2)
+    assert torch.equal(cso1, cso2)
+
+
+def test_fused_all_empty(gdn):
+    announce("fused prefill: all sequences empty (T = 0)")
+    Hk, Hv, d = 2, 4, 128
+    C = 2 * Hk * d + Hv * d
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    x = torch.empty((0, C), dtype=torch.bfloat16, device=DEV)
+    w = torch.randn((C, 4), device=DEV).to(torch.bfloat16)
+    z = torch.empty((0, Hv), dtype=torch.float32, device=DEV)
+    s0 = torch.randn((3, Hv, d, d), device=DEV)
+    cs = torch.randn((3, 3, C), device=DEV).to(torch.bfloat16)
+    cso = torch.empty_like(cs)
+    o, f = gdn.prefill(x, w, z, z, Hk, Hv, d, d, cu_seqlens=cu, conv_state_in=cs, conv_state_out=cso,
+                       initial_state=s0)
+    torch.cuda.synchronize()
+    assert o.shape == (0, Hv, d)
+    assert torch.equal(f, s0)
+    assert torch.equal(cso, cs)
 
 
 # ------------------------------------------------------------------ decode steps == prefill
