@@ -1009,6 +1009,32 @@ size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
 // only (no spinning).  Each device gets one such stream (default priority) and a small
 // pool of events, created on first use and kept for the life of the process.
 constexpr int kMaxSegments = 4;
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static std::mutex mu;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0 && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus[dev] = 0;
+    return cus[dev];
+}
+
+// Number of pipeline segments.  The overlap pays only when the state pass is long and
+// leaves at least half of the compute units to the chunk-local kernel: otherwise the two
+// kernels contend for compute units and memory and the event hops between the streams
+// cost more than the overlap hides.  (Measured on MI355X, one gdn_prefill call:
+// 4096 tokens x 16 heads, 65 chunks, 64 state workgroups: 170 us unsegmented, 183 us in
+// 4 segments; 8 sequences, 606 chunks, 512 state workgroups: 1.14 ms vs 1.24 ms;
+// 65536 tokens x 32 heads, 1025 chunks, 128 state workgroups: 4.22 ms vs 3.64 ms.)
+static int pipeline_segments(int nc, int state_blocks) {
+    const int cus = device_cus();
+    if (nc < 256 || cus <= 0 || 2 * state_blocks > cus) return 1;
+    return std::min(kMaxSegments, nc / 64);
+}
+
 struct PipeRes {
     hipStream_t side = nullptr;
     hipEvent_t ev[kMaxSegments + 1] = {};
@@ -1059,11 +1085,13 @@ static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int
 }
 
 template <int D>
+static int state_blocks(int units) { return 8 * (D / 32) * ((units + 7) / 8); }
+
+template <int D>
 static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
-    constexpr int NP = D / 32;
-    const int blocks = 8 * NP * ((units + 7) / 8);
+    const int blocks = state_blocks<D>(units);
     float *mid = reinterpret_cast<float *>((char *)a.ws + (size_t)nc * a.Hv * Rec<D>::SIZE);
     hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T, a.Hv,
                        units, a.s0, a.sf, a.o, nc, g0, g1, mid);
@@ -1092,7 +1120,7 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
         if (phases & 2) return launch_state<D>(a, st, nc, 0, nc);
         return hipSuccess;
     }
-    const int G = std::max(1, std::min(kMaxSegments, nc / 8));
+    const int G = pipeline_segments(nc, state_blocks<D>(a.N * a.Hv));
     if (G == 1) {
         e = launch_local<D>(a, st, nc, 0, nc);
         if (e != hipSuccess) return e;

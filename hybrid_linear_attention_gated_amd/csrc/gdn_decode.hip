@@ -74,7 +74,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const int i = rg + RG * r;
-            S[r] = row_active ? *reinterpret_cast<const float4 *>(sp + (size_t)i * DV) : make_float4(0, 0, 0, 0);
+            // non-temporal: the state is read once per step and is as large as the Infinity
+            // Cache, so its lines are not kept there (they would evict, for example, a
+            // prefill workspace that the next prefill call rewrites and reads back)
+            S[r] = make_float4(0, 0, 0, 0);
+            if (row_active) {
+                const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(sp + (size_t)i * DV));
+                S[r] = make_float4(t[0], t[1], t[2], t[3]);
+            }
         }
     };
     load_state(kh * group);

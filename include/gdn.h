@@ -20,8 +20,8 @@
  *    no pointer after a call returns and allocates no device memory.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *    work is enqueued asynchronously on it; buffers must stay valid until the
- *    stream work completes.  gdn_chunk_prefill with GDN_MATH_MFMA may run part of
- *    its work on a second stream of the library (created once per device, default
+ *    stream work completes.  gdn_chunk_prefill with GDN_MATH_MFMA and gdn_prefill
+ *    may run part of their work on a second stream of the library (created once per device, default
  *    priority, kept with a few events for the life of the process); that work is
  *    ordered after everything enqueued on `stream` before the call and before
  *    everything enqueued on it after the call, so to the caller it behaves as if
@@ -130,11 +130,13 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *                  of the chunk-local phase and one state per (sequence, value head).
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
  *
- * With GDN_MATH_MFMA and more than a few chunks, the packed chunks are cut into up
- * to four segments: the chunk-local phase of segment k + 1 runs while the state
- * pass of segment k runs (on the library's second stream, see the conventions);
- * a sequence's state passes between segments through the workspace.  The result
- * is bit-identical to running the two phases below one after the other.
+ * With GDN_MATH_MFMA, when the packed chunks are many (at least 256) and the state
+ * pass would occupy at most half of the device's compute units, the chunks are cut
+ * into up to four segments: the chunk-local phase of segment k + 1 runs while the
+ * state pass of segment k runs (on the library's second stream, see the
+ * conventions); a sequence's state passes between segments through the workspace.
+ * Otherwise the two phases run once each on the caller's stream.  Either way the
+ * result is bit-identical to running the two phases below one after the other.
  */
 int gdn_chunk_prefill(const float *q, const float *k, const float *v,
                       const float *g, const float *beta,

@@ -175,10 +175,11 @@ def test_core_f32_inplace_state(gdn):
     _core_case(gdn, wl, "f32", inplace=True)
 
 
-# 41 packed chunks: the one-call prefill cuts them into four pipeline segments, so
-# sequences start and end inside segments and span several of them; the batch also holds
-# an empty and a one-token sequence.
-SEGMENTED_LENGTHS = [300, 1, 0, 700, 65, 129, 1000]
+# 275 packed chunks (T / 64 + N) over 7 sequences x 4 value heads (128 state-pass
+# workgroups, half of MI355X's 256 compute units): the one-call prefill cuts them into four
+# pipeline segments, so sequences start and end inside segments and span several of them;
+# the batch also holds an empty and a one-token sequence.
+SEGMENTED_LENGTHS = [9000, 1, 0, 5000, 65, 129, 3000]
 
 
 def test_core_chunked_segmented_varlen(gdn):
@@ -325,17 +326,16 @@ def test_fused_small_varlen(gdn, dtype, d):
 def test_fused_segmented_varlen(gdn):
     """Enough chunks that the one call runs the segment pipeline (local and state
     passes on two streams)."""
-    lengths = [3000, 1, 0, 2000, 65, 129, 2500]
-    announce(f"fused prefill, segmented pipeline, lengths={lengths}")
-    _e2e(gdn, inputs.prefill_workload("fused_seg", 913, lengths, 2, 4, 128, random_states=True), fused=True)
+    announce(f"fused prefill, segmented pipeline, lengths={SEGMENTED_LENGTHS}")
+    _e2e(gdn, inputs.prefill_workload("fused_seg", 913, SEGMENTED_LENGTHS, 2, 4, 128, random_states=True),
+         fused=True)
 
 
 def test_fused_equals_split_phases(gdn):
     """gdn_prefill_local + gdn_chunk_prefill_state run the same kernels as one gdn_prefill
     call (which overlaps them segment by segment): results are bit-identical."""
-    lengths = [3000, 1, 0, 2000, 65, 129, 2500]
     announce("one-call fused prefill == prefill_local + chunk_prefill_state (bitwise)")
-    wl = inputs.prefill_workload("fused_split", 914, lengths, 2, 4, 128, random_states=True)
+    wl = inputs.prefill_workload("fused_split", 914, SEGMENTED_LENGTHS, 2, 4, 128, random_states=True)
     x, w, g, b, cu, s0, cs = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.cu_seqlens, wl.state,
                                                  wl.conv_state))
     cso1, cso2 = torch.empty_like(cs), torch.empty_like(cs)
