@@ -49,6 +49,8 @@ def lib():
         L.oracle_recurrence.restype = None
         L.oracle_decode.argtypes = [P, P, P, P, P, P, P, P, P, d, d, i, i, i, i, i]
         L.oracle_decode.restype = None
+        L.oracle_gated_rmsnorm.argtypes = [P, P, P, P, ctypes.c_long, i, d]
+        L.oracle_gated_rmsnorm.restype = None
         _lib = L
     return _lib
 
@@ -113,3 +115,18 @@ def decode(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=1e-6):
     lib().oracle_decode(_p(x), _p(w), _p(cs), _p(cs_out), _p(g), _p(beta), _p(st), _p(st_out), _p(o),
                         float(scale), float(eps), B, Hk, Hv, dk, dv)
     return o, st_out, cs_out
+
+
+def gated_rmsnorm(y, z, gamma, eps=1e-6):
+    """fp64 gated RMSNorm over the last axis: y / sqrt(mean y^2 + eps) * gamma * SiLU(z).
+    y [..., dv] (any float dtype, used as fp64), z same shape and gamma [dv] with
+    float32-representable values."""
+    y = _f64(y)
+    dv = y.shape[-1]
+    z = _f32(z)
+    gamma = _f32(gamma)
+    assert z.shape == y.shape and gamma.shape == (dv,)
+    out = np.zeros(y.shape)
+    rows = y.size // dv if dv else 0
+    lib().oracle_gated_rmsnorm(_p(y), _p(z), _p(gamma), _p(out), rows, dv, float(eps))
+    return out

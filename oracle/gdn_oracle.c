@@ -271,3 +271,30 @@ void oracle_decode(const float *x, const float *w, const float *cs_in, double *c
         free(y); free(qs); free(kn); free(m); free(delta); free(S);
     }
 }
+
+/*
+ * Gated RMSNorm epilogue of the layer output, [Book] 7.6.2 ("gated RMSNorm
+ * output": o = RMSNorm(y) (.) SiLU(z), z a separate projection of the layer
+ * input) with the RMSNorm of [Book] 7.6.3 (x * rsqrt(mean(x^2) + eps), then a
+ * per-channel gain, computed in full precision).  Readings: the norm runs over
+ * each head's dv outputs (the recurrence's y_t = S_t q_t is per head); the
+ * per-channel gain `gamma` [dv] is passed as it is applied (the zero-centred
+ * parameterisation of 7.6.3 passes 1 + w).
+ *
+ *   y   [rows][dv]  the recurrence output, one row per (token, value head)
+ *   z   [rows][dv]  the gate
+ *   out [rows][dv]  out[r][j] = y[r][j] / sqrt(mean_j y[r][j]^2 + eps) * gamma[j] * SiLU(z[r][j])
+ */
+void oracle_gated_rmsnorm(const double *y, const float *z, const float *gamma, double *out,
+                          long rows, int dv, double eps)
+{
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        const double *yr = y + (size_t)r * dv;
+        double ss = 0.0;
+        for (int j = 0; j < dv; ++j) ss += yr[j] * yr[j];
+        const double inv = 1.0 / sqrt(ss / (double)dv + eps);
+        for (int j = 0; j < dv; ++j)
+            out[(size_t)r * dv + j] = yr[j] * inv * (double)gamma[j] * silu((double)z[(size_t)r * dv + j]);
+    }
+}

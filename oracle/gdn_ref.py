@@ -169,3 +169,11 @@ def chunked(q, k, v, g, beta, cu, s0=None, scale=1.0, C=64):
                 S = np.exp(G[-1]) * S + (np.exp(G[-1] - G)[:, None] * K).T @ Delta
             fin[s, h] = S
     return o, fin
+
+
+def gated_rmsnorm(y, z, gamma, eps=1e-6):
+    """Gated RMSNorm ("7.6 Qwen3.5: the linear-attention hybrid", 7.6.2 output gate,
+    7.6.3 RMSNorm), per row of the last axis: RMSNorm(y) * gamma * SiLU(z)."""
+    y = np.asarray(y, dtype=np.float64)
+    rms = np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return (y / rms) * np.asarray(gamma, dtype=np.float64) * silu(np.asarray(z, dtype=np.float64))

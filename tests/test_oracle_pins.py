@@ -443,3 +443,92 @@ def test_planted_mistakes_are_caught():
     np.testing.assert_allclose(stepform(), ref, atol=1e-12)
     assert not np.allclose(stepform(retrieve_before_decay=True), ref, atol=1e-6)
     assert not np.allclose(stepform(sign=-1.0), ref, atol=1e-6)
+
+
+# ------------------------------------------------------------------ gated RMSNorm epilogue
+# "7.6 Qwen3.5: the linear-attention hybrid", 7.6.2 (output gate o = RMSNorm(y) * SiLU(z))
+# and 7.6.3 (RMSNorm: x * rsqrt(mean x^2 + eps) times a per-channel gain).
+
+SIGMOID_1 = 0.7310585786300049    # logistic(1), tabulated
+SIGMOID_3 = 0.9525741268224334    # logistic(3), tabulated
+
+
+def _both_norms(y, z, gamma, eps):
+    return oracle.gated_rmsnorm(y, z, gamma, eps), gdn_ref.gated_rmsnorm(y, z, gamma, eps)
+
+
+def test_gated_rmsnorm_constant_gate_closed_forms():
+    rng = np.random.default_rng(21)
+    dv = 16
+    y = _f32(rng.standard_normal((4, dv)) * 3.0)
+    ones = np.ones(dv, np.float32)
+    for c, silu_c in [(0.0, 0.0), (1.0, SIGMOID_1), (-1.0, -(1.0 - SIGMOID_1)), (3.0, 3.0 * SIGMOID_3)]:
+        z = np.full(y.shape, c, np.float32)
+        for out in _both_norms(y, z, ones, 0.0):
+            rms = np.sqrt(np.mean(out * out, axis=-1))
+            np.testing.assert_allclose(rms, abs(silu_c), rtol=1e-12, atol=1e-15)
+            if c != 0.0:   # direction of y, sign of SiLU(c)
+                yn = y / np.linalg.norm(y, axis=-1, keepdims=True)
+                on = out / np.linalg.norm(out, axis=-1, keepdims=True)
+                np.testing.assert_allclose(on, np.sign(silu_c) * yn, atol=1e-12)
+
+
+def test_gated_rmsnorm_invariants():
+    rng = np.random.default_rng(22)
+    rows, dv = 6, 32
+    y = _f32(rng.standard_normal((rows, dv)))
+    z = _f32(rng.standard_normal((rows, dv)))
+    gamma = _f32(rng.uniform(0.5, 2.0, dv))
+    base, _ = _both_norms(y, z, gamma, 0.0)
+    # scale invariance (eps = 0): powers of two keep the float32 inputs exact
+    for lam in (2.0 ** -10, 2.0 ** 12):
+        np.testing.assert_allclose(oracle.gated_rmsnorm(y * lam, z, gamma, 0.0), base, rtol=1e-12)
+    # the gain multiplies channel by channel
+    ones = np.ones(dv, np.float32)
+    unit, _ = _both_norms(y, z, ones, 0.0)
+    np.testing.assert_allclose(base, unit * gamma, rtol=1e-12)
+    # rows are independent (the norm axis is the last one): heads of very different size
+    y2 = y.copy(); y2[0] *= 1024.0; y2[3] *= 2.0 ** -10
+    out2 = oracle.gated_rmsnorm(y2, z, gamma, 0.0)
+    np.testing.assert_allclose(out2, base, rtol=1e-9)
+    # odd in y
+    np.testing.assert_allclose(oracle.gated_rmsnorm(-y, z, gamma, 0.0), -base, rtol=1e-12)
+    # eps: a constant row y = 2^-10 with eps = 2^-20 has mean y^2 = eps, so y / rms = 1/sqrt(2)
+    yc = np.full((1, dv), 2.0 ** -10, np.float32)
+    zc = np.full((1, dv), 1.0, np.float32)
+    for out in _both_norms(yc, zc, ones, 2.0 ** -20):
+        np.testing.assert_allclose(out, math.sqrt(0.5) * SIGMOID_1, rtol=1e-12)
+    # a zero row stays zero with eps > 0
+    out0 = oracle.gated_rmsnorm(np.zeros((2, dv), np.float32), z[:2], gamma, 1e-6)
+    assert np.all(out0 == 0.0)
+
+
+def test_gated_rmsnorm_matches_library_rms_norm():
+    rng = np.random.default_rng(23)
+    y = _f32(rng.standard_normal((3, 5, 64)) * np.array([1e-2, 1.0, 30.0])[:, None, None])
+    z = _f32(rng.standard_normal((3, 5, 64)) * 2.0)
+    gamma = _f32(rng.uniform(-1.0, 2.0, 64))
+    ref = F.rms_norm(torch.from_numpy(y).double(), (64,), torch.from_numpy(gamma).double(), eps=1e-6) \
+        * F.silu(torch.from_numpy(z).double())
+    for out in _both_norms(y, z, gamma, 1e-6):
+        np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_gated_rmsnorm_planted_mistakes_are_caught():
+    """Mutations of the norm (on the CPU) fail the closed-form pins above."""
+    dv = 8
+    y = np.arange(1, 2 * dv + 1, dtype=np.float64).reshape(2, dv)
+    z = np.full(y.shape, 3.0)
+    ones = np.ones(dv)
+    silu3 = 3.0 * SIGMOID_3
+
+    def rms_of(out):
+        return np.sqrt(np.mean(out * out, axis=-1))
+
+    good = gdn_ref.gated_rmsnorm(y, z, ones, 0.0)
+    np.testing.assert_allclose(rms_of(good), silu3, rtol=1e-12)
+    sum_not_mean = y / np.sqrt(np.sum(y * y, axis=-1, keepdims=True)) * gdn_ref.silu(z)
+    sigmoid_gate = y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True)) / (1.0 + np.exp(-z))
+    wrong_axis = y / np.sqrt(np.mean(y * y, axis=0, keepdims=True)) * gdn_ref.silu(z)
+    for bad in (sum_not_mean, sigmoid_gate, wrong_axis):
+        assert not np.allclose(rms_of(bad), silu3, rtol=1e-6)
