@@ -16,9 +16,13 @@ as tokens/s and state GB/s.  A second timed region runs the same prefill as
 gdn_conv_qk_prep + gdn_chunk_prefill (reported under "prefill_two_call"), and a
 third through the split-phase entry points so that every kernel sits alone
 between two HIP events on the stream it is launched on; those per-kernel
-durations give "kernels" and "roofline".  Inputs rotate over several copies at different
-addresses and each decode step streams 512 MiB of state, so nothing stays in the
-256 MB Infinity Cache from one step to the next.
+durations give "kernels" and "roofline" (the split region also times the gated
+RMSNorm epilogue, gdn_gated_rmsnorm, on the prefill output).  x, g and beta
+rotate over 3 copies at different addresses and the decode state over 2 sets
+(512 MiB), so no input is served from the 256 MB Infinity Cache; the prefill
+workspace is one buffer reused every step, as a caller reuses it, and its lines
+stay cached from one step to the next (the decode step reads its state with
+non-temporal loads).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -155,6 +159,11 @@ def main():
     fin = torch.empty((N, Hv, d, d), dtype=torch.float32, device=dev)
     ws = torch.empty(gdn.workspace_size(T, N, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=dev)
 
+    # gated RMSNorm epilogue on the prefill output (bf16 gate, gain and output)
+    zg_cpu, gam_cpu = inputs.gate_inputs(5, (T, Hv, d), d, "bf16")
+    zg, gam = zg_cpu.to(dev), gam_cpu.to(dev)
+    nout = torch.empty((T, Hv, d), dtype=torch.bfloat16, device=dev)
+
     # decode buffers: >= 2 state sets (>= 512 MiB) so no step finds its state in the Infinity Cache
     Rd = 2
     dstate = [dw.state.to(dev) for _ in range(Rd)]
@@ -190,7 +199,7 @@ def main():
     # split-phase entry points, one kernel between each pair of events: the fused chunk-local
     # kernel (gdn_prefill_local without a conv cache to write, so the interval holds that
     # kernel alone), the state pass, the decode step; then the two-call path's prep and
-    # chunk-local kernels.
+    # chunk-local kernels, and the gated RMSNorm epilogue on the prefill output.
     def step_split(i, ev):
         r = i % R
         ev[0].record()
@@ -204,6 +213,8 @@ def main():
         ev[4].record()
         gdn.chunk_prefill_local(q, k, v, gs[r], bs[r], ws, cu_seqlens=cu)
         ev[5].record()
+        gdn.gated_rmsnorm(o, zg, gam, out=nout)
+        ev[6].record()
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -222,7 +233,7 @@ def main():
         torch.cuda.synchronize()
         return evs, time.perf_counter() - t0
 
-    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local"]
+    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local", "gated_rmsnorm"]
     two_call = None
     if not args.split_only:
         evs, wall = timed(step, 3)
@@ -231,7 +242,7 @@ def main():
         two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
         two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,
                     "tokens_per_s": T / ((two_prep + two_call_ms) / 1e3)}
-    evs2, wall2 = timed(step_split, 6)
+    evs2, wall2 = timed(step_split, 7)
     per = {n: mean_ms(evs2, j) for j, n in enumerate(names)}   # ms per launch (split phases)
     if args.split_only:   # profiler runs: the metric falls back to the split-phase prefill
         wall = wall2
@@ -239,6 +250,7 @@ def main():
         decode_ms = per["decode"]
 
     prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
+    norm_b = T * Hv * d * (4 + 2 + 2) + d * 2   # y fp32 in, z bf16 in, out bf16, gain
     kern = {
         "chunk_local_fused": {"bound": "mfma", "achieved": local_f / per["chunk_local_fused"] / 1e9,
                               "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
@@ -248,6 +260,8 @@ def main():
         "state_pass": {"bound": "mfma", "achieved": state_f / per["state_pass"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
                        "unit": "TFLOP/s"},
         "decode": {"bound": "hbm", "achieved": dec_b / per["decode"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+        "gated_rmsnorm": {"bound": "hbm", "achieved": norm_b / per["gated_rmsnorm"] / 1e6, "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s"},
     }
     traffic = measured_traffic()   # HBM bytes per launch from the counter runs, or None
     for n in names:

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
+__all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_rmsnorm", "decode_step_gated", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
            "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "LIB_PATH", "abi_version", "mfma_supported"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.gdn_prefill.restype = I
         L.gdn_prefill_local.argtypes = [P, P, P, I, P, P, P, P, F, F, I, I, I, I, I, I, P, Z, P]
         L.gdn_prefill_local.restype = I
+        L.gdn_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, P]
+        L.gdn_decode_step_gated.restype = I
+        L.gdn_gated_rmsnorm.argtypes = [P, P, P, P, ctypes.c_long, I, F, I, P]
+        L.gdn_gated_rmsnorm.restype = I
         L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P]
         L.gdn_decode_step.restype = I
         L.gdn_status_string.argtypes = [I]
@@ -304,3 +308,45 @@ def decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv, scale=1.0
     if st != 0:
         raise GdnError("gdn_decode_step", st)
     return o
+
+
+def decode_step_gated(x, conv_w, conv_state, g, beta, state, z, gamma, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6,
+                      norm_eps=1e-6, out=None):
+    """decode_step with the gated RMSNorm fused: returns out [B, Hv, dv] in x's dtype,
+    RMSNorm(o) * gamma * SiLU(z) per head (z [B, Hv, dv] and gamma [dv] in x's dtype)."""
+    dt = x.dtype
+    C = 2 * Hk * dk + Hv * dv
+    _check(x, "x", dt)
+    if x.dim() != 2 or x.shape[1] != C:
+        raise ValueError(f"x must be [B, {C}]")
+    B = x.shape[0]
+    _check(conv_w, "conv_w", dt, (C, 4))
+    _check(conv_state, "conv_state", dt, (B, 3, C))
+    _check(g, "g", torch.float32, (B, Hv))
+    _check(beta, "beta", torch.float32, (B, Hv))
+    _check(state, "state", torch.float32, (B, Hv, dk, dv))
+    _check(z, "z", dt, (B, Hv, dv))
+    _check(gamma, "gamma", dt, (dv,))
+    out = torch.empty((B, Hv, dv), dtype=dt, device=x.device) if out is None else _check(out, "out", dt, (B, Hv, dv))
+    st = lib().gdn_decode_step_gated(_p(x), _p(conv_w), _p(conv_state), _p(g), _p(beta), _p(state), _p(z),
+                                     _p(gamma), _p(out), float(scale), float(l2_eps), float(norm_eps), B, Hk, Hv,
+                                     dk, dv, _dt(x), _stream())
+    if st != 0:
+        raise GdnError("gdn_decode_step_gated", st)
+    return out
+
+
+def gated_rmsnorm(y, z, gamma, eps=1e-6, out=None):
+    """Gated RMSNorm over the last axis of y (fp32, [..., dv]): y / sqrt(mean y^2 + eps) *
+    gamma * SiLU(z), returned in z's dtype (z same shape as y, gamma [dv])."""
+    _check(y, "y", torch.float32)
+    dt = z.dtype
+    dv = y.shape[-1]
+    _check(z, "z", dt, tuple(y.shape))
+    _check(gamma, "gamma", dt, (dv,))
+    out = torch.empty(y.shape, dtype=dt, device=y.device) if out is None else _check(out, "out", dt, tuple(y.shape))
+    rows = y.numel() // dv if dv else 0
+    st = lib().gdn_gated_rmsnorm(_p(y), _p(z), _p(gamma), _p(out), rows, dv, float(eps), _dt(z), _stream())
+    if st != 0:
+        raise GdnError("gdn_gated_rmsnorm", st)
+    return out

@@ -225,29 +225,84 @@ int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqle
                         scale, l2_eps, T, Hk, Hv, dk, dv, dtype, workspace, workspace_bytes, stream, 1);
 }
 
-int gdn_decode_step(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
-                    float *state, float *o, float scale, float l2_eps, int B, int Hk, int Hv, int dk, int dv,
-                    int dtype, void *stream) {
+namespace {
+
+// Shared validation + dispatch of gdn_decode_step and gdn_decode_step_gated (z, gamma, out set).
+int decode_impl(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
+                float *state, float *o, const void *z, const void *gamma, void *out, float scale, float l2_eps,
+                float norm_eps, int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream) {
     try {
+        const bool gated = out != nullptr || z != nullptr || gamma != nullptr;
         if (B < 0) return GDN_ERR_BAD_SHAPE;
-        if (!conv_w || (B > 0 && (!x || !conv_state || !g || !beta || !state || !o))) return GDN_ERR_NULL_POINTER;
+        if (!conv_w || (B > 0 && (!x || !conv_state || !g || !beta || !state))) return GDN_ERR_NULL_POINTER;
+        if (gated ? (!gamma || (B > 0 && (!z || !out))) : (B > 0 && !o)) return GDN_ERR_NULL_POINTER;
         if (int e = check_heads(Hk, Hv)) return e;
         if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128)) return GDN_ERR_UNSUPPORTED;
         if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return GDN_ERR_BAD_SHAPE;
+        if (gated && (!(norm_eps >= 0.f) || !std::isfinite(norm_eps))) return GDN_ERR_BAD_SHAPE;
         const size_t eb = elem_bytes(dtype);
         const size_t conv_dim = 2 * (size_t)Hk * dk + (size_t)Hv * dv;
         const Range rx{x, (size_t)B * conv_dim * eb}, rw{conv_w, conv_dim * 4 * eb},
             rcs{conv_state, (size_t)B * 3 * conv_dim * eb}, rg{g, (size_t)B * Hv * 4}, rb{beta, rg.bytes},
-            rst{state, (size_t)B * Hv * dk * dv * 4}, ro{o, (size_t)B * Hv * dv * 4};
-        for (Range in : {rx, rw, rcs, rg, rb, rst})
-            if (overlap(ro, in)) return GDN_ERR_ALIAS;
-        for (Range in : {rx, rw, rg, rb})
+            rst{state, (size_t)B * Hv * dk * dv * 4}, ro{gated ? nullptr : o, (size_t)B * Hv * dv * 4},
+            rz{z, (size_t)B * Hv * dv * eb}, rgm{gamma, (size_t)dv * eb}, rout{out, rz.bytes};
+        for (Range res : {ro, rout})
+            for (Range in : {rx, rw, rcs, rg, rb, rst, rz, rgm})
+                if (overlap(res, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rx, rw, rg, rb, rz, rgm})
             if (overlap(rcs, in) || overlap(rst, in)) return GDN_ERR_ALIAS;
         if (overlap(rcs, rst)) return GDN_ERR_ALIAS;
         gdn::DecodeArgs a{x, conv_w, conv_state, g, beta, state, o, scale, l2_eps, B, Hk, Hv, dk, dv,
                           dtype == GDN_BF16};
+        if (gated) {
+            a.z = z;
+            a.gamma = gamma;
+            a.out = out;
+            a.norm_eps = norm_eps;
+        }
         return hip_status(gdn::launch_decode(a, (hipStream_t)stream));
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+}  // namespace
+
+int gdn_decode_step(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
+                    float *state, float *o, float scale, float l2_eps, int B, int Hk, int Hv, int dk, int dv,
+                    int dtype, void *stream) {
+    if (!o && B > 0) return GDN_ERR_NULL_POINTER;
+    return decode_impl(x, conv_w, conv_state, g, beta, state, o, nullptr, nullptr, nullptr, scale, l2_eps, 0.f, B,
+                       Hk, Hv, dk, dv, dtype, stream);
+}
+
+int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state, const float *g,
+                          const float *beta, float *state, const void *z, const void *gamma, void *out,
+                          float scale, float l2_eps, float norm_eps, int B, int Hk, int Hv, int dk, int dv,
+                          int dtype, void *stream) {
+    if (!gamma || (B > 0 && (!z || !out))) return GDN_ERR_NULL_POINTER;
+    return decode_impl(x, conv_w, conv_state, g, beta, state, nullptr, z, gamma, out, scale, l2_eps, norm_eps, B,
+                       Hk, Hv, dk, dv, dtype, stream);
+}
+
+int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *out, long rows, int dv,
+                      float eps, int dtype, void *stream) {
+    try {
+        if (rows < 0) return GDN_ERR_BAD_SHAPE;
+        if (!gamma || (rows > 0 && (!y || !z || !out))) return GDN_ERR_NULL_POINTER;
+        if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+        if (!pow2_in(dv, 16, 256)) return GDN_ERR_UNSUPPORTED;
+        if (!(eps >= 0.f) || !std::isfinite(eps)) return GDN_ERR_BAD_SHAPE;
+        const size_t eb = elem_bytes(dtype);
+        const size_t n = (size_t)rows * dv;
+        const Range ry{y, n * 4}, rz{z, n * eb}, rgm{gamma, (size_t)dv * eb}, rout{out, n * eb};
+        // out may replace y (fp32) or z exactly: each element is read before it is written,
+        // by the same thread
+        if (overlap(rout, rgm)) return GDN_ERR_ALIAS;
+        if (bad_partial_alias(rout, ry) || bad_partial_alias(rout, rz)) return GDN_ERR_ALIAS;
+        gdn::NormArgs a{y, z, gamma, out, rows, dv, eps, dtype == GDN_BF16};
+        return hip_status(gdn::launch_gated_rmsnorm(a, (hipStream_t)stream));
     } catch (...) {
         return GDN_ERR_HIP;
     }

@@ -44,11 +44,16 @@ __device__ __forceinline__ float conv_step(const T *__restrict__ x, const T *__r
     return silu(acc);
 }
 
-template <typename T, int DK, int DV>
+// GATED: the output row of each value head goes through the gated RMSNorm epilogue
+// ("7.6 Qwen3.5: the linear-attention hybrid", sections 7.6.2 and 7.6.3) before it is
+// stored: out = o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z), in the element type.
+// The dv outputs of a head sit in the first dv/4 lanes of wave 0 (4 each), so the
+// mean square is one reduction inside that lane group.
+template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ x, const T *__restrict__ w, T *cs, const float *__restrict__ g,
     const float *__restrict__ beta, float *state, float *__restrict__ o, float scale, float eps,
-    int Hk, int Hv) {
+    int Hk, int Hv, const T *__restrict__ z, const T *__restrict__ gamma, T *__restrict__ out, float norm_eps) {
     constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
     constexpr int RG = kDecThreads / TPR;        // row groups
     constexpr int RPT = DK >= RG ? DK / RG : 1;  // rows per thread
@@ -152,7 +157,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             delta[e] = bt * (v_s[4 * cg + e] - a * sk);
             pq[e] = a * sq + delta[e] * kq;   // output column 4cg+e
         }
-        if (rg == 0) {
+        if constexpr (GATED) {
+            if (wave == 0) {   // rg == 0 is lanes 0 .. TPR - 1 of wave 0
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss = fmaf(pq[e], pq[e], ss);
+                ss = group_sum<TPR>(ss);
+                const float rn = rsqrtf(ss * (1.0f / DV) + norm_eps);
+                if (rg == 0) {
+                    const size_t off = ((size_t)b * Hv + h) * DV + 4 * cg;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        out[off + e] = from_f32<T>(pq[e] * rn * to_f32(gamma[4 * cg + e]) * silu(to_f32(z[off + e])));
+                }
+            }
+        } else if (rg == 0) {
             *reinterpret_cast<float4 *>(o + ((size_t)b * Hv + h) * DV + 4 * cg) = make_float4(pq[0], pq[1], pq[2], pq[3]);
         }
         if (row_active) {
@@ -175,9 +194,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     if (a.B == 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, DK, DV>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
-                       (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, a.o,
-                       a.scale, a.eps, a.Hk, a.Hv);
+    if (a.out) {
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
+                           (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, (float *)nullptr,
+                           a.scale, a.eps, a.Hk, a.Hv, (const T *)a.z, (const T *)a.gamma, (T *)a.out,
+                           a.norm_eps);
+    } else {
+        hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
+                           (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, a.o, a.scale, a.eps,
+                           a.Hk, a.Hv, (const T *)nullptr, (const T *)nullptr, (T *)nullptr, 0.f);
+    }
     return hipGetLastError();
 }
 

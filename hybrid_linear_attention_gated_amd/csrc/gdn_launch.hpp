@@ -55,12 +55,29 @@ struct DecodeArgs {
     float scale, eps;
     int B, Hk, Hv, dk, dv;
     bool bf16;
+    // gated output (gdn_decode_step_gated): when `out` is set, out = RMSNorm(o) * gamma *
+    // SiLU(z) in the element type is written instead of o
+    const void *z = nullptr, *gamma = nullptr;
+    void *out = nullptr;
+    float norm_eps = 0.f;
+};
+
+struct NormArgs {
+    const float *y;
+    const void *z, *gamma;
+    void *out;
+    long rows;
+    int dv;
+    float eps;
+    bool bf16;   // element type of z / gamma / out
 };
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 // conv_state_out[s] = last three inputs of sequence s (a launch of its own)
 hipError_t launch_conv_state_out(const PrepArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+// gated RMSNorm epilogue over rows of dv channels (dv in {16, 32, 64, 128, 256})
+hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st);
 
 // token-recurrent fp32 path (GDN_F32 and the small head dims)
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, hipStream_t st);

@@ -18,7 +18,9 @@ Workloads (shapes follow the 0.8B hybrid model's linear-attention layer in
 
 Distributions: x ~ N(0,1); conv weights ~ N(0, 0.5) (second parameter is the
 standard deviation); beta = sigmoid(N(0,1)); log-decay g = -softplus(N(0,1)),
-or g = log(a) with a ~ U(0.9, 1.0) where the workload says so.
+or g = log(a) with a ~ U(0.9, 1.0) where the workload says so.  Gated RMSNorm
+epilogue: gate z ~ N(0, 1), per-channel gain gamma = 1 + N(0, 0.1); standalone
+norm rows y ~ N(0, 1) times a per-row scale 10^U(-3, 2).
 Generator: numpy PCG64(1234 + index).
 """
 from __future__ import annotations
@@ -212,3 +214,20 @@ def core_workload(name: str, index: int, lengths, Hk: int, Hv: int, dk: int, dv:
 def get(name: str) -> Workload:
     return {"tiny_f32": tiny_f32, "layer_4k": layer_4k, "varlen8": varlen8,
             "decode256": decode256, "long_64k": long_64k}[name]()
+
+
+def gate_inputs(index: int, shape, dv: int, dtype: str = "bf16"):
+    """Gate z ~ N(0, 1) of `shape` (last axis dv) and gain gamma = 1 + N(0, 0.1) [dv] for
+    the gated RMSNorm epilogue, in the element type ("bf16" or "f32")."""
+    rng = _rng(index)
+    z = _normal_f32(rng, tuple(shape))
+    gamma = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    cast = _bf16 if dtype == "bf16" else _f32
+    return cast(z), cast(gamma)
+
+
+def norm_rows(index: int, rows: int, dv: int) -> torch.Tensor:
+    """fp32 rows [rows, dv] ~ N(0, 1) times a per-row scale 10^U(-3, 2)."""
+    rng = _rng(index)
+    y = rng.standard_normal((rows, dv)) * (10.0 ** rng.uniform(-3.0, 2.0, (rows, 1)))
+    return _f32(y)

@@ -32,6 +32,7 @@ KERNELS = [
     ("state_pass_kernel", "state_pass"),
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
+    ("gated_rmsnorm_kernel", "gated_rmsnorm"),
 ]
 # bench.py --copy-calibration streams a buffer through torch.neg (one elementwise
 # kernel that reads and writes COPY_BYTES); host-to-device uploads use blit

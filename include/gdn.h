@@ -27,9 +27,10 @@
  *    everything enqueued on it after the call, so to the caller it behaves as if
  *    it ran on `stream`.  Concurrent calls on one device must use distinct
  *    workspaces, as always.
- *  - Element type `dtype` (gdn_conv_qk_prep, gdn_decode_step) is the type of the
- *    pre-conv input x, the conv weights and the conv caches: GDN_BF16 or GDN_F32.
- *    Everything computed is fp32: q, k, v, o, g, beta and the recurrent states.
+ *  - Element type `dtype` (gdn_conv_qk_prep, gdn_decode_step, ...) is the type of the
+ *    pre-conv input x, the conv weights and the conv caches (and of the gate, gain
+ *    and output of the gated RMSNorm): GDN_BF16 or GDN_F32.  Everything computed is
+ *    fp32: q, k, v, o, g, beta and the recurrent states.
  *    (The outputs of this layer are heavy tailed -- the largest |o| is tens of
  *    times its RMS -- so a 16-bit q / k / v / o tensor alone would cost more than
  *    the 2e-2 RMS-relative accuracy the layer is held to.)
@@ -228,6 +229,41 @@ int gdn_decode_step(const void *x, const void *conv_w, void *conv_state,
                     float *state, float *o,
                     float scale, float l2_eps,
                     int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream);
+
+/*
+ * gdn_gated_rmsnorm -- the gated RMSNorm at the output of the linear-attention layer
+ * ("7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2: o = RMSNorm(y) (.)
+ * SiLU(z), z a separate projection of the layer input; the RMSNorm of section 7.6.3,
+ * computed in fp32), over each (token, value head) row of dv outputs:
+ *
+ *   out[r][j] = y[r][j] / sqrt(mean_j y[r][j]^2 + eps) * gamma[j] * SiLU(z[r][j])
+ *
+ *   y      [rows][dv]  fp32, the recurrence output (o of the prefill or decode calls,
+ *                      viewed as rows = tokens * Hv)
+ *   z      [rows][dv]  element type `dtype`, the gate
+ *   gamma  [dv]        element type `dtype`, the per-channel gain as applied (a
+ *                      zero-centred RMSNorm weight w of section 7.6.3 is passed as 1 + w)
+ *   out    [rows][dv]  element type `dtype`; may replace y (GDN_F32) or z exactly,
+ *                      must not overlap gamma or partly overlap y or z
+ * dv in {16, 32, 64, 128, 256}; eps >= 0 (the pages' RMSNorm uses 1e-6).
+ * Errors: GDN_ERR_NULL_POINTER, GDN_ERR_BAD_SHAPE (rows < 0, bad eps),
+ * GDN_ERR_UNSUPPORTED (dv, dtype), GDN_ERR_ALIAS.
+ */
+int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *out,
+                      long rows, int dv, float eps, int dtype, void *stream);
+
+/*
+ * gdn_decode_step_gated -- gdn_decode_step with the gated RMSNorm of
+ * gdn_gated_rmsnorm applied to each head's output inside the same kernel: instead of
+ * o, it writes out [B][Hv][dv] = RMSNorm(o) (.) gamma (.) SiLU(z) in element type
+ * `dtype`, for z [B][Hv][dv] and gamma [dv] in that type and norm_eps >= 0.  Every
+ * other argument is that of gdn_decode_step; out must not overlap any other argument.
+ */
+int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
+                          const float *g, const float *beta, float *state,
+                          const void *z, const void *gamma, void *out,
+                          float scale, float l2_eps, float norm_eps,
+                          int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(int status);

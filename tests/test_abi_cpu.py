@@ -29,7 +29,8 @@ def _declared_functions():
 def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_prefill",
-            "gdn_decode_step", "gdn_status_string", "gdn_abi_version"} <= set(names)
+            "gdn_prefill_local", "gdn_decode_step", "gdn_decode_step_gated", "gdn_gated_rmsnorm",
+            "gdn_status_string", "gdn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -149,6 +150,48 @@ def test_decode_validation(L):
     assert call(dk=256) == 3
     assert call(o=P(8)) == 6
     assert call(cs=P((5 << 24) + 8)) == 6                     # conv cache overlaps the state
+
+
+def test_gated_rmsnorm_validation(L):
+    P = _ptr
+    rows, dv = 64, 128
+    base = dict(y=P(0), z=P(1 << 24), gm=P(2 << 24), out=P(3 << 24), rows=rows, dv=dv, eps=1e-6, dt=1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_gated_rmsnorm(a["y"], a["z"], a["gm"], a["out"], ctypes.c_long(a["rows"]), a["dv"],
+                                   ctypes.c_float(a["eps"]), a["dt"], None)
+    assert call(gm=None) == 1
+    assert call(out=None) == 1
+    assert call(rows=-1) == 2
+    assert call(eps=float("nan")) == 2
+    assert call(eps=-1.0) == 2
+    assert call(dv=96) == 3
+    assert call(dv=512) == 3
+    assert call(dt=4) == 3
+    assert call(out=P((2 << 24) + 8)) == 6                       # out overlaps gamma
+    assert call(out=P(8)) == 6                                   # partial overlap with y
+    assert call(out=P(0)) == 6                                   # bf16 out cannot replace fp32 y
+
+
+def test_decode_gated_validation(L):
+    P = _ptr
+    base = dict(x=P(0), w=P(1 << 24), cs=P(2 << 24), g=P(3 << 24), b=P(4 << 24), st=P(5 << 24), z=P(6 << 24),
+                gm=P(7 << 24), out=P(8 << 24), B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1, neps=1e-6)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_decode_step_gated(a["x"], a["w"], a["cs"], a["g"], a["b"], a["st"], a["z"], a["gm"],
+                                       a["out"], ctypes.c_float(1.0), ctypes.c_float(1e-6),
+                                       ctypes.c_float(a["neps"]), a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                       a["dt"], None)
+    assert call(z=None) == 1
+    assert call(gm=None) == 1
+    assert call(out=None) == 1
+    assert call(neps=float("inf")) == 2
+    assert call(dk=256) == 3
+    assert call(out=P((6 << 24) + 8)) == 6                       # out overlaps z
+    assert call(out=P((5 << 24) + 64)) == 6                      # out overlaps the state
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

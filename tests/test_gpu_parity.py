@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL_BF16, TOL_F32, announce, assert_parity, f32np
+from helpers import TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, f32np
 from hybrid_linear_attention_gated_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -389,3 +389,87 @@ def test_decode_steps_equal_prefill(gdn):
     assert_parity("o (decode)", f32np(torch.cat(outs)), o_ref, TOL_BF16)
     assert_parity("state (decode)", f32np(st), f_ref, TOL_BF16)
     np.testing.assert_array_equal(f32np(cs)[0], f32np(wl.x)[-3:])
+
+
+# ------------------------------------------------------------------ gated RMSNorm epilogue
+
+def _check_norm_out(name, gpu, ref, dtype):
+    if dtype == "bf16":
+        assert_bf16_rounded(name, f32np(gpu), ref)
+    else:
+        assert_parity(name, f32np(gpu), ref, TOL_F32)
+
+
+@pytest.mark.parametrize("dtype,dv,rows", [("bf16", 128, 1003), ("f32", 128, 1003), ("bf16", 16, 77),
+                                           ("f32", 64, 130), ("bf16", 256, 65), ("f32", 32, 1)])
+def test_gated_rmsnorm(gdn, dtype, dv, rows):
+    announce(f"gated rmsnorm {dtype} dv={dv} rows={rows}")
+    y = inputs.norm_rows(920 + dv, rows, dv)
+    z, gamma = inputs.gate_inputs(921 + dv, (rows, dv), dv, dtype)
+    ref = oracle.gated_rmsnorm(f32np(y), f32np(z), f32np(gamma), 1e-6)
+    out = gdn.gated_rmsnorm(_cuda(y), _cuda(z), _cuda(gamma), eps=1e-6)
+    torch.cuda.synchronize()
+    _check_norm_out("out", out, ref, dtype)
+    # in place over z, and (fp32) over y
+    zd = _cuda(z)
+    gdn.gated_rmsnorm(_cuda(y), zd, _cuda(gamma), eps=1e-6, out=zd)
+    torch.cuda.synchronize()
+    assert torch.equal(zd, out)
+    if dtype == "f32":
+        yd = _cuda(y)
+        gdn.gated_rmsnorm(yd, _cuda(z), _cuda(gamma), eps=1e-6, out=yd)
+        torch.cuda.synchronize()
+        assert torch.equal(yd, out)
+
+
+def test_gated_rmsnorm_empty(gdn):
+    announce("gated rmsnorm, no rows")
+    y = torch.empty((0, 4, 128), dtype=torch.float32, device=DEV)
+    z = torch.empty((0, 4, 128), dtype=torch.bfloat16, device=DEV)
+    out = gdn.gated_rmsnorm(y, z, torch.ones(128, dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 4, 128)
+
+
+@pytest.mark.parametrize("B,Hk,Hv,d,dtype", [(5, 2, 4, 32, "bf16"), (3, 2, 2, 128, "f32"), (256, 16, 16, 128, "bf16")])
+def test_decode_gated(gdn, B, Hk, Hv, d, dtype):
+    announce(f"gated decode B={B} Hk={Hk} Hv={Hv} d={d} {dtype}")
+    dw = inputs.decode_workload("dec_gated", 930 + d, B, Hk, Hv, d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x, w, cs = dw.x.to(tdt), dw.conv_w.to(tdt), dw.conv_state.to(tdt)
+    z, gamma = inputs.gate_inputs(931 + d, (B, Hv, d), d, dtype)
+    o_ref, s_ref, cs_ref = oracle.decode(f32np(x), f32np(w), f32np(cs), f32np(dw.g), f32np(dw.beta),
+                                         f32np(dw.state), Hk, Hv, d, d)
+    ref = oracle.gated_rmsnorm(o_ref, f32np(z), f32np(gamma), 1e-6)
+    st, csd = _cuda(dw.state), _cuda(cs)
+    out = gdn.decode_step_gated(_cuda(x), _cuda(w), csd, _cuda(dw.g), _cuda(dw.beta), st, _cuda(z), _cuda(gamma),
+                                Hk, Hv, d, d)
+    torch.cuda.synchronize()
+    _check_norm_out("out", out, ref, dtype)
+    assert_parity("state", f32np(st), s_ref, TOL_F32)
+    np.testing.assert_array_equal(f32np(csd), cs_ref)
+
+
+def test_fused_prefill_then_gated_rmsnorm_layer_4k(gdn):
+    """The layer_4k prefill (one gdn_prefill call) followed by the gated RMSNorm on its
+    output, against the oracle's prep, recurrence and norm."""
+    announce("layer_4k: gdn_prefill + gated rmsnorm (bf16 gate / output)")
+    wl = inputs.layer_4k()
+    z, gamma = inputs.gate_inputs(940, (wl.T, wl.Hv, wl.dv), wl.dv, "bf16")
+    q_r, k_r, v_r, _ = oracle.prep(f32np(wl.x), f32np(wl.conv_w), wl.cu_seqlens.numpy(), wl.Hk, wl.Hv, wl.dk,
+                                   wl.dv)
+    o_ref, _ = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), wl.cu_seqlens.numpy())
+    ref = oracle.gated_rmsnorm(o_ref, f32np(z), f32np(gamma), 1e-6)
+    o, _ = gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), wl.Hk, wl.Hv, wl.dk, wl.dv,
+                       cu_seqlens=_cuda(wl.cu_seqlens))
+    out = gdn.gated_rmsnorm(o, _cuda(z), _cuda(gamma))
+    torch.cuda.synchronize()
+    # The norm makes every (token, head) row scale-free, and its bf16 output rounds each
+    # element to 2^-9 of itself (rows hold elements up to ~50x the tensor's RMS), so the
+    # end-to-end bar is per row: RMS error of the row / RMS of the row <= 2e-2.
+    og, outg = f32np(o), f32np(out)
+    row_err = np.sqrt(np.mean((outg - ref) ** 2, axis=-1) / np.mean(ref ** 2, axis=-1))
+    print(f"    out: max row-relative RMS error = {row_err.max():.3e} (tol {TOL_BF16:.0e})", flush=True)
+    assert row_err.max() <= TOL_BF16
+    # the norm itself, on the prefill's own output: one bf16 rounding of the fp64 value
+    assert_bf16_rounded("out (norm of the GPU's o)", outg, oracle.gated_rmsnorm(og, f32np(z), f32np(gamma), 1e-6))
