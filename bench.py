@@ -173,6 +173,9 @@ def main():
     dg = dw.g.to(dev)
     db = dw.beta.to(dev)
     do = torch.empty((B, Hv, d), dtype=torch.float32, device=dev)
+    dz_cpu, dgam_cpu = inputs.gate_inputs(6, (B, Hv, d), d, "bf16")
+    dz, dgam = dz_cpu.to(dev), dgam_cpu.to(dev)
+    dout = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
 
     # Timed region 1 (the metric): one step = gdn_prefill (prep fused into the chunked
     # prefill, one call) + one decode step.
@@ -199,7 +202,8 @@ def main():
     # split-phase entry points, one kernel between each pair of events: the fused chunk-local
     # kernel (gdn_prefill_local without a conv cache to write, so the interval holds that
     # kernel alone), the state pass, the decode step; then the two-call path's prep and
-    # chunk-local kernels, and the gated RMSNorm epilogue on the prefill output.
+    # chunk-local kernels, the gated RMSNorm epilogue on the prefill output and the decode
+    # step with the gated RMSNorm fused.
     def step_split(i, ev):
         r = i % R
         ev[0].record()
@@ -215,6 +219,9 @@ def main():
         ev[5].record()
         gdn.gated_rmsnorm(o, zg, gam, out=nout)
         ev[6].record()
+        gdn.decode_step_gated(dx, dcw, dcs[(i + 1) % Rd], dg, db, dstate[(i + 1) % Rd], dz, dgam, Hk, Hv, d, d,
+                              out=dout)
+        ev[7].record()
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -233,7 +240,7 @@ def main():
         torch.cuda.synchronize()
         return evs, time.perf_counter() - t0
 
-    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local", "gated_rmsnorm"]
+    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local", "gated_rmsnorm", "decode_gated"]
     two_call = None
     if not args.split_only:
         evs, wall = timed(step, 3)
@@ -242,7 +249,7 @@ def main():
         two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
         two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,
                     "tokens_per_s": T / ((two_prep + two_call_ms) / 1e3)}
-    evs2, wall2 = timed(step_split, 7)
+    evs2, wall2 = timed(step_split, 8)
     per = {n: mean_ms(evs2, j) for j, n in enumerate(names)}   # ms per launch (split phases)
     if args.split_only:   # profiler runs: the metric falls back to the split-phase prefill
         wall = wall2
@@ -251,6 +258,7 @@ def main():
 
     prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
     norm_b = T * Hv * d * (4 + 2 + 2) + d * 2   # y fp32 in, z bf16 in, out bf16, gain
+    decg_b = dec_b - B * Hv * d * 4 + B * Hv * d * (2 + 2) + d * 2   # o fp32 replaced by z in, out bf16
     kern = {
         "chunk_local_fused": {"bound": "mfma", "achieved": local_f / per["chunk_local_fused"] / 1e9,
                               "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
@@ -262,6 +270,8 @@ def main():
         "decode": {"bound": "hbm", "achieved": dec_b / per["decode"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
         "gated_rmsnorm": {"bound": "hbm", "achieved": norm_b / per["gated_rmsnorm"] / 1e6, "peak": PEAK_HBM_GBS,
                           "unit": "GB/s"},
+        "decode_gated": {"bound": "hbm", "achieved": decg_b / per["decode_gated"] / 1e6, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s"},
     }
     traffic = measured_traffic()   # HBM bytes per launch from the counter runs, or None
     for n in names:
