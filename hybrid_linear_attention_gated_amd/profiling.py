@@ -29,6 +29,7 @@ KERNELS = [
     ("conv_state_out_kernel", "conv_state_out"),
     ("chunk_local_kernel", "chunk_local"),   # "chunk_local_fused" for the FUSED = true instances
     ("chunk_local_fused", "chunk_local_fused"),
+    ("decode_gated", "decode_gated"),
     ("state_pass_kernel", "state_pass"),
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
@@ -43,6 +44,8 @@ COPY_NAMES = ("elementwise_kernel",)
 def short_name(symbol: str) -> str:
     if "chunk_local_kernel" in symbol and ("ELb1E" in symbol or ", true," in symbol):
         return "chunk_local_fused"   # mangled or demangled template argument FUSED = true
+    if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):
+        return "decode_gated"        # template argument GATED = true
     for frag, short in KERNELS:
         if frag in symbol:
             return short
