@@ -45,9 +45,9 @@ def lib():
         L.oracle_threads.restype = i
         L.oracle_prep.argtypes = [P, P, P, i, P, P, P, P, P, i, i, i, i, i, d]
         L.oracle_prep.restype = None
-        L.oracle_recurrence.argtypes = [P, P, P, P, P, P, i, P, P, P, d, i, i, i, i, i, P, i]
+        L.oracle_recurrence.argtypes = [P, P, P, P, P, P, i, P, P, P, d, i, i, i, i, i, P, i, i]
         L.oracle_recurrence.restype = None
-        L.oracle_decode.argtypes = [P, P, P, P, P, P, P, P, P, d, d, i, i, i, i, i]
+        L.oracle_decode.argtypes = [P, P, P, P, P, P, P, P, P, d, d, i, i, i, i, i, i]
         L.oracle_decode.restype = None
         L.oracle_gated_rmsnorm.argtypes = [P, P, P, P, ctypes.c_long, i, d]
         L.oracle_gated_rmsnorm.restype = None
@@ -90,10 +90,11 @@ def prep(x, w, cu, Hk, Hv, dk, dv, cs_in=None, eps=1e-6, want_cs_out=True):
     return q, k, v, cso
 
 
-def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0, heads=None):
+def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0, heads=None, order=0):
     """fp64 token recurrence.  q,k [T,Hk,dk], v [T,Hv,dv] (any float dtype;
     used as fp64), g, beta [T,Hv] fp32, s0 [N,Hv,dk,dv] fp32 or None.
-    heads: optional list of v-heads to compute (others left zero)."""
+    heads: optional list of v-heads to compute (others left zero).
+    order: 0 = decay before retrieval, 1 = retrieval from the undecayed state."""
     q = _f64(q); k = _f64(k); v = _f64(v)
     g = _f32(g); beta = _f32(beta); cu = _i32(cu)
     T, Hk, dk = k.shape
@@ -103,17 +104,17 @@ def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0, heads=None):
     o = np.zeros((T, Hv, dv)); fin = np.zeros((N, Hv, dk, dv))
     hs = None if heads is None else _i32(heads)
     lib().oracle_recurrence(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, _p(s0a), _p(fin), _p(o),
-                            float(scale), T, Hk, Hv, dk, dv, _p(hs), 0 if hs is None else len(hs))
+                            float(scale), T, Hk, Hv, dk, dv, _p(hs), 0 if hs is None else len(hs), int(order))
     return o, fin
 
 
-def decode(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=1e-6):
+def decode(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=1e-6, order=0):
     """fp64 decode step.  Returns o [B,Hv,dv], new state, new conv cache."""
     x = _f32(x); w = _f32(w); cs = _f32(cs); g = _f32(g); beta = _f32(beta); st = _f32(state)
     B = x.shape[0]
     o = np.zeros((B, Hv, dv)); st_out = np.zeros((B, Hv, dk, dv)); cs_out = np.zeros(cs.shape)
     lib().oracle_decode(_p(x), _p(w), _p(cs), _p(cs_out), _p(g), _p(beta), _p(st), _p(st_out), _p(o),
-                        float(scale), float(eps), B, Hk, Hv, dk, dv)
+                        float(scale), float(eps), B, Hk, Hv, dk, dv, int(order))
     return o, st_out, cs_out
 
 

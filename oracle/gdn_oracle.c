@@ -148,18 +148,28 @@ void oracle_prep(const float *x, const float *w, const int32_t *cu, int N,
  *   S[i][j] += k_i * delta_j         (write)
  *   o_j = sum_i S[i][j] * q_i        (read)
  * m and delta are caller-provided scratch of length dv.
+ *
+ * order = 1 is the order of [Book] 7.6.2, S_t = a S_{t-1} + k [b (v - S_{t-1}^T k)]^T:
+ * the retrieval reads the state before the decay (retrieve, then decay, correct,
+ * write, read).  The two orders agree when a = 1.
  */
 static void delta_rule_token(double *S, const double *q, const double *k, const double *v,
-                             double a, double b, int dk, int dv, double *m, double *delta, double *o)
+                             double a, double b, int dk, int dv, double *m, double *delta, double *o,
+                             int order)
 {
-    for (int i = 0; i < dk; ++i)
-        for (int j = 0; j < dv; ++j)
-            S[(size_t)i * dv + j] *= a;
+    if (order == 0)
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] *= a;
     for (int j = 0; j < dv; ++j) {
         double acc = 0.0;
         for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * k[i];
         m[j] = acc;
     }
+    if (order != 0)
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] *= a;
     for (int j = 0; j < dv; ++j) delta[j] = b * (v[j] - m[j]);
     for (int i = 0; i < dk; ++i)
         for (int j = 0; j < dv; ++j)
@@ -184,7 +194,7 @@ void oracle_recurrence(const double *q, const double *k, const double *v,
                        const int32_t *cu, int N,
                        const float *s0, double *s_final, double *o,
                        double scale, int T, int Hk, int Hv, int dk, int dv,
-                       const int32_t *heads, int n_heads)
+                       const int32_t *heads, int n_heads, int order)
 {
     (void)T;
     const int group = Hv / Hk;
@@ -208,7 +218,7 @@ void oracle_recurrence(const double *q, const double *k, const double *v,
             const double a = exp((double)g[(size_t)t * Hv + h]);
             const double b = (double)beta[(size_t)t * Hv + h];
             delta_rule_token(S, qs, kt, v + ((size_t)t * Hv + h) * dv, a, b, dk, dv, m, delta,
-                             o + ((size_t)t * Hv + h) * dv);
+                             o + ((size_t)t * Hv + h) * dv, order);
         }
         if (s_final)
             for (size_t e = 0; e < (size_t)dk * dv; ++e) s_final[st_off + e] = S[e];
@@ -227,7 +237,7 @@ void oracle_recurrence(const double *q, const double *k, const double *v,
 void oracle_decode(const float *x, const float *w, const float *cs_in, double *cs_out,
                    const float *g, const float *beta, const float *state_in, double *state_out,
                    double *o, double scale, double eps,
-                   int B, int Hk, int Hv, int dk, int dv)
+                   int B, int Hk, int Hv, int dk, int dv, int order)
 {
     const int conv_dim = 2 * Hk * dk + Hv * dv;
     const int qk_dim = Hk * dk;
@@ -265,7 +275,7 @@ void oracle_decode(const float *x, const float *w, const float *cs_in, double *c
             const double a = exp((double)g[(size_t)b * Hv + h]);
             const double bb = (double)beta[(size_t)b * Hv + h];
             delta_rule_token(S, qs, kn, y + 2 * qk_dim + h * dv, a, bb, dk, dv, m, delta,
-                             o + ((size_t)b * Hv + h) * dv);
+                             o + ((size_t)b * Hv + h) * dv, order);
             for (size_t e = 0; e < (size_t)dk * dv; ++e) state_out[st_off + e] = S[e];
         }
         free(y); free(qs); free(kn); free(m); free(delta); free(S);

@@ -81,12 +81,14 @@ def prep(x, w, cu, Hk, Hv, dk, dv, cs_in=None, eps=L2_EPS):
     return q, k, v, cs_out
 
 
-def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0):
+def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0, order=0):
     """Product-form gated delta rule, token by token, vectorised over v-heads.
 
     q, k [T,Hk,dk]; v [T,Hv,dv]; g, beta [T,Hv]; s0 [N,Hv,dk,dv] (key-major,
     the library's layout) or None.  Returns o [T,Hv,dv] and the final state
-    [N,Hv,dk,dv] (key-major).
+    [N,Hv,dk,dv] (key-major).  order 0: S_t = a S (I - b k k^T) + b v k^T;
+    order 1 (retrieval from the undecayed state, "7.6 Qwen3.5" 7.6.2):
+    S_t = S (a I - b k k^T) + b v k^T.
     """
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     g = np.asarray(g, np.float64); beta = np.asarray(beta, np.float64)
@@ -105,14 +107,18 @@ def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0):
             qt = scale * np.repeat(q[t], rep, axis=0)      # [Hv, dk]
             a = np.exp(g[t])                               # [Hv]
             b = beta[t]
-            proj = eye[None] - b[:, None, None] * kt[:, :, None] * kt[:, None, :]   # I - b k k^T
-            Sv = a[:, None, None] * (Sv @ proj) + b[:, None, None] * v[t][:, :, None] * kt[:, None, :]
+            kk = b[:, None, None] * kt[:, :, None] * kt[:, None, :]                  # b k k^T
+            if order == 0:
+                Sv = a[:, None, None] * (Sv @ (eye[None] - kk))
+            else:
+                Sv = Sv @ (a[:, None, None] * eye[None] - kk)
+            Sv = Sv + b[:, None, None] * v[t][:, :, None] * kt[:, None, :]
             o[t] = np.einsum('hjd,hd->hj', Sv, qt)
         fin[s] = np.transpose(Sv, (0, 2, 1))
     return o, fin
 
 
-def decode_step(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=L2_EPS):
+def decode_step(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=L2_EPS, order=0):
     """One decode step for every row b: conv window [cs[b], x[b]], then one
     product-form step.  Returns o [B,Hv,dv], new state, new conv cache."""
     x = np.asarray(x, np.float64); cs = np.asarray(cs, np.float64)
@@ -124,12 +130,12 @@ def decode_step(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=L2_EPS)
     for b in range(B):
         qb, kb, vb, cso = prep(x[b:b + 1], w, cu, Hk, Hv, dk, dv, cs_in=cs[b:b + 1], eps=eps)
         ob, fb = recurrence(qb, kb, vb, np.asarray(g)[b:b + 1], np.asarray(beta)[b:b + 1], cu,
-                            s0=np.asarray(state)[b:b + 1], scale=scale)
+                            s0=np.asarray(state)[b:b + 1], scale=scale, order=order)
         o[b] = ob[0]; new_state[b] = fb[0]; new_cs[b] = cso[0]
     return o, new_state, new_cs
 
 
-def chunked(q, k, v, g, beta, cu, s0=None, scale=1.0, C=64):
+def chunked(q, k, v, g, beta, cu, s0=None, scale=1.0, C=64, order=0):
     """Chunked (WY / UT) form in fp64, per sequence and v-head.
 
     Within a chunk with local cumulative log-decay G_t = sum_{s<=t} g_s:
@@ -138,6 +144,8 @@ def chunked(q, k, v, g, beta, cu, s0=None, scale=1.0, C=64):
       O = diag(e^G) Q S0 + P Delta,   P[t,i] = e^{G_t-G_i} (q_t . k_i)  (i <= t)
       S_end = e^{G_c} S0 + (diag(e^{G_c - G}) K)^T Delta
     Key-major state S [dk, dv].  Chunks restart at every sequence start.
+    order 1 (retrieval from the undecayed state) replaces e^{G_t} by e^{G_{t-1}}
+    = e^{G_t - g_t} in A (first factor) and in W; U, P, O and S_end are unchanged.
     """
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     g = np.asarray(g, np.float64); beta = np.asarray(beta, np.float64)
@@ -156,11 +164,13 @@ def chunked(q, k, v, g, beta, cu, s0=None, scale=1.0, C=64):
                 K = k[c0:c1, kh]; Q = scale * q[c0:c1, kh]; V = v[c0:c1, h]
                 b = beta[c0:c1, h]
                 G = np.cumsum(g[c0:c1, h])
+                Gr = G - g[c0:c1, h] if order else G    # decay applied before the retrieval or not
                 D = G[:, None] - G[None, :]
+                Dr = Gr[:, None] - G[None, :]
                 lower = np.tril(np.ones((c1 - c0, c1 - c0)), -1)
-                A = lower * b[:, None] * np.exp(np.where(lower > 0, D, 0.0)) * (K @ K.T)
+                A = lower * b[:, None] * np.exp(np.where(lower > 0, Dr, 0.0)) * (K @ K.T)
                 Tm = np.linalg.inv(np.eye(c1 - c0) + A)
-                W = Tm @ ((b * np.exp(G))[:, None] * K)
+                W = Tm @ ((b * np.exp(Gr))[:, None] * K)
                 U = Tm @ (b[:, None] * V)
                 Delta = U - W @ S
                 causal = np.tril(np.ones((c1 - c0, c1 - c0)))

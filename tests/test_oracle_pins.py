@@ -532,3 +532,93 @@ def test_gated_rmsnorm_planted_mistakes_are_caught():
     wrong_axis = y / np.sqrt(np.mean(y * y, axis=0, keepdims=True)) * gdn_ref.silu(z)
     for bad in (sum_not_mean, sigmoid_gate, wrong_axis):
         assert not np.allclose(rms_of(bad), silu3, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ retrieval order (NEXT-3)
+# "7.6 Qwen3.5: the linear-attention hybrid", 7.6.2 writes S_t = a S_{t-1} + k [b (v - S_{t-1}^T k)]^T:
+# the retrieval reads the state before the decay (order 1), where "Hugging Face Transformers:
+# Qwen3.5-MoE series explained", 4.3 decays first (order 0).
+
+def _rational_order1(q, k, v, a, b):
+    """S_t = S (a I - b k k^T) + b v k^T, o = S q, value-major, exact rationals."""
+    T, dk = len(k), len(k[0])
+    dv = len(v[0])
+    S = [[Fraction(0)] * dk for _ in range(dv)]
+    outs = []
+    for t in range(T):
+        kt = [Fraction(x) for x in k[t]]
+        P = [[(a[t] if i == j else Fraction(0)) - b[t] * kt[i] * kt[j] for j in range(dk)] for i in range(dk)]
+        SP = [[sum(S[r][m] * P[m][c] for m in range(dk)) for c in range(dk)] for r in range(dv)]
+        S = [[SP[r][c] + b[t] * Fraction(v[t][r]) * kt[c] for c in range(dk)] for r in range(dv)]
+        outs.append([sum(S[r][c] * Fraction(q[t][c]) for c in range(dk)) for r in range(dv)])
+    return outs, S
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_order1_exact_rational_bruteforce(seed):
+    rng = np.random.default_rng(200 + seed)
+    T, dk, dv = 5, 3, 2
+    q = rng.integers(-8, 9, (T, dk)) / 8.0
+    k = rng.integers(-8, 9, (T, dk)) / 8.0
+    v = rng.integers(-8, 9, (T, dv)) / 4.0
+    g32 = _f32(np.log(rng.uniform(0.5, 1.0, T)))
+    b32 = _f32(rng.integers(1, 8, T) / 8.0)
+    a_exact = [Fraction(math.exp(float(x))) for x in g32]
+    b_exact = [Fraction(float(x)) for x in b32]
+    outs, S = _rational_order1(q.tolist(), k.tolist(), v.tolist(), a_exact, b_exact)
+    o_ex = np.array([[float(x) for x in r] for r in outs])
+    S_ex = np.array([[float(x) for x in r] for r in S]).T
+    cu = np.array([0, T], np.int32)
+    for impl in (oracle.recurrence, gdn_ref.recurrence):
+        o, fin = impl(q[:, None], k[:, None], v[:, None], g32[:, None], b32[:, None], cu, order=1)
+        np.testing.assert_allclose(o[:, 0], o_ex, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fin[0, 0], S_ex, rtol=1e-12, atol=1e-12)
+    # with a < 1 the two orders differ; with a = 1 they coincide
+    o0, _ = oracle.recurrence(q[:, None], k[:, None], v[:, None], g32[:, None], b32[:, None], cu, order=0)
+    assert not np.allclose(o0[:, 0], o_ex, atol=1e-6)
+    z = np.zeros_like(g32)
+    oa, fa = oracle.recurrence(q[:, None], k[:, None], v[:, None], z[:, None], b32[:, None], cu, order=0)
+    ob, fb = oracle.recurrence(q[:, None], k[:, None], v[:, None], z[:, None], b32[:, None], cu, order=1)
+    np.testing.assert_array_equal(oa, ob)
+    np.testing.assert_array_equal(fa, fb)
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 200])
+def test_order1_chunked_equals_recurrent(L):
+    q, k, v, g, b, cu, s0 = _rand_core(L, 2, 4, 16, 8, RNG)
+    o_r, f_r = oracle.recurrence(q, k, v, g, b, cu, s0=s0, scale=0.7, order=1)
+    o_c, f_c = gdn_ref.chunked(q, k, v, g, b, cu, s0=s0, scale=0.7, C=64, order=1)
+    np.testing.assert_allclose(o_c, o_r, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(f_c, f_r, rtol=1e-10, atol=1e-11)
+
+
+def test_order1_c_matches_numpy_and_decode_equals_prefill():
+    lengths = [3, 70, 0, 29]
+    Hk, Hv, dk, dv = 2, 4, 8, 8
+    C = 2 * Hk * dk + Hv * dv
+    T = sum(lengths)
+    x = _f32(RNG.standard_normal((T, C)))
+    w = _f32(RNG.standard_normal((C, 4)) * 0.5)
+    g = _f32(-np.logaddexp(0, RNG.standard_normal((T, Hv))))
+    b = _f32(1 / (1 + np.exp(-RNG.standard_normal((T, Hv)))))
+    s0 = _f32(RNG.standard_normal((4, Hv, dk, dv)) * 0.1)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    q, k, v, _ = oracle.prep(x, w, cu, Hk, Hv, dk, dv)
+    oc, fc = oracle.recurrence(q, k, v, g, b, cu, s0=s0, scale=0.3, order=1)
+    on, fn = gdn_ref.recurrence(q, k, v, g, b, cu, s0=s0, scale=0.3, order=1)
+    np.testing.assert_allclose(oc, on, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(fc, fn, rtol=1e-10, atol=1e-12)
+    # decode steps of the first sequence (3 tokens, zero conv history) equal its prefill
+    st = s0[:1].astype(np.float64); cs = np.zeros((1, 3, C))
+    outs = []
+    for t in range(3):
+        csf, stf = _f32(cs), _f32(st)
+        ot, st, cs = oracle.decode(x[t:t + 1], w, csf, g[t:t + 1], b[t:t + 1], stf, Hk, Hv, dk, dv, scale=0.3,
+                                   order=1)
+        ot2, st2, _ = gdn_ref.decode_step(x[t:t + 1], w, csf, g[t:t + 1], b[t:t + 1], stf, Hk, Hv, dk, dv,
+                                          scale=0.3, order=1)
+        np.testing.assert_allclose(ot, ot2, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(st, st2, rtol=1e-10, atol=1e-12)
+        outs.append(ot[0])
+    np.testing.assert_allclose(np.stack(outs), oc[:3], rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(st[0], fc[0], rtol=1e-5, atol=1e-6)
