@@ -20,11 +20,13 @@ import os
 import torch
 
 __all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_rmsnorm", "decode_step_gated", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
-           "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "LIB_PATH", "abi_version", "mfma_supported"]
+           "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
+           "LIB_PATH", "abi_version", "mfma_supported"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MATH_F32, GDN_MATH_MFMA = 0, 1
+GDN_ORDER_DECAY_FIRST, GDN_ORDER_RETRIEVE_FIRST = 0, 1
 _lib = None
 
 
@@ -48,21 +50,21 @@ def lib() -> ctypes.CDLL:
         L.gdn_conv_qk_prep.restype = I
         L.gdn_chunk_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
         L.gdn_chunk_prefill_workspace_size.restype = Z
-        L.gdn_chunk_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_chunk_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_chunk_prefill.restype = I
-        L.gdn_chunk_prefill_local.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, P, Z, P]
+        L.gdn_chunk_prefill_local.argtypes = [P, P, P, P, P, P, I, F, I, I, I, I, I, I, P, Z, P]
         L.gdn_chunk_prefill_local.restype = I
         L.gdn_chunk_prefill_state.argtypes = [P, I, P, P, P, I, I, I, I, I, P, Z, P]
         L.gdn_chunk_prefill_state.restype = I
-        L.gdn_prefill.argtypes = [P, P, P, I, P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_prefill.argtypes = [P, P, P, I, P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_prefill.restype = I
-        L.gdn_prefill_local.argtypes = [P, P, P, I, P, P, P, P, F, F, I, I, I, I, I, I, P, Z, P]
+        L.gdn_prefill_local.argtypes = [P, P, P, I, P, P, P, P, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_prefill_local.restype = I
-        L.gdn_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, P]
+        L.gdn_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P]
         L.gdn_decode_step_gated.restype = I
         L.gdn_gated_rmsnorm.argtypes = [P, P, P, P, ctypes.c_long, I, F, I, P]
         L.gdn_gated_rmsnorm.restype = I
-        L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, P]
+        L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, I, P]
         L.gdn_decode_step.restype = I
         L.gdn_status_string.argtypes = [I]
         L.gdn_status_string.restype = ctypes.c_char_p
@@ -145,7 +147,7 @@ def conv_qk_prep(x, conv_w, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
 
 def prefill(x, conv_w, g, beta, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None, conv_state_out=None,
             initial_state=None, final_state=None, scale=1.0, l2_eps=1e-6, output_final_state=True, o=None,
-            workspace=None):
+            workspace=None, order=0):
     """conv_qk_prep + chunk_prefill (MFMA path) in one call, q / k / v never written out.
 
     x [T, conv_dim] (bf16 or fp32), conv_w [conv_dim, 4]; g, beta [T, Hv] fp32; states
@@ -176,14 +178,14 @@ def prefill(x, conv_w, g, beta, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=N
     _check(workspace, "workspace")
     st = lib().gdn_prefill(_p(x), _p(conv_w), _p(cu), N, _p(conv_state_in), _p(conv_state_out), _p(g), _p(beta),
                            _p(initial_state), _p(final_state), _p(o), float(scale), float(l2_eps), T, Hk, Hv, dk, dv,
-                           _dt(x), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+                           _dt(x), int(order), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise GdnError("gdn_prefill", st)
     return o, final_state
 
 
 def prefill_local(x, conv_w, g, beta, workspace, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
-                  conv_state_out=None, scale=1.0, l2_eps=1e-6):
+                  conv_state_out=None, scale=1.0, l2_eps=1e-6, order=0):
     """First phase of `prefill` (conv prep + chunk-local records into `workspace`);
     `chunk_prefill_state` finishes it."""
     dt = x.dtype
@@ -200,7 +202,8 @@ def prefill_local(x, conv_w, g, beta, workspace, Hk, Hv, dk, dv, cu_seqlens=None
     _check(beta, "beta", torch.float32, (T, Hv))
     _check(workspace, "workspace")
     st = lib().gdn_prefill_local(_p(x), _p(conv_w), _p(cu), N, _p(conv_state_in), _p(conv_state_out), _p(g),
-                                 _p(beta), float(scale), float(l2_eps), T, Hk, Hv, dk, dv, _dt(x), _p(workspace),
+                                 _p(beta), float(scale), float(l2_eps), T, Hk, Hv, dk, dv, _dt(x), int(order),
+                                 _p(workspace),
                                  workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise GdnError("gdn_prefill_local", st)
@@ -221,12 +224,13 @@ def workspace_size(T, N, Hk, Hv, dk, dv, math="auto") -> int:
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, final_state=None, scale=1.0,
-                  output_final_state=True, o=None, workspace=None, math="auto"):
+                  output_final_state=True, o=None, workspace=None, math="auto", order=0):
     """Gated delta rule over packed sequences.
 
     q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv]; states [N, Hv, dk, dv]; all fp32.
     math: "mfma" (chunked MFMA path), "f32" (fp32 token recurrence) or "auto"
-    (mfma where the head dims allow it).
+    (mfma where the head dims allow it).  order: 0 decays the state before the
+    retrieval, 1 retrieves from the undecayed state (GDN_ORDER_*).
     Returns (o [T, Hv, dv] fp32, final_state or None).  final_state may be initial_state
     (updated in place).
     """
@@ -253,14 +257,14 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, final_s
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().gdn_chunk_prefill(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, _p(initial_state),
-                                 _p(final_state), _p(o), float(scale), T, Hk, Hv, dk, dv, m,
+                                 _p(final_state), _p(o), float(scale), T, Hk, Hv, dk, dv, m, int(order),
                                  _p(workspace), ws_bytes, _stream())
     if st != 0:
         raise GdnError("gdn_chunk_prefill", st)
     return o, final_state
 
 
-def chunk_prefill_local(q, k, v, g, beta, workspace, cu_seqlens=None, scale=1.0):
+def chunk_prefill_local(q, k, v, g, beta, workspace, cu_seqlens=None, scale=1.0, order=0):
     """First phase of the MFMA chunked prefill: per-chunk quantities into `workspace`."""
     T, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
@@ -269,7 +273,8 @@ def chunk_prefill_local(q, k, v, g, beta, workspace, cu_seqlens=None, scale=1.0)
         _check(t, n, torch.float32)
     _check(workspace, "workspace")
     st = lib().gdn_chunk_prefill_local(_p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), N, float(scale), T, Hk, Hv,
-                                       dk, dv, _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+                                       dk, dv, int(order), _p(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream())
     if st != 0:
         raise GdnError("gdn_chunk_prefill_local", st)
 
@@ -287,7 +292,7 @@ def chunk_prefill_state(workspace, o, T, Hk, Hv, dk, dv, cu_seqlens=None, initia
         raise GdnError("gdn_chunk_prefill_state", st)
 
 
-def decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6, o=None):
+def decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6, o=None, order=0):
     """One decode token per row; conv_state [B, 3, conv_dim] and state [B, Hv, dk, dv]
     are updated in place.  Returns o [B, Hv, dv] fp32."""
     dt = x.dtype
@@ -304,14 +309,14 @@ def decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv, scale=1.0
     o = torch.empty((B, Hv, dv), dtype=torch.float32, device=x.device) if o is None else \
         _check(o, "o", torch.float32, (B, Hv, dv))
     st = lib().gdn_decode_step(_p(x), _p(conv_w), _p(conv_state), _p(g), _p(beta), _p(state), _p(o),
-                               float(scale), float(l2_eps), B, Hk, Hv, dk, dv, _dt(x), _stream())
+                               float(scale), float(l2_eps), B, Hk, Hv, dk, dv, _dt(x), int(order), _stream())
     if st != 0:
         raise GdnError("gdn_decode_step", st)
     return o
 
 
 def decode_step_gated(x, conv_w, conv_state, g, beta, state, z, gamma, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6,
-                      norm_eps=1e-6, out=None):
+                      norm_eps=1e-6, out=None, order=0):
     """decode_step with the gated RMSNorm fused: returns out [B, Hv, dv] in x's dtype,
     RMSNorm(o) * gamma * SiLU(z) per head (z [B, Hv, dv] and gamma [dv] in x's dtype)."""
     dt = x.dtype
@@ -330,7 +335,7 @@ def decode_step_gated(x, conv_w, conv_state, g, beta, state, z, gamma, Hk, Hv, d
     out = torch.empty((B, Hv, dv), dtype=dt, device=x.device) if out is None else _check(out, "out", dt, (B, Hv, dv))
     st = lib().gdn_decode_step_gated(_p(x), _p(conv_w), _p(conv_state), _p(g), _p(beta), _p(state), _p(z),
                                      _p(gamma), _p(out), float(scale), float(l2_eps), float(norm_eps), B, Hk, Hv,
-                                     dk, dv, _dt(x), _stream())
+                                     dk, dv, _dt(x), int(order), _stream())
     if st != 0:
         raise GdnError("gdn_decode_step_gated", st)
     return out

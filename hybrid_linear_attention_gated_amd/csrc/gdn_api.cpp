@@ -44,6 +44,8 @@ int check_seqs(const int32_t *cu, int N, int T) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+bool valid_order(int order) { return order == GDN_ORDER_DECAY_FIRST || order == GDN_ORDER_RETRIEVE_FIRST; }
+
 }  // namespace
 
 extern "C" {
@@ -105,7 +107,7 @@ namespace {
 // Shared validation + dispatch of gdn_chunk_prefill and its two phases.
 int chunk_prefill_impl(const float *q, const float *k, const float *v, const float *g, const float *beta,
                        const int32_t *cu_seqlens, int N, const float *initial_state, float *final_state, float *o,
-                       float scale, int T, int Hk, int Hv, int dk, int dv, int math, void *workspace,
+                       float scale, int T, int Hk, int Hv, int dk, int dv, int math, int order, void *workspace,
                        size_t workspace_bytes, void *stream, int phases) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
@@ -114,6 +116,7 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
         if (T > 0 && need_outputs && !o) return GDN_ERR_NULL_POINTER;
         if (int e = check_heads(Hk, Hv)) return e;
         if (math != GDN_MATH_F32 && math != GDN_MATH_MFMA) return GDN_ERR_UNSUPPORTED;
+        if (!valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (phases != 3 && math != GDN_MATH_MFMA) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128)) return GDN_ERR_UNSUPPORTED;
         if (math == GDN_MATH_MFMA && !gdn::chunked_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
@@ -134,6 +137,7 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
             if (overlap(rws, in)) return GDN_ERR_ALIAS;
         gdn::PrefillArgs a{q, k, v, g, beta, cu_seqlens, N, initial_state, final_state, o, scale,
                            T, Hk, Hv, dk, dv, workspace, workspace_bytes};
+        a.order = order;
         hipStream_t st = (hipStream_t)stream;
         return hip_status(chunked ? gdn::launch_prefill_chunked(a, st, phases) : gdn::launch_prefill_recurrent(a, st));
     } catch (...) {
@@ -145,25 +149,25 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
 
 int gdn_chunk_prefill(const float *q, const float *k, const float *v, const float *g, const float *beta,
                       const int32_t *cu_seqlens, int N, const float *initial_state, float *final_state, float *o,
-                      float scale, int T, int Hk, int Hv, int dk, int dv, int math, void *workspace,
+                      float scale, int T, int Hk, int Hv, int dk, int dv, int math, int order, void *workspace,
                       size_t workspace_bytes, void *stream) {
     return chunk_prefill_impl(q, k, v, g, beta, cu_seqlens, N, initial_state, final_state, o, scale, T, Hk, Hv, dk,
-                              dv, math, workspace, workspace_bytes, stream, 3);
+                              dv, math, order, workspace, workspace_bytes, stream, 3);
 }
 
 int gdn_chunk_prefill_local(const float *q, const float *k, const float *v, const float *g, const float *beta,
                             const int32_t *cu_seqlens, int N, float scale, int T, int Hk, int Hv, int dk, int dv,
-                            void *workspace, size_t workspace_bytes, void *stream) {
+                            int order, void *workspace, size_t workspace_bytes, void *stream) {
     return chunk_prefill_impl(q, k, v, g, beta, cu_seqlens, N, nullptr, nullptr, nullptr, scale, T, Hk, Hv, dk, dv,
-                              GDN_MATH_MFMA, workspace, workspace_bytes, stream, 1);
+                              GDN_MATH_MFMA, order, workspace, workspace_bytes, stream, 1);
 }
 
 int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N, const float *initial_state, float *final_state,
                             float *o, int T, int Hk, int Hv, int dk, int dv, const void *workspace,
                             size_t workspace_bytes, void *stream) {
     return chunk_prefill_impl(nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, N, initial_state, final_state,
-                              o, 1.0f, T, Hk, Hv, dk, dv, GDN_MATH_MFMA, const_cast<void *>(workspace),
-                              workspace_bytes, stream, 2);
+                              o, 1.0f, T, Hk, Hv, dk, dv, GDN_MATH_MFMA, GDN_ORDER_DECAY_FIRST,
+                              const_cast<void *>(workspace), workspace_bytes, stream, 2);
 }
 
 namespace {
@@ -172,12 +176,12 @@ namespace {
 int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N, const void *conv_state_in,
                  void *conv_state_out, const float *g, const float *beta, const float *initial_state,
                  float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
-                 int dtype, void *workspace, size_t workspace_bytes, void *stream, int phases) {
+                 int dtype, int order, void *workspace, size_t workspace_bytes, void *stream, int phases) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
         if (!conv_w || (T > 0 && (!x || !g || !beta || ((phases & 2) && !o)))) return GDN_ERR_NULL_POINTER;
         if (int e = check_heads(Hk, Hv)) return e;
-        if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+        if (!valid_dtype(dtype) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!gdn::chunked_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
         if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !std::isfinite(scale)) return GDN_ERR_BAD_SHAPE;
         const size_t need = gdn::chunked_workspace_bytes(T, N, Hv, dk, dv);
@@ -201,6 +205,7 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
         const gdn::FusedPrep fp{x, conv_w, conv_state_in, conv_state_out, dtype == GDN_BF16, l2_eps};
         gdn::PrefillArgs a{nullptr, nullptr, nullptr, g, beta, cu_seqlens, N, initial_state, final_state, o, scale,
                            T, Hk, Hv, dk, dv, workspace, workspace_bytes, &fp};
+        a.order = order;
         return hip_status(gdn::launch_prefill_chunked(a, (hipStream_t)stream, phases));
     } catch (...) {
         return GDN_ERR_HIP;
@@ -212,17 +217,18 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
 int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N, const void *conv_state_in,
                 void *conv_state_out, const float *g, const float *beta, const float *initial_state,
                 float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
-                int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+                int dtype, int order, void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
-                        final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, dtype, workspace, workspace_bytes, stream, 3);
+                        final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, dtype, order, workspace, workspace_bytes,
+                        stream, 3);
 }
 
 int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
                       const void *conv_state_in, void *conv_state_out, const float *g, const float *beta,
-                      float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv, int dtype, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+                      float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv, int dtype, int order,
+                      void *workspace, size_t workspace_bytes, void *stream) {
     return prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, nullptr, nullptr, nullptr,
-                        scale, l2_eps, T, Hk, Hv, dk, dv, dtype, workspace, workspace_bytes, stream, 1);
+                        scale, l2_eps, T, Hk, Hv, dk, dv, dtype, order, workspace, workspace_bytes, stream, 1);
 }
 
 namespace {
@@ -230,14 +236,14 @@ namespace {
 // Shared validation + dispatch of gdn_decode_step and gdn_decode_step_gated (z, gamma, out set).
 int decode_impl(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
                 float *state, float *o, const void *z, const void *gamma, void *out, float scale, float l2_eps,
-                float norm_eps, int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream) {
+                float norm_eps, int B, int Hk, int Hv, int dk, int dv, int dtype, int order, void *stream) {
     try {
         const bool gated = out != nullptr || z != nullptr || gamma != nullptr;
         if (B < 0) return GDN_ERR_BAD_SHAPE;
         if (!conv_w || (B > 0 && (!x || !conv_state || !g || !beta || !state))) return GDN_ERR_NULL_POINTER;
         if (gated ? (!gamma || (B > 0 && (!z || !out))) : (B > 0 && !o)) return GDN_ERR_NULL_POINTER;
         if (int e = check_heads(Hk, Hv)) return e;
-        if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+        if (!valid_dtype(dtype) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128)) return GDN_ERR_UNSUPPORTED;
         if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps)) return GDN_ERR_BAD_SHAPE;
         if (gated && (!(norm_eps >= 0.f) || !std::isfinite(norm_eps))) return GDN_ERR_BAD_SHAPE;
@@ -255,6 +261,7 @@ int decode_impl(const void *x, const void *conv_w, void *conv_state, const float
         if (overlap(rcs, rst)) return GDN_ERR_ALIAS;
         gdn::DecodeArgs a{x, conv_w, conv_state, g, beta, state, o, scale, l2_eps, B, Hk, Hv, dk, dv,
                           dtype == GDN_BF16};
+        a.order = order;
         if (gated) {
             a.z = z;
             a.gamma = gamma;
@@ -271,19 +278,19 @@ int decode_impl(const void *x, const void *conv_w, void *conv_state, const float
 
 int gdn_decode_step(const void *x, const void *conv_w, void *conv_state, const float *g, const float *beta,
                     float *state, float *o, float scale, float l2_eps, int B, int Hk, int Hv, int dk, int dv,
-                    int dtype, void *stream) {
+                    int dtype, int order, void *stream) {
     if (!o && B > 0) return GDN_ERR_NULL_POINTER;
     return decode_impl(x, conv_w, conv_state, g, beta, state, o, nullptr, nullptr, nullptr, scale, l2_eps, 0.f, B,
-                       Hk, Hv, dk, dv, dtype, stream);
+                       Hk, Hv, dk, dv, dtype, order, stream);
 }
 
 int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state, const float *g,
                           const float *beta, float *state, const void *z, const void *gamma, void *out,
                           float scale, float l2_eps, float norm_eps, int B, int Hk, int Hv, int dk, int dv,
-                          int dtype, void *stream) {
+                          int dtype, int order, void *stream) {
     if (!gamma || (B > 0 && (!z || !out))) return GDN_ERR_NULL_POINTER;
     return decode_impl(x, conv_w, conv_state, g, beta, state, nullptr, z, gamma, out, scale, l2_eps, norm_eps, B,
-                       Hk, Hv, dk, dv, dtype, stream);
+                       Hk, Hv, dk, dv, dtype, order, stream);
 }
 
 int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *out, long rows, int dv,

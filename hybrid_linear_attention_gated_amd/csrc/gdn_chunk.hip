@@ -16,7 +16,11 @@
 //   S' = e^{G_c} S + K^T diag(e^{G_c - G}) Delta
 //
 // It equals the token recurrence in exact arithmetic (the CPU tests check the
-// fp64 version of it against the token-by-token oracle).
+// fp64 version of it against the token-by-token oracle).  With order = 1 the
+// retrieval reads the state before the decay, as "7.6 Qwen3.5: the linear-attention
+// hybrid" (section 7.6.2) writes the recurrence; unrolling it puts Gr_t = G_t - g_t
+// in place of G_t in the first factor of A and in W (Gr = G for order 0), and
+// leaves U, P, O and S' as they are.
 //
 // Precision.  Inputs q, k, v are fp32.  The outputs of this layer are heavy
 // tailed (the largest |o| is tens of times its RMS), so one bf16 rounding of
@@ -179,10 +183,10 @@ struct LocalSmem {
     static constexpr int AOFF = ADIAG + 4 * ADIAG_BLK * 4;   // strict-lower blocks of A: [6][hi, lo][64] bf16x4
     static constexpr int PT = AOFF + 6 * 2 * 64 * 8;         // P^T blocks c <= r: [10][64] f32x4
     static constexpr int XT = PT + 10 * 64 * 16;             // scaled T^T, M^T blocks c <= r: [4][10][hi, lo][64] bf16x4
-    static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^G, e^{G_c - G}, scale e^G
+    static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^Gr, e^{G_c - G}, scale e^G, Gr
     static constexpr int VLD = D + 4;                        // fused conv: fp32 v plane [64][VLD] in the XT region
     static_assert(64 * VLD * 4 <= SCAL - XT, "v plane fits in the T / M region");
-    static constexpr int SIZE = SCAL + 5 * 64 * 4;
+    static constexpr int SIZE = SCAL + 6 * 64 * 4;
     static_assert(NW * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
 };
 
@@ -217,7 +221,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0,
-    const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps) {
+    const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
+    int order) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr int NWH = LocalShape<D>::NWH, NW = LocalShape<D>::NW, NT = LocalShape<D>::THREADS;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     f32x4 *Pt = reinterpret_cast<f32x4 *>(smem + SM::PT);           // [10][64]
     bf16x4 *Xt = reinterpret_cast<bf16x4 *>(smem + SM::XT);         // [4][10][2][64]
     float *Gs = reinterpret_cast<float *>(smem + SM::SCAL);
-    float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256;
+    float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256, *GRs = Gs + 320;
     enum { XT_TW = 0, XT_TU = 1, XT_MW = 2, XT_MU = 3 };   // published operand sets
 
     // wave index in a scalar register: wave-level branches and LDS bases stay uniform
@@ -300,9 +305,13 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         }
         const float Gc = __shfl(G, 63, kWave);
         const float eg = __expf(G);
+        // decay seen by the retrieval of token t: G_t, or G_{t-1} = G_t - g_t when the
+        // retrieval reads the state before the decay (order 1)
+        const float Gr = order == 0 ? G : G - gg;
         Gs[lane] = G;
+        GRs[lane] = Gr;
         Bs[lane] = bb;
-        BEG[lane] = bb * eg;
+        BEG[lane] = bb * (order == 0 ? eg : __expf(Gr));
         DCs[lane] = __expf(Gc - G);
         QS[lane] = scale * eg;
         if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
@@ -415,6 +424,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         const f32x4 Gb = *reinterpret_cast<const f32x4 *>(Gs + 16 * b + 4 * kg);
         if (doKK) {
             const f32x4 Bb = *reinterpret_cast<const f32x4 *>(Bs + 16 * b + 4 * kg);
+            const f32x4 Grb = *reinterpret_cast<const f32x4 *>(GRs + 16 * b + 4 * kg);
             for (int c = 0; c <= b; ++c) {
                 f32x4 acc = zero4();
 #pragma unroll
@@ -424,14 +434,14 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
                                     *reinterpret_cast<const bf16x8 *>(Kl + off)};
                     acc = mfma16x3(ka[ks], kb, acc);
                 }
-                // A[t][i] = b_t e^{G_t - G_i} k_t . k_i for i < t; t = 16b + 4kg + r, i = 16c + l16
+                // A[t][i] = b_t e^{Gr_t - G_i} k_t . k_i for i < t; t = 16b + 4kg + r, i = 16c + l16
                 const int i = 16 * c + l16;
                 const float Gi = Gs[i];
                 f32x4 a;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * b + 4 * kg + r;
-                    a[r] = i < t ? Bb[r] * __expf(Gb[r] - Gi) * acc[r] : 0.f;
+                    a[r] = i < t ? Bb[r] * __expf(Grb[r] - Gi) * acc[r] : 0.f;
                 }
                 if (c == b) {
 #pragma unroll
@@ -1071,15 +1081,15 @@ static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int
     if (!a.fp) {
         hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)nullptr,
-                           (const float *)nullptr, (const float *)nullptr, 0.f);
+                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order);
     } else if (a.fp->bf16) {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const bf16 *)a.fp->x,
-                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps);
+                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order);
     } else {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)a.fp->x,
-                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps);
+                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order);
     }
     return hipGetLastError();
 }

@@ -5,7 +5,9 @@
 // Method: the decode branch of "Hugging Face Transformers: Qwen3.5-MoE series
 // explained", section 8.2 (conv-cache update, then the recurrent rule, then
 // both caches written back) with the recurrent-mode step of section 4.3:
-// S <- a S; m = S^T k; delta = b (v - m); S <- S + k delta^T; o = S^T q.
+// S <- a S; m = S^T k; delta = b (v - m); S <- S + k delta^T; o = S^T q
+// (order 1: m is taken from the state before the decay, the recurrence as "7.6 Qwen3.5:
+// the linear-attention hybrid", section 7.6.2, writes it).
 //
 // Design (HBM-bound, ~0.84 flop per byte): one 256-thread workgroup per
 // (sequence, key head) owns the conv channels of that key head and of all value
@@ -14,7 +16,7 @@
 // (row group, column quad) keeps its rows as float4 registers, so a wave reads
 // and writes whole 512-byte rows.  Since S' = a S + k delta^T, both reductions
 // needed (S^T k and S^T q, over dk) are taken from the OLD state in the same
-// pass:  m = a (S^T k),  o = a (S^T q) + delta (k . q).  Row-group partial sums
+// pass:  m = a (S^T k) (order 1: S^T k),  o = a (S^T q) + delta (k . q).  Row-group partial sums
 // are combined with xor shuffles inside a wave and through LDS across waves.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
@@ -53,7 +55,8 @@ template <typename T, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const T *__restrict__ x, const T *__restrict__ w, T *cs, const float *__restrict__ g,
     const float *__restrict__ beta, float *state, float *__restrict__ o, float scale, float eps,
-    int Hk, int Hv, const T *__restrict__ z, const T *__restrict__ gamma, T *__restrict__ out, float norm_eps) {
+    int Hk, int Hv, const T *__restrict__ z, const T *__restrict__ gamma, T *__restrict__ out, float norm_eps,
+    int order) {
     constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
     constexpr int RG = kDecThreads / TPR;        // row groups
     constexpr int RPT = DK >= RG ? DK / RG : 1;  // rows per thread
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) { sk += red[ww][0][4 * cg + e]; sq += red[ww][1][4 * cg + e]; }
-            delta[e] = bt * (v_s[4 * cg + e] - a * sk);
+            delta[e] = bt * (v_s[4 * cg + e] - (order == 0 ? a * sk : sk));
             pq[e] = a * sq + delta[e] * kq;   // output column 4cg+e
         }
         if constexpr (GATED) {
@@ -198,11 +201,11 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
                            (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, (float *)nullptr,
                            a.scale, a.eps, a.Hk, a.Hv, (const T *)a.z, (const T *)a.gamma, (T *)a.out,
-                           a.norm_eps);
+                           a.norm_eps, a.order);
     } else {
         hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
                            (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, a.o, a.scale, a.eps,
-                           a.Hk, a.Hv, (const T *)nullptr, (const T *)nullptr, (T *)nullptr, 0.f);
+                           a.Hk, a.Hv, (const T *)nullptr, (const T *)nullptr, (T *)nullptr, 0.f, a.order);
     }
     return hipGetLastError();
 }

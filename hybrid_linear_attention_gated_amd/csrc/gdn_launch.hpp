@@ -44,6 +44,7 @@ struct PrefillArgs {
     void *ws;
     size_t ws_bytes;
     const FusedPrep *fp = nullptr;   // set: fused prep (chunked path only)
+    int order = 0;                   // 0: decay before the retrieval, 1: retrieval from the undecayed state
 };
 
 struct DecodeArgs {
@@ -55,6 +56,7 @@ struct DecodeArgs {
     float scale, eps;
     int B, Hk, Hv, dk, dv;
     bool bf16;
+    int order = 0;   // as in PrefillArgs
     // gated output (gdn_decode_step_gated): when `out` is set, out = RMSNorm(o) * gamma *
     // SiLU(z) in the element type is written instead of o
     const void *z = nullptr, *gamma = nullptr;

@@ -3,7 +3,9 @@
 //
 // Method: the recurrent-mode step of "Hugging Face Transformers: Qwen3.5-MoE
 // series explained", section 4.3 (decay, retrieve, correct, write, read), one
-// token at a time, all in fp32 arithmetic.  It serves GDN_MATH_F32 (whose
+// token at a time, all in fp32 arithmetic; with order = 1 the retrieval reads the
+// state before the decay, as "7.6 Qwen3.5: the linear-attention hybrid" (section
+// 7.6.2) writes the recurrence.  It serves GDN_MATH_F32 (whose
 // 1e-4 RMS-relative accuracy leaves no room for 16-bit MFMA operands) and the
 // head dims that the chunked MFMA path does not tile.
 //
@@ -20,7 +22,7 @@ template <int DK>
 __global__ __launch_bounds__(128) void prefill_recurrent_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
-    const float *s0, float *sf, float *__restrict__ o, float scale, int Ttot, int Hk, int Hv, int dv) {
+    const float *s0, float *sf, float *__restrict__ o, float scale, int Ttot, int Hk, int Hv, int dv, int order) {
     __shared__ float kq[2][2][DK];
     const int h = blockIdx.x, s = blockIdx.y;
     const int j = threadIdx.x;
@@ -44,8 +46,13 @@ __global__ __launch_bounds__(128) void prefill_recurrent_kernel(
         const float b = beta[(size_t)t * Hv + h];
         if (act) {
             float m = 0.f;
+            if (order == 0) {
 #pragma unroll
-            for (int i = 0; i < DK; ++i) { S[i] *= a; m = fmaf(S[i], kq[buf][0][i], m); }
+                for (int i = 0; i < DK; ++i) { S[i] *= a; m = fmaf(S[i], kq[buf][0][i], m); }
+            } else {
+#pragma unroll
+                for (int i = 0; i < DK; ++i) { m = fmaf(S[i], kq[buf][0][i], m); S[i] *= a; }
+            }
             const float d = b * (v[((size_t)t * Hv + h) * dv + j] - m);
             float acc = 0.f;
 #pragma unroll
@@ -63,7 +70,7 @@ template <int DK>
 static hipError_t launch_rec_t(const PrefillArgs &a, hipStream_t st) {
     const int threads = a.dv <= 64 ? 64 : 128;
     hipLaunchKernelGGL((prefill_recurrent_kernel<DK>), dim3(a.Hv, a.N), dim3(threads), 0, st, a.q, a.k, a.v, a.g,
-                       a.beta, a.cu, a.s0, a.sf, a.o, a.scale, a.T, a.Hk, a.Hv, a.dv);
+                       a.beta, a.cu, a.s0, a.sf, a.o, a.scale, a.T, a.Hk, a.Hv, a.dv, a.order);
     return hipGetLastError();
 }
 

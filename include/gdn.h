@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -78,6 +78,17 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
  *                 operands where the accuracy needs them (dk = dv in {64, 128});
  *                 about 1e-3 RMS-relative on the 0.8B layer shape. */
 typedef enum { GDN_MATH_F32 = 0, GDN_MATH_MFMA = 1 } gdn_math;
+
+/* Order of decay and retrieval in one step of the recurrence (argument `order`).
+ *  GDN_ORDER_DECAY_FIRST   : S <- a S; m = S^T k; delta = b (v - m); S += k delta^T;
+ *                            o = S^T q ("Hugging Face Transformers: Qwen3.5-MoE series
+ *                            explained", section 4.3).  The default.
+ *  GDN_ORDER_RETRIEVE_FIRST: m = S^T k from the state before the decay, then
+ *                            S <- a S + k [b (v - m)]^T; o = S^T q ("7.6 Qwen3.5: the
+ *                            linear-attention hybrid", section 7.6.2, as printed).
+ * The pages disagree; the two agree when a = 1.  Any other value ->
+ * GDN_ERR_UNSUPPORTED. */
+typedef enum { GDN_ORDER_DECAY_FIRST = 0, GDN_ORDER_RETRIEVE_FIRST = 1 } gdn_order;
 
 /*
  * gdn_conv_qk_prep -- depthwise causal conv1d (kernel 4, no bias) + SiLU + split
@@ -130,6 +141,7 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *                  With GDN_MATH_MFMA it holds the per-(chunk, value head) results
  *                  of the chunk-local phase and one state per (sequence, value head).
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
+ *   order          gdn_order (decay before or after the retrieval)
  *
  * With GDN_MATH_MFMA, when the packed chunks are many (at least 256) and the state
  * pass would occupy at most half of the device's compute units, the chunks are cut
@@ -144,7 +156,7 @@ int gdn_chunk_prefill(const float *q, const float *k, const float *v,
                       const int32_t *cu_seqlens, int N,
                       const float *initial_state, float *final_state,
                       float *o, float scale,
-                      int T, int Hk, int Hv, int dk, int dv, int math,
+                      int T, int Hk, int Hv, int dk, int dv, int math, int order,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -157,12 +169,12 @@ int gdn_chunk_prefill(const float *q, const float *k, const float *v,
  * state.  Arguments mean what they mean for gdn_chunk_prefill; the workspace
  * must not be modified between the two calls, and cu_seqlens, N, T and the head
  * sizes must be the same in both.  Running local then state equals one
- * gdn_chunk_prefill call with GDN_MATH_MFMA.
+ * gdn_chunk_prefill call with GDN_MATH_MFMA.  `order` only enters the local phase.
  */
 int gdn_chunk_prefill_local(const float *q, const float *k, const float *v,
                             const float *g, const float *beta,
                             const int32_t *cu_seqlens, int N, float scale,
-                            int T, int Hk, int Hv, int dk, int dv,
+                            int T, int Hk, int Hv, int dk, int dv, int order,
                             void *workspace, size_t workspace_bytes, void *stream);
 int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N,
                             const float *initial_state, float *final_state, float *o,
@@ -179,7 +191,7 @@ int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N,
  *
  *   x, conv_w, conv_state_in, conv_state_out, dtype, l2_eps   as in gdn_conv_qk_prep
  *                  (conv_state_out may alias conv_state_in exactly, or be NULL)
- *   g, beta, initial_state, final_state, o, scale   as in gdn_chunk_prefill
+ *   g, beta, initial_state, final_state, o, scale, order   as in gdn_chunk_prefill
  *   dk = dv in {64, 128} (GDN_ERR_UNSUPPORTED otherwise)
  *   workspace      at least gdn_chunk_prefill_workspace_size(T, N, Hk, Hv, dk, dv,
  *                  GDN_MATH_MFMA) bytes; must not overlap any other argument.
@@ -191,7 +203,7 @@ int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, in
                 const float *g, const float *beta,
                 const float *initial_state, float *final_state, float *o,
                 float scale, float l2_eps,
-                int T, int Hk, int Hv, int dk, int dv, int dtype,
+                int T, int Hk, int Hv, int dk, int dv, int dtype, int order,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -205,7 +217,7 @@ int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, in
 int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
                       const void *conv_state_in, void *conv_state_out,
                       const float *g, const float *beta, float scale, float l2_eps,
-                      int T, int Hk, int Hv, int dk, int dv, int dtype,
+                      int T, int Hk, int Hv, int dk, int dv, int dtype, int order,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
@@ -222,13 +234,14 @@ int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqle
  *   g, beta     [B][Hv] fp32
  *   state       [B][Hv][dk][dv]     fp32, in/out
  *   o           [B][Hv][dv]         fp32; must not overlap any other argument
+ *   order       gdn_order, as in gdn_chunk_prefill
  * dk, dv in {16, 32, 64, 128}.
  */
 int gdn_decode_step(const void *x, const void *conv_w, void *conv_state,
                     const float *g, const float *beta,
                     float *state, float *o,
                     float scale, float l2_eps,
-                    int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream);
+                    int B, int Hk, int Hv, int dk, int dv, int dtype, int order, void *stream);
 
 /*
  * gdn_gated_rmsnorm -- the gated RMSNorm at the output of the linear-attention layer
@@ -263,7 +276,7 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
                           const float *g, const float *beta, float *state,
                           const void *z, const void *gamma, void *out,
                           float scale, float l2_eps, float norm_eps,
-                          int B, int Hk, int Hv, int dk, int dv, int dtype, void *stream);
+                          int B, int Hk, int Hv, int dk, int dv, int dtype, int order, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(int status);

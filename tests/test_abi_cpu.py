@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 1
+    assert L.gdn_abi_version() == 2
     for code in range(7):
         assert L.gdn_status_string(code).decode().startswith("GDN_")
     assert b"unknown" in L.gdn_status_string(99)
@@ -79,13 +79,13 @@ def test_prefill_validation(L):
     assert L.gdn_chunk_prefill_workspace_size(T, 1, H, H, 32, 32, 1) == 0    # recurrent path needs none
 
     base = dict(q=P(0), k=P(1 << 24), v=P(2 << 24), g=P(3 << 24), b=P(4 << 24), cu=None, N=1, s0=None, sf=None,
-                o=P(5 << 24), scale=1.0, T=T, Hk=H, Hv=H, dk=d, dv=d, dt=1, ws=P(1 << 30), wsb=need)
+                o=P(5 << 24), scale=1.0, T=T, Hk=H, Hv=H, dk=d, dv=d, dt=1, order=0, ws=P(1 << 30), wsb=need)
 
     def call(**kw):
         a = dict(base, **kw)
         return L.gdn_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["b"], a["cu"], a["N"], a["s0"], a["sf"], a["o"],
                                    ctypes.c_float(a["scale"]), a["T"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"],
-                                   a["ws"], ctypes.c_size_t(a["wsb"]), None)
+                                   a["order"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
     assert call(o=None) == 1
     assert call(Hk=3, Hv=4) == 2
     assert call(dk=256) == 3
@@ -95,6 +95,8 @@ def test_prefill_validation(L):
     assert call(o=P(16)) == 6                                   # o overlaps q
     assert call(s0=P(6 << 24), sf=P((6 << 24) + 4)) == 6          # partial state alias
     assert call(scale=float("inf")) == 2
+    assert call(order=2) == 3
+    assert call(order=-1, dt=0) == 3                            # also on the fp32 path
 
 
 def test_fused_prefill_validation(L):
@@ -102,14 +104,14 @@ def test_fused_prefill_validation(L):
     T, Hk, Hv, d = 128, 2, 2, 128
     need = L.gdn_chunk_prefill_workspace_size(T, 1, Hk, Hv, d, d, 1)
     base = dict(x=P(0), w=P(1 << 24), cu=None, N=1, csi=None, cso=None, g=P(3 << 24), b=P(4 << 24), s0=None,
-                sf=None, o=P(5 << 24), scale=1.0, eps=1e-6, T=T, Hk=Hk, Hv=Hv, dk=d, dv=d, dt=1, ws=P(1 << 30),
-                wsb=need)
+                sf=None, o=P(5 << 24), scale=1.0, eps=1e-6, T=T, Hk=Hk, Hv=Hv, dk=d, dv=d, dt=1, order=0,
+                ws=P(1 << 30), wsb=need)
 
     def call(**kw):
         a = dict(base, **kw)
         return L.gdn_prefill(a["x"], a["w"], a["cu"], a["N"], a["csi"], a["cso"], a["g"], a["b"], a["s0"], a["sf"],
                              a["o"], ctypes.c_float(a["scale"]), ctypes.c_float(a["eps"]), a["T"], a["Hk"], a["Hv"],
-                             a["dk"], a["dv"], a["dt"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
+                             a["dk"], a["dv"], a["dt"], a["order"], a["ws"], ctypes.c_size_t(a["wsb"]), None)
     assert call(w=None) == 1
     assert call(x=None) == 1
     assert call(o=None) == 1
@@ -126,30 +128,33 @@ def test_fused_prefill_validation(L):
     assert call(csi=P(6 << 24), cso=P((6 << 24) + 2)) == 6      # partial conv cache alias
     assert call(s0=P(7 << 24), sf=P((7 << 24) + 4)) == 6        # partial state alias
     assert call(ws=P(8)) == 6                                   # workspace overlaps x
+    assert call(order=5) == 3
     # the local phase alone: no o or states
     assert L.gdn_prefill_local(P(0), None, None, 1, None, None, P(3 << 24), P(4 << 24), ctypes.c_float(1.0),
-                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, P(1 << 30), ctypes.c_size_t(need),
+                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, 0, P(1 << 30), ctypes.c_size_t(need),
                                None) == 1                       # no conv weights
     assert L.gdn_prefill_local(P(0), P(1 << 24), None, 1, None, None, P(3 << 24), P(4 << 24), ctypes.c_float(1.0),
-                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, P(1 << 30), ctypes.c_size_t(need - 1),
+                               ctypes.c_float(1e-6), T, Hk, Hv, d, d, 1, 0, P(1 << 30), ctypes.c_size_t(need - 1),
                                None) == 4
 
 
 def test_decode_validation(L):
     P = _ptr
     base = dict(x=P(0), w=P(1 << 24), cs=P(2 << 24), g=P(3 << 24), b=P(4 << 24), st=P(5 << 24), o=P(6 << 24),
-                B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1)
+                B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1, order=0)
 
     def call(**kw):
         a = dict(base, **kw)
         return L.gdn_decode_step(a["x"], a["w"], a["cs"], a["g"], a["b"], a["st"], a["o"], ctypes.c_float(1.0),
-                                 ctypes.c_float(1e-6), a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"], None)
+                                 ctypes.c_float(1e-6), a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["dt"],
+                                 a["order"], None)
     assert call(st=None) == 1
     assert call(B=-1) == 2
     assert call(Hv=3) == 2
     assert call(dk=256) == 3
     assert call(o=P(8)) == 6
     assert call(cs=P((5 << 24) + 8)) == 6                     # conv cache overlaps the state
+    assert call(order=3) == 3
 
 
 def test_gated_rmsnorm_validation(L):
@@ -177,14 +182,14 @@ def test_gated_rmsnorm_validation(L):
 def test_decode_gated_validation(L):
     P = _ptr
     base = dict(x=P(0), w=P(1 << 24), cs=P(2 << 24), g=P(3 << 24), b=P(4 << 24), st=P(5 << 24), z=P(6 << 24),
-                gm=P(7 << 24), out=P(8 << 24), B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1, neps=1e-6)
+                gm=P(7 << 24), out=P(8 << 24), B=4, Hk=2, Hv=2, dk=16, dv=16, dt=1, neps=1e-6, order=0)
 
     def call(**kw):
         a = dict(base, **kw)
         return L.gdn_decode_step_gated(a["x"], a["w"], a["cs"], a["g"], a["b"], a["st"], a["z"], a["gm"],
                                        a["out"], ctypes.c_float(1.0), ctypes.c_float(1e-6),
                                        ctypes.c_float(a["neps"]), a["B"], a["Hk"], a["Hv"], a["dk"], a["dv"],
-                                       a["dt"], None)
+                                       a["dt"], a["order"], None)
     assert call(z=None) == 1
     assert call(gm=None) == 1
     assert call(out=None) == 1

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, f32np
+from helpers import TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, err_ratio, f32np
 from hybrid_linear_attention_gated_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -473,3 +473,72 @@ def test_fused_prefill_then_gated_rmsnorm_layer_4k(gdn):
     assert row_err.max() <= TOL_BF16
     # the norm itself, on the prefill's own output: one bf16 rounding of the fp64 value
     assert_bf16_rounded("out (norm of the GPU's o)", outg, oracle.gated_rmsnorm(og, f32np(z), f32np(gamma), 1e-6))
+
+
+# ------------------------------------------------------------------ retrieval order 1 (undecayed retrieval)
+
+def _differs(name, gpu, other_ref, tol):
+    """The order flag reaches the kernel: the result is far from the other order's reference."""
+    r = err_ratio(gpu, other_ref)
+    print(f"    {name} vs the other order: {r:.3e}", flush=True)
+    assert r > 50 * tol
+
+
+@pytest.mark.parametrize("math,d", [("mfma", 128), ("mfma", 64), ("f32", 128), ("f32", 32)])
+def test_core_order1(gdn, math, d):
+    lengths = [1, 63, 0, 200, 65, 129]
+    announce(f"core order 1 ({math}, d={d}) lengths={lengths}")
+    wl = inputs.core_workload("ord1", 950 + d, lengths, 2, 4, d, d, random_states=True, scale=0.5)
+    tol = TOL_F32 if math == "f32" else TOL_BF16
+    args = (f32np(wl.q), f32np(wl.k), f32np(wl.v), f32np(wl.g), f32np(wl.beta), wl.cu_seqlens.numpy())
+    o1, f1 = oracle.recurrence(*args, s0=f32np(wl.state), scale=0.5, order=1)
+    o0, _ = oracle.recurrence(*args, s0=f32np(wl.state), scale=0.5, order=0)
+    o, f = gdn.chunk_prefill(_cuda(wl.q), _cuda(wl.k), _cuda(wl.v), _cuda(wl.g), _cuda(wl.beta),
+                             cu_seqlens=_cuda(wl.cu_seqlens), initial_state=_cuda(wl.state), scale=0.5, math=math,
+                             order=1)
+    torch.cuda.synchronize()
+    assert_parity("o", f32np(o), o1, tol)
+    assert_parity("final_state", f32np(f), f1, tol)
+    _differs("o", f32np(o), o0, tol)
+
+
+def test_fused_prefill_order1(gdn):
+    announce(f"fused prefill order 1, lengths={FUSED_LENGTHS}")
+    wl = inputs.prefill_workload("fused_ord1", 960, FUSED_LENGTHS, 2, 4, 128, random_states=True)
+    cu = wl.cu_seqlens
+    q_r, k_r, v_r, cs_r = oracle.prep(f32np(wl.x), f32np(wl.conv_w), cu.numpy(), 2, 4, 128, 128,
+                                      cs_in=f32np(wl.conv_state))
+    o1, f1 = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu.numpy(), s0=f32np(wl.state), order=1)
+    cso = torch.empty(wl.conv_state.shape, dtype=torch.bfloat16, device=DEV)
+    o, f = gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), 2, 4, 128, 128,
+                       cu_seqlens=_cuda(cu), conv_state_in=_cuda(wl.conv_state), conv_state_out=cso,
+                       initial_state=_cuda(wl.state), order=1)
+    torch.cuda.synchronize()
+    assert_parity("o", f32np(o), o1, TOL_BF16)
+    assert_parity("final_state", f32np(f), f1, TOL_BF16)
+    np.testing.assert_array_equal(f32np(cso), cs_r)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_order1(gdn, gated):
+    announce(f"decode order 1 (gated={gated})")
+    B, Hk, Hv, d = 6, 2, 4, 64
+    dw = inputs.decode_workload("dec_ord1", 970, B, Hk, Hv, d)
+    args = (f32np(dw.x), f32np(dw.conv_w), f32np(dw.conv_state), f32np(dw.g), f32np(dw.beta), f32np(dw.state),
+            Hk, Hv, d, d)
+    o1, s1, cs1 = oracle.decode(*args, order=1)
+    o0, _, _ = oracle.decode(*args, order=0)
+    st, cs = _cuda(dw.state), _cuda(dw.conv_state)
+    if gated:
+        z, gamma = inputs.gate_inputs(971, (B, Hv, d), d, "bf16")
+        out = gdn.decode_step_gated(_cuda(dw.x), _cuda(dw.conv_w), cs, _cuda(dw.g), _cuda(dw.beta), st, _cuda(z),
+                                    _cuda(gamma), Hk, Hv, d, d, order=1)
+        torch.cuda.synchronize()
+        assert_bf16_rounded("out", f32np(out), oracle.gated_rmsnorm(o1, f32np(z), f32np(gamma), 1e-6))
+    else:
+        o = gdn.decode_step(_cuda(dw.x), _cuda(dw.conv_w), cs, _cuda(dw.g), _cuda(dw.beta), st, Hk, Hv, d, d, order=1)
+        torch.cuda.synchronize()
+        assert_parity("o", f32np(o), o1, TOL_F32)
+        _differs("o", f32np(o), o0, TOL_F32)
+    assert_parity("state", f32np(st), s1, TOL_F32)
+    np.testing.assert_array_equal(f32np(cs), cs1)
