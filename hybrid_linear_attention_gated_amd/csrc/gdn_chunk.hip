@@ -40,11 +40,13 @@
 //    Explicit T = (I + A)^-1 and M = P T by block back substitution, then four
 //    products.  Writes -W' = -diag(e^{G_c - G}) W and Qt as fp16 MFMA A-operand
 //    fragments, K^T as bf16 hi / lo A-operand fragments, and
-//    U' = diag(e^{G_c - G}) U and Ol as fp32 accumulator-layout tiles, so the
+//    U' = diag(e^{G_c - G}) U and Ol^T as fp32 accumulator-layout tiles, so the
 //    state pass reads every operand with one coalesced 16-byte load per lane and
 //    every product accumulates straight into its MFMA chain:
-//      Delta' = diag(e^{G_c - G}) Delta = U' + (-W') S,   O = Ol + Qt S,
+//      Delta' = diag(e^{G_c - G}) Delta = U' + (-W') S,   O^T = Ol^T + S^T Qt^T,
 //      S' = e^{G_c} S + K^T Delta'.
+//    O is formed transposed (the same fragments with A and B swapped) so that a
+//    lane holds 4 consecutive columns of an output row: one 16-byte store per tile.
 //  state_pass_kernel: one workgroup per (sequence, value head, two 16-column
 //    strips of the state); a strip's fp32 state lives in MFMA accumulators for
 //    the whole sequence and the chunk loop runs the three lines above, with the
@@ -72,7 +74,7 @@ struct Rec {
     static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // K^T bf16 A frags, hi and lo: [2][NTD row tiles][2][64][8]
     static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U'  f32 tiles [NTD col tiles][4 row tiles][64][4]
                                                         //   (W' = diag(e^{G_c - G_t}) W, U' likewise)
-    static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol  f32 tiles [NTD][4][64][4]
+    static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol^T f32 tiles [NTD][4][64][4] (rows = value column)
     static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times
     static constexpr int SIZE = GM_OFF + 256;           // padded to a multiple of 256 bytes
 };
@@ -701,7 +703,10 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
             *reinterpret_cast<f16x8 *>(rec + R::Q_OFF + off) = pack_h(Xa[0][mt], Xa[1][mt]);
         }
     } else {
-        // Y = U' = (Dc T Bv) V;  Xa = Ol = (M Bv) V   (Xa's V values are consumed)
+        // Y = U' = (Dc T Bv) V;  Xa = Ol^T = V^T (M Bv)^T   (Xa's V values are consumed).
+        // Ol is formed transposed (operands swapped: the A form of V^T and the B form of
+        // (M Bv)^T are the fragments already at hand), so that the state pass, which forms
+        // O^T the same way, holds 4 consecutive columns of one output row per lane.
 #pragma unroll
         for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -715,7 +720,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) {
                     Y[ni][rt] = mfma16x3(ft, Bop[ni][ks], Y[ni][rt]);
-                    Xa[ni][rt] = mfma16x3(fm, Bop[ni][ks], Xa[ni][rt]);
+                    Xa[ni][rt] = mfma16x3(Bop[ni][ks], fm, Xa[ni][rt]);
                 }
             }
 #pragma unroll
@@ -860,8 +865,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     __syncthreads();
 
     // o rows of this lane: row 16 mt + 4 kg + qq of the chunk, column col
+    // O^T tiles: lane (kg, l16) holds columns 16 j + 4 kg .. + 3 of output row 16 mt + l16
     const int row_stride = Hv * D;
-    const int o_lane = 4 * kg * row_stride + l16;
+    const int o_lane = l16 * row_stride + 4 * kg;
 
     // Fragment groups read from LDS.  Phase 1 group p: -W and Qt fragments of row tiles
     // 2p, 2p + 1 (all k steps).  Phase 2 group p: K^T hi and lo fragments of state row
@@ -911,7 +917,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         f16x8 fr[2][GF];
         read_p1(A, 0, fr[0]);
 
-        // ---- Delta' = U' + (-W') S and O = Ol + Qt S: four independent accumulation chains
+        // ---- Delta' = U' + (-W') S and O^T = Ol^T + S^T Qt^T: four independent accumulation chains
         // per group (Delta and O of two row tiles), each one MFMA per k step
         f32x4 Dl[4], Ot[4];
 #pragma unroll
@@ -922,15 +928,15 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             if (p + 1 < NG1) read_p1(A, p + 1, fr[(p + 1) & 1]);
             else read_p2(A, 0, fr[(p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            f32x4 o0 = mfma16(F[NKS], Sh[0], Of[2 * p]);
+            f32x4 o0 = mfma16(Sh[0], F[NKS], Of[2 * p]);
             f32x4 d1 = mfma16(F[2 * NKS], Sh[0], Uf[2 * p + 1]);
-            f32x4 o1 = mfma16(F[3 * NKS], Sh[0], Of[2 * p + 1]);
+            f32x4 o1 = mfma16(Sh[0], F[3 * NKS], Of[2 * p + 1]);
 #pragma unroll
             for (int ks = 1; ks < NKS; ++ks) {
                 d0 = mfma16(F[ks], Sh[ks], d0);
-                o0 = mfma16(F[NKS + ks], Sh[ks], o0);
+                o0 = mfma16(Sh[ks], F[NKS + ks], o0);
                 d1 = mfma16(F[2 * NKS + ks], Sh[ks], d1);
-                o1 = mfma16(F[3 * NKS + ks], Sh[ks], o1);
+                o1 = mfma16(Sh[ks], F[3 * NKS + ks], o1);
             }
             Dl[2 * p] = d0; Dl[2 * p + 1] = d1;
             Ot[2 * p] = o0; Ot[2 * p + 1] = o1;
@@ -977,11 +983,8 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         const int rows = min(kChunk, L - c * kChunk);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int r = 16 * mt + 4 * kg + qq;
-                if (!LAST || r < rows) ob[o_lane + (16 * mt + qq) * row_stride] = Ot[mt][qq];
-            }
+            if (!LAST || 16 * mt + l16 < rows)
+                *reinterpret_cast<f32x4 *>(ob + o_lane + 16 * mt * row_stride) = Ot[mt];
         __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
         if constexpr (!LAST) {
 #pragma unroll
