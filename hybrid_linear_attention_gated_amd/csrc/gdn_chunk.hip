@@ -57,6 +57,7 @@
 //    accumulator tiles (kperm).
 #include <algorithm>
 #include <mutex>
+#include <numeric>
 #include <type_traits>
 
 #include "gdn_device.hpp"
@@ -122,6 +123,12 @@ __device__ __forceinline__ bool locate_chunk_wave(const int32_t *cu, int N, int 
         base += __shfl(incl, kWave - 1, kWave);
     }
     return false;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit elements;
+// out-of-range loads return 0 and out-of-range stores are dropped).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
 // ============================================================== chunk-local
@@ -190,6 +197,22 @@ struct LocalSmem {
     static_assert(64 * VLD * 4 <= SCAL - XT, "v plane fits in the T / M region");
     static constexpr int SIZE = SCAL + 6 * 64 * 4;
     static_assert(NW * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
+    // Fused prep with a 16-bit x: the next chunk's x rows (tokens -3 .. 63, the q, k and v
+    // channel groups of D each) are staged by direct-to-LDS loads while this chunk is
+    // solved.  Staged row r is XROW contiguous bytes [q | k | v]; rows 0 .. XRA - 1 sit in
+    // the plane region past the solve scratch (free from the tile phase on), the rest past
+    // SIZE.  XRA * XROW is a whole number of 1 KiB copies, so no copy straddles the two.
+    static constexpr int XROW = 3 * D * 2;
+    static constexpr int XROWS = kChunk + kConvHist;
+    static constexpr int XA = NW * SCR_WAVE;
+    static constexpr int XRQ = 1024 / std::gcd(XROW, 1024);
+    static constexpr int XRA = (4 * PLANE - XA) / XROW / XRQ * XRQ;
+    static constexpr int XB = SIZE;
+    static constexpr int XCOPIES = (3 * XROWS * 2 * D + 1023) / 1024;   // 1 KiB copies
+    static constexpr int SIZE_STAGED = XB + XCOPIES * 1024 - XRA * XROW;
+    static_assert(XA % 16 == 0 && XB % 16 == 0 && (XRA * XROW) % 1024 == 0, "staging alignment");
+    static_assert(XA + XRA * XROW <= 4 * PLANE, "staging part A fits in the planes");
+    static_assert(SIZE_STAGED <= 160 * 1024, "staging fits in LDS");
 };
 
 // One workgroup per (chunk, value head), fully parallel over chunks.  With
@@ -222,16 +245,17 @@ template <int D, bool FUSED, typename TX>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
-    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0,
+    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0, int g1, int nslots,
     const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
     int order) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
+    constexpr bool STAGE = FUSED && sizeof(TX) == 2;
     constexpr int NWH = LocalShape<D>::NWH, NW = LocalShape<D>::NW, NT = LocalShape<D>::THREADS;
     constexpr int NKS = D / 32;   // 32-wide k steps over the head dim
     constexpr int LD = SM::LD;
     constexpr int NF_K = (D / 16) * 2;
-    __shared__ __attribute__((aligned(16))) char smem[SM::SIZE];
+    __shared__ __attribute__((aligned(16))) char smem[STAGE ? SM::SIZE_STAGED : SM::SIZE];
     bf16 *Kh = reinterpret_cast<bf16 *>(smem + SM::KH);
     bf16 *Kl = reinterpret_cast<bf16 *>(smem + SM::KL);
     bf16 *Qh = reinterpret_cast<bf16 *>(smem + SM::QH);
@@ -244,19 +268,38 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256, *GRs = Gs + 320;
     enum { XT_TW = 0, XT_TU = 1, XT_MW = 2, XT_MU = 3 };   // published operand sets
 
-    // wave index in a scalar register: wave-level branches and LDS bases stay uniform
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l16 = lane & 15, kg = lane >> 4;
-    const int gc = g0 + blockIdx.x, h = blockIdx.y;   // packed chunk index, value head
+    const int h = blockIdx.y;   // value head
     const int kh = h / (Hv / Hk);
+    const int conv_dim = 2 * Hk * D + Hv * D;
+
+    // Persistent over chunks: workgroup (slot, head) takes packed chunks g0 + slot,
+    // g0 + slot + nslots, ... of its head, so one workgroup per compute unit runs the
+    // whole launch and (fused, 16-bit x) loads the next chunk's x while solving this one.
+    bool staged = false;   // this chunk's x rows are in the LDS staging area
+    // Where the chunk lives: sequence s_, its chunk c_, the sequence's token range [sb, se).
+    // Carried from one iteration to the next; searched for only when the next chunk lies
+    // in another sequence.
+    int s_ = 0, c_ = 0, sb = 0, se = 0;
+    bool have = false;
+    for (int gc = g0 + blockIdx.x; gc < g1; gc += nslots) {
+    // The thread index passes through an empty asm each iteration, so nothing derived from
+    // it is hoisted out of the loop and kept live across it (that costs registers the
+    // chunk's own work needs).
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    // wave index in a scalar register: wave-level branches and LDS bases stay uniform
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, kg = lane >> 4;
     const bool isW = wave < NWH;
     const int qw = isW ? wave : wave - NWH;   // this wave's pair of 16-wide tiles: 2qw, 2qw + 1
-
     // ---- where this chunk lives (every wave finds the same answer; no barrier)
-    int s_, c_;
-    if (!locate_chunk_wave(cu, N, Ttot, gc, s_, c_)) return;
-    const int t0 = __builtin_amdgcn_readfirstlane(seq_begin(cu, s_) + c_ * kChunk);
-    const int L = __builtin_amdgcn_readfirstlane(min(kChunk, seq_end(cu, s_, Ttot) - t0));
+    if (!have) {
+        if (!locate_chunk_wave(cu, N, Ttot, gc, s_, c_)) break;
+        sb = __builtin_amdgcn_readfirstlane(seq_begin(cu, s_));
+        se = __builtin_amdgcn_readfirstlane(seq_end(cu, s_, Ttot));
+    }
+    const int t0 = sb + c_ * kChunk;
+    const int L = min(kChunk, se - t0);
     char *rec = ws + ((size_t)h * ncmax + gc) * R::SIZE;   // head-major: a head's chunks are contiguous
 
     // ---- global loads, all issued before any is used.  Rows >= L are clamped
@@ -324,21 +367,35 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         // Rows past the chunk's last token are zeros (SiLU(0) = 0, and a zero vector stays
         // zero under the L2 norm), so padded rows of the planes are zero.
         constexpr int CB = D / 8, TGW = 64 / CB, WPG = D / 64;
-        if (wave < 3 * WPG) {
-            const int grp = wave / WPG, th = wave % WPG;
-            const int cb = lane % CB, tg = lane / CB;
-            const int ch0 = (grp == 0 ? kh * D : grp == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D) + 8 * cb;
-            const int conv_dim = 2 * Hk * D + Hv * D;
-            const int tl0 = th * TGW * 8 + 8 * tg;   // first local token of this lane
-            const bool first = c_ == 0;              // history before the sequence start
-            Raw8<TX> rows[11];
+        const bool conv_wave = wave < 3 * WPG;
+        const int grp = wave / WPG, th = wave % WPG;
+        const int cb = lane % CB, tg = lane / CB;
+        const int ch0 = (grp == 0 ? kh * D : grp == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D) + 8 * cb;
+        const int tl0 = th * TGW * 8 + 8 * tg;   // first local token of this lane
+        const bool first = c_ == 0;              // history before the sequence start
+        Raw8<TX> rows[11];
+        if (conv_wave) {
 #pragma unroll
             for (int r = 0; r < 11; ++r) {
                 const int tl = tl0 - kConvHist + r;
-                if (tl < L && (tl >= 0 || !first)) rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
-                else if (tl < 0 && cs_in) rows[r].load(cs_in + ((size_t)s_ * kConvHist + (kConvHist + tl)) * conv_dim + ch0);
-                else rows[r].zero();
+                if (tl < L && (tl >= 0 || !first)) {
+                    if (STAGE && staged) {
+                        const int sr = tl + kConvHist;   // staged row
+                        const int so = (sr < SM::XRA ? SM::XA + sr * SM::XROW : SM::XB + (sr - SM::XRA) * SM::XROW) +
+                                       grp * 2 * D + 16 * cb;
+                        rows[r].load(reinterpret_cast<const TX *>(smem + so));
+                    } else {
+                        rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
+                    }
+                } else if (tl < 0 && cs_in) {
+                    rows[r].load(cs_in + ((size_t)s_ * kConvHist + (kConvHist + tl)) * conv_dim + ch0);
+                } else {
+                    rows[r].zero();
+                }
             }
+        }
+        if constexpr (STAGE) __syncthreads();   // staging part A is read before the planes overwrite it
+        if (conv_wave) {
             float wt[4][8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -546,6 +603,47 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     }
     __syncthreads();
 
+    // ---- fused prep, 16-bit x: stage the next chunk's x rows (its tokens -3 .. 63) in LDS
+    // with direct-to-LDS buffer loads, spread over all waves.  Copy i fills staging bytes
+    // [1 KiB i, 1 KiB (i + 1)); lane l moves 16 bytes of segment (row, group) =
+    // (i * SPI + l / SEGL) / 3.  Rows before the buffer start or past its end read as 0
+    // (they are not used: history rows of a sequence's first chunk come from its conv cache,
+    // rows past its last token are masked).
+    // The next chunk of this workgroup: chunk c_ + nslots of the same sequence if it has
+    // one, else found by a search.
+    const int gn = gc + nslots;
+    int sn = s_, cn = c_ + nslots, sbn = sb, sen = se;
+    bool next_ok = false;
+    if (gn < g1) {
+        if (cn * kChunk < se - sb) {
+            next_ok = true;
+        } else if (locate_chunk_wave(cu, N, Ttot, gn, sn, cn)) {
+            next_ok = true;
+            sbn = __builtin_amdgcn_readfirstlane(seq_begin(cu, sn));
+            sen = __builtin_amdgcn_readfirstlane(seq_end(cu, sn, Ttot));
+        }
+    }
+    if constexpr (STAGE) {
+        if (next_ok) {
+            constexpr int SEGL = 2 * D / 16, SPI = 64 / SEGL;
+            const int tn = sbn + cn * kChunk;
+            const int rb = max(tn - kConvHist, 0);
+            const long bytes = (long)(Ttot - rb) * conv_dim * 2;
+            const __amdgpu_buffer_rsrc_t rx =
+                make_rsrc(x + (size_t)rb * conv_dim, (int)min(bytes, (long)0x7ffffff0));
+            for (int i = wave; i < SM::XCOPIES; i += NW) {
+                const int sg = i * SPI + lane / SEGL;
+                const int r = min(sg / 3, SM::XROWS - 1), gi = sg % 3;
+                const int chb = gi == 0 ? kh * D : gi == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D;
+                const int voff = ((tn - kConvHist + r - rb) * conv_dim + chb) * 2 + 16 * (lane % SEGL);
+                char *dst = i * 1024 < SM::XRA * SM::XROW ? smem + SM::XA + i * 1024
+                                                          : smem + SM::XB + (i * 1024 - SM::XRA * SM::XROW);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst, 16,
+                                                         voff, 0, 0, 0);
+            }
+        }
+    }
+
     // ---- 2. diagonal blocks T_cc = (I + A_cc)^-1 by forward substitution; lane (c, j)
     // computes column j of block c, then the columns are regrouped into accumulator
     // layout through this wave's scratch (lane (kg, l16) gets rows 4kg..4kg+3).
@@ -648,6 +746,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         run_chain(3 - wave);
         run_chain(4 + wave);
     }
+    if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(0);   // this wave's staging copies have landed
     __syncthreads();
 
     // ---- 4. the four products.  Row fragment (tt, ks) of a published set: lane row
@@ -733,15 +832,18 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
                 *reinterpret_cast<f32x4 *>(rec + R::O_OFF + off) = Xa[ni][rt];
             }
     }
+    __syncthreads();   // the next chunk rewrites the planes, the T / M operands and the scalars
+    if (!next_ok) break;
+    s_ = sn;
+    c_ = cn;
+    sb = sbn;
+    se = sen;
+    have = true;
+    staged = STAGE && next_ok;
+    }
 }
 
 // ============================================================== state pass
-
-// Buffer resource over `bytes` bytes at `base` (raw buffer, 32-bit elements;
-// out-of-range loads return 0 and out-of-range stores are dropped).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
-}
 
 // Copy `bytes` (a multiple of 1 KiB) at byte `src_off` of the buffer to LDS:
 // each wave instruction moves 1 KiB (lane l -> base + 16 l); completion is
@@ -1079,19 +1181,22 @@ static hipError_t pipe_resources(PipeRes **out) {
 template <int D>
 static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
     if (g1 <= g0 || a.T <= 0) return hipSuccess;
-    const dim3 grid((unsigned)(g1 - g0), a.Hv), block(LocalShape<D>::THREADS);
+    // one workgroup per compute unit (each holds most of the LDS), looping over chunks
+    const int cus = device_cus();
+    const int nslots = std::max(1, std::min(g1 - g0, (cus > 0 ? cus : 256) / a.Hv));
+    const dim3 grid((unsigned)nslots, a.Hv), block(LocalShape<D>::THREADS);
     char *ws = (char *)a.ws;
     if (!a.fp) {
         hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)nullptr,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)nullptr,
                            (const float *)nullptr, (const float *)nullptr, 0.f, a.order);
     } else if (a.fp->bf16) {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const bf16 *)a.fp->x,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const bf16 *)a.fp->x,
                            (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order);
     } else {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, (const float *)a.fp->x,
+                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)a.fp->x,
                            (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order);
     }
     return hipGetLastError();
