@@ -131,6 +131,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
+// Device-coherent record traffic for the concurrent schedule.  On this multi-die GPU
+// each die's L2 is coherent only with itself; a store or load with the device-scope
+// coherence bit (SC1) is written through / fetched past it.  Records written and read this
+// way need no L2 write-back or invalidation between producer and consumer: the producer
+// waits for its stores to complete and then raises a flag; the consumer sees the flag and
+// then reads.
+constexpr int kCohAux = 16;   // cache-policy bits: SC1
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <typename V>
+__device__ __forceinline__ void rec_store16(char *rec, int off, V v, bool coherent) {
+    static_assert(sizeof(V) == 16, "16-byte store");
+    if (coherent)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), make_rsrc(rec, 1 << 30), off, 0,
+                                               kCohAux);
+    else
+        *reinterpret_cast<V *>(rec + off) = v;
+}
+__device__ __forceinline__ f32x4 rec_load16(const char *rec, int off, bool coherent) {
+    if (coherent)
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(rec, 1 << 30), off, 0,
+                                                                               kCohAux));
+    return *reinterpret_cast<const f32x4 *>(rec + off);
+}
+
 // ============================================================== chunk-local
 
 // Index of block (c, r), c <= r, in a packed upper triangle of 4 x 4 blocks.
@@ -247,7 +272,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0, int g1, int nslots,
     const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
-    int order) {
+    int order, int *flags) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr bool STAGE = FUSED && sizeof(TX) == 2;
@@ -359,7 +384,13 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         BEG[lane] = bb * (order == 0 ? eg : __expf(Gr));
         DCs[lane] = __expf(Gc - G);
         QS[lane] = scale * eg;
-        if (lane < 4) reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
+        if (lane < 4) {
+            if (flags)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __expf(Gc)), make_rsrc(rec, 1 << 30),
+                                                      R::GM_OFF + 4 * lane, 0, kCohAux);
+            else
+                reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
+        }
     }
     if constexpr (FUSED) {
         // Waves 0 .. 3D/64 - 1 convolve: D/64 waves per group (q, k, v of this workgroup's
@@ -591,8 +622,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
                 Bop[hh][kt] = Split8{to_bf16x8(Kth[2 * kt][hh], Kth[2 * kt + 1][hh]),
                                      to_bf16x8(Ktl[2 * kt][hh], Ktl[2 * kt + 1][hh])};
                 const int off = R::K_OFF + ((m * 2 + kt) * 64 + lane) * 16;
-                *reinterpret_cast<bf16x8 *>(rec + off) = Bop[hh][kt].hi;
-                *reinterpret_cast<bf16x8 *>(rec + off + NF_K * 64 * 16) = Bop[hh][kt].lo;
+                rec_store16(rec, off, Bop[hh][kt].hi, flags != nullptr);
+                rec_store16(rec, off + NF_K * 64 * 16, Bop[hh][kt].lo, flags != nullptr);
             }
         }
     } else {
@@ -798,8 +829,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             const int off = ((mt * NKS + qw) * 64 + lane) * 16;
-            *reinterpret_cast<f16x8 *>(rec + R::W_OFF + off) = pack_h(-Y[0][mt], -Y[1][mt]);
-            *reinterpret_cast<f16x8 *>(rec + R::Q_OFF + off) = pack_h(Xa[0][mt], Xa[1][mt]);
+            rec_store16(rec, R::W_OFF + off, pack_h(-Y[0][mt], -Y[1][mt]), flags != nullptr);
+            rec_store16(rec, R::Q_OFF + off, pack_h(Xa[0][mt], Xa[1][mt]), flags != nullptr);
         }
     } else {
         // Y = U' = (Dc T Bv) V;  Xa = Ol^T = V^T (M Bv)^T   (Xa's V values are consumed).
@@ -828,11 +859,16 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
             for (int rt = 0; rt < 4; ++rt) {
                 const int nt = 2 * qw + ni;
                 const int off = ((nt * 4 + rt) * 64 + lane) * 16;
-                *reinterpret_cast<f32x4 *>(rec + R::U_OFF + off) = Y[ni][rt];
-                *reinterpret_cast<f32x4 *>(rec + R::O_OFF + off) = Xa[ni][rt];
+                rec_store16(rec, R::U_OFF + off, Y[ni][rt], flags != nullptr);
+                rec_store16(rec, R::O_OFF + off, Xa[ni][rt], flags != nullptr);
             }
     }
+    // Publishing (a state pass runs concurrently and waits for each record): the record
+    // stores are device-coherent; every wave waits until its own have completed, then one
+    // thread raises the chunk's flag.
+    if (flags) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // the next chunk rewrites the planes, the T / M operands and the scalars
+    if (flags && tid == 0) __hip_atomic_store(flags + (size_t)h * ncmax + gc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!next_ok) break;
     s_ = sn;
     c_ = cn;
@@ -850,6 +886,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 // tracked by vmcnt.  Addresses are all scalar except the constant lane offset.
 // The block order is rotated by `rot` so that workgroups copying the same
 // record at the same time touch different L2 lines.
+template <int AUX>
 __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_off, char *dst, int bytes, int lane,
                                             int rot = 0) {
     const int nblk = bytes / 1024;
@@ -858,7 +895,7 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
         int blk = i + rot;
         blk = blk >= nblk ? blk - nblk : blk;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + blk * 1024), 16,
-                                                 lane * 16, src_off + blk * 1024, 0, 0);
+                                                 lane * 16, src_off + blk * 1024, 0, AUX);
     }
 }
 
@@ -876,10 +913,16 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 // g + 1 are issued right after the first MFMA of group g, and each group runs
 // four independent MFMA chains (a dependent MFMA waits ~44 cycles, one issues
 // every 16).
-template <int D>
+// Bound on the state pass's wait for a published record (iterations of a ~128-cycle
+// sleep, about a second): a producer that never publishes ends in wrong output, not a hang.
+constexpr int kSpinMax = 1 << 24;
+
+// COH: records come from a concurrently running chunk-local kernel (wait for each chunk's
+// flag, read device-coherently); otherwise plain cached reads.
+template <int D, bool COH>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid) {
+    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const int *flags) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -921,13 +964,29 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         const int half = (wave - 2) * (ABYTES / 2);
         auto stage = [&](int c, char *dst) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(c), R::SIZE);
-            copy_to_lds(r, half, dst + half, ABYTES / 2, lane);
+            copy_to_lds<COH ? kCohAux : 0>(r, half, dst + half, ABYTES / 2, lane);
         };
+        // With `flags`, the records are written by a chunk-local kernel running at the same
+        // time: wait (bounded) until chunk c's record is published; every record load is then
+        // device-coherent.  The copy waves confirm a chunk before the barrier after which the
+        // compute waves prefetch its U' and Ol^T strips, i.e. two chunks ahead of the compute.
+        auto ready = [&](int c) {
+            const int *f = flags + (size_t)h * ncmax + gbase + c;
+            for (int it = 0; it < kSpinMax; ++it) {
+                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+                __builtin_amdgcn_s_sleep(2);
+            }
+        };
+        if constexpr (COH) {
+            if (c_lo < c_hi) ready(c_lo);
+            if (c_lo + 1 < c_hi) ready(c_lo + 1);
+        }
         if (c_lo < c_hi) stage(c_lo, abuf[c_lo & 1]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = c_lo; c < c_hi; ++c) {
             if (c + 1 < c_hi) stage(c + 1, abuf[(c + 1) & 1]);
+            if (COH && c + 2 < c_hi) ready(c + 2);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -952,19 +1011,26 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, float &g_) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            U_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::U_OFF + strip_off + mt * 1024);
-            O_[mt] = *reinterpret_cast<const f32x4 *>(rec + R::O_OFF + strip_off + mt * 1024);
+            U_[mt] = rec_load16(rec, R::U_OFF + strip_off + mt * 1024, COH);
+            O_[mt] = rec_load16(rec, R::O_OFF + strip_off + mt * 1024, COH);
         }
         // lane-varying address: a vector load (no scalar load shares lgkmcnt with LDS reads)
-        g_ = *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
+        g_ = COH ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rec, 1 << 30),
+                                                                                   R::GM_OFF + (lane & 3) * 4, 0,
+                                                                                   kCohAux))
+                   : *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
     };
-    if (c_lo < c_hi) load_strip(rec_of(c_lo), Uf, Of, gm);
+    if (!COH && c_lo < c_hi) load_strip(rec_of(c_lo), Uf, Of, gm);
     // Retire the initial state and strip loads here, once.  Left pending into the loop,
     // the compiler's wait analysis merges them into the loop header and then waits for
     // every outstanding access (the previous chunk's o stores and this chunk's prefetch)
     // before the first MFMA of each chunk.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (COH && c_lo < c_hi) {   // first strips only once the copy waves have confirmed them
+        load_strip(rec_of(c_lo), Uf, Of, gm);
+        __builtin_amdgcn_s_waitcnt(0);
+    }
 
     // o rows of this lane: row 16 mt + 4 kg + qq of the chunk, column col
     // O^T tiles: lane (kg, l16) holds columns 16 j + 4 kg .. + 3 of output row 16 mt + l16
@@ -1110,12 +1176,19 @@ bool chunked_supported(int dk, int dv) { return dk == dv && (dk == 64 || dk == 1
 
 static size_t max_chunks(int T, int N) { return (size_t)(T / kChunk) + (size_t)N; }
 
-// Workspace: the per-(chunk, value head) records, then one state per (sequence, value
-// head) that carries a sequence from one pipeline segment to the next.
+// Workspace: the per-(chunk, value head) records, one state per (sequence, value head)
+// that carries a sequence from one pipeline segment to the next, and one ready flag per
+// (value head, chunk) for the concurrent schedule.
+static size_t mid_offset(size_t nc, int Hv, int dk) {
+    return nc * (size_t)Hv * (dk == 64 ? (size_t)Rec<64>::SIZE : (size_t)Rec<128>::SIZE);
+}
+static size_t flags_offset(size_t nc, int N, int Hv, int dk) {
+    return mid_offset(nc, Hv, dk) + (size_t)N * Hv * dk * dk * sizeof(float);
+}
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     (void)dv;
-    const size_t rec = dk == 64 ? (size_t)Rec<64>::SIZE : (size_t)Rec<128>::SIZE;
-    return max_chunks(T, N) * (size_t)Hv * rec + (size_t)N * Hv * dk * dk * sizeof(float);
+    const size_t nc = max_chunks(T, N);
+    return flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(int);
 }
 
 // ---- segment pipeline of gdn_chunk_prefill: the packed chunk range is cut into
@@ -1179,25 +1252,27 @@ static hipError_t pipe_resources(PipeRes **out) {
 }
 
 template <int D>
-static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
+static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1, int cu_budget = 0,
+                               int *flags = nullptr) {
     if (g1 <= g0 || a.T <= 0) return hipSuccess;
-    // one workgroup per compute unit (each holds most of the LDS), looping over chunks
-    const int cus = device_cus();
+    // one workgroup per compute unit (each holds most of the LDS), looping over chunks;
+    // cu_budget > 0 leaves the other compute units to a concurrent state pass
+    const int cus = cu_budget > 0 ? cu_budget : device_cus();
     const int nslots = std::max(1, std::min(g1 - g0, (cus > 0 ? cus : 256) / a.Hv));
     const dim3 grid((unsigned)nslots, a.Hv), block(LocalShape<D>::THREADS);
     char *ws = (char *)a.ws;
     if (!a.fp) {
         hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)nullptr,
-                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order);
+                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order, flags);
     } else if (a.fp->bf16) {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const bf16 *)a.fp->x,
-                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order);
+                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order, flags);
     } else {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)a.fp->x,
-                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order);
+                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order, flags);
     }
     return hipGetLastError();
 }
@@ -1206,14 +1281,35 @@ template <int D>
 static int state_blocks(int units) { return 8 * (D / 32) * ((units + 7) / 8); }
 
 template <int D>
-static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
+static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1,
+                               const int *flags = nullptr) {
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
     const int blocks = state_blocks<D>(units);
-    float *mid = reinterpret_cast<float *>((char *)a.ws + (size_t)nc * a.Hv * Rec<D>::SIZE);
-    hipLaunchKernelGGL((state_pass_kernel<D>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T, a.Hv,
-                       units, a.s0, a.sf, a.o, nc, g0, g1, mid);
+    float *mid = reinterpret_cast<float *>((char *)a.ws + mid_offset(nc, a.Hv, D));
+    if (flags)
+        hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags);
+    else
+        hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags);
     return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_flags_kernel(int *f, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) f[i] = 0;
+}
+
+// Concurrent schedule: the state pass occupies at most a quarter of the compute units and the
+// chunk-local kernel has enough chunks to fill the rest for more than one round.  Then the two
+// run at the same time on two streams: the chunk-local kernel (on the remaining compute units)
+// publishes each record with a flag and the state pass waits for the flags.  The chunk-local
+// kernel never waits, so it always finishes; it is enqueued first, so even if the two streams
+// share a hardware queue the state pass starts only after it.  (Measured on MI355X at 4096
+// tokens x 16 heads: the sequential launches take the sum of the two kernels' times.)
+static bool concurrent_ok(int nc, int Hv, int sblocks, int cus) {
+    return cus > 0 && 4 * sblocks <= cus && (long long)nc * Hv >= 2LL * (cus - sblocks);
 }
 
 // Fused prefill: conv_state_out after everything that reads conv_state_in (it may alias it).
@@ -1238,7 +1334,24 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
         if (phases & 2) return launch_state<D>(a, st, nc, 0, nc);
         return hipSuccess;
     }
-    const int G = pipeline_segments(nc, state_blocks<D>(a.N * a.Hv));
+    const int sblocks = state_blocks<D>(a.N * a.Hv);
+    const int cus = device_cus();
+    if (concurrent_ok(nc, a.Hv, sblocks, cus)) {
+        PipeRes *pr = nullptr;
+        if ((e = pipe_resources(&pr)) != hipSuccess) return e;
+        int *flags = reinterpret_cast<int *>((char *)a.ws + flags_offset(nc, a.N, a.Hv, D));
+        const int nf = nc * a.Hv;
+        hipLaunchKernelGGL(zero_flags_kernel, dim3((nf + 255) / 256), dim3(256), 0, st, flags, nf);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipEventRecord(pr->ev[0], st)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(pr->side, pr->ev[0], 0)) != hipSuccess) return e;
+        if ((e = launch_local<D>(a, st, nc, 0, nc, cus - sblocks, flags)) != hipSuccess) return e;
+        if ((e = launch_state<D>(a, pr->side, nc, 0, nc, flags)) != hipSuccess) return e;
+        if ((e = hipEventRecord(pr->ev[kMaxSegments], pr->side)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0)) != hipSuccess) return e;
+        return launch_fused_cs_out(a, st);
+    }
+    const int G = pipeline_segments(nc, sblocks);
     if (G == 1) {
         e = launch_local<D>(a, st, nc, 0, nc);
         if (e != hipSuccess) return e;

@@ -542,3 +542,34 @@ def test_decode_order1(gdn, gated):
         _differs("o", f32np(o), o0, TOL_F32)
     assert_parity("state", f32np(st), s1, TOL_F32)
     np.testing.assert_array_equal(f32np(cs), cs1)
+
+
+# ------------------------------------------------------------------ concurrent schedule
+
+def test_concurrent_schedule_equals_split_phases(gdn):
+    """One sequence of 8000 tokens x 4 value heads takes the concurrent schedule (the
+    state pass waits for records the chunk-local kernel publishes while it runs).  Three
+    different batches in a row on one workspace, each bit-identical to the split-phase
+    calls and the first against the oracle, so a record read before it was written (or a
+    stale one from the previous batch) shows."""
+    announce("concurrent schedule: T=8000, Hk=2, Hv=4, three batches on one workspace")
+    T, Hk, Hv, d = 8000, 2, 4, 128
+    ws = torch.empty(gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    for it in range(3):
+        wl = inputs.prefill_workload("conc", 980 + it, [T], Hk, Hv, d, random_states=True)
+        x, w, g, b, s0, cs = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state, wl.conv_state))
+        o1, f1 = gdn.prefill(x, w, g, b, Hk, Hv, d, d, conv_state_in=cs, initial_state=s0, workspace=ws)
+        ws2 = torch.empty_like(ws)
+        o2, f2 = torch.empty_like(o1), torch.empty_like(f1)
+        gdn.prefill_local(x, w, g, b, ws2, Hk, Hv, d, d, conv_state_in=cs)
+        gdn.chunk_prefill_state(ws2, o2, T, Hk, Hv, d, d, initial_state=s0, final_state=f2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"batch {it}: o differs from the split phases"
+        assert torch.equal(f1, f2), f"batch {it}: final state differs from the split phases"
+        if it == 0:
+            cu = wl.cu_seqlens.numpy()
+            q_r, k_r, v_r, _ = oracle.prep(f32np(wl.x), f32np(wl.conv_w), cu, Hk, Hv, d, d,
+                                           cs_in=f32np(wl.conv_state))
+            o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu, s0=f32np(wl.state))
+            assert_parity("o", f32np(o1), o_ref, TOL_BF16)
+            assert_parity("final_state", f32np(f1), f_ref, TOL_BF16)
