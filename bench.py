@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-only", action="store_true",
                     help="time only the split-phase region (one launch per kernel per step), for profiler runs")
+    ap.add_argument("--metric-only", action="store_true",
+                    help="time only the metric's region (gdn_prefill + decode step) and print its two times, "
+                         "for kernel-trace runs of the concurrent prefill schedule")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, stream 512 MiB through one elementwise kernel (counter calibration)")
     args = ap.parse_args()
@@ -245,6 +248,10 @@ def main():
     if not args.split_only:
         evs, wall = timed(step, 3)
         prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)
+        if args.metric_only:
+            print(json.dumps({"prefill_ms": prefill_ms, "decode_ms": decode_ms, "entry_point": "gdn_prefill",
+                              "steps": args.steps, "warmup": args.warmup}))
+            return
         evs_two, _ = timed(step_two, 3)
         two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
         two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,

@@ -917,12 +917,53 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 // sleep, about a second): a producer that never publishes ends in wrong output, not a hang.
 constexpr int kSpinMax = 1 << 24;
 
+// Conv-cache write of the fused prefill, done by the state pass in the concurrent schedule:
+// the three rows before the end of sequence s (x rows, or input-cache rows where the
+// sequence is shorter than three tokens, or zeros without an input cache), for the
+// channels [ch0, ch0 + n).  One lane per channel reads its three values before writing
+// any, so the output cache may alias the input cache.  E is the element's bit pattern.
+struct ConvOut {
+    const void *x = nullptr;
+    const void *cs_in = nullptr;
+    void *cs_out = nullptr;   // nullptr: no conv cache to write
+    int esz = 0;              // element bytes (2 or 4)
+    int conv_dim = 0, Hk = 0, G = 1, dk = 0;
+};
+
+template <typename E>
+__device__ __forceinline__ void conv_rows_copy(const ConvOut &cv, int s, int t0, int L, int ch0, int n, int tid,
+                                               int nthreads) {
+    const E *x = static_cast<const E *>(cv.x);
+    const E *ci = static_cast<const E *>(cv.cs_in);
+    E *co = static_cast<E *>(cv.cs_out);
+    for (int c = ch0 + tid; c < ch0 + n; c += nthreads) {
+        E v[kConvHist];
+#pragma unroll
+        for (int j = 0; j < kConvHist; ++j) {
+            const int pos = L - kConvHist + j;
+            v[j] = pos >= 0 ? x[(size_t)(t0 + pos) * cv.conv_dim + c]
+                 : ci     ? ci[((size_t)s * kConvHist + (kConvHist + pos)) * cv.conv_dim + c]
+                          : E(0);
+        }
+#pragma unroll
+        for (int j = 0; j < kConvHist; ++j) co[((size_t)s * kConvHist + j) * cv.conv_dim + c] = v[j];
+    }
+}
+
+__device__ __forceinline__ void conv_rows(const ConvOut &cv, int s, int t0, int L, int ch0, int n, int tid,
+                                          int nthreads) {
+    if (cv.esz == 2) conv_rows_copy<uint16_t>(cv, s, t0, L, ch0, n, tid, nthreads);
+    else conv_rows_copy<uint32_t>(cv, s, t0, L, ch0, n, tid, nthreads);
+}
+
 // COH: records come from a concurrently running chunk-local kernel (wait for each chunk's
-// flag, read device-coherently); otherwise plain cached reads.
+// flag, read device-coherently; the conv cache of the fused prefill is written here, see
+// ConvOut); otherwise plain cached reads.
 template <int D, bool COH>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const int *flags) {
+    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const int *flags,
+    ConvOut cv) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -989,6 +1030,30 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             if (COH && c + 2 < c_hi) ready(c + 2);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+        }
+        if constexpr (COH) {
+            // Conv cache of sequence s (the concurrent schedule covers whole sequences).  Only
+            // a sequence's first chunk reads the input cache, and every chunk of head h has
+            // been confirmed above: the v channels of head h are free to overwrite.  The q and
+            // k channels of key head h / G are read by the first chunks of all G value heads of
+            // the group; the group's first head writes them once the others' are published.
+            if (cv.cs_out && pair == 0) {
+                const int ct = lane + 64 * (wave - 2);
+                conv_rows(cv, s, t0, L, 2 * cv.Hk * cv.dk + h * D, D, ct, 128);
+                if (h % cv.G == 0) {
+                    if (nc > 0 && cv.cs_in == cv.cs_out)
+                        for (int hh = h + 1; hh < h + cv.G; ++hh)
+                            for (int it = 0; it < kSpinMax; ++it) {
+                                if (__hip_atomic_load(flags + (size_t)hh * ncmax + gbase, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) != 0)
+                                    break;
+                                __builtin_amdgcn_s_sleep(2);
+                            }
+                    const int kh = h / cv.G;
+                    conv_rows(cv, s, t0, L, kh * cv.dk, cv.dk, ct, 128);
+                    conv_rows(cv, s, t0, L, (cv.Hk + kh) * cv.dk, cv.dk, ct, 128);
+                }
+            }
         }
         return;
     }
@@ -1226,6 +1291,11 @@ static int pipeline_segments(int nc, int state_blocks) {
 struct PipeRes {
     hipStream_t side = nullptr;
     hipEvent_t ev[kMaxSegments + 1] = {};
+    // end of the last concurrent-schedule chunk-local kernel and the caller stream of its call
+    hipEvent_t local_done = nullptr;
+    hipStream_t last_stream = nullptr;
+    bool has_last = false;
+    std::mutex mu;   // one concurrent-schedule launch sequence at a time
     bool ready = false;
 };
 static std::mutex g_pipe_mu;
@@ -1245,6 +1315,8 @@ static hipError_t pipe_resources(PipeRes **out) {
             e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
             if (e != hipSuccess) return e;
         }
+        e = hipEventCreateWithFlags(&r.local_done, hipEventDisableTiming);
+        if (e != hipSuccess) return e;
         r.ready = true;
     }
     *out = &r;
@@ -1282,17 +1354,17 @@ static int state_blocks(int units) { return 8 * (D / 32) * ((units + 7) / 8); }
 
 template <int D>
 static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1,
-                               const int *flags = nullptr) {
+                               const int *flags = nullptr, const ConvOut &cv = ConvOut{}) {
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
     const int blocks = state_blocks<D>(units);
     float *mid = reinterpret_cast<float *>((char *)a.ws + mid_offset(nc, a.Hv, D));
     if (flags)
         hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags);
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, cv);
     else
         hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags);
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, ConvOut{});
     return hipGetLastError();
 }
 
@@ -1306,8 +1378,20 @@ __global__ __launch_bounds__(256) void zero_flags_kernel(int *f, int n) {
 // run at the same time on two streams: the chunk-local kernel (on the remaining compute units)
 // publishes each record with a flag and the state pass waits for the flags.  The chunk-local
 // kernel never waits, so it always finishes; it is enqueued first, so even if the two streams
-// share a hardware queue the state pass starts only after it.  (Measured on MI355X at 4096
-// tokens x 16 heads: the sequential launches take the sum of the two kernels' times.)
+// share a hardware queue the state pass starts only after it.
+//   The state pass ends last, so it runs on the caller's stream and the chunk-local kernel on
+// the library's second stream, with nothing joined back: the chunk-local kernel raises a flag
+// only after all of that chunk's loads and stores have completed and does nothing after its
+// last flag, and the state pass ends only after it has seen every flag, so once the state pass
+// has ended the chunk-local kernel no longer touches memory.  The conv cache is written by the
+// state pass for the same reason.  (Measured on MI355X at 4096 tokens x 16 heads: the
+// sequential launches take the sum of the two kernels' times; an event recorded on or waited
+// for by the caller's stream after the state pass delays the caller's next kernel by 4 to 6 us.)
+//   A waiting state pass holds its compute units, so when a call comes from another caller
+// stream than the previous concurrent-schedule call, its state pass first waits for the
+// previous call's chunk-local kernel to end: then at most one state pass waits for records at
+// any time, and the chunk-local kernel it waits for is the next on the second stream and finds
+// the compute units that no waiting state pass holds.
 static bool concurrent_ok(int nc, int Hv, int sblocks, int cus) {
     return cus > 0 && 4 * sblocks <= cus && (long long)nc * Hv >= 2LL * (cus - sblocks);
 }
@@ -1339,17 +1423,32 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     if (concurrent_ok(nc, a.Hv, sblocks, cus)) {
         PipeRes *pr = nullptr;
         if ((e = pipe_resources(&pr)) != hipSuccess) return e;
+        std::lock_guard<std::mutex> lock(pr->mu);
         int *flags = reinterpret_cast<int *>((char *)a.ws + flags_offset(nc, a.N, a.Hv, D));
         const int nf = nc * a.Hv;
+        ConvOut cv;
+        if (a.fp && a.fp->cs_out) {
+            cv.x = a.fp->x;
+            cv.cs_in = a.fp->cs_in;
+            cv.cs_out = a.fp->cs_out;
+            cv.esz = a.fp->bf16 ? 2 : 4;
+            cv.conv_dim = 2 * a.Hk * a.dk + a.Hv * a.dv;
+            cv.Hk = a.Hk;
+            cv.G = a.Hv / a.Hk;
+            cv.dk = a.dk;
+        }
         hipLaunchKernelGGL(zero_flags_kernel, dim3((nf + 255) / 256), dim3(256), 0, st, flags, nf);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(pr->ev[0], st)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(pr->side, pr->ev[0], 0)) != hipSuccess) return e;
-        if ((e = launch_local<D>(a, st, nc, 0, nc, cus - sblocks, flags)) != hipSuccess) return e;
-        if ((e = launch_state<D>(a, pr->side, nc, 0, nc, flags)) != hipSuccess) return e;
-        if ((e = hipEventRecord(pr->ev[kMaxSegments], pr->side)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0)) != hipSuccess) return e;
-        return launch_fused_cs_out(a, st);
+        // the previous call's chunk-local kernel, before local_done is recorded again
+        if (pr->has_last && pr->last_stream != st && (e = hipStreamWaitEvent(st, pr->local_done, 0)) != hipSuccess)
+            return e;
+        if ((e = launch_local<D>(a, pr->side, nc, 0, nc, cus - sblocks, flags)) != hipSuccess) return e;
+        if ((e = hipEventRecord(pr->local_done, pr->side)) != hipSuccess) return e;
+        pr->last_stream = st;
+        pr->has_last = true;
+        return launch_state<D>(a, st, nc, 0, nc, flags, cv);
     }
     const int G = pipeline_segments(nc, sblocks);
     if (G == 1) {
@@ -1362,6 +1461,7 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     PipeRes *pr = nullptr;
     e = pipe_resources(&pr);
     if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(pr->mu);
     for (int k = 0; k < G; ++k) {
         const int g0 = (int)((long long)k * nc / G), g1 = (int)((long long)(k + 1) * nc / G);
         if ((e = launch_local<D>(a, st, nc, g0, g1)) != hipSuccess) return e;

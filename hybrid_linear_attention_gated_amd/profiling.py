@@ -9,6 +9,12 @@
       scaled by what it reads for the plain streaming copy of known size that
       the calibration launches, and the lines end with the SHA-256 of the kernel
       sources, so a reader can tell when the figures went stale.
+  python -m hybrid_linear_attention_gated_amd.profiling timeline DIR [FIRST [SKIP]]
+      kernel start / end offsets inside one step, averaged over the steps of a
+      `rocprofv3 --kernel-trace` run: a step begins at each launch of the kernel
+      FIRST (short name, default zero_flags: the first launch of the concurrent
+      prefill schedule) and the first SKIP steps (warm-up) are dropped.  Shows how
+      kernels on the library's two streams overlap.
 
 Only text is produced; nothing here touches the GPU.
 """
@@ -34,6 +40,7 @@ KERNELS = [
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
     ("gated_rmsnorm_kernel", "gated_rmsnorm"),
+    ("zero_flags_kernel", "zero_flags"),
 ]
 # bench.py --copy-calibration streams a buffer through torch.neg (one elementwise
 # kernel that reads and writes COPY_BYTES); host-to-device uploads use blit
@@ -118,6 +125,39 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
+def timeline(directory: str, first: str = "zero_flags", skip: int = 0) -> dict:
+    """Mean (start, end) offsets in us of each kernel of a step from the step's first start.
+
+    Kernels are keyed by short name and occurrence inside the step ("decode", "decode#2").
+    Returns {"steps": n, "kernels": [(key, start, end), ...] in order of mean start,
+    "span": mean first-start-to-last-end}."""
+    rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    steps, cur = [], None
+    for r in rows:
+        name = short_name(r["Kernel_Name"])
+        if name == first:
+            cur = []
+            steps.append(cur)
+        if cur is not None:
+            cur.append((name, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    steps = steps[skip:]
+    if not steps:
+        raise RuntimeError(f"no step starting with {first} under {directory}")
+    acc, spans = defaultdict(list), []
+    for st in steps:
+        t0 = st[0][1]
+        seen = defaultdict(int)
+        for name, a, b in st:
+            seen[name] += 1
+            key = name if seen[name] == 1 else f"{name}#{seen[name]}"
+            acc[key].append(((a - t0) / 1e3, (b - t0) / 1e3))
+        spans.append((max(b for _, _, b in st) - t0) / 1e3)
+    kern = [(k, sum(x for x, _ in v) / len(v), sum(y for _, y in v) / len(v)) for k, v in acc.items()
+            if len(v) == len(steps)]
+    kern.sort(key=lambda t: t[1])
+    return {"steps": len(steps), "kernels": kern, "span": sum(spans) / len(spans)}
+
+
 def main(argv):
     if len(argv) >= 2 and argv[0] == "stats":
         st = kernel_stats(argv[1])
@@ -134,6 +174,14 @@ def main(argv):
             print(f"{k}.write_bytes = {v['write_bytes']:.0f}")
             print(f"{k}.traffic_bytes = {v['traffic_bytes']:.0f}")
         print(f"source_sha256 = {source_sha256()}")
+        return 0
+    if len(argv) >= 2 and argv[0] == "timeline":
+        tl = timeline(argv[1], argv[2] if len(argv) > 2 else "zero_flags", int(argv[3]) if len(argv) > 3 else 0)
+        print(f"{tl['steps']} steps; offsets from the start of each step's first kernel, us (mean)")
+        print(f"{'kernel':20s} {'start':>8s} {'end':>8s} {'dur':>8s}")
+        for k, a, b in tl["kernels"]:
+            print(f"{k:20s} {a:8.1f} {b:8.1f} {b - a:8.1f}")
+        print(f"{'step span':20s} {'':8s} {tl['span']:8.1f}")
         return 0
     print(__doc__, file=sys.stderr)
     return 2

@@ -573,3 +573,70 @@ def test_concurrent_schedule_equals_split_phases(gdn):
             o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu, s0=f32np(wl.state))
             assert_parity("o", f32np(o1), o_ref, TOL_BF16)
             assert_parity("final_state", f32np(f1), f_ref, TOL_BF16)
+
+
+@pytest.mark.parametrize("alias,dtype", [(False, "bf16"), (True, "bf16"), (True, "f32")])
+def test_concurrent_schedule_conv_cache(gdn, alias, dtype):
+    """Concurrent schedule with a conv cache to write (the state pass writes it): 4
+    sequences of 2, 0, 7998 and 1 tokens, 2 key / 4 value heads (16 state units, 129
+    chunks x 4 heads: the state pass holds a quarter of the compute units), the output
+    cache separate from or aliasing the input cache.  o and the final state bit-identical
+    to the split-phase calls; the cache equal to the oracle's bit for bit (the short and
+    empty sequences take rows from the input cache).  x, conv_w and the caches in bf16
+    or fp32 (the same values)."""
+    announce(f"concurrent schedule conv cache: lengths [2, 0, 7998, 1], Hk=2, Hv=4, alias={alias} {dtype}")
+    Hk, Hv, d = 2, 4, 128
+    wl = inputs.prefill_workload("conc_cache", 1010 + int(alias), [2, 0, 7998, 1], Hk, Hv, d, random_states=True)
+    T, cu = wl.T, _cuda(wl.cu_seqlens)
+    x, w, g, b, s0 = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state))
+    cs_in = _cuda(wl.conv_state)
+    if dtype == "f32":
+        x, w, cs_in = x.float(), w.float(), cs_in.float()
+    cs_out = cs_in if alias else torch.empty_like(cs_in)
+    ws = torch.empty(gdn.workspace_size(T, 4, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty_like(ws)
+    o2 = torch.empty((T, Hv, d), dtype=torch.float32, device=DEV)
+    f2 = torch.empty_like(s0)
+    # split phases first (they read the input cache before the concurrent call may overwrite it)
+    gdn.prefill_local(x, w, g, b, ws2, Hk, Hv, d, d, cu_seqlens=cu, conv_state_in=cs_in)
+    gdn.chunk_prefill_state(ws2, o2, T, Hk, Hv, d, d, cu_seqlens=cu, initial_state=s0, final_state=f2)
+    o1, f1 = gdn.prefill(x, w, g, b, Hk, Hv, d, d, cu_seqlens=cu, conv_state_in=cs_in, conv_state_out=cs_out,
+                         initial_state=s0, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "o differs from the split phases"
+    assert torch.equal(f1, f2), "final state differs from the split phases"
+    _, _, _, cs_ref = oracle.prep(f32np(wl.x), f32np(wl.conv_w), wl.cu_seqlens.numpy(), Hk, Hv, d, d,
+                                  cs_in=f32np(wl.conv_state))
+    np.testing.assert_array_equal(f32np(cs_out), cs_ref)
+
+
+@pytest.mark.gpu
+def test_concurrent_schedule_from_several_streams(gdn):
+    """Four caller streams each start a concurrent-schedule prefill (own workspace, inputs
+    and outputs) before any of them has finished; every result is bit-identical to the
+    split-phase calls on the default stream.  Covers the ordering of state passes across
+    caller streams and the shared second stream of the library."""
+    announce("concurrent schedule: T=8000, Hk=2, Hv=4, four caller streams")
+    T, Hk, Hv, d, n = 8000, 2, 4, 128, 4
+    wsz = gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma")
+    cases = []
+    for j in range(n):
+        wl = inputs.prefill_workload("conc_streams", 990 + j, [T], Hk, Hv, d, random_states=True)
+        x, w, g, b, s0, cs = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state, wl.conv_state))
+        ws = torch.empty(wsz, dtype=torch.uint8, device=DEV)
+        o_ref = torch.empty((T, Hv, d), dtype=torch.float32, device=DEV)
+        f_ref = torch.empty((1, Hv, d, d), dtype=torch.float32, device=DEV)
+        gdn.prefill_local(x, w, g, b, ws, Hk, Hv, d, d, conv_state_in=cs)
+        gdn.chunk_prefill_state(ws, o_ref, T, Hk, Hv, d, d, initial_state=s0, final_state=f_ref)
+        cases.append(dict(x=x, w=w, g=g, b=b, s0=s0, cs=cs, ws=torch.empty(wsz, dtype=torch.uint8, device=DEV),
+                          o=torch.empty_like(o_ref), f=torch.empty_like(f_ref), o_ref=o_ref, f_ref=f_ref))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=DEV) for _ in range(n)]
+    for s, c in zip(streams, cases):
+        with torch.cuda.stream(s):
+            gdn.prefill(c["x"], c["w"], c["g"], c["b"], Hk, Hv, d, d, conv_state_in=c["cs"], initial_state=c["s0"],
+                        o=c["o"], final_state=c["f"], workspace=c["ws"])
+    torch.cuda.synchronize()
+    for j, c in enumerate(cases):
+        assert torch.equal(c["o"], c["o_ref"]), f"stream {j}: o differs from the split phases"
+        assert torch.equal(c["f"], c["f_ref"]), f"stream {j}: final state differs from the split phases"

@@ -1,0 +1,89 @@
+"""Host-side summaries of rocprofv3 output (hybrid_linear_attention_gated_amd.profiling),
+checked on small synthetic CSV files with known answers."""
+import csv
+import os
+
+import pytest
+
+from hybrid_linear_attention_gated_amd import profiling
+
+LOCAL = "void gdn::chunk_local_kernel<128, true, __hip_bfloat16>(float const*, ...)"
+STATE = "void gdn::state_pass_kernel<128, true>(char const*, ...)"
+ZERO = "gdn::zero_flags_kernel(int*, int)"
+DECODE = "void gdn::decode_kernel<float, 128, 128, false>(...)"
+COPY = "void at::native::elementwise_kernel<128, 4, ...>(int, ...)"
+
+
+def _write(path, fields, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerows(rows)
+
+
+def _trace(tmp_path, launches):
+    rows = [{"Kernel_Name": n, "Start_Timestamp": a, "End_Timestamp": b} for n, a, b in launches]
+    _write(str(tmp_path / "t" / "run_kernel_trace.csv"), ["Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    return str(tmp_path / "t")
+
+
+def test_short_names():
+    assert profiling.short_name(LOCAL) == "chunk_local_fused"
+    assert profiling.short_name(LOCAL.replace("true", "false")) == "chunk_local"
+    assert profiling.short_name(STATE) == "state_pass"
+    assert profiling.short_name(ZERO) == "zero_flags"
+    assert profiling.short_name(DECODE) == "decode"
+    assert profiling.short_name(DECODE.replace("false>", "true>")) == "decode_gated"
+    assert profiling.short_name(COPY) == "copy"
+
+
+def test_kernel_stats(tmp_path):
+    d = _trace(tmp_path, [(STATE, 0, 10_000), (STATE, 20_000, 50_000), (DECODE, 60_000, 61_000)])
+    st = profiling.kernel_stats(d)
+    assert st["state_pass"] == {"calls": 2, "avg_us": 20.0, "min_us": 10.0, "max_us": 30.0}
+    assert st["decode"]["calls"] == 1 and st["decode"]["avg_us"] == 1.0
+
+
+def test_timeline_offsets_and_skip(tmp_path):
+    # two steps: zero_flags, then chunk-local and state pass overlapping, then decode (twice in
+    # the second step's position to check occurrence keys); the first step is dropped as warm-up
+    launches = []
+    for base, extra in ((0, 999_000), (1_000_000, 0), (2_000_000, 2_000)):
+        launches += [(ZERO, base, base + 4_000), (LOCAL, base + 10_000, base + 110_000 + extra),
+                     (STATE, base + 15_000, base + 130_000), (DECODE, base + 131_000, base + 231_000),
+                     (DECODE, base + 232_000, base + 330_000)]
+    tl = profiling.timeline(_trace(tmp_path, launches), "zero_flags", 1)
+    assert tl["steps"] == 2
+    got = {k: (a, b) for k, a, b in tl["kernels"]}
+    assert [k for k, _, _ in tl["kernels"]] == ["zero_flags", "chunk_local_fused", "state_pass", "decode",
+                                                "decode#2"]
+    assert got["chunk_local_fused"] == pytest.approx((10.0, 111.0))   # ends at 110 and 112 us
+    assert got["state_pass"] == pytest.approx((15.0, 130.0))
+    assert got["decode#2"] == pytest.approx((232.0, 330.0))
+    assert tl["span"] == pytest.approx(330.0)
+    with pytest.raises(RuntimeError):
+        profiling.timeline(_trace(tmp_path, launches), "zero_flags", 3)
+
+
+def test_traffic_scaled_by_copy(tmp_path):
+    kib = profiling.COPY_BYTES / 1024.0
+
+    def counters(sub, counter, copy_kib, state_kib):
+        rows = [{"Kernel_Name": COPY, "Counter_Name": counter, "Counter_Value": copy_kib},
+                {"Kernel_Name": STATE, "Counter_Name": counter, "Counter_Value": state_kib},
+                {"Kernel_Name": STATE, "Counter_Name": counter, "Counter_Value": 3 * state_kib}]
+        _write(str(tmp_path / sub / "run_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"],
+               rows)
+        return str(tmp_path / sub)
+
+    # the counters read half (fetch) and twice (write) the copy's true bytes
+    f = counters("f", "FETCH_SIZE", kib / 2, 100.0)
+    w = counters("w", "WRITE_SIZE", kib * 2, 100.0)
+    t = profiling.traffic(f, w)
+    assert t["fetch_factor"] == pytest.approx(2.0) and t["write_factor"] == pytest.approx(0.5)
+    k = t["kernels"]["state_pass"]
+    assert k["dispatches"] == 2
+    assert k["fetch_bytes"] == pytest.approx(200.0 * 1024 * 2.0)
+    assert k["write_bytes"] == pytest.approx(200.0 * 1024 * 0.5)
+    assert "copy" not in t["kernels"]
