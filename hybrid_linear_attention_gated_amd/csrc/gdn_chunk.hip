@@ -1026,8 +1026,19 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = c_lo; c < c_hi; ++c) {
+            // The flag of chunk c + 2 is loaded before this step's copies are issued and tested
+            // after them: its round trip then overlaps the copies instead of following them
+            // (the load is unconditional, reading chunk c's flag, known to be set, when there is
+            // no chunk c + 2, and the empty asm keeps the test after the copies).
+            int published = 1;
+            if constexpr (COH)
+                published = __hip_atomic_load(flags + (size_t)h * ncmax + gbase + (c + 2 < c_hi ? c + 2 : c),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (c + 1 < c_hi) stage(c + 1, abuf[(c + 1) & 1]);
-            if (COH && c + 2 < c_hi) ready(c + 2);
+            if constexpr (COH) {
+                asm volatile("" : "+v"(published));
+                if (c + 2 < c_hi && published == 0) ready(c + 2);
+            }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
