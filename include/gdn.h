@@ -22,11 +22,11 @@
  *    work is enqueued asynchronously on it; buffers must stay valid until the
  *    stream work completes.  gdn_chunk_prefill with GDN_MATH_MFMA and gdn_prefill
  *    may run part of their work on a second stream of the library (created once per device, default
- *    priority, kept with a few events for the life of the process); that work is
- *    ordered after everything enqueued on `stream` before the call and before
- *    everything enqueued on it after the call, so to the caller it behaves as if
- *    it ran on `stream`.  Concurrent calls on one device must use distinct
- *    workspaces, as always.
+ *    priority, kept with a few events for the life of the process); that work's
+ *    memory accesses are ordered after everything enqueued on `stream` before the
+ *    call and before everything enqueued on it after the call, so to the caller it
+ *    behaves as if it ran on `stream`.  Concurrent calls on one device must use
+ *    distinct workspaces, as always.
  *  - Element type `dtype` (gdn_conv_qk_prep, gdn_decode_step, ...) is the type of the
  *    pre-conv input x, the conv weights and the conv caches (and of the gate, gain
  *    and output of the gated RMSNorm): GDN_BF16 or GDN_F32.  Everything computed is
@@ -139,17 +139,29 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *   workspace      device scratch of at least gdn_chunk_prefill_workspace_size()
  *                  bytes (may be NULL when that size is 0); contents are scratch.
  *                  With GDN_MATH_MFMA it holds the per-(chunk, value head) results
- *                  of the chunk-local phase and one state per (sequence, value head).
+ *                  of the chunk-local phase, one state per (sequence, value head) and
+ *                  one ready flag per (chunk, value head).
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
  *   order          gdn_order (decay before or after the retrieval)
  *
- * With GDN_MATH_MFMA, when the packed chunks are many (at least 256) and the state
- * pass would occupy at most half of the device's compute units, the chunks are cut
- * into up to four segments: the chunk-local phase of segment k + 1 runs while the
- * state pass of segment k runs (on the library's second stream, see the
- * conventions); a sequence's state passes between segments through the workspace.
- * Otherwise the two phases run once each on the caller's stream.  Either way the
- * result is bit-identical to running the two phases below one after the other.
+ * With GDN_MATH_MFMA the two phases below run in one of three schedules, all
+ * bit-identical to running the two phases one after the other:
+ *  - concurrent, when the state pass occupies at most a quarter of the device's
+ *    compute units and there are at least twice as many (chunk, value head) items
+ *    as the other compute units: the chunk-local phase runs on the library's second
+ *    stream, on the compute units the state pass leaves free, and raises a flag in
+ *    the workspace as each record is complete; the state pass runs at the same time
+ *    on `stream` and waits for each flag (a bounded wait: a record that is never
+ *    published ends in wrong output rather than a hang, which the library's own
+ *    chunk-local phase never causes).  When a call comes from another caller stream
+ *    than the previous concurrent one, its state pass first waits for the previous
+ *    call's chunk-local phase, so at most one state pass waits for records at a time;
+ *  - segmented, when the packed chunks are many (at least 256) and the state pass
+ *    occupies at most half of the compute units: the chunks are cut into up to four
+ *    segments, and the chunk-local phase of segment k + 1 (on `stream`) runs while
+ *    the state pass of segment k runs on the second stream; a sequence's state
+ *    passes between segments through the workspace;
+ *  - sequential otherwise: both phases on `stream`, one after the other.
  */
 int gdn_chunk_prefill(const float *q, const float *k, const float *v,
                       const float *g, const float *beta,
@@ -196,7 +208,10 @@ int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N,
  *   workspace      at least gdn_chunk_prefill_workspace_size(T, N, Hk, Hv, dk, dv,
  *                  GDN_MATH_MFMA) bytes; must not overlap any other argument.
  * o, final_state and conv_state_out must not overlap any input except the exact
- * aliases named above.  Errors as for the two calls it replaces.
+ * aliases named above.  Errors as for the two calls it replaces.  The schedules are
+ * those of gdn_chunk_prefill; in the concurrent one the state pass also writes
+ * conv_state_out (after the chunks that read conv_state_in have published), so that
+ * nothing follows the state pass on `stream`.
  */
 int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
                 const void *conv_state_in, void *conv_state_out,
