@@ -240,6 +240,115 @@ struct LocalSmem {
     static_assert(SIZE_STAGED <= 160 * 1024, "staging fits in LDS");
 };
 
+// A lane's part in the fused prep (lane = (token group tg, 8-channel block cb): TOK tokens x
+// 8 channels, the D / 8 lanes of a token group forming one row for the L2 sums).  D = 128
+// (eight waves), 16-bit x: waves 0 .. 3 convolve q and k (two waves per group, 8 tokens per
+// lane) and waves 4 .. 7 convolve v (4 tokens per lane), so each SIMD (waves w and w + 4)
+// carries the same share.  Otherwise D / 64 waves per group take q, k and v, 8 tokens per
+// lane (with fp32 rows the two lane kinds together need more registers than a wave has).
+struct ConvLane {
+    bool vsplit;   // this lane convolves v, 4 tokens
+    bool active;   // this lane convolves at all
+    int grp, cb, tl0, ch0;
+};
+template <int D, typename TX>
+__device__ __forceinline__ ConvLane conv_lane(int wave, int lane, int h, int kh, int Hk) {
+    constexpr int NW = LocalShape<D>::NW, CB = D / 8, WPG = D / 64;
+    constexpr bool VSPLIT = NW == 8 && sizeof(TX) == 2;
+    ConvLane c;
+    c.vsplit = VSPLIT && wave >= 4;
+    c.active = VSPLIT || wave < 3 * WPG;
+    c.cb = lane % CB;
+    const int tg = lane / CB;
+    c.grp = c.vsplit ? 2 : wave / WPG;
+    c.tl0 = c.vsplit ? 16 * (wave - 4) + 4 * tg : (64 / WPG) * (wave % WPG) + 8 * tg;
+    c.ch0 = (c.grp == 0 ? kh * D : c.grp == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D) + 8 * c.cb;
+    return c;
+}
+
+// Fused prep of one lane's TOK tokens x 8 channels of group grp (0 q, 1 k, 2 v): the TOK + 3
+// input rows (from the staged rows in LDS, or x, or the conv cache before the sequence
+// start, else zeros), the depthwise conv + SiLU, then for q and k the L2 norm over the D / 8
+// lanes of the token group, written to the bf16 hi / lo planes; v goes to the fp32 plane.
+// wt holds the lane's conv weights (wt[j][i]: tap j of channel ch0 + i).  Every wave calls it
+// once: with STAGE its barrier separates the reads of the staging area from the plane writes
+// that overwrite part of it.  Inactive lanes only take the barrier.
+template <int D, typename TX, bool STAGE, int TOK>
+__device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict__ x, const TX *__restrict__ cs_in, int conv_dim, int t0, int L, int s_,
+                                                bool first, bool staged, bool active, int grp, int ch0, int tl0, int cb,
+                                                float l2_eps, const float (&wt)[4][8]) {
+    using SM = LocalSmem<D>;
+    constexpr int CB = D / 8, LD = SM::LD;
+    Raw8<TX> rows[TOK + kConvHist];
+    if (active) {
+#pragma unroll
+        for (int r = 0; r < TOK + kConvHist; ++r) {
+            const int tl = tl0 - kConvHist + r;
+            if (tl < L && (tl >= 0 || !first)) {
+                if (STAGE && staged) {
+                    const int sr = tl + kConvHist;   // staged row
+                    const int so = (sr < SM::XRA ? SM::XA + sr * SM::XROW : SM::XB + (sr - SM::XRA) * SM::XROW) +
+                                   grp * 2 * D + 16 * cb;
+                    rows[r].load(reinterpret_cast<const TX *>(smem + so));
+                } else {
+                    rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
+                }
+            } else if (tl < 0 && cs_in) {
+                rows[r].load(cs_in + ((size_t)s_ * kConvHist + (kConvHist + tl)) * conv_dim + ch0);
+            } else {
+                rows[r].zero();
+            }
+        }
+    }
+    if constexpr (STAGE) __syncthreads();   // staging part A is read before the planes overwrite it
+    if (!active) return;
+    float hw[3][8];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) rows[j].to_f32(hw[j]);
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) {
+        float xt[8], y[8];
+        rows[i + kConvHist].to_f32(xt);
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = wt[0][e] * hw[0][e];
+            acc = fmaf(wt[1][e], hw[1][e], acc);
+            acc = fmaf(wt[2][e], hw[2][e], acc);
+            acc = fmaf(wt[3][e], xt[e], acc);
+            y[e] = silu(acc);
+            ss = fmaf(y[e], y[e], ss);
+        }
+        const int tl = tl0 + i;
+        if (tl >= L) {   // padded row: zero (its conv window still reaches real rows)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = 0.f;
+            ss = 0.f;
+        }
+        if (grp < 2) {
+            ss = group_sum<CB>(ss);
+            const float rn = rsqrtf(ss + l2_eps);
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float yn = y[e] * rn;
+                hi[e] = (bf16)yn;
+                lo[e] = (bf16)(yn - (float)hi[e]);
+            }
+            bf16 *ph = reinterpret_cast<bf16 *>(smem + (grp == 0 ? SM::QH : SM::KH));
+            bf16 *pl = reinterpret_cast<bf16 *>(smem + (grp == 0 ? SM::QL : SM::KL));
+            *reinterpret_cast<bf16x8 *>(ph + tl * LD + 8 * cb) = hi;
+            *reinterpret_cast<bf16x8 *>(pl + tl * LD + 8 * cb) = lo;
+        } else {
+            float *vp = reinterpret_cast<float *>(smem + SM::XT) + tl * SM::VLD + 8 * cb;
+            *reinterpret_cast<f32x4 *>(vp) = f32x4{y[0], y[1], y[2], y[3]};
+            *reinterpret_cast<f32x4 *>(vp + 4) = f32x4{y[4], y[5], y[6], y[7]};
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { hw[0][e] = hw[1][e]; hw[1][e] = hw[2][e]; hw[2][e] = xt[e]; }
+    }
+}
+
 // One workgroup per (chunk, value head), fully parallel over chunks.  With
 // T = (I + A)^-1, M = P T, Dc = diag(e^{G_c - G}), Bk = diag(b e^G), Bv = diag(b):
 //   -W' = -Dc T Bk K,  U' = Dc T Bv V,  Qt = diag(scale e^G) Q - M Bk K,  Ol = M Bv V
@@ -306,6 +415,16 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // in another sequence.
     int s_ = 0, c_ = 0, sb = 0, se = 0;
     bool have = false;
+    // Fused: the lane's conv weights, loaded once (a workgroup keeps its head, so its lanes
+    // keep their channels, for the whole launch).
+    float cwt[4][8];
+    if constexpr (FUSED) {
+        const ConvLane cl = conv_lane<D, TX>(threadIdx.x >> 6, threadIdx.x & 63, h, kh, Hk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cwt[j][i] = cl.active ? to_f32(conv_w[(size_t)(cl.ch0 + i) * kConvK + j]) : 0.f;
+    }
     for (int gc = g0 + blockIdx.x; gc < g1; gc += nslots) {
     // The thread index passes through an empty asm each iteration, so nothing derived from
     // it is hoisted out of the loop and kept live across it (that costs registers the
@@ -393,90 +512,17 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         }
     }
     if constexpr (FUSED) {
-        // Waves 0 .. 3D/64 - 1 convolve: D/64 waves per group (q, k, v of this workgroup's
-        // heads); lane = (token group tg, 8-channel block cb), 8 tokens x 8 channels each.
-        // Rows past the chunk's last token are zeros (SiLU(0) = 0, and a zero vector stays
-        // zero under the L2 norm), so padded rows of the planes are zero.
-        constexpr int CB = D / 8, TGW = 64 / CB, WPG = D / 64;
-        const bool conv_wave = wave < 3 * WPG;
-        const int grp = wave / WPG, th = wave % WPG;
-        const int cb = lane % CB, tg = lane / CB;
-        const int ch0 = (grp == 0 ? kh * D : grp == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D) + 8 * cb;
-        const int tl0 = th * TGW * 8 + 8 * tg;   // first local token of this lane
+        // conv + SiLU + L2 from x (lane roles: conv_lane); rows past the chunk's last token
+        // are zeros (SiLU(0) = 0, and a zero vector stays zero under the L2 norm), so padded
+        // rows of the planes are zero.
+        const ConvLane cl = conv_lane<D, TX>(wave, lane, h, kh, Hk);
         const bool first = c_ == 0;              // history before the sequence start
-        Raw8<TX> rows[11];
-        if (conv_wave) {
-#pragma unroll
-            for (int r = 0; r < 11; ++r) {
-                const int tl = tl0 - kConvHist + r;
-                if (tl < L && (tl >= 0 || !first)) {
-                    if (STAGE && staged) {
-                        const int sr = tl + kConvHist;   // staged row
-                        const int so = (sr < SM::XRA ? SM::XA + sr * SM::XROW : SM::XB + (sr - SM::XRA) * SM::XROW) +
-                                       grp * 2 * D + 16 * cb;
-                        rows[r].load(reinterpret_cast<const TX *>(smem + so));
-                    } else {
-                        rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
-                    }
-                } else if (tl < 0 && cs_in) {
-                    rows[r].load(cs_in + ((size_t)s_ * kConvHist + (kConvHist + tl)) * conv_dim + ch0);
-                } else {
-                    rows[r].zero();
-                }
-            }
-        }
-        if constexpr (STAGE) __syncthreads();   // staging part A is read before the planes overwrite it
-        if (conv_wave) {
-            float wt[4][8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wt[j][i] = to_f32(conv_w[(size_t)(ch0 + i) * kConvK + j]);
-            float hw[3][8];
-#pragma unroll
-            for (int j = 0; j < 3; ++j) rows[j].to_f32(hw[j]);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float xt[8], y[8];
-                rows[i + kConvHist].to_f32(xt);
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float acc = wt[0][e] * hw[0][e];
-                    acc = fmaf(wt[1][e], hw[1][e], acc);
-                    acc = fmaf(wt[2][e], hw[2][e], acc);
-                    acc = fmaf(wt[3][e], xt[e], acc);
-                    y[e] = silu(acc);
-                    ss = fmaf(y[e], y[e], ss);
-                }
-                const int tl = tl0 + i;
-                if (tl >= L) {   // padded row: zero (its conv window still reaches real rows)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = 0.f;
-                    ss = 0.f;
-                }
-                if (grp < 2) {
-                    ss = group_sum<CB>(ss);
-                    const float rn = rsqrtf(ss + l2_eps);
-                    bf16x8 hi, lo;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float yn = y[e] * rn;
-                        hi[e] = (bf16)yn;
-                        lo[e] = (bf16)(yn - (float)hi[e]);
-                    }
-                    bf16 *ph = grp == 0 ? Qh : Kh, *pl = grp == 0 ? Ql : Kl;
-                    *reinterpret_cast<bf16x8 *>(ph + tl * LD + 8 * cb) = hi;
-                    *reinterpret_cast<bf16x8 *>(pl + tl * LD + 8 * cb) = lo;
-                } else {
-                    float *vp = reinterpret_cast<float *>(smem + SM::XT) + tl * SM::VLD + 8 * cb;
-                    *reinterpret_cast<f32x4 *>(vp) = f32x4{y[0], y[1], y[2], y[3]};
-                    *reinterpret_cast<f32x4 *>(vp + 4) = f32x4{y[4], y[5], y[6], y[7]};
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { hw[0][e] = hw[1][e]; hw[1][e] = hw[2][e]; hw[2][e] = xt[e]; }
-            }
-        }
+        if (cl.vsplit)
+            fused_conv_lane<D, TX, STAGE, 4>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, true, cl.grp, cl.ch0,
+                                             cl.tl0, cl.cb, l2_eps, cwt);
+        else
+            fused_conv_lane<D, TX, STAGE, 8>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, cl.active, cl.grp,
+                                             cl.ch0, cl.tl0, cl.cb, l2_eps, cwt);
     }
     // K and Q as bf16 hi / lo planes, row-major [token][head dim]
 #pragma unroll
