@@ -8,7 +8,7 @@
       `--pmc WRITE_SIZE` runs of `bench.py --copy-calibration`: each counter is
       scaled by what it reads for the plain streaming copy of known size that
       the calibration launches, and the lines end with the SHA-256 of the kernel
-      sources, so a reader can tell when the figures went stale.
+      sources and the build script, so a reader can tell when the figures went stale.
   python -m hybrid_linear_attention_gated_amd.profiling timeline DIR [FIRST [SKIP]]
       kernel start / end offsets inside one step, averaged over the steps of a
       `rocprofv3 --kernel-trace` run: a step begins at each launch of the kernel
@@ -63,13 +63,15 @@ def short_name(symbol: str) -> str:
 
 
 def source_sha256() -> str:
-    """SHA-256 over the HIP sources and headers the library is built from."""
+    """SHA-256 over the HIP sources and headers the library is built from and the build
+    script (its compiler options shape the kernels too)."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(_CSRC, "*"))):
-        if path.endswith((".hip", ".hpp", ".cpp", ".h")):
-            h.update(os.path.basename(path).encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+    paths = [p for p in glob.glob(os.path.join(_CSRC, "*")) if p.endswith((".hip", ".hpp", ".cpp", ".h"))]
+    paths.append(os.path.join(os.path.dirname(_CSRC), "build.py"))
+    for path in sorted(paths):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
