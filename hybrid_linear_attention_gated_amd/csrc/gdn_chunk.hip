@@ -1002,6 +1002,20 @@ __device__ __forceinline__ void conv_rows(const ConvOut &cv, int s, int t0, int 
     else conv_rows_copy<uint32_t>(cv, s, t0, L, ch0, n, tid, nthreads);
 }
 
+// Sequence with chunk-count rank r (rank 0: the most chunks; ties by index) among N <= 64
+// sequences: lane i holds sequence i's chunk count and counts the sequences ranked before it.
+__device__ __forceinline__ int seq_by_rank(const int32_t *cu, int N, int Ttot, int r) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int mine = lane < N ? n_chunks(seq_end(cu, lane, Ttot) - seq_begin(cu, lane)) : -1;
+    int ahead = 0;
+    for (int j = 0; j < N; ++j) {
+        const int other = __shfl(mine, j, kWave);
+        ahead += (other > mine || (other == mine && j < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(lane < N && ahead == r);
+    return __builtin_amdgcn_readfirstlane(__ffsll((long long)hit) - 1);
+}
+
 // COH: records come from a concurrently running chunk-local kernel (wait for each chunk's
 // flag, read device-coherently; the conv cache of the fused prefill is written here, see
 // ConvOut); otherwise plain cached reads.
@@ -1021,7 +1035,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     const int u = 8 * (b / (8 * NP)) + (b % 8);
     const int pair = (b / 8) % NP;
     if (u >= units) return;
-    const int s = u / Hv, h = u % Hv;
+    // With a few sequences (N <= 64) the units go to the sequences longest first, so the
+    // workgroups dispatched last, when there are more than the compute units, have the
+    // least work (list scheduling in decreasing order).
+    const int nseq = units / Hv, h = u % Hv;
+    const int s = (cu && nseq > 1 && nseq <= kWave) ? seq_by_rank(cu, nseq, Ttot, u / Hv) : u / Hv;
     // wave index in a scalar register (the direct-to-LDS base and offset must be uniform)
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool copier = wave >= 2;
