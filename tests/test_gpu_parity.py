@@ -208,6 +208,24 @@ def test_segmented_equals_split_phases(gdn):
     assert torch.equal(f1, f2)
 
 
+# more sequences than the state pass ranks by length (64), with ties, empties and ragged tails
+MANY_LENGTHS = [int(x) for x in np.random.default_rng(4242).integers(0, 200, size=80)] + [0, 64, 64, 130]
+
+
+def test_core_chunked_many_sequences(gdn):
+    announce(f"core chunked d=128, {len(MANY_LENGTHS)} sequences (0..199 tokens)")
+    wl = inputs.core_workload("many", 4300, MANY_LENGTHS, 2, 4, 128, 128, random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
+def test_core_chunked_ranked_sequences(gdn):
+    """60 sequences (the state pass takes them longest first) with repeated chunk counts."""
+    lengths = MANY_LENGTHS[:60]
+    announce(f"core chunked d=64, {len(lengths)} sequences, longest-first state pass")
+    wl = inputs.core_workload("ranked", 4301, lengths, 2, 2, 64, 64, random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
 def test_core_empty_sequences(gdn):
     announce("core: all sequences empty (T = 0)")
     H, d = 2, 128
