@@ -6,8 +6,9 @@ input:
   prefill of one linear-attention layer of the 0.8B hybrid shape
   (T = 4096 tokens, 16 key / 16 value heads, head dims 128, bf16 pre-conv x):
       gdn_prefill (one call: conv + SiLU + L2 inside the chunk-local kernel,
-      whose segments overlap the state pass on two streams; q, k, v never
-      reach HBM)
+      which runs on the library's second stream while the state pass, on the
+      caller's stream, consumes each chunk's record as soon as it is published;
+      q, k, v never reach HBM)
   followed by one decode step of 256 sequences (gdn_decode_step, fp32 state in place).
 
 `value` is prefill tokens/s: 4096 tokens over the event time of the gdn_prefill
@@ -25,6 +26,10 @@ stay cached from one step to the next (the decode step reads its state with
 non-temporal loads).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+Profiler runs: --split-only (the split-phase region alone), --metric-only (the
+gdn_prefill + decode region alone, for kernel traces of the concurrent schedule),
+--copy-calibration (a 512 MiB streaming copy after the timed steps, for the
+FETCH_SIZE / WRITE_SIZE scaling).
 """
 from __future__ import annotations
 
