@@ -135,8 +135,8 @@ def main():
                     help="after the timed steps, stream 512 MiB through one elementwise kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the hot path is data-parallel per sequence and per head and this "
-              "build runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the hot path is data-parallel per sequence and per head, and the "
+              "library runs on a single MI355X; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
