@@ -157,7 +157,7 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *    than the previous concurrent one, its state pass first waits for the previous
  *    call's chunk-local phase, so at most one state pass waits for records at a time;
  *  - segmented, when the packed chunks are many (at least 256) and the state pass
- *    occupies at most half of the compute units: the chunks are cut into up to four
+ *    occupies at most half of the compute units: the chunks are cut into up to sixteen
  *    segments, and the chunk-local phase of segment k + 1 (on `stream`) runs while
  *    the state pass of segment k runs on the second stream; a sequence's state
  *    passes between segments through the workspace;
