@@ -36,7 +36,9 @@
 //    rounded.
 //
 // Kernels.
-//  chunk_local_kernel: one workgroup per (chunk, value head), fully parallel.
+//  chunk_local_kernel: the (chunk, value head) items are independent; the kernel is
+//    persistent, one workgroup per compute unit looping over its head's chunks
+//    (FUSED: it also runs the conv + SiLU + L2 prep of its chunk's tokens from x).
 //    Explicit T = (I + A)^-1 and M = P T by block back substitution, then four
 //    products.  Writes -W' = -diag(e^{G_c - G}) W and Qt as fp16 MFMA A-operand
 //    fragments, K^T as bf16 hi / lo A-operand fragments, and
@@ -55,6 +57,11 @@
 //    MFMA may be permuted as long as A and B share the permutation, and the
 //    stored A fragments carry the permutation that matches two stacked
 //    accumulator tiles (kperm).
+//
+// Schedules (host side, end of file): the two kernels run one after the other, or
+// in segments whose chunk-local and state-pass phases overlap on two streams, or
+// concurrently, the state pass waiting for each record's ready flag while the
+// chunk-local kernel, on the other compute units, publishes them.
 #include <algorithm>
 #include <mutex>
 #include <numeric>
