@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "gdn_launch.hpp"
 
@@ -46,6 +47,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 bool valid_order(int order) { return order == GDN_ORDER_DECAY_FIRST || order == GDN_ORDER_RETRIEVE_FIRST; }
 
+// Every non-NULL device pointer is 16-byte aligned (the kernels move 16-byte vectors).
+bool aligned16(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +67,7 @@ const char *gdn_status_string(int status) {
         case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
         case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch or runtime call failed";
         case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input it must not overlap";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a device pointer is not 16-byte aligned";
         default: return "unknown gdn status";
     }
 }
@@ -71,6 +80,7 @@ int gdn_conv_qk_prep(const void *x, const void *conv_w, const int32_t *cu_seqlen
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
         if (!conv_w || (T > 0 && (!x || !q || !k || !v))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({x, conv_w, cu_seqlens, conv_state_in, conv_state_out, q, k, v})) return GDN_ERR_ALIGN;
         if (int e = check_heads(Hk, Hv)) return e;
         if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 256) || dv < 8 || dv > 256 || dv % 8 != 0) return GDN_ERR_UNSUPPORTED;
@@ -114,6 +124,7 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
         const bool need_inputs = phases & 1, need_outputs = phases & 2;
         if (T > 0 && need_inputs && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL_POINTER;
         if (T > 0 && need_outputs && !o) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, o, workspace})) return GDN_ERR_ALIGN;
         if (int e = check_heads(Hk, Hv)) return e;
         if (math != GDN_MATH_F32 && math != GDN_MATH_MFMA) return GDN_ERR_UNSUPPORTED;
         if (!valid_order(order)) return GDN_ERR_UNSUPPORTED;
@@ -180,6 +191,9 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
         if (!conv_w || (T > 0 && (!x || !g || !beta || ((phases & 2) && !o)))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({x, conv_w, cu_seqlens, conv_state_in, conv_state_out, g, beta, initial_state, final_state, o,
+                        workspace}))
+            return GDN_ERR_ALIGN;
         if (int e = check_heads(Hk, Hv)) return e;
         if (!valid_dtype(dtype) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!gdn::chunked_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
@@ -242,6 +256,7 @@ int decode_impl(const void *x, const void *conv_w, void *conv_state, const float
         if (B < 0) return GDN_ERR_BAD_SHAPE;
         if (!conv_w || (B > 0 && (!x || !conv_state || !g || !beta || !state))) return GDN_ERR_NULL_POINTER;
         if (gated ? (!gamma || (B > 0 && (!z || !out))) : (B > 0 && !o)) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({x, conv_w, conv_state, g, beta, state, o, z, gamma, out})) return GDN_ERR_ALIGN;
         if (int e = check_heads(Hk, Hv)) return e;
         if (!valid_dtype(dtype) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128)) return GDN_ERR_UNSUPPORTED;
@@ -298,6 +313,7 @@ int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *ou
     try {
         if (rows < 0) return GDN_ERR_BAD_SHAPE;
         if (!gamma || (rows > 0 && (!y || !z || !out))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({y, z, gamma, out})) return GDN_ERR_ALIGN;
         if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dv, 16, 256)) return GDN_ERR_UNSUPPORTED;
         if (!(eps >= 0.f) || !std::isfinite(eps)) return GDN_ERR_BAD_SHAPE;

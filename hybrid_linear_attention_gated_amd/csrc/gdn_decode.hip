@@ -46,6 +46,27 @@ __device__ __forceinline__ float conv_step(const T *__restrict__ x, const T *__r
     return silu(acc);
 }
 
+// Four consecutive elements of the element type as one vector access (8 or 16 bytes).
+__device__ __forceinline__ void load4(const bf16 *p, float *o) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (float)v[e];
+}
+__device__ __forceinline__ void load4(const float *p, float *o) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = v[e];
+}
+__device__ __forceinline__ void store4(bf16 *p, const float *i) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)i[e];
+    *reinterpret_cast<bf16x4 *>(p) = v;
+}
+__device__ __forceinline__ void store4(float *p, const float *i) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{i[0], i[1], i[2], i[3]};
+}
+
 // GATED: the output row of each value head goes through the gated RMSNorm epilogue
 // ("7.6 Qwen3.5: the linear-attention hybrid", sections 7.6.2 and 7.6.3) before it is
 // stored: out = o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z), in the element type.
@@ -93,6 +114,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
     };
     load_state(kh * group);
+    // gated epilogue: this lane's gate and gain values, loaded with the state (lanes 0 ..
+    // TPR - 1 of wave 0 hold a head's outputs), so the store at the end does not wait for them
+    float zf[4] = {0.f, 0.f, 0.f, 0.f}, gf[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool gate_lane = GATED && wave == 0 && rg == 0;
+    auto load_gate = [&](int h) {
+        if (gate_lane) load4(z + ((size_t)b * Hv + h) * DV + 4 * cg, zf);
+    };
+    if (gate_lane) load4(gamma + 4 * cg, gf);
+    load_gate(kh * group);
 
     // q and k channels of this key head
     for (int ch = tid; ch < 2 * DK; ch += kDecThreads) {
@@ -124,7 +154,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 
     for (int gi = 0; gi < group; ++gi) {
         const int h = kh * group + gi;
-        if (gi > 0) load_state(h);
+        if (gi > 0) {
+            load_state(h);
+            load_gate(h);
+        }
         for (int ch = tid; ch < DV; ch += kDecThreads)
             v_s[ch] = conv_step(x, w, cs, b, 2 * Hk * DK + h * DV + ch, conv_dim);
 
@@ -168,10 +201,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 ss = group_sum<TPR>(ss);
                 const float rn = rsqrtf(ss * (1.0f / DV) + norm_eps);
                 if (rg == 0) {
-                    const size_t off = ((size_t)b * Hv + h) * DV + 4 * cg;
+                    float r4[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        out[off + e] = from_f32<T>(pq[e] * rn * to_f32(gamma[4 * cg + e]) * silu(to_f32(z[off + e])));
+                    for (int e = 0; e < 4; ++e) r4[e] = pq[e] * rn * gf[e] * silu(zf[e]);
+                    store4(out + ((size_t)b * Hv + h) * DV + 4 * cg, r4);
                 }
             }
         } else if (rg == 0) {

@@ -44,6 +44,10 @@
  *    (N must then be 1).  Zero-length sequences are allowed.  These device values
  *    are a precondition and are not validated.
  *  - Tensor pointers may be NULL when the tensor is empty (T = 0, or B = 0).
+ *  - Every non-NULL device pointer (tensors, cu_seqlens, workspace) must be 16-byte
+ *    aligned, as every device allocator returns them: the kernels move 16-byte
+ *    vectors and stage rows with 16-byte direct-to-LDS loads.  A misaligned pointer
+ *    returns GDN_ERR_ALIGN.
  *  - Return value: GDN_OK or a gdn_status code.  Argument errors are detected on
  *    the host before anything is enqueued; nothing is written then.  Launch
  *    failures map to GDN_ERR_HIP.  No function aborts or throws.
@@ -58,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -67,7 +71,8 @@ typedef enum {
     GDN_ERR_UNSUPPORTED = 3,    /* head dim / dtype combination not implemented         */
     GDN_ERR_WORKSPACE = 4,      /* workspace NULL or smaller than the queried size      */
     GDN_ERR_HIP = 5,            /* a HIP launch or runtime call failed                  */
-    GDN_ERR_ALIAS = 6           /* an output overlaps an input it must not overlap      */
+    GDN_ERR_ALIAS = 6,          /* an output overlaps an input it must not overlap      */
+    GDN_ERR_ALIGN = 7           /* a device pointer is not 16-byte aligned              */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -275,7 +280,7 @@ int gdn_decode_step(const void *x, const void *conv_w, void *conv_state,
  *                      must not overlap gamma or partly overlap y or z
  * dv in {16, 32, 64, 128, 256}; eps >= 0 (the pages' RMSNorm uses 1e-6).
  * Errors: GDN_ERR_NULL_POINTER, GDN_ERR_BAD_SHAPE (rows < 0, bad eps),
- * GDN_ERR_UNSUPPORTED (dv, dtype), GDN_ERR_ALIAS.
+ * GDN_ERR_UNSUPPORTED (dv, dtype), GDN_ERR_ALIAS, GDN_ERR_ALIGN.
  */
 int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *out,
                       long rows, int dv, float eps, int dtype, void *stream);

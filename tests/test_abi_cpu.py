@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 2
-    for code in range(7):
+    assert L.gdn_abi_version() == 3
+    for code in range(8):
         assert L.gdn_status_string(code).decode().startswith("GDN_")
     assert b"unknown" in L.gdn_status_string(99)
 
@@ -66,7 +66,9 @@ def test_prep_validation(L):
     assert call(dk=24) == 3
     assert call(dv=12) == 3
     assert call(eps=float("nan")) == 2
-    assert call(q=P(8)) == 6           # q overlaps x
+    assert call(q=P(16)) == 6          # q overlaps x
+    assert call(q=P((2 << 24) + 4)) == 7   # misaligned output
+    assert call(csi=P((6 << 24) + 2)) == 7  # misaligned conv cache
     assert call(cso=P(5 << 24), csi=P((5 << 24) + 64)) == 6   # partial overlap of the conv caches
 
 
@@ -93,7 +95,9 @@ def test_prefill_validation(L):
     assert call(ws=None) == 4
     assert call(wsb=need - 1) == 4
     assert call(o=P(16)) == 6                                   # o overlaps q
-    assert call(s0=P(6 << 24), sf=P((6 << 24) + 4)) == 6          # partial state alias
+    assert call(s0=P(6 << 24), sf=P((6 << 24) + 16)) == 6         # partial state alias
+    assert call(ws=P((1 << 30) + 8)) == 7                       # misaligned workspace
+    assert call(g=P((3 << 24) + 4)) == 7                        # misaligned input
     assert call(scale=float("inf")) == 2
     assert call(order=2) == 3
     assert call(order=-1, dt=0) == 3                            # also on the fp32 path
@@ -125,9 +129,10 @@ def test_fused_prefill_validation(L):
     assert call(wsb=need - 1) == 4
     assert call(o=P(16)) == 6                                   # o overlaps x
     assert call(cso=P(1 << 24)) == 6                            # conv cache overlaps the weights
-    assert call(csi=P(6 << 24), cso=P((6 << 24) + 2)) == 6      # partial conv cache alias
-    assert call(s0=P(7 << 24), sf=P((7 << 24) + 4)) == 6        # partial state alias
-    assert call(ws=P(8)) == 6                                   # workspace overlaps x
+    assert call(csi=P(6 << 24), cso=P((6 << 24) + 16)) == 6     # partial conv cache alias
+    assert call(s0=P(7 << 24), sf=P((7 << 24) + 16)) == 6       # partial state alias
+    assert call(ws=P(16)) == 6                                  # workspace overlaps x
+    assert call(x=P(2)) == 7                                    # misaligned x (a bf16 view at an odd offset)
     assert call(order=5) == 3
     # the local phase alone: no o or states
     assert L.gdn_prefill_local(P(0), None, None, 1, None, None, P(3 << 24), P(4 << 24), ctypes.c_float(1.0),
@@ -152,8 +157,9 @@ def test_decode_validation(L):
     assert call(B=-1) == 2
     assert call(Hv=3) == 2
     assert call(dk=256) == 3
-    assert call(o=P(8)) == 6
-    assert call(cs=P((5 << 24) + 8)) == 6                     # conv cache overlaps the state
+    assert call(o=P(16)) == 6
+    assert call(cs=P((5 << 24) + 16)) == 6                    # conv cache overlaps the state
+    assert call(st=P((5 << 24) + 4)) == 7                     # misaligned state
     assert call(order=3) == 3
 
 
@@ -174,8 +180,9 @@ def test_gated_rmsnorm_validation(L):
     assert call(dv=96) == 3
     assert call(dv=512) == 3
     assert call(dt=4) == 3
-    assert call(out=P((2 << 24) + 8)) == 6                       # out overlaps gamma
-    assert call(out=P(8)) == 6                                   # partial overlap with y
+    assert call(out=P((2 << 24) + 16)) == 6                      # out overlaps gamma
+    assert call(out=P(16)) == 6                                  # partial overlap with y
+    assert call(z=P((1 << 24) + 2)) == 7                         # misaligned gate
     assert call(out=P(0)) == 6                                   # bf16 out cannot replace fp32 y
 
 
@@ -195,7 +202,8 @@ def test_decode_gated_validation(L):
     assert call(out=None) == 1
     assert call(neps=float("inf")) == 2
     assert call(dk=256) == 3
-    assert call(out=P((6 << 24) + 8)) == 6                       # out overlaps z
+    assert call(out=P((6 << 24) + 16)) == 6                      # out overlaps z
+    assert call(gm=P((7 << 24) + 8)) == 7                        # misaligned gain
     assert call(out=P((5 << 24) + 64)) == 6                      # out overlaps the state
 
 
