@@ -131,3 +131,46 @@ def gated_rmsnorm(y, z, gamma, eps=1e-6):
     rows = y.size // dv if dv else 0
     lib().oracle_gated_rmsnorm(_p(y), _p(z), _p(gamma), _p(out), rows, dv, float(eps))
     return out
+
+
+def layer_prefill(hidden, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, cs_in=None, s0=None, scale=1.0,
+                  l2_eps=1e-6, norm_eps=1e-6, order=0, heads=None):
+    """Layer forward of ``gdn_ref.layer_prefill`` with the conv prep, the recurrence and
+    the gated RMSNorm taken from the C library (fast enough for the 0.8B layer shape).
+    heads: optional list of value heads whose recurrence is computed (the others'
+    outputs and states are zero, and so is ``out``'s dependence on them); ``None`` =
+    all heads.  Returns out [T, E], final states, conv caches, and the intermediate
+    tensors {x, z, g, beta, y} (y = the bf16 normalised output entering the output
+    projection)."""
+    from . import gdn_ref
+    hidden = _f64(hidden)
+    T = hidden.shape[0]
+    xp, zp, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
+    x = gdn_ref.bf16_round(xp)
+    z = gdn_ref.bf16_round(zp)
+    g, beta = gdn_ref.layer_gates(ap, bp)
+    q, k, v, cs_out = prep(x, conv_w, cu, Hk, Hv, dk, dv, cs_in, l2_eps)
+    o, fin = recurrence(q, k, v, g, beta, cu, s0, scale, heads=heads, order=order)
+    y = gdn_ref.bf16_round(gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps)).reshape(T, Hv * dv)
+    if heads is not None:
+        keep = np.zeros((Hv, dv))
+        keep[list(heads)] = 1.0
+        y = y * keep.reshape(1, Hv * dv)
+    out = y @ _f64(w_out).T
+    return out, fin, cs_out, {"x": x, "z": z, "g": g, "beta": beta, "y": y}
+
+
+def layer_decode(hidden, w_in, conv_w, gamma, w_out, cs, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6,
+                 norm_eps=1e-6, order=0):
+    """``gdn_ref.layer_decode`` with the decode step and the gated RMSNorm taken from
+    the C library.  Returns out [B, E], new state, new conv cache, and {x, z, g, beta, y}."""
+    from . import gdn_ref
+    hidden = _f64(hidden)
+    B = hidden.shape[0]
+    xp, zp, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
+    x = gdn_ref.bf16_round(xp)
+    z = gdn_ref.bf16_round(zp)
+    g, beta = gdn_ref.layer_gates(ap, bp)
+    o, st, cso = decode(x, conv_w, cs, g, beta, state, Hk, Hv, dk, dv, scale, l2_eps, order)
+    y = gdn_ref.bf16_round(gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps)).reshape(B, Hv * dv)
+    return y @ _f64(w_out).T, st, cso, {"x": x, "z": z, "g": g, "beta": beta, "y": y}

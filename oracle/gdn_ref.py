@@ -187,3 +187,85 @@ def gated_rmsnorm(y, z, gamma, eps=1e-6):
     y = np.asarray(y, dtype=np.float64)
     rms = np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
     return (y / rms) * np.asarray(gamma, dtype=np.float64) * silu(np.asarray(z, dtype=np.float64))
+
+
+# ---------------------------------------------------------------- layer forward
+#
+# The whole linear-attention token mixer around the core ("7.6 Qwen3.5: the
+# linear-attention hybrid", section 7.6.2, with the layer widths of the 7.6.1 table;
+# "Hugging Face Transformers: Qwen3.5-MoE series explained", sections 4.3 and 8.2):
+# a bias-free input projection gives the pre-conv q|k|v, the output gate z and one
+# decay and one update pre-activation per value head; conv + SiLU + L2 and the gated
+# delta rule follow; the output passes the gated RMSNorm with SiLU(z) and a bias-free
+# output projection.  The pages do not say how the two gate pre-activations become
+# gates; the reading taken here is g = -softplus(a) (so a = exp(g) lies in (0, 1)) and
+# beta = sigmoid(b), the maps under which N(0, 1) pre-activations give the layer
+# shape's gate distributions.  The layer's intermediate tensors have the library's
+# types: the pre-conv q|k|v, z and the normalised output entering the output
+# projection are bf16 (the element type), g and beta fp32; everything else is fp64.
+
+
+def bf16_round(x):
+    """Nearest bfloat16 value of each element (8 significant bits, ties to even),
+    as an fp64 array; for values in the normal range."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                      # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def softplus(x):
+    """log(1 + e^x), without overflow."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def sigmoid(x):
+    """1 / (1 + e^-x), without overflow."""
+    return 0.5 * (1.0 + np.tanh(0.5 * np.asarray(x, dtype=np.float64)))
+
+
+def layer_gates(a, b):
+    """Decay log g = -softplus(a) and update gate beta = sigmoid(b), rounded to fp32."""
+    return (-softplus(a)).astype(np.float32), sigmoid(b).astype(np.float32)
+
+
+def layer_split(proj, Hk, Hv, dk, dv):
+    """Split input-projection outputs [rows, conv_dim + Hv dv + 2 Hv] into the
+    pre-conv q|k|v, z, a and b column blocks (in that order)."""
+    C = 2 * Hk * dk + Hv * dv
+    Z = Hv * dv
+    assert proj.shape[1] == C + Z + 2 * Hv
+    return proj[:, :C], proj[:, C:C + Z], proj[:, C + Z:C + Z + Hv], proj[:, C + Z + Hv:]
+
+
+def layer_prefill(hidden, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, cs_in=None, s0=None, scale=1.0,
+                  l2_eps=L2_EPS, norm_eps=1e-6, order=0):
+    """Layer forward over packed sequences.  hidden [T, E], w_in [conv_dim + Hv dv +
+    2 Hv, E] and w_out [E, Hv dv] stored as a linear layer stores them (out = in W^T);
+    conv_w [conv_dim, 4]; gamma [dv] the gain as applied.  Returns out [T, E], the
+    final states [N, Hv, dk, dv] and the conv caches [N, 3, conv_dim]."""
+    hidden = np.asarray(hidden, np.float64)
+    T = hidden.shape[0]
+    xp, zp, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
+    x = bf16_round(xp)
+    z = bf16_round(zp)
+    g, beta = layer_gates(ap, bp)
+    q, k, v, cs_out = prep(x, conv_w, cu, Hk, Hv, dk, dv, cs_in, l2_eps)
+    o, fin = recurrence(q, k, v, g, beta, cu, s0, scale, order)
+    y = bf16_round(gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps)).reshape(T, Hv * dv)
+    return y @ np.asarray(w_out, np.float64).T, fin, cs_out
+
+
+def layer_decode(hidden, w_in, conv_w, gamma, w_out, cs, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=L2_EPS,
+                 norm_eps=1e-6, order=0):
+    """One token of B sequences through the layer: hidden [B, E]; cs [B, 3, conv_dim]
+    and state [B, Hv, dk, dv] are the caches.  Returns out [B, E], the new state and
+    the new conv cache."""
+    hidden = np.asarray(hidden, np.float64)
+    B = hidden.shape[0]
+    xp, zp, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
+    x = bf16_round(xp)
+    z = bf16_round(zp)
+    g, beta = layer_gates(ap, bp)
+    o, new_state, new_cs = decode_step(x, conv_w, cs, g, beta, state, Hk, Hv, dk, dv, scale, l2_eps, order)
+    y = bf16_round(gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps)).reshape(B, Hv * dv)
+    return y @ np.asarray(w_out, np.float64).T, new_state, new_cs

@@ -622,3 +622,219 @@ def test_order1_c_matches_numpy_and_decode_equals_prefill():
         outs.append(ot[0])
     np.testing.assert_allclose(np.stack(outs), oc[:3], rtol=1e-5, atol=1e-6)
     np.testing.assert_allclose(st[0], fc[0], rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------------ layer forward (NEXT-4)
+# "7.6 Qwen3.5: the linear-attention hybrid", 7.6.1 (layer widths) and 7.6.2 (input
+# projection -> causal conv -> L2 -> gated delta rule -> RMSNorm(y) * SiLU(z) -> output
+# projection); the gate maps g = -softplus(a), beta = sigmoid(b) are the reading stated in
+# the oracle.
+
+def _bf16_vals(a):
+    """fp64 array of bf16-representable values (torch's fp32 -> bf16 rounding)."""
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_round_matches_library_rounding():
+    rng = np.random.default_rng(300)
+    x = _f32(rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000)))
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(gdn_ref.bf16_round(x.astype(np.float64)), ref)
+    # ties go to the even neighbour; anything above a tie goes up
+    one = 1.0
+    assert gdn_ref.bf16_round(one + 2.0 ** -8) == one
+    assert gdn_ref.bf16_round(one + 3 * 2.0 ** -8) == one + 2.0 ** -6
+    assert gdn_ref.bf16_round(one + 2.0 ** -8 + 2.0 ** -40) == one + 2.0 ** -7
+    assert gdn_ref.bf16_round(-(one + 2.0 ** -8 + 2.0 ** -40)) == -(one + 2.0 ** -7)
+    assert gdn_ref.bf16_round(0.0) == 0.0
+
+
+def test_layer_gates_closed_forms():
+    a = np.array([0.0, math.log(math.e - 1.0), -40.0, 40.0])
+    b = np.array([0.0, math.log(3.0), -math.log(3.0), 0.0])
+    g, beta = gdn_ref.layer_gates(a, b)
+    assert g.dtype == np.float32 and beta.dtype == np.float32
+    np.testing.assert_allclose(g[:2], [-math.log(2.0), -1.0], rtol=1e-7)
+    np.testing.assert_allclose(g[2], -math.exp(-40.0), rtol=1e-6)     # softplus(x) ~ e^x far left
+    np.testing.assert_allclose(g[3], -40.0, rtol=1e-7)                  # softplus(x) ~ x far right
+    np.testing.assert_allclose(beta[:3], [0.5, 0.75, 0.25], rtol=1e-7)
+    x = np.random.default_rng(301).standard_normal(64) * 5
+    gl, bl = gdn_ref.layer_gates(x, x)
+    np.testing.assert_allclose(gl, -F.softplus(torch.from_numpy(x)).numpy(), rtol=1e-6)
+    np.testing.assert_allclose(bl, torch.sigmoid(torch.from_numpy(x)).numpy(), rtol=1e-6)
+
+
+def _layer_params(rng, E, Hk, Hv, dk, dv, scale_in=None):
+    C = 2 * Hk * dk + Hv * dv
+    rows = C + Hv * dv + 2 * Hv
+    w_in = _bf16_vals(rng.standard_normal((rows, E)) * (scale_in or 1.0 / math.sqrt(E)))
+    conv_w = _bf16_vals(rng.standard_normal((C, 4)) * 0.5)
+    gamma = _bf16_vals(rng.uniform(0.5, 1.5, dv))
+    w_out = _bf16_vals(rng.standard_normal((E, Hv * dv)) / math.sqrt(Hv * dv))
+    return w_in, conv_w, gamma, w_out
+
+
+def _both_layers(*args, **kw):
+    out_c, fin_c, cs_c, _ = oracle.layer_prefill(*args, **kw)
+    out_n, fin_n, cs_n = gdn_ref.layer_prefill(*args, **kw)
+    return (out_c, fin_c, cs_c), (out_n, fin_n, cs_n)
+
+
+def test_layer_single_token_closed_form():
+    """One token from a zero state and zero conv history, eps = 0: the state after the
+    token is beta v k^T, so o = scale beta (k.q) v, and the gated RMSNorm removes the
+    scalar up to its sign: y_h = sign(scale beta k.q) v_h / rms(v_h) * gamma * SiLU(z_h)."""
+    rng = np.random.default_rng(302)
+    E, Hk, Hv, dk, dv = 24, 1, 2, 4, 4
+    C = 2 * Hk * dk + Hv * dv
+    w_in, conv_w, gamma, w_out = _layer_params(rng, E, Hk, Hv, dk, dv, scale_in=0.4)
+    h = _bf16_vals(rng.standard_normal((1, E)))
+    cu = np.array([0, 1], np.int32)
+    proj = h @ w_in.T
+    x = gdn_ref.bf16_round(proj[0, :C])
+    z = gdn_ref.bf16_round(proj[0, C:C + Hv * dv]).reshape(Hv, dv)
+    beta = 1.0 / (1.0 + np.exp(-proj[0, C + Hv * dv + Hv:]))
+    u = x * conv_w[:, 3]                      # only the newest tap sees a nonzero input
+    act = u / (1.0 + np.exp(-u))
+    qv, kv, vv = act[:dk], act[dk:2 * dk], act[2 * dk:].reshape(Hv, dv)
+    scale = -0.75
+    kq = np.dot(kv, qv)                       # the key head is shared by both value heads
+    y = np.zeros((Hv, dv))
+    for hh in range(Hv):
+        s = np.sign(scale * beta[hh] * kq)
+        y[hh] = s * vv[hh] / np.sqrt(np.mean(vv[hh] ** 2)) * gamma * (z[hh] / (1.0 + np.exp(-z[hh])))
+    ref = gdn_ref.bf16_round(y.reshape(1, Hv * dv)) @ w_out.T
+    for out, fin, cs in _both_layers(h, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, scale=scale, l2_eps=0.0,
+                                     norm_eps=0.0):
+        np.testing.assert_allclose(out, ref, rtol=1e-9, atol=1e-12)
+        # final state beta v k^T / |k| (key-major), conv cache [0, 0, x]
+        kn = kv / np.linalg.norm(kv)
+        for hh in range(Hv):
+            np.testing.assert_allclose(fin[0, hh], beta[hh].astype(np.float32) * np.outer(kn, vv[hh]),
+                                       rtol=1e-6, atol=1e-12)
+        np.testing.assert_allclose(cs[0], np.stack([np.zeros(C), np.zeros(C), x]), atol=0)
+
+
+def _identity_layer_case(seed):
+    """Identity input projection, selecting output projection: the layer reduces to the
+    pinned conv prep, recurrence and gated RMSNorm on columns of the input, with the gates
+    from the library's softplus and logistic functions."""
+    rng = np.random.default_rng(seed)
+    Hk, Hv, dk, dv = 1, 2, 8, 8
+    C = 2 * Hk * dk + Hv * dv
+    E = C + Hv * dv + 2 * Hv
+    lengths = [5, 0, 9]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    h = _bf16_vals(rng.standard_normal((T, E)))
+    w_in = np.eye(E)
+    _, conv_w, gamma, _ = _layer_params(rng, E, Hk, Hv, dk, dv)
+    w_out = np.zeros((Hv * dv + 3, Hv * dv))
+    w_out[:Hv * dv] = np.eye(Hv * dv)
+    cs_in = _bf16_vals(rng.standard_normal((3, 3, C)))
+    s0 = _f32(rng.standard_normal((3, Hv, dk, dv)) * 0.2)
+    a_cols = torch.from_numpy(h[:, C + Hv * dv:C + Hv * dv + Hv])
+    b_cols = torch.from_numpy(h[:, C + Hv * dv + Hv:])
+    g = _f32(-F.softplus(a_cols).numpy())
+    beta = _f32(torch.sigmoid(b_cols).numpy())
+    q, k, v, cs_ref = oracle.prep(h[:, :C], conv_w, cu, Hk, Hv, dk, dv, cs_in=cs_in)
+    o, fin_ref = oracle.recurrence(q, k, v, g, beta, cu, s0=s0, scale=0.5)
+    y = oracle.gated_rmsnorm(o, h[:, C:C + Hv * dv].reshape(T, Hv, dv), gamma).reshape(T, Hv * dv)
+    args = (h, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv)
+    kw = dict(cs_in=cs_in, s0=s0, scale=0.5)
+    return args, kw, gdn_ref.bf16_round(y), fin_ref, cs_ref
+
+
+def test_layer_identity_projections_reduce_to_the_core():
+    args, kw, y_ref, fin_ref, cs_ref = _identity_layer_case(303)
+    n = y_ref.shape[1]
+    for out, fin, cs in _both_layers(*args, **kw):
+        np.testing.assert_allclose(out[:, :n], y_ref, rtol=1e-12, atol=1e-12)
+        assert np.all(out[:, n:] == 0.0)
+        np.testing.assert_allclose(fin, fin_ref, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(cs, cs_ref, atol=0)
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_layer_decode_continues_prefill(order):
+    """Prefill of L + 1 tokens = prefill of L tokens, then one decode step of the layer."""
+    rng = np.random.default_rng(304 + order)
+    E, Hk, Hv, dk, dv = 40, 1, 2, 8, 8
+    L = 6
+    w_in, conv_w, gamma, w_out = _layer_params(rng, E, Hk, Hv, dk, dv)
+    h = _bf16_vals(rng.standard_normal((L + 1, E)))
+    s0 = _f32(rng.standard_normal((1, Hv, dk, dv)) * 0.2)
+    kw = dict(scale=0.3, order=order)
+    full, fin_full, cs_full, _ = oracle.layer_prefill(h, w_in, conv_w, gamma, w_out, np.array([0, L + 1], np.int32),
+                                                      Hk, Hv, dk, dv, s0=s0, **kw)
+    part, fin_part, cs_part, _ = oracle.layer_prefill(h[:L], w_in, conv_w, gamma, w_out, np.array([0, L], np.int32),
+                                                      Hk, Hv, dk, dv, s0=s0, **kw)
+    for impl in (oracle.layer_decode, gdn_ref.layer_decode):
+        # the decode step takes the carried state as fp32 (the library's state type), so
+        # agreement is to fp32 rounding of that state
+        res = impl(h[L:], w_in, conv_w, gamma, w_out, cs_part, _f32(fin_part), Hk, Hv, dk, dv, **kw)
+        np.testing.assert_allclose(res[0], full[L:], rtol=2e-6, atol=1e-8)
+        np.testing.assert_allclose(res[1], fin_full, rtol=2e-6, atol=1e-8)
+        np.testing.assert_allclose(res[2], cs_full, atol=0)
+    np.testing.assert_allclose(part, full[:L], rtol=1e-12, atol=1e-14)
+
+
+def test_layer_c_matches_numpy_reference():
+    rng = np.random.default_rng(305)
+    E, Hk, Hv, dk, dv = 48, 2, 4, 8, 8
+    lengths = [7, 1, 12]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    w_in, conv_w, gamma, w_out = _layer_params(rng, E, Hk, Hv, dk, dv)
+    h = _bf16_vals(rng.standard_normal((sum(lengths), E)))
+    (oc, fc, cc), (on, fn, cn) = _both_layers(h, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, scale=0.7)
+    np.testing.assert_allclose(oc, on, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(fc, fn, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(cc, cn, atol=0)
+
+
+def test_layer_planted_mistakes_are_caught():
+    """Mutations of the layer's wiring (on the CPU) fail the pins above: v and z swapped
+    fails the single-token closed form; the gate columns swapped or the decay sign
+    flipped fails the identity-projection reduction (one token from a zero state never
+    sees the decay, and beta cancels in the norm, so those need several tokens)."""
+    rng = np.random.default_rng(306)
+    E, Hk, Hv, dk, dv = 24, 1, 2, 4, 4
+    w_in, conv_w, gamma, w_out = _layer_params(rng, E, Hk, Hv, dk, dv, scale_in=0.4)
+    h = _bf16_vals(rng.standard_normal((1, E)))
+    cu = np.array([0, 1], np.int32)
+    kw1 = dict(scale=1.0, l2_eps=0.0, norm_eps=0.0)
+    good1 = gdn_ref.layer_prefill(h, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, **kw1)[0]
+    args, kw, y_ref, _, _ = _identity_layer_case(307)
+    n = y_ref.shape[1]
+    np.testing.assert_allclose(gdn_ref.layer_prefill(*args, **kw)[0][:, :n], y_ref, rtol=1e-12, atol=1e-12)
+    split = gdn_ref.layer_split
+
+    def swapped_zv(proj, *a):
+        x, z, ga, gb = split(proj, *a)
+        C = x.shape[1]
+        x2 = np.concatenate([x[:, :C - z.shape[1]], z], axis=1)
+        return x2, x[:, C - z.shape[1]:], ga, gb
+
+    def swapped_gates(proj, *a):
+        x, z, ga, gb = split(proj, *a)
+        return x, z, gb, ga
+
+    def flipped_decay(a, b):
+        return (+gdn_ref.softplus(a)).astype(np.float32) * 0.1, gdn_ref.sigmoid(b).astype(np.float32)
+
+    for name, fn, single in [("layer_split", swapped_zv, True), ("layer_split", swapped_gates, False),
+                             ("layer_gates", flipped_decay, False)]:
+        saved = getattr(gdn_ref, name)
+        setattr(gdn_ref, name, fn)
+        try:
+            if single:
+                bad = gdn_ref.layer_prefill(h, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, **kw1)[0]
+                assert not np.allclose(bad, good1, rtol=1e-6), fn.__name__
+            else:
+                bad = gdn_ref.layer_prefill(*args, **kw)[0][:, :n]
+                assert not np.allclose(bad, y_ref, rtol=1e-6), fn.__name__
+        finally:
+            setattr(gdn_ref, name, saved)
+    # a transposed output projection does not even fit
+    with pytest.raises(ValueError):
+        gdn_ref.layer_prefill(h, w_in, conv_w, gamma, w_out.T.copy(), cu, Hk, Hv, dk, dv, **kw1)
