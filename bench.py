@@ -11,6 +11,12 @@ input:
       q, k, v never reach HBM)
   followed by one decode step of 256 sequences (gdn_decode_step, fp32 state in place).
 
+Reported beside it (not part of `value`): the whole linear-attention layer at the
+same shape with hidden size 1024 and random weights, gdn_layer_prefill (input
+projection, the prefill above, gated RMSNorm, output projection) and
+gdn_layer_decode for the 256 decode rows, under "layer", with torch's library GEMM
+(torch.mm) on the two projection shapes timed in the same region for context.
+
 `value` is prefill tokens/s: 4096 tokens over the event time of the gdn_prefill
 call, averaged over the timed steps; the decode part is reported under "decode"
 as tokens/s and state GB/s.  A second timed region runs the same prefill as
@@ -18,7 +24,8 @@ gdn_conv_qk_prep + gdn_chunk_prefill (reported under "prefill_two_call"), and a
 third through the split-phase entry points so that every kernel sits alone
 between two HIP events on the stream it is launched on; those per-kernel
 durations give "kernels" and "roofline" (the split region also times the gated
-RMSNorm epilogue, gdn_gated_rmsnorm, on the prefill output).  x, g and beta
+RMSNorm epilogue, gdn_gated_rmsnorm, on the prefill output, and the layer's input and
+output projections, gdn_in_proj and gdn_linear).  x, g and beta
 rotate over 3 copies at different addresses and the decode state over 2 sets
 (512 MiB), so no input is served from the 256 MB Infinity Cache; the prefill
 workspace is one buffer reused every step, as a caller reuses it, and its lines
@@ -43,6 +50,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA, TFLOP/s
 
 METRIC = "GDN prefill tokens/s + decode state GB/s (fraction of MI355X roofline)"
+LAYER_HIDDEN = 1024            # hidden size of the 0.8B model's layers
+# bench kernel name -> the profile's name for the kernel that call launches
+PROFILE_NAME = {"in_proj": "proj_256", "out_proj": "proj_128"}
 
 
 def algorithmic_counts(T, Hk, Hv, d, C, N, B):
@@ -185,6 +195,28 @@ def main():
     dz, dgam = dz_cpu.to(dev), dgam_cpu.to(dev)
     dout = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
 
+    # layer forward (hidden size 1024 of the 0.8B model): inputs rotated like x
+    E = LAYER_HIDDEN
+    Z = Hv * d
+    lw = inputs.layer_weights(7, E, Hk, Hv, d, d)
+    w_in, lcw, lgam, w_out = lw.w_in.to(dev), lw.conv_w.to(dev), lw.gamma.to(dev), lw.w_out.to(dev)
+    hs = [inputs.layer_hidden(8 + i, T, E).to(dev) for i in range(R)]
+    lout = torch.empty((T, E), dtype=torch.bfloat16, device=dev)
+    lcso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=dev)
+    lfin = torch.empty((N, Hv, d, d), dtype=torch.float32, device=dev)
+    lws = torch.empty(gdn.layer_prefill_workspace_size(T, N, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
+    dh = inputs.layer_hidden(11, B, E).to(dev)
+    dlout = torch.empty((B, E), dtype=torch.bfloat16, device=dev)
+    dlws = torch.empty(gdn.layer_decode_workspace_size(B, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
+    px = torch.empty((T, wl.conv_dim), dtype=torch.bfloat16, device=dev)
+    pz = torch.empty((T, Z), dtype=torch.bfloat16, device=dev)
+    pg = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    pb = torch.empty((T, Hv), dtype=torch.float32, device=dev)
+    nout.copy_(zg)            # defined values until the split region's gated RMSNorm writes it
+    ynorm = nout.view(T, Z)   # the gated RMSNorm's bf16 output feeds the output projection
+    pout = torch.empty((T, E), dtype=torch.bfloat16, device=dev)
+    lib_in = torch.empty((T, w_in.shape[0]), dtype=torch.bfloat16, device=dev)
+
     # Timed region 1 (the metric): one step = gdn_prefill (prep fused into the chunked
     # prefill, one call) + one decode step.
     def step(i, ev):
@@ -230,6 +262,26 @@ def main():
         gdn.decode_step_gated(dx, dcw, dcs[(i + 1) % Rd], dg, db, dstate[(i + 1) % Rd], dz, dgam, Hk, Hv, d, d,
                               out=dout)
         ev[7].record()
+        gdn.in_proj(hs[r], w_in, Hk, Hv, d, d, x=px, z=pz, g=pg, beta=pb)
+        ev[8].record()
+        gdn.linear(ynorm, w_out, y=pout)
+        ev[9].record()
+
+    # Timed region 3: the whole layer (prefill of the 4096 tokens, then one decode step
+    # of the 256 rows), and the library GEMM on the two projection shapes.
+    def step_layer(i, ev):
+        r = i % R
+        ev[0].record()
+        gdn.layer_prefill(hs[r], w_in, lcw, lgam, w_out, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=lcso,
+                          final_state=lfin, out=lout, workspace=lws)
+        ev[1].record()
+        gdn.layer_decode(dh, w_in, lcw, lgam, w_out, dcs[i % Rd], dstate[i % Rd], Hk, Hv, d, d, out=dlout,
+                         workspace=dlws)
+        ev[2].record()
+        torch.mm(hs[r], w_in.t(), out=lib_in)
+        ev[3].record()
+        torch.mm(ynorm, w_out.t(), out=pout)
+        ev[4].record()
 
     def events(n):
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -248,8 +300,10 @@ def main():
         torch.cuda.synchronize()
         return evs, time.perf_counter() - t0
 
-    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local", "gated_rmsnorm", "decode_gated"]
+    names = ["chunk_local_fused", "state_pass", "decode", "prep", "chunk_local", "gated_rmsnorm", "decode_gated",
+             "in_proj", "out_proj"]
     two_call = None
+    layer = None
     if not args.split_only:
         evs, wall = timed(step, 3)
         prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)
@@ -261,7 +315,14 @@ def main():
         two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
         two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,
                     "tokens_per_s": T / ((two_prep + two_call_ms) / 1e3)}
-    evs2, wall2 = timed(step_split, 8)
+        evs_l, _ = timed(step_layer, 5)
+        lp, ld, gi, go = (mean_ms(evs_l, j) for j in range(4))
+        layer = {"workload": f"linear-attention layer, hidden {E}, T={T} prefill + B={B} decode, random bf16 "
+                             "weights",
+                 "prefill_ms": lp, "prefill_tokens_per_s": T / (lp / 1e3),
+                 "decode_ms": ld, "decode_tokens_per_s": B / (ld / 1e3),
+                 "library_gemm_ms": {"in_proj": gi, "out_proj": go}}
+    evs2, wall2 = timed(step_split, 10)
     per = {n: mean_ms(evs2, j) for j, n in enumerate(names)}   # ms per launch (split phases)
     if args.split_only:   # profiler runs: the metric falls back to the split-phase prefill
         wall = wall2
@@ -271,6 +332,8 @@ def main():
     prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
     norm_b = T * Hv * d * (4 + 2 + 2) + d * 2   # y fp32 in, z bf16 in, out bf16, gain
     decg_b = dec_b - B * Hv * d * 4 + B * Hv * d * (2 + 2) + d * 2   # o fp32 replaced by z in, out bf16
+    in_f = 2 * T * E * w_in.shape[0]    # input projection: T x E times E x (conv_dim + Hv dv + 2 Hv)
+    out_f = 2 * T * Z * E               # output projection: T x Hv dv times Hv dv x E
     kern = {
         "chunk_local_fused": {"bound": "mfma", "achieved": local_f / per["chunk_local_fused"] / 1e9,
                               "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
@@ -284,12 +347,16 @@ def main():
                           "unit": "GB/s"},
         "decode_gated": {"bound": "hbm", "achieved": decg_b / per["decode_gated"] / 1e6, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s"},
+        "in_proj": {"bound": "mfma", "achieved": in_f / per["in_proj"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
+                    "unit": "TFLOP/s"},
+        "out_proj": {"bound": "mfma", "achieved": out_f / per["out_proj"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s"},
     }
     traffic = measured_traffic()   # HBM bytes per launch from the counter runs, or None
     for n in names:
         kern[n]["ms"] = per[n]
         kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
-        kern[n]["traffic"] = traffic.get(n)
+        kern[n]["traffic"] = traffic.get(PROFILE_NAME.get(n, n))
     dominant = max(["chunk_local_fused", "state_pass"], key=lambda n: per[n])   # the metric path's prefill
     roof = {key: kern[dominant][key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
@@ -315,6 +382,7 @@ def main():
                     "algorithmic_tflops": (local_f + state_f) / prefill_ms / 1e9,
                     "frac_mfma": (local_f + state_f) / prefill_ms / 1e9 / PEAK_MFMA_TFLOPS},
         "prefill_two_call": two_call,
+        "layer": layer,
         "decode": {"ms": decode_ms, "tokens_per_s": B / (decode_ms / 1e3),
                    "state_gb_per_s": dec_b / decode_ms / 1e6, "frac_hbm": dec_b / decode_ms / 1e6 / PEAK_HBM_GBS,
                    "bytes_per_step": dec_b},

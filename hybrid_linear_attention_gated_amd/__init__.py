@@ -11,6 +11,8 @@ computation runs in the library's HIP kernels; there is no fallback.
     o, final_state = chunk_prefill(q, k, v, g, beta, cu_seqlens, initial_state)
     o, final_state = prefill(x, conv_w, g, beta, Hk, Hv, dk, dv, cu_seqlens, ...)   # both in one call
     o = decode_step(x, conv_w, conv_state, g, beta, state, Hk, Hv, dk, dv)
+    out, final_state = layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, ...)
+    out = layer_decode(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, dk, dv)
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ import torch
 
 __all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_rmsnorm", "decode_step_gated", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
            "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
-           "LIB_PATH", "abi_version", "mfma_supported"]
+           "LIB_PATH", "abi_version", "mfma_supported", "linear", "in_proj", "layer_prefill", "layer_decode",
+           "layer_prefill_workspace_size", "layer_decode_workspace_size"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
@@ -66,6 +69,18 @@ def lib() -> ctypes.CDLL:
         L.gdn_gated_rmsnorm.restype = I
         L.gdn_decode_step.argtypes = [P, P, P, P, P, P, P, F, F, I, I, I, I, I, I, I, P]
         L.gdn_decode_step.restype = I
+        L.gdn_linear.argtypes = [P, P, P, I, I, I, P]
+        L.gdn_linear.restype = I
+        L.gdn_in_proj.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P]
+        L.gdn_in_proj.restype = I
+        L.gdn_layer_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
+        L.gdn_layer_prefill_workspace_size.restype = Z
+        L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
+        L.gdn_layer_prefill.restype = I
+        L.gdn_layer_decode_workspace_size.argtypes = [I, I, I, I, I]
+        L.gdn_layer_decode_workspace_size.restype = Z
+        L.gdn_layer_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
+        L.gdn_layer_decode.restype = I
         L.gdn_status_string.argtypes = [I]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -354,4 +369,123 @@ def gated_rmsnorm(y, z, gamma, eps=1e-6, out=None):
     st = lib().gdn_gated_rmsnorm(_p(y), _p(z), _p(gamma), _p(out), rows, dv, float(eps), _dt(z), _stream())
     if st != 0:
         raise GdnError("gdn_gated_rmsnorm", st)
+    return out
+
+
+# ------------------------------------------------------------------ layer forward
+
+def linear(a, w, y=None):
+    """y = a w^T on bf16 MFMA: a [M, K], w [N, K] bf16 (K % 64 == 0, N % 4 == 0);
+    returns y [M, N] bf16."""
+    bf = torch.bfloat16
+    _check(a, "a", bf)
+    _check(w, "w", bf)
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1]:
+        raise ValueError(f"a [M, K] and w [N, K] expected, got {tuple(a.shape)} and {tuple(w.shape)}")
+    M, K = a.shape
+    N = w.shape[0]
+    y = torch.empty((M, N), dtype=bf, device=a.device) if y is None else _check(y, "y", bf, (M, N))
+    st = lib().gdn_linear(_p(a), _p(w), _p(y), M, N, K, _stream())
+    if st != 0:
+        raise GdnError("gdn_linear", st)
+    return y
+
+
+def _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv):
+    bf = torch.bfloat16
+    C = 2 * Hk * dk + Hv * dv
+    _check(w_in, "w_in", bf, (C + Hv * dv + 2 * Hv, E))
+    if conv_w is not None:
+        _check(conv_w, "conv_w", bf, (C, 4))
+    if gamma is not None:
+        _check(gamma, "gamma", bf, (dv,))
+    if w_out is not None:
+        _check(w_out, "w_out", bf, (E, Hv * dv))
+    return C
+
+
+def in_proj(hidden, w_in, Hk, Hv, dk, dv, x=None, z=None, g=None, beta=None):
+    """The layer's input projection: hidden [T, E] bf16, w_in [conv_dim + Hv dv + 2 Hv, E]
+    bf16 (rows q|k|v, z, a, b).  Returns x [T, conv_dim] bf16, z [T, Hv dv] bf16,
+    g = -softplus(a) and beta = sigmoid(b) [T, Hv] fp32 (written into the given tensors
+    when passed)."""
+    _check(hidden, "hidden", torch.bfloat16)
+    T, E = hidden.shape
+    C = _layer_weights(w_in, None, None, None, E, Hk, Hv, dk, dv)
+    dev = hidden.device
+    bf, f32 = torch.bfloat16, torch.float32
+    x = torch.empty((T, C), dtype=bf, device=dev) if x is None else _check(x, "x", bf, (T, C))
+    z = torch.empty((T, Hv * dv), dtype=bf, device=dev) if z is None else _check(z, "z", bf, (T, Hv * dv))
+    g = torch.empty((T, Hv), dtype=f32, device=dev) if g is None else _check(g, "g", f32, (T, Hv))
+    beta = torch.empty((T, Hv), dtype=f32, device=dev) if beta is None else _check(beta, "beta", f32, (T, Hv))
+    st = lib().gdn_in_proj(_p(hidden), _p(w_in), _p(x), _p(z), _p(g), _p(beta), T, E, Hk, Hv, dk, dv, _stream())
+    if st != 0:
+        raise GdnError("gdn_in_proj", st)
+    return x, z, g, beta
+
+
+def layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) -> int:
+    return int(lib().gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv))
+
+
+def layer_decode_workspace_size(B, Hk, Hv, dk, dv) -> int:
+    return int(lib().gdn_layer_decode_workspace_size(B, Hk, Hv, dk, dv))
+
+
+def layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
+                  conv_state_out=None, initial_state=None, final_state=None, scale=1.0, l2_eps=1e-6,
+                  norm_eps=1e-6, output_final_state=True, out=None, workspace=None, order=0):
+    """The linear-attention layer over packed sequences: hidden [T, E] bf16 -> out [T, E]
+    bf16 (input projection, conv + SiLU + L2, gated delta rule, gated RMSNorm, output
+    projection).  Weights bf16: w_in [conv_dim + Hv dv + 2 Hv, E], conv_w [conv_dim, 4],
+    gamma [dv], w_out [E, Hv dv].  Caches as in `prefill`.  Returns (out, final_state)."""
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(hidden, "hidden", bf)
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [T, E]")
+    T, E = hidden.shape
+    C = _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv)
+    cu, N = _seqs(cu_seqlens, T)
+    _check(conv_state_in, "conv_state_in", bf, (N, 3, C), optional=True)
+    _check(conv_state_out, "conv_state_out", bf, (N, 3, C), optional=True)
+    _check(initial_state, "initial_state", f32, (N, Hv, dk, dv), optional=True)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, dk, dv), dtype=f32, device=hidden.device)
+    _check(final_state, "final_state", f32, (N, Hv, dk, dv), optional=True)
+    out = torch.empty((T, E), dtype=bf, device=hidden.device) if out is None else _check(out, "out", bf, (T, E))
+    need = layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    _check(workspace, "workspace")
+    st = lib().gdn_layer_prefill(_p(hidden), _p(w_in), _p(conv_w), _p(gamma), _p(w_out), _p(cu), N,
+                                 _p(conv_state_in), _p(conv_state_out), _p(initial_state), _p(final_state), _p(out),
+                                 float(scale), float(l2_eps), float(norm_eps), T, E, Hk, Hv, dk, dv, int(order),
+                                 _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_layer_prefill", st)
+    return out, final_state
+
+
+def layer_decode(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6,
+                 norm_eps=1e-6, out=None, workspace=None, order=0):
+    """One token per sequence through the layer: hidden [B, E] bf16 -> out [B, E] bf16;
+    conv_state [B, 3, conv_dim] bf16 and state [B, Hv, dk, dv] fp32 are updated in place."""
+    bf = torch.bfloat16
+    _check(hidden, "hidden", bf)
+    if hidden.dim() != 2:
+        raise ValueError("hidden must be [B, E]")
+    B, E = hidden.shape
+    C = _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv)
+    _check(conv_state, "conv_state", bf, (B, 3, C))
+    _check(state, "state", torch.float32, (B, Hv, dk, dv))
+    out = torch.empty((B, E), dtype=bf, device=hidden.device) if out is None else _check(out, "out", bf, (B, E))
+    need = layer_decode_workspace_size(B, Hk, Hv, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    _check(workspace, "workspace")
+    st = lib().gdn_layer_decode(_p(hidden), _p(w_in), _p(conv_w), _p(gamma), _p(w_out), _p(conv_state), _p(state),
+                                _p(out), float(scale), float(l2_eps), float(norm_eps), B, E, Hk, Hv, dk, dv,
+                                int(order), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st != 0:
+        raise GdnError("gdn_layer_decode", st)
     return out

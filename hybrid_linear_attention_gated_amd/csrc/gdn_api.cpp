@@ -331,4 +331,212 @@ int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *ou
     }
 }
 
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Host checks shared by the projections: K a positive multiple of 64 (two MFMA k-steps
+// per LDS stage), output row lengths multiples of 4 (8-byte stores of 4 bf16).
+bool proj_shape_ok(int M, int N, int K) { return M >= 0 && N > 0 && N % 4 == 0 && K > 0 && K % 64 == 0; }
+
+int in_proj_impl(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta, int T, int E,
+                 int Hk, int Hv, int dk, int dv, hipStream_t st) {
+    const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+    gdn::ProjArgs a{hidden, w_in, T, (int)(C + Z), E, x, (int)C, (int)C, z, (int)Z};
+    a.g = g;
+    a.beta = beta;
+    a.heads = Hv;
+    return hip_status(gdn::launch_proj(a, st));
+}
+
+int linear_impl(const void *a, const void *w, void *y, int M, int N, int K, hipStream_t st) {
+    gdn::ProjArgs p{a, w, M, N, K, y, N, N, nullptr, 0};
+    return hip_status(gdn::launch_proj(p, st));
+}
+
+// Shapes the layer entry points accept: the projections' k extents (E and Hv dv) are
+// multiples of 64, the gate columns fit the gate workgroups, and dk, dv are 16-multiples.
+int check_layer_shape(int E, int Hk, int Hv, int dk, int dv) {
+    if (int e = check_heads(Hk, Hv)) return e;
+    if (E <= 0) return GDN_ERR_BAD_SHAPE;
+    if (E % 64 != 0 || ((size_t)Hv * dv) % 64 != 0 || !gdn::proj_gates_supported(Hv)) return GDN_ERR_UNSUPPORTED;
+    if (dk % 16 != 0 || dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
+    return GDN_OK;
+}
+
+struct LayerWs {
+    size_t x, z, g, beta, o, core, total;
+};
+
+LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
+    const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+    LayerWs w{};
+    w.x = 0;
+    w.z = w.x + align256((size_t)T * C * 2);
+    w.g = w.z + align256((size_t)T * Z * 2);
+    w.beta = w.g + align256((size_t)T * Hv * 4);
+    w.o = w.beta + align256((size_t)T * Hv * 4);
+    w.core = w.o + align256((size_t)T * Z * 4);
+    w.total = w.core + align256(gdn::chunked_workspace_bytes(T, N, Hv, dk, dv));
+    return w;
+}
+
+struct LayerDecodeWs {
+    size_t x, z, g, beta, y, total;
+};
+
+LayerDecodeWs layer_decode_ws(int B, int Hk, int Hv, int dk, int dv) {
+    const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+    LayerDecodeWs w{};
+    w.x = 0;
+    w.z = w.x + align256((size_t)B * C * 2);
+    w.g = w.z + align256((size_t)B * Z * 2);
+    w.beta = w.g + align256((size_t)B * Hv * 4);
+    w.y = w.beta + align256((size_t)B * Hv * 4);
+    w.total = w.y + align256((size_t)B * Z * 2);
+    return w;
+}
+
+}  // namespace
+
+int gdn_linear(const void *a, const void *w, void *y, int M, int N, int K, void *stream) {
+    try {
+        if (!proj_shape_ok(M, N, K)) return M < 0 || N <= 0 || K <= 0 ? GDN_ERR_BAD_SHAPE : GDN_ERR_UNSUPPORTED;
+        if (!w || (M > 0 && (!a || !y))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({a, w, y})) return GDN_ERR_ALIGN;
+        const Range ra{a, (size_t)M * K * 2}, rw{w, (size_t)N * K * 2}, ry{y, (size_t)M * N * 2};
+        if (overlap(ry, ra) || overlap(ry, rw)) return GDN_ERR_ALIAS;
+        return linear_impl(a, w, y, M, N, K, (hipStream_t)stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta, int T, int E,
+                int Hk, int Hv, int dk, int dv, void *stream) {
+    try {
+        if (T < 0) return GDN_ERR_BAD_SHAPE;
+        if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
+        if (!w_in || (T > 0 && (!hidden || !x || !z || !g || !beta))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({hidden, w_in, x, z, g, beta})) return GDN_ERR_ALIGN;
+        const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+        const Range rh{hidden, (size_t)T * E * 2}, rw{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
+            rx{x, (size_t)T * C * 2}, rz{z, (size_t)T * Z * 2}, rg{g, (size_t)T * Hv * 4}, rb{beta, rg.bytes};
+        const Range outs[] = {rx, rz, rg, rb};
+        for (int i = 0; i < 4; ++i) {
+            if (overlap(outs[i], rh) || overlap(outs[i], rw)) return GDN_ERR_ALIAS;
+            for (int j = i + 1; j < 4; ++j)
+                if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+        }
+        return in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, (hipStream_t)stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+size_t gdn_layer_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv) {
+    if (T < 0 || N < 1 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !gdn::chunked_supported(dk, dv)) return 0;
+    return layer_ws(T, N, Hk, Hv, dk, dv).total;
+}
+
+int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
+                      const void *w_out, const int32_t *cu_seqlens, int N, const void *conv_state_in,
+                      void *conv_state_out, const float *initial_state, float *final_state, void *out, float scale,
+                      float l2_eps, float norm_eps, int T, int E, int Hk, int Hv, int dk, int dv, int order,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    try {
+        if (int e = check_seqs(cu_seqlens, N, T)) return e;
+        if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
+        if (!gdn::chunked_supported(dk, dv) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
+        if (!w_in || !conv_w || !gamma || !w_out || (T > 0 && (!hidden || !out))) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({hidden, w_in, conv_w, gamma, w_out, cu_seqlens, conv_state_in, conv_state_out,
+                        initial_state, final_state, out, workspace}))
+            return GDN_ERR_ALIGN;
+        if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
+            !std::isfinite(norm_eps))
+            return GDN_ERR_BAD_SHAPE;
+        const LayerWs L = layer_ws(T, N, Hk, Hv, dk, dv);
+        if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+        const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+        const size_t st_bytes = (size_t)N * Hv * dk * dv * 4, cs_bytes = (size_t)N * 3 * C * 2;
+        const Range rh{hidden, (size_t)T * E * 2}, rwi{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
+            rcw{conv_w, C * 4 * 2}, rgm{gamma, (size_t)dv * 2}, rwo{w_out, (size_t)E * Z * 2},
+            rci{conv_state_in, cs_bytes}, rco{conv_state_out, cs_bytes}, rs0{initial_state, st_bytes},
+            rsf{final_state, st_bytes}, rout{out, (size_t)T * E * 2}, rws{workspace, L.total};
+        for (Range in : {rh, rwi, rcw, rgm, rwo, rci, rco, rs0, rsf, rout})
+            if (overlap(rws, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rh, rwi, rcw, rgm, rwo, rci, rco, rs0, rsf})
+            if (overlap(rout, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rh, rwi, rcw, rgm, rwo, rs0})
+            if (overlap(rco, in) || overlap(rsf, in)) return GDN_ERR_ALIAS;
+        if (overlap(rco, rsf) || bad_partial_alias(rco, rci) || bad_partial_alias(rsf, rs0) || overlap(rsf, rci))
+            return GDN_ERR_ALIAS;
+        char *ws = static_cast<char *>(workspace);
+        void *x = ws + L.x, *z = ws + L.z;
+        float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
+        float *o = reinterpret_cast<float *>(ws + L.o);
+        hipStream_t st = (hipStream_t)stream;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st)) return e;
+        if (int e = prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
+                                 final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_BF16, order, ws + L.core,
+                                 L.total - L.core, stream, 3))
+            return e;
+        // the normalised output replaces z (bf16) in place, then feeds the output projection
+        gdn::NormArgs na{o, z, gamma, z, (long)T * Hv, dv, norm_eps, true};
+        if (T > 0)
+            if (int e = hip_status(gdn::launch_gated_rmsnorm(na, st))) return e;
+        return linear_impl(z, w_out, out, T, E, (int)Z, st);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
+size_t gdn_layer_decode_workspace_size(int B, int Hk, int Hv, int dk, int dv) {
+    if (B < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return 0;
+    return layer_decode_ws(B, Hk, Hv, dk, dv).total;
+}
+
+int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
+                     const void *w_out, void *conv_state, float *state, void *out, float scale, float l2_eps,
+                     float norm_eps, int B, int E, int Hk, int Hv, int dk, int dv, int order, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+    try {
+        if (B < 0) return GDN_ERR_BAD_SHAPE;
+        if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
+        if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
+        if (!w_in || !conv_w || !gamma || !w_out || (B > 0 && (!hidden || !conv_state || !state || !out)))
+            return GDN_ERR_NULL_POINTER;
+        if (!aligned16({hidden, w_in, conv_w, gamma, w_out, conv_state, state, out, workspace})) return GDN_ERR_ALIGN;
+        if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
+            !std::isfinite(norm_eps))
+            return GDN_ERR_BAD_SHAPE;
+        const LayerDecodeWs L = layer_decode_ws(B, Hk, Hv, dk, dv);
+        if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
+        const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
+        const Range rh{hidden, (size_t)B * E * 2}, rwi{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
+            rcw{conv_w, C * 4 * 2}, rgm{gamma, (size_t)dv * 2}, rwo{w_out, (size_t)E * Z * 2},
+            rcs{conv_state, (size_t)B * 3 * C * 2}, rst{state, (size_t)B * Hv * dk * dv * 4},
+            rout{out, (size_t)B * E * 2}, rws{workspace, L.total};
+        for (Range in : {rh, rwi, rcw, rgm, rwo, rcs, rst, rout})
+            if (overlap(rws, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rh, rwi, rcw, rgm, rwo, rcs, rst})
+            if (overlap(rout, in)) return GDN_ERR_ALIAS;
+        for (Range in : {rh, rwi, rcw, rgm, rwo})
+            if (overlap(rcs, in) || overlap(rst, in)) return GDN_ERR_ALIAS;
+        if (overlap(rcs, rst)) return GDN_ERR_ALIAS;
+        char *ws = static_cast<char *>(workspace);
+        void *x = ws + L.x, *z = ws + L.z, *y = ws + L.y;
+        float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
+        hipStream_t st = (hipStream_t)stream;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, B, E, Hk, Hv, dk, dv, st)) return e;
+        if (int e = decode_impl(x, conv_w, conv_state, g, beta, state, nullptr, z, gamma, y, scale, l2_eps,
+                                norm_eps, B, Hk, Hv, dk, dv, GDN_BF16, order, stream))
+            return e;
+        return linear_impl(y, w_out, out, B, E, (int)Z, st);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
+}
+
 }  // extern "C"

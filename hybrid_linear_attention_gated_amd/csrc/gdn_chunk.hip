@@ -1345,8 +1345,8 @@ size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
 // pool of events, created on first use and kept for the life of the process.
 constexpr int kMaxSegments = 16;
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
     static std::mutex mu;
     static int cus[64] = {};
     int dev = 0;

@@ -74,12 +74,33 @@ struct NormArgs {
     bool bf16;   // element type of z / gamma / out
 };
 
+// y = a w^T on bf16 MFMA (a [M][K], w [N + 2 heads][K], bf16): columns n < n_split go to
+// y0[m][n] (row length ld0), the others to y1[m][n - n_split] (row length ld1); with
+// heads > 0 the 2 heads rows of w after row N give g[m][h] = -softplus and
+// beta[m][h] = sigmoid of their products.  K % 64 == 0, N % 4 == 0, 2 heads <= 64.
+struct ProjArgs {
+    const void *a, *w;
+    int M, N, K;
+    void *y0;
+    int ld0, n_split;
+    void *y1;
+    int ld1;
+    float *g = nullptr, *beta = nullptr;
+    int heads = 0;
+    int tiles_m = 0, tiles_n = 0, ntiles = 0;   // set by the launcher
+};
+
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
 // conv_state_out[s] = last three inputs of sequence s (a launch of its own)
 hipError_t launch_conv_state_out(const PrepArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 // gated RMSNorm epilogue over rows of dv channels (dv in {16, 32, 64, 128, 256})
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st);
+
+hipError_t launch_proj(const ProjArgs &a, hipStream_t st);
+bool proj_gates_supported(int heads);
+// compute units of the current device (cached per device; 0 if unknown)
+int device_cus();
 
 // token-recurrent fp32 path (GDN_F32 and the small head dims)
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, hipStream_t st);

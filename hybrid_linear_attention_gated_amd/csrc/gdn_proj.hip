@@ -1,0 +1,333 @@
+// gdn_proj.hip -- the linear-attention layer's projections on bf16 MFMA:
+//
+//   y[m][n] = sum_k a[m][k] w[n][k]     (w stored as a linear layer stores its weight)
+//
+// "7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2: a bias-free input
+// projection of the layer input gives the pre-conv q|k|v, the output gate z and the
+// two gate pre-activations per value head; the gated RMSNorm's output passes a
+// bias-free output projection.  The input projection's epilogue splits its columns
+// into x (q|k|v, bf16), z (bf16), g = -softplus(a) and beta = sigmoid(b) (fp32): the
+// maps that turn the gate pre-activations into a log-decay and an update gate.
+//
+// Design (dense contraction: MFMA-bound at these shapes, K = 1024 or 2048):
+//  - One 256-thread workgroup (4 waves, 2 x 2) per output tile; a wave owns a
+//    WM x WN block: WM = WN = 128 (tile 256 x 256, 256 fp32 accumulators per lane in
+//    the accumulator registers) when there are enough tiles to fill the chip, else
+//    WM = WN = 64 (tile 128 x 128).
+//  - 32 x 32 x 16 MFMAs.  The weight rows are the A operand and the activation rows
+//    the B operand, so a lane's accumulator holds runs of 4 consecutive output
+//    columns of one row: 8-byte stores.  Both operands are k-contiguous rows, so a
+//    lane's fragment (8 consecutive k of one row) is one 16-byte LDS read, and one
+//    k-step's fragments (8 reads for 16 MFMAs in the large tile) are small enough to
+//    double-buffer beside 256 accumulators.
+//  - k advances BK at a time (64 for the large tile, 128 for the small one when K
+//    allows) through two LDS stages: every thread loads its share of the next stage
+//    into registers with buffer loads (rows past the matrix edge read as zeros), the
+//    loads in flight during the stage's MFMAs, writes it to the other stage after
+//    them, and one barrier per stage orders everything.  The loop body has no branch;
+//    the fragments of k-step s + 1 are read from LDS between the MFMAs of step s (one
+//    read per group of MFMAs, by scheduling hints), so with one wave per SIMD the
+//    matrix unit does not wait on LDS.  The 16-byte chunks of an LDS row are
+//    XOR-swizzled by the row index, so the eight rows that one LDS read cycle serves
+//    hit eight different bank groups.
+//  - Tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs in
+//    turn) takes a contiguous run of tiles in which groups of four row tiles share
+//    column tiles: the tiles resident on one XCD at a time reuse each other's rows
+//    from its L2.
+//  - The gate columns (2 Hv of them) are left out of the tile grid: after the tiles,
+//    workgroups of 16 rows each split k over their four waves, sum the partial
+//    products through LDS and apply the gate maps.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+constexpr int kProjThreads = 256;
+constexpr int kGateRows = 16;        // rows per gate workgroup
+constexpr int kGateMaxTiles = 4;     // 16-column tiles of gate outputs: 2 Hv <= 64
+constexpr int kGateBatch = 8;        // k-steps per wave whose loads are in flight together
+constexpr int kTileGroup = 4;        // row tiles that share a run of column tiles
+
+template <int WM, int WN, int BK>
+struct ProjTile {
+    static constexpr int BM = 2 * WM, BN = 2 * WN;
+    static constexpr int MT = WM / 32, NT = WN / 32;     // 32 x 32 MFMA blocks per wave
+    static constexpr int ROWB = BK * 2;                  // LDS bytes per row (one k stage)
+    static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+    static constexpr int RPP = kProjThreads / CPR;       // rows one pass of the threads stages
+    static constexpr int A_BYTES = BM * ROWB, W_BYTES = BN * ROWB;
+    static constexpr int STAGE = A_BYTES + W_BYTES;
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int A_LD = BM / RPP, W_LD = BN / RPP;   // 16-byte chunks per thread and stage
+    static constexpr int KSTEPS = BK / 16;               // MFMA k-steps of 16 per stage
+    static_assert(LDS >= (kProjThreads / kWave - 1) * kGateMaxTiles * kWave * 16, "gate partial sums fit");
+};
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D += A B with A 32 x 16, B 16 x 32 (bf16), D 32 x 32 (fp32): lane l holds
+// A[l % 32][8 (l / 32) + v] and B[8 (l / 32) + v][l % 32] for v < 8, and
+// D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32] for v < 16.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Byte offset of 16-byte chunk c of LDS row `row`: the chunk index is XORed with the
+// row's low three bits, so eight consecutive rows read at one chunk index fall into
+// eight different 16-byte bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ bf16x8 zero8() {
+    bf16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.f;
+    return z;
+}
+
+__device__ __forceinline__ void store_bf16x4(bf16 *p, f32x4 v) {
+    bf16x4 o;
+    o[0] = (bf16)v[0]; o[1] = (bf16)v[1]; o[2] = (bf16)v[2]; o[3] = (bf16)v[3];
+    *reinterpret_cast<bf16x4 *>(p) = o;
+}
+
+// log(1 + e^x) in fp32: x itself beyond 20 (e^-20 is below fp32 resolution there),
+// else log1p(e^x), accurate also far to the left where it tends to e^x.
+__device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.f / (1.f + expf(-x)); }
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over the rows [r0, rows) of a [rows][K] bf16 matrix: loads past the
+// last row return zeros (the hardware's range check), which pads the tile edges.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16 *base, int r0, int rows, int K) {
+    const long bytes = (long)max(rows - r0, 0) * K * 2;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16 *>(base + (size_t)r0 * K), (short)0,
+                                             (int)min(bytes, (long)0x7fffffff), 0x00020000);
+}
+
+// One output tile: rows m0.., columns n0.. of the main (non-gate) columns.
+template <int WM, int WN, int BK>
+__device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, char *smem) {
+    using S = ProjTile<WM, WN, BK>;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = tm * S::BM, n0 = tn * S::BN;
+    const int K = p.K, M = p.M, N = p.N;
+    const __amdgpu_buffer_rsrc_t ra_src = rows_rsrc(static_cast<const bf16 *>(p.a), m0, M, K);
+    const __amdgpu_buffer_rsrc_t rw_src = rows_rsrc(static_cast<const bf16 *>(p.w), n0, N, K);
+
+    // staging: thread tid moves chunk tid % CPR of rows tid / CPR + RPP i
+    const int crow = tid / S::CPR, cc = tid % S::CPR;
+    const int voff = crow * K * 2 + cc * 16;
+    u32x4 ra[S::A_LD], rw[S::W_LD];
+    auto gload = [&](int kt) {
+        const int vo = voff + kt * S::ROWB;
+#pragma unroll
+        for (int i = 0; i < S::A_LD; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
+#pragma unroll
+        for (int i = 0; i < S::W_LD; ++i) rw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw_src, vo, i * S::RPP * K * 2, 0);
+    };
+    auto swrite = [&](int buf) {
+        char *sa = smem + buf * S::STAGE, *sw = sa + S::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < S::A_LD; ++i) *reinterpret_cast<u32x4 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < S::W_LD; ++i) *reinterpret_cast<u32x4 *>(sw + swz<S::ROWB>(crow + S::RPP * i, cc)) = rw[i];
+    };
+
+    f32x16 acc[S::NT][S::MT];
+#pragma unroll
+    for (int i = 0; i < S::NT; ++i)
+#pragma unroll
+        for (int j = 0; j < S::MT; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int arow = wm * WM + (lane & 31), wrow = wn * WN + (lane & 31);
+    // fragments of one k-step of 16: lane holds 8 consecutive k of its row
+    struct Frags {
+        bf16x8 a[S::MT], w[S::NT];
+    };
+    auto fread = [&](int buf, int s, Frags &f) {
+        const char *sa = smem + buf * S::STAGE, *sw = sa + S::A_BYTES;
+        const int c = s * 2 + (lane >> 5);
+#pragma unroll
+        for (int j = 0; j < S::MT; ++j) f.a[j] = *reinterpret_cast<const bf16x8 *>(sa + swz<S::ROWB>(arow + 32 * j, c));
+#pragma unroll
+        for (int i = 0; i < S::NT; ++i) f.w[i] = *reinterpret_cast<const bf16x8 *>(sw + swz<S::ROWB>(wrow + 32 * i, c));
+    };
+    auto mfmas = [&](const Frags &f) {
+#pragma unroll
+        for (int i = 0; i < S::NT; ++i)
+#pragma unroll
+            for (int j = 0; j < S::MT; ++j) acc[i][j] = mfma32(f.w[i], f.a[j], acc[i][j]);
+    };
+    constexpr int FR = S::MT + S::NT;              // fragment reads per k-step
+    constexpr int MF = S::MT * S::NT;              // MFMAs per k-step
+    constexpr int PER = MF / FR > 0 ? MF / FR : 1; // MFMAs between two reads of the next step
+
+    constexpr int NW = S::A_LD + S::W_LD;          // staging loads (and LDS writes) per stage
+    constexpr int W_EACH = NW > MF ? NW / MF : 1;  // LDS writes per group in the last step
+    constexpr int M_EACH = MF > NW ? MF / NW : 1;  // MFMAs per group in the last step
+    static_assert(MF % FR == 0 || FR % MF == 0, "read / MFMA interleave");
+    static_assert((NW > MF ? NW % MF : MF % NW) == 0, "write / MFMA interleave");
+
+    const int KT = K / BK;
+    gload(0);
+    swrite(0);
+    __syncthreads();
+    // Branch-free stage loop (the last stage reloads itself into the idle buffer), in the
+    // order the scheduling groups below fix: step 0's fragment reads, the next stage's
+    // global loads, then each step's MFMAs with the next step's reads between them, and
+    // the staging writes between the last step's MFMAs (by then the loads have had the
+    // stage's other MFMAs to arrive).
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        Frags f0, f1;
+        fread(buf, 0, f0);
+        gload(min(kt + 1, KT - 1));
+#pragma unroll
+        for (int s = 0; s < S::KSTEPS; ++s) {
+            Frags &cur = (s & 1) ? f1 : f0;
+            Frags &nxt = (s & 1) ? f0 : f1;
+            if (s + 1 < S::KSTEPS) fread(buf, s + 1, nxt);
+            mfmas(cur);
+        }
+        swrite(buf ^ 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);    // DS reads of step 0
+        __builtin_amdgcn_sched_group_barrier(0x020, NW, 0);    // VMEM reads of the next stage
+#pragma unroll
+        for (int s = 0; s + 1 < S::KSTEPS; ++s) {
+#pragma unroll
+            for (int g = 0; g < FR; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read (step s + 1)
+                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // MFMA (step s)
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < (NW > MF ? MF : NW); ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x200, W_EACH, 0);  // DS write
+            __builtin_amdgcn_sched_group_barrier(0x008, M_EACH, 0);  // MFMA (last step)
+        }
+        __syncthreads();
+    }
+
+    // lane holds y[m][n + 8 g + 4 (lane / 32) + 0..3] of each 32 x 32 block, g < 4
+#pragma unroll
+    for (int j = 0; j < S::MT; ++j) {
+        const int m = m0 + wm * WM + 32 * j + (lane & 31);
+        if (m >= M) continue;
+#pragma unroll
+        for (int i = 0; i < S::NT; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * WN + 32 * i + 8 * g + 4 * (lane >> 5);
+                if (n >= N) continue;
+                bf16 *dst = n < p.n_split ? static_cast<bf16 *>(p.y0) + (size_t)m * p.ld0 + n
+                                          : static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split);
+                store_bf16x4(dst, f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                        acc[i][j][4 * g + 3]});
+            }
+        }
+    }
+}
+
+// Gate outputs of rows r0 .. r0 + 15: the 2 Hv gate rows of w start at row N.  Wave
+// `wave` takes the k-steps wave, wave + 4, ...; partial sums meet in LDS.
+__device__ __forceinline__ void gate_rows(const ProjArgs &p, int gb, char *smem) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int r0 = gb * kGateRows, K = p.K, KS = K / 32, G = 2 * p.heads;
+    const int m = r0 + (lane & 15), kc = 8 * (lane >> 4);
+    const bf16 *w = static_cast<const bf16 *>(p.w);
+    const bf16 *arow = static_cast<const bf16 *>(p.a) + (size_t)min(m, p.M - 1) * K + kc;
+    const bool mok = m < p.M;
+    f32x4 acc[kGateMaxTiles];
+#pragma unroll
+    for (int i = 0; i < kGateMaxTiles; ++i) acc[i] = zero4();
+    for (int base = 0; base < KS; base += 4 * kGateBatch) {
+        bf16x8 af[kGateBatch], wf[kGateBatch][kGateMaxTiles];
+#pragma unroll
+        for (int b = 0; b < kGateBatch; ++b) {
+            const int ks = base + wave + 4 * b;
+            const bool kok = ks < KS;
+            af[b] = kok && mok ? *reinterpret_cast<const bf16x8 *>(arow + ks * 32) : zero8();
+#pragma unroll
+            for (int i = 0; i < kGateMaxTiles; ++i) {
+                const int gi = 16 * i + (lane & 15);
+                wf[b][i] = kok && gi < G
+                               ? *reinterpret_cast<const bf16x8 *>(w + (size_t)(p.N + gi) * K + kc + ks * 32)
+                               : zero8();
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < kGateBatch; ++b)
+#pragma unroll
+            for (int i = 0; i < kGateMaxTiles; ++i) acc[i] = mfma16(wf[b][i], af[b], acc[i]);
+    }
+    f32x4 *part = reinterpret_cast<f32x4 *>(smem);
+    if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < kGateMaxTiles; ++i) part[((wave - 1) * kGateMaxTiles + i) * kWave + lane] = acc[i];
+    }
+    __syncthreads();
+    if (wave != 0 || !mok) return;
+#pragma unroll
+    for (int i = 0; i < kGateMaxTiles; ++i) {
+#pragma unroll
+        for (int v = 1; v < kProjThreads / kWave; ++v) acc[i] += part[((v - 1) * kGateMaxTiles + i) * kWave + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int gi = 16 * i + 4 * (lane >> 4) + r;
+            if (gi < p.heads) p.g[(size_t)m * p.heads + gi] = -softplus_f32(acc[i][r]);
+            else if (gi < G) p.beta[(size_t)m * p.heads + (gi - p.heads)] = sigmoid_f32(acc[i][r]);
+        }
+    }
+}
+
+template <int WM, int WN, int BK>
+__global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
+    using S = ProjTile<WM, WN, BK>;
+    __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+    int b = blockIdx.x;
+    if (b >= p.ntiles) {
+        gate_rows(p, b - p.ntiles, smem);
+        return;
+    }
+    // XCD x (blocks x, x + 8, ...) takes tiles [x T / 8, (x + 1) T / 8)
+    if ((p.ntiles & 7) == 0) b = (b & 7) * (p.ntiles >> 3) + (b >> 3);
+    // groups of kTileGroup row tiles run over all column tiles, row tile fastest
+    const int per_group = kTileGroup * p.tiles_n;
+    const int grp = b / per_group, first = grp * kTileGroup;
+    const int gm = min(kTileGroup, p.tiles_m - first);
+    const int r = b - grp * per_group;
+    proj_tile<WM, WN, BK>(p, first + r % gm, r / gm, smem);
+}
+
+template <int WM, int WN, int BK>
+static hipError_t launch_proj_t(ProjArgs p, hipStream_t st) {
+    using S = ProjTile<WM, WN, BK>;
+    p.tiles_m = (p.M + S::BM - 1) / S::BM;
+    p.tiles_n = (p.N + S::BN - 1) / S::BN;
+    p.ntiles = p.tiles_m * p.tiles_n;
+    const int gate_blocks = p.heads > 0 ? (p.M + kGateRows - 1) / kGateRows : 0;
+    const long blocks = (long)p.ntiles + gate_blocks;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((proj_kernel<WM, WN, BK>), dim3((unsigned)blocks), dim3(kProjThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+bool proj_gates_supported(int heads) { return 2 * heads <= 16 * kGateMaxTiles; }
+
+hipError_t launch_proj(const ProjArgs &a, hipStream_t st) {
+    if (a.M <= 0) return hipSuccess;
+    // large tiles when they alone fill the compute units
+    const long big = (long)((a.M + 255) / 256) * ((a.N + 255) / 256);
+    const int cus = device_cus();
+    if (big >= (cus > 0 ? cus : 256)) return launch_proj_t<128, 128, 64>(a, st);
+    // small tiles take k 128 deep per stage when K allows, so a stage's MFMAs outlast its loads
+    return a.K % 128 == 0 ? launch_proj_t<64, 64, 128>(a, st) : launch_proj_t<64, 64, 64>(a, st);
+}
+
+}  // namespace gdn

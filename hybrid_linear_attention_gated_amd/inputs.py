@@ -21,6 +21,11 @@ standard deviation); beta = sigmoid(N(0,1)); log-decay g = -softplus(N(0,1)),
 or g = log(a) with a ~ U(0.9, 1.0) where the workload says so.  Gated RMSNorm
 epilogue: gate z ~ N(0, 1), per-channel gain gamma = 1 + N(0, 0.1); standalone
 norm rows y ~ N(0, 1) times a per-row scale 10^U(-3, 2).
+Layer forward (input projection -> core -> gated RMSNorm -> output projection, at the
+0.8B layer widths of section 7.6.1: hidden 1024): hidden ~ N(0, 1); input projection
+weight ~ N(0, 1/E) and output projection weight ~ N(0, 1/(Hv dv)), so every projected
+value is ~N(0, 1) like the pre-conv x and the gate pre-activations of the core
+workloads; conv weights, gain and caches as above.
 Generator: numpy PCG64(1234 + index).
 """
 from __future__ import annotations
@@ -43,7 +48,7 @@ def _normal_f32(rng, shape, std=1.0):
     """N(0, std^2) draws in float32, generated in row blocks (same stream as one draw)."""
     shape = tuple(int(s) for s in shape)
     out = np.empty(shape, dtype=np.float32)
-    flat = out.reshape(shape[0], -1) if len(shape) > 1 else out.reshape(-1, 1)
+    flat = out.reshape(shape[0], int(np.prod(shape[1:]))) if len(shape) > 1 else out.reshape(-1, 1)
     for r0 in range(0, flat.shape[0], _BLOCK_ROWS):
         r1 = min(r0 + _BLOCK_ROWS, flat.shape[0])
         flat[r0:r1] = rng.standard_normal((r1 - r0, flat.shape[1]), dtype=np.float32)
@@ -231,3 +236,51 @@ def norm_rows(index: int, rows: int, dv: int) -> torch.Tensor:
     rng = _rng(index)
     y = rng.standard_normal((rows, dv)) * (10.0 ** rng.uniform(-3.0, 2.0, (rows, 1)))
     return _f32(y)
+
+
+@dataclass
+class LayerWeights:
+    """bf16 weights of one linear-attention layer (stored as a linear layer stores them)."""
+    w_in: torch.Tensor      # [conv_dim + Hv dv + 2 Hv, E]: rows q|k|v, z, a, b
+    conv_w: torch.Tensor    # [conv_dim, 4]
+    gamma: torch.Tensor     # [dv], the gain as applied
+    w_out: torch.Tensor     # [E, Hv dv]
+
+
+def _on_grid(a: np.ndarray, step: float, bound: float) -> np.ndarray:
+    """Draws moved to the nearest multiple of `step` and clipped to [-bound, bound]."""
+    return (np.clip(np.rint(a / step), -bound / step, bound / step) * step).astype(np.float32)
+
+
+def layer_weights(index: int, E: int, Hk: int, Hv: int, dk: int, dv: int, exact: bool = False) -> LayerWeights:
+    """exact: the input projection weight on multiples of 2^-6 in [-1/2, 1/2] (see
+    layer_hidden), so that with a grid input every projected value is exact in fp32."""
+    rng = _rng(index)
+    C = 2 * Hk * dk + Hv * dv
+    w_in = _normal_f32(rng, (C + Hv * dv + 2 * Hv, E), std=1.0 / np.sqrt(E))
+    if exact:
+        w_in = _on_grid(w_in, 2.0 ** -6, 0.5)
+    conv_w = _normal_f32(rng, (C, 4), std=0.5)
+    gamma = (1.0 + 0.1 * rng.standard_normal(dv)).astype(np.float32)
+    w_out = _normal_f32(rng, (E, Hv * dv), std=1.0 / np.sqrt(Hv * dv))
+    return LayerWeights(_bf16(w_in), _bf16(conv_w), _bf16(gamma), _bf16(w_out))
+
+
+def layer_hidden(index: int, T: int, E: int, exact: bool = False) -> torch.Tensor:
+    """Layer input rows [T, E] ~ N(0, 1), bf16.  exact: on multiples of 1/8 in [-4, 4].
+    With a grid weight every product is a multiple of 2^-9 of size <= 2 and every partial
+    sum over E <= 2^13 terms stays below 2^14 in size, i.e. within 23 significant bits:
+    any summation order in fp32 gives the exact value, so its bf16 rounding is one
+    decision, whoever computes it."""
+    h = _normal_f32(_rng(index), (T, E))
+    return _bf16(_on_grid(h, 0.125, 4.0) if exact else h)
+
+
+def layer_caches(index: int, N: int, Hk: int, Hv: int, dk: int, dv: int):
+    """Incoming conv caches [N, 3, conv_dim] ~ N(0, 1) (bf16) and states
+    [N, Hv, dk, dv] ~ N(0, 0.1) (fp32)."""
+    rng = _rng(index)
+    C = 2 * Hk * dk + Hv * dv
+    cs = _normal_f32(rng, (N, 3, C))
+    st = _normal_f32(rng, (N, Hv, dk, dv), std=0.1)
+    return _bf16(cs), _f32(st)

@@ -53,6 +53,8 @@ def short_name(symbol: str) -> str:
         return "chunk_local_fused"   # mangled or demangled template argument FUSED = true
     if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):
         return "decode_gated"        # template argument GATED = true
+    if "proj_kernel" in symbol:      # projection GEMM, named by its output tile
+        return "proj_256" if ("ILi128ELi128E" in symbol or "<128, 128>" in symbol) else "proj_128"
     for frag, short in KERNELS:
         if frag in symbol:
             return short

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -297,6 +297,78 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
                           const void *z, const void *gamma, void *out,
                           float scale, float l2_eps, float norm_eps,
                           int B, int Hk, int Hv, int dk, int dv, int dtype, int order, void *stream);
+
+/*
+ * Linear-attention layer forward around the core ("7.6 Qwen3.5: the linear-attention
+ * hybrid", section 7.6.2, layer widths of the section 7.6.1 table; cache handling of
+ * "Hugging Face Transformers: Qwen3.5-MoE series explained", section 8.2): a bias-free
+ * input projection of the layer input gives the pre-conv q|k|v, the output gate z and
+ * two gate pre-activations a, b per value head; the conv + SiLU + L2 and the gated delta
+ * rule follow; the output passes the gated RMSNorm with SiLU(z) and a bias-free output
+ * projection.  The pages leave the gate maps open: here g = -softplus(a) (so the decay
+ * exp(g) lies in (0, 1)) and beta = sigmoid(b).  Weights and activations are bf16;
+ * products accumulate in fp32 on MFMA.  Weights are stored as a linear layer stores
+ * them: W[out][in], y = x W^T.
+ *
+ * gdn_linear -- y = a w^T.
+ *   a [M][K] bf16, w [N][K] bf16, y [M][N] bf16 (fp32 sums rounded to nearest even).
+ *   K a positive multiple of 64 and N a positive multiple of 4 (GDN_ERR_UNSUPPORTED
+ *   otherwise), M >= 0; y must not overlap a or w.
+ */
+int gdn_linear(const void *a, const void *w, void *y, int M, int N, int K, void *stream);
+
+/*
+ * gdn_in_proj -- the layer's input projection with its epilogue.
+ *   hidden [T][E] bf16; w_in [conv_dim + Hv*dv + 2*Hv][E] bf16, rows in the order
+ *   q|k|v (conv_dim), z (Hv*dv), a (Hv), b (Hv);
+ *   x [T][conv_dim] bf16, z [T][Hv*dv] bf16: those columns of hidden w_in^T;
+ *   g, beta [T][Hv] fp32: -softplus and sigmoid of the a and b columns.
+ * E a positive multiple of 64, Hv*dv a multiple of 64, Hv <= 32, dk and dv multiples of
+ * 16 (GDN_ERR_UNSUPPORTED otherwise).  Outputs must not overlap each other or an input.
+ */
+int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta,
+                int T, int E, int Hk, int Hv, int dk, int dv, void *stream);
+
+/*
+ * gdn_layer_prefill -- the whole layer over packed sequences in one call:
+ * gdn_in_proj, gdn_prefill (element type bf16), gdn_gated_rmsnorm over each (token,
+ * value head) row, gdn_linear with w_out.
+ *   hidden [T][E], w_in as in gdn_in_proj, conv_w [conv_dim][4], gamma [dv] (the gain
+ *   as applied), w_out [E][Hv*dv]: bf16.
+ *   cu_seqlens, N, conv_state_in / conv_state_out [N][3][conv_dim] bf16,
+ *   initial_state / final_state [N][Hv][dk][dv] fp32, scale, l2_eps, order: as in
+ *   gdn_prefill (the same exact aliases allowed).
+ *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
+ *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
+ *              (x, z, g, beta, o and the prefill's workspace); must not overlap any
+ *              other argument.
+ * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
+ * The four steps run in order on `stream` (the prefill as in gdn_prefill).
+ */
+size_t gdn_layer_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv);
+int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
+                      const void *w_out, const int32_t *cu_seqlens, int N,
+                      const void *conv_state_in, void *conv_state_out,
+                      const float *initial_state, float *final_state, void *out,
+                      float scale, float l2_eps, float norm_eps,
+                      int T, int E, int Hk, int Hv, int dk, int dv, int order,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_layer_decode -- one token for each of B sequences through the layer:
+ * gdn_in_proj, gdn_decode_step_gated (element type bf16, caches in place),
+ * gdn_linear with w_out.
+ *   hidden [B][E] bf16; weights as in gdn_layer_prefill; conv_state [B][3][conv_dim]
+ *   bf16 and state [B][Hv][dk][dv] fp32 in/out; out [B][E] bf16.
+ *   workspace  at least gdn_layer_decode_workspace_size(B, Hk, Hv, dk, dv) bytes.
+ * dk, dv in {16, 32, 64, 128}; E and Hv as in gdn_in_proj.
+ */
+size_t gdn_layer_decode_workspace_size(int B, int Hk, int Hv, int dk, int dv);
+int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
+                     const void *w_out, void *conv_state, float *state, void *out,
+                     float scale, float l2_eps, float norm_eps,
+                     int B, int E, int Hk, int Hv, int dk, int dv, int order,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(int status);

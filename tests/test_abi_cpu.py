@@ -30,13 +30,14 @@ def test_exports_every_declared_symbol(L):
     names = _declared_functions()
     assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_prefill",
             "gdn_prefill_local", "gdn_decode_step", "gdn_decode_step_gated", "gdn_gated_rmsnorm",
-            "gdn_status_string", "gdn_abi_version"} <= set(names)
+            "gdn_status_string", "gdn_abi_version", "gdn_linear", "gdn_in_proj", "gdn_layer_prefill",
+            "gdn_layer_prefill_workspace_size", "gdn_layer_decode", "gdn_layer_decode_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 3
+    assert L.gdn_abi_version() == 4
     for code in range(8):
         assert L.gdn_status_string(code).decode().startswith("GDN_")
     assert b"unknown" in L.gdn_status_string(99)
@@ -205,6 +206,95 @@ def test_decode_gated_validation(L):
     assert call(out=P((6 << 24) + 16)) == 6                      # out overlaps z
     assert call(gm=P((7 << 24) + 8)) == 7                        # misaligned gain
     assert call(out=P((5 << 24) + 64)) == 6                      # out overlaps the state
+
+
+def test_linear_validation(L):
+    P = _ptr
+
+    def call(a=P(0), w=P(1 << 24), y=P(2 << 24), M=8, N=16, K=64):
+        return L.gdn_linear(a, w, y, M, N, K, None)
+    assert call(M=-1) == 2
+    assert call(K=0) == 2
+    assert call(K=96) == 3                                       # k extent not a multiple of 64
+    assert call(N=18) == 3                                       # rows of 4-column stores
+    assert call(w=None) == 1
+    assert call(a=None) == 1
+    assert call(y=P(8)) == 7
+    assert call(y=P(64)) == 6                                    # y overlaps a
+    assert call(y=P((1 << 24) + 256)) == 6                       # y overlaps w
+
+
+def test_in_proj_validation(L):
+    P = _ptr
+    base = dict(h=P(0), w=P(1 << 24), x=P(2 << 24), z=P(3 << 24), g=P(4 << 24), b=P(5 << 24), T=8, E=64, Hk=1,
+                Hv=2, dk=16, dv=32)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_in_proj(a["h"], a["w"], a["x"], a["z"], a["g"], a["b"], a["T"], a["E"], a["Hk"], a["Hv"],
+                             a["dk"], a["dv"], None)
+    assert call(T=-1) == 2
+    assert call(Hk=2, Hv=3) == 2                                 # Hv % Hk != 0
+    assert call(Hv=3) == 3                                       # output projection k extent 96
+    assert call(E=0) == 2
+    assert call(E=96) == 3
+    assert call(Hk=1, Hv=34, dv=32) == 3                         # more gate columns than the gate path takes
+    assert call(dk=24) == 3
+    assert call(g=None) == 1
+    assert call(b=P((5 << 24) + 4)) == 7
+    assert call(z=P((2 << 24) + 256)) == 6                       # z overlaps x
+    assert call(b=P((4 << 24) + 16)) == 6                        # beta overlaps g
+    assert call(x=P(256)) == 6                                   # x overlaps hidden
+
+
+def test_layer_prefill_validation(L):
+    P = _ptr
+    ws = L.gdn_layer_prefill_workspace_size(8, 1, 1, 2, 64, 64)
+    assert ws > 0
+    assert L.gdn_layer_prefill_workspace_size(8, 1, 1, 2, 32, 32) == 0      # no chunked path for head dim 32
+    base = dict(h=P(0), wi=P(1 << 24), cw=P(2 << 24), gm=P(3 << 24), wo=P(4 << 24), cu=None, N=1, ci=None, co=None,
+                s0=None, sf=P(5 << 24), out=P(6 << 24), T=8, E=64, Hk=1, Hv=2, dk=64, dv=64, order=0, ws=P(1 << 28),
+                wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_layer_prefill(a["h"], a["wi"], a["cw"], a["gm"], a["wo"], a["cu"], a["N"], a["ci"], a["co"],
+                                   a["s0"], a["sf"], a["out"], ctypes.c_float(1.0), ctypes.c_float(1e-6),
+                                   ctypes.c_float(1e-6), a["T"], a["E"], a["Hk"], a["Hv"], a["dk"], a["dv"],
+                                   a["order"], a["ws"], a["wsb"], None)
+    assert call(N=2) == 2                                        # two sequences need cu_seqlens
+    assert call(E=100) == 3
+    assert call(dk=32, dv=32) == 3
+    assert call(order=2) == 3
+    assert call(gm=None) == 1
+    assert call(out=None) == 1
+    assert call(wo=P((4 << 24) + 2)) == 7
+    assert call(wsb=ws - 1) == 4
+    assert call(ws=None) == 4
+    assert call(out=P(512)) == 6                                 # out overlaps hidden
+    assert call(ws=P(6 << 24)) == 6                              # workspace overlaps out
+    assert call(sf=P((1 << 24) + 1024)) == 6                     # final state overlaps w_in
+
+
+def test_layer_decode_validation(L):
+    P = _ptr
+    ws = L.gdn_layer_decode_workspace_size(4, 1, 2, 64, 64)
+    assert ws > 0
+    base = dict(h=P(0), wi=P(1 << 24), cw=P(2 << 24), gm=P(3 << 24), wo=P(4 << 24), cs=P(5 << 24), st=P(6 << 24),
+                out=P(7 << 24), B=4, E=64, Hk=1, Hv=2, dk=64, dv=64, order=0, ws=P(1 << 28), wsb=ws)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.gdn_layer_decode(a["h"], a["wi"], a["cw"], a["gm"], a["wo"], a["cs"], a["st"], a["out"],
+                                  ctypes.c_float(1.0), ctypes.c_float(1e-6), ctypes.c_float(1e-6), a["B"], a["E"],
+                                  a["Hk"], a["Hv"], a["dk"], a["dv"], a["order"], a["ws"], a["wsb"], None)
+    assert call(B=-1) == 2
+    assert call(dk=256) == 3
+    assert call(st=None) == 1
+    assert call(wsb=ws - 1) == 4
+    assert call(out=P((6 << 24) + 64)) == 6                      # out overlaps the state
+    assert call(cs=P((6 << 24) + 16)) == 6                       # conv cache overlaps the state
+    assert call(h=P(4)) == 7
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
