@@ -34,9 +34,9 @@
 //    turn) takes a contiguous run of tiles in which groups of four row tiles share
 //    column tiles: the tiles resident on one XCD at a time reuse each other's rows
 //    from its L2.
-//  - The gate columns (2 Hv of them) are left out of the tile grid: after the tiles,
+//  - The gate columns (2 Hv of them) are left out of the tile grid: before the tiles,
 //    workgroups of 16 rows each split k over their four waves, sum the partial
-//    products through LDS and apply the gate maps.
+//    products through LDS and apply the gate maps (one 16-column tile per wave).
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -60,7 +60,7 @@ struct ProjTile {
     static constexpr int LDS = 2 * STAGE;
     static constexpr int A_LD = BM / RPP, W_LD = BN / RPP;   // 16-byte chunks per thread and stage
     static constexpr int KSTEPS = BK / 16;               // MFMA k-steps of 16 per stage
-    static_assert(LDS >= (kProjThreads / kWave - 1) * kGateMaxTiles * kWave * 16, "gate partial sums fit");
+    static_assert(LDS >= (kProjThreads / kWave) * kGateMaxTiles * kWave * 16, "gate partial sums fit");
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -234,54 +234,56 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
 }
 
 // Gate outputs of rows r0 .. r0 + 15: the 2 Hv gate rows of w start at row N.  Wave
-// `wave` takes the k-steps wave, wave + 4, ...; partial sums meet in LDS.
+// `wave` takes the k-steps wave, wave + 4, ... (all its loads in flight together, rows
+// and gate columns past the edge reading as zeros); the partial sums meet in LDS, and
+// wave i finishes gate column tile i (-softplus for the a columns, sigmoid for b).
 __device__ __forceinline__ void gate_rows(const ProjArgs &p, int gb, char *smem) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int r0 = gb * kGateRows, K = p.K, KS = K / 32, G = 2 * p.heads;
-    const int m = r0 + (lane & 15), kc = 8 * (lane >> 4);
-    const bf16 *w = static_cast<const bf16 *>(p.w);
-    const bf16 *arow = static_cast<const bf16 *>(p.a) + (size_t)min(m, p.M - 1) * K + kc;
-    const bool mok = m < p.M;
+    const int kc = 8 * (lane >> 4);
+    const __amdgpu_buffer_rsrc_t ra_src = rows_rsrc(static_cast<const bf16 *>(p.a), r0, p.M, K);
+    const __amdgpu_buffer_rsrc_t rw_src = rows_rsrc(static_cast<const bf16 *>(p.w), p.N, p.N + G, K);
+    const int voff = (lane & 15) * K * 2 + kc * 2;
     f32x4 acc[kGateMaxTiles];
 #pragma unroll
     for (int i = 0; i < kGateMaxTiles; ++i) acc[i] = zero4();
     for (int base = 0; base < KS; base += 4 * kGateBatch) {
-        bf16x8 af[kGateBatch], wf[kGateBatch][kGateMaxTiles];
+        u32x4 af[kGateBatch], wf[kGateBatch][kGateMaxTiles];
 #pragma unroll
         for (int b = 0; b < kGateBatch; ++b) {
+            // k-steps past K read beyond every row's end: redirect them to k-step 0 with a
+            // zero operand instead (a row's bytes stay in range)
             const int ks = base + wave + 4 * b;
-            const bool kok = ks < KS;
-            af[b] = kok && mok ? *reinterpret_cast<const bf16x8 *>(arow + ks * 32) : zero8();
+            const int kb = ks < KS ? ks * 64 : 0;
+            af[b] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, voff + kb, 0, 0);
 #pragma unroll
-            for (int i = 0; i < kGateMaxTiles; ++i) {
-                const int gi = 16 * i + (lane & 15);
-                wf[b][i] = kok && gi < G
-                               ? *reinterpret_cast<const bf16x8 *>(w + (size_t)(p.N + gi) * K + kc + ks * 32)
-                               : zero8();
-            }
+            for (int i = 0; i < kGateMaxTiles; ++i)
+                wf[b][i] = __builtin_amdgcn_raw_buffer_load_b128(rw_src, voff + kb, 16 * i * K * 2, 0);
         }
 #pragma unroll
-        for (int b = 0; b < kGateBatch; ++b)
+        for (int b = 0; b < kGateBatch; ++b) {
+            if (base + wave + 4 * b >= KS) continue;
 #pragma unroll
-            for (int i = 0; i < kGateMaxTiles; ++i) acc[i] = mfma16(wf[b][i], af[b], acc[i]);
+            for (int i = 0; i < kGateMaxTiles; ++i)
+                acc[i] = mfma16(__builtin_bit_cast(bf16x8, wf[b][i]), __builtin_bit_cast(bf16x8, af[b]), acc[i]);
+        }
     }
     f32x4 *part = reinterpret_cast<f32x4 *>(smem);
-    if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < kGateMaxTiles; ++i) part[((wave - 1) * kGateMaxTiles + i) * kWave + lane] = acc[i];
-    }
+    for (int i = 0; i < kGateMaxTiles; ++i) part[(wave * kGateMaxTiles + i) * kWave + lane] = acc[i];
     __syncthreads();
-    if (wave != 0 || !mok) return;
+    // wave i sums tile i over the four waves: lane holds rows r0 + lane % 16, gate
+    // columns 16 i + 4 (lane / 16) + 0..3
+    const int i = wave, m = r0 + (lane & 15);
+    if (i >= kGateMaxTiles || m >= p.M) return;
+    f32x4 t = part[i * kWave + lane];
 #pragma unroll
-    for (int i = 0; i < kGateMaxTiles; ++i) {
+    for (int v = 1; v < kProjThreads / kWave; ++v) t += part[(v * kGateMaxTiles + i) * kWave + lane];
 #pragma unroll
-        for (int v = 1; v < kProjThreads / kWave; ++v) acc[i] += part[((v - 1) * kGateMaxTiles + i) * kWave + lane];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int gi = 16 * i + 4 * (lane >> 4) + r;
-            if (gi < p.heads) p.g[(size_t)m * p.heads + gi] = -softplus_f32(acc[i][r]);
-            else if (gi < G) p.beta[(size_t)m * p.heads + (gi - p.heads)] = sigmoid_f32(acc[i][r]);
-        }
+    for (int r = 0; r < 4; ++r) {
+        const int gi = 16 * i + 4 * (lane >> 4) + r;
+        if (gi < p.heads) p.g[(size_t)m * p.heads + gi] = -softplus_f32(t[r]);
+        else if (gi < G) p.beta[(size_t)m * p.heads + (gi - p.heads)] = sigmoid_f32(t[r]);
     }
 }
 
@@ -289,11 +291,15 @@ template <int WM, int WN, int BK>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
     using S = ProjTile<WM, WN, BK>;
     __shared__ __attribute__((aligned(16))) char smem[S::LDS];
+    // the gate workgroups come first: short, they delay every compute unit's first tile
+    // by the same small amount instead of forming a tail round after the tiles
     int b = blockIdx.x;
-    if (b >= p.ntiles) {
-        gate_rows(p, b - p.ntiles, smem);
+    const int gate_blocks = p.heads > 0 ? (p.M + kGateRows - 1) / kGateRows : 0;
+    if (b < gate_blocks) {
+        gate_rows(p, b, smem);
         return;
     }
+    b -= gate_blocks;
     // XCD x (blocks x, x + 8, ...) takes tiles [x T / 8, (x + 1) T / 8)
     if ((p.ntiles & 7) == 0) b = (b & 7) * (p.ntiles >> 3) + (b >> 3);
     // groups of kTileGroup row tiles run over all column tiles, row tile fastest
