@@ -42,6 +42,8 @@ KERNELS = [
     ("gated_rmsnorm_kernel", "gated_rmsnorm"),
     ("zero_flags_kernel", "zero_flags"),
 ]
+# the projection kernel's two tile shapes (named by short_name from its template arguments)
+PROJ_NAMES = ("proj_256", "proj_128")
 # bench.py --copy-calibration streams a buffer through torch.neg (one elementwise
 # kernel that reads and writes COPY_BYTES); host-to-device uploads use blit
 # kernels of other names and are not counted as the calibration copy.
@@ -54,7 +56,7 @@ def short_name(symbol: str) -> str:
     if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):
         return "decode_gated"        # template argument GATED = true
     if "proj_kernel" in symbol:      # projection GEMM, named by its output tile
-        return "proj_256" if ("ILi128ELi128E" in symbol or "<128, 128>" in symbol) else "proj_128"
+        return "proj_256" if ("ILi128ELi128E" in symbol or "proj_kernel<128, 128" in symbol) else "proj_128"
     for frag, short in KERNELS:
         if frag in symbol:
             return short
@@ -118,7 +120,7 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     f_fac = COPY_BYTES / (fetch["copy"][1] * 1024.0)
     w_fac = COPY_BYTES / (write["copy"][1] * 1024.0)
     out = {"fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
-    known = {short for _, short in KERNELS}
+    known = {short for _, short in KERNELS} | set(PROJ_NAMES)
     for k in fetch:
         if k not in known or k not in write:
             continue

@@ -36,9 +36,9 @@ def test_short_names():
     assert profiling.short_name(DECODE) == "decode"
     assert profiling.short_name(DECODE.replace("false>", "true>")) == "decode_gated"
     assert profiling.short_name(COPY) == "copy"
-    assert profiling.short_name("void gdn::proj_kernel<128, 128>(gdn::ProjArgs)") == "proj_256"
-    assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128EEEvNS_8ProjArgsE") == "proj_256"
-    assert profiling.short_name("void gdn::proj_kernel<64, 64>(gdn::ProjArgs)") == "proj_128"
+    assert profiling.short_name("void gdn::proj_kernel<128, 128, 64>(gdn::ProjArgs)") == "proj_256"
+    assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64EEEvNS_8ProjArgsE") == "proj_256"
+    assert profiling.short_name("void gdn::proj_kernel<64, 64, 128>(gdn::ProjArgs)") == "proj_128"
 
 
 def test_kernel_stats(tmp_path):
