@@ -21,10 +21,10 @@
 //    k-step's fragments (8 reads for 16 MFMAs in the large tile) are small enough to
 //    double-buffer beside 256 accumulators.
 //  - k advances BK at a time (64 for the large tile, 128 for the small one when K
-//    allows) through two LDS stages: every thread loads its share of the next stage
-//    into registers with buffer loads (rows past the matrix edge read as zeros), the
-//    loads in flight during the stage's MFMAs, writes it to the other stage after
-//    them, and one barrier per stage orders everything.  The loop body has no branch;
+//    allows) through two LDS stages: every thread loads its share of a stage into
+//    registers with buffer loads (rows past the matrix edge read as zeros) two stages
+//    ahead, in one of two register sets, and writes it to the idle LDS stage during
+//    the stage before its use; one barrier per stage orders everything.  The loop body has no branch;
 //    the fragments of k-step s + 1 are read from LDS between the MFMAs of step s (one
 //    read per group of MFMAs, by scheduling hints), so with one wave per SIMD the
 //    matrix unit does not wait on LDS.  The 16-byte chunks of an LDS row are
@@ -72,11 +72,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte chunk c of LDS row `row`: the chunk index is XORed with the
-// row's low three bits, so eight consecutive rows read at one chunk index fall into
-// eight different 16-byte bank groups.
+// Byte offset of 16-byte chunk c of LDS row `row`.  The LDS serves a 16-byte access of
+// 16 lanes per cycle from its 64 four-byte banks, i.e. sixteen 16-byte bank groups, and
+// a fragment read has 16 consecutive rows read at one chunk index.  With 128-byte rows
+// two rows fill the 64 banks (even rows the lower half), so the chunk index is XORed
+// with bits 1..3 of the row; with 256-byte rows, with bits 0..3.  Either way the 16 rows
+// hit 16 different groups, and the staging writes (16 lanes = 16 chunks of one or two
+// rows) stay conflict-free.  (An XOR with bits 0..2 alone maps rows r and r + 8 onto the
+// same banks: a 2-way conflict on every fragment read.)
 template <int ROWB>
-__device__ __forceinline__ int swz(int row, int c) { return row * ROWB + ((c ^ (row & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int c) {
+    static_assert(ROWB == 128 || ROWB == 256, "row of 8 or 16 chunks");
+    const int f = ROWB == 128 ? (row >> 1) & 7 : row & 15;
+    return row * ROWB + ((c ^ f) << 4);
+}
 
 __device__ __forceinline__ bf16x8 zero8() {
     bf16x8 z;
@@ -117,23 +126,26 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
     const __amdgpu_buffer_rsrc_t ra_src = rows_rsrc(static_cast<const bf16 *>(p.a), m0, M, K);
     const __amdgpu_buffer_rsrc_t rw_src = rows_rsrc(static_cast<const bf16 *>(p.w), n0, N, K);
 
-    // staging: thread tid moves chunk tid % CPR of rows tid / CPR + RPP i
+    // staging: thread tid moves chunk tid % CPR of rows tid / CPR + RPP i; two register
+    // sets, so a stage's loads are issued two stages before their LDS writes
     const int crow = tid / S::CPR, cc = tid % S::CPR;
     const int voff = crow * K * 2 + cc * 16;
-    u32x4 ra[S::A_LD], rw[S::W_LD];
-    auto gload = [&](int kt) {
+    struct Stg {
+        u32x4 a[S::A_LD], w[S::W_LD];
+    };
+    auto gload = [&](int kt, Stg &r) {
         const int vo = voff + kt * S::ROWB;
 #pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
+        for (int i = 0; i < S::A_LD; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
 #pragma unroll
-        for (int i = 0; i < S::W_LD; ++i) rw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw_src, vo, i * S::RPP * K * 2, 0);
+        for (int i = 0; i < S::W_LD; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw_src, vo, i * S::RPP * K * 2, 0);
     };
-    auto swrite = [&](int buf) {
+    auto swrite = [&](int buf, const Stg &r) {
         char *sa = smem + buf * S::STAGE, *sw = sa + S::A_BYTES;
 #pragma unroll
-        for (int i = 0; i < S::A_LD; ++i) *reinterpret_cast<u32x4 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = ra[i];
+        for (int i = 0; i < S::A_LD; ++i) *reinterpret_cast<u32x4 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = r.a[i];
 #pragma unroll
-        for (int i = 0; i < S::W_LD; ++i) *reinterpret_cast<u32x4 *>(sw + swz<S::ROWB>(crow + S::RPP * i, cc)) = rw[i];
+        for (int i = 0; i < S::W_LD; ++i) *reinterpret_cast<u32x4 *>(sw + swz<S::ROWB>(crow + S::RPP * i, cc)) = r.w[i];
     };
 
     f32x16 acc[S::NT][S::MT];
@@ -174,19 +186,16 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
     static_assert((NW > MF ? NW % MF : MF % NW) == 0, "write / MFMA interleave");
 
     const int KT = K / BK;
-    gload(0);
-    swrite(0);
-    __syncthreads();
-    // Branch-free stage loop (the last stage reloads itself into the idle buffer), in the
-    // order the scheduling groups below fix: step 0's fragment reads, the next stage's
-    // global loads, then each step's MFMAs with the next step's reads between them, and
-    // the staging writes between the last step's MFMAs (by then the loads have had the
-    // stage's other MFMAs to arrive).
-    for (int kt = 0; kt < KT; ++kt) {
+    // One stage: `wr` holds stage kt + 1 (loaded a stage ago) and is written to the idle LDS
+    // buffer during the last k-step; `ld` (free) receives stage kt + 2's loads at the start.
+    // The order is fixed by scheduling groups: step 0's fragment reads, the global loads,
+    // each step's MFMAs with the next step's reads between them, the LDS writes between
+    // the last step's MFMAs.  Past the end the loads repeat the last stage (never used).
+    auto stage = [&](int kt, const Stg &wr, Stg &ld) {
         const int buf = kt & 1;
         Frags f0, f1;
         fread(buf, 0, f0);
-        gload(min(kt + 1, KT - 1));
+        gload(min(kt + 2, KT - 1), ld);
 #pragma unroll
         for (int s = 0; s < S::KSTEPS; ++s) {
             Frags &cur = (s & 1) ? f1 : f0;
@@ -194,9 +203,9 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
             if (s + 1 < S::KSTEPS) fread(buf, s + 1, nxt);
             mfmas(cur);
         }
-        swrite(buf ^ 1);
+        swrite(buf ^ 1, wr);
         __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);    // DS reads of step 0
-        __builtin_amdgcn_sched_group_barrier(0x020, NW, 0);    // VMEM reads of the next stage
+        __builtin_amdgcn_sched_group_barrier(0x020, NW, 0);    // VMEM reads of stage kt + 2
 #pragma unroll
         for (int s = 0; s + 1 < S::KSTEPS; ++s) {
 #pragma unroll
@@ -207,11 +216,22 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
         }
 #pragma unroll
         for (int g = 0; g < (NW > MF ? MF : NW); ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x200, W_EACH, 0);  // DS write
+            __builtin_amdgcn_sched_group_barrier(0x200, W_EACH, 0);  // DS write (stage kt + 1)
             __builtin_amdgcn_sched_group_barrier(0x008, M_EACH, 0);  // MFMA (last step)
         }
         __syncthreads();
+    };
+    Stg s0, s1;
+    gload(0, s0);
+    gload(min(1, KT - 1), s1);
+    swrite(0, s0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        stage(kt, s1, s0);
+        stage(kt + 1, s0, s1);
     }
+    if (kt < KT) stage(kt, s1, s0);
 
     // lane holds y[m][n + 8 g + 4 (lane / 32) + 0..3] of each 32 x 32 block, g < 4
 #pragma unroll
