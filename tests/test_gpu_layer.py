@@ -51,8 +51,13 @@ def _sample_rows(M, n, seed):
 
 # ------------------------------------------------------------------ projections
 
+# the 256 x 256 tile runs when its tiles alone fill the chip (M, N >= 4096 here) and takes k
+# 64 deep per stage, two stages per loop pass: K = 64, 128, 192 give one, two and three stages
+# (a lone stage, one pass, a pass and a tail); the 128 x 128 tile takes k 128 deep when K allows
+# (K = 128, 1024, 2048) and 64 deep otherwise (K = 64, 192)
 @pytest.mark.parametrize("M,N,K", [(1, 16, 64), (77, 100, 128), (300, 260, 192), (513, 1028, 1024),
-                                   (0, 64, 64), (4100, 4100, 128), (4096, 1024, 2048)])
+                                   (0, 64, 64), (4100, 4100, 128), (4096, 1024, 2048), (4096, 4096, 64),
+                                   (4100, 4108, 192)])
 def test_linear(gdn, M, N, K):
     announce(f"linear M={M} N={N} K={K}")
     rng = np.random.default_rng(7000 + M + N + K)
