@@ -85,8 +85,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     static_assert(TPR <= kWave, "row must fit in a wave");
 
     __shared__ float qk_s[2 * DK];   // raw SiLU(conv) of q then k
-    __shared__ float v_s[DV];
-    __shared__ float red[NW][2][DV];
+    // 16-byte aligned: the cross-wave sums and v are moved as one float4 per lane (16 lanes
+    // cover 256 contiguous bytes, one LDS cycle without bank conflicts)
+    __shared__ __attribute__((aligned(16))) float v_s[DV];
+    __shared__ __attribute__((aligned(16))) float red[NW][2][DV];
     __shared__ float scal[3];
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -178,20 +180,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             }
         }
         if (lane < TPR) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { red[wave][0][4 * cg + e] = pm[e]; red[wave][1][4 * cg + e] = pq[e]; }
+            *reinterpret_cast<f32x4 *>(&red[wave][0][4 * cg]) = f32x4{pm[0], pm[1], pm[2], pm[3]};
+            *reinterpret_cast<f32x4 *>(&red[wave][1][4 * cg]) = f32x4{pq[0], pq[1], pq[2], pq[3]};
         }
         __syncthreads();   // red and v_s complete
         const float a = __expf(g[(size_t)b * Hv + h]);
         const float bt = beta[(size_t)b * Hv + h];
+        f32x4 sk = zero4(), sq = zero4();
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            sk += *reinterpret_cast<const f32x4 *>(&red[ww][0][4 * cg]);
+            sq += *reinterpret_cast<const f32x4 *>(&red[ww][1][4 * cg]);
+        }
+        const f32x4 v4 = *reinterpret_cast<const f32x4 *>(&v_s[4 * cg]);
         float delta[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) { sk += red[ww][0][4 * cg + e]; sq += red[ww][1][4 * cg + e]; }
-            delta[e] = bt * (v_s[4 * cg + e] - (order == 0 ? a * sk : sk));
-            pq[e] = a * sq + delta[e] * kq;   // output column 4cg+e
+            delta[e] = bt * (v4[e] - (order == 0 ? a * sk[e] : sk[e]));
+            pq[e] = a * sq[e] + delta[e] * kq;   // output column 4cg+e
         }
         if constexpr (GATED) {
             if (wave == 0) {   // rg == 0 is lanes 0 .. TPR - 1 of wave 0
