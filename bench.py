@@ -30,7 +30,9 @@ rotate over 3 copies at different addresses and the decode state over 2 sets
 (512 MiB), so no input is served from the 256 MB Infinity Cache; the prefill
 workspace is one buffer reused every step, as a caller reuses it, and its lines
 stay cached from one step to the next (the decode step reads its state with
-non-temporal loads).
+non-temporal loads).  After the timed regions, "achievable" records two measured
+ceilings (a plain streaming kernel's GB/s, the library's bf16 GEMM on 8192^3), and the
+decode and projection figures are also given as fractions of them.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 Profiler runs: --split-only (the split-phase region alone), --metric-only (the
@@ -127,6 +129,37 @@ def copy_calibration(torch, dev):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def achievable_peaks(torch, dev):
+    """Measured ceilings on this GPU, for context beside the datasheet peaks: a plain
+    elementwise stream (torch.neg, 512 MiB read + 512 MiB written) and the library's bf16
+    GEMM (torch.mm, hipBLASLt) on an 8192^3 product; HIP events, best of several runs."""
+    n = (512 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+
+    def best_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return min(times)
+
+    stream_ms = best_ms(lambda: torch.neg(src, out=dst), 10)
+    gemm_ms = best_ms(lambda: torch.mm(a, b.t(), out=c), 5)
+    del src, dst, a, b, c
+    return {"stream_gb_per_s": 2 * n * 4 / stream_ms / 1e6, "library_gemm_tflops": 2 * 8192 ** 3 / gemm_ms / 1e9,
+            "what": "torch.neg over 512 MiB fp32 (read + write); torch.mm bf16 8192^3; best of 10 / 5 runs"}
 
 
 def main():
@@ -389,6 +422,12 @@ def main():
         "roofline": roof,
         "kernels": kern,
     }
+    if not (args.split_only or args.metric_only):
+        cal = achievable_peaks(torch, dev)
+        out["achievable"] = cal
+        out["decode"]["frac_of_stream"] = out["decode"]["state_gb_per_s"] / cal["stream_gb_per_s"]
+        for n in ("in_proj", "out_proj"):
+            kern[n]["frac_of_library_gemm"] = kern[n]["achieved"] / cal["library_gemm_tflops"]
     if args.copy_calibration:
         copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
