@@ -336,9 +336,13 @@ namespace {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Host checks shared by the projections: K a positive multiple of 64 (two MFMA k-steps
-// per LDS stage), output row lengths multiples of 4 (8-byte stores of 4 bf16).
-bool proj_shape_ok(int M, int N, int K) { return M >= 0 && N > 0 && N % 4 == 0 && K > 0 && K % 64 == 0; }
+// Host checks shared by the projections: K a positive multiple of 64 (the k-stage depth)
+// and at most 2^20 (a tile's 256 rows then span < 2^31 bytes, the reach of the kernel's
+// 32-bit buffer offsets), output row lengths multiples of 4 (8-byte stores of 4 bf16).
+constexpr int kProjMaxK = 1 << 20;
+bool proj_shape_ok(int M, int N, int K) {
+    return M >= 0 && N > 0 && N % 4 == 0 && K > 0 && K % 64 == 0 && K <= kProjMaxK;
+}
 
 int in_proj_impl(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta, int T, int E,
                  int Hk, int Hv, int dk, int dv, hipStream_t st) {
@@ -361,6 +365,7 @@ int check_layer_shape(int E, int Hk, int Hv, int dk, int dv) {
     if (int e = check_heads(Hk, Hv)) return e;
     if (E <= 0) return GDN_ERR_BAD_SHAPE;
     if (E % 64 != 0 || ((size_t)Hv * dv) % 64 != 0 || !gdn::proj_gates_supported(Hv)) return GDN_ERR_UNSUPPORTED;
+    if (E > kProjMaxK || (size_t)Hv * dv > (size_t)kProjMaxK) return GDN_ERR_UNSUPPORTED;
     if (dk % 16 != 0 || dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
 }

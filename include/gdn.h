@@ -312,8 +312,8 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
  *
  * gdn_linear -- y = a w^T.
  *   a [M][K] bf16, w [N][K] bf16, y [M][N] bf16 (fp32 sums rounded to nearest even).
- *   K a positive multiple of 64 and N a positive multiple of 4 (GDN_ERR_UNSUPPORTED
- *   otherwise), M >= 0; y must not overlap a or w.
+ *   K a positive multiple of 64, at most 2^20, and N a positive multiple of 4
+ *   (GDN_ERR_UNSUPPORTED otherwise), M >= 0; y must not overlap a or w.
  */
 int gdn_linear(const void *a, const void *w, void *y, int M, int N, int K, void *stream);
 
@@ -323,8 +323,9 @@ int gdn_linear(const void *a, const void *w, void *y, int M, int N, int K, void 
  *   q|k|v (conv_dim), z (Hv*dv), a (Hv), b (Hv);
  *   x [T][conv_dim] bf16, z [T][Hv*dv] bf16: those columns of hidden w_in^T;
  *   g, beta [T][Hv] fp32: -softplus and sigmoid of the a and b columns.
- * E a positive multiple of 64, Hv*dv a multiple of 64, Hv <= 32, dk and dv multiples of
- * 16 (GDN_ERR_UNSUPPORTED otherwise).  Outputs must not overlap each other or an input.
+ * E a positive multiple of 64 (at most 2^20), Hv*dv a multiple of 64, Hv <= 32, dk and dv
+ * multiples of 16 (GDN_ERR_UNSUPPORTED otherwise).  Outputs must not overlap each other or
+ * an input.
  */
 int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta,
                 int T, int E, int Hk, int Hv, int dk, int dv, void *stream);

@@ -216,6 +216,7 @@ def test_linear_validation(L):
     assert call(M=-1) == 2
     assert call(K=0) == 2
     assert call(K=96) == 3                                       # k extent not a multiple of 64
+    assert call(K=(1 << 20) + 64) == 3                           # beyond the 32-bit tile offsets
     assert call(N=18) == 3                                       # rows of 4-column stores
     assert call(w=None) == 1
     assert call(a=None) == 1
