@@ -382,13 +382,21 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 // and the 3 before them ("7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2; history
 // from the sequence's own earlier tokens, else its conv cache, else zeros), with the same
 // arithmetic as gdn_conv_qk_prep.
+// Ready flags of the concurrent schedule: 64-bit values, one per (value head, chunk), set
+// to the call's own value (a fixed 32-bit tag in the high word, a per-device call counter in
+// the low word).  A flag counts as raised only when it holds this call's value, so the flags
+// need no clearing between calls: values left by earlier calls hold older counters, and a
+// fresh workspace would have to hold the exact 64-bit pattern by chance.
+typedef unsigned long long flag_t;
+constexpr unsigned kFlagTag = 0x9e3779b9u;
+
 template <int D, bool FUSED, typename TX>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0, int g1, int nslots,
     const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
-    int order, int *flags) {
+    int order, flag_t *flags, flag_t flag_val) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr bool STAGE = FUSED && sizeof(TX) == 2;
@@ -921,7 +929,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // thread raises the chunk's flag.
     if (flags) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();   // the next chunk rewrites the planes, the T / M operands and the scalars
-    if (flags && tid == 0) __hip_atomic_store(flags + (size_t)h * ncmax + gc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (flags && tid == 0)
+        __hip_atomic_store(flags + (size_t)h * ncmax + gc, flag_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!next_ok) break;
     s_ = sn;
     c_ = cn;
@@ -1029,8 +1038,8 @@ __device__ __forceinline__ int seq_by_rank(const int32_t *cu, int N, int Ttot, i
 template <int D, bool COH>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const int *flags,
-    ConvOut cv) {
+    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const flag_t *flags,
+    flag_t flag_val, ConvOut cv) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -1083,9 +1092,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         // device-coherent.  The copy waves confirm a chunk before the barrier after which the
         // compute waves prefetch its U' and Ol^T strips, i.e. two chunks ahead of the compute.
         auto ready = [&](int c) {
-            const int *f = flags + (size_t)h * ncmax + gbase + c;
+            const flag_t *f = flags + (size_t)h * ncmax + gbase + c;
             for (int it = 0; it < kSpinMax; ++it) {
-                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == flag_val) break;
                 __builtin_amdgcn_s_sleep(2);
             }
         };
@@ -1101,14 +1110,14 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             // after them: its round trip then overlaps the copies instead of following them
             // (the load is unconditional, reading chunk c's flag, known to be set, when there is
             // no chunk c + 2, and the empty asm keeps the test after the copies).
-            int published = 1;
+            flag_t published = flag_val;
             if constexpr (COH)
                 published = __hip_atomic_load(flags + (size_t)h * ncmax + gbase + (c + 2 < c_hi ? c + 2 : c),
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (c + 1 < c_hi) stage(c + 1, abuf[(c + 1) & 1]);
             if constexpr (COH) {
                 asm volatile("" : "+v"(published));
-                if (c + 2 < c_hi && published == 0) ready(c + 2);
+                if (c + 2 < c_hi && published != flag_val) ready(c + 2);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -1127,7 +1136,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
                         for (int hh = h + 1; hh < h + cv.G; ++hh)
                             for (int it = 0; it < kSpinMax; ++it) {
                                 if (__hip_atomic_load(flags + (size_t)hh * ncmax + gbase, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) != 0)
+                                                      __HIP_MEMORY_SCOPE_AGENT) == flag_val)
                                     break;
                                 __builtin_amdgcn_s_sleep(2);
                             }
@@ -1335,7 +1344,7 @@ static size_t flags_offset(size_t nc, int N, int Hv, int dk) {
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     (void)dv;
     const size_t nc = max_chunks(T, N);
-    return flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(int);
+    return flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(flag_t);
 }
 
 // ---- segment pipeline of gdn_chunk_prefill: the packed chunk range is cut into
@@ -1380,6 +1389,7 @@ struct PipeRes {
     hipStream_t last_stream = nullptr;
     bool has_last = false;
     std::mutex mu;   // one concurrent-schedule launch sequence at a time
+    unsigned epoch = 0;   // concurrent-schedule calls so far: the low word of their flag value
     bool ready = false;
 };
 static std::mutex g_pipe_mu;
@@ -1409,7 +1419,7 @@ static hipError_t pipe_resources(PipeRes **out) {
 
 template <int D>
 static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1, int cu_budget = 0,
-                               int *flags = nullptr) {
+                               flag_t *flags = nullptr, flag_t flag_val = 0) {
     if (g1 <= g0 || a.T <= 0) return hipSuccess;
     // one workgroup per compute unit (each holds most of the LDS), looping over chunks;
     // cu_budget > 0 leaves the other compute units to a concurrent state pass
@@ -1420,15 +1430,15 @@ static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int
     if (!a.fp) {
         hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)nullptr,
-                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order, flags);
+                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order, flags, flag_val);
     } else if (a.fp->bf16) {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const bf16 *)a.fp->x,
-                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order, flags);
+                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order, flags, flag_val);
     } else {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)a.fp->x,
-                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order, flags);
+                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order, flags, flag_val);
     }
     return hipGetLastError();
 }
@@ -1438,23 +1448,19 @@ static int state_blocks(int units) { return 8 * (D / 32) * ((units + 7) / 8); }
 
 template <int D>
 static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1,
-                               const int *flags = nullptr, const ConvOut &cv = ConvOut{}) {
+                               const flag_t *flags = nullptr, flag_t flag_val = 0,
+                               const ConvOut &cv = ConvOut{}) {
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
     const int blocks = state_blocks<D>(units);
     float *mid = reinterpret_cast<float *>((char *)a.ws + mid_offset(nc, a.Hv, D));
     if (flags)
         hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, cv);
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, cv);
     else
         hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, ConvOut{});
+                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, ConvOut{});
     return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void zero_flags_kernel(int *f, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) f[i] = 0;
 }
 
 // Concurrent schedule: the state pass occupies at most a quarter of the compute units and the
@@ -1508,8 +1514,8 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
         PipeRes *pr = nullptr;
         if ((e = pipe_resources(&pr)) != hipSuccess) return e;
         std::lock_guard<std::mutex> lock(pr->mu);
-        int *flags = reinterpret_cast<int *>((char *)a.ws + flags_offset(nc, a.N, a.Hv, D));
-        const int nf = nc * a.Hv;
+        flag_t *flags = reinterpret_cast<flag_t *>((char *)a.ws + flags_offset(nc, a.N, a.Hv, D));
+        const flag_t flag_val = ((flag_t)kFlagTag << 32) | ++pr->epoch;
         ConvOut cv;
         if (a.fp && a.fp->cs_out) {
             cv.x = a.fp->x;
@@ -1521,18 +1527,16 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
             cv.G = a.Hv / a.Hk;
             cv.dk = a.dk;
         }
-        hipLaunchKernelGGL(zero_flags_kernel, dim3((nf + 255) / 256), dim3(256), 0, st, flags, nf);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(pr->ev[0], st)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(pr->side, pr->ev[0], 0)) != hipSuccess) return e;
         // the previous call's chunk-local kernel, before local_done is recorded again
         if (pr->has_last && pr->last_stream != st && (e = hipStreamWaitEvent(st, pr->local_done, 0)) != hipSuccess)
             return e;
-        if ((e = launch_local<D>(a, pr->side, nc, 0, nc, cus - sblocks, flags)) != hipSuccess) return e;
+        if ((e = launch_local<D>(a, pr->side, nc, 0, nc, cus - sblocks, flags, flag_val)) != hipSuccess) return e;
         if ((e = hipEventRecord(pr->local_done, pr->side)) != hipSuccess) return e;
         pr->last_stream = st;
         pr->has_last = true;
-        return launch_state<D>(a, st, nc, 0, nc, flags, cv);
+        return launch_state<D>(a, st, nc, 0, nc, flags, flag_val, cv);
     }
     const int G = pipeline_segments(nc, sblocks);
     if (G == 1) {

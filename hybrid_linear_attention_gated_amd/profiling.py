@@ -12,8 +12,9 @@
   python -m hybrid_linear_attention_gated_amd.profiling timeline DIR [FIRST [SKIP]]
       kernel start / end offsets inside one step, averaged over the steps of a
       `rocprofv3 --kernel-trace` run: a step begins at each launch of the kernel
-      FIRST (short name, default zero_flags: the first launch of the concurrent
-      prefill schedule) and the first SKIP steps (warm-up) are dropped.  Shows how
+      FIRST (short name, default state_pass: the first launch of the concurrent
+      prefill schedule, whose chunk-local kernel starts after a wait on the second
+      stream) and the first SKIP steps (warm-up) are dropped.  Shows how
       kernels on the library's two streams overlap.
 
 Only text is produced; nothing here touches the GPU.
@@ -40,7 +41,6 @@ KERNELS = [
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
     ("gated_rmsnorm_kernel", "gated_rmsnorm"),
-    ("zero_flags_kernel", "zero_flags"),
 ]
 # the projection kernel's two tile shapes (named by short_name from its template arguments)
 PROJ_NAMES = ("proj_256", "proj_128")
@@ -131,7 +131,7 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
-def timeline(directory: str, first: str = "zero_flags", skip: int = 0) -> dict:
+def timeline(directory: str, first: str = "state_pass", skip: int = 0) -> dict:
     """Mean (start, end) offsets in us of each kernel of a step from the step's first start.
 
     Kernels are keyed by short name and occurrence inside the step ("decode", "decode#2").
@@ -182,7 +182,7 @@ def main(argv):
         print(f"source_sha256 = {source_sha256()}")
         return 0
     if len(argv) >= 2 and argv[0] == "timeline":
-        tl = timeline(argv[1], argv[2] if len(argv) > 2 else "zero_flags", int(argv[3]) if len(argv) > 3 else 0)
+        tl = timeline(argv[1], argv[2] if len(argv) > 2 else "state_pass", int(argv[3]) if len(argv) > 3 else 0)
         print(f"{tl['steps']} steps; offsets from the start of each step's first kernel, us (mean)")
         print(f"{'kernel':20s} {'start':>8s} {'end':>8s} {'dur':>8s}")
         for k, a, b in tl["kernels"]:

@@ -569,10 +569,12 @@ def test_concurrent_schedule_equals_split_phases(gdn):
     state pass waits for records the chunk-local kernel publishes while it runs).  Three
     different batches in a row on one workspace, each bit-identical to the split-phase
     calls and the first against the oracle, so a record read before it was written (or a
-    stale one from the previous batch) shows."""
+    stale one from the previous batch) shows.  The workspace starts with every byte 0xff
+    and then holds the previous batch's ready flags: a flag counts only with the call's own
+    value."""
     announce("concurrent schedule: T=8000, Hk=2, Hv=4, three batches on one workspace")
     T, Hk, Hv, d = 8000, 2, 4, 128
-    ws = torch.empty(gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    ws = torch.full((gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"),), 255, dtype=torch.uint8, device=DEV)
     for it in range(3):
         wl = inputs.prefill_workload("conc", 980 + it, [T], Hk, Hv, d, random_states=True)
         x, w, g, b, s0, cs = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state, wl.conv_state))

@@ -9,7 +9,6 @@ from hybrid_linear_attention_gated_amd import profiling
 
 LOCAL = "void gdn::chunk_local_kernel<128, true, __hip_bfloat16>(float const*, ...)"
 STATE = "void gdn::state_pass_kernel<128, true>(char const*, ...)"
-ZERO = "gdn::zero_flags_kernel(int*, int)"
 DECODE = "void gdn::decode_kernel<float, 128, 128, false>(...)"
 COPY = "void at::native::elementwise_kernel<128, 4, ...>(int, ...)"
 
@@ -32,7 +31,6 @@ def test_short_names():
     assert profiling.short_name(LOCAL) == "chunk_local_fused"
     assert profiling.short_name(LOCAL.replace("true", "false")) == "chunk_local"
     assert profiling.short_name(STATE) == "state_pass"
-    assert profiling.short_name(ZERO) == "zero_flags"
     assert profiling.short_name(DECODE) == "decode"
     assert profiling.short_name(DECODE.replace("false>", "true>")) == "decode_gated"
     assert profiling.short_name(COPY) == "copy"
@@ -49,24 +47,22 @@ def test_kernel_stats(tmp_path):
 
 
 def test_timeline_offsets_and_skip(tmp_path):
-    # two steps: zero_flags, then chunk-local and state pass overlapping, then decode (twice in
-    # the second step's position to check occurrence keys); the first step is dropped as warm-up
+    # three steps: the state pass, the chunk-local kernel overlapping it, then decode (twice,
+    # to check occurrence keys); the first step is dropped as warm-up
     launches = []
     for base, extra in ((0, 999_000), (1_000_000, 0), (2_000_000, 2_000)):
-        launches += [(ZERO, base, base + 4_000), (LOCAL, base + 10_000, base + 110_000 + extra),
-                     (STATE, base + 15_000, base + 130_000), (DECODE, base + 131_000, base + 231_000),
-                     (DECODE, base + 232_000, base + 330_000)]
-    tl = profiling.timeline(_trace(tmp_path, launches), "zero_flags", 1)
+        launches += [(STATE, base, base + 130_000), (LOCAL, base + 10_000, base + 110_000 + extra),
+                     (DECODE, base + 131_000, base + 231_000), (DECODE, base + 232_000, base + 330_000)]
+    tl = profiling.timeline(_trace(tmp_path, launches), "state_pass", 1)
     assert tl["steps"] == 2
     got = {k: (a, b) for k, a, b in tl["kernels"]}
-    assert [k for k, _, _ in tl["kernels"]] == ["zero_flags", "chunk_local_fused", "state_pass", "decode",
-                                                "decode#2"]
+    assert [k for k, _, _ in tl["kernels"]] == ["state_pass", "chunk_local_fused", "decode", "decode#2"]
     assert got["chunk_local_fused"] == pytest.approx((10.0, 111.0))   # ends at 110 and 112 us
-    assert got["state_pass"] == pytest.approx((15.0, 130.0))
+    assert got["state_pass"] == pytest.approx((0.0, 130.0))
     assert got["decode#2"] == pytest.approx((232.0, 330.0))
     assert tl["span"] == pytest.approx(330.0)
     with pytest.raises(RuntimeError):
-        profiling.timeline(_trace(tmp_path, launches), "zero_flags", 3)
+        profiling.timeline(_trace(tmp_path, launches), "state_pass", 3)
 
 
 def test_traffic_scaled_by_copy(tmp_path):
