@@ -145,7 +145,8 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *                  bytes (may be NULL when that size is 0); contents are scratch.
  *                  With GDN_MATH_MFMA it holds the per-(chunk, value head) results
  *                  of the chunk-local phase, one state per (sequence, value head) and
- *                  one ready flag per (chunk, value head).
+ *                  one ready flag per (chunk, value head).  It needs no initialisation:
+ *                  each call's ready flags carry a value of that call's own.
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
  *   order          gdn_order (decay before or after the retrieval)
  *
