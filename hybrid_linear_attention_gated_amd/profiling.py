@@ -131,29 +131,35 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
-def timeline(directory: str, first: str = "state_pass", skip: int = 0) -> dict:
+def timeline(directory: str, first: str = "state_pass", skip: int = 0, lead_us: float = 20.0) -> dict:
     """Mean (start, end) offsets in us of each kernel of a step from the step's first start.
 
-    Kernels are keyed by short name and occurrence inside the step ("decode", "decode#2").
-    Returns {"steps": n, "kernels": [(key, start, end), ...] in order of mean start,
-    "span": mean first-start-to-last-end}."""
+    A step begins at each launch of the kernel `first`; a kernel that starts up to
+    `lead_us` before such a launch belongs to that step too (kernels on two streams do not
+    always start in issue order).  Kernels are keyed by short name and occurrence inside
+    the step ("decode", "decode#2").  Returns {"steps": n, "kernels": [(key, start, end),
+    ...] in order of mean start, "span": mean first-start-to-last-end}."""
     rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
-    steps, cur = [], None
-    for r in rows:
-        name = short_name(r["Kernel_Name"])
-        if name == first:
-            cur = []
-            steps.append(cur)
-        if cur is not None:
-            cur.append((name, int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    recs = [(short_name(r["Kernel_Name"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+    marks = [a for n, a, _ in recs if n == first]
+    if not marks:
+        raise RuntimeError(f"no step starting with {first} under {directory}")
+    steps = [[] for _ in marks]
+    lead = int(lead_us * 1e3)
+    j = -1
+    for rec in recs:
+        while j + 1 < len(marks) and marks[j + 1] <= rec[1] + lead:
+            j += 1
+        if j >= 0:
+            steps[j].append(rec)
     steps = steps[skip:]
     if not steps:
         raise RuntimeError(f"no step starting with {first} under {directory}")
     acc, spans = defaultdict(list), []
     for st in steps:
-        t0 = st[0][1]
+        t0 = min(a for _, a, _ in st)
         seen = defaultdict(int)
-        for name, a, b in st:
+        for name, a, b in sorted(st, key=lambda t: t[1]):
             seen[name] += 1
             key = name if seen[name] == 1 else f"{name}#{seen[name]}"
             acc[key].append(((a - t0) / 1e3, (b - t0) / 1e3))

@@ -47,22 +47,25 @@ def test_kernel_stats(tmp_path):
 
 
 def test_timeline_offsets_and_skip(tmp_path):
-    # three steps: the state pass, the chunk-local kernel overlapping it, then decode (twice,
-    # to check occurrence keys); the first step is dropped as warm-up
+    # four steps: the state pass, the chunk-local kernel overlapping it, then decode (twice,
+    # to check occurrence keys); the first step is dropped as warm-up; in the last step the
+    # chunk-local kernel starts 2 us before the state pass and still belongs to that step
     launches = []
-    for base, extra in ((0, 999_000), (1_000_000, 0), (2_000_000, 2_000)):
-        launches += [(STATE, base, base + 130_000), (LOCAL, base + 10_000, base + 110_000 + extra),
+    for base, local0, extra in ((0, 10_000, 999_000), (1_000_000, 10_000, 0), (2_000_000, 10_000, 2_000),
+                                (3_000_000, -2_000, 0)):
+        launches += [(STATE, base, base + 130_000), (LOCAL, base + local0, base + 110_000 + extra),
                      (DECODE, base + 131_000, base + 231_000), (DECODE, base + 232_000, base + 330_000)]
     tl = profiling.timeline(_trace(tmp_path, launches), "state_pass", 1)
-    assert tl["steps"] == 2
+    assert tl["steps"] == 3
     got = {k: (a, b) for k, a, b in tl["kernels"]}
     assert [k for k, _, _ in tl["kernels"]] == ["state_pass", "chunk_local_fused", "decode", "decode#2"]
-    assert got["chunk_local_fused"] == pytest.approx((10.0, 111.0))   # ends at 110 and 112 us
-    assert got["state_pass"] == pytest.approx((0.0, 130.0))
-    assert got["decode#2"] == pytest.approx((232.0, 330.0))
-    assert tl["span"] == pytest.approx(330.0)
+    # offsets count from each step's first start: the last step starts with the chunk-local kernel
+    assert got["chunk_local_fused"] == pytest.approx(((10 + 10 + 0) / 3, (110 + 112 + 112) / 3))
+    assert got["state_pass"] == pytest.approx(((0 + 0 + 2) / 3, (130 + 130 + 132) / 3))
+    assert got["decode#2"] == pytest.approx(((232 + 232 + 234) / 3, (330 + 330 + 332) / 3))
+    assert tl["span"] == pytest.approx((330 + 330 + 332) / 3)
     with pytest.raises(RuntimeError):
-        profiling.timeline(_trace(tmp_path, launches), "state_pass", 3)
+        profiling.timeline(_trace(tmp_path, launches), "state_pass", 4)
 
 
 def test_traffic_scaled_by_copy(tmp_path):
