@@ -240,7 +240,7 @@ def main():
     lws = torch.empty(gdn.layer_prefill_workspace_size(T, N, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
     dh = inputs.layer_hidden(11, B, E).to(dev)
     dlout = torch.empty((B, E), dtype=torch.bfloat16, device=dev)
-    dlws = torch.empty(gdn.layer_decode_workspace_size(B, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
+    dlws = torch.empty(gdn.layer_decode_workspace_size(B, E, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
     px = torch.empty((T, wl.conv_dim), dtype=torch.bfloat16, device=dev)
     pz = torch.empty((T, Z), dtype=torch.bfloat16, device=dev)
     pg = torch.empty((T, Hv), dtype=torch.float32, device=dev)

@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_prefill_workspace_size.restype = Z
         L.gdn_layer_prefill.argtypes = [P, P, P, P, P, P, I, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_layer_prefill.restype = I
-        L.gdn_layer_decode_workspace_size.argtypes = [I, I, I, I, I]
+        L.gdn_layer_decode_workspace_size.argtypes = [I, I, I, I, I, I]
         L.gdn_layer_decode_workspace_size.restype = Z
         L.gdn_layer_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_layer_decode.restype = I
@@ -428,8 +428,8 @@ def layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) -> int:
     return int(lib().gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv))
 
 
-def layer_decode_workspace_size(B, Hk, Hv, dk, dv) -> int:
-    return int(lib().gdn_layer_decode_workspace_size(B, Hk, Hv, dk, dv))
+def layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) -> int:
+    return int(lib().gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv))
 
 
 def layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, cu_seqlens=None, conv_state_in=None,
@@ -479,7 +479,7 @@ def layer_decode(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, 
     _check(conv_state, "conv_state", bf, (B, 3, C))
     _check(state, "state", torch.float32, (B, Hv, dk, dv))
     out = torch.empty((B, E), dtype=bf, device=hidden.device) if out is None else _check(out, "out", bf, (B, E))
-    need = layer_decode_workspace_size(B, Hk, Hv, dk, dv)
+    need = layer_decode_workspace_size(B, E, Hk, Hv, dk, dv)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
     _check(workspace, "workspace")

@@ -354,10 +354,18 @@ int in_proj_impl(const void *hidden, const void *w_in, void *x, void *z, float *
     return hip_status(gdn::launch_proj(a, st));
 }
 
-int linear_impl(const void *a, const void *w, void *y, int M, int N, int K, hipStream_t st) {
+// partial (optional, partial_cap floats): lets the launcher split k when the output has
+// few tiles (the layer decode's output projection)
+int linear_impl(const void *a, const void *w, void *y, int M, int N, int K, hipStream_t st,
+                float *partial = nullptr, size_t partial_cap = 0) {
     gdn::ProjArgs p{a, w, M, N, K, y, N, N, nullptr, 0};
+    p.partial = partial;
+    p.partial_cap = partial_cap;
     return hip_status(gdn::launch_proj(p, st));
 }
+
+// k slices the layer decode's output projection may be split into (partial-sum planes)
+constexpr int kDecodeProjSplits = 16;
 
 // Shapes the layer entry points accept: the projections' k extents (E and Hv dv) are
 // multiples of 64, the gate columns fit the gate workgroups, and dk, dv are 16-multiples.
@@ -388,10 +396,10 @@ LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
 }
 
 struct LayerDecodeWs {
-    size_t x, z, g, beta, y, total;
+    size_t x, z, g, beta, y, partial, total;
 };
 
-LayerDecodeWs layer_decode_ws(int B, int Hk, int Hv, int dk, int dv) {
+LayerDecodeWs layer_decode_ws(int B, int E, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerDecodeWs w{};
     w.x = 0;
@@ -399,7 +407,8 @@ LayerDecodeWs layer_decode_ws(int B, int Hk, int Hv, int dk, int dv) {
     w.g = w.z + align256((size_t)B * Z * 2);
     w.beta = w.g + align256((size_t)B * Hv * 4);
     w.y = w.beta + align256((size_t)B * Hv * 4);
-    w.total = w.y + align256((size_t)B * Z * 2);
+    w.partial = w.y + align256((size_t)B * Z * 2);
+    w.total = w.partial + align256((size_t)kDecodeProjSplits * B * E * 4);
     return w;
 }
 
@@ -497,9 +506,9 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
     }
 }
 
-size_t gdn_layer_decode_workspace_size(int B, int Hk, int Hv, int dk, int dv) {
-    if (B < 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return 0;
-    return layer_decode_ws(B, Hk, Hv, dk, dv).total;
+size_t gdn_layer_decode_workspace_size(int B, int E, int Hk, int Hv, int dk, int dv) {
+    if (B < 0 || E <= 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return 0;
+    return layer_decode_ws(B, E, Hk, Hv, dk, dv).total;
 }
 
 int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
@@ -516,7 +525,7 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
         if (!std::isfinite(scale) || !(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !(norm_eps >= 0.f) ||
             !std::isfinite(norm_eps))
             return GDN_ERR_BAD_SHAPE;
-        const LayerDecodeWs L = layer_decode_ws(B, Hk, Hv, dk, dv);
+        const LayerDecodeWs L = layer_decode_ws(B, E, Hk, Hv, dk, dv);
         if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
         const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
         const Range rh{hidden, (size_t)B * E * 2}, rwi{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
@@ -538,7 +547,8 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
         if (int e = decode_impl(x, conv_w, conv_state, g, beta, state, nullptr, z, gamma, y, scale, l2_eps,
                                 norm_eps, B, Hk, Hv, dk, dv, GDN_BF16, order, stream))
             return e;
-        return linear_impl(y, w_out, out, B, E, (int)Z, st);
+        return linear_impl(y, w_out, out, B, E, (int)Z, st, reinterpret_cast<float *>(ws + L.partial),
+                           (size_t)kDecodeProjSplits * B * E);
     } catch (...) {
         return GDN_ERR_HIP;
     }

@@ -87,7 +87,11 @@ struct ProjArgs {
     int ld1;
     float *g = nullptr, *beta = nullptr;
     int heads = 0;
-    int tiles_m = 0, tiles_n = 0, ntiles = 0;   // set by the launcher
+    // optional fp32 buffer of partial_cap floats: with few tiles (and no gate columns) the
+    // launcher splits k and sums the slices' planes in a second pass
+    float *partial = nullptr;
+    size_t partial_cap = 0;
+    int tiles_m = 0, tiles_n = 0, ntiles = 0, ksplit = 1;   // set by the launcher
 };
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st);

@@ -40,6 +40,8 @@
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
+#include <algorithm>
+
 namespace gdn {
 
 constexpr int kProjThreads = 256;
@@ -116,8 +118,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16 *base, in
 }
 
 // One output tile: rows m0.., columns n0.. of the main (non-gate) columns.
+// k stages [kt0, kt1) of the tile; with p.ksplit > 1 the fp32 sums go to partial sum
+// plane `split` instead of the bf16 outputs.
 template <int WM, int WN, int BK>
-__device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, char *smem) {
+__device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, char *smem, int kt0, int kt1,
+                                          int split) {
     using S = ProjTile<WM, WN, BK>;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave >> 1, wn = wave & 1;
@@ -185,17 +190,16 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
     static_assert(MF % FR == 0 || FR % MF == 0, "read / MFMA interleave");
     static_assert((NW > MF ? NW % MF : MF % NW) == 0, "write / MFMA interleave");
 
-    const int KT = K / BK;
     // One stage: `wr` holds stage kt + 1 (loaded a stage ago) and is written to the idle LDS
     // buffer during the last k-step; `ld` (free) receives stage kt + 2's loads at the start.
     // The order is fixed by scheduling groups: step 0's fragment reads, the global loads,
     // each step's MFMAs with the next step's reads between them, the LDS writes between
     // the last step's MFMAs.  Past the end the loads repeat the last stage (never used).
     auto stage = [&](int kt, const Stg &wr, Stg &ld) {
-        const int buf = kt & 1;
+        const int buf = (kt - kt0) & 1;
         Frags f0, f1;
         fread(buf, 0, f0);
-        gload(min(kt + 2, KT - 1), ld);
+        gload(min(kt + 2, kt1 - 1), ld);
 #pragma unroll
         for (int s = 0; s < S::KSTEPS; ++s) {
             Frags &cur = (s & 1) ? f1 : f0;
@@ -222,16 +226,16 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
         __syncthreads();
     };
     Stg s0, s1;
-    gload(0, s0);
-    gload(min(1, KT - 1), s1);
+    gload(kt0, s0);
+    gload(min(kt0 + 1, kt1 - 1), s1);
     swrite(0, s0);
     __syncthreads();
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
+    int kt = kt0;
+    for (; kt + 1 < kt1; kt += 2) {
         stage(kt, s1, s0);
         stage(kt + 1, s0, s1);
     }
-    if (kt < KT) stage(kt, s1, s0);
+    if (kt < kt1) stage(kt, s1, s0);
 
     // lane holds y[m][n + 8 g + 4 (lane / 32) + 0..3] of each 32 x 32 block, g < 4
 #pragma unroll
@@ -244,6 +248,11 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * WN + 32 * i + 8 * g + 4 * (lane >> 5);
                 if (n >= N) continue;
+                if (p.ksplit > 1) {
+                    *reinterpret_cast<f32x4 *>(p.partial + ((size_t)split * M + m) * N + n) =
+                        f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    continue;
+                }
                 bf16 *dst = n < p.n_split ? static_cast<bf16 *>(p.y0) + (size_t)m * p.ld0 + n
                                           : static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split);
                 store_bf16x4(dst, f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
@@ -320,6 +329,12 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
         return;
     }
     b -= gate_blocks;
+    const int KT = p.K / BK;
+    if (p.ksplit > 1) {   // split k: block = (tile, k slice), the slices of a tile adjacent
+        const int split = b % p.ksplit, tile = b / p.ksplit, per = KT / p.ksplit;
+        proj_tile<WM, WN, BK>(p, tile / p.tiles_n, tile % p.tiles_n, smem, split * per, split * per + per, split);
+        return;
+    }
     // XCD x (blocks x, x + 8, ...) takes tiles [x T / 8, (x + 1) T / 8)
     if ((p.ntiles & 7) == 0) b = (b & 7) * (p.ntiles >> 3) + (b >> 3);
     // groups of kTileGroup row tiles run over all column tiles, row tile fastest
@@ -327,7 +342,22 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs p) {
     const int grp = b / per_group, first = grp * kTileGroup;
     const int gm = min(kTileGroup, p.tiles_m - first);
     const int r = b - grp * per_group;
-    proj_tile<WM, WN, BK>(p, first + r % gm, r / gm, smem);
+    proj_tile<WM, WN, BK>(p, first + r % gm, r / gm, smem, 0, KT, 0);
+}
+
+// Split-k second pass: y = bf16(sum of the ksplit fp32 partial planes, in plane order),
+// routed like the tile epilogue; one thread per 4 consecutive columns.
+__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs p) {
+    const long q = (long)blockIdx.x * 256 + threadIdx.x;
+    const int nq = p.N / 4;
+    if (q >= (long)p.M * nq) return;
+    const int m = (int)(q / nq), n = 4 * (int)(q % nq);
+    const size_t plane = (size_t)p.M * p.N, at = (size_t)m * p.N + n;
+    f32x4 t = *reinterpret_cast<const f32x4 *>(p.partial + at);
+    for (int sp = 1; sp < p.ksplit; ++sp) t += *reinterpret_cast<const f32x4 *>(p.partial + sp * plane + at);
+    bf16 *dst = n < p.n_split ? static_cast<bf16 *>(p.y0) + (size_t)m * p.ld0 + n
+                              : static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split);
+    store_bf16x4(dst, t);
 }
 
 template <int WM, int WN, int BK>
@@ -336,11 +366,29 @@ static hipError_t launch_proj_t(ProjArgs p, hipStream_t st) {
     p.tiles_m = (p.M + S::BM - 1) / S::BM;
     p.tiles_n = (p.N + S::BN - 1) / S::BN;
     p.ntiles = p.tiles_m * p.tiles_n;
+    // Split k when the tiles fill a quarter of the compute units or less and a partial-sum
+    // buffer is given: the largest divisor of the stage count up to cus / tiles (at least 4)
+    // whose planes fit the buffer.  The slices' fp32 sums meet in a second pass, in a fixed
+    // order.
+    p.ksplit = 1;
+    if (p.partial && p.heads == 0) {
+        const int KT = p.K / BK, cus = device_cus() > 0 ? device_cus() : 256;
+        const int want = cus / p.ntiles;
+        for (int d = std::min(want, KT); d >= 4; --d)
+            if (KT % d == 0 && (size_t)d * p.M * p.N <= p.partial_cap) {
+                p.ksplit = d;
+                break;
+            }
+    }
     const int gate_blocks = p.heads > 0 ? (p.M + kGateRows - 1) / kGateRows : 0;
-    const long blocks = (long)p.ntiles + gate_blocks;
+    const long blocks = (long)p.ntiles * p.ksplit + gate_blocks;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
     hipLaunchKernelGGL((proj_kernel<WM, WN, BK>), dim3((unsigned)blocks), dim3(kProjThreads), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.ksplit == 1) return e;
+    const long quads = (long)p.M * (p.N / 4);
+    hipLaunchKernelGGL(proj_reduce_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

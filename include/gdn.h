@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum {
     GDN_OK = 0,
@@ -362,10 +362,12 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
  * gdn_linear with w_out.
  *   hidden [B][E] bf16; weights as in gdn_layer_prefill; conv_state [B][3][conv_dim]
  *   bf16 and state [B][Hv][dk][dv] fp32 in/out; out [B][E] bf16.
- *   workspace  at least gdn_layer_decode_workspace_size(B, Hk, Hv, dk, dv) bytes.
+ *   workspace  at least gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) bytes (x, z, g,
+ *              beta, the normalised output and fp32 partial sums of the output projection,
+ *              whose k extent is split over more compute units when B is small).
  * dk, dv in {16, 32, 64, 128}; E and Hv as in gdn_in_proj.
  */
-size_t gdn_layer_decode_workspace_size(int B, int Hk, int Hv, int dk, int dv);
+size_t gdn_layer_decode_workspace_size(int B, int E, int Hk, int Hv, int dk, int dv);
 int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
                      const void *w_out, void *conv_state, float *state, void *out,
                      float scale, float l2_eps, float norm_eps,

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 4
+    assert L.gdn_abi_version() == 5
     for code in range(8):
         assert L.gdn_status_string(code).decode().startswith("GDN_")
     assert b"unknown" in L.gdn_status_string(99)
@@ -279,7 +279,7 @@ def test_layer_prefill_validation(L):
 
 def test_layer_decode_validation(L):
     P = _ptr
-    ws = L.gdn_layer_decode_workspace_size(4, 1, 2, 64, 64)
+    ws = L.gdn_layer_decode_workspace_size(4, 64, 1, 2, 64, 64)
     assert ws > 0
     base = dict(h=P(0), wi=P(1 << 24), cw=P(2 << 24), gm=P(3 << 24), wo=P(4 << 24), cs=P(5 << 24), st=P(6 << 24),
                 out=P(7 << 24), B=4, E=64, Hk=1, Hv=2, dk=64, dv=64, order=0, ws=P(1 << 28), wsb=ws)

@@ -165,7 +165,10 @@ def _decode_case(gdn, B, E, Hk, Hv, d, seed, order=0):
     return (out, std, csd), (out_ref, st_ref, cs_ref)
 
 
-@pytest.mark.parametrize("B,E,Hk,Hv,d,order", [(5, 128, 2, 4, 32, 0), (3, 64, 1, 1, 64, 1), (256, 1024, 16, 16, 128, 0)])
+# (33, 192, ...) and (256, 1024, ...) split the output projection's k extent (4 and 16 slices
+# summed in a second pass; 33 x 192 also leaves a partial column tile)
+@pytest.mark.parametrize("B,E,Hk,Hv,d,order", [(5, 128, 2, 4, 32, 0), (3, 64, 1, 1, 64, 1), (33, 192, 2, 4, 128, 0),
+                                               (256, 1024, 16, 16, 128, 0)])
 def test_layer_decode(gdn, B, E, Hk, Hv, d, order):
     announce(f"layer decode B={B} E={E} Hk={Hk} Hv={Hv} d={d} order={order}")
     (out, st, cs), (out_ref, st_ref, cs_ref) = _decode_case(gdn, B, E, Hk, Hv, d, 660 + B, order)
