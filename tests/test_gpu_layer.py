@@ -132,6 +132,16 @@ def test_layer_prefill_gqa_128(gdn):
     np.testing.assert_array_equal(f32np(cs), cs_ref)
 
 
+def test_layer_prefill_wide_gates_gqa4(gdn):
+    """32 value heads over 8 key heads (the widest gate block the input projection takes: 64
+    gate columns) at head dim 64, two sequences with caches in."""
+    announce("layer prefill Hk=8 Hv=32 d=64 two sequences")
+    (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [120, 77], 256, 8, 32, 64, 635, True, 0.5)
+    assert_parity("out", f32np(out), out_ref, TOL_BF16)
+    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
+    np.testing.assert_array_equal(f32np(cs), cs_ref)
+
+
 def test_layer_prefill_0p8b_shape(gdn):
     """The 0.8B layer shape: T = 4096, hidden 1024, 16 / 16 heads of 128, zero caches."""
     announce("layer prefill T=4096 E=1024 16/16 heads d=128")
