@@ -235,10 +235,11 @@ def main():
     w_in, lcw, lgam, w_out = lw.w_in.to(dev), lw.conv_w.to(dev), lw.gamma.to(dev), lw.w_out.to(dev)
     hs = [inputs.layer_hidden(8 + i, T, E).to(dev) for i in range(R)]
     lout = torch.empty((T, E), dtype=torch.bfloat16, device=dev)
-    lcso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=dev)
+    lcso = torch.empty((N, 3, wl.conv_dim), dtype=torch.float32, device=dev)
     lfin = torch.empty((N, Hv, d, d), dtype=torch.float32, device=dev)
     lws = torch.empty(gdn.layer_prefill_workspace_size(T, N, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
     dh = inputs.layer_hidden(11, B, E).to(dev)
+    lcs_dec = [dw.conv_state.float().to(dev) for _ in range(Rd)]   # the layer keeps fp32 conv caches
     dlout = torch.empty((B, E), dtype=torch.bfloat16, device=dev)
     dlws = torch.empty(gdn.layer_decode_workspace_size(B, E, Hk, Hv, d, d), dtype=torch.uint8, device=dev)
     px = torch.empty((T, wl.conv_dim), dtype=torch.bfloat16, device=dev)
@@ -308,7 +309,7 @@ def main():
         gdn.layer_prefill(hs[r], w_in, lcw, lgam, w_out, Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=lcso,
                           final_state=lfin, out=lout, workspace=lws)
         ev[1].record()
-        gdn.layer_decode(dh, w_in, lcw, lgam, w_out, dcs[i % Rd], dstate[i % Rd], Hk, Hv, d, d, out=dlout,
+        gdn.layer_decode(dh, w_in, lcw, lgam, w_out, lcs_dec[i % Rd], dstate[i % Rd], Hk, Hv, d, d, out=dlout,
                          workspace=dlws)
         ev[2].record()
         torch.mm(hs[r], w_in.t(), out=lib_in)

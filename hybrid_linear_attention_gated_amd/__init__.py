@@ -24,12 +24,15 @@ import torch
 __all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_rmsnorm", "decode_step_gated", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
            "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
            "LIB_PATH", "abi_version", "mfma_supported", "linear", "in_proj", "layer_prefill", "layer_decode",
-           "layer_prefill_workspace_size", "layer_decode_workspace_size"]
+           "layer_prefill_workspace_size", "layer_decode_workspace_size", "prefill_workspace_status",
+           "GDN_OK", "GDN_ERR_TIMEOUT", "GDN_ERR_NONFINITE", "set_wait_bound"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 GDN_MATH_F32, GDN_MATH_MFMA = 0, 1
 GDN_ORDER_DECAY_FIRST, GDN_ORDER_RETRIEVE_FIRST = 0, 1
+GDN_OK, GDN_ERR_TIMEOUT, GDN_ERR_NONFINITE = 0, 8, 9
+_SPIN_TAG = 0x7370696E   # high half of the workspace header word that bounds the state pass's waits
 _lib = None
 
 
@@ -81,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_decode_workspace_size.restype = Z
         L.gdn_layer_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_layer_decode.restype = I
+        L.gdn_prefill_workspace_status.argtypes = [P, Z, P]
+        L.gdn_prefill_workspace_status.restype = I
         L.gdn_status_string.argtypes = [I]
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_abi_version.argtypes = []
@@ -222,6 +227,25 @@ def prefill_local(x, conv_w, g, beta, workspace, Hk, Hv, dk, dv, cu_seqlens=None
                                  workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise GdnError("gdn_prefill_local", st)
+
+
+def prefill_workspace_status(workspace) -> int:
+    """Status of the chunked prefills that used `workspace` since the last query (GDN_OK,
+    GDN_ERR_TIMEOUT or GDN_ERR_NONFINITE); waits for their completion and clears it."""
+    _check(workspace, "workspace")
+    st = lib().gdn_prefill_workspace_status(_p(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if st not in (GDN_OK, GDN_ERR_TIMEOUT, GDN_ERR_NONFINITE):
+        raise GdnError("gdn_prefill_workspace_status", st)
+    return st
+
+
+def set_wait_bound(workspace, iterations=None):
+    """Write the workspace header word that bounds the concurrent state pass's waits for a
+    record (`iterations` of a ~128-cycle sleep), or restore the default (None).  For tests
+    of the timeout path."""
+    _check(workspace, "workspace", torch.uint8)
+    word = 0 if iterations is None else (_SPIN_TAG << 32) | int(iterations)
+    workspace[8:16].copy_(torch.tensor([word], dtype=torch.int64).view(torch.uint8))
 
 
 def mfma_supported(dk, dv) -> bool:
@@ -438,7 +462,8 @@ def layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, cu_seqlens
     """The linear-attention layer over packed sequences: hidden [T, E] bf16 -> out [T, E]
     bf16 (input projection, conv + SiLU + L2, gated delta rule, gated RMSNorm, output
     projection).  Weights bf16: w_in [conv_dim + Hv dv + 2 Hv, E], conv_w [conv_dim, 4],
-    gamma [dv], w_out [E, Hv dv].  Caches as in `prefill`.  Returns (out, final_state)."""
+    gamma [dv], w_out [E, Hv dv].  Conv caches [N, 3, conv_dim] fp32 (the layer keeps its
+    pre-conv inputs in fp32), states as in `prefill`.  Returns (out, final_state)."""
     bf, f32 = torch.bfloat16, torch.float32
     _check(hidden, "hidden", bf)
     if hidden.dim() != 2:
@@ -446,8 +471,8 @@ def layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, cu_seqlens
     T, E = hidden.shape
     C = _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv)
     cu, N = _seqs(cu_seqlens, T)
-    _check(conv_state_in, "conv_state_in", bf, (N, 3, C), optional=True)
-    _check(conv_state_out, "conv_state_out", bf, (N, 3, C), optional=True)
+    _check(conv_state_in, "conv_state_in", f32, (N, 3, C), optional=True)
+    _check(conv_state_out, "conv_state_out", f32, (N, 3, C), optional=True)
     _check(initial_state, "initial_state", f32, (N, Hv, dk, dv), optional=True)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, Hv, dk, dv), dtype=f32, device=hidden.device)
@@ -469,14 +494,14 @@ def layer_prefill(hidden, w_in, conv_w, gamma, w_out, Hk, Hv, dk, dv, cu_seqlens
 def layer_decode(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, dk, dv, scale=1.0, l2_eps=1e-6,
                  norm_eps=1e-6, out=None, workspace=None, order=0):
     """One token per sequence through the layer: hidden [B, E] bf16 -> out [B, E] bf16;
-    conv_state [B, 3, conv_dim] bf16 and state [B, Hv, dk, dv] fp32 are updated in place."""
+    conv_state [B, 3, conv_dim] fp32 and state [B, Hv, dk, dv] fp32 are updated in place."""
     bf = torch.bfloat16
     _check(hidden, "hidden", bf)
     if hidden.dim() != 2:
         raise ValueError("hidden must be [B, E]")
     B, E = hidden.shape
     C = _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv)
-    _check(conv_state, "conv_state", bf, (B, 3, C))
+    _check(conv_state, "conv_state", torch.float32, (B, 3, C))
     _check(state, "state", torch.float32, (B, Hv, dk, dv))
     out = torch.empty((B, E), dtype=bf, device=hidden.device) if out is None else _check(out, "out", bf, (B, E))
     need = layer_decode_workspace_size(B, E, Hk, Hv, dk, dv)

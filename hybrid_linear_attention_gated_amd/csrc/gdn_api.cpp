@@ -7,7 +7,10 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 #include <initializer_list>
+#include <vector>
 
 #include "gdn_launch.hpp"
 
@@ -47,6 +50,38 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
 bool valid_order(int order) { return order == GDN_ORDER_DECAY_FIRST || order == GDN_ORDER_RETRIEVE_FIRST; }
 
+static_assert(gdn::kStatusTimeout == GDN_ERR_TIMEOUT && gdn::kStatusNonFinite == GDN_ERR_NONFINITE,
+              "device status codes are the ABI's");
+
+// GDN_DEBUG_CHECK set (and not "0") in the environment when the library first looks:
+// prefill calls then check cu_seqlens on the host before launching and wait for their own
+// completion to return the workspace status (timeout, non-finite output).
+bool debug_check() {
+    static const bool on = [] {
+        const char *v = std::getenv("GDN_DEBUG_CHECK");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+// The debug check of cu_seqlens: cu[0] = 0, non-decreasing, cu[N] = T.
+int check_seqlens_on_host(const int32_t *cu, int N, int T, hipStream_t st) {
+    if (!cu) return GDN_OK;
+    std::vector<int32_t> h((size_t)N + 1);
+    if (gdn::copy_seqlens(cu, N + 1, st, h.data()) != hipSuccess) return GDN_ERR_HIP;
+    if (h[0] != 0 || h[(size_t)N] != T) return GDN_ERR_BAD_SHAPE;
+    for (int i = 0; i < N; ++i)
+        if (h[(size_t)i + 1] < h[(size_t)i]) return GDN_ERR_BAD_SHAPE;
+    return GDN_OK;
+}
+
+// The status of a chunked prefill's workspace (its header word), cleared as it is read.
+int take_status(void *ws, hipStream_t st) {
+    unsigned long long w = 0;
+    if (gdn::workspace_status(ws, st, &w, true) != hipSuccess) return GDN_ERR_HIP;
+    return (unsigned)(w >> 32) == gdn::kStatusTag ? (int)(w & 0xffffffffu) : GDN_OK;
+}
+
 // Every non-NULL device pointer is 16-byte aligned (the kernels move 16-byte vectors).
 bool aligned16(std::initializer_list<const void *> ptrs) {
     for (const void *p : ptrs)
@@ -68,6 +103,9 @@ const char *gdn_status_string(int status) {
         case GDN_ERR_HIP: return "GDN_ERR_HIP: a HIP launch or runtime call failed";
         case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps an input it must not overlap";
         case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a device pointer is not 16-byte aligned";
+        case GDN_ERR_TIMEOUT:
+            return "GDN_ERR_TIMEOUT: the state pass stopped waiting for a chunk's record; outputs are NaN";
+        case GDN_ERR_NONFINITE: return "GDN_ERR_NONFINITE: an output or final state is inf or NaN";
         default: return "unknown gdn status";
     }
 }
@@ -150,7 +188,15 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
                            T, Hk, Hv, dk, dv, workspace, workspace_bytes};
         a.order = order;
         hipStream_t st = (hipStream_t)stream;
-        return hip_status(chunked ? gdn::launch_prefill_chunked(a, st, phases) : gdn::launch_prefill_recurrent(a, st));
+        const bool dbg = debug_check();
+        if (dbg) {
+            if (int e = check_seqlens_on_host(cu_seqlens, N, T, st)) return e;
+            if (chunked && (phases & 1)) (void)take_status(workspace, st);   // start from a clear status word
+        }
+        if (int e = hip_status(chunked ? gdn::launch_prefill_chunked(a, st, phases)
+                                       : gdn::launch_prefill_recurrent(a, st)))
+            return e;
+        return dbg && chunked && (phases & 2) ? take_status(workspace, st) : GDN_OK;
     } catch (...) {
         return GDN_ERR_HIP;
     }
@@ -184,10 +230,13 @@ int gdn_chunk_prefill_state(const int32_t *cu_seqlens, int N, const float *initi
 namespace {
 
 // Shared validation + dispatch of gdn_prefill (phases 3) and gdn_prefill_local (phase 1).
+// layer_types: the layer's prefill (x and the conv caches fp32, conv weights bf16; dtype
+// is then ignored).
 int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N, const void *conv_state_in,
                  void *conv_state_out, const float *g, const float *beta, const float *initial_state,
                  float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
-                 int dtype, int order, void *workspace, size_t workspace_bytes, void *stream, int phases) {
+                 int dtype, int order, void *workspace, size_t workspace_bytes, void *stream, int phases,
+                 bool layer_types = false) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
         if (!conv_w || (T > 0 && (!x || !g || !beta || ((phases & 2) && !o)))) return GDN_ERR_NULL_POINTER;
@@ -200,10 +249,10 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
         if (!(l2_eps >= 0.f) || !std::isfinite(l2_eps) || !std::isfinite(scale)) return GDN_ERR_BAD_SHAPE;
         const size_t need = gdn::chunked_workspace_bytes(T, N, Hv, dk, dv);
         if (!workspace || workspace_bytes < need) return GDN_ERR_WORKSPACE;
-        const size_t eb = elem_bytes(dtype);
+        const size_t eb = layer_types ? 4 : elem_bytes(dtype), wb = layer_types ? 2 : eb;
         const size_t conv_dim = 2 * (size_t)Hk * dk + (size_t)Hv * dv;
         const size_t st_bytes = (size_t)N * Hv * dk * dv * 4;
-        const Range rx{x, (size_t)T * conv_dim * eb}, rw{conv_w, conv_dim * 4 * eb};
+        const Range rx{x, (size_t)T * conv_dim * eb}, rw{conv_w, conv_dim * 4 * wb};
         const Range rci{conv_state_in, (size_t)N * 3 * conv_dim * eb}, rco{conv_state_out, rci.bytes};
         const Range rg{g, (size_t)T * Hv * 4}, rb{beta, rg.bytes}, rs0{initial_state, st_bytes},
             rsf{final_state, st_bytes}, ro{o, (size_t)T * Hv * dv * 4}, rws{workspace, need};
@@ -216,11 +265,19 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
         for (Range in : {rx, rw, rci, rg, rb, rs0})
             if (overlap(rws, in)) return GDN_ERR_ALIAS;
         if (bad_partial_alias(rsf, rs0) || bad_partial_alias(rco, rci)) return GDN_ERR_ALIAS;
-        const gdn::FusedPrep fp{x, conv_w, conv_state_in, conv_state_out, dtype == GDN_BF16, l2_eps};
+        const gdn::FusedPrep fp{x, conv_w, conv_state_in, conv_state_out, !layer_types && dtype == GDN_BF16, l2_eps,
+                                layer_types};
         gdn::PrefillArgs a{nullptr, nullptr, nullptr, g, beta, cu_seqlens, N, initial_state, final_state, o, scale,
                            T, Hk, Hv, dk, dv, workspace, workspace_bytes, &fp};
         a.order = order;
-        return hip_status(gdn::launch_prefill_chunked(a, (hipStream_t)stream, phases));
+        hipStream_t st = (hipStream_t)stream;
+        const bool dbg = debug_check();
+        if (dbg) {
+            if (int e = check_seqlens_on_host(cu_seqlens, N, T, st)) return e;
+            (void)take_status(workspace, st);   // start from a clear status word
+        }
+        if (int e = hip_status(gdn::launch_prefill_chunked(a, st, phases))) return e;
+        return dbg && (phases & 2) ? take_status(workspace, st) : GDN_OK;
     } catch (...) {
         return GDN_ERR_HIP;
     }
@@ -235,6 +292,17 @@ int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, in
     return prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
                         final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, dtype, order, workspace, workspace_bytes,
                         stream, 3);
+}
+
+int gdn_prefill_workspace_status(void *workspace, size_t workspace_bytes, void *stream) {
+    try {
+        if (!workspace) return GDN_ERR_NULL_POINTER;
+        if (!aligned16({workspace})) return GDN_ERR_ALIGN;
+        if (workspace_bytes < gdn::kWsHeader) return GDN_ERR_WORKSPACE;
+        return take_status(workspace, (hipStream_t)stream);
+    } catch (...) {
+        return GDN_ERR_HIP;
+    }
 }
 
 int gdn_prefill_local(const void *x, const void *conv_w, const int32_t *cu_seqlens, int N,
@@ -344,13 +412,20 @@ bool proj_shape_ok(int M, int N, int K) {
     return M >= 0 && N > 0 && N % 4 == 0 && K > 0 && K % 64 == 0 && K <= kProjMaxK;
 }
 
+// gain == NULL: the public input projection (x and z bf16).  gain set: the layer's (x
+// fp32, and gain * SiLU(z) in bf16 in place of z).
 int in_proj_impl(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta, int T, int E,
-                 int Hk, int Hv, int dk, int dv, hipStream_t st) {
+                 int Hk, int Hv, int dk, int dv, hipStream_t st, const void *gain = nullptr) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     gdn::ProjArgs a{hidden, w_in, T, (int)(C + Z), E, x, (int)C, (int)C, z, (int)Z};
     a.g = g;
     a.beta = beta;
     a.heads = Hv;
+    if (gain) {
+        a.y0_f32 = true;
+        a.gate_gain = gain;
+        a.gate_dv = dv;
+    }
     return hip_status(gdn::launch_proj(a, st));
 }
 
@@ -369,10 +444,13 @@ constexpr int kDecodeProjSplits = 16;
 
 // Shapes the layer entry points accept: the projections' k extents (E and Hv dv) are
 // multiples of 64, the gate columns fit the gate workgroups, and dk, dv are 16-multiples.
-int check_layer_shape(int E, int Hk, int Hv, int dk, int dv) {
+// norm_stage: the output projection forms the gated RMSNorm as it stages whole heads 128 k
+// deep (the layer prefill), so Hv dv is a multiple of 128.
+int check_layer_shape(int E, int Hk, int Hv, int dk, int dv, bool norm_stage = false) {
     if (int e = check_heads(Hk, Hv)) return e;
     if (E <= 0) return GDN_ERR_BAD_SHAPE;
     if (E % 64 != 0 || ((size_t)Hv * dv) % 64 != 0 || !gdn::proj_gates_supported(Hv)) return GDN_ERR_UNSUPPORTED;
+    if (norm_stage && !gdn::proj_norm_supported(Hv * dv, dv)) return GDN_ERR_UNSUPPORTED;
     if (E > kProjMaxK || (size_t)Hv * dv > (size_t)kProjMaxK) return GDN_ERR_UNSUPPORTED;
     if (dk % 16 != 0 || dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
@@ -382,11 +460,13 @@ struct LayerWs {
     size_t x, z, g, beta, o, core, total;
 };
 
+// x fp32 [T][conv_dim], the gate product bf16 [T][Hv dv], g and beta fp32 [T][Hv], the
+// recurrence output fp32 [T][Hv dv], then the prefill's own workspace.
 LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerWs w{};
     w.x = 0;
-    w.z = w.x + align256((size_t)T * C * 2);
+    w.z = w.x + align256((size_t)T * C * 4);
     w.g = w.z + align256((size_t)T * Z * 2);
     w.beta = w.g + align256((size_t)T * Hv * 4);
     w.o = w.beta + align256((size_t)T * Hv * 4);
@@ -403,7 +483,7 @@ LayerDecodeWs layer_decode_ws(int B, int E, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerDecodeWs w{};
     w.x = 0;
-    w.z = w.x + align256((size_t)B * C * 2);
+    w.z = w.x + align256((size_t)B * C * 4);
     w.g = w.z + align256((size_t)B * Z * 2);
     w.beta = w.g + align256((size_t)B * Hv * 4);
     w.y = w.beta + align256((size_t)B * Hv * 4);
@@ -461,7 +541,7 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
                       void *workspace, size_t workspace_bytes, void *stream) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
-        if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
+        if (int e = check_layer_shape(E, Hk, Hv, dk, dv, true)) return e;
         if (!gdn::chunked_supported(dk, dv) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!w_in || !conv_w || !gamma || !w_out || (T > 0 && (!hidden || !out))) return GDN_ERR_NULL_POINTER;
         if (!aligned16({hidden, w_in, conv_w, gamma, w_out, cu_seqlens, conv_state_in, conv_state_out,
@@ -473,7 +553,7 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
         const LayerWs L = layer_ws(T, N, Hk, Hv, dk, dv);
         if (!workspace || workspace_bytes < L.total) return GDN_ERR_WORKSPACE;
         const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
-        const size_t st_bytes = (size_t)N * Hv * dk * dv * 4, cs_bytes = (size_t)N * 3 * C * 2;
+        const size_t st_bytes = (size_t)N * Hv * dk * dv * 4, cs_bytes = (size_t)N * 3 * C * 4;
         const Range rh{hidden, (size_t)T * E * 2}, rwi{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
             rcw{conv_w, C * 4 * 2}, rgm{gamma, (size_t)dv * 2}, rwo{w_out, (size_t)E * Z * 2},
             rci{conv_state_in, cs_bytes}, rco{conv_state_out, cs_bytes}, rs0{initial_state, st_bytes},
@@ -491,16 +571,20 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
         float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
         float *o = reinterpret_cast<float *>(ws + L.o);
         hipStream_t st = (hipStream_t)stream;
-        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st)) return e;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st, gamma)) return e;
         if (int e = prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
-                                 final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_BF16, order, ws + L.core,
-                                 L.total - L.core, stream, 3))
+                                 final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_F32, order, ws + L.core,
+                                 L.total - L.core, stream, 3, true))
             return e;
-        // the normalised output replaces z (bf16) in place, then feeds the output projection
-        gdn::NormArgs na{o, z, gamma, z, (long)T * Hv, dv, norm_eps, true};
-        if (T > 0)
-            if (int e = hip_status(gdn::launch_gated_rmsnorm(na, st))) return e;
-        return linear_impl(z, w_out, out, T, E, (int)Z, st);
+        // output projection with the gated RMSNorm formed in its operand staging: its A rows
+        // are o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z) per head, from o and the gate
+        // product that the input projection wrote in place of z
+        gdn::ProjArgs pa{nullptr, w_out, T, E, (int)Z, out, E, E, nullptr, 0};
+        pa.norm_o = o;
+        pa.norm_zg = z;
+        pa.norm_eps = norm_eps;
+        pa.norm_dv = dv;
+        return hip_status(gdn::launch_proj(pa, st));
     } catch (...) {
         return GDN_ERR_HIP;
     }
@@ -530,7 +614,7 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
         const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
         const Range rh{hidden, (size_t)B * E * 2}, rwi{w_in, (C + Z + 2 * (size_t)Hv) * E * 2},
             rcw{conv_w, C * 4 * 2}, rgm{gamma, (size_t)dv * 2}, rwo{w_out, (size_t)E * Z * 2},
-            rcs{conv_state, (size_t)B * 3 * C * 2}, rst{state, (size_t)B * Hv * dk * dv * 4},
+            rcs{conv_state, (size_t)B * 3 * C * 4}, rst{state, (size_t)B * Hv * dk * dv * 4},
             rout{out, (size_t)B * E * 2}, rws{workspace, L.total};
         for (Range in : {rh, rwi, rcw, rgm, rwo, rcs, rst, rout})
             if (overlap(rws, in)) return GDN_ERR_ALIAS;
@@ -543,10 +627,19 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
         void *x = ws + L.x, *z = ws + L.z, *y = ws + L.y;
         float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
         hipStream_t st = (hipStream_t)stream;
-        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, B, E, Hk, Hv, dk, dv, st)) return e;
-        if (int e = decode_impl(x, conv_w, conv_state, g, beta, state, nullptr, z, gamma, y, scale, l2_eps,
-                                norm_eps, B, Hk, Hv, dk, dv, GDN_BF16, order, stream))
-            return e;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, B, E, Hk, Hv, dk, dv, st, gamma)) return e;
+        if (B > 0) {
+            // the decode step with the gated RMSNorm fused; z holds the gate product already
+            gdn::DecodeArgs a{x, conv_w, conv_state, g, beta, state, nullptr, scale, l2_eps, B, Hk, Hv, dk, dv,
+                              false};
+            a.order = order;
+            a.z = z;
+            a.gamma = nullptr;
+            a.out = y;
+            a.norm_eps = norm_eps;
+            a.layer_types = true;
+            if (int e = hip_status(gdn::launch_decode(a, st))) return e;
+        }
         return linear_impl(y, w_out, out, B, E, (int)Z, st, reinterpret_cast<float *>(ws + L.partial),
                            (size_t)kDecodeProjSplits * B * E);
     } catch (...) {

@@ -7,7 +7,7 @@
 // is the chunk-mode call of section 8.2, which returns the outputs and the last
 // state.  The chunk form below follows from unrolling that recurrence over a
 // chunk of c <= 64 tokens (key-major state S[dk][dv], local cumulative
-// log-decay G_t = g_1 + ... + g_t, q already multiplied by `scale`):
+// log-decay G_t = g_1 + ... + g_t; the query scale multiplies the outputs, see below):
 //
 //   A[t][i] = b_t e^{G_t - G_i} (k_t . k_i)  for i < t,   T = (I + A)^-1
 //   W = T diag(b e^G) K,     U = T diag(b) V,      Delta = U - W S
@@ -32,8 +32,10 @@
 //  - in the state pass: fp16 MFMA (11-bit significand) with W', Qt and the
 //    state as single fp16 operands, and K and Delta' as bf16 hi + lo pairs
 //    (three MFMAs for K^T Delta').
-//    fp16 operands assume |state| < 6.5e4; the fp32 master state is never
-//    rounded.
+//    The query scale is applied to the fp32 outputs after the MFMAs (O is linear in
+//    it), so it never enters a 16-bit operand.  fp16 operands assume |state| < 6.5e4;
+//    the fp32 master state is never rounded, and a state beyond that range makes the
+//    outputs non-finite, which the state pass reports in the workspace status word.
 //
 // Kernels.
 //  chunk_local_kernel: the (chunk, value head) items are independent; the kernel is
@@ -83,7 +85,7 @@ struct Rec {
     static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U'  f32 tiles [NTD col tiles][4 row tiles][64][4]
                                                         //   (W' = diag(e^{G_c - G_t}) W, U' likewise)
     static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol^T f32 tiles [NTD][4][64][4] (rows = value column)
-    static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times
+    static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times; then the query scale
     static constexpr int SIZE = GM_OFF + 256;           // padded to a multiple of 256 bytes
 };
 
@@ -224,7 +226,7 @@ struct LocalSmem {
     static constexpr int AOFF = ADIAG + 4 * ADIAG_BLK * 4;   // strict-lower blocks of A: [6][hi, lo][64] bf16x4
     static constexpr int PT = AOFF + 6 * 2 * 64 * 8;         // P^T blocks c <= r: [10][64] f32x4
     static constexpr int XT = PT + 10 * 64 * 16;             // scaled T^T, M^T blocks c <= r: [4][10][hi, lo][64] bf16x4
-    static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^Gr, e^{G_c - G}, scale e^G, Gr
+    static constexpr int SCAL = XT + 4 * 10 * 2 * 64 * 8;    // token scalars: G, beta, beta e^Gr, e^{G_c - G}, e^G, Gr
     static constexpr int VLD = D + 4;                        // fused conv: fp32 v plane [64][VLD] in the XT region
     static_assert(64 * VLD * 4 <= SCAL - XT, "v plane fits in the T / M region");
     static constexpr int SIZE = SCAL + 6 * 64 * 4;
@@ -358,7 +360,7 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 
 // One workgroup per (chunk, value head), fully parallel over chunks.  With
 // T = (I + A)^-1, M = P T, Dc = diag(e^{G_c - G}), Bk = diag(b e^G), Bv = diag(b):
-//   -W' = -Dc T Bk K,  U' = Dc T Bv V,  Qt = diag(scale e^G) Q - M Bk K,  Ol = M Bv V
+//   -W' = -Dc T Bk K,  U' = Dc T Bv V,  Qt = diag(e^G) Q - M Bk K,  Ol = M Bv V
 // (the state pass uses Delta' = Dc Delta = U' - W' S, so the per-token decay of the
 // state update is already applied and the keys enter it unscaled).  Every MFMA
 // output lands in the layout its consumer wants, so nothing is transposed through
@@ -378,7 +380,7 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 //     U waves: U' = (Dc T Bv) V and Ol = (M Bv) V.
 // Products use two-term bf16 splits of both operands (three MFMAs each).
 // FUSED: q, k, v are not inputs; the workgroup runs the depthwise conv (kernel 4) + SiLU +
-// per-head L2 of q and k itself from the pre-conv input x (element type TX) of its 64 tokens
+// per-head L2 of q and k itself from the pre-conv input x (element type TX; conv weights TW) of its 64 tokens
 // and the 3 before them ("7.6 Qwen3.5: the linear-attention hybrid", section 7.6.2; history
 // from the sequence's own earlier tokens, else its conv cache, else zeros), with the same
 // arithmetic as gdn_conv_qk_prep.
@@ -390,12 +392,12 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 typedef unsigned long long flag_t;
 constexpr unsigned kFlagTag = 0x9e3779b9u;
 
-template <int D, bool FUSED, typename TX>
+template <int D, bool FUSED, typename TX, typename TW = TX>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
     int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0, int g1, int nslots,
-    const TX *__restrict__ x, const TX *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
+    const TX *__restrict__ x, const TW *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
     int order, flag_t *flags, flag_t flag_val) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
@@ -517,13 +519,14 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         Bs[lane] = bb;
         BEG[lane] = bb * (order == 0 ? eg : __expf(Gr));
         DCs[lane] = __expf(Gc - G);
-        QS[lane] = scale * eg;
-        if (lane < 4) {
+        QS[lane] = eg;
+        if (lane < 5) {   // e^{G_c} four times, then the query scale (applied by the state pass)
+            const float val = lane < 4 ? __expf(Gc) : scale;
             if (flags)
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __expf(Gc)), make_rsrc(rec, 1 << 30),
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, val), make_rsrc(rec, 1 << 30),
                                                       R::GM_OFF + 4 * lane, 0, kCohAux);
             else
-                reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = __expf(Gc);
+                reinterpret_cast<float *>(rec + R::GM_OFF)[lane] = val;
         }
     }
     if constexpr (FUSED) {
@@ -613,14 +616,14 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
                                     *reinterpret_cast<const bf16x8 *>(Ql + off)};
                     acc = mfma16x3(ka[ks], qb, acc);
                 }
-                // P^T[i][t] = scale e^{G_t - G_i} q_t . k_i for i <= t; i = 16b + 4kg + rr, t = 16r + l16
+                // P^T[i][t] = e^{G_t - G_i} q_t . k_i for i <= t; i = 16b + 4kg + rr, t = 16r + l16
                 const int t = 16 * r + l16;
                 const float Gt = Gs[t];
                 f32x4 p;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int i = 16 * b + 4 * kg + rr;
-                    p[rr] = i <= t ? scale * __expf(Gt - Gb[rr]) * acc[rr] : 0.f;
+                    p[rr] = i <= t ? __expf(Gt - Gb[rr]) * acc[rr] : 0.f;
                 }
                 Pt[tri_idx(b, r) * 64 + lane] = p;
             }
@@ -869,7 +872,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) Y[a][b] = zero4();
     if (isW) {
-        // Y = W'^T = K^T (Bk T^T Dc);  Xa = Qt^T = scale e^G Q^T - K^T (Bk M^T)
+        // Y = W'^T = K^T (Bk T^T Dc);  Xa = Qt^T = e^G Q^T - K^T (Bk M^T)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const float qs = QS[16 * tt + l16];
@@ -976,8 +979,18 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 // four independent MFMA chains (a dependent MFMA waits ~44 cycles, one issues
 // every 16).
 // Bound on the state pass's wait for a published record (iterations of a ~128-cycle
-// sleep, about a second): a producer that never publishes ends in wrong output, not a hang.
+// sleep, about a second).  A wait that runs out marks the call failed: the status word
+// of the workspace reports GDN_ERR_TIMEOUT and the outputs of the chunks not yet done and
+// the final state are written as NaN, so a producer that never publishes ends in a
+// reported failure, never in a hang or in plausible-looking output.
 constexpr int kSpinMax = 1 << 24;
+
+// The workspace status word (first 8 bytes of the workspace header): a kernel that meets
+// a failure stores (kStatusTag << 32) | gdn status code; only the host clears it.
+__device__ __forceinline__ void report_status(unsigned long long *status, unsigned code) {
+    __hip_atomic_store(status, ((unsigned long long)kStatusTag << 32) | code, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Conv-cache write of the fused prefill, done by the state pass in the concurrent schedule:
 // the three rows before the end of sequence s (x rows, or input-cache rows where the
@@ -1039,7 +1052,7 @@ template <int D, bool COH>
 __global__ __launch_bounds__(256) void state_pass_kernel(
     const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
     const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const flag_t *flags,
-    flag_t flag_val, ConvOut cv) {
+    flag_t flag_val, ConvOut cv, unsigned long long *status) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -1077,6 +1090,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     if (nc > 0 ? c_lo >= c_hi : g0 != 0) return;
     const float *s_in = c_lo == 0 ? s0 : mid;
     float *s_out = c_hi == nc ? sf : mid;
+    // set by a copy wave whose wait for a record ran out; read by the compute waves after
+    // every chunk barrier
+    __shared__ int sfail;
+    if (threadIdx.x == 0) sfail = 0;
+    __syncthreads();
 
     if (copier) {
         // Each copy wave moves half of the A operands with direct-to-LDS buffer loads
@@ -1091,11 +1109,25 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         // time: wait (bounded) until chunk c's record is published; every record load is then
         // device-coherent.  The copy waves confirm a chunk before the barrier after which the
         // compute waves prefetch its U' and Ol^T strips, i.e. two chunks ahead of the compute.
-        auto ready = [&](int c) {
-            const flag_t *f = flags + (size_t)h * ncmax + gbase + c;
-            for (int it = 0; it < kSpinMax; ++it) {
-                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == flag_val) break;
+        // the bound on each wait: the workspace header's second word when it holds kSpinTag
+        // in its high half (a caller's setting, for tests), else kSpinMax
+        int spin_max = kSpinMax;
+        if constexpr (COH) {
+            const unsigned long long sw = __hip_atomic_load(status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((unsigned)(sw >> 32) == kSpinTag) spin_max = (int)(sw & 0x7fffffffu);
+        }
+        auto wait_flag = [&](const flag_t *f) {
+            for (int it = 0; it < spin_max; ++it) {
+                if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == flag_val) return true;
                 __builtin_amdgcn_s_sleep(2);
+            }
+            return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == flag_val;
+        };
+        auto ready = [&](int c) {
+            if (sfail) return;   // already failed: its outputs are NaN, no further waits
+            if (!wait_flag(flags + (size_t)h * ncmax + gbase + c)) {
+                sfail = 1;
+                if (lane == 0) report_status(status, kStatusTimeout);
             }
         };
         if constexpr (COH) {
@@ -1132,17 +1164,17 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
                 const int ct = lane + 64 * (wave - 2);
                 conv_rows(cv, s, t0, L, 2 * cv.Hk * cv.dk + h * D, D, ct, 128);
                 if (h % cv.G == 0) {
+                    bool others_read = true;
                     if (nc > 0 && cv.cs_in == cv.cs_out)
                         for (int hh = h + 1; hh < h + cv.G; ++hh)
-                            for (int it = 0; it < kSpinMax; ++it) {
-                                if (__hip_atomic_load(flags + (size_t)hh * ncmax + gbase, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) == flag_val)
-                                    break;
-                                __builtin_amdgcn_s_sleep(2);
-                            }
+                            others_read = wait_flag(flags + (size_t)hh * ncmax + gbase) && others_read;
                     const int kh = h / cv.G;
-                    conv_rows(cv, s, t0, L, kh * cv.dk, cv.dk, ct, 128);
-                    conv_rows(cv, s, t0, L, (cv.Hk + kh) * cv.dk, cv.dk, ct, 128);
+                    if (others_read) {
+                        conv_rows(cv, s, t0, L, kh * cv.dk, cv.dk, ct, 128);
+                        conv_rows(cv, s, t0, L, (cv.Hk + kh) * cv.dk, cv.dk, ct, 128);
+                    } else if (lane == 0) {   // the input cache may still be read: leave it
+                        report_status(status, kStatusTimeout);
+                    }
                 }
             }
         }
@@ -1176,7 +1208,17 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
                                                                                    kCohAux))
                    : *reinterpret_cast<const float *>(rec + R::GM_OFF + (lane & 3) * 4);
     };
-    if (!COH && c_lo < c_hi) load_strip(rec_of(c_lo), Uf, Of, gm);
+    // the query scale of the call (stored in every record), applied to the fp32 outputs
+    float osc = 1.f;
+    auto load_scale = [&](const char *rec) {
+        osc = COH ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rec, 1 << 30),
+                                                                                    R::GM_OFF + 16, 0, kCohAux))
+                  : *reinterpret_cast<const float *>(rec + R::GM_OFF + 16);
+    };
+    if (!COH && c_lo < c_hi) {
+        load_strip(rec_of(c_lo), Uf, Of, gm);
+        load_scale(rec_of(c_lo));
+    }
     // Retire the initial state and strip loads here, once.  Left pending into the loop,
     // the compiler's wait analysis merges them into the loop header and then waits for
     // every outstanding access (the previous chunk's o stores and this chunk's prefetch)
@@ -1185,8 +1227,10 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     __syncthreads();
     if (COH && c_lo < c_hi) {   // first strips only once the copy waves have confirmed them
         load_strip(rec_of(c_lo), Uf, Of, gm);
+        load_scale(rec_of(c_lo));
         __builtin_amdgcn_s_waitcnt(0);
     }
+    bool nonfinite = false;   // an output or the final state is inf / NaN (reported at the end)
 
     // o rows of this lane: row 16 mt + 4 kg + qq of the chunk, column col
     // O^T tiles: lane (kg, l16) holds columns 16 j + 4 kg .. + 3 of output row 16 mt + l16
@@ -1301,14 +1345,21 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             for (int dm = 0; dm < 4; ++dm) S[4 * p + dm] = a[dm];
         }
 
-        // ---- this chunk's outputs: uniform row base, per-lane 32-bit offsets
+        // ---- this chunk's outputs (times the query scale; NaN once a record wait has run
+        // out): uniform row base, per-lane 32-bit offsets
         const int tb = t0 + c * kChunk;
         float *ob = o + ((size_t)tb * Hv + h) * D + 16 * j;
         const int rows = min(kChunk, L - c * kChunk);
+        const float oscale = (COH && sfail) ? __builtin_nanf("") : osc;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            if (!LAST || 16 * mt + l16 < rows)
+        for (int mt = 0; mt < 4; ++mt) {
+            Ot[mt] = Ot[mt] * oscale;
+            if (!LAST || 16 * mt + l16 < rows) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nonfinite |= !__builtin_isfinite(Ot[mt][e]);
                 *reinterpret_cast<f32x4 *>(ob + o_lane + 16 * mt * row_stride) = Ot[mt];
+            }
+        }
         __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
         if constexpr (!LAST) {
 #pragma unroll
@@ -1319,11 +1370,19 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     for (int c = c_lo; c + 1 < c_hi; ++c) chunk_step(c, std::false_type{});
     if (c_lo < c_hi) chunk_step(c_hi - 1, std::true_type{});
     if (s_out) {
+        const bool poison = COH && sfail;
 #pragma unroll
         for (int m = 0; m < NTD; ++m)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) s_out[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = S[m][qq];
+            for (int qq = 0; qq < 4; ++qq) {
+                const float v = poison ? __builtin_nanf("") : S[m][qq];
+                nonfinite |= !__builtin_isfinite(v);
+                s_out[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = v;
+            }
     }
+    // inf / NaN in an output or the state (an fp16 operand out of range, non-finite inputs,
+    // or the poisoning above): one report per wave
+    if (__ballot(nonfinite) && lane == 0 && !(COH && sfail)) report_status(status, kStatusNonFinite);
 }
 
 // ============================================================== host side
@@ -1341,10 +1400,12 @@ static size_t mid_offset(size_t nc, int Hv, int dk) {
 static size_t flags_offset(size_t nc, int N, int Hv, int dk) {
     return mid_offset(nc, Hv, dk) + (size_t)N * Hv * dk * dk * sizeof(float);
 }
+// The layout above starts kWsHeader bytes into the workspace, after the header (status
+// word, wait bound).
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     (void)dv;
     const size_t nc = max_chunks(T, N);
-    return flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(flag_t);
+    return kWsHeader + flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(flag_t);
 }
 
 // ---- segment pipeline of gdn_chunk_prefill: the packed chunk range is cut into
@@ -1426,7 +1487,7 @@ static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int
     const int cus = cu_budget > 0 ? cu_budget : device_cus();
     const int nslots = std::max(1, std::min(g1 - g0, (cus > 0 ? cus : 256) / a.Hv));
     const dim3 grid((unsigned)nslots, a.Hv), block(LocalShape<D>::THREADS);
-    char *ws = (char *)a.ws;
+    char *ws = (char *)a.ws + kWsHeader;
     if (!a.fp) {
         hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)nullptr,
@@ -1435,6 +1496,11 @@ static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int
         hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const bf16 *)a.fp->x,
                            (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order, flags, flag_val);
+    } else if (a.fp->w_bf16) {   // fp32 x and caches, bf16 conv weights (the layer's prefill)
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, float, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g,
+                           a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots,
+                           (const float *)a.fp->x, (const bf16 *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps,
+                           a.order, flags, flag_val);
     } else {
         hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
                            a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)a.fp->x,
@@ -1453,13 +1519,15 @@ static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
     const int blocks = state_blocks<D>(units);
-    float *mid = reinterpret_cast<float *>((char *)a.ws + mid_offset(nc, a.Hv, D));
+    const char *recs = (const char *)a.ws + kWsHeader;
+    float *mid = reinterpret_cast<float *>((char *)a.ws + kWsHeader + mid_offset(nc, a.Hv, D));
+    unsigned long long *hdr = reinterpret_cast<unsigned long long *>(a.ws);
     if (flags)
-        hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, cv);
+        hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, recs, a.cu, a.T, a.Hv, units,
+                           a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, cv, hdr);
     else
-        hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, (const char *)a.ws, a.cu, a.T,
-                           a.Hv, units, a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, ConvOut{});
+        hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, recs, a.cu, a.T, a.Hv, units,
+                           a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, ConvOut{}, hdr);
     return hipGetLastError();
 }
 
@@ -1510,11 +1578,21 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     }
     const int sblocks = state_blocks<D>(a.N * a.Hv);
     const int cus = device_cus();
+    // Under stream capture (a HIP graph being recorded) both phases go on `stream` one after
+    // the other: the concurrent schedule's kernels must run at the same time (a graph may
+    // run sibling nodes one after the other) and it is never joined back to `stream`.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
+    if (cap != hipStreamCaptureStatusNone) {
+        if ((e = launch_local<D>(a, st, nc, 0, nc)) != hipSuccess) return e;
+        if ((e = launch_state<D>(a, st, nc, 0, nc)) != hipSuccess) return e;
+        return launch_fused_cs_out(a, st);
+    }
     if (concurrent_ok(nc, a.Hv, sblocks, cus)) {
         PipeRes *pr = nullptr;
         if ((e = pipe_resources(&pr)) != hipSuccess) return e;
         std::lock_guard<std::mutex> lock(pr->mu);
-        flag_t *flags = reinterpret_cast<flag_t *>((char *)a.ws + flags_offset(nc, a.N, a.Hv, D));
+        flag_t *flags = reinterpret_cast<flag_t *>((char *)a.ws + kWsHeader + flags_offset(nc, a.N, a.Hv, D));
         const flag_t flag_val = ((flag_t)kFlagTag << 32) | ++pr->epoch;
         ConvOut cv;
         if (a.fp && a.fp->cs_out) {
@@ -1560,6 +1638,36 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     if ((e = hipEventRecord(pr->ev[kMaxSegments], pr->side)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(st, pr->ev[kMaxSegments], 0)) != hipSuccess) return e;
     return launch_fused_cs_out(a, st);
+}
+
+// Read (and with `clear`, reset) the workspace status word once everything a call enqueued
+// has completed: the caller's stream and the library's second stream of this device.
+hipError_t workspace_status(void *ws, hipStream_t st, unsigned long long *word, bool clear) {
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return e;
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        hipStream_t side = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(g_pipe_mu);
+            if (g_pipe[dev].ready) side = g_pipe[dev].side;
+        }
+        if (side && (e = hipStreamSynchronize(side)) != hipSuccess) return e;
+    }
+    if ((e = hipMemcpy(word, ws, sizeof(*word), hipMemcpyDeviceToHost)) != hipSuccess) return e;
+    if (clear) {
+        const unsigned long long zero = 0;
+        e = hipMemcpy(ws, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    }
+    return e;
+}
+
+// cu_seqlens on the host (synchronous; the debug check only).
+hipError_t copy_seqlens(const int32_t *cu, int n, hipStream_t st, int32_t *host) {
+    hipError_t e = hipMemcpyAsync(host, cu, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return e;
+    return hipStreamSynchronize(st);
 }
 
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases) {

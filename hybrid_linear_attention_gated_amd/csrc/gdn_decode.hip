@@ -18,6 +18,8 @@
 // needed (S^T k and S^T q, over dk) are taken from the OLD state in the same
 // pass:  m = a (S^T k) (order 1: S^T k),  o = a (S^T q) + delta (k . q).  Row-group partial sums
 // are combined with xor shuffles inside a wave and through LDS across waves.
+#include <type_traits>
+
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -25,8 +27,8 @@ namespace gdn {
 
 constexpr int kDecThreads = 256;
 
-template <typename T>
-__device__ __forceinline__ float conv_step(const T *__restrict__ x, const T *__restrict__ w, T *cs,
+template <typename T, typename TW>
+__device__ __forceinline__ float conv_step(const T *__restrict__ x, const TW *__restrict__ w, T *cs,
                                            int b, int c, int conv_dim) {
     // window = [slot0, slot1, slot2, x]; afterwards the cache is [slot1, slot2, x]
     T *cb = cs + (size_t)b * kConvHist * conv_dim + c;
@@ -35,7 +37,7 @@ __device__ __forceinline__ float conv_step(const T *__restrict__ x, const T *__r
     const T s2raw = cb[2 * (size_t)conv_dim];
     const T xraw = x[(size_t)b * conv_dim + c];
     const float s2 = to_f32(s2raw), xn = to_f32(xraw);
-    const T *wc = w + (size_t)c * kConvK;
+    const TW *wc = w + (size_t)c * kConvK;
     float acc = to_f32(wc[0]) * s0;
     acc = fmaf(to_f32(wc[1]), s1, acc);
     acc = fmaf(to_f32(wc[2]), s2, acc);
@@ -69,14 +71,16 @@ __device__ __forceinline__ void store4(float *p, const float *i) {
 
 // GATED: the output row of each value head goes through the gated RMSNorm epilogue
 // ("7.6 Qwen3.5: the linear-attention hybrid", sections 7.6.2 and 7.6.3) before it is
-// stored: out = o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z), in the element type.
-// The dv outputs of a head sit in the first dv/4 lanes of wave 0 (4 each), so the
-// mean square is one reduction inside that lane group.
-template <typename T, int DK, int DV, bool GATED>
+// stored: out = o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z), in the gate's element
+// type TG; with gamma NULL, z already holds the product gamma * SiLU(z) (the layer's input
+// projection forms it).  The dv outputs of a head sit in the first dv/4 lanes of wave 0
+// (4 each), so the mean square is one reduction inside that lane group.
+// T: element type of x and the conv cache; TW: of the conv weights.
+template <typename T, typename TW, typename TG, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
-    const T *__restrict__ x, const T *__restrict__ w, T *cs, const float *__restrict__ g,
+    const T *__restrict__ x, const TW *__restrict__ w, T *cs, const float *__restrict__ g,
     const float *__restrict__ beta, float *state, float *__restrict__ o, float scale, float eps,
-    int Hk, int Hv, const T *__restrict__ z, const T *__restrict__ gamma, T *__restrict__ out, float norm_eps,
+    int Hk, int Hv, const TG *__restrict__ z, const TG *__restrict__ gamma, TG *__restrict__ out, float norm_eps,
     int order) {
     constexpr int TPR = DV / 4;                  // threads per state row (one float4 each)
     constexpr int RG = kDecThreads / TPR;        // row groups
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     auto load_gate = [&](int h) {
         if (gate_lane) load4(z + ((size_t)b * Hv + h) * DV + 4 * cg, zf);
     };
-    if (gate_lane) load4(gamma + 4 * cg, gf);
+    if (gate_lane && gamma) load4(gamma + 4 * cg, gf);
     load_gate(kh * group);
 
     // q and k channels of this key head
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 if (rg == 0) {
                     float r4[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r4[e] = pq[e] * rn * gf[e] * silu(zf[e]);
+                    for (int e = 0; e < 4; ++e) r4[e] = pq[e] * rn * (gamma ? gf[e] * silu(zf[e]) : zf[e]);
                     store4(out + ((size_t)b * Hv + h) * DV + 4 * cg, r4);
                 }
             }
@@ -233,46 +237,49 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     }
 }
 
-template <typename T, int DK, int DV>
+template <typename T, typename TW, typename TG, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     if (a.B == 0) return hipSuccess;
     if (a.out) {
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, true>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
-                           (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, (float *)nullptr,
-                           a.scale, a.eps, a.Hk, a.Hv, (const T *)a.z, (const T *)a.gamma, (T *)a.out,
+        hipLaunchKernelGGL((decode_kernel<T, TW, TG, DK, DV, true>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
+                           (const T *)a.x, (const TW *)a.w, (T *)a.cs, a.g, a.beta, a.state, (float *)nullptr,
+                           a.scale, a.eps, a.Hk, a.Hv, (const TG *)a.z, (const TG *)a.gamma, (TG *)a.out,
                            a.norm_eps, a.order);
-    } else {
-        hipLaunchKernelGGL((decode_kernel<T, DK, DV, false>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
+    } else if constexpr (std::is_same<T, TW>::value && std::is_same<T, TG>::value) {
+        hipLaunchKernelGGL((decode_kernel<T, T, T, DK, DV, false>), dim3(a.B * a.Hk), dim3(kDecThreads), 0, st,
                            (const T *)a.x, (const T *)a.w, (T *)a.cs, a.g, a.beta, a.state, a.o, a.scale, a.eps,
                            a.Hk, a.Hv, (const T *)nullptr, (const T *)nullptr, (T *)nullptr, 0.f, a.order);
+    } else {
+        return hipErrorInvalidValue;   // mixed element types only with the gated output
     }
     return hipGetLastError();
 }
 
-template <typename T, int DK>
+template <typename T, typename TW, typename TG, int DK>
 static hipError_t launch_decode_dv(const DecodeArgs &a, hipStream_t st) {
     switch (a.dv) {
-        case 16: return launch_decode_t<T, DK, 16>(a, st);
-        case 32: return launch_decode_t<T, DK, 32>(a, st);
-        case 64: return launch_decode_t<T, DK, 64>(a, st);
-        case 128: return launch_decode_t<T, DK, 128>(a, st);
+        case 16: return launch_decode_t<T, TW, TG, DK, 16>(a, st);
+        case 32: return launch_decode_t<T, TW, TG, DK, 32>(a, st);
+        case 64: return launch_decode_t<T, TW, TG, DK, 64>(a, st);
+        case 128: return launch_decode_t<T, TW, TG, DK, 128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T>
+template <typename T, typename TW, typename TG>
 static hipError_t launch_decode_dk(const DecodeArgs &a, hipStream_t st) {
     switch (a.dk) {
-        case 16: return launch_decode_dv<T, 16>(a, st);
-        case 32: return launch_decode_dv<T, 32>(a, st);
-        case 64: return launch_decode_dv<T, 64>(a, st);
-        case 128: return launch_decode_dv<T, 128>(a, st);
+        case 16: return launch_decode_dv<T, TW, TG, 16>(a, st);
+        case 32: return launch_decode_dv<T, TW, TG, 32>(a, st);
+        case 64: return launch_decode_dv<T, TW, TG, 64>(a, st);
+        case 128: return launch_decode_dv<T, TW, TG, 128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
-    return a.bf16 ? launch_decode_dk<bf16>(a, st) : launch_decode_dk<float>(a, st);
+    if (a.layer_types) return launch_decode_dk<float, bf16, bf16>(a, st);   // the layer's decode
+    return a.bf16 ? launch_decode_dk<bf16, bf16, bf16>(a, st) : launch_decode_dk<float, float, float>(a, st);
 }
 
 }  // namespace gdn

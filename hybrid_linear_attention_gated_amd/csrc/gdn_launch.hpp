@@ -9,6 +9,17 @@
 
 namespace gdn {
 
+// Workspace status word of the chunked prefill (see gdn_prefill_workspace_status in gdn.h):
+// (kStatusTag << 32) | status code, stored by a kernel that meets a failure.
+constexpr unsigned kStatusTag = 0x67646e73u;
+constexpr unsigned kStatusTimeout = 8;     // GDN_ERR_TIMEOUT
+constexpr unsigned kStatusNonFinite = 9;   // GDN_ERR_NONFINITE
+// Header at the start of the chunked prefill's workspace: the status word (8 bytes), then
+// an optional bound on the state pass's record waits ((kSpinTag << 32) | iterations; any
+// other value means the default, about a second).
+constexpr size_t kWsHeader = 256;
+constexpr unsigned kSpinTag = 0x7370696eu;
+
 struct PrepArgs {
     const void *x, *w;
     const int32_t *cu;
@@ -29,6 +40,7 @@ struct FusedPrep {
     void *cs_out;
     bool bf16;   // element type of x / conv_w / conv states
     float eps;
+    bool w_bf16 = false;   // with bf16 false: conv_w is bf16 while x and the conv states are fp32
 };
 
 struct PrefillArgs {
@@ -58,10 +70,13 @@ struct DecodeArgs {
     bool bf16;
     int order = 0;   // as in PrefillArgs
     // gated output (gdn_decode_step_gated): when `out` is set, out = RMSNorm(o) * gamma *
-    // SiLU(z) in the element type is written instead of o
+    // SiLU(z) in the element type is written instead of o (gamma NULL: z holds the product
+    // gamma * SiLU(z))
     const void *z = nullptr, *gamma = nullptr;
     void *out = nullptr;
     float norm_eps = 0.f;
+    // the layer's decode: x and the conv cache fp32, conv weights, z and out bf16 (gated only)
+    bool layer_types = false;
 };
 
 struct NormArgs {
@@ -91,6 +106,19 @@ struct ProjArgs {
     // launcher splits k and sums the slices' planes in a second pass
     float *partial = nullptr;
     size_t partial_cap = 0;
+    // layer epilogue: columns n < n_split go to y0 as fp32 (y0_f32); with gate_gain set,
+    // columns n >= n_split are the output gate z and y1 receives
+    // bf16(gate_gain[(n - n_split) % gate_dv] * SiLU(z)) instead of z
+    bool y0_f32 = false;
+    const void *gate_gain = nullptr;   // bf16 [gate_dv]
+    int gate_dv = 0;
+    // gated RMSNorm on the A operand (set norm_o; `a` is then unused): the A row m is
+    //   norm_o[m][k] * rsqrt(mean over k's head of norm_o^2 + norm_eps) * norm_zg[m][k],
+    // heads of norm_dv consecutive k, rounded to bf16 as it is staged
+    const float *norm_o = nullptr;     // fp32 [M][K]
+    const void *norm_zg = nullptr;     // bf16 [M][K]
+    float norm_eps = 0.f;
+    int norm_dv = 0;
     int tiles_m = 0, tiles_n = 0, ntiles = 0, ksplit = 1;   // set by the launcher
 };
 
@@ -103,6 +131,8 @@ hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st);
 
 hipError_t launch_proj(const ProjArgs &a, hipStream_t st);
 bool proj_gates_supported(int heads);
+// the A-operand norm of ProjArgs needs whole heads in one k stage of the small tile
+bool proj_norm_supported(int K, int dv);
 // compute units of the current device (cached per device; 0 if unknown)
 int device_cus();
 
@@ -114,5 +144,10 @@ bool chunked_supported(int dk, int dv);
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv);
 // phases: bit 0 = chunk-local kernel, bit 1 = state-pass kernel
 hipError_t launch_prefill_chunked(const PrefillArgs &a, hipStream_t st, int phases);
+// the chunked prefill workspace's status word, read after `st` and the library's second
+// stream have drained (reset to 0 with `clear`)
+hipError_t workspace_status(void *ws, hipStream_t st, unsigned long long *word, bool clear);
+// n int32 of device memory to the host, synchronously on `st`
+hipError_t copy_seqlens(const int32_t *cu, int n, hipStream_t st, int32_t *host);
 
 }  // namespace gdn

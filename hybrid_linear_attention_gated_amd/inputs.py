@@ -25,7 +25,7 @@ Layer forward (input projection -> core -> gated RMSNorm -> output projection, a
 0.8B layer widths of section 7.6.1: hidden 1024): hidden ~ N(0, 1); input projection
 weight ~ N(0, 1/E) and output projection weight ~ N(0, 1/(Hv dv)), so every projected
 value is ~N(0, 1) like the pre-conv x and the gate pre-activations of the core
-workloads; conv weights, gain and caches as above.
+workloads; conv weights, gain and caches as above (the layer's conv caches in fp32).
 Generator: numpy PCG64(1234 + index).
 """
 from __future__ import annotations
@@ -277,10 +277,10 @@ def layer_hidden(index: int, T: int, E: int, exact: bool = False) -> torch.Tenso
 
 
 def layer_caches(index: int, N: int, Hk: int, Hv: int, dk: int, dv: int):
-    """Incoming conv caches [N, 3, conv_dim] ~ N(0, 1) (bf16) and states
-    [N, Hv, dk, dv] ~ N(0, 0.1) (fp32)."""
+    """Incoming conv caches [N, 3, conv_dim] ~ N(0, 1) and states [N, Hv, dk, dv] ~
+    N(0, 0.1), both fp32 (the layer keeps its pre-conv inputs in fp32)."""
     rng = _rng(index)
     C = 2 * Hk * dk + Hv * dv
     cs = _normal_f32(rng, (N, 3, C))
     st = _normal_f32(rng, (N, Hv, dk, dv), std=0.1)
-    return _bf16(cs), _f32(st)
+    return _f32(cs), _f32(st)

@@ -42,7 +42,12 @@
  *  - cu_seqlens (int32, N+1 entries, cu[0] = 0, non-decreasing, cu[N] = T) packs
  *    N variable-length sequences along T.  NULL means one sequence of length T
  *    (N must then be 1).  Zero-length sequences are allowed.  These device values
- *    are a precondition and are not validated.
+ *    are a precondition and are not validated, unless the environment variable
+ *    GDN_DEBUG_CHECK is set (to anything but "0") when the library first looks: the
+ *    prefill calls then copy cu_seqlens to the host and return GDN_ERR_BAD_SHAPE for a
+ *    bad one before launching anything, and wait for their own completion to return
+ *    the workspace status (GDN_ERR_TIMEOUT, GDN_ERR_NONFINITE; see
+ *    gdn_prefill_workspace_status).  Debug-checked calls synchronise the stream.
  *  - Tensor pointers may be NULL when the tensor is empty (T = 0, or B = 0).
  *  - Every non-NULL device pointer (tensors, cu_seqlens, workspace) must be 16-byte
  *    aligned, as every device allocator returns them: the kernels move 16-byte
@@ -62,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum {
     GDN_OK = 0,
@@ -72,7 +77,9 @@ typedef enum {
     GDN_ERR_WORKSPACE = 4,      /* workspace NULL or smaller than the queried size      */
     GDN_ERR_HIP = 5,            /* a HIP launch or runtime call failed                  */
     GDN_ERR_ALIAS = 6,          /* an output overlaps an input it must not overlap      */
-    GDN_ERR_ALIGN = 7           /* a device pointer is not 16-byte aligned              */
+    GDN_ERR_ALIGN = 7,          /* a device pointer is not 16-byte aligned              */
+    GDN_ERR_TIMEOUT = 8,        /* the state pass stopped waiting for a chunk's record  */
+    GDN_ERR_NONFINITE = 9       /* a prefill output or final state is inf or NaN        */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -143,9 +150,11 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *   o              [T][Hv][dv]   fp32; o_t = S_t (scale * q_t); must not overlap any input
  *   workspace      device scratch of at least gdn_chunk_prefill_workspace_size()
  *                  bytes (may be NULL when that size is 0); contents are scratch.
- *                  With GDN_MATH_MFMA it holds the per-(chunk, value head) results
- *                  of the chunk-local phase, one state per (sequence, value head) and
- *                  one ready flag per (chunk, value head).  It needs no initialisation:
+ *                  With GDN_MATH_MFMA it starts with a 256-byte header (a status word,
+ *                  see gdn_prefill_workspace_status; then an optional bound on the state
+ *                  pass's waits, below) and holds the per-(chunk, value head) results of
+ *                  the chunk-local phase, one state per (sequence, value head) and one
+ *                  ready flag per (chunk, value head).  It needs no initialisation:
  *                  each call's ready flags carry a value of that call's own.
  *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
  *   order          gdn_order (decay before or after the retrieval)
@@ -157,9 +166,14 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *    as the other compute units: the chunk-local phase runs on the library's second
  *    stream, on the compute units the state pass leaves free, and raises a flag in
  *    the workspace as each record is complete; the state pass runs at the same time
- *    on `stream` and waits for each flag (a bounded wait: a record that is never
- *    published ends in wrong output rather than a hang, which the library's own
- *    chunk-local phase never causes).  When a call comes from another caller stream
+ *    on `stream` and waits for each flag.  The wait is bounded (about a second; the
+ *    header's second 64-bit word, when it holds 0x7370696e in its high half, sets the
+ *    bound to its low half in iterations of a ~128-cycle sleep, for tests): a record
+ *    that is never published ends the call with NaN outputs and final states and the
+ *    status GDN_ERR_TIMEOUT, never in a hang; the library's own chunk-local phase
+ *    publishes every record.  After such a failure the second stream's kernel may
+ *    still run when `stream` moves on: gdn_prefill_workspace_status waits for it.
+ *    When a call comes from another caller stream
  *    than the previous concurrent one, its state pass first waits for the previous
  *    call's chunk-local phase, so at most one state pass waits for records at a time;
  *  - segmented, when the packed chunks are many (at least 256) and the state pass
@@ -167,7 +181,13 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *    segments, and the chunk-local phase of segment k + 1 (on `stream`) runs while
  *    the state pass of segment k runs on the second stream; a sequence's state
  *    passes between segments through the workspace;
- *  - sequential otherwise: both phases on `stream`, one after the other.
+ *  - sequential otherwise, and always while `stream` is capturing a HIP graph: both
+ *    phases on `stream`, one after the other (a graph may run sibling nodes one after
+ *    the other, and the concurrent schedule is never joined back to `stream`).
+ * The query scale multiplies the fp32 outputs after the 16-bit products, so any finite
+ * scale is exact to apply; the state pass rounds the state to fp16 for its products,
+ * so a state element beyond +-65504 makes outputs non-finite, which the status word
+ * reports (GDN_ERR_NONFINITE).
  */
 int gdn_chunk_prefill(const float *q, const float *k, const float *v,
                       const float *g, const float *beta,
@@ -226,6 +246,23 @@ int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, in
                 float scale, float l2_eps,
                 int T, int Hk, int Hv, int dk, int dv, int dtype, int order,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_prefill_workspace_status -- the outcome of the chunked prefills (gdn_chunk_prefill
+ * with GDN_MATH_MFMA, the split phases, gdn_prefill, gdn_layer_prefill through its own
+ * workspace's prefill part) that used `workspace` since the previous query.  Waits for
+ * `stream` and the library's second stream on the current device, reads the status word
+ * at the start of the workspace and clears it.
+ *   GDN_OK             no failure recorded (or a word that no kernel wrote)
+ *   GDN_ERR_TIMEOUT    a state pass stopped waiting for a record (outputs NaN)
+ *   GDN_ERR_NONFINITE  an output or a final state came out inf or NaN
+ *   GDN_ERR_NULL_POINTER / GDN_ERR_ALIGN / GDN_ERR_WORKSPACE (fewer than 256 bytes),
+ *   GDN_ERR_HIP        argument or runtime errors of the query itself
+ * A freshly allocated workspace reports GDN_OK unless its first 8 bytes happen to hold
+ * the status tag 0x67646e73 in their high half; a caller that wants certainty queries
+ * once before the first call.
+ */
+int gdn_prefill_workspace_status(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_prefill_local -- the first phase of gdn_prefill: conv prep + chunk-local
@@ -307,9 +344,14 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
  * two gate pre-activations a, b per value head; the conv + SiLU + L2 and the gated delta
  * rule follow; the output passes the gated RMSNorm with SiLU(z) and a bias-free output
  * projection.  The pages leave the gate maps open: here g = -softplus(a) (so the decay
- * exp(g) lies in (0, 1)) and beta = sigmoid(b).  Weights and activations are bf16;
+ * exp(g) lies in (0, 1)) and beta = sigmoid(b).  Weights and the layer input are bf16;
  * products accumulate in fp32 on MFMA.  Weights are stored as a linear layer stores
  * them: W[out][in], y = x W^T.
+ * Inside the layer calls the pre-conv q|k|v that the recurrence reads stays fp32, and so
+ * do the layer's conv caches (the recurrent state amplifies a one-ulp bf16 change of its
+ * inputs beyond the 2e-2 accuracy the layer is held to); the gate and the normalised
+ * output that enters the output projection are bf16 (one bf16 rounding of a
+ * multiplicative gate costs at most 2^-9 of the value).
  *
  * gdn_linear -- y = a w^T.
  *   a [M][K] bf16, w [N][K] bf16, y [M][N] bf16 (fp32 sums rounded to nearest even).
@@ -332,20 +374,24 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
                 int T, int E, int Hk, int Hv, int dk, int dv, void *stream);
 
 /*
- * gdn_layer_prefill -- the whole layer over packed sequences in one call:
- * gdn_in_proj, gdn_prefill (element type bf16), gdn_gated_rmsnorm over each (token,
- * value head) row, gdn_linear with w_out.
+ * gdn_layer_prefill -- the whole layer over packed sequences in one call: the input
+ * projection (as gdn_in_proj, but x leaves it in fp32 and the gate as the bf16 product
+ * gamma * SiLU(z)), the prefill of gdn_prefill on the fp32 x, and the output projection
+ * with the gated RMSNorm formed in its operand staging: its A rows are
+ * o * rsqrt(mean over the head's dv outputs of o^2 + norm_eps) * gamma * SiLU(z), rounded
+ * to bf16 as they enter LDS, so no normalised copy of the output is written.
  *   hidden [T][E], w_in as in gdn_in_proj, conv_w [conv_dim][4], gamma [dv] (the gain
  *   as applied), w_out [E][Hv*dv]: bf16.
- *   cu_seqlens, N, conv_state_in / conv_state_out [N][3][conv_dim] bf16,
+ *   cu_seqlens, N, conv_state_in / conv_state_out [N][3][conv_dim] fp32,
  *   initial_state / final_state [N][Hv][dk][dv] fp32, scale, l2_eps, order: as in
  *   gdn_prefill (the same exact aliases allowed).
  *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
  *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
- *              (x, z, g, beta, o and the prefill's workspace); must not overlap any
- *              other argument.
- * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
- * The four steps run in order on `stream` (the prefill as in gdn_prefill).
+ *              (x, the gate product, g, beta, o and the prefill's workspace); must not
+ *              overlap any other argument.
+ * dk = dv in {64, 128}; E and Hv as in gdn_in_proj, and Hv*dv a multiple of 128.  out must
+ * not overlap an input.  The three steps run in order on `stream` (the prefill as in
+ * gdn_prefill).
  */
 size_t gdn_layer_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv);
 int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
@@ -357,14 +403,15 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * gdn_layer_decode -- one token for each of B sequences through the layer:
- * gdn_in_proj, gdn_decode_step_gated (element type bf16, caches in place),
- * gdn_linear with w_out.
+ * gdn_layer_decode -- one token for each of B sequences through the layer: the input
+ * projection of gdn_layer_prefill (x fp32, the gate product bf16), the decode step with the
+ * gated RMSNorm fused (gdn_decode_step_gated, caches in place), gdn_linear with w_out.
  *   hidden [B][E] bf16; weights as in gdn_layer_prefill; conv_state [B][3][conv_dim]
- *   bf16 and state [B][Hv][dk][dv] fp32 in/out; out [B][E] bf16.
- *   workspace  at least gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) bytes (x, z, g,
- *              beta, the normalised output and fp32 partial sums of the output projection,
- *              whose k extent is split over more compute units when B is small).
+ *   fp32 and state [B][Hv][dk][dv] fp32 in/out; out [B][E] bf16.
+ *   workspace  at least gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) bytes (x, the
+ *              gate product, g, beta, the normalised output and fp32 partial sums of the
+ *              output projection, whose k extent is split over more compute units when B
+ *              is small).
  * dk, dv in {16, 32, 64, 128}; E and Hv as in gdn_in_proj.
  */
 size_t gdn_layer_decode_workspace_size(int B, int E, int Hk, int Hv, int dk, int dv);

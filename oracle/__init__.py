@@ -76,13 +76,13 @@ def threads(units: int) -> int:
 
 
 def prep(x, w, cu, Hk, Hv, dk, dv, cs_in=None, eps=1e-6, want_cs_out=True):
-    """fp64 conv+SiLU+L2.  x [T,C], w [C,4], cu [N+1], cs_in [N,3,C] or None.
-    Inputs must be exactly representable in float32 (bf16 or fp32 values)."""
-    x = _f32(x); w = _f32(w); cu = _i32(cu)
+    """fp64 conv+SiLU+L2.  x [T,C], w [C,4], cu [N+1], cs_in [N,3,C] or None (any float
+    dtype; used as fp64)."""
+    x = _f64(x); w = _f64(w); cu = _i32(cu)
     T, C = x.shape
     assert C == 2 * Hk * dk + Hv * dv and w.shape == (C, 4)
     N = len(cu) - 1
-    csi = None if cs_in is None else _f32(cs_in)
+    csi = None if cs_in is None else _f64(cs_in)
     q = np.zeros((T, Hk, dk)); k = np.zeros((T, Hk, dk)); v = np.zeros((T, Hv, dv))
     cso = np.zeros((N, 3, C)) if want_cs_out else None
     lib().oracle_prep(_p(x), _p(w), _p(cu), N, _p(csi), _p(cso), _p(q), _p(k), _p(v),
@@ -109,8 +109,9 @@ def recurrence(q, k, v, g, beta, cu, s0=None, scale=1.0, heads=None, order=0):
 
 
 def decode(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=1e-6, order=0):
-    """fp64 decode step.  Returns o [B,Hv,dv], new state, new conv cache."""
-    x = _f32(x); w = _f32(w); cs = _f32(cs); g = _f32(g); beta = _f32(beta); st = _f32(state)
+    """fp64 decode step (x, w, cs of any float dtype, used as fp64; g, beta and the state
+    as float32, the library's types).  Returns o [B,Hv,dv], new state, new conv cache."""
+    x = _f64(x); w = _f64(w); cs = _f64(cs); g = _f32(g); beta = _f32(beta); st = _f32(state)
     B = x.shape[0]
     o = np.zeros((B, Hv, dv)); st_out = np.zeros((B, Hv, dk, dv)); cs_out = np.zeros(cs.shape)
     lib().oracle_decode(_p(x), _p(w), _p(cs), _p(cs_out), _p(g), _p(beta), _p(st), _p(st_out), _p(o),
@@ -120,12 +121,11 @@ def decode(x, w, cs, g, beta, state, Hk, Hv, dk, dv, scale=1.0, eps=1e-6, order=
 
 def gated_rmsnorm(y, z, gamma, eps=1e-6):
     """fp64 gated RMSNorm over the last axis: y / sqrt(mean y^2 + eps) * gamma * SiLU(z).
-    y [..., dv] (any float dtype, used as fp64), z same shape and gamma [dv] with
-    float32-representable values."""
+    y [..., dv], z same shape and gamma [dv] (any float dtype, used as fp64)."""
     y = _f64(y)
     dv = y.shape[-1]
-    z = _f32(z)
-    gamma = _f32(gamma)
+    z = _f64(z)
+    gamma = _f64(gamma)
     assert z.shape == y.shape and gamma.shape == (dv,)
     out = np.zeros(y.shape)
     rows = y.size // dv if dv else 0
@@ -140,18 +140,16 @@ def layer_prefill(hidden, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, cs_in=
     heads: optional list of value heads whose recurrence is computed (the others'
     outputs and states are zero, and so is ``out``'s dependence on them); ``None`` =
     all heads.  Returns out [T, E], final states, conv caches, and the intermediate
-    tensors {x, z, g, beta, y} (y = the bf16 normalised output entering the output
-    projection)."""
+    tensors {x, z, g, beta, y} (y = the normalised output entering the output
+    projection).  Nothing between the input projection and the output is rounded."""
     from . import gdn_ref
     hidden = _f64(hidden)
     T = hidden.shape[0]
-    xp, zp, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
-    x = gdn_ref.bf16_round(xp)
-    z = gdn_ref.bf16_round(zp)
+    x, z, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
     g, beta = gdn_ref.layer_gates(ap, bp)
     q, k, v, cs_out = prep(x, conv_w, cu, Hk, Hv, dk, dv, cs_in, l2_eps)
     o, fin = recurrence(q, k, v, g, beta, cu, s0, scale, heads=heads, order=order)
-    y = gdn_ref.bf16_round(gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps)).reshape(T, Hv * dv)
+    y = gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps).reshape(T, Hv * dv)
     if heads is not None:
         keep = np.zeros((Hv, dv))
         keep[list(heads)] = 1.0
@@ -167,10 +165,8 @@ def layer_decode(hidden, w_in, conv_w, gamma, w_out, cs, state, Hk, Hv, dk, dv, 
     from . import gdn_ref
     hidden = _f64(hidden)
     B = hidden.shape[0]
-    xp, zp, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
-    x = gdn_ref.bf16_round(xp)
-    z = gdn_ref.bf16_round(zp)
+    x, z, ap, bp = gdn_ref.layer_split(hidden @ _f64(w_in).T, Hk, Hv, dk, dv)
     g, beta = gdn_ref.layer_gates(ap, bp)
     o, st, cso = decode(x, conv_w, cs, g, beta, state, Hk, Hv, dk, dv, scale, l2_eps, order)
-    y = gdn_ref.bf16_round(gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps)).reshape(B, Hv * dv)
+    y = gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps).reshape(B, Hv * dv)
     return y @ _f64(w_out).T, st, cso, {"x": x, "z": z, "g": g, "beta": beta, "y": y}

@@ -15,9 +15,12 @@
  *             paper.xwysyy.cn), section 7.6.2 (recurrence, depthwise causal
  *             conv1d with kernel 4, L2 normalisation of q and k).
  *
- * Everything here is computed in double precision from input values that are
- * passed as float32 arrays.  bf16 and fp32 inputs are exactly representable in
- * float32, so the oracle sees the exact stored values.
+ * Everything here is computed in double precision.  Inputs are passed as double
+ * arrays (the pre-conv x, conv weights, conv caches, the gate z) or as float32 arrays
+ * (g, beta, the recurrent states, which the library stores in fp32); the bf16 and
+ * fp32 values of stored inputs are exact in either, so the oracle sees the exact
+ * stored values, and inputs that are themselves exact products (the layer's
+ * projections) reach it unrounded.
  *
  * Layouts (row-major, contiguous):
  *   x        [T][conv_dim]        conv_dim = 2*Hk*dk + Hv*dv, channel order q | k | v
@@ -73,8 +76,8 @@ static double silu(double y) { return y / (1.0 + exp(-y)); }
  *
  * cs_in may be NULL (zero history).  cs_out may be NULL.
  */
-void oracle_prep(const float *x, const float *w, const int32_t *cu, int N,
-                 const float *cs_in, double *cs_out,
+void oracle_prep(const double *x, const double *w, const int32_t *cu, int N,
+                 const double *cs_in, double *cs_out,
                  double *q, double *k, double *v,
                  int T, int Hk, int Hv, int dk, int dv, double eps)
 {
@@ -234,7 +237,7 @@ void oracle_recurrence(const double *q, const double *k, const double *v,
  *   cs[b] <- [cs[b][1], cs[b][2], x[b]]
  * Inputs are never modified; updated caches go to cs_out / state_out.
  */
-void oracle_decode(const float *x, const float *w, const float *cs_in, double *cs_out,
+void oracle_decode(const double *x, const double *w, const double *cs_in, double *cs_out,
                    const float *g, const float *beta, const float *state_in, double *state_out,
                    double *o, double scale, double eps,
                    int B, int Hk, int Hv, int dk, int dv, int order)
@@ -295,7 +298,7 @@ void oracle_decode(const float *x, const float *w, const float *cs_in, double *c
  *   z   [rows][dv]  the gate
  *   out [rows][dv]  out[r][j] = y[r][j] / sqrt(mean_j y[r][j]^2 + eps) * gamma[j] * SiLU(z[r][j])
  */
-void oracle_gated_rmsnorm(const double *y, const float *z, const float *gamma, double *out,
+void oracle_gated_rmsnorm(const double *y, const double *z, const double *gamma, double *out,
                           long rows, int dv, double eps)
 {
 #pragma omp parallel for schedule(static)

@@ -200,17 +200,10 @@ def gated_rmsnorm(y, z, gamma, eps=1e-6):
 # output projection.  The pages do not say how the two gate pre-activations become
 # gates; the reading taken here is g = -softplus(a) (so a = exp(g) lies in (0, 1)) and
 # beta = sigmoid(b), the maps under which N(0, 1) pre-activations give the layer
-# shape's gate distributions.  The layer's intermediate tensors have the library's
-# types: the pre-conv q|k|v, z and the normalised output entering the output
-# projection are bf16 (the element type), g and beta fp32; everything else is fp64.
-
-
-def bf16_round(x):
-    """Nearest bfloat16 value of each element (8 significant bits, ties to even),
-    as an fp64 array; for values in the normal range."""
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)                      # x = m 2^e, 0.5 <= |m| < 1
-    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+# shape's gate distributions.  Nothing between the input projection and the output
+# is rounded: the pre-conv q|k|v, z and the normalised output entering the output
+# projection are the exact fp64 values; g and beta are taken as fp32 (the library's
+# gate type, as for the core's inputs).
 
 
 def softplus(x):
@@ -245,13 +238,11 @@ def layer_prefill(hidden, w_in, conv_w, gamma, w_out, cu, Hk, Hv, dk, dv, cs_in=
     final states [N, Hv, dk, dv] and the conv caches [N, 3, conv_dim]."""
     hidden = np.asarray(hidden, np.float64)
     T = hidden.shape[0]
-    xp, zp, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
-    x = bf16_round(xp)
-    z = bf16_round(zp)
+    x, z, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
     g, beta = layer_gates(ap, bp)
     q, k, v, cs_out = prep(x, conv_w, cu, Hk, Hv, dk, dv, cs_in, l2_eps)
     o, fin = recurrence(q, k, v, g, beta, cu, s0, scale, order)
-    y = bf16_round(gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps)).reshape(T, Hv * dv)
+    y = gated_rmsnorm(o, z.reshape(T, Hv, dv), gamma, norm_eps).reshape(T, Hv * dv)
     return y @ np.asarray(w_out, np.float64).T, fin, cs_out
 
 
@@ -262,10 +253,8 @@ def layer_decode(hidden, w_in, conv_w, gamma, w_out, cs, state, Hk, Hv, dk, dv, 
     the new conv cache."""
     hidden = np.asarray(hidden, np.float64)
     B = hidden.shape[0]
-    xp, zp, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
-    x = bf16_round(xp)
-    z = bf16_round(zp)
+    x, z, ap, bp = layer_split(hidden @ np.asarray(w_in, np.float64).T, Hk, Hv, dk, dv)
     g, beta = layer_gates(ap, bp)
     o, new_state, new_cs = decode_step(x, conv_w, cs, g, beta, state, Hk, Hv, dk, dv, scale, l2_eps, order)
-    y = bf16_round(gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps)).reshape(B, Hv * dv)
+    y = gated_rmsnorm(o, z.reshape(B, Hv, dv), gamma, norm_eps).reshape(B, Hv * dv)
     return y @ np.asarray(w_out, np.float64).T, new_state, new_cs

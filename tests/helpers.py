@@ -48,3 +48,18 @@ def assert_bf16_rounded(name, gpu, ref):
     worst = float(np.max(np.abs(gpu - ref) / bound)) if ref.size else 0.0
     print(f"    {name}: max |err| / (1 bf16 ulp) = {worst:.3f}", flush=True)
     assert worst <= 1.0, f"{name}: error exceeds one bf16 ulp (ratio {worst:.3f})"
+
+
+def assert_parity_bf16_out(name, gpu, ref, tol):
+    """Parity of an output the GPU stores in bf16: within tol * RMS(oracle) plus the
+    output's own rounding, one bf16 ulp (2^-8 relative) of the oracle value, per element."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape
+    assert np.all(np.isfinite(gpu)), "non-finite GPU output"
+    rms = np.sqrt(np.mean(ref * ref))
+    err = np.abs(gpu - ref)
+    worst = float(np.max(err / (tol * rms + 2.0 ** -8 * np.abs(ref)))) if ref.size else 0.0
+    print(f"    {name}: max|err|/rms = {float(np.max(err)) / rms if ref.size else 0.0:.3e}; "
+          f"max err / (tol rms + 1 bf16 ulp) = {worst:.3f} (tol {tol:.0e})", flush=True)
+    assert worst <= 1.0, f"{name}: error beyond {tol:.0e} RMS + one bf16 ulp (ratio {worst:.3f})"

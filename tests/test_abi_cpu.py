@@ -31,13 +31,14 @@ def test_exports_every_declared_symbol(L):
     assert {"gdn_conv_qk_prep", "gdn_chunk_prefill", "gdn_chunk_prefill_workspace_size", "gdn_prefill",
             "gdn_prefill_local", "gdn_decode_step", "gdn_decode_step_gated", "gdn_gated_rmsnorm",
             "gdn_status_string", "gdn_abi_version", "gdn_linear", "gdn_in_proj", "gdn_layer_prefill",
-            "gdn_layer_prefill_workspace_size", "gdn_layer_decode", "gdn_layer_decode_workspace_size"} <= set(names)
+            "gdn_layer_prefill_workspace_size", "gdn_layer_decode", "gdn_layer_decode_workspace_size",
+            "gdn_prefill_workspace_status"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.gdn_abi_version() == 5
+    assert L.gdn_abi_version() == 6
     for code in range(8):
         assert L.gdn_status_string(code).decode().startswith("GDN_")
     assert b"unknown" in L.gdn_status_string(99)
@@ -265,6 +266,7 @@ def test_layer_prefill_validation(L):
                                    a["order"], a["ws"], a["wsb"], None)
     assert call(N=2) == 2                                        # two sequences need cu_seqlens
     assert call(E=100) == 3
+    assert call(Hk=1, Hv=1) == 3                                 # Hv dv = 64: not whole 128-deep stages
     assert call(dk=32, dv=32) == 3
     assert call(order=2) == 3
     assert call(gm=None) == 1
@@ -296,6 +298,15 @@ def test_layer_decode_validation(L):
     assert call(out=P((6 << 24) + 64)) == 6                      # out overlaps the state
     assert call(cs=P((6 << 24) + 16)) == 6                       # conv cache overlaps the state
     assert call(h=P(4)) == 7
+
+
+def test_workspace_status_validation(L):
+    L.gdn_prefill_workspace_status.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert L.gdn_prefill_workspace_status(None, 1024, None) == 1
+    assert L.gdn_prefill_workspace_status(_ptr(8), 1024, None) == 7
+    assert L.gdn_prefill_workspace_status(_ptr(0x10000), 255, None) == 4
+    for code in (8, 9):
+        assert L.gdn_status_string(code).decode().startswith(("GDN_ERR_TIMEOUT", "GDN_ERR_NONFINITE"))
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

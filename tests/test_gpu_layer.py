@@ -3,15 +3,16 @@ RMSNorm) through the C ABI against the fp64 CPU oracle.
 
 Projection outputs the GPU stores in bf16 are checked element by element against the
 fp64 products (within one bf16 rounding, see helpers.assert_bf16_rounded); the gates to
-fp32 accuracy.  The layer cases draw the input and the input projection on grids for
-which every projected value is exact in fp32 (inputs.layer_hidden, exact=True): the GPU
-and the oracle then round the same values to the bf16 x and z, so their conv caches match
-bit for bit, and the layer outputs and final states are held to 2e-2 RMS (bf16 weights
-and activations, fp32 state).  With unconstrained draws the bf16 rounding of x is a
-different decision on the two sides for the few values within an fp32 rounding of a
-midpoint, and the state is sensitive to those one-ulp changes of its inputs (a few
-hundred such values in the 0.8B decode batch move the state by 2.5e-2 RMS on their
-own): both results are correct roundings, so the parity check fixes the decision.
+fp32 accuracy.  The layer cases draw their inputs and weights from N(0, 1)-scaled
+distributions with no constraint (the bench's own layer inputs among them) and hold the
+final states to 2e-2 RMS (bf16 weights and layer input, fp32 state) and the bf16 layer
+output to 2e-2 RMS plus its own rounding (one bf16 ulp of each element).
+The oracle rounds nothing between the input projection and the output: inside the
+layer the pre-conv q|k|v and the conv caches are fp32 on the GPU (the recurrent state
+amplifies one-ulp changes of its inputs), and the gate and the normalised output that
+enter the output projection are bf16, whose roundings the 2e-2 bar covers.  One case
+draws the input and the input projection on grids on which every projected value is
+exact in fp32, as an extra check of the same path.
 """
 import numpy as np
 import pytest
@@ -19,7 +20,7 @@ import torch
 
 import oracle
 from oracle import gdn_ref
-from helpers import TOL_BF16, announce, assert_bf16_rounded, assert_parity, f32np
+from helpers import TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, assert_parity_bf16_out, f32np
 from hybrid_linear_attention_gated_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -93,19 +94,19 @@ def test_in_proj(gdn, T, E, Hk, Hv, d):
 
 # ------------------------------------------------------------------ layer prefill
 
-def _layer_case(gdn, lengths, E, Hk, Hv, d, seed, caches, scale, order=0, heads=None):
+def _layer_case(gdn, lengths, E, Hk, Hv, d, seed, caches, scale, order=0, exact=False, hidden_seed=None):
     T = int(sum(lengths))
     N = len(lengths)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
-    wts = inputs.layer_weights(seed, E, Hk, Hv, d, d, exact=True)
-    h = inputs.layer_hidden(seed + 1, T, E, exact=True)
+    wts = inputs.layer_weights(seed, E, Hk, Hv, d, d, exact=exact)
+    h = inputs.layer_hidden(seed + 1 if hidden_seed is None else hidden_seed, T, E, exact=exact)
     cs_in, s0 = inputs.layer_caches(seed + 2, N, Hk, Hv, d, d) if caches else (None, None)
     out_ref, fin_ref, cs_ref, _ = oracle.layer_prefill(
         f32np(h), f32np(wts.w_in), f32np(wts.conv_w), f32np(wts.gamma), f32np(wts.w_out), cu.numpy(), Hk, Hv, d, d,
         cs_in=None if cs_in is None else f32np(cs_in), s0=None if s0 is None else f32np(s0), scale=scale,
-        order=order, heads=heads)
+        order=order)
     C = 2 * Hk * d + Hv * d
-    cs_out = torch.empty((N, 3, C), dtype=torch.bfloat16, device=DEV)
+    cs_out = torch.empty((N, 3, C), dtype=torch.float32, device=DEV)
     out, fin = gdn.layer_prefill(_cuda(h), _cuda(wts.w_in), _cuda(wts.conv_w), _cuda(wts.gamma), _cuda(wts.w_out),
                                  Hk, Hv, d, d, cu_seqlens=_cuda(cu) if N > 1 else None,
                                  conv_state_in=_cuda(cs_in), conv_state_out=cs_out, initial_state=_cuda(s0),
@@ -114,41 +115,50 @@ def _layer_case(gdn, lengths, E, Hk, Hv, d, seed, caches, scale, order=0, heads=
     return (out, fin, cs_out), (out_ref, fin_ref, cs_ref)
 
 
+def _check_layer(out, fin, cs, out_ref, fin_ref, cs_ref):
+    # the layer output is stored in bf16: its own rounding (one bf16 ulp at most) on top of
+    # the 2e-2 RMS bar
+    assert_parity_bf16_out("out", f32np(out), out_ref, TOL_BF16)
+    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
+    # the conv cache holds fp32 projections (or copies of the incoming cache)
+    assert_parity("conv cache", f32np(cs), cs_ref, TOL_F32)
+
+
 @pytest.mark.parametrize("order", [0, 1])
 def test_layer_prefill_small_varlen(gdn, order):
     announce(f"layer prefill varlen small order={order}")
-    (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [70, 0, 150, 1], 128, 1, 2, 64, 620, True, 0.125,
-                                                             order)
-    assert_parity("out", f32np(out), out_ref, TOL_BF16)
-    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+    gpu, ref = _layer_case(gdn, [70, 0, 150, 1], 128, 1, 2, 64, 620, True, 0.125, order)
+    _check_layer(*gpu, *ref)
 
 
 def test_layer_prefill_gqa_128(gdn):
     announce("layer prefill Hk=2 Hv=4 d=128 two sequences")
-    (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [129, 200], 256, 2, 4, 128, 630, True, 1.0)
-    assert_parity("out", f32np(out), out_ref, TOL_BF16)
-    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+    gpu, ref = _layer_case(gdn, [129, 200], 256, 2, 4, 128, 630, True, 1.0)
+    _check_layer(*gpu, *ref)
 
 
 def test_layer_prefill_wide_gates_gqa4(gdn):
     """32 value heads over 8 key heads (the widest gate block the input projection takes: 64
     gate columns) at head dim 64, two sequences with caches in."""
     announce("layer prefill Hk=8 Hv=32 d=64 two sequences")
-    (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [120, 77], 256, 8, 32, 64, 635, True, 0.5)
-    assert_parity("out", f32np(out), out_ref, TOL_BF16)
-    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+    gpu, ref = _layer_case(gdn, [120, 77], 256, 8, 32, 64, 635, True, 0.5)
+    _check_layer(*gpu, *ref)
 
 
-def test_layer_prefill_0p8b_shape(gdn):
-    """The 0.8B layer shape: T = 4096, hidden 1024, 16 / 16 heads of 128, zero caches."""
-    announce("layer prefill T=4096 E=1024 16/16 heads d=128")
-    (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [4096], 1024, 16, 16, 128, 640, False, 1.0)
-    assert_parity("out", f32np(out), out_ref, TOL_BF16)
-    assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+def test_layer_prefill_0p8b_shape_bench_inputs(gdn):
+    """The 0.8B layer shape with the bench's own layer inputs: T = 4096, hidden 1024, 16 / 16
+    heads of 128, zero caches, weights from seed 7 and the hidden rows from seed 8."""
+    announce("layer prefill T=4096 E=1024 16/16 heads d=128 (bench inputs)")
+    gpu, ref = _layer_case(gdn, [4096], 1024, 16, 16, 128, 7, False, 1.0, hidden_seed=8)
+    _check_layer(*gpu, *ref)
+
+
+def test_layer_prefill_grid_inputs(gdn):
+    """The layer on grid-drawn input and input projection (every projected value exact in
+    fp32), two sequences with caches in."""
+    announce("layer prefill on grid inputs, Hk=2 Hv=4 d=128")
+    gpu, ref = _layer_case(gdn, [300, 65], 512, 2, 4, 128, 640, True, 1.0, exact=True)
+    _check_layer(*gpu, *ref)
 
 
 def test_layer_prefill_empty(gdn):
@@ -161,30 +171,55 @@ def test_layer_prefill_empty(gdn):
 
 # ------------------------------------------------------------------ layer decode
 
-def _decode_case(gdn, B, E, Hk, Hv, d, seed, order=0):
-    wts = inputs.layer_weights(seed, E, Hk, Hv, d, d, exact=True)
-    h = inputs.layer_hidden(seed + 1, B, E, exact=True)
+def _decode_case(gdn, B, E, Hk, Hv, d, seed, order=0, exact=False):
+    wts = inputs.layer_weights(seed, E, Hk, Hv, d, d, exact=exact)
+    h = inputs.layer_hidden(seed + 1, B, E, exact=exact)
     cs, st = inputs.layer_caches(seed + 2, B, Hk, Hv, d, d)
+    return _decode_run(gdn, wts, h, cs, st, Hk, Hv, d, 0.5, order)
+
+
+def _decode_run(gdn, wts, h, cs, st, Hk, Hv, d, scale, order=0):
     out_ref, st_ref, cs_ref, _ = oracle.layer_decode(f32np(h), f32np(wts.w_in), f32np(wts.conv_w), f32np(wts.gamma),
                                                      f32np(wts.w_out), f32np(cs), f32np(st), Hk, Hv, d, d,
-                                                     scale=0.5, order=order)
+                                                     scale=scale, order=order)
     csd, std = _cuda(cs), _cuda(st)
     out = gdn.layer_decode(_cuda(h), _cuda(wts.w_in), _cuda(wts.conv_w), _cuda(wts.gamma), _cuda(wts.w_out), csd, std,
-                           Hk, Hv, d, d, scale=0.5, order=order)
+                           Hk, Hv, d, d, scale=scale, order=order)
     torch.cuda.synchronize()
     return (out, std, csd), (out_ref, st_ref, cs_ref)
 
 
+def _check_decode(out, st, cs, out_ref, st_ref, cs_ref):
+    assert_parity_bf16_out("out", f32np(out), out_ref, TOL_BF16)
+    assert_parity("state", f32np(st), st_ref, TOL_BF16)
+    assert_parity("conv cache", f32np(cs), cs_ref, TOL_F32)
+
+
 # (33, 192, ...) and (256, 1024, ...) split the output projection's k extent (4 and 16 slices
 # summed in a second pass; 33 x 192 also leaves a partial column tile)
-@pytest.mark.parametrize("B,E,Hk,Hv,d,order", [(5, 128, 2, 4, 32, 0), (3, 64, 1, 1, 64, 1), (33, 192, 2, 4, 128, 0),
+@pytest.mark.parametrize("B,E,Hk,Hv,d,order", [(5, 128, 2, 4, 32, 0), (3, 64, 1, 2, 64, 1), (33, 192, 2, 4, 128, 0),
                                                (256, 1024, 16, 16, 128, 0)])
 def test_layer_decode(gdn, B, E, Hk, Hv, d, order):
     announce(f"layer decode B={B} E={E} Hk={Hk} Hv={Hv} d={d} order={order}")
-    (out, st, cs), (out_ref, st_ref, cs_ref) = _decode_case(gdn, B, E, Hk, Hv, d, 660 + B, order)
-    assert_parity("out", f32np(out), out_ref, TOL_BF16)
-    assert_parity("state", f32np(st), st_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+    gpu, ref = _decode_case(gdn, B, E, Hk, Hv, d, 660 + B, order)
+    _check_decode(*gpu, *ref)
+
+
+def test_layer_decode_bench_inputs(gdn):
+    """The bench's layer decode step: 256 rows of hidden 1024 (seed 11) through the layer
+    weights of seed 7, with the decode256 workload's state and conv cache (as fp32)."""
+    announce("layer decode B=256 E=1024 16/16 heads d=128 (bench inputs)")
+    dw = inputs.decode256()
+    wts = inputs.layer_weights(7, 1024, 16, 16, 128, 128)
+    h = inputs.layer_hidden(11, 256, 1024)
+    gpu, ref = _decode_run(gdn, wts, h, dw.conv_state.float(), dw.state, 16, 16, 128, 1.0)
+    _check_decode(*gpu, *ref)
+
+
+def test_layer_decode_grid_inputs(gdn):
+    announce("layer decode on grid inputs, B=40 Hk=2 Hv=4 d=64")
+    gpu, ref = _decode_case(gdn, 40, 256, 2, 4, 64, 690, exact=True)
+    _check_decode(*gpu, *ref)
 
 
 def test_layer_decode_continues_layer_prefill(gdn):
@@ -192,19 +227,19 @@ def test_layer_decode_continues_layer_prefill(gdn):
     L + 1 tokens."""
     announce("layer prefill + decode vs oracle prefill of one more token")
     E, Hk, Hv, d, L = 256, 2, 4, 64, 131
-    wts = inputs.layer_weights(670, E, Hk, Hv, d, d, exact=True)
-    h = inputs.layer_hidden(671, L + 1, E, exact=True)
+    wts = inputs.layer_weights(670, E, Hk, Hv, d, d)
+    h = inputs.layer_hidden(671, L + 1, E)
     cu = np.array([0, L + 1], np.int32)
     out_ref, fin_ref, cs_ref, _ = oracle.layer_prefill(f32np(h), f32np(wts.w_in), f32np(wts.conv_w),
                                                        f32np(wts.gamma), f32np(wts.w_out), cu, Hk, Hv, d, d)
     C = 2 * Hk * d + Hv * d
-    cs = torch.zeros((1, 3, C), dtype=torch.bfloat16, device=DEV)
+    cs = torch.zeros((1, 3, C), dtype=torch.float32, device=DEV)
     out_p, fin = gdn.layer_prefill(_cuda(h[:L]), _cuda(wts.w_in), _cuda(wts.conv_w), _cuda(wts.gamma),
                                    _cuda(wts.w_out), Hk, Hv, d, d, conv_state_out=cs)
     out_d = gdn.layer_decode(_cuda(h[L:]), _cuda(wts.w_in), _cuda(wts.conv_w), _cuda(wts.gamma), _cuda(wts.w_out),
                              cs, fin, Hk, Hv, d, d)
     torch.cuda.synchronize()
     gpu = np.concatenate([f32np(out_p), f32np(out_d)])
-    assert_parity("out", gpu, out_ref, TOL_BF16)
+    assert_parity_bf16_out("out", gpu, out_ref, TOL_BF16)
     assert_parity("final state", f32np(fin), fin_ref, TOL_BF16)
-    np.testing.assert_array_equal(f32np(cs), cs_ref)
+    assert_parity("conv cache", f32np(cs), cs_ref, TOL_F32)

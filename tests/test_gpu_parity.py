@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, err_ratio, f32np
+from helpers import (TOL_BF16, TOL_F32, announce, assert_bf16_rounded, assert_parity, assert_parity_bf16_out,
+                     err_ratio, f32np)
 from hybrid_linear_attention_gated_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -241,16 +242,33 @@ def test_core_empty_sequences(gdn):
 
 # ------------------------------------------------------------------ end to end: prep + chunk prefill
 
-def _e2e(gdn, wl, heads=None, fused=False):
+def _e2e_reference(wl):
+    """The oracle's prep and recurrence for a workload, over every value head."""
     cu = wl.cu_seqlens
-    N = wl.N
     x32 = f32np(wl.x)
     q_r, k_r, v_r, cs_r = oracle.prep(x32, f32np(wl.conv_w), cu.numpy(), wl.Hk, wl.Hv, wl.dk, wl.dv,
                                       cs_in=None if wl.conv_state is None else f32np(wl.conv_state))
     del x32
     o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, f32np(wl.g), f32np(wl.beta), cu.numpy(),
-                                     s0=None if wl.state is None else f32np(wl.state), heads=heads)
-    del q_r, k_r, v_r
+                                     s0=None if wl.state is None else f32np(wl.state))
+    return o_ref, f_ref, cs_r
+
+
+# The long_64k reference (65536 tokens x 32 value heads, every head) takes the oracle about
+# ten seconds on the box's cores; the two long_64k tests share it.
+_LONG_REF = {}
+
+
+def _long_64k_reference(wl):
+    if "ref" not in _LONG_REF:
+        _LONG_REF["ref"] = _e2e_reference(wl)
+    return _LONG_REF["ref"]
+
+
+def _e2e(gdn, wl, fused=False, ref=None):
+    cu = wl.cu_seqlens
+    N = wl.N
+    o_ref, f_ref, cs_r = _e2e_reference(wl) if ref is None else ref
     cso = torch.empty((N, 3, wl.conv_dim), dtype=torch.bfloat16, device=DEV)
     if fused:
         o, f = gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), wl.Hk, wl.Hv, wl.dk, wl.dv,
@@ -262,11 +280,8 @@ def _e2e(gdn, wl, heads=None, fused=False):
         o, f = gdn.chunk_prefill(q, k, v, _cuda(wl.g), _cuda(wl.beta), cu_seqlens=_cuda(cu),
                                  initial_state=_cuda(wl.state), math="mfma")
     torch.cuda.synchronize()
-    o, f = f32np(o), f32np(f)
-    if heads is not None:
-        o, o_ref, f, f_ref = o[:, heads], o_ref[:, heads], f[:, heads], f_ref[:, heads]
-    assert_parity("o", o, o_ref, TOL_BF16)
-    assert_parity("final_state", f, f_ref, TOL_BF16)
+    assert_parity("o", f32np(o), o_ref, TOL_BF16)
+    assert_parity("final_state", f32np(f), f_ref, TOL_BF16)
     np.testing.assert_array_equal(f32np(cso), cs_r)
 
 
@@ -280,9 +295,10 @@ def test_varlen8_config(gdn):
     _e2e(gdn, inputs.varlen8())
 
 
-def test_long_64k_config_sampled_heads(gdn):
-    announce("long_64k config end to end (oracle on sampled value heads 0, 1, 17, 31)")
-    _e2e(gdn, inputs.long_64k(), heads=[0, 1, 17, 31])
+def test_long_64k_config(gdn):
+    announce("long_64k config end to end (all 32 value heads)")
+    wl = inputs.long_64k()
+    _e2e(gdn, wl, ref=_long_64k_reference(wl))
 
 
 # ------------------------------------------------------------------ fused prep + chunk prefill (one call)
@@ -297,9 +313,11 @@ def test_fused_varlen8_config(gdn):
     _e2e(gdn, inputs.varlen8(), fused=True)
 
 
-def test_fused_long_64k_config_sampled_heads(gdn):
-    announce("long_64k config, fused prefill (oracle on sampled value heads 0, 1, 17, 31)")
-    _e2e(gdn, inputs.long_64k(), heads=[0, 1, 17, 31], fused=True)
+def test_fused_long_64k_config(gdn):
+    announce("long_64k config, fused prefill (all 32 value heads)")
+    wl = inputs.long_64k()
+    _e2e(gdn, wl, fused=True, ref=_long_64k_reference(wl))
+    _LONG_REF.clear()
 
 
 # short and empty sequences, sequences shorter than the conv window, ragged tails
@@ -470,7 +488,7 @@ def test_decode_gated(gdn, B, Hk, Hv, d, dtype):
 
 def test_fused_prefill_then_gated_rmsnorm_layer_4k(gdn):
     """The layer_4k prefill (one gdn_prefill call) followed by the gated RMSNorm on its
-    output, against the oracle's prep, recurrence and norm."""
+    output, element by element against the oracle's prep, recurrence and norm."""
     announce("layer_4k: gdn_prefill + gated rmsnorm (bf16 gate / output)")
     wl = inputs.layer_4k()
     z, gamma = inputs.gate_inputs(940, (wl.T, wl.Hv, wl.dv), wl.dv, "bf16")
@@ -482,15 +500,9 @@ def test_fused_prefill_then_gated_rmsnorm_layer_4k(gdn):
                        cu_seqlens=_cuda(wl.cu_seqlens))
     out = gdn.gated_rmsnorm(o, _cuda(z), _cuda(gamma))
     torch.cuda.synchronize()
-    # The norm makes every (token, head) row scale-free, and its bf16 output rounds each
-    # element to 2^-9 of itself (rows hold elements up to ~50x the tensor's RMS), so the
-    # end-to-end bar is per row: RMS error of the row / RMS of the row <= 2e-2.
-    og, outg = f32np(o), f32np(out)
-    row_err = np.sqrt(np.mean((outg - ref) ** 2, axis=-1) / np.mean(ref ** 2, axis=-1))
-    print(f"    out: max row-relative RMS error = {row_err.max():.3e} (tol {TOL_BF16:.0e})", flush=True)
-    assert row_err.max() <= TOL_BF16
-    # the norm itself, on the prefill's own output: one bf16 rounding of the fp64 value
-    assert_bf16_rounded("out (norm of the GPU's o)", outg, oracle.gated_rmsnorm(og, f32np(z), f32np(gamma), 1e-6))
+    # the norm's bf16 output is heavy tailed (elements of ~30 RMS): 2e-2 RMS plus its own
+    # rounding, one bf16 ulp of each element
+    assert_parity_bf16_out("out", f32np(out), ref, TOL_BF16)
 
 
 # ------------------------------------------------------------------ retrieval order 1 (undecayed retrieval)
@@ -660,3 +672,138 @@ def test_concurrent_schedule_from_several_streams(gdn):
     for j, c in enumerate(cases):
         assert torch.equal(c["o"], c["o_ref"]), f"stream {j}: o differs from the split phases"
         assert torch.equal(c["f"], c["f_ref"]), f"stream {j}: final state differs from the split phases"
+
+
+# ------------------------------------------------------------------ failure reporting and graph capture
+
+def test_concurrent_wait_bound_reports_timeout(gdn):
+    """The concurrent schedule's state pass with its record waits bounded to one sleep
+    (set in the workspace header from the host): the first record is not published that
+    fast, so the state pass stops waiting, writes NaN outputs and final states and sets
+    the workspace status to GDN_ERR_TIMEOUT; the chunk-local kernel runs to its end.  With
+    the default bound restored, the same workspace gives the split phases' result and the
+    status reads GDN_OK."""
+    announce("concurrent schedule with a one-sleep wait bound: T=8000, Hk=2, Hv=4")
+    T, Hk, Hv, d = 8000, 2, 4, 128
+    wl = inputs.prefill_workload("timeout", 1020, [T], Hk, Hv, d, random_states=True)
+    x, w, g, b, s0 = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state))
+    ws = torch.zeros(gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
+    gdn.set_wait_bound(ws, 1)
+    o1, f1 = gdn.prefill(x, w, g, b, Hk, Hv, d, d, initial_state=s0, workspace=ws)
+    torch.cuda.synchronize()
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_ERR_TIMEOUT
+    assert torch.isnan(f1).any(), "the final state of a failed call is NaN"
+    assert torch.isnan(o1).any(), "the outputs of a failed call are NaN"
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK   # the query cleared it
+    gdn.set_wait_bound(ws, None)
+    o2, f2 = gdn.prefill(x, w, g, b, Hk, Hv, d, d, initial_state=s0, workspace=ws)
+    ws_ref = torch.empty_like(ws)
+    o_ref, f_ref = torch.empty_like(o2), torch.empty_like(f2)
+    gdn.prefill_local(x, w, g, b, ws_ref, Hk, Hv, d, d)
+    gdn.chunk_prefill_state(ws_ref, o_ref, T, Hk, Hv, d, d, initial_state=s0, final_state=f_ref)
+    torch.cuda.synchronize()
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
+    assert torch.equal(o2, o_ref) and torch.equal(f2, f_ref)
+
+
+@pytest.mark.parametrize("T", [200, 8000])
+def test_state_overflow_reports_nonfinite(gdn, T):
+    """An initial state beyond the fp16 range of the state pass's operands (+-65504) makes
+    the outputs non-finite; the status word says so (sequential schedule at T = 200, the
+    concurrent one at T = 8000)."""
+    announce(f"state beyond the fp16 range, T={T}: status GDN_ERR_NONFINITE")
+    Hk, Hv, d = 2, 4, 128
+    wl = inputs.prefill_workload("overflow", 1030, [T], Hk, Hv, d, random_states=True)
+    s0 = wl.state.clone()
+    s0[0, 1, 5, 7] = 1.0e6
+    ws = torch.zeros(gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    o, f = gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), Hk, Hv, d, d,
+                       initial_state=_cuda(s0), workspace=ws)
+    torch.cuda.synchronize()
+    assert not bool(torch.isfinite(o).all()) or not bool(torch.isfinite(f).all())
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_ERR_NONFINITE
+    # a finite call on the same workspace reports nothing
+    gdn.prefill(_cuda(wl.x), _cuda(wl.conv_w), _cuda(wl.g), _cuda(wl.beta), Hk, Hv, d, d,
+                initial_state=_cuda(wl.state), workspace=ws)
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
+
+
+_DEBUG_CHILD = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import hybrid_linear_attention_gated_amd as gdn
+from hybrid_linear_attention_gated_amd import inputs
+dev = "cuda:0"
+wl = inputs.prefill_workload("dbg", 1040, [70, 0, 130], 2, 4, 128, random_states=True)
+x, w, g, b, s0 = (t.to(dev) for t in (wl.x, wl.conv_w, wl.g, wl.beta, wl.state))
+cu = wl.cu_seqlens.to(dev)
+o, f = gdn.prefill(x, w, g, b, 2, 4, 128, 128, cu_seqlens=cu, initial_state=s0)
+torch.cuda.synchronize()
+bad = torch.tensor([0, 70, 60, 200], dtype=torch.int32, device=dev)   # decreasing
+codes = []
+for cus, st in ((bad, s0), (cu, None)):
+    if st is None:
+        st = s0.clone()
+        st[2, 2, 3, 4] = 1.0e6   # sequence 2 (130 tokens; sequence 1 is empty)
+    try:
+        gdn.prefill(x, w, g, b, 2, 4, 128, 128, cu_seqlens=cus, initial_state=st)
+        codes.append(0)
+    except gdn.GdnError as e:
+        codes.append(e.status)
+print("codes", codes[0], codes[1], flush=True)
+"""
+
+
+def test_debug_check_environment(gdn, tmp_path):
+    """With GDN_DEBUG_CHECK=1 (a child process: the library reads it once), a prefill call
+    returns GDN_ERR_BAD_SHAPE for a decreasing cu_seqlens before launching anything, and
+    GDN_ERR_NONFINITE itself for a state beyond the fp16 range."""
+    import os
+    import subprocess
+    import sys
+    announce("GDN_DEBUG_CHECK=1 in a child process: bad cu_seqlens, non-finite output")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, GDN_DEBUG_CHECK="1")
+    r = subprocess.run([sys.executable, "-c", _DEBUG_CHILD, root], env=env, capture_output=True, text=True,
+                       timeout=100)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    assert "codes 2 9" in r.stdout
+
+
+def test_graph_capture_of_layer_4k_prefill(gdn):
+    """gdn_prefill at the layer_4k shape captured into a HIP graph (torch.cuda.graph): under
+    capture the library takes the one-stream schedule.  The graph is replayed three times
+    with other eager work and synchronisations in between; every replay is bit-identical to
+    the eager call (which takes the concurrent schedule)."""
+    announce("graph capture of gdn_prefill at layer_4k, three replays")
+    wl = inputs.layer_4k()
+    x, w, g, b = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta))
+    T, Hk, Hv, d = wl.T, wl.Hk, wl.Hv, wl.dk
+    ws = torch.empty(gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma"), dtype=torch.uint8, device=DEV)
+    o = torch.empty((T, Hv, d), dtype=torch.float32, device=DEV)
+    f = torch.empty((1, Hv, d, d), dtype=torch.float32, device=DEV)
+    cso = torch.empty((1, 3, wl.conv_dim), dtype=torch.bfloat16, device=DEV)
+    o_ref, f_ref = gdn.prefill(x, w, g, b, Hk, Hv, d, d, conv_state_out=cso)
+    cso_ref = cso.clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            gdn.prefill(x, w, g, b, Hk, Hv, d, d, conv_state_out=cso, o=o, final_state=f, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.zero_()
+        f.zero_()
+        cso.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {rep}: o differs from the eager call"
+        assert torch.equal(f, f_ref), f"replay {rep}: final state differs from the eager call"
+        assert torch.equal(cso, cso_ref), f"replay {rep}: conv cache differs"
+        del junk
