@@ -174,6 +174,9 @@ def main():
     ap.add_argument("--metric-only", action="store_true",
                     help="time only the metric's region (gdn_prefill + decode step) and print its two times, "
                          "for kernel-trace runs of the concurrent prefill schedule")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the layer region (gdn_layer_prefill + gdn_layer_decode) and print its times, "
+                         "for kernel traces of the layer path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, stream 512 MiB through one elementwise kernel (counter calibration)")
     args = ap.parse_args()
@@ -338,6 +341,11 @@ def main():
              "in_proj", "out_proj"]
     two_call = None
     layer = None
+    if args.layer_only:
+        evs_l, _ = timed(step_layer, 5)
+        print(json.dumps({"layer_prefill_ms": mean_ms(evs_l, 0), "layer_decode_ms": mean_ms(evs_l, 1),
+                          "steps": args.steps, "warmup": args.warmup}))
+        return
     if not args.split_only:
         evs, wall = timed(step, 3)
         prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)

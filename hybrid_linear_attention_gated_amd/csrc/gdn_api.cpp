@@ -412,20 +412,15 @@ bool proj_shape_ok(int M, int N, int K) {
     return M >= 0 && N > 0 && N % 4 == 0 && K > 0 && K % 64 == 0 && K <= kProjMaxK;
 }
 
-// gain == NULL: the public input projection (x and z bf16).  gain set: the layer's (x
-// fp32, and gain * SiLU(z) in bf16 in place of z).
+// x_f32: the layer's input projection (x fp32); otherwise the public one (x bf16).
 int in_proj_impl(const void *hidden, const void *w_in, void *x, void *z, float *g, float *beta, int T, int E,
-                 int Hk, int Hv, int dk, int dv, hipStream_t st, const void *gain = nullptr) {
+                 int Hk, int Hv, int dk, int dv, hipStream_t st, bool x_f32 = false) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     gdn::ProjArgs a{hidden, w_in, T, (int)(C + Z), E, x, (int)C, (int)C, z, (int)Z};
     a.g = g;
     a.beta = beta;
     a.heads = Hv;
-    if (gain) {
-        a.y0_f32 = true;
-        a.gate_gain = gain;
-        a.gate_dv = dv;
-    }
+    a.y0_f32 = x_f32;
     return hip_status(gdn::launch_proj(a, st));
 }
 
@@ -444,13 +439,10 @@ constexpr int kDecodeProjSplits = 16;
 
 // Shapes the layer entry points accept: the projections' k extents (E and Hv dv) are
 // multiples of 64, the gate columns fit the gate workgroups, and dk, dv are 16-multiples.
-// norm_stage: the output projection forms the gated RMSNorm as it stages whole heads 128 k
-// deep (the layer prefill), so Hv dv is a multiple of 128.
-int check_layer_shape(int E, int Hk, int Hv, int dk, int dv, bool norm_stage = false) {
+int check_layer_shape(int E, int Hk, int Hv, int dk, int dv) {
     if (int e = check_heads(Hk, Hv)) return e;
     if (E <= 0) return GDN_ERR_BAD_SHAPE;
     if (E % 64 != 0 || ((size_t)Hv * dv) % 64 != 0 || !gdn::proj_gates_supported(Hv)) return GDN_ERR_UNSUPPORTED;
-    if (norm_stage && !gdn::proj_norm_supported(Hv * dv, dv)) return GDN_ERR_UNSUPPORTED;
     if (E > kProjMaxK || (size_t)Hv * dv > (size_t)kProjMaxK) return GDN_ERR_UNSUPPORTED;
     if (dk % 16 != 0 || dv % 16 != 0) return GDN_ERR_UNSUPPORTED;
     return GDN_OK;
@@ -460,8 +452,8 @@ struct LayerWs {
     size_t x, z, g, beta, o, core, total;
 };
 
-// x fp32 [T][conv_dim], the gate product bf16 [T][Hv dv], g and beta fp32 [T][Hv], the
-// recurrence output fp32 [T][Hv dv], then the prefill's own workspace.
+// x fp32 [T][conv_dim], z bf16 [T][Hv dv] (then the normalised output in its place), g and
+// beta fp32 [T][Hv], the recurrence output fp32 [T][Hv dv], then the prefill's own workspace.
 LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerWs w{};
@@ -541,7 +533,7 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
                       void *workspace, size_t workspace_bytes, void *stream) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
-        if (int e = check_layer_shape(E, Hk, Hv, dk, dv, true)) return e;
+        if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
         if (!gdn::chunked_supported(dk, dv) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!w_in || !conv_w || !gamma || !w_out || (T > 0 && (!hidden || !out))) return GDN_ERR_NULL_POINTER;
         if (!aligned16({hidden, w_in, conv_w, gamma, w_out, cu_seqlens, conv_state_in, conv_state_out,
@@ -571,20 +563,16 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
         float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
         float *o = reinterpret_cast<float *>(ws + L.o);
         hipStream_t st = (hipStream_t)stream;
-        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st, gamma)) return e;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st, true)) return e;
         if (int e = prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
                                  final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_F32, order, ws + L.core,
                                  L.total - L.core, stream, 3, true))
             return e;
-        // output projection with the gated RMSNorm formed in its operand staging: its A rows
-        // are o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z) per head, from o and the gate
-        // product that the input projection wrote in place of z
-        gdn::ProjArgs pa{nullptr, w_out, T, E, (int)Z, out, E, E, nullptr, 0};
-        pa.norm_o = o;
-        pa.norm_zg = z;
-        pa.norm_eps = norm_eps;
-        pa.norm_dv = dv;
-        return hip_status(gdn::launch_proj(pa, st));
+        // the normalised output replaces z (bf16) in place, then feeds the output projection
+        gdn::NormArgs na{o, z, gamma, z, (long)T * Hv, dv, norm_eps, true};
+        if (T > 0)
+            if (int e = hip_status(gdn::launch_gated_rmsnorm(na, st))) return e;
+        return linear_impl(z, w_out, out, T, E, (int)Z, st);
     } catch (...) {
         return GDN_ERR_HIP;
     }
@@ -627,14 +615,15 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
         void *x = ws + L.x, *z = ws + L.z, *y = ws + L.y;
         float *g = reinterpret_cast<float *>(ws + L.g), *beta = reinterpret_cast<float *>(ws + L.beta);
         hipStream_t st = (hipStream_t)stream;
-        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, B, E, Hk, Hv, dk, dv, st, gamma)) return e;
+        if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, B, E, Hk, Hv, dk, dv, st, true)) return e;
         if (B > 0) {
-            // the decode step with the gated RMSNorm fused; z holds the gate product already
+            // the decode step with the gated RMSNorm fused (x and the conv cache fp32, the
+            // conv weights, z, gamma and the normalised output bf16)
             gdn::DecodeArgs a{x, conv_w, conv_state, g, beta, state, nullptr, scale, l2_eps, B, Hk, Hv, dk, dv,
                               false};
             a.order = order;
             a.z = z;
-            a.gamma = nullptr;
+            a.gamma = gamma;
             a.out = y;
             a.norm_eps = norm_eps;
             a.layer_types = true;

@@ -72,9 +72,8 @@ __device__ __forceinline__ void store4(float *p, const float *i) {
 // GATED: the output row of each value head goes through the gated RMSNorm epilogue
 // ("7.6 Qwen3.5: the linear-attention hybrid", sections 7.6.2 and 7.6.3) before it is
 // stored: out = o * rsqrt(mean o^2 + norm_eps) * gamma * SiLU(z), in the gate's element
-// type TG; with gamma NULL, z already holds the product gamma * SiLU(z) (the layer's input
-// projection forms it).  The dv outputs of a head sit in the first dv/4 lanes of wave 0
-// (4 each), so the mean square is one reduction inside that lane group.
+// type TG.  The dv outputs of a head sit in the first dv/4 lanes of wave 0 (4 each), so the
+// mean square is one reduction inside that lane group.
 // T: element type of x and the conv cache; TW: of the conv weights.
 template <typename T, typename TW, typename TG, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     auto load_gate = [&](int h) {
         if (gate_lane) load4(z + ((size_t)b * Hv + h) * DV + 4 * cg, zf);
     };
-    if (gate_lane && gamma) load4(gamma + 4 * cg, gf);
+    if (gate_lane) load4(gamma + 4 * cg, gf);
     load_gate(kh * group);
 
     // q and k channels of this key head
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
                 if (rg == 0) {
                     float r4[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r4[e] = pq[e] * rn * (gamma ? gf[e] * silu(zf[e]) : zf[e]);
+                    for (int e = 0; e < 4; ++e) r4[e] = pq[e] * rn * gf[e] * silu(zf[e]);
                     store4(out + ((size_t)b * Hv + h) * DV + 4 * cg, r4);
                 }
             }

@@ -70,8 +70,7 @@ struct DecodeArgs {
     bool bf16;
     int order = 0;   // as in PrefillArgs
     // gated output (gdn_decode_step_gated): when `out` is set, out = RMSNorm(o) * gamma *
-    // SiLU(z) in the element type is written instead of o (gamma NULL: z holds the product
-    // gamma * SiLU(z))
+    // SiLU(z) in the element type is written instead of o
     const void *z = nullptr, *gamma = nullptr;
     void *out = nullptr;
     float norm_eps = 0.f;
@@ -106,19 +105,8 @@ struct ProjArgs {
     // launcher splits k and sums the slices' planes in a second pass
     float *partial = nullptr;
     size_t partial_cap = 0;
-    // layer epilogue: columns n < n_split go to y0 as fp32 (y0_f32); with gate_gain set,
-    // columns n >= n_split are the output gate z and y1 receives
-    // bf16(gate_gain[(n - n_split) % gate_dv] * SiLU(z)) instead of z
+    // the layer's input projection: columns n < n_split go to y0 as fp32
     bool y0_f32 = false;
-    const void *gate_gain = nullptr;   // bf16 [gate_dv]
-    int gate_dv = 0;
-    // gated RMSNorm on the A operand (set norm_o; `a` is then unused): the A row m is
-    //   norm_o[m][k] * rsqrt(mean over k's head of norm_o^2 + norm_eps) * norm_zg[m][k],
-    // heads of norm_dv consecutive k, rounded to bf16 as it is staged
-    const float *norm_o = nullptr;     // fp32 [M][K]
-    const void *norm_zg = nullptr;     // bf16 [M][K]
-    float norm_eps = 0.f;
-    int norm_dv = 0;
     int tiles_m = 0, tiles_n = 0, ntiles = 0, ksplit = 1;   // set by the launcher
 };
 
@@ -131,8 +119,6 @@ hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st);
 
 hipError_t launch_proj(const ProjArgs &a, hipStream_t st);
 bool proj_gates_supported(int heads);
-// the A-operand norm of ProjArgs needs whole heads in one k stage of the small tile
-bool proj_norm_supported(int K, int dv);
 // compute units of the current device (cached per device; 0 if unknown)
 int device_cus();
 

@@ -6,8 +6,9 @@
 // projection of the layer input gives the pre-conv q|k|v, the output gate z and the
 // two gate pre-activations per value head; the gated RMSNorm's output passes a
 // bias-free output projection.  The input projection's epilogue splits its columns
-// into x (q|k|v, bf16), z (bf16), g = -softplus(a) and beta = sigmoid(b) (fp32): the
-// maps that turn the gate pre-activations into a log-decay and an update gate.
+// into x (q|k|v: bf16, or fp32 inside the layer calls), z (bf16), g = -softplus(a) and
+// beta = sigmoid(b) (fp32): the maps that turn the gate pre-activations into a log-decay
+// and an update gate.
 //
 // Design (dense contraction: MFMA-bound at these shapes, K = 1024 or 2048):
 //  - One 256-thread workgroup (4 waves, 2 x 2) per output tile; a wave owns a
@@ -118,8 +119,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16 *base, in
 }
 
 // Four consecutive outputs y[m][n .. n + 3] (n % 4 == 0, so the four lie on one side of
-// n_split, a multiple of 4): columns before n_split to y0 (bf16; fp32 in the LAYER
-// epilogue), the others to y1 (bf16; LAYER: the gate product gamma * SiLU(z) in place of z).
+// n_split, a multiple of 4): columns before n_split to y0 (bf16; fp32 for the layer's input
+// projection, LAYER), the others to y1 (bf16).
 template <bool LAYER>
 __device__ __forceinline__ void store_out(const ProjArgs &p, int m, int n, f32x4 v) {
     if (n < p.n_split) {
@@ -127,118 +128,48 @@ __device__ __forceinline__ void store_out(const ProjArgs &p, int m, int n, f32x4
         else store_bf16x4(static_cast<bf16 *>(p.y0) + (size_t)m * p.ld0 + n, v);
         return;
     }
-    const int c = n - p.n_split;
-    if (LAYER) {
-        // gate_dv % 4 == 0: the four share a head; their gains are one 8-byte load
-        const bf16x4 gg = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(p.gate_gain) + c % p.gate_dv);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (float)gg[e] * silu(v[e]);
-    }
-    store_bf16x4(static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + c, v);
+    store_bf16x4(static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split), v);
 }
+
+// Kernel modes: plain (bf16 outputs) and the layer's input projection (fp32 x).  (The
+// fp32 x store is its own instance: as a run-time branch beside the plain store it costs the
+// large tile's epilogue 16 spilled registers.)
+enum { kProjPlain = 0, kProjLayerIn = 1 };
 
 // One output tile: rows m0.., columns n0.. of the main (non-gate) columns.
 // k stages [kt0, kt1) of the tile; with p.ksplit > 1 the fp32 sums go to partial sum
 // plane `split` instead of the bf16 outputs.
-// NORM: the A rows are formed while they are staged, as the gated RMSNorm of the layer
-// output ("7.6 Qwen3.5: the linear-attention hybrid", sections 7.6.2 and 7.6.3):
-// A[m][k] = o[m][k] * rsqrt(mean_{k' in head(k)} o[m][k']^2 + eps) * zg[m][k] with
-// zg = gamma * SiLU(z), rounded to bf16.  A stage holds BK / dv whole heads, and the CPR
-// threads that stage one row are one 16-lane DPP row, so a head's sum of squares is a
-// reduction over dv / 8 adjacent lanes.  The A loads of a stage are issued one stage
-// ahead (one register set: o is fp32, three times the bytes of a bf16 row).
-// Kernel modes: plain (bf16 outputs), the layer's input projection (fp32 x, gate product)
-// and the layer's output projection (gated RMSNorm on the A operand).
-enum { kProjPlain = 0, kProjLayerIn = 1, kProjNormA = 2 };
-
 template <int WM, int WN, int BK, int MODE>
 __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, char *smem, int kt0, int kt1,
                                           int split) {
     using S = ProjTile<WM, WN, BK>;
-    constexpr bool NORM = MODE == kProjNormA;
-    static_assert(!NORM || S::CPR == 16, "a staged row is one 16-lane DPP row");
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = tm * S::BM, n0 = tn * S::BN;
     const int K = p.K, M = p.M, N = p.N;
-    const __amdgpu_buffer_rsrc_t ra_src =
-        rows_rsrc(static_cast<const bf16 *>(NORM ? p.norm_zg : p.a), m0, M, K);
+    const __amdgpu_buffer_rsrc_t ra_src = rows_rsrc(static_cast<const bf16 *>(p.a), m0, M, K);
     const __amdgpu_buffer_rsrc_t rw_src = rows_rsrc(static_cast<const bf16 *>(p.w), n0, N, K);
-    // NORM: o rows [m0, M) as fp32 (twice the bytes of the bf16 rows above)
-    __amdgpu_buffer_rsrc_t ro_src = ra_src;
-    if constexpr (NORM) {
-        const long bytes = (long)max(M - m0, 0) * K * 4;
-        ro_src = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(p.norm_o + (size_t)m0 * K), (short)0,
-                                                   (int)min(bytes, (long)0x7fffffff), 0x00020000);
-    }
 
     // staging: thread tid moves chunk tid % CPR of rows tid / CPR + RPP i; two register
     // sets, so a stage's loads are issued two stages before their LDS writes
     const int crow = tid / S::CPR, cc = tid % S::CPR;
     const int voff = crow * K * 2 + cc * 16;
     struct Stg {
-        u32x4 a[NORM ? 1 : S::A_LD], w[S::W_LD];
-    };
-    struct StgN {   // NORM: one stage of A inputs (o fp32, zg bf16)
-        u32x4 o[NORM ? S::A_LD : 1][2], z[NORM ? S::A_LD : 1];
+        u32x4 a[S::A_LD], w[S::W_LD];
     };
     auto gload = [&](int kt, Stg &r) {
         const int vo = voff + kt * S::ROWB;
-        if constexpr (!NORM) {
 #pragma unroll
-            for (int i = 0; i < S::A_LD; ++i)
-                r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
-        }
+        for (int i = 0; i < S::A_LD; ++i) r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
 #pragma unroll
         for (int i = 0; i < S::W_LD; ++i) r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(rw_src, vo, i * S::RPP * K * 2, 0);
     };
-    auto gload_n = [&](int kt, StgN &r) {
-        if constexpr (NORM) {
-            const int vo = voff + kt * S::ROWB;
-            const int vo4 = 2 * voff + kt * S::ROWB * 2;
-#pragma unroll
-            for (int i = 0; i < S::A_LD; ++i) {
-                r.o[i][0] = __builtin_amdgcn_raw_buffer_load_b128(ro_src, vo4, i * S::RPP * K * 4, 0);
-                r.o[i][1] = __builtin_amdgcn_raw_buffer_load_b128(ro_src, vo4 + 16, i * S::RPP * K * 4, 0);
-                r.z[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_src, vo, i * S::RPP * K * 2, 0);
-            }
-        }
-    };
     auto swrite = [&](int buf, const Stg &r) {
         char *sa = smem + buf * S::STAGE, *sw = sa + S::A_BYTES;
-        if constexpr (!NORM) {
 #pragma unroll
-            for (int i = 0; i < S::A_LD; ++i)
-                *reinterpret_cast<u32x4 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = r.a[i];
-        }
+        for (int i = 0; i < S::A_LD; ++i) *reinterpret_cast<u32x4 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = r.a[i];
 #pragma unroll
         for (int i = 0; i < S::W_LD; ++i) *reinterpret_cast<u32x4 *>(sw + swz<S::ROWB>(crow + S::RPP * i, cc)) = r.w[i];
-    };
-    // NORM: the gated RMSNorm of each staged row chunk (8 channels), then bf16 to LDS
-    const int hg = p.norm_dv / 8;              // lanes per head in a staged row
-    const float inv_dv = 1.0f / (float)max(p.norm_dv, 1);
-    auto swrite_n = [&](int buf, const StgN &r) {
-        if constexpr (NORM) {
-            char *sa = smem + buf * S::STAGE;
-#pragma unroll
-            for (int i = 0; i < S::A_LD; ++i) {
-                const f32x4 o0 = __builtin_bit_cast(f32x4, r.o[i][0]), o1 = __builtin_bit_cast(f32x4, r.o[i][1]);
-                const bf16x8 zb = __builtin_bit_cast(bf16x8, r.z[i]);
-                float ss = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ss = fmaf(o0[e], o0[e], fmaf(o1[e], o1[e], ss));
-                ss = hg == 16 ? group_sum<16>(ss) : hg == 8 ? group_sum<8>(ss) : hg == 4 ? group_sum<4>(ss)
-                                                                                         : group_sum<2>(ss);
-                const float rn = rsqrtf(fmaf(ss, inv_dv, p.norm_eps));
-                bf16x8 y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    y[e] = (bf16)(o0[e] * rn * (float)zb[e]);
-                    y[4 + e] = (bf16)(o1[e] * rn * (float)zb[4 + e]);
-                }
-                *reinterpret_cast<bf16x8 *>(sa + swz<S::ROWB>(crow + S::RPP * i, cc)) = y;
-            }
-        }
     };
 
     f32x16 acc[S::NT][S::MT];
@@ -283,13 +214,11 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
     // The order is fixed by scheduling groups: step 0's fragment reads, the global loads,
     // each step's MFMAs with the next step's reads between them, the LDS writes between
     // the last step's MFMAs.  Past the end the loads repeat the last stage (never used).
-    StgN sn;   // NORM: the A inputs of the next stage
     auto stage = [&](int kt, const Stg &wr, Stg &ld) {
         const int buf = (kt - kt0) & 1;
         Frags f0, f1;
         fread(buf, 0, f0);
         gload(min(kt + 2, kt1 - 1), ld);
-        if constexpr (NORM) gload_n(min(kt + 1, kt1 - 1), sn);
 #pragma unroll
         for (int s = 0; s < S::KSTEPS; ++s) {
             Frags &cur = (s & 1) ? f1 : f0;
@@ -298,46 +227,26 @@ __device__ __forceinline__ void proj_tile(const ProjArgs &p, int tm, int tn, cha
             mfmas(cur);
         }
         swrite(buf ^ 1, wr);
-        if constexpr (NORM) {
-            // the W writes and the A rows (norm arithmetic, then writes) follow the MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, S::W_LD + 3 * S::A_LD, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);    // DS reads of step 0
+        __builtin_amdgcn_sched_group_barrier(0x020, NW, 0);    // VMEM reads of stage kt + 2
 #pragma unroll
-            for (int s = 0; s + 1 < S::KSTEPS; ++s) {
+        for (int s = 0; s + 1 < S::KSTEPS; ++s) {
 #pragma unroll
-                for (int g = 0; g < FR; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-                }
+            for (int g = 0; g < FR; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read (step s + 1)
+                __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // MFMA (step s)
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-            swrite_n(buf ^ 1, sn);
-        } else {
-            __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);    // DS reads of step 0
-            __builtin_amdgcn_sched_group_barrier(0x020, NW, 0);    // VMEM reads of stage kt + 2
+        }
 #pragma unroll
-            for (int s = 0; s + 1 < S::KSTEPS; ++s) {
-#pragma unroll
-                for (int g = 0; g < FR; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read (step s + 1)
-                    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0); // MFMA (step s)
-                }
-            }
-#pragma unroll
-            for (int g = 0; g < (NW > MF ? MF : NW); ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x200, W_EACH, 0);  // DS write (stage kt + 1)
-                __builtin_amdgcn_sched_group_barrier(0x008, M_EACH, 0);  // MFMA (last step)
-            }
+        for (int g = 0; g < (NW > MF ? MF : NW); ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x200, W_EACH, 0);  // DS write (stage kt + 1)
+            __builtin_amdgcn_sched_group_barrier(0x008, M_EACH, 0);  // MFMA (last step)
         }
         __syncthreads();
     };
     Stg s0, s1;
     gload(kt0, s0);
     gload(min(kt0 + 1, kt1 - 1), s1);
-    if constexpr (NORM) {
-        gload_n(kt0, sn);
-        swrite_n(0, sn);
-    }
     swrite(0, s0);
     __syncthreads();
     int kt = kt0;
@@ -479,7 +388,7 @@ static hipError_t launch_proj_t(ProjArgs p, hipStream_t st) {
     // whose planes fit the buffer.  The slices' fp32 sums meet in a second pass, in a fixed
     // order.
     p.ksplit = 1;
-    if (p.partial && p.heads == 0 && !p.gate_gain) {
+    if (p.partial && p.heads == 0) {
         const int KT = p.K / BK, cus = device_cus() > 0 ? device_cus() : 256;
         const int want = cus / p.ntiles;
         for (int d = std::min(want, KT); d >= 4; --d)
@@ -502,10 +411,6 @@ static hipError_t launch_proj_t(ProjArgs p, hipStream_t st) {
 
 bool proj_gates_supported(int heads) { return 2 * heads <= 16 * kGateMaxTiles; }
 
-bool proj_norm_supported(int K, int dv) {
-    return (dv == 16 || dv == 32 || dv == 64 || dv == 128) && K % 128 == 0;
-}
-
 template <int MODE>
 static hipError_t launch_proj_m(const ProjArgs &a, hipStream_t st) {
     // large tiles when they alone fill the compute units
@@ -518,8 +423,6 @@ static hipError_t launch_proj_m(const ProjArgs &a, hipStream_t st) {
 
 hipError_t launch_proj(const ProjArgs &a, hipStream_t st) {
     if (a.M <= 0) return hipSuccess;
-    // the normalised A operand: small tiles, 128-deep k stages (whole heads per stage)
-    if (a.norm_o) return launch_proj_t<64, 64, 128, kProjNormA>(a, st);
     return a.y0_f32 ? launch_proj_m<kProjLayerIn>(a, st) : launch_proj_m<kProjPlain>(a, st);
 }
 

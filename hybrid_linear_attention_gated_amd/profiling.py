@@ -17,6 +17,13 @@
       stream) and the first SKIP steps (warm-up) are dropped.  Shows how
       kernels on the library's two streams overlap.
 
+  python -m hybrid_linear_attention_gated_amd.profiling counters DIR [DIR ...]
+      per-kernel mean per dispatch of every counter of `rocprofv3 --pmc` runs (CSV).
+  python -m hybrid_linear_attention_gated_amd.profiling bytes DIR [DIR ...]
+      HBM-side read and write bytes per dispatch from the L2's memory-fabric request
+      counters (TCC_EA0_RDREQ_32B/_64B/_128B_sum, TCC_EA0_WRREQ_sum and _64B_sum), and the
+      `<kernel>.traffic_bytes` lines bench.py reads.
+
 Only text is produced; nothing here touches the GPU.
 """
 from __future__ import annotations
@@ -43,7 +50,7 @@ KERNELS = [
     ("gated_rmsnorm_kernel", "gated_rmsnorm"),
 ]
 # the projection kernel's two tile shapes (named by short_name from its template arguments)
-PROJ_NAMES = ("proj_256", "proj_128")
+PROJ_NAMES = ("proj_256", "proj_128", "proj_256_layer", "proj_128_layer")
 # bench.py --copy-calibration streams a buffer through torch.neg (one elementwise
 # kernel that reads and writes COPY_BYTES); host-to-device uploads use blit
 # kernels of other names and are not counted as the calibration copy.
@@ -52,11 +59,15 @@ COPY_NAMES = ("elementwise_kernel",)
 
 def short_name(symbol: str) -> str:
     if "chunk_local_kernel" in symbol and ("ELb1E" in symbol or ", true," in symbol):
-        return "chunk_local_fused"   # mangled or demangled template argument FUSED = true
+        # FUSED = true; fp32 x (the layer's prefill) or 16-bit x
+        return "chunk_local_fused_x32" if ("ELb1Ef" in symbol or ", true, float" in symbol) else "chunk_local_fused"
     if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):
         return "decode_gated"        # template argument GATED = true
-    if "proj_kernel" in symbol:      # projection GEMM, named by its output tile
-        return "proj_256" if ("ILi128ELi128E" in symbol or "proj_kernel<128, 128" in symbol) else "proj_128"
+    if "proj_kernel" in symbol:      # projection GEMM, named by its output tile and mode
+        base = "proj_256" if ("ILi128ELi128E" in symbol or "proj_kernel<128, 128" in symbol) else "proj_128"
+        if "ELi1EE" in symbol or symbol.rstrip(")").split("(")[0].endswith(", 1>"):
+            return base + "_layer"   # the layer's input projection (fp32 x)
+        return base
     for frag, short in KERNELS:
         if frag in symbol:
             return short
@@ -109,6 +120,43 @@ def counter_means(directory: str, counter: str) -> dict:
 
 # The calibration copy moves this many bytes each way (bench.py --copy-calibration).
 COPY_BYTES = 512 << 20
+
+# Counters whose per-dispatch value is the maximum over their dimensions (a clock that every
+# XCD counts) rather than the sum (events counted per instance).
+_MAX_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT")
+
+
+def counter_table(*directories: str) -> dict:
+    """short name -> {counter: mean value per dispatch} over the `counter_collection.csv`
+    files under the directories (one rocprofv3 --pmc pass each).  Rows of one dispatch and
+    counter (one per hardware instance, when the file lists them separately) are summed,
+    or for a clock counter the largest is taken."""
+    per = defaultdict(lambda: defaultdict(dict))   # kernel -> counter -> dispatch -> value
+    for d in directories:
+        for r in _csv_rows(d, "counter_collection.csv"):
+            name, ctr = short_name(r["Kernel_Name"]), r["Counter_Name"]
+            disp = (d, r.get("Dispatch_Id") or r.get("Correlation_Id") or len(per[name][ctr]))
+            v = float(r["Counter_Value"])
+            old = per[name][ctr].get(disp)
+            if old is None:
+                per[name][ctr][disp] = v
+            else:
+                per[name][ctr][disp] = max(old, v) if ctr in _MAX_COUNTERS else old + v
+    return {k: {c: sum(vals.values()) / len(vals) for c, vals in ctrs.items()} for k, ctrs in per.items()}
+
+
+def request_bytes(row: dict) -> tuple:
+    """HBM-side bytes per dispatch from the L2's memory-fabric request counters: reads of
+    32, 64 and 128 bytes (TCC_EA0_RDREQ_32B / _64B / _128B), writes of 32 or 64 bytes
+    (TCC_EA0_WRREQ, of which TCC_EA0_WRREQ_64B are 64 bytes).  Returns (read, write) or
+    None for a side whose counters are missing."""
+    rd = wr = None
+    if all(f"TCC_EA0_RDREQ_{w}B_sum" in row for w in (32, 64, 128)):
+        rd = 32 * row["TCC_EA0_RDREQ_32B_sum"] + 64 * row["TCC_EA0_RDREQ_64B_sum"] + 128 * row["TCC_EA0_RDREQ_128B_sum"]
+    if "TCC_EA0_WRREQ_sum" in row and "TCC_EA0_WRREQ_64B_sum" in row:
+        w64 = row["TCC_EA0_WRREQ_64B_sum"]
+        wr = 32 * (row["TCC_EA0_WRREQ_sum"] - w64) + 64 * w64
+    return rd, wr
 
 
 def traffic(fetch_dir: str, write_dir: str) -> dict:
@@ -194,6 +242,28 @@ def main(argv):
         for k, a, b in tl["kernels"]:
             print(f"{k:20s} {a:8.1f} {b:8.1f} {b - a:8.1f}")
         print(f"{'step span':20s} {'':8s} {tl['span']:8.1f}")
+        return 0
+    if len(argv) >= 2 and argv[0] == "counters":
+        tab = counter_table(*argv[1:])
+        ctrs = sorted({c for row in tab.values() for c in row})
+        print("kernel," + ",".join(ctrs))
+        for k in sorted(tab):
+            print(k + "," + ",".join(f"{tab[k][c]:.6g}" if c in tab[k] else "" for c in ctrs))
+        return 0
+    if len(argv) >= 2 and argv[0] == "bytes":
+        tab = counter_table(*argv[1:])
+        print(f"{'kernel':20s} {'read_MB':>10s} {'write_MB':>10s}")
+        for k in sorted(tab):
+            rd, wr = request_bytes(tab[k])
+            if rd is None and wr is None:
+                continue
+            print(f"{k:20s} {'' if rd is None else f'{rd / 1e6:10.2f}':>10s} "
+                  f"{'' if wr is None else f'{wr / 1e6:10.2f}':>10s}")
+        for k in sorted(tab):
+            rd, wr = request_bytes(tab[k])
+            if rd is not None and wr is not None and k in {s for _, s in KERNELS} | set(PROJ_NAMES):
+                print(f"{k}.traffic_bytes = {rd + wr:.0f}")
+        print(f"source_sha256 = {source_sha256()}")
         return 0
     print(__doc__, file=sys.stderr)
     return 2

@@ -349,9 +349,9 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state,
  * them: W[out][in], y = x W^T.
  * Inside the layer calls the pre-conv q|k|v that the recurrence reads stays fp32, and so
  * do the layer's conv caches (the recurrent state amplifies a one-ulp bf16 change of its
- * inputs beyond the 2e-2 accuracy the layer is held to); the gate and the normalised
- * output that enters the output projection are bf16 (one bf16 rounding of a
- * multiplicative gate costs at most 2^-9 of the value).
+ * inputs beyond the 2e-2 accuracy the layer is held to); z and the normalised output
+ * that enters the output projection are bf16 (one bf16 rounding of a multiplicative gate
+ * costs at most 2^-9 of the value).
  *
  * gdn_linear -- y = a w^T.
  *   a [M][K] bf16, w [N][K] bf16, y [M][N] bf16 (fp32 sums rounded to nearest even).
@@ -375,11 +375,9 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
 
 /*
  * gdn_layer_prefill -- the whole layer over packed sequences in one call: the input
- * projection (as gdn_in_proj, but x leaves it in fp32 and the gate as the bf16 product
- * gamma * SiLU(z)), the prefill of gdn_prefill on the fp32 x, and the output projection
- * with the gated RMSNorm formed in its operand staging: its A rows are
- * o * rsqrt(mean over the head's dv outputs of o^2 + norm_eps) * gamma * SiLU(z), rounded
- * to bf16 as they enter LDS, so no normalised copy of the output is written.
+ * projection (as gdn_in_proj, but x leaves it in fp32), gdn_prefill on the fp32 x,
+ * gdn_gated_rmsnorm over each (token, value head) row (bf16 z, gamma and output), and
+ * gdn_linear with w_out.
  *   hidden [T][E], w_in as in gdn_in_proj, conv_w [conv_dim][4], gamma [dv] (the gain
  *   as applied), w_out [E][Hv*dv]: bf16.
  *   cu_seqlens, N, conv_state_in / conv_state_out [N][3][conv_dim] fp32,
@@ -387,11 +385,10 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
  *   gdn_prefill (the same exact aliases allowed).
  *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
  *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
- *              (x, the gate product, g, beta, o and the prefill's workspace); must not
- *              overlap any other argument.
- * dk = dv in {64, 128}; E and Hv as in gdn_in_proj, and Hv*dv a multiple of 128.  out must
- * not overlap an input.  The three steps run in order on `stream` (the prefill as in
- * gdn_prefill).
+ *              (x, z, g, beta, o and the prefill's workspace); must not overlap any
+ *              other argument.
+ * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
+ * The four steps run in order on `stream` (the prefill as in gdn_prefill).
  */
 size_t gdn_layer_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv);
 int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
@@ -404,14 +401,13 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
 
 /*
  * gdn_layer_decode -- one token for each of B sequences through the layer: the input
- * projection of gdn_layer_prefill (x fp32, the gate product bf16), the decode step with the
- * gated RMSNorm fused (gdn_decode_step_gated, caches in place), gdn_linear with w_out.
+ * projection of gdn_layer_prefill (x fp32), the decode step with the gated RMSNorm fused
+ * (gdn_decode_step_gated, caches in place), gdn_linear with w_out.
  *   hidden [B][E] bf16; weights as in gdn_layer_prefill; conv_state [B][3][conv_dim]
  *   fp32 and state [B][Hv][dk][dv] fp32 in/out; out [B][E] bf16.
- *   workspace  at least gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) bytes (x, the
- *              gate product, g, beta, the normalised output and fp32 partial sums of the
- *              output projection, whose k extent is split over more compute units when B
- *              is small).
+ *   workspace  at least gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) bytes (x, z, g,
+ *              beta, the normalised output and fp32 partial sums of the output projection,
+ *              whose k extent is split over more compute units when B is small).
  * dk, dv in {16, 32, 64, 128}; E and Hv as in gdn_in_proj.
  */
 size_t gdn_layer_decode_workspace_size(int B, int E, int Hk, int Hv, int dk, int dv);

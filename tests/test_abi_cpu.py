@@ -266,7 +266,6 @@ def test_layer_prefill_validation(L):
                                    a["order"], a["ws"], a["wsb"], None)
     assert call(N=2) == 2                                        # two sequences need cu_seqlens
     assert call(E=100) == 3
-    assert call(Hk=1, Hv=1) == 3                                 # Hv dv = 64: not whole 128-deep stages
     assert call(dk=32, dv=32) == 3
     assert call(order=2) == 3
     assert call(gm=None) == 1

@@ -37,6 +37,11 @@ def test_short_names():
     assert profiling.short_name("void gdn::proj_kernel<128, 128, 64>(gdn::ProjArgs)") == "proj_256"
     assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64EEEvNS_8ProjArgsE") == "proj_256"
     assert profiling.short_name("void gdn::proj_kernel<64, 64, 128>(gdn::ProjArgs)") == "proj_128"
+    assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64ELi0EEEvNS_8ProjArgsE") == "proj_256"
+    assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64ELi1EEEvNS_8ProjArgsE") == "proj_256_layer"
+    assert profiling.short_name("void gdn::proj_kernel<64, 64, 128, 1>(gdn::ProjArgs)") == "proj_128_layer"
+    assert profiling.short_name("_ZN3gdn18chunk_local_kernelILi128ELb1EfDF16bEEvPKf") == "chunk_local_fused_x32"
+    assert profiling.short_name("_ZN3gdn18chunk_local_kernelILi128ELb1EDF16bS1_EEvPKf") == "chunk_local_fused"
 
 
 def test_kernel_stats(tmp_path):
@@ -89,3 +94,24 @@ def test_traffic_scaled_by_copy(tmp_path):
     assert k["fetch_bytes"] == pytest.approx(200.0 * 1024 * 2.0)
     assert k["write_bytes"] == pytest.approx(200.0 * 1024 * 0.5)
     assert "copy" not in t["kernels"]
+
+
+def test_counter_table_and_request_bytes(tmp_path):
+    """Rows of one dispatch are summed (clock counters: the largest), dispatches averaged;
+    request counts become bytes by their widths."""
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    rows = []
+    for disp, scale in ((1, 1), (2, 3)):
+        for inst in range(2):   # two hardware instances listed separately
+            rows += [{"Dispatch_Id": disp, "Kernel_Name": STATE, "Counter_Name": c, "Counter_Value": v * scale}
+                     for c, v in (("TCC_EA0_RDREQ_32B_sum", 1), ("TCC_EA0_RDREQ_64B_sum", 2),
+                                  ("TCC_EA0_RDREQ_128B_sum", 3), ("TCC_EA0_WRREQ_sum", 10),
+                                  ("TCC_EA0_WRREQ_64B_sum", 4), ("GRBM_GUI_ACTIVE", 100 + inst))]
+    _write(str(tmp_path / "c" / "run_counter_collection.csv"), fields, rows)
+    tab = profiling.counter_table(str(tmp_path / "c"))
+    row = tab["state_pass"]
+    assert row["TCC_EA0_RDREQ_32B_sum"] == 4.0          # (2 + 6) / 2 dispatches
+    assert row["GRBM_GUI_ACTIVE"] == (101 + 303) / 2    # the larger instance of each dispatch
+    rd, wr = profiling.request_bytes(row)
+    assert rd == 32 * 4 + 64 * 8 + 128 * 12
+    assert wr == 32 * (40 - 16) + 64 * 16
