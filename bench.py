@@ -50,6 +50,7 @@ import time
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector, TFLOP/s
 
 METRIC = "GDN prefill tokens/s + decode state GB/s (fraction of MI355X roofline)"
 LAYER_HIDDEN = 1024            # hidden size of the 0.8B model's layers
@@ -76,10 +77,21 @@ def algorithmic_counts(T, Hk, Hv, d, C, N, B):
     return prep_bytes, local_flops, state_flops, dec_bytes
 
 
-def cpu_baseline(wl, min_seconds=10.0):
-    """The fp64 oracle on the same prefill batch, on this host's cores: whole
-    passes (prep, then the token recurrence) repeated until at least
-    `min_seconds` have run (three passes at least); the median pass is reported."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, dw, dec_bytes, min_seconds=10.0):
+    """The fp64 oracle on the same batches, on this host's cores: whole layer_4k prefill
+    passes (prep, then the token recurrence) repeated until at least `min_seconds` have run
+    (three passes at least), then decode256 steps for a few seconds; medians are reported."""
     import numpy as np
     import oracle
     x = wl.x.float().numpy()
@@ -96,12 +108,110 @@ def cpu_baseline(wl, min_seconds=10.0):
         oracle.recurrence(q, k, v, g, b, cu)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
+    dargs = [t.float().numpy() for t in (dw.x, dw.conv_w, dw.conv_state, dw.g, dw.beta, dw.state)]
+    dtimes = []
+    start = time.perf_counter()
+    while len(dtimes) < 3 or time.perf_counter() - start < 3.0:
+        t0 = time.perf_counter()
+        oracle.decode(*dargs, dw.Hk, dw.Hv, dw.dk, dw.dv)
+        dtimes.append(time.perf_counter() - t0)
+    td = float(np.median(dtimes))
     threads = oracle.threads(1 << 30)
     return {"value": wl.T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
             "sample": f"whole layer_4k prefill (conv+SiLU+L2 over T={wl.T}, then the fp64 token recurrence over all "
                       f"{wl.Hv} heads) repeated {len(times)} times ({sum(times):.1f} s); median pass {t:.2f} s. "
                       f"OpenMP: {threads} threads over tokens in prep, min({threads}, {wl.Hv}) over heads in the "
-                      f"recurrence"}
+                      f"recurrence",
+            "decode": {"steps_per_s": 1.0 / td, "tokens_per_s": dw.N / td, "gb_per_s": dec_bytes / td / 1e9,
+                       "sample": f"decode256 step (B={dw.N}, {dw.Hv} heads, fp64 state) repeated {len(dtimes)} "
+                                 f"times; median {td * 1e3:.1f} ms; OpenMP over rows; GB/s counts the GPU's "
+                                 f"algorithmic bytes per step"}}
+
+
+def prefill_flops_per_token_head(d, C=64):
+    """The chunk method's algorithmic flops per token and value head at head dim d:
+    (3C - 1) d + 2C d + C^2/3 (chunk-local products and solve) + 6 d^2 (state contractions)."""
+    return (3 * C - 1) * d + 2 * C * d + C * C // 3 + 6 * d * d
+
+
+def ratio(gpu, ref):
+    import numpy as np
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(gpu - ref)) / np.sqrt(np.mean(ref * ref)))
+
+
+def config_records(torch, gdn, inputs, dev, reps=10):
+    """One record per prefill configuration not in the metric (tiny_f32, varlen8, long_64k):
+    the prefill call timed with HIP events (inputs resident, `reps` calls after 2 warm-ups,
+    mean), tokens/s, algorithmic flop rate and its fraction of the peak the arithmetic
+    runs on, and parity against the fp64 oracle (max|err|/RMS of o and of the final state)."""
+    import oracle
+    recs = {}
+
+    def time_calls(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # tiny_f32: the core alone in fp32, chunked WY / UT form in fp32 and the token recurrence
+    wl = inputs.tiny_f32()
+    args = [t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+    cu = wl.cu_seqlens.to(dev)
+    o_ref, f_ref = oracle.recurrence(*(t.numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)), wl.cu_seqlens.numpy())
+    rec = {"workload": "tiny_f32 (T=64, H=2, dk=dv=16, fp32, core only)", "tolerance": 1e-4}
+    flops = wl.T * wl.Hv * prefill_flops_per_token_head(wl.dk)
+    for math in ("f32_chunked", "f32"):
+        fn = lambda: gdn.chunk_prefill(*args, cu_seqlens=cu, math=math)
+        ms = time_calls(fn, reps)
+        o, f = fn()
+        torch.cuda.synchronize()
+        rec[math] = {"ms": ms, "tokens_per_s": wl.T / (ms / 1e3), "achieved_tflops": flops / ms / 1e9,
+                     "frac_fp32_vector_peak": flops / ms / 1e9 / PEAK_F32_TFLOPS,
+                     "parity": {"o": ratio(o.cpu(), o_ref), "final_state": ratio(f.cpu(), f_ref)}}
+    recs["tiny_f32"] = rec
+
+    # varlen8 and long_64k: gdn_prefill (fused prep) with bf16 x, fp32 state
+    for name, n_rep in (("varlen8", reps), ("long_64k", max(2, reps // 2))):
+        wl = inputs.get(name)
+        x, w, g, b = (t.to(dev) for t in (wl.x, wl.conv_w, wl.g, wl.beta))
+        cu = wl.cu_seqlens.to(dev)
+        s0 = None if wl.state is None else wl.state.to(dev)
+        csi = None if wl.conv_state is None else wl.conv_state.to(dev)
+        ws = torch.empty(gdn.workspace_size(wl.T, wl.N, wl.Hk, wl.Hv, wl.dk, wl.dv, "mfma"), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty((wl.T, wl.Hv, wl.dv), dtype=torch.float32, device=dev)
+        fin = torch.empty((wl.N, wl.Hv, wl.dk, wl.dv), dtype=torch.float32, device=dev)
+        fn = lambda: gdn.prefill(x, w, g, b, wl.Hk, wl.Hv, wl.dk, wl.dv, cu_seqlens=cu, conv_state_in=csi,
+                                 initial_state=s0, final_state=fin, o=o, workspace=ws)
+        ms = time_calls(fn, n_rep)
+        fn()
+        torch.cuda.synchronize()
+        o_gpu, f_gpu = o.cpu(), fin.cpu()
+        del x, w, g, b, ws, o, fin
+        torch.cuda.empty_cache()
+        q_r, k_r, v_r, _ = oracle.prep(wl.x.float().numpy(), wl.conv_w.float().numpy(), wl.cu_seqlens.numpy(),
+                                       wl.Hk, wl.Hv, wl.dk, wl.dv,
+                                       cs_in=None if wl.conv_state is None else wl.conv_state.float().numpy())
+        o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, wl.g.numpy(), wl.beta.numpy(), wl.cu_seqlens.numpy(),
+                                         s0=None if wl.state is None else wl.state.numpy())
+        del q_r, k_r, v_r
+        flops = wl.T * wl.Hv * prefill_flops_per_token_head(wl.dk)
+        recs[name] = {"workload": f"{name} (T={wl.T}, N={wl.N}, Hk={wl.Hk}, Hv={wl.Hv}, dk=dv={wl.dk}, bf16 x, "
+                                  f"fp32 state)", "entry_point": "gdn_prefill", "ms": ms,
+                      "tokens_per_s": wl.T / (ms / 1e3), "achieved_tflops": flops / ms / 1e9,
+                      "frac_mfma": flops / ms / 1e9 / PEAK_MFMA_TFLOPS, "tolerance": 2e-2,
+                      "parity": {"o": ratio(o_gpu, o_ref), "final_state": ratio(f_gpu, f_ref)}}
+        del o_ref, f_ref, o_gpu, f_gpu
+    return recs
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_layer_4k.txt")
@@ -169,6 +279,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=3, help="input copies rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration records (tiny_f32, varlen8, long_64k) and the parity checks")
     ap.add_argument("--split-only", action="store_true",
                     help="time only the split-phase region (one launch per kernel per step), for profiler runs")
     ap.add_argument("--metric-only", action="store_true",
@@ -439,8 +551,29 @@ def main():
             kern[n]["frac_of_library_gemm"] = kern[n]["achieved"] / cal["library_gemm_tflops"]
     if args.copy_calibration:
         copy_calibration(torch, dev)
+    if not (args.split_only or args.no_configs):
+        # parity of the metric's own configurations (layer_4k prefill, decode256 step) on the
+        # outputs of the last timed calls, then the other configurations' records
+        import oracle
+        gdn.prefill(xs[0], cw, gs[0], bs[0], Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, final_state=fin,
+                    o=o, workspace=ws)
+        torch.cuda.synchronize()
+        o_last, f_last = o.cpu(), fin.cpu()
+        q_r, k_r, v_r, _ = oracle.prep(wl.x.float().numpy(), wl.conv_w.float().numpy(), wl.cu_seqlens.numpy(),
+                                       Hk, Hv, d, d)
+        o_ref, f_ref = oracle.recurrence(q_r, k_r, v_r, wl.g.numpy(), wl.beta.numpy(), wl.cu_seqlens.numpy())
+        out["prefill"]["parity"] = {"o": ratio(o_last, o_ref), "final_state": ratio(f_last, f_ref), "tolerance": 2e-2}
+        ds, dc = dw.state.to(dev), dw.conv_state.to(dev)
+        do_ = gdn.decode_step(dx, dcw, dc, dg, db, ds, Hk, Hv, d, d)
+        torch.cuda.synchronize()
+        do_ref, ds_ref, _ = oracle.decode(*(t.float().numpy() for t in (dw.x, dw.conv_w, dw.conv_state, dw.g,
+                                                                          dw.beta, dw.state)), Hk, Hv, d, d)
+        out["decode"]["parity"] = {"o": ratio(do_.cpu(), do_ref), "state": ratio(ds.cpu(), ds_ref),
+                                   "tolerance": 1e-4}
+        del ds, dc, q_r, k_r, v_r, o_ref, f_ref
+        out["configs"] = config_records(torch, gdn, inputs, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"] = cpu_baseline(wl, dw, dec_b)
     print(json.dumps(out))
 
 

@@ -22,14 +22,14 @@ import os
 import torch
 
 __all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_rmsnorm", "decode_step_gated", "chunk_prefill_local", "chunk_prefill_state", "decode_step", "workspace_size", "lib", "GdnError",
-           "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
+           "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_MATH_F32_CHUNKED", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
            "LIB_PATH", "abi_version", "mfma_supported", "linear", "in_proj", "layer_prefill", "layer_decode",
            "layer_prefill_workspace_size", "layer_decode_workspace_size", "prefill_workspace_status",
            "GDN_OK", "GDN_ERR_TIMEOUT", "GDN_ERR_NONFINITE", "set_wait_bound"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
-GDN_MATH_F32, GDN_MATH_MFMA = 0, 1
+GDN_MATH_F32, GDN_MATH_MFMA, GDN_MATH_F32_CHUNKED = 0, 1, 2
 GDN_ORDER_DECAY_FIRST, GDN_ORDER_RETRIEVE_FIRST = 0, 1
 GDN_OK, GDN_ERR_TIMEOUT, GDN_ERR_NONFINITE = 0, 8, 9
 _SPIN_TAG = 0x7370696E   # high half of the workspace header word that bounds the state pass's waits
@@ -255,7 +255,7 @@ def mfma_supported(dk, dv) -> bool:
 def _math(math, dk, dv) -> int:
     if math == "auto":
         return GDN_MATH_MFMA if mfma_supported(dk, dv) else GDN_MATH_F32
-    return {"f32": GDN_MATH_F32, "mfma": GDN_MATH_MFMA}[math]
+    return {"f32": GDN_MATH_F32, "mfma": GDN_MATH_MFMA, "f32_chunked": GDN_MATH_F32_CHUNKED}[math]
 
 
 def workspace_size(T, N, Hk, Hv, dk, dv, math="auto") -> int:
@@ -267,8 +267,9 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, final_s
     """Gated delta rule over packed sequences.
 
     q, k [T, Hk, dk]; v [T, Hv, dv]; g, beta [T, Hv]; states [N, Hv, dk, dv]; all fp32.
-    math: "mfma" (chunked MFMA path), "f32" (fp32 token recurrence) or "auto"
-    (mfma where the head dims allow it).  order: 0 decays the state before the
+    math: "mfma" (chunked MFMA path), "f32" (fp32 token recurrence), "f32_chunked" (the
+    chunked form in fp32, head dims 16..64) or "auto" (mfma where the head dims allow it,
+    else f32).  order: 0 decays the state before the
     retrieval, 1 retrieves from the undecayed state (GDN_ORDER_*).
     Returns (o [T, Hv, dv] fp32, final_state or None).  final_state may be initial_state
     (updated in place).

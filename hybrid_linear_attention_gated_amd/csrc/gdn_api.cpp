@@ -164,11 +164,12 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
         if (T > 0 && need_outputs && !o) return GDN_ERR_NULL_POINTER;
         if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, o, workspace})) return GDN_ERR_ALIGN;
         if (int e = check_heads(Hk, Hv)) return e;
-        if (math != GDN_MATH_F32 && math != GDN_MATH_MFMA) return GDN_ERR_UNSUPPORTED;
+        if (math != GDN_MATH_F32 && math != GDN_MATH_MFMA && math != GDN_MATH_F32_CHUNKED) return GDN_ERR_UNSUPPORTED;
         if (!valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (phases != 3 && math != GDN_MATH_MFMA) return GDN_ERR_UNSUPPORTED;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128)) return GDN_ERR_UNSUPPORTED;
         if (math == GDN_MATH_MFMA && !gdn::chunked_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
+        if (math == GDN_MATH_F32_CHUNKED && !gdn::chunked_f32_supported(dk, dv)) return GDN_ERR_UNSUPPORTED;
         if (!std::isfinite(scale)) return GDN_ERR_BAD_SHAPE;
         const bool chunked = math == GDN_MATH_MFMA;
         const size_t need = chunked ? gdn::chunked_workspace_bytes(T, N, Hv, dk, dv) : 0;
@@ -193,8 +194,9 @@ int chunk_prefill_impl(const float *q, const float *k, const float *v, const flo
             if (int e = check_seqlens_on_host(cu_seqlens, N, T, st)) return e;
             if (chunked && (phases & 1)) (void)take_status(workspace, st);   // start from a clear status word
         }
-        if (int e = hip_status(chunked ? gdn::launch_prefill_chunked(a, st, phases)
-                                       : gdn::launch_prefill_recurrent(a, st)))
+        if (int e = hip_status(chunked                          ? gdn::launch_prefill_chunked(a, st, phases)
+                               : math == GDN_MATH_F32_CHUNKED ? gdn::launch_prefill_chunked_f32(a, st)
+                                                              : gdn::launch_prefill_recurrent(a, st)))
             return e;
         return dbg && chunked && (phases & 2) ? take_status(workspace, st) : GDN_OK;
     } catch (...) {

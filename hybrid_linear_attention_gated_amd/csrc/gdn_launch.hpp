@@ -125,6 +125,10 @@ int device_cus();
 // token-recurrent fp32 path (GDN_F32 and the small head dims)
 hipError_t launch_prefill_recurrent(const PrefillArgs &a, hipStream_t st);
 
+// chunked (WY / UT) form in fp32 for dk, dv in {16, 32, 64} (GDN_MATH_F32_CHUNKED)
+bool chunked_f32_supported(int dk, int dv);
+hipError_t launch_prefill_chunked_f32(const PrefillArgs &a, hipStream_t st);
+
 // chunked MFMA path (dk = dv in {64, 128})
 bool chunked_supported(int dk, int dv);
 size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv);

@@ -85,11 +85,14 @@ typedef enum {
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 /* Arithmetic of gdn_chunk_prefill.
- *  GDN_MATH_F32 : token-by-token recurrence in fp32 (any dk, dv in {16, 32, 64, 128}).
- *  GDN_MATH_MFMA: chunked WY / UT form (chunk 64) on 16-bit MFMA with split
- *                 operands where the accuracy needs them (dk = dv in {64, 128});
- *                 about 1e-3 RMS-relative on the 0.8B layer shape. */
-typedef enum { GDN_MATH_F32 = 0, GDN_MATH_MFMA = 1 } gdn_math;
+ *  GDN_MATH_F32        : token-by-token recurrence in fp32 (any dk, dv in {16, 32, 64, 128}).
+ *  GDN_MATH_MFMA       : chunked WY / UT form (chunk 64) on 16-bit MFMA with split
+ *                        operands where the accuracy needs them (dk = dv in {64, 128});
+ *                        about 1e-3 RMS-relative on the 0.8B layer shape.
+ *  GDN_MATH_F32_CHUNKED: the same chunked WY / UT form with every product an fp32 sum
+ *                        (dk, dv in {16, 32, 64}; one workgroup per (sequence, value head)
+ *                        carries the state through the chunks); no workspace. */
+typedef enum { GDN_MATH_F32 = 0, GDN_MATH_MFMA = 1, GDN_MATH_F32_CHUNKED = 2 } gdn_math;
 
 /* Order of decay and retrieval in one step of the recurrence (argument `order`).
  *  GDN_ORDER_DECAY_FIRST   : S <- a S; m = S^T k; delta = b (v - m); S += k delta^T;
@@ -156,7 +159,8 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *                  the chunk-local phase, one state per (sequence, value head) and one
  *                  ready flag per (chunk, value head).  It needs no initialisation:
  *                  each call's ready flags carry a value of that call's own.
- *   math           gdn_math; GDN_MATH_MFMA with other head dims -> GDN_ERR_UNSUPPORTED
+ *   math           gdn_math; GDN_MATH_MFMA or GDN_MATH_F32_CHUNKED with other head dims
+ *                  -> GDN_ERR_UNSUPPORTED
  *   order          gdn_order (decay before or after the retrieval)
  *
  * With GDN_MATH_MFMA the two phases below run in one of three schedules, all

@@ -103,6 +103,9 @@ def test_prefill_validation(L):
     assert call(scale=float("inf")) == 2
     assert call(order=2) == 3
     assert call(order=-1, dt=0) == 3                            # also on the fp32 path
+    assert call(dt=2) == 3                                      # chunked fp32 form: head dims up to 64
+    assert call(dt=2, dk=64, dv=64, o=None) == 1
+    assert L.gdn_chunk_prefill_workspace_size(T, 1, H, H, 64, 64, 2) == 0     # no workspace
 
 
 def test_fused_prefill_validation(L):

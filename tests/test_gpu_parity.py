@@ -117,7 +117,7 @@ def test_prep_varlen(gdn, dtype, d):
 # ------------------------------------------------------------------ core (chunk prefill)
 
 def _core_case(gdn, wl, math, heads=None, inplace=False):
-    tol = TOL_F32 if math == "f32" else TOL_BF16
+    tol = TOL_F32 if math in ("f32", "f32_chunked") else TOL_BF16
     cu = wl.cu_seqlens
     o_ref, f_ref = oracle.recurrence(f32np(wl.q), f32np(wl.k), f32np(wl.v), f32np(wl.g), f32np(wl.beta),
                                      cu.numpy(), s0=None if wl.state is None else f32np(wl.state),
@@ -139,6 +139,29 @@ def _core_case(gdn, wl, math, heads=None, inplace=False):
 def test_tiny_f32_config(gdn):
     announce("tiny_f32 config (fp32 recurrent path)")
     _core_case(gdn, inputs.tiny_f32(), "f32")
+
+
+def test_tiny_f32_config_chunked(gdn):
+    """The tiny fp32 configuration through the chunked WY / UT form computed in fp32."""
+    announce("tiny_f32 config (chunked form in fp32)")
+    _core_case(gdn, inputs.tiny_f32(), "f32_chunked")
+
+
+@pytest.mark.parametrize("dk,dv,lengths", [(16, 16, [70, 0, 5, 130]), (32, 32, [1, 63, 64, 65, 200]),
+                                           (64, 32, [129, 0, 3]), (32, 64, [300]), (64, 64, [64, 191, 2])])
+def test_core_f32_chunked_path(gdn, dk, dv, lengths):
+    """Chunked fp32 path: ragged sequences (empty, single token, chunk edges, several chunks),
+    two value heads per key head, random initial states, scale 0.5."""
+    announce(f"core chunked fp32 path dk={dk} dv={dv} lengths={lengths}")
+    wl = inputs.core_workload("chf32", 560 + dk + dv + len(lengths), lengths, 2, 4, dk, dv, random_states=True,
+                              scale=0.5)
+    _core_case(gdn, wl, "f32_chunked")
+
+
+def test_core_f32_chunked_slow_decay_inplace(gdn):
+    announce("core chunked fp32 path, slow decay, final state aliasing the initial state")
+    wl = inputs.core_workload("chf32slow", 590, [500, 77], 1, 2, 32, 32, random_states=True, decay="slow")
+    _core_case(gdn, wl, "f32_chunked", inplace=True)
 
 
 @pytest.mark.parametrize("dk,dv", [(16, 16), (32, 32), (64, 32), (128, 128)])
@@ -514,12 +537,13 @@ def _differs(name, gpu, other_ref, tol):
     assert r > 50 * tol
 
 
-@pytest.mark.parametrize("math,d", [("mfma", 128), ("mfma", 64), ("f32", 128), ("f32", 32)])
+@pytest.mark.parametrize("math,d", [("mfma", 128), ("mfma", 64), ("f32", 128), ("f32", 32), ("f32_chunked", 32),
+                                    ("f32_chunked", 64)])
 def test_core_order1(gdn, math, d):
     lengths = [1, 63, 0, 200, 65, 129]
     announce(f"core order 1 ({math}, d={d}) lengths={lengths}")
     wl = inputs.core_workload("ord1", 950 + d, lengths, 2, 4, d, d, random_states=True, scale=0.5)
-    tol = TOL_F32 if math == "f32" else TOL_BF16
+    tol = TOL_F32 if math in ("f32", "f32_chunked") else TOL_BF16
     args = (f32np(wl.q), f32np(wl.k), f32np(wl.v), f32np(wl.g), f32np(wl.beta), wl.cu_seqlens.numpy())
     o1, f1 = oracle.recurrence(*args, s0=f32np(wl.state), scale=0.5, order=1)
     o0, _ = oracle.recurrence(*args, s0=f32np(wl.state), scale=0.5, order=0)
