@@ -3,7 +3,7 @@
 // overlap checks, and dispatch to the kernels' launchers.
 #include "gdn.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdint>
@@ -35,13 +35,20 @@ bool overlap(Range a, Range b) {
 // Exact aliasing is allowed where documented; partial overlap never is.
 bool bad_partial_alias(Range a, Range b) { return overlap(a, b) && !(a.p == b.p && a.bytes == b.bytes); }
 
+// Size limits that keep every byte count the checks below form within 64 bits (tensor
+// sizes are products of up to five of these with int token counts): heads, sequences or
+// decode rows, and rows of the standalone norm.
+constexpr int kMaxHeads = 4096;
+constexpr int kMaxSeqs = 1 << 24;
+constexpr long kMaxNormRows = 1L << 40;
+
 int check_heads(int Hk, int Hv) {
-    if (Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return GDN_ERR_BAD_SHAPE;
+    if (Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || Hk > kMaxHeads || Hv > kMaxHeads) return GDN_ERR_BAD_SHAPE;
     return GDN_OK;
 }
 
 int check_seqs(const int32_t *cu, int N, int T) {
-    if (T < 0 || N < 1) return GDN_ERR_BAD_SHAPE;
+    if (T < 0 || N < 1 || N > kMaxSeqs) return GDN_ERR_BAD_SHAPE;
     if (!cu && N != 1) return GDN_ERR_BAD_SHAPE;
     return GDN_OK;
 }
@@ -144,8 +151,7 @@ int gdn_conv_qk_prep(const void *x, const void *conv_w, const int32_t *cu_seqlen
 }
 
 size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv, int math) {
-    (void)Hk;
-    if (T < 0 || N < 1 || Hv <= 0) return 0;
+    if (T < 0 || N < 1 || N > kMaxSeqs || check_heads(Hk, Hv) != GDN_OK) return 0;
     if (math != GDN_MATH_MFMA || !gdn::chunked_supported(dk, dv)) return 0;
     return gdn::chunked_workspace_bytes(T, N, Hv, dk, dv);
 }
@@ -323,7 +329,7 @@ int decode_impl(const void *x, const void *conv_w, void *conv_state, const float
                 float norm_eps, int B, int Hk, int Hv, int dk, int dv, int dtype, int order, void *stream) {
     try {
         const bool gated = out != nullptr || z != nullptr || gamma != nullptr;
-        if (B < 0) return GDN_ERR_BAD_SHAPE;
+        if (B < 0 || B > kMaxSeqs) return GDN_ERR_BAD_SHAPE;
         if (!conv_w || (B > 0 && (!x || !conv_state || !g || !beta || !state))) return GDN_ERR_NULL_POINTER;
         if (gated ? (!gamma || (B > 0 && (!z || !out))) : (B > 0 && !o)) return GDN_ERR_NULL_POINTER;
         if (!aligned16({x, conv_w, conv_state, g, beta, state, o, z, gamma, out})) return GDN_ERR_ALIGN;
@@ -381,7 +387,7 @@ int gdn_decode_step_gated(const void *x, const void *conv_w, void *conv_state, c
 int gdn_gated_rmsnorm(const float *y, const void *z, const void *gamma, void *out, long rows, int dv,
                       float eps, int dtype, void *stream) {
     try {
-        if (rows < 0) return GDN_ERR_BAD_SHAPE;
+        if (rows < 0 || rows > kMaxNormRows) return GDN_ERR_BAD_SHAPE;
         if (!gamma || (rows > 0 && (!y || !z || !out))) return GDN_ERR_NULL_POINTER;
         if (!aligned16({y, z, gamma, out})) return GDN_ERR_ALIGN;
         if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
@@ -524,7 +530,7 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
 }
 
 size_t gdn_layer_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, int dv) {
-    if (T < 0 || N < 1 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0 || !gdn::chunked_supported(dk, dv)) return 0;
+    if (T < 0 || N < 1 || N > kMaxSeqs || check_heads(Hk, Hv) != GDN_OK || !gdn::chunked_supported(dk, dv)) return 0;
     return layer_ws(T, N, Hk, Hv, dk, dv).total;
 }
 
@@ -556,9 +562,11 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
             if (overlap(rws, in)) return GDN_ERR_ALIAS;
         for (Range in : {rh, rwi, rcw, rgm, rwo, rci, rco, rs0, rsf})
             if (overlap(rout, in)) return GDN_ERR_ALIAS;
-        for (Range in : {rh, rwi, rcw, rgm, rwo, rs0})
+        for (Range in : {rh, rwi, rcw, rgm, rwo})
             if (overlap(rco, in) || overlap(rsf, in)) return GDN_ERR_ALIAS;
-        if (overlap(rco, rsf) || bad_partial_alias(rco, rci) || bad_partial_alias(rsf, rs0) || overlap(rsf, rci))
+        // the output caches may replace the input ones exactly (and only exactly)
+        if (overlap(rco, rs0) || overlap(rco, rsf) || bad_partial_alias(rco, rci) || bad_partial_alias(rsf, rs0) ||
+            overlap(rsf, rci))
             return GDN_ERR_ALIAS;
         char *ws = static_cast<char *>(workspace);
         void *x = ws + L.x, *z = ws + L.z;
@@ -581,7 +589,9 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
 }
 
 size_t gdn_layer_decode_workspace_size(int B, int E, int Hk, int Hv, int dk, int dv) {
-    if (B < 0 || E <= 0 || Hk <= 0 || Hv <= 0 || Hv % Hk != 0) return 0;
+    if (B < 0 || B > kMaxSeqs || E <= 0 || E > kProjMaxK || check_heads(Hk, Hv) != GDN_OK || dk <= 0 || dk > 256 ||
+        dv <= 0 || dv > 256)
+        return 0;
     return layer_decode_ws(B, E, Hk, Hv, dk, dv).total;
 }
 
@@ -590,7 +600,7 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
                      float norm_eps, int B, int E, int Hk, int Hv, int dk, int dv, int order, void *workspace,
                      size_t workspace_bytes, void *stream) {
     try {
-        if (B < 0) return GDN_ERR_BAD_SHAPE;
+        if (B < 0 || B > kMaxSeqs) return GDN_ERR_BAD_SHAPE;
         if (int e = check_layer_shape(E, Hk, Hv, dk, dv)) return e;
         if (!pow2_in(dk, 16, 128) || !pow2_in(dv, 16, 128) || !valid_order(order)) return GDN_ERR_UNSUPPORTED;
         if (!w_in || !conv_w || !gamma || !w_out || (B > 0 && (!hidden || !conv_state || !state || !out)))

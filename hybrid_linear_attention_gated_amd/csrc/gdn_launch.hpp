@@ -3,7 +3,7 @@
 // these is called; each returns the first HIP error it meets.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

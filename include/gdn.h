@@ -53,6 +53,9 @@
  *    aligned, as every device allocator returns them: the kernels move 16-byte
  *    vectors and stage rows with 16-byte direct-to-LDS loads.  A misaligned pointer
  *    returns GDN_ERR_ALIGN.
+ *  - Size limits (GDN_ERR_BAD_SHAPE beyond them), which keep every byte count the
+ *    library forms within 64 bits: Hk, Hv <= 4096; N sequences and B decode rows
+ *    <= 2^24; rows of gdn_gated_rmsnorm <= 2^40.
  *  - Return value: GDN_OK or a gdn_status code.  Argument errors are detected on
  *    the host before anything is enqueued; nothing is written then.  Launch
  *    failures map to GDN_ERR_HIP.  No function aborts or throws.

@@ -161,6 +161,28 @@ def test_layer_prefill_grid_inputs(gdn):
     _check_layer(*gpu, *ref)
 
 
+def test_layer_prefill_state_in_place(gdn):
+    """final_state aliasing initial_state and conv_state_out aliasing conv_state_in (the
+    exact aliases the ABI allows): the same results as separate output buffers."""
+    announce("layer prefill with the state and the conv cache updated in place")
+    lengths, E, Hk, Hv, d = [90, 0, 40], 128, 1, 2, 64
+    T, N = sum(lengths), len(lengths)
+    cu = _cuda(torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)))
+    wts = inputs.layer_weights(645, E, Hk, Hv, d, d)
+    h = _cuda(inputs.layer_hidden(646, T, E))
+    cs_in, s0 = inputs.layer_caches(647, N, Hk, Hv, d, d)
+    w = [_cuda(t) for t in (wts.w_in, wts.conv_w, wts.gamma, wts.w_out)]
+    cso = torch.empty(cs_in.shape, dtype=torch.float32, device=DEV)
+    out1, fin1 = gdn.layer_prefill(h, *w, Hk, Hv, d, d, cu_seqlens=cu, conv_state_in=_cuda(cs_in),
+                                   conv_state_out=cso, initial_state=_cuda(s0))
+    cs2, st2 = _cuda(cs_in), _cuda(s0)
+    out2, fin2 = gdn.layer_prefill(h, *w, Hk, Hv, d, d, cu_seqlens=cu, conv_state_in=cs2, conv_state_out=cs2,
+                                   initial_state=st2, final_state=st2)
+    torch.cuda.synchronize()
+    assert fin2 is st2
+    assert torch.equal(out1, out2) and torch.equal(fin1, st2) and torch.equal(cso, cs2)
+
+
 def test_layer_prefill_empty(gdn):
     announce("layer prefill T=0 with caches")
     (out, fin, cs), (out_ref, fin_ref, cs_ref) = _layer_case(gdn, [0, 0], 128, 1, 2, 64, 650, True, 1.0)
