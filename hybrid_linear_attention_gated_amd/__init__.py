@@ -25,7 +25,7 @@ __all__ = ["conv_qk_prep", "chunk_prefill", "prefill", "prefill_local", "gated_r
            "GDN_F32", "GDN_BF16", "GDN_MATH_F32", "GDN_MATH_MFMA", "GDN_MATH_F32_CHUNKED", "GDN_ORDER_DECAY_FIRST", "GDN_ORDER_RETRIEVE_FIRST",
            "LIB_PATH", "abi_version", "mfma_supported", "linear", "in_proj", "layer_prefill", "layer_decode",
            "layer_prefill_workspace_size", "layer_decode_workspace_size", "prefill_workspace_status",
-           "GDN_OK", "GDN_ERR_TIMEOUT", "GDN_ERR_NONFINITE", "set_wait_bound"]
+           "GDN_OK", "GDN_ERR_TIMEOUT", "GDN_ERR_NONFINITE", "set_wait_bound", "layer_decode_noalloc"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.gdn_layer_decode_workspace_size.restype = Z
         L.gdn_layer_decode.argtypes = [P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P, Z, P]
         L.gdn_layer_decode.restype = I
+        L.gdn_layer_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, F, F, F, I, I, I, I, I, I, I, P]
+        L.gdn_layer_decode_noalloc.restype = I
         L.gdn_prefill_workspace_status.argtypes = [P, Z, P]
         L.gdn_prefill_workspace_status.restype = I
         L.gdn_status_string.argtypes = [I]
@@ -514,4 +516,24 @@ def layer_decode(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, 
                                 int(order), _p(workspace), workspace.numel() * workspace.element_size(), _stream())
     if st != 0:
         raise GdnError("gdn_layer_decode", st)
+    return out
+
+
+def layer_decode_noalloc(hidden, w_in, conv_w, gamma, w_out, conv_state, state, Hk, Hv, dk, dv, out, scale=1.0,
+                         l2_eps=1e-6, norm_eps=1e-6, order=0):
+    """`layer_decode` through the allocation-free entry point: the intermediates live in the
+    library's scratch array on the device, and `out` [B, E] bf16 must be given (nothing is
+    allocated)."""
+    bf = torch.bfloat16
+    _check(hidden, "hidden", bf)
+    B, E = hidden.shape
+    C = _layer_weights(w_in, conv_w, gamma, w_out, E, Hk, Hv, dk, dv)
+    _check(conv_state, "conv_state", torch.float32, (B, 3, C))
+    _check(state, "state", torch.float32, (B, Hv, dk, dv))
+    _check(out, "out", bf, (B, E))
+    st = lib().gdn_layer_decode_noalloc(_p(hidden), _p(w_in), _p(conv_w), _p(gamma), _p(w_out), _p(conv_state),
+                                        _p(state), _p(out), float(scale), float(l2_eps), float(norm_eps), B, E, Hk,
+                                        Hv, dk, dv, int(order), _stream())
+    if st != 0:
+        raise GdnError("gdn_layer_decode_noalloc", st)
     return out

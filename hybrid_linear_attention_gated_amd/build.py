@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_api.cpp", "gdn_prep.hip", "gdn_decode.hip", "gdn_prefill_recurrent.hip", "gdn_chunk.hip",
-           "gdn_chunk_f32.hip", "gdn_norm.hip", "gdn_proj.hip"]
+           "gdn_chunk_f32.hip", "gdn_norm.hip", "gdn_proj.hip", "gdn_noalloc.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

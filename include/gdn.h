@@ -424,6 +424,23 @@ int gdn_layer_decode(const void *hidden, const void *w_in, const void *conv_w, c
                      int B, int E, int Hk, int Hv, int dk, int dv, int order,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * gdn_layer_decode_noalloc -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid allocation): gdn_layer_decode with its
+ * intermediate tensors in a scratch array that the library holds on each GPU it is loaded
+ * on (64 MiB, kept until the process ends) instead of a caller's workspace.  Arguments and
+ * results are those of gdn_layer_decode without the workspace.  Sizes whose intermediates
+ * exceed the scratch (gdn_layer_decode_workspace_size(B, E, Hk, Hv, dk, dv) > 64 MiB, about
+ * 680 rows at hidden 1024 and 16 value heads of 128) return GDN_ERR_WORKSPACE before
+ * anything runs.  All calls on one GPU share its scratch: calls that overlap in time on one
+ * GPU (two streams, or two threads) race; calls ordered on one stream do not.  No device
+ * memory is allocated or freed by this call.
+ */
+int gdn_layer_decode_noalloc(const void *hidden, const void *w_in, const void *conv_w, const void *gamma,
+                             const void *w_out, void *conv_state, float *state, void *out,
+                             float scale, float l2_eps, float norm_eps,
+                             int B, int E, int Hk, int Hv, int dk, int dv, int order, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *gdn_status_string(int status);
 
