@@ -407,6 +407,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     constexpr int LD = SM::LD;
     constexpr int NF_K = (D / 16) * 2;
     __shared__ __attribute__((aligned(16))) char smem[STAGE ? SM::SIZE_STAGED : SM::SIZE];
+    __shared__ int tflag;   // diagonal blocks of the current chunk published (value: chunk + 1)
+    if (threadIdx.x == 0) tflag = -1;   // seen by every wave after the chunk loop's first barrier
     bf16 *Kh = reinterpret_cast<bf16 *>(smem + SM::KH);
     bf16 *Kl = reinterpret_cast<bf16 *>(smem + SM::KL);
     bf16 *Qh = reinterpret_cast<bf16 *>(smem + SM::QH);
@@ -566,70 +568,85 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     // ---- 1. tiles with key block b as the A operand: K K^T (b, c <= b) and K Q^T (b, r >= b).
     // Eight waves: wave b takes the K K^T tiles of block b, wave 4 + b the K Q^T tiles;
     // four waves: wave b takes both.
+    // The tile loops run at compile time (one instance per key block), so the next tile's
+    // operand reads are issued under the current tile's MFMAs.
     {
         const int b = wave & 3;
         const bool doKK = NW == 4 || wave < 4, doKQ = NW == 4 || wave >= 4;
-        Split8 ka[NKS];
+        auto tiles = [&](auto btag) __attribute__((always_inline)) {
+            constexpr int B = decltype(btag)::value;
+            Split8 ka[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int off = (16 * b + l16) * LD + 32 * ks + 8 * kg;
-            ka[ks] = Split8{*reinterpret_cast<const bf16x8 *>(Kh + off), *reinterpret_cast<const bf16x8 *>(Kl + off)};
-        }
-        const f32x4 Gb = *reinterpret_cast<const f32x4 *>(Gs + 16 * b + 4 * kg);
-        if (doKK) {
-            const f32x4 Bb = *reinterpret_cast<const f32x4 *>(Bs + 16 * b + 4 * kg);
-            const f32x4 Grb = *reinterpret_cast<const f32x4 *>(GRs + 16 * b + 4 * kg);
-            for (int c = 0; c <= b; ++c) {
-                f32x4 acc = zero4();
+            for (int ks = 0; ks < NKS; ++ks) {
+                const int off = (16 * B + l16) * LD + 32 * ks + 8 * kg;
+                ka[ks] = Split8{*reinterpret_cast<const bf16x8 *>(Kh + off),
+                                *reinterpret_cast<const bf16x8 *>(Kl + off)};
+            }
+            if (doKK) {
+                const f32x4 Bb = *reinterpret_cast<const f32x4 *>(Bs + 16 * B + 4 * kg);
+                const f32x4 Grb = *reinterpret_cast<const f32x4 *>(GRs + 16 * B + 4 * kg);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off = (16 * c + l16) * LD + 32 * ks + 8 * kg;
-                    const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off),
-                                    *reinterpret_cast<const bf16x8 *>(Kl + off)};
-                    acc = mfma16x3(ka[ks], kb, acc);
-                }
-                // A[t][i] = b_t e^{Gr_t - G_i} k_t . k_i for i < t; t = 16b + 4kg + r, i = 16c + l16
-                const int i = 16 * c + l16;
-                const float Gi = Gs[i];
-                f32x4 a;
+                for (int c = 0; c <= B; ++c) {
+                    Acc3 s3 = acc3_zero();
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * b + 4 * kg + r;
-                    a[r] = i < t ? Bb[r] * __expf(Grb[r] - Gi) * acc[r] : 0.f;
-                }
-                if (c == b) {
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int off = (16 * c + l16) * LD + 32 * ks + 8 * kg;
+                        const Split8 kb{*reinterpret_cast<const bf16x8 *>(Kh + off),
+                                        *reinterpret_cast<const bf16x8 *>(Kl + off)};
+                        mfma3_acc(s3, ka[ks], kb);
+                    }
+                    const f32x4 acc = acc3_sum(s3);
+                    // A[t][i] = b_t e^{Gr_t - G_i} k_t . k_i for i < t; t = 16B + 4kg + r, i = 16c + l16
+                    const int i = 16 * c + l16;
+                    const float Gi = Gs[i];
+                    f32x4 a;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Adiag[c * SM::ADIAG_BLK + (4 * kg + r) * 16 + l16] = a[r];
-                } else {
-                    const int s = stri_idx(b, c);
-                    split_store(a, &Aoff[(s * 2 + 0) * 64 + lane], &Aoff[(s * 2 + 1) * 64 + lane]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int t = 16 * B + 4 * kg + r;
+                        a[r] = i < t ? Bb[r] * __expf(Grb[r] - Gi) * acc[r] : 0.f;
+                    }
+                    if (c == B) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Adiag[c * SM::ADIAG_BLK + (4 * kg + r) * 16 + l16] = a[r];
+                    } else {
+                        const int s = stri_idx(B, c);
+                        split_store(a, &Aoff[(s * 2 + 0) * 64 + lane], &Aoff[(s * 2 + 1) * 64 + lane]);
+                    }
                 }
             }
-        }
-        if (doKQ) {
-            for (int r = b; r < 4; ++r) {
-                f32x4 acc = zero4();
+            if (doKQ) {
+                const f32x4 Gb = *reinterpret_cast<const f32x4 *>(Gs + 16 * B + 4 * kg);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off = (16 * r + l16) * LD + 32 * ks + 8 * kg;
-                    const Split8 qb{*reinterpret_cast<const bf16x8 *>(Qh + off),
-                                    *reinterpret_cast<const bf16x8 *>(Ql + off)};
-                    acc = mfma16x3(ka[ks], qb, acc);
-                }
-                // P^T[i][t] = e^{G_t - G_i} q_t . k_i for i <= t; i = 16b + 4kg + rr, t = 16r + l16
-                const int t = 16 * r + l16;
-                const float Gt = Gs[t];
-                f32x4 p;
+                for (int r = B; r < 4; ++r) {
+                    Acc3 s3 = acc3_zero();
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * b + 4 * kg + rr;
-                    p[rr] = i <= t ? __expf(Gt - Gb[rr]) * acc[rr] : 0.f;
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int off = (16 * r + l16) * LD + 32 * ks + 8 * kg;
+                        const Split8 qb{*reinterpret_cast<const bf16x8 *>(Qh + off),
+                                        *reinterpret_cast<const bf16x8 *>(Ql + off)};
+                        mfma3_acc(s3, ka[ks], qb);
+                    }
+                    const f32x4 acc = acc3_sum(s3);
+                    // P^T[i][t] = e^{G_t - G_i} q_t . k_i for i <= t; i = 16B + 4kg + rr, t = 16r + l16
+                    const int t = 16 * r + l16;
+                    const float Gt = Gs[t];
+                    f32x4 p;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * B + 4 * kg + rr;
+                        p[rr] = i <= t ? __expf(Gt - Gb[rr]) * acc[rr] : 0.f;
+                    }
+                    Pt[tri_idx(B, r) * 64 + lane] = p;
                 }
-                Pt[tri_idx(b, r) * 64 + lane] = p;
             }
+        };
+        switch (b) {
+        case 0: tiles(std::integral_constant<int, 0>{}); break;
+        case 1: tiles(std::integral_constant<int, 1>{}); break;
+        case 2: tiles(std::integral_constant<int, 2>{}); break;
+        default: tiles(std::integral_constant<int, 3>{}); break;
         }
     }
-
     // W waves: K in accumulator layout (rows = token) for head-dim tiles 2qw, 2qw + 1, on
     // MFMA from the row fragments: D = K_rows x Sel with Sel[k][j] = (k == 16 hh + j).  The hi
     // and lo planes go through separately, so the results are exact bf16 values and form the
@@ -718,32 +735,13 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
             sen = __builtin_amdgcn_readfirstlane(seq_end(cu, sn, Ttot));
         }
     }
-    if constexpr (STAGE) {
-        if (next_ok) {
-            constexpr int SEGL = 2 * D / 16, SPI = 64 / SEGL;
-            const int tn = sbn + cn * kChunk;
-            const int rb = max(tn - kConvHist, 0);
-            const long bytes = (long)(Ttot - rb) * conv_dim * 2;
-            const __amdgpu_buffer_rsrc_t rx =
-                make_rsrc(x + (size_t)rb * conv_dim, (int)min(bytes, (long)0x7ffffff0));
-            for (int i = wave; i < SM::XCOPIES; i += NW) {
-                const int sg = i * SPI + lane / SEGL;
-                const int r = min(sg / 3, SM::XROWS - 1), gi = sg % 3;
-                const int chb = gi == 0 ? kh * D : gi == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D;
-                const int voff = ((tn - kConvHist + r - rb) * conv_dim + chb) * 2 + 16 * (lane % SEGL);
-                char *dst = i * 1024 < SM::XRA * SM::XROW ? smem + SM::XA + i * 1024
-                                                          : smem + SM::XB + (i * 1024 - SM::XRA * SM::XROW);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst, 16,
-                                                         voff, 0, 0, 0);
-            }
-        }
-    }
-
-    // ---- 2. diagonal blocks T_cc = (I + A_cc)^-1 by forward substitution; lane (c, j)
-    // computes column j of block c, then the columns are regrouped into accumulator
-    // layout through this wave's scratch (lane (kg, l16) gets rows 4kg..4kg+3).
-    Split8 Tcc[4];   // A-operand form of T_cc^T (= accumulator layout of T_cc)
-    {
+    // Eight waves: wave 0 alone solves the diagonal blocks (one wave's 64 lanes cover all
+    // four) and hands them over through LDS with a flag, while waves 1 .. 7 issue the next
+    // chunk's staging copies; a barrier there would make every wave wait for its copies.
+    constexpr bool ONE_SOLVER = NW == 8;
+    constexpr int SW0 = ONE_SOLVER ? 1 : 0;   // first staging wave
+    float *scr = reinterpret_cast<float *>(smem + SM::SCR + (ONE_SOLVER ? 0 : wave) * SM::SCR_WAVE);
+    if (!ONE_SOLVER || wave == 0) {
         const int c = kg, j = l16;
         const float *Ab = Adiag + c * SM::ADIAG_BLK;
         float x[16];
@@ -762,17 +760,47 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
             }
             x[t] = s0 + s1;
         }
-        float *scr = reinterpret_cast<float *>(smem + SM::SCR + wave * SM::SCR_WAVE);
 #pragma unroll
         for (int t4 = 0; t4 < 16; t4 += 4)
             *reinterpret_cast<f32x4 *>(scr + (c * 16 + j) * SM::SCR_LANE + t4) =
                 f32x4{x[t4], x[t4 + 1], x[t4 + 2], x[t4 + 3]};
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's scratch writes are done
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            Tcc[cc] = split_block(*reinterpret_cast<const f32x4 *>(scr + (cc * 16 + l16) * SM::SCR_LANE + 4 * kg));
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the scratch writes are done
+        if (ONE_SOLVER) __hip_atomic_store(&tflag, gc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    if constexpr (STAGE) {
+        if (next_ok && wave >= SW0) {
+            constexpr int SEGL = 2 * D / 16, SPI = 64 / SEGL;
+            const int tn = sbn + cn * kChunk;
+            const int rb = max(tn - kConvHist, 0);
+            const long bytes = (long)(Ttot - rb) * conv_dim * 2;
+            const __amdgpu_buffer_rsrc_t rx =
+                make_rsrc(x + (size_t)rb * conv_dim, (int)min(bytes, (long)0x7ffffff0));
+            for (int i = wave - SW0; i < SM::XCOPIES; i += NW - SW0) {
+                const int sg = i * SPI + lane / SEGL;
+                const int r = min(sg / 3, SM::XROWS - 1), gi = sg % 3;
+                const int chb = gi == 0 ? kh * D : gi == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D;
+                const int voff = ((tn - kConvHist + r - rb) * conv_dim + chb) * 2 + 16 * (lane % SEGL);
+                char *dst = i * 1024 < SM::XRA * SM::XROW ? smem + SM::XA + i * 1024
+                                                          : smem + SM::XB + (i * 1024 - SM::XRA * SM::XROW);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst, 16,
+                                                         voff, 0, 0, 0);
+            }
+        }
     }
 
+    if (ONE_SOLVER && wave != 0) {
+        // wave 0 raises the flag unconditionally a few thousand cycles after the barrier; the
+        // bound only keeps a broken invariant from hanging the kernel
+        for (int it = 0; it < (1 << 20); ++it) {
+            if (__hip_atomic_load(&tflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == gc + 1) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    }
+    Split8 Tcc[4];   // A-operand form of T_cc^T (= accumulator layout of T_cc)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+        Tcc[cc] = split_block(*reinterpret_cast<const f32x4 *>(scr + (cc * 16 + l16) * SM::SCR_LANE + 4 * kg));
     // ---- 3. back substitution (I + A^T) X = [I | P^T], one column block per chain:
     //   X_cr = T_cc^T (RHS_cr - sum_{k = c+1..r} (A^T)_ck X_kr),  c = r, r-1, .., 0
     // chains 0..3: column blocks of T^T (RHS = I); chains 4..7: column blocks of M^T.
@@ -786,41 +814,47 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         const int s = (set * 10 + tri_idx(c, r)) * 2;
         split_store(x * rs * colscale, &Xt[(s + 0) * 64 + lane], &Xt[(s + 1) * 64 + lane]);
     };
+    // Right-looking: as soon as block X_kr is known it is split once and its products with
+    // (A^T)_ck go into every pending accumulator, the one of block k - 1 first (it gates
+    // the next step of the chain), and the block is published while those MFMAs run.
     auto solve_T = [&](auto rtag) __attribute__((always_inline)) {
         constexpr int r = decltype(rtag)::value;
-        f32x4 X[4];
         bf16x8 eye;
 #pragma unroll
         for (int vv = 0; vv < 8; ++vv) eye[vv] = (bf16)((vv < 4 && 4 * kg + vv == l16) ? 1.f : 0.f);
-        X[r] = mfma16(Tcc[r].lo, eye, mfma16(Tcc[r].hi, eye, zero4()));   // T_rr^T
+        f32x4 X = mfma16(Tcc[r].lo, eye, mfma16(Tcc[r].hi, eye, zero4()));   // T_rr^T
+        f32x4 acc[4];
 #pragma unroll
-        for (int c = r - 1; c >= 0; --c) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = c + 1; kk <= r; ++kk) acc = mfma16x3(aT(kk, c), split_block(X[kk]), acc);
-            X[c] = -mfma16x3(Tcc[c], split_block(acc), zero4());
-        }
+        for (int c = 0; c < r; ++c) acc[c] = zero4();
         const float dc = DCs[16 * r + l16];
 #pragma unroll
-        for (int c = 0; c <= r; ++c) {
-            publish(XT_TW, c, r, X[c], BEG, dc);
-            publish(XT_TU, c, r, X[c], Bs, dc);
+        for (int k = r; k >= 0; --k) {
+            if (k > 0) {
+                const Split8 xs = split_block(X);
+#pragma unroll
+                for (int c = k - 1; c >= 0; --c) acc[c] = mfma16x3(aT(k, c), xs, acc[c]);
+            }
+            publish(XT_TW, k, r, X, BEG, dc);
+            publish(XT_TU, k, r, X, Bs, dc);
+            if (k > 0) X = mfma16x3p(Tcc[k - 1], split_block(-acc[k - 1]));
         }
     };
     auto solve_M = [&](auto rtag) __attribute__((always_inline)) {
         constexpr int r = decltype(rtag)::value;
-        f32x4 X[4];
+        f32x4 acc[4];
 #pragma unroll
-        for (int c = r; c >= 0; --c) {
-            f32x4 acc = Pt[tri_idx(c, r) * 64 + lane];
+        for (int c = 0; c <= r; ++c) acc[c] = Pt[tri_idx(c, r) * 64 + lane];
+        f32x4 X = mfma16x3p(Tcc[r], split_block(acc[r]));
 #pragma unroll
-            for (int kk = c + 1; kk <= r; ++kk) acc = mfma16x3(neg_split(aT(kk, c)), split_block(X[kk]), acc);
-            X[c] = mfma16x3(Tcc[c], split_block(acc), zero4());
-        }
+        for (int k = r; k >= 0; --k) {
+            if (k > 0) {
+                const Split8 xs = split_block(-X);
 #pragma unroll
-        for (int c = 0; c <= r; ++c) {
-            publish(XT_MW, c, r, X[c], BEG, 1.f);
-            publish(XT_MU, c, r, X[c], Bs, 1.f);
+                for (int c = k - 1; c >= 0; --c) acc[c] = mfma16x3(aT(k, c), xs, acc[c]);
+            }
+            publish(XT_MW, k, r, X, BEG, 1.f);
+            publish(XT_MU, k, r, X, Bs, 1.f);
+            if (k > 0) X = mfma16x3p(Tcc[k - 1], split_block(acc[k - 1]));
         }
     };
     auto run_chain = [&](int ch) __attribute__((always_inline)) {
@@ -836,7 +870,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         }
     };
     if (NW == 8) {
-        run_chain(wave);
+        // waves w and w + 4 share a SIMD: T chain w with M chain 3 - w keeps the long chains apart
+        run_chain(wave < 4 ? wave : 11 - wave);
     } else {   // four waves: long and short chains paired
         run_chain(3 - wave);
         run_chain(4 + wave);
@@ -866,66 +901,71 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         }
         return f;
     };
-    f32x4 Y[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) Y[a][b] = zero4();
+    // Each wave forms its first product tile by tile and stores every tile as soon as it is
+    // complete, so the stores drain while the second product runs.  The three partial products
+    // of each split product accumulate separately (six independent MFMA chains per step).
     if (isW) {
-        // Y = W'^T = K^T (Bk T^T Dc);  Xa = Qt^T = e^G Q^T - K^T (Bk M^T)
+        // W'^T = K^T (Bk T^T Dc), stored negated as fp16 A fragments
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const float qs = QS[16 * tt + l16];
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi) Xa[mi][tt] = Xa[mi][tt] * qs;
+            Acc3 y[2] = {acc3_zero(), acc3_zero()};
 #pragma unroll
             for (int ks = 0; 2 * ks <= tt; ++ks) {
                 const Split8 ft = row_frag(XT_TW, tt, ks);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) mfma3_acc(y[mi], Bop[mi][ks], ft);
+            }
+            const int off = ((tt * NKS + qw) * 64 + lane) * 16;
+            rec_store16(rec, R::W_OFF + off, pack_h(-acc3_sum(y[0]), -acc3_sum(y[1])), flags != nullptr);
+        }
+        // Qt^T = e^G Q^T - K^T (Bk M^T)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const float qs = QS[16 * tt + l16];
+            Acc3 x[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) x[mi] = Acc3{Xa[mi][tt] * qs, zero4(), zero4()};
+#pragma unroll
+            for (int ks = 0; 2 * ks <= tt; ++ks) {
                 const Split8 fm = neg_split(row_frag(XT_MW, tt, ks));
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
-                    Y[mi][tt] = mfma16x3(Bop[mi][ks], ft, Y[mi][tt]);
-                    Xa[mi][tt] = mfma16x3(Bop[mi][ks], fm, Xa[mi][tt]);
-                }
+                for (int mi = 0; mi < 2; ++mi) mfma3_acc(x[mi], Bop[mi][ks], fm);
             }
-        }
-        // -W' and Qt as the state pass's A-operand fragments (k = head dim in kperm order)
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int off = ((mt * NKS + qw) * 64 + lane) * 16;
-            rec_store16(rec, R::W_OFF + off, pack_h(-Y[0][mt], -Y[1][mt]), flags != nullptr);
-            rec_store16(rec, R::Q_OFF + off, pack_h(Xa[0][mt], Xa[1][mt]), flags != nullptr);
+            const int off = ((tt * NKS + qw) * 64 + lane) * 16;
+            rec_store16(rec, R::Q_OFF + off, pack_h(acc3_sum(x[0]), acc3_sum(x[1])), flags != nullptr);
         }
     } else {
-        // Y = U' = (Dc T Bv) V;  Xa = Ol^T = V^T (M Bv)^T   (Xa's V values are consumed).
-        // Ol is formed transposed (operands swapped: the A form of V^T and the B form of
-        // (M Bv)^T are the fragments already at hand), so that the state pass, which forms
-        // O^T the same way, holds 4 consecutive columns of one output row per lane.
+        // U' = (Dc T Bv) V, then Ol^T = V^T (M Bv)^T (formed transposed: the A form of V^T and
+        // the B form of (M Bv)^T are the fragments at hand, and the state pass, which forms O^T
+        // the same way, then holds 4 consecutive columns of one output row per lane)
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) Xa[a][b] = zero4();
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+            Acc3 y[2] = {acc3_zero(), acc3_zero()};
 #pragma unroll
             for (int ks = 0; 2 * ks <= rt; ++ks) {
                 const Split8 ft = row_frag(XT_TU, rt, ks);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) mfma3_acc(y[ni], ft, Bop[ni][ks]);
+            }
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                rec_store16(rec, R::U_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 16, acc3_sum(y[ni]),
+                            flags != nullptr);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            Acc3 x[2] = {acc3_zero(), acc3_zero()};
+#pragma unroll
+            for (int ks = 0; 2 * ks <= rt; ++ks) {
                 const Split8 fm = row_frag(XT_MU, rt, ks);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    Y[ni][rt] = mfma16x3(ft, Bop[ni][ks], Y[ni][rt]);
-                    Xa[ni][rt] = mfma16x3(Bop[ni][ks], fm, Xa[ni][rt]);
-                }
+                for (int ni = 0; ni < 2; ++ni) mfma3_acc(x[ni], Bop[ni][ks], fm);
             }
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const int nt = 2 * qw + ni;
-                const int off = ((nt * 4 + rt) * 64 + lane) * 16;
-                rec_store16(rec, R::U_OFF + off, Y[ni][rt], flags != nullptr);
-                rec_store16(rec, R::O_OFF + off, Xa[ni][rt], flags != nullptr);
-            }
+            for (int ni = 0; ni < 2; ++ni)
+                rec_store16(rec, R::O_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 16, acc3_sum(x[ni]),
+                            flags != nullptr);
+        }
     }
     // Publishing (a state pass runs concurrently and waits for each record): the record
     // stores are device-coherent; every wave waits until its own have completed, then one

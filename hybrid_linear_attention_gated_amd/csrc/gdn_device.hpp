@@ -171,6 +171,27 @@ __device__ __forceinline__ f32x4 mfma16x3(const Split8 &a, const Split8 &b, f32x
     c = mfma16(a.hi, b.lo, c);
     return mfma16(a.hi, b.hi, c);
 }
+// The three partial products in separate accumulators: three independent MFMA chains
+// that issue back to back instead of one chain whose every step waits for the last.
+struct Acc3 {
+    f32x4 hh, hl, lh;
+};
+__device__ __forceinline__ Acc3 acc3_zero() {
+    const f32x4 z{0.f, 0.f, 0.f, 0.f};
+    return Acc3{z, z, z};
+}
+__device__ __forceinline__ void mfma3_acc(Acc3 &s, const Split8 &a, const Split8 &b) {
+    s.lh = mfma16(a.lo, b.hi, s.lh);
+    s.hl = mfma16(a.hi, b.lo, s.hl);
+    s.hh = mfma16(a.hi, b.hi, s.hh);
+}
+__device__ __forceinline__ f32x4 acc3_sum(const Acc3 &s) { return s.hh + (s.hl + s.lh); }
+// a * b from zero with the three products independent
+__device__ __forceinline__ f32x4 mfma16x3p(const Split8 &a, const Split8 &b) {
+    Acc3 s = acc3_zero();
+    mfma3_acc(s, a, b);
+    return acc3_sum(s);
+}
 
 // The k order used when a B operand is built from two fp32 D tiles held in
 // registers (rows 0-15 in tile 0, rows 16-31 in tile 1): lane group kg holds
