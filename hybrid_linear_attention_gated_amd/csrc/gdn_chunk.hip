@@ -1270,32 +1270,22 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         load_scale(rec_of(c_lo));
         __builtin_amdgcn_s_waitcnt(0);
     }
-    bool nonfinite = false;   // an output or the final state is inf / NaN (reported at the end)
+    // inf / NaN detection for the outputs and the final state: x * 0 is 0 for every finite x
+    // and NaN otherwise, so one FMA per value folds them into a sum that ends non-finite
+    // exactly when some value was (reported at the end)
+    float nfacc = 0.f;
 
     // o rows of this lane: row 16 mt + 4 kg + qq of the chunk, column col
     // O^T tiles: lane (kg, l16) holds columns 16 j + 4 kg .. + 3 of output row 16 mt + l16
     const int row_stride = Hv * D;
     const int o_lane = l16 * row_stride + 4 * kg;
 
-    // Fragment groups read from LDS.  Phase 1 group p: -W and Qt fragments of row tiles
-    // 2p, 2p + 1 (all k steps).  Phase 2 group p: K^T hi and lo fragments of state row
-    // tiles 4p .. 4p + 3 (both k steps).
-    constexpr int NG1 = 2;                 // phase 1 groups
+    // Fragment groups read from LDS (16 fragments each at D = 128).  Phase 1: the -W
+    // fragments of all four row tiles (all k steps), then the Qt fragments.  Phase 2 group p:
+    // K^T hi and lo fragments of state row tiles 4p .. 4p + 3 (both k steps).
     constexpr int NG2 = NTD / 4;           // phase 2 groups
     constexpr int GF = 16;                 // fragments per group (both phases, D = 128)
-    constexpr int GF1 = 4 * NKS;           // phase 1 fragments per group
-    static_assert(GF1 <= GF, "group size");
-    auto read_p1 = [&](const char *A, int p, f16x8 *F) {
-#pragma unroll
-        for (int dm = 0; dm < 2; ++dm)
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const int mt = 2 * p + dm;
-                F[dm * 2 * NKS + ks] = *reinterpret_cast<const f16x8 *>(A + R::W_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-                F[dm * 2 * NKS + NKS + ks] =
-                    *reinterpret_cast<const f16x8 *>(A + R::Q_OFF + ((mt * NKS + ks) * 64 + lane) * 16);
-            }
-    };
+    static_assert(4 * NKS <= GF, "group size");
     auto read_p2 = [&](const char *A, int p, f16x8 *F) {
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm)
@@ -1322,33 +1312,38 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) Sh[ks] = pack_h(S[2 * ks], S[2 * ks + 1]);
 
+        // ---- Delta' = U' + (-W') S first (four row-tile chains, one MFMA per k step), then
+        // O^T = Ol^T + S^T Qt^T (four chains): the bf16 split of Delta' below is independent
+        // of the O MFMAs and is scheduled among them, off the path from one state to the next
         f16x8 fr[2][GF];
-        read_p1(A, 0, fr[0]);
-
-        // ---- Delta' = U' + (-W') S and O^T = Ol^T + S^T Qt^T: four independent accumulation chains
-        // per group (Delta and O of two row tiles), each one MFMA per k step
+        auto read_a = [&](const char *A_, int off, f16x8 *F) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    F[mt * NKS + ks] = *reinterpret_cast<const f16x8 *>(A_ + off + ((mt * NKS + ks) * 64 + lane) * 16);
+        };
+        read_a(A, R::W_OFF, fr[0]);
         f32x4 Dl[4], Ot[4];
 #pragma unroll
-        for (int p = 0; p < NG1; ++p) {
-            const f16x8 *F = fr[p & 1];
-            f32x4 d0 = mfma16(F[0], Sh[0], Uf[2 * p]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (p + 1 < NG1) read_p1(A, p + 1, fr[(p + 1) & 1]);
-            else read_p2(A, 0, fr[(p + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            f32x4 o0 = mfma16(Sh[0], F[NKS], Of[2 * p]);
-            f32x4 d1 = mfma16(F[2 * NKS], Sh[0], Uf[2 * p + 1]);
-            f32x4 o1 = mfma16(Sh[0], F[3 * NKS], Of[2 * p + 1]);
+        for (int mt = 0; mt < 4; ++mt) Dl[mt] = mfma16(fr[0][mt * NKS], Sh[0], Uf[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(A, R::Q_OFF, fr[1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 1; ks < NKS; ++ks) {
-                d0 = mfma16(F[ks], Sh[ks], d0);
-                o0 = mfma16(Sh[ks], F[NKS + ks], o0);
-                d1 = mfma16(F[2 * NKS + ks], Sh[ks], d1);
-                o1 = mfma16(Sh[ks], F[3 * NKS + ks], o1);
-            }
-            Dl[2 * p] = d0; Dl[2 * p + 1] = d1;
-            Ot[2 * p] = o0; Ot[2 * p + 1] = o1;
-        }
+        for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Dl[mt] = mfma16(fr[0][mt * NKS + ks], Sh[ks], Dl[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) Ot[mt] = mfma16(Sh[0], fr[1][mt * NKS], Of[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+        read_p2(A, 0, fr[0]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) Ot[mt] = mfma16(Sh[ks], fr[1][mt * NKS + ks], Ot[mt]);
+        constexpr int P2F = 0;   // phase 2's first fragment group sits in fr[0]
 
         // ---- S = e^{G_c} S + K^T Delta' with Delta' = diag(e^{G_c - G_t}) Delta; K and
         // Delta' as bf16 hi + lo pairs (the lo x lo term is dropped): one six-MFMA chain
@@ -1363,11 +1358,11 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         auto kf = [](f16x8 x) { return __builtin_bit_cast(bf16x8, x); };   // K fragments are bf16
 #pragma unroll
         for (int p = 0; p < NG2; ++p) {
-            const f16x8 *F = fr[(NG1 + p) & 1];
+            const f16x8 *F = fr[(P2F + p) & 1];
             f32x4 a[4];
             a[0] = mfma16(kf(F[0]), Dh[0], S[4 * p] * gm);
             __builtin_amdgcn_sched_barrier(0);
-            if (p + 1 < NG2) read_p2(A, p + 1, fr[(NG1 + p + 1) & 1]);
+            if (p + 1 < NG2) read_p2(A, p + 1, fr[(P2F + p + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dm = 1; dm < 4; ++dm) a[dm] = mfma16(kf(F[4 * dm]), Dh[0], S[4 * p + dm] * gm);
@@ -1396,7 +1391,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             Ot[mt] = Ot[mt] * oscale;
             if (!LAST || 16 * mt + l16 < rows) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) nonfinite |= !__builtin_isfinite(Ot[mt][e]);
+                for (int e = 0; e < 4; ++e) nfacc = __builtin_fmaf(Ot[mt][e], 0.f, nfacc);
                 *reinterpret_cast<f32x4 *>(ob + o_lane + 16 * mt * row_stride) = Ot[mt];
             }
         }
@@ -1416,13 +1411,13 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
                 const float v = poison ? __builtin_nanf("") : S[m][qq];
-                nonfinite |= !__builtin_isfinite(v);
+                nfacc = __builtin_fmaf(v, 0.f, nfacc);
                 s_out[st_off + (size_t)(16 * m + 4 * kg + qq) * D + col] = v;
             }
     }
     // inf / NaN in an output or the state (an fp16 operand out of range, non-finite inputs,
     // or the poisoning above): one report per wave
-    if (__ballot(nonfinite) && lane == 0 && !(COH && sfail)) report_status(status, kStatusNonFinite);
+    if (__ballot(!__builtin_isfinite(nfacc)) && lane == 0 && !(COH && sfail)) report_status(status, kStatusNonFinite);
 }
 
 // ============================================================== host side
