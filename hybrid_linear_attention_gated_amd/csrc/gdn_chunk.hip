@@ -186,12 +186,9 @@ __device__ __forceinline__ Split8 block_operand(bf16x4 hi, bf16x4 lo) {
 }
 __device__ __forceinline__ Split8 neg_split(Split8 s) { return Split8{-s.hi, -s.lo}; }
 __device__ __forceinline__ void split_store(f32x4 x, bf16x4 *hi, bf16x4 *lo) {
+    const float v[4] = {x[0], x[1], x[2], x[3]};
     bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h[i] = (bf16)x[i];
-        l[i] = (bf16)(x[i] - (float)h[i]);
-    }
+    split4(v, &h, &l);
     *hi = h;
     *lo = l;
 }
@@ -337,13 +334,11 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
         if (grp < 2) {
             ss = group_sum<CB>(ss);
             const float rn = rsqrtf(ss + l2_eps);
-            bf16x8 hi, lo;
+            float yn[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float yn = y[e] * rn;
-                hi[e] = (bf16)yn;
-                lo[e] = (bf16)(yn - (float)hi[e]);
-            }
+            for (int e = 0; e < 8; ++e) yn[e] = y[e] * rn;
+            const Split8 sp = split8(yn);
+            const bf16x8 hi = sp.hi, lo = sp.lo;
             bf16 *ph = reinterpret_cast<bf16 *>(smem + (grp == 0 ? SM::QH : SM::KH));
             bf16 *pl = reinterpret_cast<bf16 *>(smem + (grp == 0 ? SM::QL : SM::KL));
             *reinterpret_cast<bf16x8 *>(ph + tl * LD + 8 * cb) = hi;
@@ -551,13 +546,15 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         const bool live = r < L;
         const float kk[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
         const float qq[4] = {qv[i].x, qv[i].y, qv[i].z, qv[i].w};
-        bf16x4 khi, klo, qhi, qlo;
+        float ka4[4], qa4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float a = live ? kk[j] : 0.f, b = live ? qq[j] : 0.f;
-            khi[j] = (bf16)a; klo[j] = (bf16)(a - (float)khi[j]);
-            qhi[j] = (bf16)b; qlo[j] = (bf16)(b - (float)qhi[j]);
+            ka4[j] = live ? kk[j] : 0.f;
+            qa4[j] = live ? qq[j] : 0.f;
         }
+        bf16x4 khi, klo, qhi, qlo;
+        split4(ka4, &khi, &klo);
+        split4(qa4, &qhi, &qlo);
         *reinterpret_cast<bf16x4 *>(Kh + r * LD + c4) = khi;
         *reinterpret_cast<bf16x4 *>(Kl + r * LD + c4) = klo;
         *reinterpret_cast<bf16x4 *>(Qh + r * LD + c4) = qhi;

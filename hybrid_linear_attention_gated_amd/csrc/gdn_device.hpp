@@ -156,15 +156,32 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 struct Split8 {
     bf16x8 hi, lo;
 };
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// hi / lo of two values as packed bf16 pairs: one paired conversion gives both hi, whose
+// fp32 values are the pair's high halves moved up (shift) or masked in place, then one
+// paired conversion of the two remainders.  Same result as converting each value alone.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned &hi, unsigned &lo) {
+    hi = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+    const float h0 = __builtin_bit_cast(float, hi << 16), h1 = __builtin_bit_cast(float, hi & 0xffff0000u);
+    lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{x0 - h0, x1 - h1}, bf16x2));
+}
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ Split8 split8(const float *x) {
-    Split8 r;
+    unsigned h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const bf16 h = (bf16)x[i];
-        r.hi[i] = h;
-        r.lo[i] = (bf16)(x[i] - (float)h);
-    }
-    return r;
+    for (int i = 0; i < 4; ++i) split_pair(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    return Split8{__builtin_bit_cast(bf16x8, u32x4v{h[0], h[1], h[2], h[3]}),
+                  __builtin_bit_cast(bf16x8, u32x4v{l[0], l[1], l[2], l[3]})};
+}
+// hi / lo of four values as packed bf16 quads
+__device__ __forceinline__ void split4(const float *x, bf16x4 *hi, bf16x4 *lo) {
+    unsigned h[2], l[2];
+    split_pair(x[0], x[1], h[0], l[0]);
+    split_pair(x[2], x[3], h[1], l[1]);
+    *hi = __builtin_bit_cast(bf16x4, u32x2{h[0], h[1]});
+    *lo = __builtin_bit_cast(bf16x4, u32x2{l[0], l[1]});
 }
 __device__ __forceinline__ f32x4 mfma16x3(const Split8 &a, const Split8 &b, f32x4 c) {
     c = mfma16(a.lo, b.hi, c);
