@@ -30,15 +30,22 @@ rotate over 3 copies at different addresses and the decode state over 2 sets
 (512 MiB), so no input is served from the 256 MB Infinity Cache; the prefill
 workspace is one buffer reused every step, as a caller reuses it, and its lines
 stay cached from one step to the next (the decode step reads its state with
-non-temporal loads).  After the timed regions, "achievable" records two measured
+non-temporal loads).  "prefill_cold_ms" times the same gdn_prefill call with the
+caches flushed before every call (a 1 GiB buffer read and written in between).
+"kernels" and "roofline" also carry, while the library sources match those of the
+committed counter summary (profiles/counters_layer_4k.txt), each kernel's HBM
+bytes from the L2's memory-fabric request counters ("traffic") and, for the MFMA
+kernels, the MFMA work it executes (split-operand repeats included) over this
+run's time and its MFMA busy fraction under the profiler ("counter_mfma";
+"counter_mfma_frac" / "counter_mfma_busy" in "roofline").  After the timed regions, "achievable" records two measured
 ceilings (a plain streaming kernel's GB/s, the library's bf16 GEMM on 8192^3), and the
 decode and projection figures are also given as fractions of them.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 Profiler runs: --split-only (the split-phase region alone), --metric-only (the
 gdn_prefill + decode region alone, for kernel traces of the concurrent schedule),
---copy-calibration (a 512 MiB streaming copy after the timed steps, for the
-FETCH_SIZE / WRITE_SIZE scaling).
+--copy-calibration (a 512 MiB streaming copy after the timed steps, a check of the
+request-counter bytes against a known stream).
 """
 from __future__ import annotations
 
@@ -214,22 +221,28 @@ def config_records(torch, gdn, inputs, dev, reps=10):
     return recs
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_layer_4k.txt")
+COUNTERS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "counters_layer_4k.txt")
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, per kernel; a
-    kernel's figure is dropped when the library sources changed since."""
+def measured_counters():
+    """Per-kernel figures of the committed counter summary (HBM bytes, MFMA flops executed,
+    MFMA busy fraction per launch): {kernel: {figure: value}}, empty when the library sources
+    changed since the counters were taken."""
     from hybrid_linear_attention_gated_amd import profiling
-    rec = profiling.read_traffic(TRAFFIC_FILE)
+    rec = profiling.read_traffic(COUNTERS_FILE)
     if not rec or rec.get("source_sha256") != profiling.source_sha256():
         return {}
-    return {k[: -len(".traffic_bytes")]: float(v) for k, v in rec.items() if k.endswith(".traffic_bytes")}
+    out = {}
+    for key, val in rec.items():
+        if "." in key and key != "source_sha256":
+            kern, fig = key.split(".", 1)
+            out.setdefault(kern, {})[fig] = float(val)
+    return out
 
 
 def copy_calibration(torch, dev):
-    """A plain streaming copy of known size (torch.neg over 512 MiB) for the
-    FETCH_SIZE / WRITE_SIZE calibration of the counter runs."""
+    """A plain streaming copy of known size (torch.neg over 512 MiB): a check of the
+    request-counter bytes of the counter runs against a known stream."""
     from hybrid_linear_attention_gated_amd import profiling
     n = profiling.COPY_BYTES // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -453,6 +466,7 @@ def main():
              "in_proj", "out_proj"]
     two_call = None
     layer = None
+    prefill_cold_ms = None
     if args.layer_only:
         evs_l, _ = timed(step_layer, 5)
         print(json.dumps({"layer_prefill_ms": mean_ms(evs_l, 0), "layer_decode_ms": mean_ms(evs_l, 1),
@@ -465,6 +479,22 @@ def main():
             print(json.dumps({"prefill_ms": prefill_ms, "decode_ms": decode_ms, "entry_point": "gdn_prefill",
                               "steps": args.steps, "warmup": args.warmup}))
             return
+        # Timed region 1c: the same gdn_prefill with every cache cold.  Before each call a
+        # 1 GiB buffer (four times the Infinity Cache) is read and written, so the call finds
+        # neither its workspace nor its inputs in the Infinity Cache or the L2, as in a model
+        # whose other layers run between two calls of this one.
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+        def step_cold(i, ev):
+            r = i % R
+            flush.neg_()
+            ev[0].record()
+            gdn.prefill(xs[r], cw, gs[r], bs[r], Hk, Hv, d, d, cu_seqlens=cu, conv_state_out=cso, final_state=fin,
+                        o=o, workspace=ws)
+            ev[1].record()
+        evs_cold, _ = timed(step_cold, 2)
+        prefill_cold_ms = mean_ms(evs_cold, 0)
+        del flush
         evs_two, _ = timed(step_two, 3)
         two_prep, two_call_ms = mean_ms(evs_two, 0), mean_ms(evs_two, 1)
         two_call = {"ms": two_prep + two_call_ms, "prep_ms": two_prep, "chunk_prefill_ms": two_call_ms,
@@ -506,14 +536,24 @@ def main():
         "out_proj": {"bound": "mfma", "achieved": out_f / per["out_proj"] / 1e9, "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s"},
     }
-    traffic = measured_traffic()   # HBM bytes per launch from the counter runs, or None
+    counters = measured_counters()   # per-launch counter figures of the committed summary, or {}
     for n in names:
         kern[n]["ms"] = per[n]
         kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
-        kern[n]["traffic"] = traffic.get(PROFILE_NAME.get(n, n))
+        c = counters.get(PROFILE_NAME.get(n, n), {})
+        kern[n]["traffic"] = c.get("traffic_bytes")
+        if kern[n]["bound"] == "mfma" and "mfma_flops" in c:
+            # MFMA work the kernel executes (split-operand repeats and zero padding included)
+            # over this run's time, and the MFMA busy fraction under the profiler
+            kern[n]["counter_mfma"] = {"executed_tflops": c["mfma_flops"] / per[n] / 1e9,
+                                       "frac": c["mfma_flops"] / per[n] / 1e9 / PEAK_MFMA_TFLOPS,
+                                       "busy_frac": c.get("mfma_busy_frac")}
     dominant = max(["chunk_local_fused", "state_pass"], key=lambda n: per[n])   # the metric path's prefill
     roof = {key: kern[dominant][key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
+    if "counter_mfma" in kern[dominant]:
+        roof["counter_mfma_frac"] = kern[dominant]["counter_mfma"]["frac"]
+        roof["counter_mfma_busy"] = kern[dominant]["counter_mfma"]["busy_frac"]
 
     out = {
         "metric": METRIC,
@@ -535,6 +575,7 @@ def main():
                     "tokens_per_s": T / (prefill_ms / 1e3),
                     "algorithmic_tflops": (local_f + state_f) / prefill_ms / 1e9,
                     "frac_mfma": (local_f + state_f) / prefill_ms / 1e9 / PEAK_MFMA_TFLOPS},
+        "prefill_cold_ms": prefill_cold_ms,
         "prefill_two_call": two_call,
         "layer": layer,
         "decode": {"ms": decode_ms, "tokens_per_s": B / (decode_ms / 1e3),

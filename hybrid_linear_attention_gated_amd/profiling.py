@@ -23,6 +23,12 @@
       HBM-side read and write bytes per dispatch from the L2's memory-fabric request
       counters (TCC_EA0_RDREQ_32B/_64B/_128B_sum, TCC_EA0_WRREQ_sum and _64B_sum), and the
       `<kernel>.traffic_bytes` lines bench.py reads.
+  python -m hybrid_linear_attention_gated_amd.profiling summary DIR [DIR ...]
+      per-kernel counter summary of `rocprofv3 --pmc` passes over the same workload: MFMA
+      work executed (SQ_INSTS_VALU_MFMA_MOPS_F16 / _BF16, 512 flops each), MFMA busy
+      fraction (SQ_VALU_MFMA_BUSY_CYCLES over every SIMD's share of GRBM_GUI_ACTIVE), VALU
+      instructions, LDS instructions and bank-conflict cycles, HBM-side bytes as above; then
+      the `<kernel>.<figure> = value` lines bench.py reads and the sources' SHA-256.
 
 Only text is produced; nothing here touches the GPU.
 """
@@ -265,8 +271,61 @@ def main(argv):
                 print(f"{k}.traffic_bytes = {rd + wr:.0f}")
         print(f"source_sha256 = {source_sha256()}")
         return 0
+    if len(argv) >= 2 and argv[0] == "summary":
+        print(summary(*argv[1:]), end="")
+        return 0
     print(__doc__, file=sys.stderr)
     return 2
+
+
+# MI355X: 256 compute units of 4 SIMDs in 8 XCDs.  GRBM_GUI_ACTIVE is counted by every XCD
+# and the per-dispatch value sums them; the MFMA busy counter sums every SIMD.
+N_SIMD, N_XCD = 1024, 8
+MFMA_FLOPS_PER_MOP = 512   # SQ_INSTS_VALU_MFMA_MOPS_* count 512-flop units
+
+
+def summary(*directories: str) -> str:
+    """Counter summary of the library's kernels (text, see the module docstring)."""
+    tab = counter_table(*directories)
+    known = {short for _, short in KERNELS} | set(PROJ_NAMES)
+    rows = []
+    keys = []
+    for k in sorted(tab):
+        if k not in known:
+            continue
+        r = tab[k]
+        rd, wr = request_bytes(r)
+        gui = r.get("GRBM_GUI_ACTIVE")
+        gui_x = gui / N_XCD if gui else None
+        mops = None
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in r or "SQ_INSTS_VALU_MFMA_MOPS_BF16" in r:
+            mops = r.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + r.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        flops = None if mops is None else mops * MFMA_FLOPS_PER_MOP
+        busy = None
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in r and gui_x:
+            busy = r["SQ_VALU_MFMA_BUSY_CYCLES"] / (N_SIMD * gui_x)
+        valu = r.get("SQ_INSTS_VALU")
+        lds = r.get("SQ_INSTS_LDS")
+        conf = r.get("SQ_LDS_BANK_CONFLICT")
+        rows.append((k, gui_x, flops, busy, valu, lds, conf, rd, wr))
+        for name, val in (("gui_cycles_per_xcd", gui_x), ("mfma_flops", flops), ("mfma_busy_frac", busy),
+                          ("valu_insts", valu), ("lds_insts", lds), ("lds_bank_conflict_cycles", conf),
+                          ("read_bytes", rd), ("write_bytes", wr),
+                          ("traffic_bytes", None if rd is None or wr is None else rd + wr)):
+            if val is not None:
+                keys.append(f"{k}.{name} = {val:.6g}" if name.endswith("frac") else f"{k}.{name} = {val:.0f}")
+
+    def f(v, scale=1.0, fmt="{:10.2f}"):
+        return f"{'-':>10s}" if v is None else fmt.format(v / scale)
+    out = [f"{'kernel':22s} {'cycles/XCD':>10s} {'MFMA GF':>10s} {'MFMA busy':>10s} {'VALU k':>10s} "
+           f"{'LDS k':>10s} {'conflict k':>10s} {'read MB':>10s} {'write MB':>10s}"]
+    for k, gui_x, flops, busy, valu, lds, conf, rd, wr in rows:
+        out.append(f"{k:22s} {f(gui_x, 1, '{:10.0f}')} {f(flops, 1e9)} {f(busy, 1, '{:10.4f}')} {f(valu, 1e3, '{:10.1f}')} "
+                   f"{f(lds, 1e3, '{:10.1f}')} {f(conf, 1e3, '{:10.1f}')} {f(rd, 1e6)} {f(wr, 1e6)}")
+    out.append("")
+    out += keys
+    out.append(f"source_sha256 = {source_sha256()}")
+    return "\n".join(out) + "\n"
 
 
 def read_traffic(path: str) -> dict:

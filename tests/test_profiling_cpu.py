@@ -115,3 +115,42 @@ def test_counter_table_and_request_bytes(tmp_path):
     rd, wr = profiling.request_bytes(row)
     assert rd == 32 * 4 + 64 * 8 + 128 * 12
     assert wr == 32 * (40 - 16) + 64 * 16
+
+
+def test_summary_figures_and_bench_reader(tmp_path, monkeypatch):
+    """The counter summary turns MFMA op counts into flops (512 each), the busy counter into
+    a fraction of every SIMD's share of the clock, and the request counts into bytes; the
+    key = value lines it ends with are what bench.py reads back."""
+    fields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    gui = 8 * 1000.0                     # 1000 cycles on each of the 8 XCDs
+    rows = [{"Dispatch_Id": 1, "Kernel_Name": STATE, "Counter_Name": c, "Counter_Value": v}
+            for c, v in (("SQ_INSTS_VALU_MFMA_MOPS_F16", 300.0), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 100.0),
+                         ("SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * 1024 * 1000), ("GRBM_GUI_ACTIVE", gui),
+                         ("SQ_INSTS_VALU", 5000.0), ("TCC_EA0_RDREQ_32B_sum", 0.0),
+                         ("TCC_EA0_RDREQ_64B_sum", 10.0), ("TCC_EA0_RDREQ_128B_sum", 20.0),
+                         ("TCC_EA0_WRREQ_sum", 7.0), ("TCC_EA0_WRREQ_64B_sum", 7.0))]
+    _write(str(tmp_path / "s" / "run_counter_collection.csv"), fields, rows)
+    text = profiling.summary(str(tmp_path / "s"))
+    path = tmp_path / "counters.txt"
+    path.write_text("# header\n" + text)
+    rec = profiling.read_traffic(str(path))
+    assert float(rec["state_pass.mfma_flops"]) == 400 * 512
+    assert float(rec["state_pass.mfma_busy_frac"]) == pytest.approx(0.25)
+    assert float(rec["state_pass.gui_cycles_per_xcd"]) == 1000
+    assert float(rec["state_pass.read_bytes"]) == 64 * 10 + 128 * 20
+    assert float(rec["state_pass.write_bytes"]) == 64 * 7
+    assert float(rec["state_pass.traffic_bytes"]) == 64 * 10 + 128 * 20 + 64 * 7
+    assert rec["source_sha256"] == profiling.source_sha256()
+
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(path))
+    got = bench.measured_counters()
+    assert got["state_pass"]["mfma_flops"] == 400 * 512
+    assert got["state_pass"]["traffic_bytes"] == 64 * 10 + 128 * 20 + 64 * 7
+    # a summary of other sources is ignored
+    path.write_text(text.replace(profiling.source_sha256(), "0" * 64))
+    assert bench.measured_counters() == {}
