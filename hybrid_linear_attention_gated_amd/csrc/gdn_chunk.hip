@@ -712,12 +712,11 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     }
     __syncthreads();
 
-    // ---- fused prep, 16-bit x: stage the next chunk's x rows (its tokens -3 .. 63) in LDS
-    // with direct-to-LDS buffer loads, spread over all waves.  Copy i fills staging bytes
-    // [1 KiB i, 1 KiB (i + 1)); lane l moves 16 bytes of segment (row, group) =
-    // (i * SPI + l / SEGL) / 3.  Rows before the buffer start or past its end read as 0
-    // (they are not used: history rows of a sequence's first chunk come from its conv cache,
-    // rows past its last token are masked).
+    // ---- fused prep, 16-bit x: stage the next chunk's x rows (its tokens -3 .. 63) in LDS,
+    // spread over all waves.  Copy i (1 KiB) fills staging bytes [1 KiB i, 1 KiB (i + 1));
+    // lane l moves 16 bytes of segment (row, group) = (i * SPI + l / SEGL) / 3.  Rows before
+    // the buffer start or past its end read as 0 (they are not used: history rows of a
+    // sequence's first chunk come from its conv cache, rows past its last token are masked).
     // The next chunk of this workgroup: chunk c_ + nslots of the same sequence if it has
     // one, else found by a search.
     const int gn = gc + nslots;
@@ -733,10 +732,8 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         }
     }
     // Eight waves: wave 0 alone solves the diagonal blocks (one wave's 64 lanes cover all
-    // four) and hands them over through LDS with a flag, while waves 1 .. 7 issue the next
-    // chunk's staging copies; a barrier there would make every wave wait for its copies.
+    // four) and hands them over through LDS with a flag, while the other waves go on.
     constexpr bool ONE_SOLVER = NW == 8;
-    constexpr int SW0 = ONE_SOLVER ? 1 : 0;   // first staging wave
     float *scr = reinterpret_cast<float *>(smem + SM::SCR + (ONE_SOLVER ? 0 : wave) * SM::SCR_WAVE);
     if (!ONE_SOLVER || wave == 0) {
         const int c = kg, j = l16;
@@ -764,23 +761,31 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the scratch writes are done
         if (ONE_SOLVER) __hip_atomic_store(&tflag, gc + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    // Staging by registers, not direct-to-LDS loads: after a direct-to-LDS load the compiler
+    // makes the wave's next LDS access wait for it, which would put the load's whole memory
+    // latency in the middle of this chunk.  Plain loads are waited for only where their
+    // registers are read, at the end of this chunk when they are written to LDS.
+    constexpr int XPW = (SM::XCOPIES + NW - 1) / NW;   // 16-byte loads per lane
+    u32x4 xst[STAGE ? XPW : 1];
     if constexpr (STAGE) {
-        if (next_ok && wave >= SW0) {
+        if (next_ok) {
             constexpr int SEGL = 2 * D / 16, SPI = 64 / SEGL;
-            const int tn = sbn + cn * kChunk;
+            // wave-uniform (scalar) so that the buffer resource is one scalar descriptor
+            const int tn = __builtin_amdgcn_readfirstlane(sbn + cn * kChunk);
             const int rb = max(tn - kConvHist, 0);
             const long bytes = (long)(Ttot - rb) * conv_dim * 2;
             const __amdgpu_buffer_rsrc_t rx =
                 make_rsrc(x + (size_t)rb * conv_dim, (int)min(bytes, (long)0x7ffffff0));
-            for (int i = wave - SW0; i < SM::XCOPIES; i += NW - SW0) {
-                const int sg = i * SPI + lane / SEGL;
-                const int r = min(sg / 3, SM::XROWS - 1), gi = sg % 3;
-                const int chb = gi == 0 ? kh * D : gi == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D;
-                const int voff = ((tn - kConvHist + r - rb) * conv_dim + chb) * 2 + 16 * (lane % SEGL);
-                char *dst = i * 1024 < SM::XRA * SM::XROW ? smem + SM::XA + i * 1024
-                                                          : smem + SM::XB + (i * 1024 - SM::XRA * SM::XROW);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst, 16,
-                                                         voff, 0, 0, 0);
+#pragma unroll
+            for (int k = 0; k < XPW; ++k) {
+                const int i = wave + k * NW;
+                if (i < SM::XCOPIES) {
+                    const int sg = i * SPI + lane / SEGL;
+                    const int r = min(sg / 3, SM::XROWS - 1), gi = sg % 3;
+                    const int chb = gi == 0 ? kh * D : gi == 1 ? (Hk + kh) * D : 2 * Hk * D + h * D;
+                    const int voff = ((tn - kConvHist + r - rb) * conv_dim + chb) * 2 + 16 * (lane % SEGL);
+                    xst[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, 0, 0);
+                }
             }
         }
     }
@@ -873,7 +878,6 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
         run_chain(3 - wave);
         run_chain(4 + wave);
     }
-    if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(0);   // this wave's staging copies have landed
     __syncthreads();
 
     // ---- 4. the four products.  Row fragment (tt, ks) of a published set: lane row
@@ -962,6 +966,21 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
             for (int ni = 0; ni < 2; ++ni)
                 rec_store16(rec, R::O_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 16, acc3_sum(x[ni]),
                             flags != nullptr);
+        }
+    }
+    // the next chunk's x rows into the staging area (copy i fills staging bytes [1 KiB i,
+    // 1 KiB (i + 1)), lane l the 16 bytes at 16 l)
+    if constexpr (STAGE) {
+        if (next_ok) {
+#pragma unroll
+            for (int k = 0; k < XPW; ++k) {
+                const int i = wave + k * NW;
+                if (i < SM::XCOPIES) {
+                    char *dst = i * 1024 < SM::XRA * SM::XROW ? smem + SM::XA + i * 1024
+                                                              : smem + SM::XB + (i * 1024 - SM::XRA * SM::XROW);
+                    *reinterpret_cast<u32x4 *>(dst + 16 * lane) = xst[k];
+                }
+            }
         }
     }
     // Publishing (a state pass runs concurrently and waits for each record): the record
