@@ -1159,7 +1159,9 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
         const int half = (wave - 2) * (ABYTES / 2);
         auto stage = [&](int c, char *dst) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(c), R::SIZE);
-            copy_to_lds<COH ? kCohAux : 0>(r, half, dst + half, ABYTES / 2, lane);
+            // the NP workgroups of a head copy the same record at the same time: each starts
+            // at its own NP-th of the half, so that at any moment they read different lines
+            copy_to_lds<COH ? kCohAux : 0>(r, half, dst + half, ABYTES / 2, lane, pair * (ABYTES / 2 / 1024 / NP));
         };
         // With `flags`, the records are written by a chunk-local kernel running at the same
         // time: wait (bounded) until chunk c's record is published; every record load is then
