@@ -229,10 +229,11 @@ struct LocalSmem {
     static constexpr int SIZE = SCAL + 6 * 64 * 4;
     static_assert(NW * SCR_WAVE <= 4 * PLANE, "solve scratch fits in the planes");
     // Fused prep with a 16-bit x: the next chunk's x rows (tokens -3 .. 63, the q, k and v
-    // channel groups of D each) are staged by direct-to-LDS loads while this chunk is
-    // solved.  Staged row r is XROW contiguous bytes [q | k | v]; rows 0 .. XRA - 1 sit in
-    // the plane region past the solve scratch (free from the tile phase on), the rest past
-    // SIZE.  XRA * XROW is a whole number of 1 KiB copies, so no copy straddles the two.
+    // channel groups of D each) are loaded into registers while this chunk is solved and
+    // written to a staging area at its end.  Staged row r is XROW contiguous bytes
+    // [q | k | v]; rows 0 .. XRA - 1 sit in the plane region past the solve scratch (free
+    // from the tile phase on), the rest past SIZE.  XRA * XROW is a whole number of 1 KiB
+    // copies, so no copy straddles the two.
     static constexpr int XROW = 3 * D * 2;
     static constexpr int XROWS = kChunk + kConvHist;
     static constexpr int XA = NW * SCR_WAVE;
@@ -363,8 +364,9 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 //  1. K K^T and K Q^T tiles with key block b as the A operand -> A (strict lower)
 //     and P^T, scaled by the decays.  K K^T is symmetric, so A's accumulator tile
 //     (k, c) is also the A-operand form of A^T block (c, k).
-//  2. Every wave solves the four 16 x 16 diagonal blocks T_cc by forward
-//     substitution (lane (c, j) owns column j of block c), so no barrier.
+//  2. The four 16 x 16 diagonal blocks T_cc by forward substitution (lane (c, j)
+//     owns column j of block c): with eight waves wave 0 solves them and hands them
+//     to the others through LDS with a flag (no barrier); with four, every wave.
 //  3. Block back substitution of (I + A^T) X = [I | P^T] gives T^T and M^T in
 //     accumulator layout, one column block per chain; the blocks are published
 //     with the scalings above folded in.
@@ -1030,10 +1032,11 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int src_of
 // wave keeps too few requests in flight to stream a record at memory latency,
 // and a wave with direct-to-LDS loads in flight cannot wait on its own LDS reads
 // precisely.  The compute waves prefetch their strip's U and Ol tiles one chunk
-// ahead into registers and read fragments from LDS in groups; the reads of group
-// g + 1 are issued right after the first MFMA of group g, and each group runs
-// four independent MFMA chains (a dependent MFMA waits ~44 cycles, one issues
-// every 16).
+// ahead into registers and read fragments from LDS in groups of 16; the next group's
+// reads are issued right after the first MFMAs of the current one, and every group
+// runs four independent MFMA chains (a dependent MFMA waits ~44 cycles, one issues
+// every 16).  Delta' of all four row tiles comes first, then the outputs, so that the
+// split of Delta' into bf16 hi / lo runs among the output MFMAs.
 // Bound on the state pass's wait for a published record (iterations of a ~128-cycle
 // sleep, about a second).  A wait that runs out marks the call failed: the status word
 // of the workspace reports GDN_ERR_TIMEOUT and the outputs of the chunks not yet done and
