@@ -5,10 +5,9 @@ One step = one pass of the whole hot path over one batch of seeded synthetic
 input:
   prefill of one linear-attention layer of the 0.8B hybrid shape
   (T = 4096 tokens, 16 key / 16 value heads, head dims 128, bf16 pre-conv x):
-      gdn_prefill (one call: conv + SiLU + L2 inside the chunk-local kernel,
-      which runs on the library's second stream while the state pass, on the
-      caller's stream, consumes each chunk's record as soon as it is published;
-      q, k, v never reach HBM)
+      gdn_prefill (one call, one launch: conv + SiLU + L2 inside the chunk-local
+      workgroups, while the same launch's state-pass workgroups consume each
+      chunk's record as soon as it is published; q, k, v never reach HBM)
   followed by one decode step of 256 sequences (gdn_decode_step, fp32 state in place).
 
 Reported beside it (not part of `value`): the whole linear-attention layer at the
@@ -23,9 +22,12 @@ as tokens/s and state GB/s.  A second timed region runs the same prefill as
 gdn_conv_qk_prep + gdn_chunk_prefill (reported under "prefill_two_call"), and a
 third through the split-phase entry points so that every kernel sits alone
 between two HIP events on the stream it is launched on; those per-kernel
-durations give "kernels" and "roofline" (the split region also times the gated
-RMSNorm epilogue, gdn_gated_rmsnorm, on the prefill output, and the layer's input and
-output projections, gdn_in_proj and gdn_linear).  x, g and beta
+durations give "kernels" (the split region also times the gated RMSNorm epilogue,
+gdn_gated_rmsnorm, on the prefill output, and the layer's input and output
+projections, gdn_in_proj and gdn_linear).  At this shape gdn_prefill is one launch
+(prefill_concurrent_kernel: the chunk-local workgroups and the state pass's in one
+grid), so the first region's events time that kernel: it is "roofline" (the whole
+prefill's algorithmic flops over its duration) and kernels["prefill_concurrent"].  x, g and beta
 rotate over 3 copies at different addresses and the decode state over 2 sets
 (512 MiB), so no input is served from the 256 MB Infinity Cache; the prefill
 workspace is one buffer reused every step, as a caller reuses it, and its lines
@@ -42,8 +44,8 @@ ceilings (a plain streaming kernel's GB/s, the library's bf16 GEMM on 8192^3), a
 decode and projection figures are also given as fractions of them.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-Profiler runs: --split-only (the split-phase region alone), --metric-only (the
-gdn_prefill + decode region alone, for kernel traces of the concurrent schedule),
+Profiler runs: --split-only (the metric's region and the split-phase region),
+--metric-only (the gdn_prefill + decode region alone),
 --copy-calibration (a 512 MiB streaming copy after the timed steps, a check of the
 request-counter bytes against a known stream).
 """
@@ -295,7 +297,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration records (tiny_f32, varlen8, long_64k) and the parity checks")
     ap.add_argument("--split-only", action="store_true",
-                    help="time only the split-phase region (one launch per kernel per step), for profiler runs")
+                    help="time only the metric's region and the split-phase region (one launch per kernel per "
+                         "step), for profiler runs")
     ap.add_argument("--metric-only", action="store_true",
                     help="time only the metric's region (gdn_prefill + decode step) and print its two times, "
                          "for kernel-trace runs of the concurrent prefill schedule")
@@ -472,13 +475,13 @@ def main():
         print(json.dumps({"layer_prefill_ms": mean_ms(evs_l, 0), "layer_decode_ms": mean_ms(evs_l, 1),
                           "steps": args.steps, "warmup": args.warmup}))
         return
+    evs, wall = timed(step, 3)
+    prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)
+    if args.metric_only:
+        print(json.dumps({"prefill_ms": prefill_ms, "decode_ms": decode_ms, "entry_point": "gdn_prefill",
+                          "steps": args.steps, "warmup": args.warmup}))
+        return
     if not args.split_only:
-        evs, wall = timed(step, 3)
-        prefill_ms, decode_ms = mean_ms(evs, 0), mean_ms(evs, 1)
-        if args.metric_only:
-            print(json.dumps({"prefill_ms": prefill_ms, "decode_ms": decode_ms, "entry_point": "gdn_prefill",
-                              "steps": args.steps, "warmup": args.warmup}))
-            return
         # Timed region 1c: the same gdn_prefill with every cache cold.  Before each call a
         # 1 GiB buffer (four times the Infinity Cache) is read and written, so the call finds
         # neither its workspace nor its inputs in the Infinity Cache or the L2, as in a model
@@ -506,12 +509,11 @@ def main():
                  "prefill_ms": lp, "prefill_tokens_per_s": T / (lp / 1e3),
                  "decode_ms": ld, "decode_tokens_per_s": B / (ld / 1e3),
                  "library_gemm_ms": {"in_proj": gi, "out_proj": go}}
-    evs2, wall2 = timed(step_split, 10)
+    evs2, _ = timed(step_split, 10)
     per = {n: mean_ms(evs2, j) for j, n in enumerate(names)}   # ms per launch (split phases)
-    if args.split_only:   # profiler runs: the metric falls back to the split-phase prefill
-        wall = wall2
-        prefill_ms = per["chunk_local_fused"] + per["state_pass"]
-        decode_ms = per["decode"]
+    # gdn_prefill at this shape is one launch (prefill_concurrent_kernel: the chunk-local
+    # workgroups and the state pass's), so the metric region's events time that kernel
+    per["prefill_concurrent"] = prefill_ms
 
     prep_b, local_f, state_f, dec_b = algorithmic_counts(T, Hk, Hv, d, 64, N, B)
     norm_b = T * Hv * d * (4 + 2 + 2) + d * 2   # y fp32 in, z bf16 in, out bf16, gain
@@ -519,6 +521,8 @@ def main():
     in_f = 2 * T * E * w_in.shape[0]    # input projection: T x E times E x (conv_dim + Hv dv + 2 Hv)
     out_f = 2 * T * Z * E               # output projection: T x Hv dv times Hv dv x E
     kern = {
+        "prefill_concurrent": {"bound": "mfma", "achieved": (local_f + state_f) / per["prefill_concurrent"] / 1e9,
+                               "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
         "chunk_local_fused": {"bound": "mfma", "achieved": local_f / per["chunk_local_fused"] / 1e9,
                               "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s"},
         "prep": {"bound": "hbm", "achieved": prep_b / per["prep"] / 1e6, "peak": PEAK_HBM_GBS, "unit": "GB/s"},
@@ -537,7 +541,7 @@ def main():
                      "unit": "TFLOP/s"},
     }
     counters = measured_counters()   # per-launch counter figures of the committed summary, or {}
-    for n in names:
+    for n in ["prefill_concurrent"] + names:
         kern[n]["ms"] = per[n]
         kern[n]["frac"] = kern[n]["achieved"] / kern[n]["peak"]
         c = counters.get(PROFILE_NAME.get(n, n), {})
@@ -548,7 +552,7 @@ def main():
             kern[n]["counter_mfma"] = {"executed_tflops": c["mfma_flops"] / per[n] / 1e9,
                                        "frac": c["mfma_flops"] / per[n] / 1e9 / PEAK_MFMA_TFLOPS,
                                        "busy_frac": c.get("mfma_busy_frac")}
-    dominant = max(["chunk_local_fused", "state_pass"], key=lambda n: per[n])   # the metric path's prefill
+    dominant = "prefill_concurrent"   # the metric path's prefill: one launch
     roof = {key: kern[dominant][key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dominant
     if "counter_mfma" in kern[dominant]:
@@ -571,7 +575,7 @@ def main():
         "config": {"workload": "layer_4k prefill (T=4096, Hk=Hv=16, dk=dv=128, chunk 64, bf16 x, fp32 q/k/v/o) "
                                "+ decode256 step (B=256, fp32 state 256 MiB, 2 rotating state sets)",
                    "T": T, "heads_k": Hk, "heads_v": Hv, "head_dim": d, "chunk": 64, "decode_batch": B},
-        "prefill": {"ms": prefill_ms, "entry_point": "gdn_prefill" if not args.split_only else "split phases",
+        "prefill": {"ms": prefill_ms, "entry_point": "gdn_prefill",
                     "tokens_per_s": T / (prefill_ms / 1e3),
                     "algorithmic_tflops": (local_f + state_f) / prefill_ms / 1e9,
                     "frac_mfma": (local_f + state_f) / prefill_ms / 1e9 / PEAK_MFMA_TFLOPS},

@@ -389,13 +389,35 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 typedef unsigned long long flag_t;
 constexpr unsigned kFlagTag = 0x9e3779b9u;
 
-template <int D, bool FUSED, typename TX, typename TW = TX>
-__global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
-    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu, int N,
-    int Ttot, int Hk, int Hv, float scale, char *__restrict__ ws, int ncmax, int g0, int g1, int nslots,
-    const TX *__restrict__ x, const TW *__restrict__ conv_w, const TX *__restrict__ cs_in, float l2_eps,
-    int order, flag_t *flags, flag_t flag_val) {
+// LDS of the chunk-local kernel
+template <int D, typename TX, bool FUSED>
+constexpr int local_lds_bytes() {
+    return FUSED && sizeof(TX) == 2 ? LocalSmem<D>::SIZE_STAGED : LocalSmem<D>::SIZE;
+}
+
+// Arguments of the chunk-local kernel (one struct, shared with the combined kernel of the
+// concurrent schedule).
+template <typename TX, typename TW>
+struct LocalArgs {
+    const float *q, *k, *v, *g, *beta;
+    const int32_t *cu;
+    int N, Ttot, Hk, Hv;
+    float scale;
+    char *ws;
+    int ncmax, g0, g1, nslots;
+    const TX *x;
+    const TW *conv_w;
+    const TX *cs_in;
+    float l2_eps;
+    int order;
+    flag_t *flags;
+    flag_t flag_val;
+};
+
+// The chunk-local work of workgroup (slot, value head h): smem is the workgroup's LDS
+// (local_lds_bytes), tflag_ one LDS word.
+template <int D, bool FUSED, typename TX, typename TW>
+__device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int slot, int h, const LocalArgs<TX, TW> &P) {
     using R = Rec<D>;
     using SM = LocalSmem<D>;
     constexpr bool STAGE = FUSED && sizeof(TX) == 2;
@@ -403,8 +425,19 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     constexpr int NKS = D / 32;   // 32-wide k steps over the head dim
     constexpr int LD = SM::LD;
     constexpr int NF_K = (D / 16) * 2;
-    __shared__ __attribute__((aligned(16))) char smem[STAGE ? SM::SIZE_STAGED : SM::SIZE];
-    __shared__ int tflag;   // diagonal blocks of the current chunk published (value: chunk + 1)
+    const float *__restrict__ q = P.q, *__restrict__ k = P.k, *__restrict__ v = P.v;
+    const float *__restrict__ g = P.g, *__restrict__ beta = P.beta;
+    const int32_t *__restrict__ cu = P.cu;
+    const int N = P.N, Ttot = P.Ttot, Hk = P.Hk, Hv = P.Hv, ncmax = P.ncmax, g0 = P.g0, g1 = P.g1;
+    const int nslots = P.nslots, order = P.order;
+    const float scale = P.scale, l2_eps = P.l2_eps;
+    char *__restrict__ ws = P.ws;
+    const TX *__restrict__ x = P.x;
+    const TW *__restrict__ conv_w = P.conv_w;
+    const TX *__restrict__ cs_in = P.cs_in;
+    flag_t *flags = P.flags;
+    const flag_t flag_val = P.flag_val;
+    int &tflag = *tflag_;   // diagonal blocks of the current chunk published (value: chunk + 1)
     if (threadIdx.x == 0) tflag = -1;   // seen by every wave after the chunk loop's first barrier
     bf16 *Kh = reinterpret_cast<bf16 *>(smem + SM::KH);
     bf16 *Kl = reinterpret_cast<bf16 *>(smem + SM::KL);
@@ -418,7 +451,6 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     float *Bs = Gs + 64, *BEG = Gs + 128, *DCs = Gs + 192, *QS = Gs + 256, *GRs = Gs + 320;
     enum { XT_TW = 0, XT_TU = 1, XT_MW = 2, XT_MU = 3 };   // published operand sets
 
-    const int h = blockIdx.y;   // value head
     const int kh = h / (Hv / Hk);
     const int conv_dim = 2 * Hk * D + Hv * D;
 
@@ -441,7 +473,7 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) cwt[j][i] = cl.active ? to_f32(conv_w[(size_t)(cl.ch0 + i) * kConvK + j]) : 0.f;
     }
-    for (int gc = g0 + blockIdx.x; gc < g1; gc += nslots) {
+    for (int gc = g0 + slot; gc < g1; gc += nslots) {
     // The thread index passes through an empty asm each iteration, so nothing derived from
     // it is hoisted out of the loop and kept live across it (that costs registers the
     // chunk's own work needs).
@@ -1002,6 +1034,13 @@ __global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(
     }
 }
 
+template <int D, bool FUSED, typename TX, typename TW = TX>
+__global__ __launch_bounds__(LocalShape<D>::THREADS) void chunk_local_kernel(LocalArgs<TX, TW> P) {
+    __shared__ __attribute__((aligned(16))) char smem[local_lds_bytes<D, TX, FUSED>()];
+    __shared__ int tflag;
+    chunk_local_body<D, FUSED, TX, TW>(smem, &tflag, blockIdx.x, blockIdx.y, P);
+}
+
 // ============================================================== state pass
 
 // Copy `bytes` (a multiple of 1 KiB) at byte `src_off` of the buffer to LDS:
@@ -1107,19 +1146,44 @@ __device__ __forceinline__ int seq_by_rank(const int32_t *cu, int N, int Ttot, i
 // COH: records come from a concurrently running chunk-local kernel (wait for each chunk's
 // flag, read device-coherently; the conv cache of the fused prefill is written here, see
 // ConvOut); otherwise plain cached reads.
+template <int D>
+constexpr int state_lds_bytes() { return 2 * Rec<D>::U_OFF; }
+
+struct StateArgs {
+    const char *ws;
+    const int32_t *cu;
+    int Ttot, Hv, units;
+    const float *s0;
+    float *sf, *o;
+    int ncmax, g0, g1;
+    float *mid;
+    const flag_t *flags;
+    flag_t flag_val;
+    ConvOut cv;
+    unsigned long long *status;
+};
+
+// The state pass of workgroup b (waves 0 .. 3 of the workgroup; further waves only take the
+// barriers): lds is the workgroup's LDS (state_lds_bytes), sfail_ one LDS word.
 template <int D, bool COH>
-__global__ __launch_bounds__(256) void state_pass_kernel(
-    const char *__restrict__ ws, const int32_t *__restrict__ cu, int Ttot, int Hv, int units,
-    const float *s0, float *sf, float *__restrict__ o, int ncmax, int g0, int g1, float *mid, const flag_t *flags,
-    flag_t flag_val, ConvOut cv, unsigned long long *status) {
+__device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, const StateArgs &P) {
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
     static_assert(ABYTES % 2048 == 0, "copy granularity");
-    __shared__ __attribute__((aligned(16))) char abuf[2][ABYTES];
+    const char *__restrict__ ws = P.ws;
+    const int32_t *__restrict__ cu = P.cu;
+    const int Ttot = P.Ttot, Hv = P.Hv, units = P.units, ncmax = P.ncmax, g0 = P.g0, g1 = P.g1;
+    const float *s0 = P.s0;
+    float *sf = P.sf, *__restrict__ o = P.o, *mid = P.mid;
+    const flag_t *flags = P.flags;
+    const flag_t flag_val = P.flag_val;
+    const ConvOut &cv = P.cv;
+    unsigned long long *status = P.status;
+    // the two A-operand buffers: lds and lds + ABYTES
+    auto abuf = [lds](int i) { return lds + (i & 1) * ABYTES; };
 
     // block -> (unit, strip pair) so that the NP blocks of one unit land on the same XCD
-    const int b = blockIdx.x;
     const int u = 8 * (b / (8 * NP)) + (b % 8);
     const int pair = (b / 8) % NP;
     if (u >= units) return;
@@ -1151,10 +1215,17 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     float *s_out = c_hi == nc ? sf : mid;
     // set by a copy wave whose wait for a record ran out; read by the compute waves after
     // every chunk barrier
-    __shared__ int sfail;
+    int &sfail = *sfail_;
     if (threadIdx.x == 0) sfail = 0;
     __syncthreads();
 
+    if (wave >= 4) {
+        // waves past the state pass's four (eight-wave workgroups of the combined kernel): they
+        // take the same barriers as the copy waves and nothing else
+        __syncthreads();
+        for (int c = c_lo; c < c_hi; ++c) __syncthreads();
+        return;
+    }
     if (copier) {
         // Each copy wave moves half of the A operands with direct-to-LDS buffer loads
         // (lane l of each 16-byte load lands at base + 16 l), then waits for them before
@@ -1195,7 +1266,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             if (c_lo < c_hi) ready(c_lo);
             if (c_lo + 1 < c_hi) ready(c_lo + 1);
         }
-        if (c_lo < c_hi) stage(c_lo, abuf[c_lo & 1]);
+        if (c_lo < c_hi) stage(c_lo, abuf(c_lo));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         for (int c = c_lo; c < c_hi; ++c) {
@@ -1207,7 +1278,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
             if constexpr (COH)
                 published = __hip_atomic_load(flags + (size_t)h * ncmax + gbase + (c + 2 < c_hi ? c + 2 : c),
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (c + 1 < c_hi) stage(c + 1, abuf[(c + 1) & 1]);
+            if (c + 1 < c_hi) stage(c + 1, abuf(c + 1));
             if constexpr (COH) {
                 asm volatile("" : "+v"(published));
                 if (c + 2 < c_hi && published != flag_val) ready(c + 2);
@@ -1325,7 +1396,7 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     // instead of for every outstanding access.
     auto chunk_step = [&](int c, auto last_tag) {
         constexpr bool LAST = decltype(last_tag)::value;
-        const char *A = abuf[c & 1];
+        const char *A = abuf(c);
         f32x4 Un[4], On[4];
         float gn = 0.f;
         if constexpr (!LAST) load_strip(rec_of(c + 1), Un, On, gn);
@@ -1441,6 +1512,35 @@ __global__ __launch_bounds__(256) void state_pass_kernel(
     if (__ballot(!__builtin_isfinite(nfacc)) && lane == 0 && !(COH && sfail)) report_status(status, kStatusNonFinite);
 }
 
+template <int D, bool COH>
+__global__ __launch_bounds__(256) void state_pass_kernel(StateArgs P) {
+    __shared__ __attribute__((aligned(16))) char lds[state_lds_bytes<D>()];
+    __shared__ int sfail;
+    state_pass_body<D, COH>(lds, &sfail, blockIdx.x, P);
+}
+
+// The concurrent schedule in one launch.  Workgroups [0, nslots * Hv) run the chunk-local
+// kernel, persistent as (slot, head) = (block mod nslots, block / nslots), and publish each
+// record with a flag; workgroups [soff, soff + state blocks) run the state pass (waves 0 .. 3;
+// with eight-wave workgroups the other four only take its barriers) and wait for the flags;
+// the workgroups in between (to make soff a multiple of 8, so that block - soff and block
+// fall on the same XCD) end at once.
+// Workgroups are dispatched in index order, so a state-pass workgroup starts only once every
+// producer has been dispatched, and producers never wait: every wait ends.
+template <int D, bool FUSED, typename TX, typename TW>
+__global__ __launch_bounds__(LocalShape<D>::THREADS) void prefill_concurrent_kernel(LocalArgs<TX, TW> PL,
+                                                                                    StateArgs PS, int soff) {
+    constexpr int LB = local_lds_bytes<D, TX, FUSED>(), SB = state_lds_bytes<D>();
+    __shared__ __attribute__((aligned(16))) char lds[LB > SB ? LB : SB];
+    __shared__ int word;
+    const int b = blockIdx.x;
+    if (b >= soff) {
+        state_pass_body<D, true>(lds, &word, b - soff, PS);
+    } else if (b < PL.nslots * PL.Hv) {
+        chunk_local_body<D, FUSED, TX, TW>(lds, &word, b % PL.nslots, b / PL.nslots, PL);
+    }
+}
+
 // ============================================================== host side
 
 bool chunked_supported(int dk, int dv) { return dk == dv && (dk == 64 || dk == 128); }
@@ -1501,10 +1601,11 @@ static int pipeline_segments(int nc, int state_blocks) {
 struct PipeRes {
     hipStream_t side = nullptr;
     hipEvent_t ev[kMaxSegments + 1] = {};
-    // end of the last concurrent-schedule chunk-local kernel and the caller stream of its call
-    hipEvent_t local_done = nullptr;
+    // the caller stream of the last concurrent-schedule call; once calls came from more than
+    // one stream (multi), the end of each call's combined kernel
+    hipEvent_t last_done = nullptr;
     hipStream_t last_stream = nullptr;
-    bool has_last = false;
+    bool has_last = false, multi = false;
     std::mutex mu;   // one concurrent-schedule launch sequence at a time
     unsigned epoch = 0;   // concurrent-schedule calls so far: the low word of their flag value
     bool ready = false;
@@ -1526,7 +1627,7 @@ static hipError_t pipe_resources(PipeRes **out) {
             e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
             if (e != hipSuccess) return e;
         }
-        e = hipEventCreateWithFlags(&r.local_done, hipEventDisableTiming);
+        e = hipEventCreateWithFlags(&r.last_done, hipEventDisableTiming);
         if (e != hipSuccess) return e;
         r.ready = true;
     }
@@ -1534,33 +1635,49 @@ static hipError_t pipe_resources(PipeRes **out) {
     return hipSuccess;
 }
 
+// chunk-local workgroups per value head: one per compute unit of the budget (each holds most
+// of the LDS), looping over chunks
+static int local_slots(int cus, int nchunks, int Hv) {
+    return std::max(1, std::min(nchunks, (cus > 0 ? cus : 256) / Hv));
+}
+
+template <typename TX, typename TW>
+static LocalArgs<TX, TW> local_args(const PrefillArgs &a, int nc, int g0, int g1, int nslots, flag_t *flags,
+                                    flag_t flag_val) {
+    LocalArgs<TX, TW> P;
+    P.q = a.q; P.k = a.k; P.v = a.v; P.g = a.g; P.beta = a.beta;
+    P.cu = a.cu;
+    P.N = a.N; P.Ttot = a.T; P.Hk = a.Hk; P.Hv = a.Hv;
+    P.scale = a.scale;
+    P.ws = (char *)a.ws + kWsHeader;
+    P.ncmax = nc; P.g0 = g0; P.g1 = g1; P.nslots = nslots;
+    P.x = a.fp ? (const TX *)a.fp->x : nullptr;
+    P.conv_w = a.fp ? (const TW *)a.fp->w : nullptr;
+    P.cs_in = a.fp ? (const TX *)a.fp->cs_in : nullptr;
+    P.l2_eps = a.fp ? a.fp->eps : 0.f;
+    P.order = a.order;
+    P.flags = flags;
+    P.flag_val = flag_val;
+    return P;
+}
+
 template <int D>
-static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1, int cu_budget = 0,
-                               flag_t *flags = nullptr, flag_t flag_val = 0) {
+static hipError_t launch_local(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1) {
     if (g1 <= g0 || a.T <= 0) return hipSuccess;
-    // one workgroup per compute unit (each holds most of the LDS), looping over chunks;
-    // cu_budget > 0 leaves the other compute units to a concurrent state pass
-    const int cus = cu_budget > 0 ? cu_budget : device_cus();
-    const int nslots = std::max(1, std::min(g1 - g0, (cus > 0 ? cus : 256) / a.Hv));
+    const int nslots = local_slots(device_cus(), g1 - g0, a.Hv);
     const dim3 grid((unsigned)nslots, a.Hv), block(LocalShape<D>::THREADS);
-    char *ws = (char *)a.ws + kWsHeader;
     if (!a.fp) {
-        hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)nullptr,
-                           (const float *)nullptr, (const float *)nullptr, 0.f, a.order, flags, flag_val);
+        hipLaunchKernelGGL((chunk_local_kernel<D, false, float>), grid, block, 0, st,
+                           local_args<float, float>(a, nc, g0, g1, nslots, nullptr, 0));
     } else if (a.fp->bf16) {
-        hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const bf16 *)a.fp->x,
-                           (const bf16 *)a.fp->w, (const bf16 *)a.fp->cs_in, a.fp->eps, a.order, flags, flag_val);
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, bf16>), grid, block, 0, st,
+                           local_args<bf16, bf16>(a, nc, g0, g1, nslots, nullptr, 0));
     } else if (a.fp->w_bf16) {   // fp32 x and caches, bf16 conv weights (the layer's prefill)
-        hipLaunchKernelGGL((chunk_local_kernel<D, true, float, bf16>), grid, block, 0, st, a.q, a.k, a.v, a.g,
-                           a.beta, a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots,
-                           (const float *)a.fp->x, (const bf16 *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps,
-                           a.order, flags, flag_val);
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, float, bf16>), grid, block, 0, st,
+                           local_args<float, bf16>(a, nc, g0, g1, nslots, nullptr, 0));
     } else {
-        hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st, a.q, a.k, a.v, a.g, a.beta,
-                           a.cu, a.N, a.T, a.Hk, a.Hv, a.scale, ws, nc, g0, g1, nslots, (const float *)a.fp->x,
-                           (const float *)a.fp->w, (const float *)a.fp->cs_in, a.fp->eps, a.order, flags, flag_val);
+        hipLaunchKernelGGL((chunk_local_kernel<D, true, float>), grid, block, 0, st,
+                           local_args<float, float>(a, nc, g0, g1, nslots, nullptr, 0));
     }
     return hipGetLastError();
 }
@@ -1569,43 +1686,78 @@ template <int D>
 static int state_blocks(int units) { return 8 * (D / 32) * ((units + 7) / 8); }
 
 template <int D>
+static StateArgs state_args(const PrefillArgs &a, int nc, int g0, int g1, const flag_t *flags, flag_t flag_val,
+                            const ConvOut &cv) {
+    StateArgs P;
+    P.ws = (const char *)a.ws + kWsHeader;
+    P.cu = a.cu;
+    P.Ttot = a.T; P.Hv = a.Hv; P.units = a.N * a.Hv;
+    P.s0 = a.s0; P.sf = a.sf; P.o = a.o;
+    P.ncmax = nc; P.g0 = g0; P.g1 = g1;
+    P.mid = reinterpret_cast<float *>((char *)a.ws + kWsHeader + mid_offset(nc, a.Hv, D));
+    P.flags = flags;
+    P.flag_val = flag_val;
+    P.cv = flags ? cv : ConvOut{};
+    P.status = reinterpret_cast<unsigned long long *>(a.ws);
+    return P;
+}
+
+template <int D>
 static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int g0, int g1,
                                const flag_t *flags = nullptr, flag_t flag_val = 0,
                                const ConvOut &cv = ConvOut{}) {
     const int units = a.N * a.Hv;
     if (units <= 0) return hipSuccess;
     const int blocks = state_blocks<D>(units);
-    const char *recs = (const char *)a.ws + kWsHeader;
-    float *mid = reinterpret_cast<float *>((char *)a.ws + kWsHeader + mid_offset(nc, a.Hv, D));
-    unsigned long long *hdr = reinterpret_cast<unsigned long long *>(a.ws);
+    const StateArgs P = state_args<D>(a, nc, g0, g1, flags, flag_val, cv);
     if (flags)
-        hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, recs, a.cu, a.T, a.Hv, units,
-                           a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, cv, hdr);
+        hipLaunchKernelGGL((state_pass_kernel<D, true>), dim3(blocks), dim3(256), 0, st, P);
     else
-        hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, recs, a.cu, a.T, a.Hv, units,
-                           a.s0, a.sf, a.o, nc, g0, g1, mid, flags, flag_val, ConvOut{}, hdr);
+        hipLaunchKernelGGL((state_pass_kernel<D, false>), dim3(blocks), dim3(256), 0, st, P);
+    return hipGetLastError();
+}
+
+// The combined kernel of the concurrent schedule on `st`: the chunk-local workgroups on the
+// compute units the state pass leaves, then the state pass's.
+template <int D>
+static hipError_t launch_concurrent(const PrefillArgs &a, hipStream_t st, int nc, int cus, int sblocks,
+                                    flag_t *flags, flag_t flag_val, const ConvOut &cv) {
+    const int nslots = local_slots(cus - sblocks, nc, a.Hv);
+    const int soff = (nslots * a.Hv + 7) / 8 * 8;
+    const dim3 grid((unsigned)(soff + sblocks)), block(LocalShape<D>::THREADS);
+    const StateArgs PS = state_args<D>(a, nc, 0, nc, flags, flag_val, cv);
+    if (!a.fp) {
+        hipLaunchKernelGGL((prefill_concurrent_kernel<D, false, float, float>), grid, block, 0, st,
+                           local_args<float, float>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
+    } else if (a.fp->bf16) {
+        hipLaunchKernelGGL((prefill_concurrent_kernel<D, true, bf16, bf16>), grid, block, 0, st,
+                           local_args<bf16, bf16>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
+    } else if (a.fp->w_bf16) {
+        hipLaunchKernelGGL((prefill_concurrent_kernel<D, true, float, bf16>), grid, block, 0, st,
+                           local_args<float, bf16>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
+    } else {
+        hipLaunchKernelGGL((prefill_concurrent_kernel<D, true, float, float>), grid, block, 0, st,
+                           local_args<float, float>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
+    }
     return hipGetLastError();
 }
 
 // Concurrent schedule: the state pass occupies at most a quarter of the compute units and the
-// chunk-local kernel has enough chunks to fill the rest for more than one round.  Then the two
-// run at the same time on two streams: the chunk-local kernel (on the remaining compute units)
-// publishes each record with a flag and the state pass waits for the flags.  The chunk-local
-// kernel never waits, so it always finishes; it is enqueued first, so even if the two streams
-// share a hardware queue the state pass starts only after it.
-//   The state pass ends last, so it runs on the caller's stream and the chunk-local kernel on
-// the library's second stream, with nothing joined back: the chunk-local kernel raises a flag
-// only after all of that chunk's loads and stores have completed and does nothing after its
-// last flag, and the state pass ends only after it has seen every flag, so once the state pass
-// has ended the chunk-local kernel no longer touches memory.  The conv cache is written by the
-// state pass for the same reason.  (Measured on MI355X at 4096 tokens x 16 heads: the
-// sequential launches take the sum of the two kernels' times; an event recorded on or waited
-// for by the caller's stream after the state pass delays the caller's next kernel by 4 to 6 us.)
-//   A waiting state pass holds its compute units, so when a call comes from another caller
-// stream than the previous concurrent-schedule call, its state pass first waits for the
-// previous call's chunk-local kernel to end: then at most one state pass waits for records at
-// any time, and the chunk-local kernel it waits for is the next on the second stream and finds
-// the compute units that no waiting state pass holds.
+// chunk-local work has enough chunks to fill the rest for more than one round.  Then both run
+// at the same time in one launch (prefill_concurrent_kernel): the chunk-local workgroups (on
+// the remaining compute units) publish each record with a flag and the state pass's
+// workgroups wait for the flags.  A chunk-local workgroup raises a flag only after all of that
+// chunk's loads and stores have completed, and the state pass writes the conv cache once the
+// records that read the input cache are published, so the kernel's end orders everything.
+// (Measured on MI355X at 4096 tokens x 16 heads: launched as two kernels on two streams, the
+// second one started ~5.6 us after the first, and an event recorded on or waited for by the
+// caller's stream after a kernel delays the caller's next kernel by 4 to 6 us.)
+//   A waiting state pass holds its compute units.  Calls on one stream run one after the
+// other.  Once calls have come from more than one stream, every combined kernel records an
+// event after it, and a call from another stream than the previous one waits for that event:
+// so at most two combined kernels run at the same time (the one before the first change of
+// stream, which has no event, and the next), whose state passes hold at most half of the
+// compute units.
 static bool concurrent_ok(int nc, int Hv, int sblocks, int cus) {
     return cus > 0 && 4 * sblocks <= cus && (long long)nc * Hv >= 2LL * (cus - sblocks);
 }
@@ -1661,16 +1813,14 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
             cv.G = a.Hv / a.Hk;
             cv.dk = a.dk;
         }
-        if ((e = hipEventRecord(pr->ev[0], st)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(pr->side, pr->ev[0], 0)) != hipSuccess) return e;
-        // the previous call's chunk-local kernel, before local_done is recorded again
-        if (pr->has_last && pr->last_stream != st && (e = hipStreamWaitEvent(st, pr->local_done, 0)) != hipSuccess)
-            return e;
-        if ((e = launch_local<D>(a, pr->side, nc, 0, nc, cus - sblocks, flags, flag_val)) != hipSuccess) return e;
-        if ((e = hipEventRecord(pr->local_done, pr->side)) != hipSuccess) return e;
+        const bool other = pr->has_last && pr->last_stream != st;
+        if (other && pr->multi && (e = hipStreamWaitEvent(st, pr->last_done, 0)) != hipSuccess) return e;
+        if (other) pr->multi = true;
+        if ((e = launch_concurrent<D>(a, st, nc, cus, sblocks, flags, flag_val, cv)) != hipSuccess) return e;
+        if (pr->multi && (e = hipEventRecord(pr->last_done, st)) != hipSuccess) return e;
         pr->last_stream = st;
         pr->has_last = true;
-        return launch_state<D>(a, st, nc, 0, nc, flags, flag_val, cv);
+        return hipSuccess;
     }
     const int G = pipeline_segments(nc, sblocks);
     if (G == 1) {

@@ -12,10 +12,9 @@
   python -m hybrid_linear_attention_gated_amd.profiling timeline DIR [FIRST [SKIP]]
       kernel start / end offsets inside one step, averaged over the steps of a
       `rocprofv3 --kernel-trace` run: a step begins at each launch of the kernel
-      FIRST (short name, default state_pass: the first launch of the concurrent
-      prefill schedule, whose chunk-local kernel starts after a wait on the second
-      stream) and the first SKIP steps (warm-up) are dropped.  Shows how
-      kernels on the library's two streams overlap.
+      FIRST (short name, default prefill_concurrent: the one launch of the concurrent
+      prefill schedule) and the first SKIP steps (warm-up) are dropped.  Shows how
+      the kernels of a step follow one another (or, on two streams, overlap).
 
   python -m hybrid_linear_attention_gated_amd.profiling counters DIR [DIR ...]
       per-kernel mean per dispatch of every counter of `rocprofv3 --pmc` runs (CSV).
@@ -51,6 +50,7 @@ KERNELS = [
     ("chunk_local_fused", "chunk_local_fused"),
     ("decode_gated", "decode_gated"),
     ("state_pass_kernel", "state_pass"),
+    ("prefill_concurrent_kernel", "prefill_concurrent"),   # "_x32" for the fp32-x instances
     ("prefill_recurrent_kernel", "prefill_recurrent"),
     ("decode_kernel", "decode"),
     ("gated_rmsnorm_kernel", "gated_rmsnorm"),
@@ -67,6 +67,10 @@ def short_name(symbol: str) -> str:
     if "chunk_local_kernel" in symbol and ("ELb1E" in symbol or ", true," in symbol):
         # FUSED = true; fp32 x (the layer's prefill) or 16-bit x
         return "chunk_local_fused_x32" if ("ELb1Ef" in symbol or ", true, float" in symbol) else "chunk_local_fused"
+    if "prefill_concurrent_kernel" in symbol:
+        # chunk-local and state pass in one launch; fp32 x (the layer's prefill) or 16-bit x
+        fp32x = "ELb1Ef" in symbol or ", true, float" in symbol
+        return "prefill_concurrent_x32" if fp32x else "prefill_concurrent"
     if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):
         return "decode_gated"        # template argument GATED = true
     if "proj_kernel" in symbol:      # projection GEMM, named by its output tile and mode
@@ -185,7 +189,7 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
-def timeline(directory: str, first: str = "state_pass", skip: int = 0, lead_us: float = 20.0) -> dict:
+def timeline(directory: str, first: str = "prefill_concurrent", skip: int = 0, lead_us: float = 20.0) -> dict:
     """Mean (start, end) offsets in us of each kernel of a step from the step's first start.
 
     A step begins at each launch of the kernel `first`; a kernel that starts up to
@@ -242,7 +246,7 @@ def main(argv):
         print(f"source_sha256 = {source_sha256()}")
         return 0
     if len(argv) >= 2 and argv[0] == "timeline":
-        tl = timeline(argv[1], argv[2] if len(argv) > 2 else "state_pass", int(argv[3]) if len(argv) > 3 else 0)
+        tl = timeline(argv[1], argv[2] if len(argv) > 2 else "prefill_concurrent", int(argv[3]) if len(argv) > 3 else 0)
         print(f"{tl['steps']} steps; offsets from the start of each step's first kernel, us (mean)")
         print(f"{'kernel':20s} {'start':>8s} {'end':>8s} {'dur':>8s}")
         for k, a, b in tl["kernels"]:

@@ -21,8 +21,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
  *    work is enqueued asynchronously on it; buffers must stay valid until the
  *    stream work completes.  gdn_chunk_prefill with GDN_MATH_MFMA and gdn_prefill
- *    may run part of their work on a second stream of the library (created once per device, default
- *    priority, kept with a few events for the life of the process); that work's
+ *    may run part of their work on a second stream of the library (the segmented
+ *    schedule below; created once per device, default priority, kept with a few
+ *    events for the life of the process); that work's
  *    memory accesses are ordered after everything enqueued on `stream` before the
  *    call and before everything enqueued on it after the call, so to the caller it
  *    behaves as if it ran on `stream`.  Concurrent calls on one device must use
@@ -170,27 +171,26 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  * bit-identical to running the two phases one after the other:
  *  - concurrent, when the state pass occupies at most a quarter of the device's
  *    compute units and there are at least twice as many (chunk, value head) items
- *    as the other compute units: the chunk-local phase runs on the library's second
- *    stream, on the compute units the state pass leaves free, and raises a flag in
- *    the workspace as each record is complete; the state pass runs at the same time
- *    on `stream` and waits for each flag.  The wait is bounded (about a second; the
- *    header's second 64-bit word, when it holds 0x7370696e in its high half, sets the
- *    bound to its low half in iterations of a ~128-cycle sleep, for tests): a record
- *    that is never published ends the call with NaN outputs and final states and the
- *    status GDN_ERR_TIMEOUT, never in a hang; the library's own chunk-local phase
- *    publishes every record.  After such a failure the second stream's kernel may
- *    still run when `stream` moves on: gdn_prefill_workspace_status waits for it.
- *    When a call comes from another caller stream
- *    than the previous concurrent one, its state pass first waits for the previous
- *    call's chunk-local phase, so at most one state pass waits for records at a time;
+ *    as the other compute units: both phases in one launch on `stream`, whose first
+ *    workgroups run the chunk-local phase on the compute units the state pass leaves
+ *    free and raise a flag in the workspace as each record is complete, while its
+ *    last workgroups run the state pass and wait for each flag.  The wait is bounded
+ *    (about a second; the header's second 64-bit word, when it holds 0x7370696e in
+ *    its high half, sets the bound to its low half in iterations of a ~128-cycle
+ *    sleep, for tests): a record that is never published ends the call with NaN
+ *    outputs and final states and the status GDN_ERR_TIMEOUT, never in a hang; the
+ *    chunk-local phase publishes every record.  Once calls have come from more than
+ *    one caller stream, a call from another stream than the previous concurrent one
+ *    first waits for that call's launch, so at most two such launches run at a time;
  *  - segmented, when the packed chunks are many (at least 256) and the state pass
  *    occupies at most half of the compute units: the chunks are cut into up to sixteen
  *    segments, and the chunk-local phase of segment k + 1 (on `stream`) runs while
  *    the state pass of segment k runs on the second stream; a sequence's state
  *    passes between segments through the workspace;
  *  - sequential otherwise, and always while `stream` is capturing a HIP graph: both
- *    phases on `stream`, one after the other (a graph may run sibling nodes one after
- *    the other, and the concurrent schedule is never joined back to `stream`).
+ *    phases on `stream`, one after the other (a graph would replay the concurrent
+ *    launch with the same flag value every time, and may run the segmented
+ *    schedule's sibling nodes one after the other).
  * The query scale multiplies the fp32 outputs after the 16-bit products, so any finite
  * scale is exact to apply; the state pass rounds the state to fp16 for its products,
  * so a state element beyond +-65504 makes outputs non-finite, which the status word

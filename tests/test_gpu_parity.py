@@ -670,8 +670,9 @@ def test_concurrent_schedule_conv_cache(gdn, alias, dtype):
 def test_concurrent_schedule_from_several_streams(gdn):
     """Four caller streams each start a concurrent-schedule prefill (own workspace, inputs
     and outputs) before any of them has finished; every result is bit-identical to the
-    split-phase calls on the default stream.  Covers the ordering of state passes across
-    caller streams and the shared second stream of the library."""
+    split-phase calls on the default stream.  Covers the ordering of the one-launch
+    concurrent schedule across caller streams (the first change of stream, then the
+    event that a call from another stream waits for)."""
     announce("concurrent schedule: T=8000, Hk=2, Hv=4, four caller streams")
     T, Hk, Hv, d, n = 8000, 2, 4, 128, 4
     wsz = gdn.workspace_size(T, 1, Hk, Hv, d, d, "mfma")

@@ -31,6 +31,13 @@ def test_short_names():
     assert profiling.short_name(LOCAL) == "chunk_local_fused"
     assert profiling.short_name(LOCAL.replace("true", "false")) == "chunk_local"
     assert profiling.short_name(STATE) == "state_pass"
+    assert profiling.short_name(
+        "void gdn::prefill_concurrent_kernel<128, true, __hip_bfloat16, __hip_bfloat16>(...)") == "prefill_concurrent"
+    assert profiling.short_name(
+        "void gdn::prefill_concurrent_kernel<128, true, float, __hip_bfloat16>(...)") == "prefill_concurrent_x32"
+    assert profiling.short_name(
+        "_ZN3gdn25prefill_concurrent_kernelILi128ELb1EfDF16bEEvNS_9LocalArgsIT1_T2_EENS_9StateArgsEi") == \
+        "prefill_concurrent_x32"
     assert profiling.short_name(DECODE) == "decode"
     assert profiling.short_name(DECODE.replace("false>", "true>")) == "decode_gated"
     assert profiling.short_name(COPY) == "copy"
