@@ -277,17 +277,31 @@ __device__ __forceinline__ ConvLane conv_lane(int wave, int lane, int h, int kh,
 // input rows (from the staged rows in LDS, or x, or the conv cache before the sequence
 // start, else zeros), the depthwise conv + SiLU, then for q and k the L2 norm over the D / 8
 // lanes of the token group, written to the bf16 hi / lo planes; v goes to the fp32 plane.
-// wt holds the lane's conv weights (wt[j][i]: tap j of channel ch0 + i).  Every wave calls it
-// once: with STAGE its barrier separates the reads of the staging area from the plane writes
-// that overwrite part of it.  Inactive lanes only take the barrier.
-template <int D, typename TX, bool STAGE, int TOK>
+// wt holds the lane's conv weights (wt[j][i]: tap j of channel ch0 + i); with DOT2 (16-bit x
+// and weights) wp holds them as bf16 pairs (wp[j][i]: taps 2j, 2j + 1) and each output is two
+// two-term dot products of a weight pair with the channel's values at two consecutive tokens
+// (the products of two bf16 values are exact in fp32).  Every wave calls it once: with STAGE
+// its barrier separates the reads of the staging area from the plane writes that overwrite
+// part of it.  Inactive lanes only take the barrier.
+template <int D, typename TX, bool STAGE, int TOK, bool DOT2>
 __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict__ x, const TX *__restrict__ cs_in, int conv_dim, int t0, int L, int s_,
                                                 bool first, bool staged, bool active, int grp, int ch0, int tl0, int cb,
-                                                float l2_eps, const float (&wt)[4][8]) {
+                                                float l2_eps, const float (&wt)[4][8], const unsigned (&wp)[2][8]) {
     using SM = LocalSmem<D>;
     constexpr int CB = D / 8, LD = SM::LD;
+    const int grp_ = TOK == 4 ? 2 : grp;   // four-token lanes convolve v only
     Raw8<TX> rows[TOK + kConvHist];
-    if (active) {
+    // A full chunk with its rows staged that does not start its sequence (the common case,
+    // wave-uniform): every row is a staged row, part A below XRA, part B from XRA on.
+    const bool fast = STAGE && staged && !first && L == kChunk;
+    if (active && fast) {
+        const int cross = SM::XRA - tl0;
+        const int base_a = SM::XA + tl0 * SM::XROW + grp_ * 2 * D + 16 * cb;
+        const int base_b = base_a + (SM::XB - SM::XA - SM::XRA * SM::XROW);
+#pragma unroll
+        for (int r = 0; r < TOK + kConvHist; ++r)
+            rows[r].load(reinterpret_cast<const TX *>(smem + (r >= cross ? base_b : base_a) + r * SM::XROW));
+    } else if (active) {
 #pragma unroll
         for (int r = 0; r < TOK + kConvHist; ++r) {
             const int tl = tl0 - kConvHist + r;
@@ -295,7 +309,7 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
                 if (STAGE && staged) {
                     const int sr = tl + kConvHist;   // staged row
                     const int so = (sr < SM::XRA ? SM::XA + sr * SM::XROW : SM::XB + (sr - SM::XRA) * SM::XROW) +
-                                   grp * 2 * D + 16 * cb;
+                                   grp_ * 2 * D + 16 * cb;
                     rows[r].load(reinterpret_cast<const TX *>(smem + so));
                 } else {
                     rows[r].load(x + (size_t)(t0 + tl) * conv_dim + ch0);
@@ -310,29 +324,40 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
     if constexpr (STAGE) __syncthreads();   // staging part A is read before the planes overwrite it
     if (!active) return;
     float hw[3][8];
+    if constexpr (!DOT2) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) rows[j].to_f32(hw[j]);
+        for (int j = 0; j < 3; ++j) rows[j].to_f32(hw[j]);
+    }
 #pragma unroll
     for (int i = 0; i < TOK; ++i) {
         float xt[8], y[8];
-        rows[i + kConvHist].to_f32(xt);
+        if constexpr (!DOT2) rows[i + kConvHist].to_f32(xt);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float acc = wt[0][e] * hw[0][e];
-            acc = fmaf(wt[1][e], hw[1][e], acc);
-            acc = fmaf(wt[2][e], hw[2][e], acc);
-            acc = fmaf(wt[3][e], xt[e], acc);
+            float acc;
+            if constexpr (DOT2) {
+                // (x[r][e], x[r + 1][e]) as one bf16 pair: the low or high halves of the two rows'
+                // words holding channels e & ~1, e | 1
+                const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                auto word = [&](int r) { return __builtin_bit_cast(u32x4v, rows[r].v)[e >> 1]; };
+                const unsigned p01 = __builtin_amdgcn_perm(word(i + 1), word(i), sel);
+                const unsigned p23 = __builtin_amdgcn_perm(word(i + 3), word(i + 2), sel);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[0][e]),
+                                                      __builtin_bit_cast(bf16x2, p01), 0.f, false);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wp[1][e]),
+                                                      __builtin_bit_cast(bf16x2, p23), acc, false);
+            } else {
+                acc = wt[0][e] * hw[0][e];
+                acc = fmaf(wt[1][e], hw[1][e], acc);
+                acc = fmaf(wt[2][e], hw[2][e], acc);
+                acc = fmaf(wt[3][e], xt[e], acc);
+            }
             y[e] = silu(acc);
             ss = fmaf(y[e], y[e], ss);
         }
         const int tl = tl0 + i;
-        if (tl >= L) {   // padded row: zero (its conv window still reaches real rows)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = 0.f;
-            ss = 0.f;
-        }
-        if (grp < 2) {
+        if (grp_ < 2) {
             ss = group_sum<CB>(ss);
             const float rn = rsqrtf(ss + l2_eps);
             float yn[8];
@@ -349,8 +374,10 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
             *reinterpret_cast<f32x4 *>(vp) = f32x4{y[0], y[1], y[2], y[3]};
             *reinterpret_cast<f32x4 *>(vp + 4) = f32x4{y[4], y[5], y[6], y[7]};
         }
+        if constexpr (!DOT2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { hw[0][e] = hw[1][e]; hw[1][e] = hw[2][e]; hw[2][e] = xt[e]; }
+            for (int e = 0; e < 8; ++e) { hw[0][e] = hw[1][e]; hw[1][e] = hw[2][e]; hw[2][e] = xt[e]; }
+        }
     }
 }
 
@@ -465,13 +492,23 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     bool have = false;
     // Fused: the lane's conv weights, loaded once (a workgroup keeps its head, so its lanes
     // keep their channels, for the whole launch).
+    // With 16-bit x and weights the taps go in pairs: cwp[j][i] holds taps 2j, 2j + 1 of
+    // channel ch0 + i as a bf16 pair (low half first), for two-term dot products.
+    constexpr bool DOT2 = STAGE && sizeof(TW) == 2;
     float cwt[4][8];
+    unsigned cwp[2][8];
     if constexpr (FUSED) {
         const ConvLane cl = conv_lane<D, TX>(threadIdx.x >> 6, threadIdx.x & 63, h, kh, Hk);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) cwt[j][i] = cl.active ? to_f32(conv_w[(size_t)(cl.ch0 + i) * kConvK + j]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)   // bf16 values held exactly in fp32: the high halves
+                cwp[j][i] = (__builtin_bit_cast(unsigned, cwt[2 * j][i]) >> 16) |
+                            (__builtin_bit_cast(unsigned, cwt[2 * j + 1][i]) & 0xffff0000u);
     }
     for (int gc = g0 + slot; gc < g1; gc += nslots) {
     // The thread index passes through an empty asm each iteration, so nothing derived from
@@ -561,17 +598,18 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
         }
     }
     if constexpr (FUSED) {
-        // conv + SiLU + L2 from x (lane roles: conv_lane); rows past the chunk's last token
-        // are zeros (SiLU(0) = 0, and a zero vector stays zero under the L2 norm), so padded
-        // rows of the planes are zero.
+        // conv + SiLU + L2 from x (lane roles: conv_lane).  Tokens past the chunk's last one
+        // (a sequence's last chunk) get finite values that no stored result depends on: their
+        // beta and g are 0, so their rows of A, W' and U' are exactly zero (T's row is the
+        // identity row), Delta' vanishes there and their outputs are not stored.
         const ConvLane cl = conv_lane<D, TX>(wave, lane, h, kh, Hk);
         const bool first = c_ == 0;              // history before the sequence start
         if (cl.vsplit)
-            fused_conv_lane<D, TX, STAGE, 4>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, true, cl.grp, cl.ch0,
-                                             cl.tl0, cl.cb, l2_eps, cwt);
+            fused_conv_lane<D, TX, STAGE, 4, DOT2>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, true, cl.grp,
+                                                   cl.ch0, cl.tl0, cl.cb, l2_eps, cwt, cwp);
         else
-            fused_conv_lane<D, TX, STAGE, 8>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, cl.active, cl.grp,
-                                             cl.ch0, cl.tl0, cl.cb, l2_eps, cwt);
+            fused_conv_lane<D, TX, STAGE, 8, DOT2>(smem, x, cs_in, conv_dim, t0, L, s_, first, staged, cl.active,
+                                                   cl.grp, cl.ch0, cl.tl0, cl.cb, l2_eps, cwt, cwp);
     }
     // K and Q as bf16 hi / lo planes, row-major [token][head dim]
 #pragma unroll
