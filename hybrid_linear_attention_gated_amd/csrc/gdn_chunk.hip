@@ -634,16 +634,17 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     }
     __syncthreads();
 
-    // ---- 1. tiles with key block b as the A operand: K K^T (b, c <= b) and K Q^T (b, r >= b).
-    // Eight waves: wave b takes the K K^T tiles of block b, wave 4 + b the K Q^T tiles;
-    // four waves: wave b takes both.
+    // ---- 1. tiles with key block b as the A operand: K K^T (b, c <= b) and K Q^T (b, r >= b),
+    // five in all, numbered j = 0 .. 4 (K K^T c = j for j <= b, then K Q^T r = j - 1).
+    // Eight waves: wave b takes tiles 0 and 1 of block b and wave 4 + b tiles 2 .. 4 (the W
+    // waves have the heavier work after this phase); four waves: wave b takes all five.
     // The tile loops run at compile time (one instance per key block), so the next tile's
     // operand reads are issued under the current tile's MFMAs.
     {
         const int b = wave & 3;
-        const bool doKK = NW == 4 || wave < 4, doKQ = NW == 4 || wave >= 4;
-        auto tiles = [&](auto btag) __attribute__((always_inline)) {
+        auto tiles = [&](auto btag, auto lotag, auto hitag) __attribute__((always_inline)) {
             constexpr int B = decltype(btag)::value;
+            constexpr int j0 = decltype(lotag)::value, j1 = decltype(hitag)::value;   // tiles [j0, j1)
             Split8 ka[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -651,11 +652,12 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
                 ka[ks] = Split8{*reinterpret_cast<const bf16x8 *>(Kh + off),
                                 *reinterpret_cast<const bf16x8 *>(Kl + off)};
             }
-            if (doKK) {
+            if constexpr (j0 <= B) {
                 const f32x4 Bb = *reinterpret_cast<const f32x4 *>(Bs + 16 * B + 4 * kg);
                 const f32x4 Grb = *reinterpret_cast<const f32x4 *>(GRs + 16 * B + 4 * kg);
 #pragma unroll
                 for (int c = 0; c <= B; ++c) {
+                    if (c < j0 || c >= j1) continue;
                     Acc3 s3 = acc3_zero();
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
@@ -683,10 +685,11 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
                     }
                 }
             }
-            if (doKQ) {
+            if constexpr (j1 > B + 1) {
                 const f32x4 Gb = *reinterpret_cast<const f32x4 *>(Gs + 16 * B + 4 * kg);
 #pragma unroll
                 for (int r = B; r < 4; ++r) {
+                    if (r + 1 < j0 || r + 1 >= j1) continue;
                     Acc3 s3 = acc3_zero();
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks) {
@@ -709,11 +712,29 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
                 }
             }
         };
-        switch (b) {
-        case 0: tiles(std::integral_constant<int, 0>{}); break;
-        case 1: tiles(std::integral_constant<int, 1>{}); break;
-        case 2: tiles(std::integral_constant<int, 2>{}); break;
-        default: tiles(std::integral_constant<int, 3>{}); break;
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using I5 = std::integral_constant<int, 5>;
+        if constexpr (NW == 4) {
+            switch (b) {
+            case 0: tiles(I0{}, I0{}, I5{}); break;
+            case 1: tiles(I1{}, I0{}, I5{}); break;
+            case 2: tiles(I2{}, I0{}, I5{}); break;
+            default: tiles(I3{}, I0{}, I5{}); break;
+            }
+        } else {
+            switch (wave) {
+            case 0: tiles(I0{}, I0{}, I2{}); break;
+            case 1: tiles(I1{}, I0{}, I2{}); break;
+            case 2: tiles(I2{}, I0{}, I2{}); break;
+            case 3: tiles(I3{}, I0{}, I2{}); break;
+            case 4: tiles(I0{}, I2{}, I5{}); break;
+            case 5: tiles(I1{}, I2{}, I5{}); break;
+            case 6: tiles(I2{}, I2{}, I5{}); break;
+            default: tiles(I3{}, I2{}, I5{}); break;
+            }
         }
     }
     // W waves: K in accumulator layout (rows = token) for head-dim tiles 2qw, 2qw + 1, on
