@@ -809,7 +809,8 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     // spread over all waves.  Copy i (1 KiB) fills staging bytes [1 KiB i, 1 KiB (i + 1));
     // lane l moves 16 bytes of segment (row, group) = (i * SPI + l / SEGL) / 3.  Rows before
     // the buffer start or past its end read as 0 (they are not used: history rows of a
-    // sequence's first chunk come from its conv cache, rows past its last token are masked).
+    // sequence's first chunk come from its conv cache, rows past its last token feed only
+    // tokens on which no stored result depends).
     // The next chunk of this workgroup: chunk c_ + nslots of the same sequence if it has
     // one, else found by a search.
     const int gn = gc + nslots;
