@@ -242,6 +242,14 @@ def test_core_chunked_many_sequences(gdn):
     _core_case(gdn, wl, "mfma")
 
 
+def test_core_chunked_many_sequences_d64(gdn):
+    """The many-sequence case at d = 64: 336 (sequence, head) units, so the state pass's 672
+    workgroups take several rounds of the compute units."""
+    announce(f"core chunked d=64, {len(MANY_LENGTHS)} sequences, several rounds of state-pass workgroups")
+    wl = inputs.core_workload("many64", 4302, MANY_LENGTHS, 2, 4, 64, 64, random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
 def test_core_chunked_ranked_sequences(gdn):
     """60 sequences (the state pass takes them longest first) with repeated chunk counts."""
     lengths = MANY_LENGTHS[:60]
