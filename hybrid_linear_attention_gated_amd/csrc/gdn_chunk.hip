@@ -412,9 +412,12 @@ __device__ __forceinline__ void fused_conv_lane(char *smem, const TX *__restrict
 // to the call's own value (a fixed 32-bit tag in the high word, a per-device call counter in
 // the low word).  A flag counts as raised only when it holds this call's value, so the flags
 // need no clearing between calls: values left by earlier calls hold older counters, and a
-// fresh workspace would have to hold the exact 64-bit pattern by chance.
+// fresh workspace would have to hold the exact 64-bit pattern by chance.  A call captured in
+// a HIP graph replays with one value, so there the flags are cleared by a kernel first and
+// every replay uses the value (kFlagTagGraph << 32) | 1, which no other call uses.
 typedef unsigned long long flag_t;
 constexpr unsigned kFlagTag = 0x9e3779b9u;
+constexpr unsigned kFlagTagGraph = 0x7f4a7c15u;
 
 // LDS of the chunk-local kernel
 template <int D, typename TX, bool FUSED>
@@ -1777,6 +1780,12 @@ static hipError_t launch_state(const PrefillArgs &a, hipStream_t st, int nc, int
     return hipGetLastError();
 }
 
+// Clear n ready flags (a captured concurrent-schedule call, before its launch).
+__global__ void zero_flags_kernel(flag_t *f, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) f[i] = 0ull;
+}
+
 // The combined kernel of the concurrent schedule on `st`: the chunk-local workgroups on the
 // compute units the state pass leaves, then the state pass's.
 template <int D>
@@ -1846,12 +1855,32 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
     }
     const int sblocks = state_blocks<D>(a.N * a.Hv);
     const int cus = device_cus();
-    // Under stream capture (a HIP graph being recorded) both phases go on `stream` one after
-    // the other: the concurrent schedule's kernels must run at the same time (a graph may
-    // run sibling nodes one after the other) and it is never joined back to `stream`.
+    flag_t *flags = reinterpret_cast<flag_t *>((char *)a.ws + kWsHeader + flags_offset(nc, a.N, a.Hv, D));
+    ConvOut cv;   // the conv cache, written by the concurrent schedule's state pass
+    if (a.fp && a.fp->cs_out) {
+        cv.x = a.fp->x;
+        cv.cs_in = a.fp->cs_in;
+        cv.cs_out = a.fp->cs_out;
+        cv.esz = a.fp->bf16 ? 2 : 4;
+        cv.conv_dim = 2 * a.Hk * a.dk + a.Hv * a.dv;
+        cv.Hk = a.Hk;
+        cv.G = a.Hv / a.Hk;
+        cv.dk = a.dk;
+    }
+    // Under stream capture (a HIP graph being recorded) everything goes on `stream` and no
+    // event is recorded or waited for: the concurrent schedule as one launch after a kernel
+    // that clears its flags (each replay then uses the graph's fixed flag value), otherwise
+    // the two phases one after the other (the segmented schedule's second stream cannot be
+    // captured as it runs).
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
     if (cap != hipStreamCaptureStatusNone) {
+        if (concurrent_ok(nc, a.Hv, sblocks, cus)) {
+            const int nflags = nc * a.Hv;
+            hipLaunchKernelGGL(zero_flags_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, flags, nflags);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            return launch_concurrent<D>(a, st, nc, cus, sblocks, flags, ((flag_t)kFlagTagGraph << 32) | 1u, cv);
+        }
         if ((e = launch_local<D>(a, st, nc, 0, nc)) != hipSuccess) return e;
         if ((e = launch_state<D>(a, st, nc, 0, nc)) != hipSuccess) return e;
         return launch_fused_cs_out(a, st);
@@ -1860,19 +1889,7 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
         PipeRes *pr = nullptr;
         if ((e = pipe_resources(&pr)) != hipSuccess) return e;
         std::lock_guard<std::mutex> lock(pr->mu);
-        flag_t *flags = reinterpret_cast<flag_t *>((char *)a.ws + kWsHeader + flags_offset(nc, a.N, a.Hv, D));
         const flag_t flag_val = ((flag_t)kFlagTag << 32) | ++pr->epoch;
-        ConvOut cv;
-        if (a.fp && a.fp->cs_out) {
-            cv.x = a.fp->x;
-            cv.cs_in = a.fp->cs_in;
-            cv.cs_out = a.fp->cs_out;
-            cv.esz = a.fp->bf16 ? 2 : 4;
-            cv.conv_dim = 2 * a.Hk * a.dk + a.Hv * a.dv;
-            cv.Hk = a.Hk;
-            cv.G = a.Hv / a.Hk;
-            cv.dk = a.dk;
-        }
         const bool other = pr->has_last && pr->last_stream != st;
         if (other && pr->multi && (e = hipStreamWaitEvent(st, pr->last_done, 0)) != hipSuccess) return e;
         if (other) pr->multi = true;

@@ -187,10 +187,11 @@ size_t gdn_chunk_prefill_workspace_size(int T, int N, int Hk, int Hv, int dk, in
  *    segments, and the chunk-local phase of segment k + 1 (on `stream`) runs while
  *    the state pass of segment k runs on the second stream; a sequence's state
  *    passes between segments through the workspace;
- *  - sequential otherwise, and always while `stream` is capturing a HIP graph: both
- *    phases on `stream`, one after the other (a graph would replay the concurrent
- *    launch with the same flag value every time, and may run the segmented
- *    schedule's sibling nodes one after the other).
+ *  - sequential otherwise: both phases on `stream`, one after the other.
+ * While `stream` is capturing a HIP graph, the concurrent schedule is captured as a kernel
+ * that clears the ready flags followed by the one launch (every replay waits for a
+ * graph-only flag value), and the segmented one as the sequential schedule; nothing is
+ * enqueued on the library's second stream and no event is recorded or waited for.
  * The query scale multiplies the fp32 outputs after the 16-bit products, so any finite
  * scale is exact to apply; the state pass rounds the state to fp16 for its products,
  * so a state element beyond +-65504 makes outputs non-finite, which the status word

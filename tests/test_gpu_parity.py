@@ -807,9 +807,11 @@ def test_debug_check_environment(gdn, tmp_path):
 
 def test_graph_capture_of_layer_4k_prefill(gdn):
     """gdn_prefill at the layer_4k shape captured into a HIP graph (torch.cuda.graph): under
-    capture the library takes the one-stream schedule.  The graph is replayed three times
-    with other eager work and synchronisations in between; every replay is bit-identical to
-    the eager call (which takes the concurrent schedule)."""
+    capture the concurrent schedule's one launch follows a kernel that clears its ready flags,
+    and every replay uses the graph's own flag value.  The graph is replayed three times with
+    other eager work and synchronisations in between; every replay is bit-identical to the
+    eager call, and so is an eager call on the same workspace after the replays (the flags
+    the replays left do not pass for its own)."""
     announce("graph capture of gdn_prefill at layer_4k, three replays")
     wl = inputs.layer_4k()
     x, w, g, b = (_cuda(t) for t in (wl.x, wl.conv_w, wl.g, wl.beta))
@@ -840,3 +842,9 @@ def test_graph_capture_of_layer_4k_prefill(gdn):
         assert torch.equal(f, f_ref), f"replay {rep}: final state differs from the eager call"
         assert torch.equal(cso, cso_ref), f"replay {rep}: conv cache differs"
         del junk
+    o.zero_()
+    f.zero_()
+    gdn.prefill(x, w, g, b, Hk, Hv, d, d, conv_state_out=cso, o=o, final_state=f, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(f, f_ref), "eager call after the replays differs"
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
