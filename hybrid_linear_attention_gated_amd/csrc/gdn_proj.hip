@@ -29,8 +29,8 @@
 //    the fragments of k-step s + 1 are read from LDS between the MFMAs of step s (one
 //    read per group of MFMAs, by scheduling hints), so with one wave per SIMD the
 //    matrix unit does not wait on LDS.  The 16-byte chunks of an LDS row are
-//    XOR-swizzled by the row index, so the eight rows that one LDS read cycle serves
-//    hit eight different bank groups.
+//    XOR-swizzled by row bits (swz below), so the 16 rows of one fragment read land
+//    in the LDS's 16 different 16-byte bank groups.
 //  - Tiles are numbered so that each XCD (workgroups are dealt to the eight XCDs in
 //    turn) takes a contiguous run of tiles in which groups of four row tiles share
 //    column tiles: the tiles resident on one XCD at a time reuse each other's rows
