@@ -103,19 +103,21 @@ __device__ __forceinline__ int chunk_base_wave(const int32_t *cu, int s) {
     return acc;
 }
 
-// Wave-parallel: which sequence holds packed chunk gc, and which chunk of it.
-// Returns false when gc is past the last chunk.
+// Wave-parallel: which sequence holds packed chunk gc, which chunk of it, and the
+// sequence's token range [sb_out, se_out) (from the same loads).  Returns false when gc is
+// past the last chunk.
 __device__ __forceinline__ bool locate_chunk_wave(const int32_t *cu, int N, int Ttot, int gc, int &s_out,
-                                                  int &c_out) {
+                                                  int &c_out, int &sb_out, int &se_out) {
     const int lane = threadIdx.x & (kWave - 1);
     if (!cu) {
-        s_out = 0; c_out = gc;
+        s_out = 0; c_out = gc; sb_out = 0; se_out = Ttot;
         return gc < n_chunks(Ttot);
     }
     int base = 0;
     for (int i0 = 0; i0 < N; i0 += kWave) {
         const int i = i0 + lane;
-        const int n = i < N ? n_chunks(cu[i + 1] - cu[i]) : 0;
+        const int ta = i < N ? cu[i] : 0, tb = i < N ? cu[i + 1] : 0;
+        const int n = i < N ? n_chunks(tb - ta) : 0;
         int incl = n;
         for (int o = 1; o < kWave; o <<= 1) {
             const int y = __shfl_up(incl, o, kWave);
@@ -127,6 +129,8 @@ __device__ __forceinline__ bool locate_chunk_wave(const int32_t *cu, int N, int 
             const int src = __ffsll((long long)hit) - 1;
             s_out = i0 + src;
             c_out = gc - __shfl(excl, src, kWave);
+            sb_out = __builtin_amdgcn_readfirstlane(__shfl(ta, src, kWave));
+            se_out = __builtin_amdgcn_readfirstlane(__shfl(tb, src, kWave));
             return true;
         }
         base += __shfl(incl, kWave - 1, kWave);
@@ -502,16 +506,28 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     unsigned cwp[2][8];
     if constexpr (FUSED) {
         const ConvLane cl = conv_lane<D, TX>(threadIdx.x >> 6, threadIdx.x & 63, h, kh, Hk);
+        if constexpr (DOT2) {
+            // A channel's four bf16 taps are 8 contiguous bytes: its words (taps 0, 1) and
+            // (taps 2, 3) are already the pairs, low half first.  Four 16-byte loads cover the
+            // lane's 8 channels; nothing waits for them before the first conv.
+            const u32x4 *cw4 = reinterpret_cast<const u32x4 *>(conv_w + (size_t)cl.ch0 * kConvK);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const u32x4 w = cl.active ? cw4[q4] : u32x4{0u, 0u, 0u, 0u};
+                cwp[0][2 * q4] = w[0]; cwp[1][2 * q4] = w[1];
+                cwp[0][2 * q4 + 1] = w[2]; cwp[1][2 * q4 + 1] = w[3];
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cwt[j][i] = cl.active ? to_f32(conv_w[(size_t)(cl.ch0 + i) * kConvK + j]) : 0.f;
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+                for (int j = 0; j < 4; ++j) cwt[j][i] = 0.f;   // not used with the pairs
+        } else {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)   // bf16 values held exactly in fp32: the high halves
-                cwp[j][i] = (__builtin_bit_cast(unsigned, cwt[2 * j][i]) >> 16) |
-                            (__builtin_bit_cast(unsigned, cwt[2 * j + 1][i]) & 0xffff0000u);
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    cwt[j][i] = cl.active ? to_f32(conv_w[(size_t)(cl.ch0 + i) * kConvK + j]) : 0.f;
+        }
     }
     for (int gc = g0 + slot; gc < g1; gc += nslots) {
     // The thread index passes through an empty asm each iteration, so nothing derived from
@@ -525,11 +541,7 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     const bool isW = wave < NWH;
     const int qw = isW ? wave : wave - NWH;   // this wave's pair of 16-wide tiles: 2qw, 2qw + 1
     // ---- where this chunk lives (every wave finds the same answer; no barrier)
-    if (!have) {
-        if (!locate_chunk_wave(cu, N, Ttot, gc, s_, c_)) break;
-        sb = __builtin_amdgcn_readfirstlane(seq_begin(cu, s_));
-        se = __builtin_amdgcn_readfirstlane(seq_end(cu, s_, Ttot));
-    }
+    if (!have && !locate_chunk_wave(cu, N, Ttot, gc, s_, c_, sb, se)) break;
     const int t0 = sb + c_ * kChunk;
     const int L = min(kChunk, se - t0);
     char *rec = ws + ((size_t)h * ncmax + gc) * R::SIZE;   // head-major: a head's chunks are contiguous
@@ -822,10 +834,8 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
     if (gn < g1) {
         if (cn * kChunk < se - sb) {
             next_ok = true;
-        } else if (locate_chunk_wave(cu, N, Ttot, gn, sn, cn)) {
+        } else if (locate_chunk_wave(cu, N, Ttot, gn, sn, cn, sbn, sen)) {
             next_ok = true;
-            sbn = __builtin_amdgcn_readfirstlane(seq_begin(cu, sn));
-            sen = __builtin_amdgcn_readfirstlane(seq_end(cu, sn, Ttot));
         }
     }
     // Eight waves: wave 0 alone solves the diagonal blocks (one wave's 64 lanes cover all
