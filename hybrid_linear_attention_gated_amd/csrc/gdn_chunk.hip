@@ -82,10 +82,10 @@ struct Rec {
     static constexpr int W_OFF = 0;                     // -W' f16 A frags [4 row tiles][NKS][64 lanes][8]
     static constexpr int Q_OFF = W_OFF + 64 * D * 2;    // Qt  f16 A frags [4][NKS][64][8]
     static constexpr int K_OFF = Q_OFF + 64 * D * 2;    // K^T bf16 A frags, hi and lo: [2][NTD row tiles][2][64][8]
-    static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U'  f32 tiles [NTD col tiles][4 row tiles][64][4]
+    static constexpr int U_OFF = K_OFF + 64 * D * 4;    // U'  24-bit tiles [NTD col tiles][4 row tiles][64][12 B]
                                                         //   (W' = diag(e^{G_c - G_t}) W, U' likewise)
-    static constexpr int O_OFF = U_OFF + 64 * D * 4;    // Ol^T f32 tiles [NTD][4][64][4] (rows = value column)
-    static constexpr int GM_OFF = O_OFF + 64 * D * 4;   // e^{G_c}, f32, stored 4 times; then the query scale
+    static constexpr int O_OFF = U_OFF + 64 * D * 3;    // Ol^T 24-bit tiles [NTD][4][64][12 B] (rows = value column)
+    static constexpr int GM_OFF = O_OFF + 64 * D * 3;   // e^{G_c}, f32, stored 4 times; then the query scale
     static constexpr int SIZE = GM_OFF + 256;           // padded to a multiple of 256 bytes
 };
 
@@ -162,11 +162,33 @@ __device__ __forceinline__ void rec_store16(char *rec, int off, V v, bool cohere
     else
         *reinterpret_cast<V *>(rec + off) = v;
 }
-__device__ __forceinline__ f32x4 rec_load16(const char *rec, int off, bool coherent) {
+// U' and Ol^T tiles are kept as 24-bit floats: the fp32 value with its low byte rounded
+// away (half up in magnitude: sign, exponent and 15 mantissa bits remain, a relative step of
+// 2^-16), four values in 12 bytes, value i's three bytes at bytes 3i .. 3i + 2.  Byte
+// permutes pack and unpack them (selector 0x0c gives a zero byte).
+typedef unsigned u32x3 __attribute__((ext_vector_type(3)));
+// (The values are bit-cast as whole vectors: a bit cast of one subscripted element of a
+// vector value was compiled as a cast of element 0.)
+__device__ __forceinline__ u32x3 pack24(f32x4 v) {
+    const u32x4 r = __builtin_bit_cast(u32x4, v) + 0x80u;
+    return u32x3{__builtin_amdgcn_perm(r[1], r[0], 0x05030201u), __builtin_amdgcn_perm(r[2], r[1], 0x06050302u),
+                 __builtin_amdgcn_perm(r[3], r[2], 0x07060503u)};
+}
+__device__ __forceinline__ f32x4 unpack24(u32x3 d) {
+    const u32x4 r = {d[0] << 8, __builtin_amdgcn_perm(d[1], d[0], 0x0504030cu), __builtin_amdgcn_perm(d[2], d[1], 0x0403020cu),
+                     d[2] & 0xffffff00u};
+    return __builtin_bit_cast(f32x4, r);
+}
+// 12 bytes of a record (coherent: device scope, as rec_store16)
+__device__ __forceinline__ void rec_store12(char *rec, int off, u32x3 v, bool coherent) {
     if (coherent)
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(rec, 1 << 30), off, 0,
-                                                                               kCohAux));
-    return *reinterpret_cast<const f32x4 *>(rec + off);
+        __builtin_amdgcn_raw_buffer_store_b96(v, make_rsrc(rec, 1 << 30), off, 0, kCohAux);
+    else
+        __builtin_amdgcn_raw_buffer_store_b96(v, make_rsrc(rec, 1 << 30), off, 0, 0);
+}
+__device__ __forceinline__ u32x3 rec_load12(const char *rec, int off, bool coherent) {
+    if (coherent) return __builtin_amdgcn_raw_buffer_load_b96(make_rsrc(rec, 1 << 30), off, 0, kCohAux);
+    return __builtin_amdgcn_raw_buffer_load_b96(make_rsrc(rec, 1 << 30), off, 0, 0);
 }
 
 // ============================================================== chunk-local
@@ -1057,7 +1079,7 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
             }
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-                rec_store16(rec, R::U_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 16, acc3_sum(y[ni]),
+                rec_store12(rec, R::U_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 12, pack24(acc3_sum(y[ni])),
                             flags != nullptr);
         }
 #pragma unroll
@@ -1071,7 +1093,7 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
             }
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-                rec_store16(rec, R::O_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 16, acc3_sum(x[ni]),
+                rec_store12(rec, R::O_OFF + (((2 * qw + ni) * 4 + rt) * 64 + lane) * 12, pack24(acc3_sum(x[ni])),
                             flags != nullptr);
         }
     }
@@ -1397,15 +1419,17 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
 #pragma unroll
         for (int m = 0; m < NTD; ++m) S[m] = zero4();
     }
-    // this lane's part of the strip's U and Ol tiles (uniform record base + lane offset)
-    const int strip_off = (j * 4 * 64 + lane) * 16;
+    // this lane's part of the strip's U and Ol tiles (uniform record base + lane offset),
+    // kept packed until the step that uses them
+    const int strip_off = (j * 4 * 64 + lane) * 12;
     f32x4 Uf[4], Of[4];
+    u32x3 Uh0[4] = {}, Oh0[4] = {};
     float gm = 0.f;
-    auto load_strip = [&](const char *rec, f32x4 *U_, f32x4 *O_, float &g_) {
+    auto load_strip = [&](const char *rec, u32x3 *U_, u32x3 *O_, float &g_) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            U_[mt] = rec_load16(rec, R::U_OFF + strip_off + mt * 1024, COH);
-            O_[mt] = rec_load16(rec, R::O_OFF + strip_off + mt * 1024, COH);
+            U_[mt] = rec_load12(rec, R::U_OFF + strip_off + mt * 768, COH);
+            O_[mt] = rec_load12(rec, R::O_OFF + strip_off + mt * 768, COH);
         }
         // lane-varying address: a vector load (no scalar load shares lgkmcnt with LDS reads)
         g_ = COH ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(rec, 1 << 30),
@@ -1421,7 +1445,7 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
                   : *reinterpret_cast<const float *>(rec + R::GM_OFF + 16);
     };
     if (!COH && c_lo < c_hi) {
-        load_strip(rec_of(c_lo), Uf, Of, gm);
+        load_strip(rec_of(c_lo), Uh0, Oh0, gm);
         load_scale(rec_of(c_lo));
     }
     // Retire the initial state and strip loads here, once.  Left pending into the loop,
@@ -1431,10 +1455,12 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (COH && c_lo < c_hi) {   // first strips only once the copy waves have confirmed them
-        load_strip(rec_of(c_lo), Uf, Of, gm);
+        load_strip(rec_of(c_lo), Uh0, Oh0, gm);
         load_scale(rec_of(c_lo));
         __builtin_amdgcn_s_waitcnt(0);
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) { Uf[mt] = unpack24(Uh0[mt]); Of[mt] = unpack24(Oh0[mt]); }
     // inf / NaN detection for the outputs and the final state: x * 0 is 0 for every finite x
     // and NaN otherwise, so one FMA per value folds them into a sum that ends non-finite
     // exactly when some value was (reported at the end)
@@ -1470,7 +1496,7 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
     auto chunk_step = [&](int c, auto last_tag) {
         constexpr bool LAST = decltype(last_tag)::value;
         const char *A = abuf(c);
-        f32x4 Un[4], On[4];
+        u32x3 Un[4], On[4];
         float gn = 0.f;
         if constexpr (!LAST) load_strip(rec_of(c + 1), Un, On, gn);
         f16x8 Sh[NKS];
@@ -1563,7 +1589,7 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
         __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
         if constexpr (!LAST) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) { Uf[mt] = Un[mt]; Of[mt] = On[mt]; }
+            for (int mt = 0; mt < 4; ++mt) { Uf[mt] = unpack24(Un[mt]); Of[mt] = unpack24(On[mt]); }
             gm = gn;
         }
     };
