@@ -31,7 +31,8 @@
 //    products that form W', Qt, U', Ol);
 //  - in the state pass: fp16 MFMA (11-bit significand) with W', Qt and the
 //    state as single fp16 operands, and K and Delta' as bf16 hi + lo pairs
-//    (three MFMAs for K^T Delta').
+//    (three MFMAs for K^T Delta'); U' and Ol enter the fp32 accumulators with a
+//    relative step of 2^-16 (24-bit floats, as precise as a hi + lo pair).
 //    The query scale is applied to the fp32 outputs after the MFMAs (O is linear in
 //    it), so it never enters a 16-bit operand.  fp16 operands assume |state| < 6.5e4;
 //    the fp32 master state is never rounded, and a state beyond that range makes the
@@ -44,9 +45,10 @@
 //    Explicit T = (I + A)^-1 and M = P T by block back substitution, then four
 //    products.  Writes -W' = -diag(e^{G_c - G}) W and Qt as fp16 MFMA A-operand
 //    fragments, K^T as bf16 hi / lo A-operand fragments, and
-//    U' = diag(e^{G_c - G}) U and Ol^T as fp32 accumulator-layout tiles, so the
-//    state pass reads every operand with one coalesced 16-byte load per lane and
-//    every product accumulates straight into its MFMA chain:
+//    U' = diag(e^{G_c - G}) U and Ol^T as accumulator-layout tiles of 24-bit floats
+//    (fp32 with the low byte rounded away, 12 bytes per lane and tile), so the
+//    state pass reads every operand with one coalesced load per lane and every
+//    product accumulates straight into its MFMA chain:
 //      Delta' = diag(e^{G_c - G}) Delta = U' + (-W') S,   O^T = Ol^T + S^T Qt^T,
 //      S' = e^{G_c} S + K^T Delta'.
 //    O is formed transposed (the same fragments with A and B swapped) so that a
