@@ -470,6 +470,10 @@ struct LocalArgs {
     int order;
     flag_t *flags;
     flag_t flag_val;
+    // value heads per stored K^T: the value heads of a key head share k, so with kgroup > 1
+    // only a group's first head stores the K^T fragments of its records (the state pass
+    // reads them from there)
+    int kgroup;
 };
 
 // The chunk-local work of workgroup (slot, value head h): smem is the workgroup's LDS
@@ -832,8 +836,10 @@ __device__ __forceinline__ void chunk_local_body(char *smem, int *tflag_, int sl
                 Bop[hh][kt] = Split8{to_bf16x8(Kth[2 * kt][hh], Kth[2 * kt + 1][hh]),
                                      to_bf16x8(Ktl[2 * kt][hh], Ktl[2 * kt + 1][hh])};
                 const int off = R::K_OFF + ((m * 2 + kt) * 64 + lane) * 16;
-                rec_store16(rec, off, Bop[hh][kt].hi, flags != nullptr);
-                rec_store16(rec, off + NF_K * 64 * 16, Bop[hh][kt].lo, flags != nullptr);
+                if (h % P.kgroup == 0) {
+                    rec_store16(rec, off, Bop[hh][kt].hi, flags != nullptr);
+                    rec_store16(rec, off + NF_K * 64 * 16, Bop[hh][kt].lo, flags != nullptr);
+                }
             }
         }
     } else {
@@ -1258,6 +1264,7 @@ struct StateArgs {
     flag_t flag_val;
     ConvOut cv;
     unsigned long long *status;
+    int kgroup;   // as in LocalArgs: head h's K^T is in the records of head h - h % kgroup
 };
 
 // The state pass of workgroup b (waves 0 .. 3 of the workgroup; further waves only take the
@@ -1327,9 +1334,12 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
         // Each copy wave moves half of the A operands with direct-to-LDS buffer loads
         // (lane l of each 16-byte load lands at base + 16 l), then waits for them before
         // the barrier that hands the buffer to the compute waves.
+        // (wave 2: -W' and Qt; wave 3: K^T, from the record of the key group's first head)
         const int half = (wave - 2) * (ABYTES / 2);
+        static_assert(ABYTES / 2 == R::K_OFF, "the second half is K^T");
+        const int hsrc = wave == 3 ? h - h % P.kgroup : h;
         auto stage = [&](int c, char *dst) {
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(rec_of(c), R::SIZE);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(ws + ((size_t)hsrc * ncmax + gbase + c) * R::SIZE, R::SIZE);
             // the NP workgroups of a head copy the same record at the same time: each starts
             // at its own NP-th of the half, so that at any moment they read different lines
             copy_to_lds<COH ? kCohAux : 0>(r, half, dst + half, ABYTES / 2, lane, pair * (ABYTES / 2 / 1024 / NP));
@@ -1759,6 +1769,7 @@ static LocalArgs<TX, TW> local_args(const PrefillArgs &a, int nc, int g0, int g1
     P.order = a.order;
     P.flags = flags;
     P.flag_val = flag_val;
+    P.kgroup = flags ? 1 : a.Hv / a.Hk;
     return P;
 }
 
@@ -1800,6 +1811,7 @@ static StateArgs state_args(const PrefillArgs &a, int nc, int g0, int g1, const 
     P.flag_val = flag_val;
     P.cv = flags ? cv : ConvOut{};
     P.status = reinterpret_cast<unsigned long long *>(a.ws);
+    P.kgroup = flags ? 1 : a.Hv / a.Hk;
     return P;
 }
 
