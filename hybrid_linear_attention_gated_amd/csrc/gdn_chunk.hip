@@ -1288,7 +1288,12 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
     auto abuf = [lds](int i) { return lds + (i & 1) * ABYTES; };
 
     // block -> (unit, strip pair) so that the NP blocks of one unit land on the same XCD
-    const int u = 8 * (b / (8 * NP)) + (b % 8);
+    // (workgroups are dealt to the 8 XCDs in turn).  When a key group's value heads share the
+    // K^T records and the units fill whole runs of 8 groups, the units of a group land on one
+    // XCD as well, so the group's later heads find its K^T lines in that XCD's L2.
+    const int v = 8 * (b / (8 * NP)) + (b % 8);
+    const int G = P.kgroup;
+    const int u = (G > 1 && units % (8 * G) == 0) ? 8 * G * (v / (8 * G)) + G * (v % 8) + (v / 8) % G : v;
     const int pair = (b / 8) % NP;
     if (u >= units) return;
     // With a few sequences (N <= 64) the units go to the sequences longest first, so the
