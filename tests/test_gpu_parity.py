@@ -187,6 +187,17 @@ def test_core_chunked_gqa_scale_slow_decay(gdn, d):
     _core_case(gdn, wl, "mfma")
 
 
+@pytest.mark.parametrize("Hk,Hv,lengths", [(2, 8, [300, 129, 64, 1]), (1, 8, [190, 0, 65, 7, 128, 64, 33, 250])])
+def test_core_chunked_key_groups(gdn, Hk, Hv, lengths):
+    """Four and eight value heads per key head at d = 128 in the sequential schedule: only a
+    key group's first value head stores K^T in its records and the state passes of the
+    others copy it from there; the (sequence, head) units fill whole runs of 8 groups, so a
+    group's units also share an XCD.  Every head against the oracle."""
+    announce(f"core chunked d=128, {Hv // Hk} value heads per key head, lengths={lengths}")
+    wl = inputs.core_workload("kgrp", 720 + Hv // Hk + len(lengths), lengths, Hk, Hv, 128, 128, random_states=True)
+    _core_case(gdn, wl, "mfma")
+
+
 def test_core_chunked_inplace_state(gdn):
     announce("core chunked in-place state (final_state aliases initial_state)")
     wl = inputs.core_workload("inplace", 801, [150, 64], 2, 2, 128, 128, random_states=True)
