@@ -244,7 +244,7 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
                  void *conv_state_out, const float *g, const float *beta, const float *initial_state,
                  float *final_state, float *o, float scale, float l2_eps, int T, int Hk, int Hv, int dk, int dv,
                  int dtype, int order, void *workspace, size_t workspace_bytes, void *stream, int phases,
-                 bool layer_types = false) {
+                 bool layer_types = false, gdn::NormEpi *norm = nullptr) {
     try {
         if (int e = check_seqs(cu_seqlens, N, T)) return e;
         if (!conv_w || (T > 0 && (!x || !g || !beta || ((phases & 2) && !o)))) return GDN_ERR_NULL_POINTER;
@@ -278,6 +278,7 @@ int prefill_impl(const void *x, const void *conv_w, const int32_t *cu_seqlens, i
         gdn::PrefillArgs a{nullptr, nullptr, nullptr, g, beta, cu_seqlens, N, initial_state, final_state, o, scale,
                            T, Hk, Hv, dk, dv, workspace, workspace_bytes, &fp};
         a.order = order;
+        a.norm = norm;
         hipStream_t st = (hipStream_t)stream;
         const bool dbg = debug_check();
         if (dbg) {
@@ -457,11 +458,12 @@ int check_layer_shape(int E, int Hk, int Hv, int dk, int dv) {
 }
 
 struct LayerWs {
-    size_t x, z, g, beta, o, core, total;
+    size_t x, z, g, beta, o, nsums, core, total;
 };
 
 // x fp32 [T][conv_dim], z bf16 [T][Hv dv] (then the normalised output in its place), g and
-// beta fp32 [T][Hv], the recurrence output fp32 [T][Hv dv], then the prefill's own workspace.
+// beta fp32 [T][Hv], the recurrence output fp32 [T][Hv dv], the flags of the epilogue formed
+// (row-sum words) formed in the prefill, then the prefill's own workspace.
 LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerWs w{};
@@ -470,9 +472,17 @@ LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
     w.g = w.z + align256((size_t)T * Z * 2);
     w.beta = w.g + align256((size_t)T * Hv * 4);
     w.o = w.beta + align256((size_t)T * Hv * 4);
-    w.core = w.o + align256((size_t)T * Z * 4);
+    w.nsums = w.o + align256((size_t)T * Z * 4);
+    w.core = w.nsums + align256(gdn::norm_epi_words(T, N, Hv, dv) * 8);
     w.total = w.core + align256(gdn::chunked_workspace_bytes(T, N, Hv, dk, dv));
     return w;
+}
+
+// GDN_LAYER_NORM_SEPARATE set (and not "0"): the layer's prefill runs its gated RMSNorm as a
+// pass of its own even where the prefill could form it (read at every call; for tests).
+bool layer_norm_separate() {
+    const char *v = std::getenv("GDN_LAYER_NORM_SEPARATE");
+    return v && *v && std::strcmp(v, "0") != 0;
 }
 
 struct LayerDecodeWs {
@@ -574,13 +584,15 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
         float *o = reinterpret_cast<float *>(ws + L.o);
         hipStream_t st = (hipStream_t)stream;
         if (int e = in_proj_impl(hidden, w_in, x, z, g, beta, T, E, Hk, Hv, dk, dv, st, true)) return e;
+        // the normalised output replaces z (bf16) in place, then feeds the output projection:
+        // formed by the prefill where its schedule allows, else as a pass of its own over o
+        gdn::NormEpi ne{z, gamma, z, norm_eps, reinterpret_cast<unsigned long long *>(ws + L.nsums)};
         if (int e = prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
                                  final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_F32, order, ws + L.core,
-                                 L.total - L.core, stream, 3, true))
+                                 L.total - L.core, stream, 3, true, layer_norm_separate() ? nullptr : &ne))
             return e;
-        // the normalised output replaces z (bf16) in place, then feeds the output projection
         gdn::NormArgs na{o, z, gamma, z, (long)T * Hv, dv, norm_eps, true};
-        if (T > 0)
+        if (T > 0 && !ne.fused)
             if (int e = hip_status(gdn::launch_gated_rmsnorm(na, st))) return e;
         return linear_impl(z, w_out, out, T, E, (int)Z, st);
     } catch (...) {

@@ -1249,8 +1249,20 @@ __device__ __forceinline__ int seq_by_rank(const int32_t *cu, int N, int Ttot, i
 // COH: records come from a concurrently running chunk-local kernel (wait for each chunk's
 // flag, read device-coherently; the conv cache of the fused prefill is written here, see
 // ConvOut); otherwise plain cached reads.
-template <int D>
-constexpr int state_lds_bytes() { return 2 * Rec<D>::U_OFF; }
+// Gated RMSNorm epilogue in the state pass (NORM instances, D = 128, the concurrent
+// schedule's eight-wave workgroups; the layer output of "7.6 Qwen3.5: the linear-attention
+// hybrid", section 7.6.2: the core output passes RMSNorm and is gated by SiLU(z), the
+// RMSNorm of section 7.6.3 in fp32 with the gain as given).  The compute waves leave each
+// chunk's two O strips in LDS instead of storing them; waves 6 and 7, otherwise idle,
+// take them, publish each row's sum of squares over the workgroup's 32 columns, combine
+// the four workgroups' sums of the row a few steps later and write the normalised, gated
+// rows.  o never reaches memory.
+constexpr int kNormOst = 36;                        // fp32 row stride of a staged O strip pair
+constexpr int kNormBuf = kChunk * kNormOst * 4;     // one chunk's staged strips (bytes)
+constexpr int kNormLag = 4;                         // a row sum stored in step j + 1 is loaded in step j + kNormLag
+
+template <int D, bool NORM = false>
+constexpr int state_lds_bytes() { return 2 * Rec<D>::U_OFF + (NORM ? 2 * kNormBuf : 0); }
 
 struct StateArgs {
     const char *ws;
@@ -1265,12 +1277,212 @@ struct StateArgs {
     ConvOut cv;
     unsigned long long *status;
     int kgroup;   // as in LocalArgs: head h's K^T is in the records of head h - h % kgroup
+    // gated RMSNorm epilogue (NORM instances): gate rows z and output rows out ([T][Hv D]
+    // bf16, out may be z), the gain (D), epsilon, and the row-sum words
+    // [Hv][ncmax][D / 32][64] (high half: the call's tag, low half: the fp32 sum)
+    const bf16 *nz = nullptr, *ngamma = nullptr;
+    bf16 *nout = nullptr;
+    float neps = 0.f;
+    unsigned long long *nsums = nullptr;
 };
+
+// The NW norm waves of one state-pass workgroup (w = 0 .. NW - 1: waves 8 - NW .. 7; wave w
+// takes rows 64 w / NW .. of every chunk, NW lanes of 32 / NW columns per row; the workgroup's
+// strip pair p holds columns 32 p .. 32 p + 31).  Waves w and w + 4 of a workgroup share a
+// SIMD, so waves 6 and 7 (NW = 2) run beside the copy waves; four norm waves, two of them
+// beside the compute waves, measured 3 to 4 us slower per call at 4096 tokens x 16 heads.
+// They take the compute waves' barriers.  For chunk j:
+//  - step j + 1, first thing: its O strips from LDS into registers; each row's sum of
+//    squares over the 32 columns goes out as one 64-bit word, the call's tag in the high
+//    half and the sum in the low half (a single store: no flag, no wait for completion);
+//  - step j + kNormLag: the words of the head's D / 32 workgroups for these rows, and the
+//    gates, are loaded;
+//  - step j + kNormLag + 2: once every word carries the tag, the sums are added in
+//    workgroup order (the same in every workgroup, so results do not depend on timing) and
+//    the normalised, gated rows are stored.
+// A word is loaded three steps after it was stored and used two steps after that, so no
+// barrier waits on device-coherent traffic unless a workgroup of the head lags (with two
+// steps, measured at 4096 tokens x 16 heads, 8 % of the loads still missed a word and the
+// waits fed each other); the last chunks are finished after the loop.  A wait that runs out
+// (the bound of the record waits) reports GDN_ERR_TIMEOUT and writes NaN.
+template <int D, int NW>
+__device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf, int w, int lane, int pair, int h,
+                                           int t0, int L, int c_lo, int c_hi, int gbase, unsigned tag) {
+    constexpr int NP = D / 32;          // workgroups per head (strip pairs)
+    constexpr int RPW = kChunk / NW;    // rows per wave
+    constexpr int LPR = kWave / RPW;    // lanes per row
+    constexpr int CPL = 32 / LPR;       // columns per lane
+    constexpr int WPL = NP / LPR;       // row-sum words per lane
+    static_assert(NP == 4 && (NW == 2 || NW == 4) && CPL % 8 == 0 && WPL >= 1, "norm lane layout");
+    const int Hv = P.Hv;
+    const int q = lane % LPR;                         // lane in its row
+    const int r = RPW * w + lane / LPR;               // row in the chunk
+    const int cl = CPL * q;                           // first column in the workgroup's 32
+    const int cb = 32 * pair + cl;                    // first column in the head
+    const size_t rstride = (size_t)Hv * D;
+    float gm[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL / 8; ++i) {
+        const bf16x8 g8 = *reinterpret_cast<const bf16x8 *>(P.ngamma + cb + 8 * i);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gm[8 * i + e] = (float)g8[e];
+    }
+    int spin_max = kSpinMax;
+    {
+        const unsigned long long sw = __hip_atomic_load(P.status + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(sw >> 32) == kSpinTag) spin_max = (int)(sw & 0x7fffffffu);
+    }
+    unsigned long long *sums = P.nsums + ((size_t)h * P.ncmax + gbase) * NP * 64;   // chunk c: + c * NP * 64
+    auto rows_of = [&](int c) { return min(kChunk, L - c * kChunk); };
+    struct Strip { f32x4 v[CPL / 4]; };
+    struct Pend {
+        unsigned long long wd[WPL];   // the words of workgroups WPL q .. WPL q + WPL - 1
+        bf16x8 z[CPL / 8];
+    };
+    // step j + 1: chunk j's strips from LDS (buffer j & 1), row sums out
+    auto take = [&](int c, Strip &S_) {
+        const float *src = reinterpret_cast<const float *>(obuf + (c & 1) * kNormBuf) + r * kNormOst + cl;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL / 4; ++i) {
+            S_.v[i] = *reinterpret_cast<const f32x4 *>(src + 4 * i);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss = fmaf(S_.v[i][e], S_.v[i][e], ss);
+        }
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, kWave);   // the same value in every lane of the row
+        // every lane of the row stores the same word (no branch around the store)
+        __hip_atomic_store(sums + ((size_t)c * NP + pair) * 64 + r,
+                           ((unsigned long long)tag << 32) | __builtin_bit_cast(unsigned, ss), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto load_words = [&](int c, Pend &Q) {
+#pragma unroll
+        for (int i = 0; i < WPL; ++i)
+            Q.wd[i] = __hip_atomic_load(sums + ((size_t)c * NP + WPL * q + i) * 64 + r, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    };
+    // step j + kNormLag: the words and gates of chunk j (full: all its rows are tokens)
+    auto fetch = [&](int c, Pend &Q, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        load_words(c, Q);
+        if (FULL || r < rows_of(c)) {
+            const bf16 *zr = P.nz + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
+#pragma unroll
+            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = *reinterpret_cast<const bf16x8 *>(zr + 8 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = bf16x8{};
+        }
+    };
+    auto tagged = [&](const Pend &Q) {
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) ok = ok && (unsigned)(Q.wd[i] >> 32) == tag;
+        return __ballot(!ok) == 0;
+    };
+    // step j + kNormLag + 2: out = o * rsqrt(mean o^2 + eps) * gamma * SiLU(z)
+    auto finish = [&](int c, const Strip &S_, Pend &Q, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        bool ok = tagged(Q);
+        for (int it = 0; !ok && it < spin_max; ++it) {
+            __builtin_amdgcn_s_sleep(2);
+            load_words(c, Q);
+            ok = tagged(Q);
+        }
+        if (!ok && lane == 0) report_status(P.status, kStatusTimeout);
+        // the NP sums of the row, added in workgroup order (word p sits in lane p / WPL of the row)
+        float tot = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            tot += __shfl(__builtin_bit_cast(float, (unsigned)Q.wd[p % WPL]), lane - q + p / WPL, kWave);
+        const float rn = ok ? rsqrtf(tot * (1.0f / D) + P.neps) : __builtin_nanf("");
+        if (FULL || r < rows_of(c)) {
+            bf16x8 y[CPL / 8];
+#pragma unroll
+            for (int k = 0; k < CPL; ++k)
+                y[k / 8][k % 8] = (bf16)(S_.v[k / 4][k % 4] * rn * gm[k] * silu((float)Q.z[k / 8][k % 8]));
+            bf16 *yr = P.nout + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
+#pragma unroll
+            for (int i = 0; i < CPL / 8; ++i) *reinterpret_cast<bf16x8 *>(yr + 8 * i) = y[i];
+        }
+    };
+
+    static_assert(kNormLag == 4, "the loop below keeps five strips and two loads in flight");
+    __syncthreads();   // the compute waves' barrier after their first loads
+    // At the top of step c: s0 .. s4 = strips of chunks c - 2 .. c - 6 (LDS reads, complete);
+    // the slot of step c (pa when c - c_lo is even, else pb) holds the words and gates of
+    // chunk c - 6, the other one those of chunk c - 5, still in flight.  The loads are never
+    // copied (a copy would wait for them), and the steps from c_lo + 6 on, whose chunks are
+    // all full, have no memory access behind a branch, so the compiler can count them and
+    // waits for each load only where it is used.
+    Strip s0, s1, s2, s3, s4;
+    Pend pa, pb;
+    const std::true_type full{};
+    const std::false_type part{};
+    // chunk c - 1's strips are taken first (its row sums go out before any wait of the
+    // step) and enter s0 only after chunk c - 6 has been finished from s4
+    auto shift_in = [&](const Strip &t) {
+        s4 = s3;
+        s3 = s2;
+        s2 = s1;
+        s1 = s0;
+        s0 = t;
+    };
+    auto first_step = [&](int c, Pend &pq) {   // c < c_lo + 6: only the actions that exist
+        if (c - 1 >= c_lo) {
+            Strip t;
+            take(c - 1, t);
+            shift_in(t);
+        }
+        if (c - 4 >= c_lo) fetch(c - 4, pq, part);
+        __syncthreads();
+    };
+    auto step = [&](int c, Pend &pq) {         // c >= c_lo + 6: chunks c - 6 and c - 4 are full
+        Strip t;
+        take(c - 1, t);
+        finish(c - 6, s4, pq, full);
+        fetch(c - 4, pq, full);
+        shift_in(t);
+        __syncthreads();
+    };
+    const int cs = min(c_hi, c_lo + 6);
+    for (int c = c_lo; c < cs; ++c) {
+        if ((c - c_lo) & 1) first_step(c, pb);
+        else first_step(c, pa);
+    }
+    int c = cs;
+    for (; c + 1 < c_hi; c += 2) {   // c - c_lo is even here
+        step(c, pa);
+        step(c + 1, pb);
+    }
+    if (c < c_hi) step(c, pa);
+    // after the last step: s0 .. s4 = chunks c_hi - 2 .. c_hi - 6; the slot of step c_hi
+    // holds chunk c_hi - 6, the other chunk c_hi - 5
+    auto tail = [&](Pend &p6, Pend &p5) {
+        Strip sl;
+        if (c_hi - 1 >= c_lo) take(c_hi - 1, sl);
+        if (c_hi - 6 >= c_lo) finish(c_hi - 6, s4, p6, part);
+        Pend q3, q2, q1;
+        if (c_hi - 4 >= c_lo) fetch(c_hi - 4, p6, part);
+        if (c_hi - 3 >= c_lo) fetch(c_hi - 3, q3, part);
+        if (c_hi - 2 >= c_lo) fetch(c_hi - 2, q2, part);
+        if (c_hi - 1 >= c_lo) fetch(c_hi - 1, q1, part);
+        if (c_hi - 5 >= c_lo) finish(c_hi - 5, s3, p5, part);
+        if (c_hi - 4 >= c_lo) finish(c_hi - 4, s2, p6, part);
+        if (c_hi - 3 >= c_lo) finish(c_hi - 3, s1, q3, part);
+        if (c_hi - 2 >= c_lo) finish(c_hi - 2, s0, q2, part);
+        if (c_hi - 1 >= c_lo) finish(c_hi - 1, sl, q1, part);
+    };
+    if ((c_hi - c_lo) & 1) tail(pb, pa);
+    else tail(pa, pb);
+}
 
 // The state pass of workgroup b (waves 0 .. 3 of the workgroup; further waves only take the
 // barriers): lds is the workgroup's LDS (state_lds_bytes), sfail_ one LDS word.
-template <int D, bool COH>
+template <int D, bool COH, bool NORM = false>
 __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, const StateArgs &P) {
+    static_assert(!NORM || (COH && D == 128), "the norm epilogue runs in the concurrent schedule at D = 128");
     using R = Rec<D>;
     constexpr int NKS = R::NKS, NTD = R::NTD, NS = D / 16, NP = NS / 2;
     constexpr int ABYTES = R::U_OFF;                  // A-operand fragments of one chunk
@@ -1329,6 +1541,13 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
     __syncthreads();
 
     if (wave >= 4) {
+        if constexpr (NORM) {
+            if (wave >= 6) {   // the SIMDs of the copy waves
+                norm_waves<D, 2>(P, lds + 2 * ABYTES, wave - 6, lane, pair, h, t0, L, c_lo, c_hi, gbase,
+                                 (unsigned)(flag_val >> 32) ^ (unsigned)flag_val);
+                return;
+            }
+        }
         // waves past the state pass's four (eight-wave workgroups of the combined kernel): they
         // take the same barriers as the copy waves and nothing else
         __syncthreads();
@@ -1600,7 +1819,11 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
             if (!LAST || 16 * mt + l16 < rows) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) nfacc = __builtin_fmaf(Ot[mt][e], 0.f, nfacc);
-                *reinterpret_cast<f32x4 *>(ob + o_lane + 16 * mt * row_stride) = Ot[mt];
+                if constexpr (NORM)   // to the norm waves: row 16 mt + l16, this strip's columns
+                    *reinterpret_cast<f32x4 *>(lds + 2 * ABYTES + (c & 1) * kNormBuf +
+                                               ((16 * mt + l16) * kNormOst + 16 * (wave & 1) + 4 * kg) * 4) = Ot[mt];
+                else
+                    *reinterpret_cast<f32x4 *>(ob + o_lane + 16 * mt * row_stride) = Ot[mt];
             }
         }
         __syncthreads();                 // next chunk's A operands are in LDS; buffer c & 1 is free
@@ -1612,6 +1835,7 @@ __device__ __forceinline__ void state_pass_body(char *lds, int *sfail_, int b, c
     };
     for (int c = c_lo; c + 1 < c_hi; ++c) chunk_step(c, std::false_type{});
     if (c_lo < c_hi) chunk_step(c_hi - 1, std::true_type{});
+
     if (s_out) {
         const bool poison = COH && sfail;
 #pragma unroll
@@ -1643,15 +1867,16 @@ __global__ __launch_bounds__(256) void state_pass_kernel(StateArgs P) {
 // fall on the same XCD) end at once.
 // Workgroups are dispatched in index order, so a state-pass workgroup starts only once every
 // producer has been dispatched, and producers never wait: every wait ends.
-template <int D, bool FUSED, typename TX, typename TW>
+// NORM: the state pass also forms the gated RMSNorm epilogue (norm_waves).
+template <int D, bool FUSED, typename TX, typename TW, bool NORM = false>
 __global__ __launch_bounds__(LocalShape<D>::THREADS) void prefill_concurrent_kernel(LocalArgs<TX, TW> PL,
                                                                                     StateArgs PS, int soff) {
-    constexpr int LB = local_lds_bytes<D, TX, FUSED>(), SB = state_lds_bytes<D>();
+    constexpr int LB = local_lds_bytes<D, TX, FUSED>(), SB = state_lds_bytes<D, NORM>();
     __shared__ __attribute__((aligned(16))) char lds[LB > SB ? LB : SB];
     __shared__ int word;
     const int b = blockIdx.x;
     if (b >= soff) {
-        state_pass_body<D, true>(lds, &word, b - soff, PS);
+        state_pass_body<D, true, NORM>(lds, &word, b - soff, PS);
     } else if (b < PL.nslots * PL.Hv) {
         chunk_local_body<D, FUSED, TX, TW>(lds, &word, b % PL.nslots, b / PL.nslots, PL);
     }
@@ -1679,6 +1904,8 @@ size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     const size_t nc = max_chunks(T, N);
     return kWsHeader + flags_offset(nc, N, Hv, dk) + nc * (size_t)Hv * sizeof(flag_t);
 }
+
+size_t norm_epi_words(int T, int N, int Hv, int dv) { return max_chunks(T, N) * (size_t)Hv * (dv / 32) * 64; }
 
 // ---- segment pipeline of gdn_chunk_prefill: the packed chunk range is cut into
 // segments; the chunk-local kernel of segment k + 1 runs on the caller's stream while
@@ -1843,13 +2070,34 @@ __global__ void zero_flags_kernel(flag_t *f, int n) {
 
 // The combined kernel of the concurrent schedule on `st`: the chunk-local workgroups on the
 // compute units the state pass leaves, then the state pass's.
+// Whether the concurrent schedule of this call forms the gated RMSNorm epilogue itself: the
+// layer's element types (fp32 x, bf16 conv weights) at D = 128.
+template <int D>
+static bool norm_fused(const PrefillArgs &a) {
+    return D == 128 && a.norm && a.fp && !a.fp->bf16 && a.fp->w_bf16;
+}
+
 template <int D>
 static hipError_t launch_concurrent(const PrefillArgs &a, hipStream_t st, int nc, int cus, int sblocks,
                                     flag_t *flags, flag_t flag_val, const ConvOut &cv) {
     const int nslots = local_slots(cus - sblocks, nc, a.Hv);
     const int soff = (nslots * a.Hv + 7) / 8 * 8;
     const dim3 grid((unsigned)(soff + sblocks)), block(LocalShape<D>::THREADS);
-    const StateArgs PS = state_args<D>(a, nc, 0, nc, flags, flag_val, cv);
+    StateArgs PS = state_args<D>(a, nc, 0, nc, flags, flag_val, cv);
+    if constexpr (D == 128) {
+        if (norm_fused<D>(a)) {
+            PS.nz = static_cast<const bf16 *>(a.norm->z);
+            PS.ngamma = static_cast<const bf16 *>(a.norm->gamma);
+            PS.nout = static_cast<bf16 *>(a.norm->out);
+            PS.neps = a.norm->eps;
+            PS.nsums = a.norm->sums;
+            hipLaunchKernelGGL((prefill_concurrent_kernel<D, true, float, bf16, true>), grid, block, 0, st,
+                               local_args<float, bf16>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
+            const hipError_t e = hipGetLastError();
+            if (e == hipSuccess) a.norm->fused = true;
+            return e;
+        }
+    }
     if (!a.fp) {
         hipLaunchKernelGGL((prefill_concurrent_kernel<D, false, float, float>), grid, block, 0, st,
                            local_args<float, float>(a, nc, 0, nc, nslots, flags, flag_val), PS, soff);
@@ -1934,6 +2182,11 @@ static hipError_t launch_chunked_t(const PrefillArgs &a, hipStream_t st, int pha
             const int nflags = nc * a.Hv;
             hipLaunchKernelGGL(zero_flags_kernel, dim3((nflags + 255) / 256), dim3(256), 0, st, flags, nflags);
             if ((e = hipGetLastError()) != hipSuccess) return e;
+            if (norm_fused<D>(a)) {   // the epilogue's row-sum words as well
+                const int nn = nflags * (D / 32) * 64;
+                hipLaunchKernelGGL(zero_flags_kernel, dim3((nn + 255) / 256), dim3(256), 0, st, a.norm->sums, nn);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+            }
             return launch_concurrent<D>(a, st, nc, cus, sblocks, flags, ((flag_t)kFlagTagGraph << 32) | 1u, cv);
         }
         if ((e = launch_local<D>(a, st, nc, 0, nc)) != hipSuccess) return e;

@@ -43,6 +43,22 @@ struct FusedPrep {
     bool w_bf16 = false;   // with bf16 false: conv_w is bf16 while x and the conv states are fp32
 };
 
+// Gated RMSNorm epilogue formed inside the prefill (the layer's prefill): out = o *
+// rsqrt(mean o^2 + eps) * gamma * SiLU(z) per (token, value head) row of dv channels, all
+// bf16 ([T][Hv dv] rows; out may be z itself).  `sums` holds the row-sum words the
+// workgroups of a head exchange (norm_epi_words of them).  The launcher applies it where
+// its schedule can (and then sets `fused`); otherwise the caller runs the separate
+// epilogue over o.
+struct NormEpi {
+    const void *z, *gamma;
+    void *out;
+    float eps;
+    unsigned long long *sums;
+    bool fused = false;
+};
+// 64-bit words NormEpi::sums needs for T tokens in N sequences and Hv value heads of dv channels
+size_t norm_epi_words(int T, int N, int Hv, int dv);
+
 struct PrefillArgs {
     const float *q, *k, *v;
     const float *g, *beta;
@@ -57,6 +73,7 @@ struct PrefillArgs {
     size_t ws_bytes;
     const FusedPrep *fp = nullptr;   // set: fused prep (chunked path only)
     int order = 0;                   // 0: decay before the retrieval, 1: retrieval from the undecayed state
+    NormEpi *norm = nullptr;         // set: the gated RMSNorm epilogue where the schedule allows it
 };
 
 struct DecodeArgs {

@@ -29,6 +29,7 @@ size_t chunked_workspace_bytes(int T, int N, int Hv, int dk, int dv) {
     return kWsHeader + ((size_t)T / 64 + (size_t)N) * (size_t)Hv * ((size_t)dk * 1024 + 256) +
            (size_t)N * Hv * dk * dk * 4;
 }
+size_t norm_epi_words(int T, int N, int Hv, int dv) { return ((size_t)T / 64 + (size_t)N) * (size_t)Hv * (dv / 32) * 64; }
 hipError_t launch_prefill_chunked(const PrefillArgs &, hipStream_t, int) { ++g_launches; return hipSuccess; }
 hipError_t workspace_status(void *ws, hipStream_t, unsigned long long *word, bool clear) {
     std::memcpy(word, ws, sizeof(*word));   // host memory stands in for the workspace

@@ -161,6 +161,84 @@ def test_layer_prefill_grid_inputs(gdn):
     _check_layer(*gpu, *ref)
 
 
+def test_layer_prefill_norm_in_prefill_ragged(gdn):
+    """Four sequences (3000, 3, 2900 and 64 tokens) over 2 key / 4 value heads of 128, caches
+    in: 16 (sequence, head) units and 97 chunks put the prefill in its concurrent schedule,
+    where the state pass forms the gated RMSNorm itself (ragged last chunks, a sequence
+    shorter than the conv window, one of exactly one chunk)."""
+    announce("layer prefill, norm formed in the prefill, 4 ragged sequences, Hk=2 Hv=4 d=128")
+    gpu, ref = _layer_case(gdn, [3000, 3, 2900, 64], 256, 2, 4, 128, 655, True, 0.5)
+    _check_layer(*gpu, *ref)
+
+
+def _layer_4k_bench_run(gdn, separate, monkeypatch, **kw):
+    wts = inputs.layer_weights(7, 1024, 16, 16, 128, 128)
+    h = _cuda(inputs.layer_hidden(8, 4096, 1024))
+    w = [_cuda(t) for t in (wts.w_in, wts.conv_w, wts.gamma, wts.w_out)]
+    if separate:
+        monkeypatch.setenv("GDN_LAYER_NORM_SEPARATE", "1")
+    else:
+        monkeypatch.delenv("GDN_LAYER_NORM_SEPARATE", raising=False)
+    out, fin = gdn.layer_prefill(h, *w, 16, 16, 128, 128, **kw)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("GDN_LAYER_NORM_SEPARATE", raising=False)
+    return (h, w), out, fin
+
+
+def test_layer_prefill_norm_in_prefill_vs_separate_pass(gdn, monkeypatch):
+    """The bench's layer (T = 4096, hidden 1024, 16 / 16 heads of 128) with the gated RMSNorm
+    formed inside the prefill against the same call with the norm as a pass of its own over
+    the fp32 core output (GDN_LAYER_NORM_SEPARATE).  The two take each row's mean square in
+    different orders, so a few normalised values (a few dozen of 8.4 M) round to the
+    neighbouring bf16 value, and the output projection spreads each such one-ulp change over
+    a row of the output.  So: the final states are bit-identical, fewer than 0.1 % of the
+    outputs differ, by at most 2^-5 of the output RMS (one bf16 ulp of an output near 1 is
+    about 1.3 % of it), and the outputs are not all equal (the two paths really ran)."""
+    announce("layer prefill T=4096: norm in the prefill vs a separate norm pass")
+    _, out_f, fin_f = _layer_4k_bench_run(gdn, False, monkeypatch)
+    _, out_s, fin_s = _layer_4k_bench_run(gdn, True, monkeypatch)
+    assert torch.equal(fin_f, fin_s), "the final states differ"
+    a, b = out_f.float(), out_s.float()
+    diff = (a - b).abs()
+    rms = float(b.pow(2).mean().sqrt())
+    assert float(diff.max()) <= 2.0 ** -5 * rms, f"max |diff| {float(diff.max()):.3g}, rms {rms:.3g}"
+    assert int((diff > 0).sum()) <= a.numel() // 1000, f"{int((diff > 0).sum())} outputs differ"
+    assert not torch.equal(out_f, out_s), "identical outputs: the norm was not formed in the prefill"
+
+
+def test_graph_capture_of_layer_prefill_4k(gdn, monkeypatch):
+    """gdn_layer_prefill at the bench's layer shape captured into a HIP graph: under capture
+    the prefill's ready flags and the norm's strip flags are cleared by kernels before the
+    combined launch.  Three replays with eager work in between, each bit-identical to the
+    eager call, then an eager call on the same workspace."""
+    announce("graph capture of gdn_layer_prefill at T=4096, three replays")
+    (h, w), out_ref, fin_ref = _layer_4k_bench_run(gdn, False, monkeypatch)
+    ws = torch.empty(gdn.layer_prefill_workspace_size(4096, 1, 16, 16, 128, 128), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(out_ref)
+    fin = torch.empty_like(fin_ref)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            gdn.layer_prefill(h, *w, 16, 16, 128, 128, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        fin.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, out_ref), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(fin, fin_ref), f"replay {rep}: final state differs from the eager call"
+        del junk
+    out.zero_()
+    gdn.layer_prefill(h, *w, 16, 16, 128, 128, out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref) and torch.equal(fin, fin_ref), "eager call after the replays differs"
+
+
 def test_layer_prefill_state_in_place(gdn):
     """final_state aliasing initial_state and conv_state_out aliasing conv_state_in (the
     exact aliases the ABI allows): the same results as separate output buffers."""
