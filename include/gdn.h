@@ -384,8 +384,14 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
 /*
  * gdn_layer_prefill -- the whole layer over packed sequences in one call: the input
  * projection (as gdn_in_proj, but x leaves it in fp32), gdn_prefill on the fp32 x,
- * gdn_gated_rmsnorm over each (token, value head) row (bf16 z, gamma and output), and
- * gdn_linear with w_out.
+ * the gated RMSNorm of gdn_gated_rmsnorm over each (token, value head) row (bf16 z,
+ * gamma and output), and gdn_linear with w_out.  Where the prefill runs its concurrent
+ * schedule at dk = dv = 128 (one launch; at most a quarter of the compute units for the
+ * state pass), the state pass forms the norm itself and the core output never reaches
+ * memory; the row's mean square is then summed in another order than
+ * gdn_gated_rmsnorm's, so a normalised value can differ from the separate pass's by one
+ * bf16 ulp.  The environment variable GDN_LAYER_NORM_SEPARATE (set, not "0"; read at
+ * every call) selects the separate pass everywhere.
  *   hidden [T][E], w_in as in gdn_in_proj, conv_w [conv_dim][4], gamma [dv] (the gain
  *   as applied), w_out [E][Hv*dv]: bf16.
  *   cu_seqlens, N, conv_state_in / conv_state_out [N][3][conv_dim] fp32,
@@ -393,8 +399,8 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
  *   gdn_prefill (the same exact aliases allowed).
  *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
  *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
- *              (x, z, g, beta, o and the prefill's workspace); must not overlap any
- *              other argument.
+ *              (x, z, g, beta, o, the norm's row-sum words and the prefill's
+ *              workspace); must not overlap any other argument.
  * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
  * The four steps run in order on `stream` (the prefill as in gdn_prefill).
  */
