@@ -68,7 +68,10 @@ def short_name(symbol: str) -> str:
         # FUSED = true; fp32 x (the layer's prefill) or 16-bit x
         return "chunk_local_fused_x32" if ("ELb1Ef" in symbol or ", true, float" in symbol) else "chunk_local_fused"
     if "prefill_concurrent_kernel" in symbol:
-        # chunk-local and state pass in one launch; fp32 x (the layer's prefill) or 16-bit x
+        # chunk-local and state pass in one launch; fp32 x (the layer's prefill) or 16-bit x;
+        # last template argument NORM = true: the layer's gated RMSNorm formed in the state pass
+        if "Lb1EEEv" in symbol or ", true>(" in symbol or symbol.endswith(", true>"):
+            return "prefill_concurrent_norm"
         fp32x = "ELb1Ef" in symbol or ", true, float" in symbol
         return "prefill_concurrent_x32" if fp32x else "prefill_concurrent"
     if "decode_kernel" in symbol and ("Lb1E" in symbol or ", true>" in symbol):

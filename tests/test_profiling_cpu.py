@@ -38,6 +38,16 @@ def test_short_names():
     assert profiling.short_name(
         "_ZN3gdn25prefill_concurrent_kernelILi128ELb1EfDF16bEEvNS_9LocalArgsIT1_T2_EENS_9StateArgsEi") == \
         "prefill_concurrent_x32"
+    assert profiling.short_name(
+        "_ZN3gdn25prefill_concurrent_kernelILi128ELb1EfDF16bLb0EEEvNS_9LocalArgsIT1_T2_EENS_9StateArgsEi") == \
+        "prefill_concurrent_x32"
+    assert profiling.short_name(
+        "_ZN3gdn25prefill_concurrent_kernelILi128ELb1EfDF16bLb1EEEvNS_9LocalArgsIT1_T2_EENS_9StateArgsEi") == \
+        "prefill_concurrent_norm"
+    assert profiling.short_name(
+        "void gdn::prefill_concurrent_kernel<128, true, float, __hip_bfloat16, true>(...)") == "prefill_concurrent_norm"
+    assert profiling.short_name(
+        "void gdn::prefill_concurrent_kernel<128, true, float, __hip_bfloat16, false>(...)") == "prefill_concurrent_x32"
     assert profiling.short_name(DECODE) == "decode"
     assert profiling.short_name(DECODE.replace("false>", "true>")) == "decode_gated"
     assert profiling.short_name(COPY) == "copy"
