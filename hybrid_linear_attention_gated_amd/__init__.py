@@ -243,8 +243,9 @@ def prefill_workspace_status(workspace) -> int:
 
 def set_wait_bound(workspace, iterations=None):
     """Write the workspace header word that bounds the concurrent state pass's waits for a
-    record (`iterations` of a ~128-cycle sleep), or restore the default (None).  For tests
-    of the timeout path."""
+    record or a row sum (`iterations` of a ~128-cycle sleep), or restore the default (None).
+    A prefill workspace or a layer prefill workspace (which starts with its prefill's).  For
+    tests of the timeout path."""
     _check(workspace, "workspace", torch.uint8)
     word = 0 if iterations is None else (_SPIN_TAG << 32) | int(iterations)
     workspace[8:16].copy_(torch.tensor([word], dtype=torch.int64).view(torch.uint8))

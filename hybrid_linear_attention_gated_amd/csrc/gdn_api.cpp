@@ -461,20 +461,21 @@ struct LayerWs {
     size_t x, z, g, beta, o, nsums, core, total;
 };
 
-// x fp32 [T][conv_dim], z bf16 [T][Hv dv] (then the normalised output in its place), g and
-// beta fp32 [T][Hv], the recurrence output fp32 [T][Hv dv], the flags of the epilogue formed
-// (row-sum words) formed in the prefill, then the prefill's own workspace.
+// The prefill's own workspace first (so its header, the status word and the wait bound, is the
+// layer workspace's), then x fp32 [T][conv_dim], z bf16 [T][Hv dv] (then the normalised output
+// in its place), g and beta fp32 [T][Hv], the recurrence output fp32 [T][Hv dv] and the row-sum
+// words of the norm formed in the prefill.
 LayerWs layer_ws(int T, int N, int Hk, int Hv, int dk, int dv) {
     const size_t C = 2 * (size_t)Hk * dk + (size_t)Hv * dv, Z = (size_t)Hv * dv;
     LayerWs w{};
-    w.x = 0;
+    w.core = 0;
+    w.x = w.core + align256(gdn::chunked_workspace_bytes(T, N, Hv, dk, dv));
     w.z = w.x + align256((size_t)T * C * 4);
     w.g = w.z + align256((size_t)T * Z * 2);
     w.beta = w.g + align256((size_t)T * Hv * 4);
     w.o = w.beta + align256((size_t)T * Hv * 4);
     w.nsums = w.o + align256((size_t)T * Z * 4);
-    w.core = w.nsums + align256(gdn::norm_epi_words(T, N, Hv, dv) * 8);
-    w.total = w.core + align256(gdn::chunked_workspace_bytes(T, N, Hv, dk, dv));
+    w.total = w.nsums + align256(gdn::norm_epi_words(T, N, Hv, dv) * 8);
     return w;
 }
 
@@ -589,7 +590,7 @@ int gdn_layer_prefill(const void *hidden, const void *w_in, const void *conv_w, 
         gdn::NormEpi ne{z, gamma, z, norm_eps, reinterpret_cast<unsigned long long *>(ws + L.nsums)};
         if (int e = prefill_impl(x, conv_w, cu_seqlens, N, conv_state_in, conv_state_out, g, beta, initial_state,
                                  final_state, o, scale, l2_eps, T, Hk, Hv, dk, dv, GDN_F32, order, ws + L.core,
-                                 L.total - L.core, stream, 3, true, layer_norm_separate() ? nullptr : &ne))
+                                 L.x - L.core, stream, 3, true, layer_norm_separate() ? nullptr : &ne))
             return e;
         gdn::NormArgs na{o, z, gamma, z, (long)T * Hv, dv, norm_eps, true};
         if (T > 0 && !ne.fused)

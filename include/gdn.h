@@ -257,12 +257,13 @@ int gdn_prefill(const void *x, const void *conv_w, const int32_t *cu_seqlens, in
 
 /*
  * gdn_prefill_workspace_status -- the outcome of the chunked prefills (gdn_chunk_prefill
- * with GDN_MATH_MFMA, the split phases, gdn_prefill, gdn_layer_prefill through its own
- * workspace's prefill part) that used `workspace` since the previous query.  Waits for
+ * with GDN_MATH_MFMA, the split phases, gdn_prefill, gdn_layer_prefill, whose workspace
+ * starts with its prefill's) that used `workspace` since the previous query.  Waits for
  * `stream` and the library's second stream on the current device, reads the status word
  * at the start of the workspace and clears it.
  *   GDN_OK             no failure recorded (or a word that no kernel wrote)
- *   GDN_ERR_TIMEOUT    a state pass stopped waiting for a record (outputs NaN)
+ *   GDN_ERR_TIMEOUT    a state pass stopped waiting for a record, or (the layer prefill's
+ *                      norm formed in the state pass) for a row sum (outputs NaN)
  *   GDN_ERR_NONFINITE  an output or a final state came out inf or NaN
  *   GDN_ERR_NULL_POINTER / GDN_ERR_ALIGN / GDN_ERR_WORKSPACE (fewer than 256 bytes),
  *   GDN_ERR_HIP        argument or runtime errors of the query itself
@@ -399,8 +400,9 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
  *   gdn_prefill (the same exact aliases allowed).
  *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
  *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
- *              (x, z, g, beta, o, the norm's row-sum words and the prefill's
- *              workspace); must not overlap any other argument.
+ *              (the prefill's workspace first, with its status word and wait bound,
+ *              then x, z, g, beta, o and the norm's row-sum words); must not overlap any
+ *              other argument.
  * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
  * The four steps run in order on `stream` (the prefill as in gdn_prefill).
  */

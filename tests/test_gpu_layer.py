@@ -239,6 +239,29 @@ def test_graph_capture_of_layer_prefill_4k(gdn, monkeypatch):
     assert torch.equal(out, out_ref) and torch.equal(fin, fin_ref), "eager call after the replays differs"
 
 
+def test_layer_prefill_wait_bound_reports_timeout(gdn, monkeypatch):
+    """The bench's layer with the concurrent state pass's waits (for records and for the
+    norm's row sums) bounded to one sleep through the layer workspace's header: the call
+    ends (every kernel exits), its output and final state are NaN and the workspace status
+    reads GDN_ERR_TIMEOUT.  With the default bound restored the same workspace gives the
+    unbounded call's result and the status reads GDN_OK."""
+    announce("layer prefill T=4096 with a one-sleep wait bound: status GDN_ERR_TIMEOUT")
+    (h, w), out_ref, fin_ref = _layer_4k_bench_run(gdn, False, monkeypatch)
+    ws = torch.zeros(gdn.layer_prefill_workspace_size(4096, 1, 16, 16, 128, 128), dtype=torch.uint8, device=DEV)
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
+    gdn.set_wait_bound(ws, 1)
+    out1, fin1 = gdn.layer_prefill(h, *w, 16, 16, 128, 128, workspace=ws)
+    torch.cuda.synchronize()
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_ERR_TIMEOUT
+    assert torch.isnan(fin1.float()).any(), "the final state of a failed call is NaN"
+    assert torch.isnan(out1.float()).any(), "the output of a failed call is NaN"
+    gdn.set_wait_bound(ws, None)
+    out2, fin2 = gdn.layer_prefill(h, *w, 16, 16, 128, 128, workspace=ws)
+    torch.cuda.synchronize()
+    assert gdn.prefill_workspace_status(ws) == gdn.GDN_OK
+    assert torch.equal(out2, out_ref) and torch.equal(fin2, fin_ref)
+
+
 def test_layer_prefill_state_in_place(gdn):
     """final_state aliasing initial_state and conv_state_out aliasing conv_state_in (the
     exact aliases the ABI allows): the same results as separate output buffers."""
