@@ -76,7 +76,7 @@ __device__ __forceinline__ void store4(float *p, const float *i) {
 // mean square is one reduction inside that lane group.
 // T: element type of x and the conv cache; TW: of the conv weights.
 template <typename T, typename TW, typename TG, int DK, int DV, bool GATED>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_kernel(
     const T *__restrict__ x, const TW *__restrict__ w, T *cs, const float *__restrict__ g,
     const float *__restrict__ beta, float *state, float *__restrict__ o, float scale, float eps,
     int Hk, int Hv, const TG *__restrict__ z, const TG *__restrict__ gamma, TG *__restrict__ out, float norm_eps,
@@ -149,13 +149,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const float rk = rsqrtf(scal[1] + eps);
     const float kq = scal[2] * rq * rk;                // k_hat . (scale q_hat)
 
-    float kr[RPT], qr[RPT];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const int i = rg + RG * r;
-        kr[r] = row_active ? qk_s[DK + i] * rk : 0.f;
-        qr[r] = row_active ? qk_s[i] * rq : 0.f;
-    }
+    // the scaled key and query entries of this thread's rows, read from LDS where they are used
+    // (the lanes of a row group read the same word: broadcast reads) instead of held in 2 RPT
+    // registers: with them the kernel needed 150 VGPRs, three workgroups per compute unit and
+    // 5.3 rounds of workgroups at decode256; now four per compute unit, four rounds (decode
+    // step 1-3 us faster by HIP events in the bench's order, same arithmetic)
+    auto kr = [&](int r) { return row_active ? qk_s[DK + rg + RG * r] * rk : 0.f; };
+    auto qr = [&](int r) { return row_active ? qk_s[rg + RG * r] * rq : 0.f; };
 
     for (int gi = 0; gi < group; ++gi) {
         const int h = kh * group + gi;
@@ -169,10 +169,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         float pm[4] = {0, 0, 0, 0}, pq[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            pm[0] = fmaf(S[r].x, kr[r], pm[0]); pm[1] = fmaf(S[r].y, kr[r], pm[1]);
-            pm[2] = fmaf(S[r].z, kr[r], pm[2]); pm[3] = fmaf(S[r].w, kr[r], pm[3]);
-            pq[0] = fmaf(S[r].x, qr[r], pq[0]); pq[1] = fmaf(S[r].y, qr[r], pq[1]);
-            pq[2] = fmaf(S[r].z, qr[r], pq[2]); pq[3] = fmaf(S[r].w, qr[r], pq[3]);
+            pm[0] = fmaf(S[r].x, kr(r), pm[0]); pm[1] = fmaf(S[r].y, kr(r), pm[1]);
+            pm[2] = fmaf(S[r].z, kr(r), pm[2]); pm[3] = fmaf(S[r].w, kr(r), pm[3]);
+            pq[0] = fmaf(S[r].x, qr(r), pq[0]); pq[1] = fmaf(S[r].y, qr(r), pq[1]);
+            pq[2] = fmaf(S[r].z, qr(r), pq[2]); pq[3] = fmaf(S[r].w, qr(r), pq[3]);
         }
 #pragma unroll
         for (int m = TPR; m < kWave; m <<= 1) {
@@ -225,10 +225,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
             for (int r = 0; r < RPT; ++r) {
                 const int i = rg + RG * r;
                 float4 n;
-                n.x = fmaf(a, S[r].x, kr[r] * delta[0]);
-                n.y = fmaf(a, S[r].y, kr[r] * delta[1]);
-                n.z = fmaf(a, S[r].z, kr[r] * delta[2]);
-                n.w = fmaf(a, S[r].w, kr[r] * delta[3]);
+                n.x = fmaf(a, S[r].x, kr(r) * delta[0]);
+                n.y = fmaf(a, S[r].y, kr(r) * delta[1]);
+                n.z = fmaf(a, S[r].z, kr(r) * delta[2]);
+                n.w = fmaf(a, S[r].w, kr(r) * delta[3]);
                 *reinterpret_cast<float4 *>(sp + (size_t)i * DV) = n;
             }
         }
