@@ -1277,10 +1277,11 @@ struct StateArgs {
     ConvOut cv;
     unsigned long long *status;
     int kgroup;   // as in LocalArgs: head h's K^T is in the records of head h - h % kgroup
-    // gated RMSNorm epilogue (NORM instances): gate rows z and output rows out ([T][Hv D]
-    // bf16, out may be z), the gain (D), epsilon, and the row-sum words
+    // gated RMSNorm epilogue (NORM instances): gate rows z ([T][Hv D] fp32), output rows out
+    // ([T][Hv D] bf16), the gain (D, bf16), epsilon, and the row-sum words
     // [Hv][ncmax][D / 32][64] (high half: the call's tag, low half: the fp32 sum)
-    const bf16 *nz = nullptr, *ngamma = nullptr;
+    const float *nz = nullptr;
+    const bf16 *ngamma = nullptr;
     bf16 *nout = nullptr;
     float neps = 0.f;
     unsigned long long *nsums = nullptr;
@@ -1299,7 +1300,7 @@ struct StateArgs {
 //    gates, are loaded;
 //  - step j + kNormLag + 2: once every word carries the tag, the sums are added in
 //    workgroup order (the same in every workgroup, so results do not depend on timing) and
-//    the normalised, gated rows are stored.
+//    the normalised, gated rows are stored (z fp32, out bf16).
 // A word is loaded three steps after it was stored and used two steps after that, so no
 // barrier waits on device-coherent traffic unless a workgroup of the head lags (with two
 // steps, measured at 4096 tokens x 16 heads, 8 % of the loads still missed a word and the
@@ -1337,7 +1338,7 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
     struct Strip { f32x4 v[CPL / 4]; };
     struct Pend {
         unsigned long long wd[WPL];   // the words of workgroups WPL q .. WPL q + WPL - 1
-        bf16x8 z[CPL / 8];
+        f32x4 z[CPL / 4];
     };
     // step j + 1: chunk j's strips from LDS (buffer j & 1), row sums out
     auto take = [&](int c, Strip &S_) {
@@ -1367,12 +1368,12 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
         constexpr bool FULL = decltype(full_tag)::value;
         load_words(c, Q);
         if (FULL || r < rows_of(c)) {
-            const bf16 *zr = P.nz + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
+            const float *zr = P.nz + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
 #pragma unroll
-            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = *reinterpret_cast<const bf16x8 *>(zr + 8 * i);
+            for (int i = 0; i < CPL / 4; ++i) Q.z[i] = *reinterpret_cast<const f32x4 *>(zr + 4 * i);
         } else {
 #pragma unroll
-            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = bf16x8{};
+            for (int i = 0; i < CPL / 4; ++i) Q.z[i] = zero4();
         }
     };
     auto tagged = [&](const Pend &Q) {
@@ -1401,7 +1402,7 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
             bf16x8 y[CPL / 8];
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
-                y[k / 8][k % 8] = (bf16)(S_.v[k / 4][k % 4] * rn * gm[k] * silu((float)Q.z[k / 8][k % 8]));
+                y[k / 8][k % 8] = (bf16)(S_.v[k / 4][k % 4] * rn * gm[k] * silu(Q.z[k / 4][k % 4]));
             bf16 *yr = P.nout + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
 #pragma unroll
             for (int i = 0; i < CPL / 8; ++i) *reinterpret_cast<bf16x8 *>(yr + 8 * i) = y[i];
@@ -1459,18 +1460,20 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
     if (c < c_hi) step(c, pa);
     // after the last step: s0 .. s4 = chunks c_hi - 2 .. c_hi - 6; the slot of step c_hi
     // holds chunk c_hi - 6, the other chunk c_hi - 5
+    // (the two loaded chunks are finished before the last four are loaded: at most four loads
+    // live at once)
     auto tail = [&](Pend &p6, Pend &p5) {
         Strip sl;
         if (c_hi - 1 >= c_lo) take(c_hi - 1, sl);
         if (c_hi - 6 >= c_lo) finish(c_hi - 6, s4, p6, part);
-        Pend q3, q2, q1;
+        if (c_hi - 5 >= c_lo) finish(c_hi - 5, s3, p5, part);
+        Pend q2, q1;
         if (c_hi - 4 >= c_lo) fetch(c_hi - 4, p6, part);
-        if (c_hi - 3 >= c_lo) fetch(c_hi - 3, q3, part);
+        if (c_hi - 3 >= c_lo) fetch(c_hi - 3, p5, part);
         if (c_hi - 2 >= c_lo) fetch(c_hi - 2, q2, part);
         if (c_hi - 1 >= c_lo) fetch(c_hi - 1, q1, part);
-        if (c_hi - 5 >= c_lo) finish(c_hi - 5, s3, p5, part);
         if (c_hi - 4 >= c_lo) finish(c_hi - 4, s2, p6, part);
-        if (c_hi - 3 >= c_lo) finish(c_hi - 3, s1, q3, part);
+        if (c_hi - 3 >= c_lo) finish(c_hi - 3, s1, p5, part);
         if (c_hi - 2 >= c_lo) finish(c_hi - 2, s0, q2, part);
         if (c_hi - 1 >= c_lo) finish(c_hi - 1, sl, q1, part);
     };
@@ -2086,7 +2089,7 @@ static hipError_t launch_concurrent(const PrefillArgs &a, hipStream_t st, int nc
     StateArgs PS = state_args<D>(a, nc, 0, nc, flags, flag_val, cv);
     if constexpr (D == 128) {
         if (norm_fused<D>(a)) {
-            PS.nz = static_cast<const bf16 *>(a.norm->z);
+            PS.nz = static_cast<const float *>(a.norm->z);
             PS.ngamma = static_cast<const bf16 *>(a.norm->gamma);
             PS.nout = static_cast<bf16 *>(a.norm->out);
             PS.neps = a.norm->eps;

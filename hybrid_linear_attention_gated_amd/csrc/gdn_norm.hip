@@ -55,9 +55,9 @@ struct NormShape {
 
 // Each lane group takes RPT rows spaced kNormThreads / LPR apart and issues all their
 // loads (RPT * NV of y and as many of z per lane) before any arithmetic.
-template <typename T, int DV>
+template <typename TZ, typename T, int DV>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
-    const float *y, const T *z, const T *__restrict__ gamma, T *out, long rows, float eps) {
+    const float *y, const TZ *z, const T *__restrict__ gamma, T *out, long rows, float eps) {
     using S = NormShape<DV>;
     constexpr int LPR = S::LPR, NV = S::NV, RPT = S::RPT, STRIDE = kNormThreads / LPR;
     const int tid = threadIdx.x, sub = tid % LPR;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
             const int c = 4 * (sub + LPR * i);
             if (r < rows) {
                 Vec4<float>::load(y + r * DV + c, yv[k][i]);
-                Vec4<T>::load(z + r * DV + c, zv[k][i]);
+                Vec4<TZ>::load(z + r * DV + c, zv[k][i]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { yv[k][i][e] = 0.f; zv[k][i][e] = 0.f; }
@@ -102,31 +102,32 @@ __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     }
 }
 
-template <typename T, int DV>
+template <typename TZ, typename T, int DV>
 static hipError_t launch_norm_t(const NormArgs &a, hipStream_t st) {
     constexpr int RPB = NormShape<DV>::RPB;
     const long blocks = (a.rows + RPB - 1) / RPB;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gated_rmsnorm_kernel<T, DV>), dim3((unsigned)blocks), dim3(kNormThreads), 0, st, a.y,
-                       (const T *)a.z, (const T *)a.gamma, (T *)a.out, a.rows, a.eps);
+    hipLaunchKernelGGL((gated_rmsnorm_kernel<TZ, T, DV>), dim3((unsigned)blocks), dim3(kNormThreads), 0, st, a.y,
+                       (const TZ *)a.z, (const T *)a.gamma, (T *)a.out, a.rows, a.eps);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename TZ, typename T>
 static hipError_t launch_norm_dv(const NormArgs &a, hipStream_t st) {
     switch (a.dv) {
-        case 16: return launch_norm_t<T, 16>(a, st);
-        case 32: return launch_norm_t<T, 32>(a, st);
-        case 64: return launch_norm_t<T, 64>(a, st);
-        case 128: return launch_norm_t<T, 128>(a, st);
-        case 256: return launch_norm_t<T, 256>(a, st);
+        case 16: return launch_norm_t<TZ, T, 16>(a, st);
+        case 32: return launch_norm_t<TZ, T, 32>(a, st);
+        case 64: return launch_norm_t<TZ, T, 64>(a, st);
+        case 128: return launch_norm_t<TZ, T, 128>(a, st);
+        case 256: return launch_norm_t<TZ, T, 256>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st) {
-    return a.bf16 ? launch_norm_dv<bf16>(a, st) : launch_norm_dv<float>(a, st);
+    if (a.bf16 && a.z_f32) return launch_norm_dv<float, bf16>(a, st);   // the layer prefill's fp32 gate
+    return a.bf16 ? launch_norm_dv<bf16, bf16>(a, st) : launch_norm_dv<float, float>(a, st);
 }
 
 }  // namespace gdn

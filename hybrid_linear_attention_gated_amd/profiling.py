@@ -78,8 +78,9 @@ def short_name(symbol: str) -> str:
         return "decode_gated"        # template argument GATED = true
     if "proj_kernel" in symbol:      # projection GEMM, named by its output tile and mode
         base = "proj_256" if ("ILi128ELi128E" in symbol or "proj_kernel<128, 128" in symbol) else "proj_128"
-        if "ELi1EE" in symbol or symbol.rstrip(")").split("(")[0].endswith(", 1>"):
-            return base + "_layer"   # the layer's input projection (fp32 x)
+        head = symbol.rstrip(")").split("(")[0]
+        if "ELi1EE" in symbol or "ELi2EE" in symbol or head.endswith(", 1>") or head.endswith(", 2>"):
+            return base + "_layer"   # the layer's input projections (fp32 x; the prefill's also fp32 z)
         return base
     for frag, short in KERNELS:
         if frag in symbol:

@@ -384,8 +384,8 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
 
 /*
  * gdn_layer_prefill -- the whole layer over packed sequences in one call: the input
- * projection (as gdn_in_proj, but x leaves it in fp32), gdn_prefill on the fp32 x,
- * the gated RMSNorm of gdn_gated_rmsnorm over each (token, value head) row (bf16 z,
+ * projection (as gdn_in_proj, but x and z leave it in fp32), gdn_prefill on the fp32 x,
+ * the gated RMSNorm of gdn_gated_rmsnorm over each (token, value head) row (fp32 z, bf16
  * gamma and output), and gdn_linear with w_out.  Where the prefill runs its concurrent
  * schedule at dk = dv = 128 (one launch; at most a quarter of the compute units for the
  * state pass), the state pass forms the norm itself and the core output never reaches
@@ -401,7 +401,7 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
  *   out [T][E] bf16; norm_eps >= 0 the RMSNorm epsilon.
  *   workspace  at least gdn_layer_prefill_workspace_size(T, N, Hk, Hv, dk, dv) bytes
  *              (the prefill's workspace first, with its status word and wait bound,
- *              then x, z, g, beta, o and the norm's row-sum words); must not overlap any
+ *              then x, z, y, g, beta, o and the norm's row-sum words); must not overlap any
  *              other argument.
  * dk = dv in {64, 128}; E and Hv as in gdn_in_proj.  out must not overlap an input.
  * The four steps run in order on `stream` (the prefill as in gdn_prefill).

@@ -171,6 +171,16 @@ def test_layer_prefill_norm_in_prefill_ragged(gdn):
     _check_layer(*gpu, *ref)
 
 
+def test_layer_prefill_norm_in_prefill_degenerate_sequences(gdn):
+    """Seven sequences over 1 key / 2 value heads of 128, among them an empty one, a single
+    token and three tokens, caches in: 14 units and 192 chunks keep the prefill in its
+    concurrent schedule, so the norm waves run their prologue and tail on sequences of 0, 1
+    and a few chunks beside long ones."""
+    announce("layer prefill, norm formed in the prefill, 7 sequences incl. empty / 1 / 3 tokens, Hv=2 d=128")
+    gpu, ref = _layer_case(gdn, [5200, 0, 3, 4100, 64, 2500, 1], 256, 1, 2, 128, 660, True, 1.0)
+    _check_layer(*gpu, *ref)
+
+
 def _layer_4k_bench_run(gdn, separate, monkeypatch, **kw):
     wts = inputs.layer_weights(7, 1024, 16, 16, 128, 128)
     h = _cuda(inputs.layer_hidden(8, 4096, 1024))

@@ -57,6 +57,8 @@ def test_short_names():
     assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64ELi0EEEvNS_8ProjArgsE") == "proj_256"
     assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64ELi1EEEvNS_8ProjArgsE") == "proj_256_layer"
     assert profiling.short_name("void gdn::proj_kernel<64, 64, 128, 1>(gdn::ProjArgs)") == "proj_128_layer"
+    assert profiling.short_name("_ZN3gdn11proj_kernelILi128ELi128ELi64ELi2EEEvNS_8ProjArgsE") == "proj_256_layer"
+    assert profiling.short_name("void gdn::proj_kernel<128, 128, 64, 2>(gdn::ProjArgs)") == "proj_256_layer"
     assert profiling.short_name("_ZN3gdn18chunk_local_kernelILi128ELb1EfDF16bEEvPKf") == "chunk_local_fused_x32"
     assert profiling.short_name("_ZN3gdn18chunk_local_kernelILi128ELb1EDF16bS1_EEvPKf") == "chunk_local_fused"
 
