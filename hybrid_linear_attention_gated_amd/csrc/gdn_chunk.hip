@@ -1277,10 +1277,10 @@ struct StateArgs {
     ConvOut cv;
     unsigned long long *status;
     int kgroup;   // as in LocalArgs: head h's K^T is in the records of head h - h % kgroup
-    // gated RMSNorm epilogue (NORM instances): gate rows z ([T][Hv D] fp32), output rows out
+    // gated RMSNorm epilogue (NORM instances): gate rows z ([T][Hv D] fp16), output rows out
     // ([T][Hv D] bf16), the gain (D, bf16), epsilon, and the row-sum words
     // [Hv][ncmax][D / 32][64] (high half: the call's tag, low half: the fp32 sum)
-    const float *nz = nullptr;
+    const f16 *nz = nullptr;
     const bf16 *ngamma = nullptr;
     bf16 *nout = nullptr;
     float neps = 0.f;
@@ -1300,7 +1300,7 @@ struct StateArgs {
 //    gates, are loaded;
 //  - step j + kNormLag + 2: once every word carries the tag, the sums are added in
 //    workgroup order (the same in every workgroup, so results do not depend on timing) and
-//    the normalised, gated rows are stored (z fp32, out bf16).
+//    the normalised, gated rows are stored (z fp16, out bf16).
 // A word is loaded three steps after it was stored and used two steps after that, so no
 // barrier waits on device-coherent traffic unless a workgroup of the head lags (with two
 // steps, measured at 4096 tokens x 16 heads, 8 % of the loads still missed a word and the
@@ -1338,7 +1338,7 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
     struct Strip { f32x4 v[CPL / 4]; };
     struct Pend {
         unsigned long long wd[WPL];   // the words of workgroups WPL q .. WPL q + WPL - 1
-        f32x4 z[CPL / 4];
+        f16x8 z[CPL / 8];
     };
     // step j + 1: chunk j's strips from LDS (buffer j & 1), row sums out
     auto take = [&](int c, Strip &S_) {
@@ -1368,12 +1368,12 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
         constexpr bool FULL = decltype(full_tag)::value;
         load_words(c, Q);
         if (FULL || r < rows_of(c)) {
-            const float *zr = P.nz + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
+            const f16 *zr = P.nz + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
 #pragma unroll
-            for (int i = 0; i < CPL / 4; ++i) Q.z[i] = *reinterpret_cast<const f32x4 *>(zr + 4 * i);
+            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = *reinterpret_cast<const f16x8 *>(zr + 8 * i);
         } else {
 #pragma unroll
-            for (int i = 0; i < CPL / 4; ++i) Q.z[i] = zero4();
+            for (int i = 0; i < CPL / 8; ++i) Q.z[i] = f16x8{};
         }
     };
     auto tagged = [&](const Pend &Q) {
@@ -1402,7 +1402,7 @@ __device__ __forceinline__ void norm_waves(const StateArgs &P, const char *obuf,
             bf16x8 y[CPL / 8];
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
-                y[k / 8][k % 8] = (bf16)(S_.v[k / 4][k % 4] * rn * gm[k] * silu(Q.z[k / 4][k % 4]));
+                y[k / 8][k % 8] = (bf16)(S_.v[k / 4][k % 4] * rn * gm[k] * silu((float)Q.z[k / 8][k % 8]));
             bf16 *yr = P.nout + (size_t)(t0 + c * kChunk + r) * rstride + (size_t)h * D + cb;
 #pragma unroll
             for (int i = 0; i < CPL / 8; ++i) *reinterpret_cast<bf16x8 *>(yr + 8 * i) = y[i];
@@ -2089,7 +2089,7 @@ static hipError_t launch_concurrent(const PrefillArgs &a, hipStream_t st, int nc
     StateArgs PS = state_args<D>(a, nc, 0, nc, flags, flag_val, cv);
     if constexpr (D == 128) {
         if (norm_fused<D>(a)) {
-            PS.nz = static_cast<const float *>(a.norm->z);
+            PS.nz = static_cast<const f16 *>(a.norm->z);
             PS.ngamma = static_cast<const bf16 *>(a.norm->gamma);
             PS.nout = static_cast<bf16 *>(a.norm->out);
             PS.neps = a.norm->eps;

@@ -45,7 +45,7 @@ struct FusedPrep {
 
 // Gated RMSNorm epilogue formed inside the prefill (the layer's prefill): out = o *
 // rsqrt(mean o^2 + eps) * gamma * SiLU(z) per (token, value head) row of dv channels ([T][Hv dv]
-// rows; z fp32, gamma and out bf16).  `sums` holds the row-sum words the
+// rows; z fp16, gamma and out bf16).  `sums` holds the row-sum words the
 // workgroups of a head exchange (norm_epi_words of them).  The launcher applies it where
 // its schedule can (and then sets `fused`); otherwise the caller runs the separate
 // epilogue over o.
@@ -103,7 +103,7 @@ struct NormArgs {
     int dv;
     float eps;
     bool bf16;   // element type of z / gamma / out
-    bool z_f32 = false;   // with bf16: z is fp32 (the layer prefill's gate), gamma and out bf16
+    bool z_f16 = false;   // with bf16: z is fp16 (the layer prefill's gate), gamma and out bf16
 };
 
 // y = a w^T on bf16 MFMA (a [M][K], w [N + 2 heads][K], bf16): columns n < n_split go to
@@ -123,10 +123,10 @@ struct ProjArgs {
     // launcher splits k and sums the slices' planes in a second pass
     float *partial = nullptr;
     size_t partial_cap = 0;
-    // the layer's input projection: columns n < n_split go to y0 as fp32 (and with y1_f32, the
-    // others to y1 as fp32 too: the layer prefill's gate z)
+    // the layer's input projection: columns n < n_split go to y0 as fp32 (and with y1_f16, the
+    // others to y1 as fp16, clamped to its range: the layer prefill's gate z)
     bool y0_f32 = false;
-    bool y1_f32 = false;
+    bool y1_f16 = false;
     int tiles_m = 0, tiles_n = 0, ntiles = 0, ksplit = 1;   // set by the launcher
 };
 

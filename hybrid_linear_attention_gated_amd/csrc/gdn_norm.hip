@@ -33,6 +33,12 @@ template <> struct Vec4<float> {
         *reinterpret_cast<f32x4 *>(p) = f32x4{i[0], i[1], i[2], i[3]};
     }
 };
+template <> struct Vec4<f16> {
+    static __device__ __forceinline__ void load(const f16 *p, float *o) {
+        const f16x4 v = __builtin_nontemporal_load(reinterpret_cast<const f16x4 *>(p));
+        o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+    }
+};
 template <> struct Vec4<bf16> {
     static __device__ __forceinline__ void load(const bf16 *p, float *o) {
         const bf16x4 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x4 *>(p));
@@ -126,7 +132,7 @@ static hipError_t launch_norm_dv(const NormArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t st) {
-    if (a.bf16 && a.z_f32) return launch_norm_dv<float, bf16>(a, st);   // the layer prefill's fp32 gate
+    if (a.bf16 && a.z_f16) return launch_norm_dv<f16, bf16>(a, st);   // the layer prefill's fp16 gate
     return a.bf16 ? launch_norm_dv<bf16, bf16>(a, st) : launch_norm_dv<float, float>(a, st);
 }
 

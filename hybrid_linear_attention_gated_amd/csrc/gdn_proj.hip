@@ -119,28 +119,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const bf16 *base, in
 }
 
 // Kernel modes: plain (bf16 outputs), the layer's input projection (fp32 x) and the layer
-// prefill's input projection (fp32 x and z).  (Each store kind is its own instance: as a
+// prefill's input projection (fp32 x, fp16 z).  (Each store kind is its own instance: as a
 // run-time branch beside the plain store the fp32 one cost the large tile's epilogue 16
 // spilled registers.)
 enum { kProjPlain = 0, kProjLayerIn = 1, kProjLayerInZ = 2 };
 
+// z as fp16, clamped to the fp16 range (an out-of-range gate stays finite)
+__device__ __forceinline__ void store_f16x4_sat(f16 *p, f32x4 v) {
+    f16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (f16)__builtin_fminf(__builtin_fmaxf(v[e], -65504.f), 65504.f);
+    *reinterpret_cast<f16x4 *>(p) = o;
+}
+
 // Four consecutive outputs y[m][n .. n + 3] (n % 4 == 0, so the four lie on one side of
 // n_split, a multiple of 4): columns before n_split to y0 (bf16; fp32 for the layer's input
-// projections), the others to y1 (bf16; fp32 for the layer prefill's).
+// projections), the others to y1 (bf16; fp16 for the layer prefill's).
 template <int MODE>
 __device__ __forceinline__ void store_out(const ProjArgs &p, int m, int n, f32x4 v) {
-    if constexpr (MODE == kProjLayerInZ) {   // both sides fp32: one store through a selected row
-        float *dst = n < p.n_split ? static_cast<float *>(p.y0) + (size_t)m * p.ld0 + n
-                                   : static_cast<float *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split);
-        *reinterpret_cast<f32x4 *>(dst) = v;
-        return;
-    }
     if (n < p.n_split) {
         if (MODE != kProjPlain) *reinterpret_cast<f32x4 *>(static_cast<float *>(p.y0) + (size_t)m * p.ld0 + n) = v;
         else store_bf16x4(static_cast<bf16 *>(p.y0) + (size_t)m * p.ld0 + n, v);
         return;
     }
-    store_bf16x4(static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split), v);
+    if (MODE == kProjLayerInZ) store_f16x4_sat(static_cast<f16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split), v);
+    else store_bf16x4(static_cast<bf16 *>(p.y1) + (size_t)m * p.ld1 + (n - p.n_split), v);
 }
 
 // One output tile: rows m0.., columns n0.. of the main (non-gate) columns.
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs p) {
     const size_t plane = (size_t)p.M * p.N, at = (size_t)m * p.N + n;
     f32x4 t = *reinterpret_cast<const f32x4 *>(p.partial + at);
     for (int sp = 1; sp < p.ksplit; ++sp) t += *reinterpret_cast<const f32x4 *>(p.partial + sp * plane + at);
-    if (p.y1_f32) store_out<kProjLayerInZ>(p, m, n, t);
+    if (p.y1_f16) store_out<kProjLayerInZ>(p, m, n, t);
     else if (p.y0_f32) store_out<kProjLayerIn>(p, m, n, t);
     else store_out<kProjPlain>(p, m, n, t);
 }
@@ -431,7 +434,7 @@ static hipError_t launch_proj_m(const ProjArgs &a, hipStream_t st) {
 
 hipError_t launch_proj(const ProjArgs &a, hipStream_t st) {
     if (a.M <= 0) return hipSuccess;
-    if (a.y1_f32) return launch_proj_m<kProjLayerInZ>(a, st);
+    if (a.y1_f16) return launch_proj_m<kProjLayerInZ>(a, st);
     return a.y0_f32 ? launch_proj_m<kProjLayerIn>(a, st) : launch_proj_m<kProjPlain>(a, st);
 }
 

@@ -384,9 +384,9 @@ int gdn_in_proj(const void *hidden, const void *w_in, void *x, void *z, float *g
 
 /*
  * gdn_layer_prefill -- the whole layer over packed sequences in one call: the input
- * projection (as gdn_in_proj, but x and z leave it in fp32), gdn_prefill on the fp32 x,
- * the gated RMSNorm of gdn_gated_rmsnorm over each (token, value head) row (fp32 z, bf16
- * gamma and output), and gdn_linear with w_out.  Where the prefill runs its concurrent
+ * projection (as gdn_in_proj, but x leaves it in fp32 and z in fp16, clamped to the fp16
+ * range), gdn_prefill on the fp32 x, the gated RMSNorm of gdn_gated_rmsnorm over each
+ * (token, value head) row (fp16 z, bf16 gamma and output), and gdn_linear with w_out.  Where the prefill runs its concurrent
  * schedule at dk = dv = 128 (one launch; at most a quarter of the compute units for the
  * state pass), the state pass forms the norm itself and the core output never reaches
  * memory; the row's mean square is then summed in another order than
