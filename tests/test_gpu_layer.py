@@ -181,6 +181,14 @@ def test_layer_prefill_norm_in_prefill_degenerate_sequences(gdn):
     _check_layer(*gpu, *ref)
 
 
+def test_layer_prefill_norm_in_prefill_order1(gdn):
+    """The retrieval-order variant (order 1) through the layer with the norm formed in the
+    prefill: four sequences over 2 key / 4 value heads of 128 in the concurrent schedule."""
+    announce("layer prefill, norm formed in the prefill, order 1, Hk=2 Hv=4 d=128")
+    gpu, ref = _layer_case(gdn, [2500, 700, 2900, 17], 256, 2, 4, 128, 665, True, 0.5, order=1)
+    _check_layer(*gpu, *ref)
+
+
 def _layer_4k_bench_run(gdn, separate, monkeypatch, **kw):
     wts = inputs.layer_weights(7, 1024, 16, 16, 128, 128)
     h = _cuda(inputs.layer_hidden(8, 4096, 1024))
