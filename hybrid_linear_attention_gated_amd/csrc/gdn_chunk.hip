@@ -65,7 +65,9 @@
 // Schedules (host side, end of file): the two kernels run one after the other, or
 // in segments whose chunk-local and state-pass phases overlap on two streams, or
 // concurrently, the state pass waiting for each record's ready flag while the
-// chunk-local kernel, on the other compute units, publishes them.
+// chunk-local kernel, on the other compute units, publishes them.  In the layer's
+// prefill at D = 128 the concurrent schedule's state pass also forms the gated RMSNorm
+// of the outputs (norm_waves): o stays in LDS and only the normalised rows are stored.
 #include <algorithm>
 #include <mutex>
 #include <numeric>
