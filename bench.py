@@ -12,7 +12,8 @@ input:
 
 Reported beside it (not part of `value`): the whole linear-attention layer at the
 same shape with hidden size 1024 and random weights, gdn_layer_prefill (input
-projection, the prefill above, gated RMSNorm, output projection) and
+projection, the prefill above with the gated RMSNorm formed in its state pass, output
+projection) and
 gdn_layer_decode for the 256 decode rows, under "layer", with torch's library GEMM
 (torch.mm) on the two projection shapes timed in the same region for context.
 
